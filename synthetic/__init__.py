@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU-side tests.
+
+This module draws numbers and encodes them into storage formats. It holds none
+of the normalisation arithmetic: no squares, no means, no reciprocal roots.
+
+Generator (a reading: the pages name no seeds and no generator):
+  * SplitMix64 in counter form.  The stream for (seed, stream id) starts from
+    key = mix64(seed * GOLDEN + stream + 1); its i-th output is
+    mix64(key + (i + 1) * GOLDEN), where mix64 is Steele, Lea and Flood's
+    SplitMix64 finaliser (OOPSLA 2014) and GOLDEN = 0x9E3779B97F4A7C15.
+  * Uniforms use the top 53 bits: u = (bits >> 11) * 2**-53 in [0, 1).
+  * Normals use Box-Muller in float64 on outputs (2k, 2k+1) of the stream:
+    rad = sqrt(-2 ln(1 - u0)), theta = 2 pi u1; element 2k takes rad*cos(theta),
+    element 2k+1 takes rad*sin(theta).
+  * A float64 draw is stored with one round-to-nearest-even into the target
+    format.  bfloat16 goes through float32 first; that double rounding is
+    harmless because float32 keeps 24 >= 2*8 + 2 significand bits.
+
+Stream ids: x = 0, weight = 1, residual = 2, upstream gradient = 3,
+outlier mask = 4, outlier value = 5.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+STREAM_X = 0
+STREAM_W = 1
+STREAM_RESIDUAL = 2
+STREAM_DY = 3
+STREAM_OUTLIER_MASK = 4
+STREAM_OUTLIER_VALUE = 5
+
+# Storage formats, by name.  "bf16" arrays are returned as uint16 bit patterns.
+DTYPES = ("f32", "f16", "bf16")
+
+_CHUNK = 1 << 22
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+def _key(seed: int, stream: int) -> np.uint64:
+    with np.errstate(over="ignore"):
+        s = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) * GOLDEN + np.uint64(stream + 1)
+    return _mix64(np.array([s], dtype=np.uint64))[0]
+
+
+def raw_bits(seed: int, stream: int, start: int, count: int) -> np.ndarray:
+    """Outputs start .. start+count-1 of the counter stream, as uint64."""
+    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return _mix64(_key(seed, stream) + idx * GOLDEN)
+
+
+def uniform(seed: int, stream: int, n: int) -> np.ndarray:
+    """n float64 uniforms in [0, 1)."""
+    out = np.empty(n, dtype=np.float64)
+    for s in range(0, n, _CHUNK):
+        c = min(_CHUNK, n - s)
+        out[s:s + c] = (raw_bits(seed, stream, s, c) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    return out
+
+
+def normal(seed: int, stream: int, n: int, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    """n float64 draws from N(mean, std**2) (std is the standard deviation)."""
+    out = np.empty(n, dtype=np.float64)
+    npairs = (n + 1) // 2
+    for s in range(0, npairs, _CHUNK // 2):
+        c = min(_CHUNK // 2, npairs - s)
+        b = raw_bits(seed, stream, 2 * s, 2 * c) >> np.uint64(11)
+        u0 = b[0::2].astype(np.float64) * (2.0 ** -53)
+        u1 = b[1::2].astype(np.float64) * (2.0 ** -53)
+        rad = np.sqrt(-2.0 * np.log1p(-u0))
+        theta = (2.0 * np.pi) * u1
+        pair = np.empty(2 * c, dtype=np.float64)
+        pair[0::2] = rad * np.cos(theta)
+        pair[1::2] = rad * np.sin(theta)
+        lo, hi = 2 * s, min(2 * s + 2 * c, n)
+        out[lo:hi] = pair[: hi - lo]
+    if mean != 0.0 or std != 1.0:
+        out *= std
+        out += mean
+    return out
+
+
+def encode(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage format (round to nearest even).
+
+    f32 -> float32 array, f16 -> float16 array, bf16 -> uint16 bit patterns.
+    """
+    v = np.asarray(values, dtype=np.float64)
+    if dtype == "f32":
+        return v.astype(np.float32)
+    if dtype == "f16":
+        return v.astype(np.float16)
+    if dtype == "bf16":
+        f = v.astype(np.float32)
+        u = f.view(np.uint32)
+        nan = np.isnan(f)
+        lsb = (u >> np.uint32(16)) & np.uint32(1)
+        with np.errstate(over="ignore"):
+            r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+        if nan.any():
+            r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+        return r
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of stored elements."""
+    if dtype in ("f32", "f16"):
+        return np.asarray(bits).astype(np.float64)
+    if dtype == "bf16":
+        return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def element_size(dtype: str) -> int:
+    return {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+
+
+def normal_tensor(seed: int, stream: int, shape, dtype: str, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+    n = int(np.prod(shape))
+    return encode(normal(seed, stream, n, mean, std), dtype).reshape(shape)
+
+
+def with_outliers(seed: int, shape, dtype: str, mean: float, std: float,
+                  frac: float, lo: float, hi: float) -> np.ndarray:
+    """N(mean, std) draws where each element independently (probability frac)
+    is replaced by sign * U(lo, hi), the sign +1 or -1 with equal odds."""
+    n = int(np.prod(shape))
+    v = normal(seed, STREAM_X, n, mean, std)
+    pick = uniform(seed, STREAM_OUTLIER_MASK, n) < frac
+    idx = np.nonzero(pick)[0]
+    if idx.size:
+        # value stream: output 2i decides the sign, output 2i+1 the magnitude
+        # (drawn only where needed, from the same counter positions each time)
+        key = _key(seed, STREAM_OUTLIER_VALUE)
+        with np.errstate(over="ignore"):
+            bs = _mix64(key + (2 * idx.astype(np.uint64) + np.uint64(1)) * GOLDEN)
+            bm = _mix64(key + (2 * idx.astype(np.uint64) + np.uint64(2)) * GOLDEN)
+        us = (bs >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        um = (bm >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        v[idx] = np.where(us < 0.5, 1.0, -1.0) * (lo + (hi - lo) * um)
+    return encode(v, dtype).reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.  Shapes, distributions and eps follow the five RMSNorm
+# workloads this library is measured on; seeds are fixed per workload.
+# ---------------------------------------------------------------------------
+
+WORKLOADS = {
+    "fwd_f32_64x512": dict(kind="fwd", M=64, H=512, dtype="f32", wdtype="f32",
+                           x=(0.0, 1.0), w=(1.0, 0.1), eps=1e-6, seed=1001),
+    "fwd_bf16_8192x4096": dict(kind="fwd", M=8192, H=4096, dtype="bf16", wdtype="bf16",
+                               x=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1002),
+    "fwd_bf16_32768x2048": dict(kind="fwd", M=32768, H=2048, dtype="bf16", wdtype="bf16",
+                                x=(0.0, 2.0), w=(1.0, 0.1), eps=1e-6, seed=1003),
+    "fwd_f16_32768x2048_outliers": dict(kind="fwd", M=32768, H=2048, dtype="f16", wdtype="f16",
+                                        x=(0.0, 2.0), w=(1.0, 0.1), eps=1e-6, seed=1013,
+                                        outliers=(0.01, 200.0, 300.0)),
+    "fwd_residual_bf16_16384x8192": dict(kind="fwd_residual", M=16384, H=8192, dtype="bf16", wdtype="bf16",
+                                         x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1004),
+    "bwd_bf16_8192x6144": dict(kind="bwd", M=8192, H=6144, dtype="bf16", wdtype="bf16",
+                               x=(0.0, 1.0), w=(1.0, 0.1), dy=(0.0, 1.0), eps=1e-6, seed=1005),
+}
+
+
+def make_inputs(name: str, rows: int | None = None) -> dict:
+    """Host arrays for a named workload.  rows, if given, keeps the first rows
+    rows of every (M, H) tensor (the draws of those rows are unchanged)."""
+    spec = dict(WORKLOADS[name])
+    M, H, dt, wdt, seed = spec["M"], spec["H"], spec["dtype"], spec["wdtype"], spec["seed"]
+    m = M if rows is None else min(rows, M)
+    out = dict(spec)
+    out["M"] = m
+    n = m * H
+    if "outliers" in spec:
+        # every draw is keyed by its position, so the first m rows equal the
+        # first m rows of the full tensor
+        out["x"] = with_outliers(seed, (m, H), dt, *spec["x"], *spec["outliers"])
+    else:
+        out["x"] = encode(normal(seed, STREAM_X, n, *spec["x"]), dt).reshape(m, H)
+    out["w"] = encode(normal(seed, STREAM_W, H, *spec["w"]), wdt)
+    if "r" in spec:
+        out["r"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["r"]), dt).reshape(m, H)
+    if "dy" in spec:
+        out["dy"] = encode(normal(seed, STREAM_DY, n, *spec["dy"]), dt).reshape(m, H)
+    return out
+

@@ -1,0 +1,484 @@
+"""Checks that pin the float64 oracle to facts other than its own code.
+
+Each check takes an oracle.Oracle and raises AssertionError when a fact fails.
+The facts come from the definition of RMSNorm on the page "Skill: Write a
+Triton RMSNorm Kernel" (ahel.ai; "Purpose", "Required reasoning process"
+steps 5-12, "Correctness requirements") and from mathematics:
+
+  * exact cases worked out with rational arithmetic (Fraction), where
+    mean(x^2) + eps is the square of a dyadic rational;
+  * closed forms (constant rows, zero rows, H = 1);
+  * invariants (weightless mean square, column-indexed weight, scaling,
+    permutation, strided rows, x/residual symmetry);
+  * central finite differences of L = sum(dy * y) for the backward pass, and
+    identities that follow from differentiating the forward definition;
+  * library routines for the storage formats (numpy float16/float32, torch
+    bfloat16) and Python's decimal module for high-precision brute force.
+
+test_oracle_pins.py runs every check on the oracle; test_oracle_mutants.py
+runs them on copies of the oracle with planted mistakes and requires each copy
+to fail at least one check.
+"""
+
+from __future__ import annotations
+
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+RNG_SEED = 12345
+
+
+def _rng(k=0):
+    return np.random.default_rng(RNG_SEED + k)
+
+
+def _bf16_bits_from_f32(f32):
+    """bfloat16 bits via torch's float32 -> bfloat16 conversion (a library routine)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_values(bits):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+def _storage(values, dtype):
+    """Store float64 values that are already exact in the format."""
+    v = np.asarray(values, dtype=np.float64)
+    if dtype == "f32":
+        out = v.astype(np.float32)
+    elif dtype == "f16":
+        out = v.astype(np.float16)
+    elif dtype == "bf16":
+        out = _bf16_bits_from_f32(v.astype(np.float32))
+    elif dtype == "f64":
+        out = v.copy()
+    else:
+        raise ValueError(dtype)
+    back = v if dtype == "f64" else (_bf16_values(out) if dtype == "bf16" else out.astype(np.float64))
+    assert np.array_equal(back, v), "test input not exact in its format"
+    return out
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+# ---------------------------------------------------------------------------
+
+def check_decode_all_16bit_patterns(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got16 = o.decode(bits.view(np.float16), "f16")
+    ref16 = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref16)
+    assert np.array_equal(np.isnan(got16), nan)
+    assert np.array_equal(got16[~nan], ref16[~nan])
+    assert np.array_equal(np.signbit(got16[~nan]), np.signbit(ref16[~nan]))
+    gotb = o.decode(bits, "bf16")
+    refb = _bf16_values(bits)
+    nan = np.isnan(refb)
+    assert np.array_equal(np.isnan(gotb), nan)
+    assert np.array_equal(gotb[~nan], refb[~nan])
+    assert np.array_equal(np.signbit(gotb[~nan]), np.signbit(refb[~nan]))
+
+
+def _encode_probe_values():
+    rng = _rng(1)
+    parts = [
+        rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000)),
+        rng.standard_normal(5000) * 1e-6,                 # fp16 subnormal range
+        rng.standard_normal(5000) * 1e-39,                # fp32/bf16 subnormal range
+        rng.uniform(65000, 66000, 2000) * rng.choice([-1, 1], 2000),   # fp16 overflow edge
+        np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.99, 65520.0, 3.4e38, 3.5e38]),
+    ]
+    # exact midpoints between neighbouring representable values (ties)
+    for p in (11, 8, 24):
+        m = rng.integers(1 << (p - 1), 1 << p, 2000).astype(np.float64)
+        e = rng.integers(-10, 10, 2000)
+        parts.append((m + 0.5) * np.exp2(e - (p - 1)))
+    return np.concatenate(parts)
+
+
+def check_encode_matches_libraries(o):
+    v = _encode_probe_values()
+    # float16: numpy rounds float64 -> float16 directly, to nearest even
+    got = o.encode(v, "f16")
+    ref = v.astype(np.float16)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+    # float32: the C/numpy float64 -> float32 conversion
+    got = o.encode(v, "f32")
+    ref = v.astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # bfloat16: torch float32 -> bfloat16 after numpy float64 -> float32; the
+    # two roundings equal one because float32 keeps >= 2*8+2 significand bits
+    got = o.encode(v, "bf16")
+    ref = _bf16_bits_from_f32(v.astype(np.float32))
+    assert np.array_equal(got, ref)
+
+
+def check_encode_ties_by_hand(o):
+    # 1 + 2^-8 lies half way between bf16 neighbours 1 and 1 + 2^-7: ties go to
+    # the even significand (1.0); 1 + 3*2^-8 goes up to 1 + 2^-6.
+    got = o.encode(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)]), "bf16")
+    assert list(got) == [0x3F80, 0x3F82, 0xBF80]
+    # fp16: 1 + 2^-11 ties to 1.0 (0x3C00), 1 + 3*2^-11 to 1 + 2^-9 (0x3C02);
+    # 2^-25 ties to 0, 3*2^-25 rounds to 2*2^-24 (0x0002)
+    got = o.encode(np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -25, 3 * 2.0 ** -25]), "f16")
+    assert list(got.view(np.uint16)) == [0x3C00, 0x3C02, 0x0000, 0x0002]
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+# rows whose mean square plus eps is a perfect square of a dyadic rational
+_EXACT_FWD = [
+    # (row, eps, expected rrms)
+    ([6, 8], 14, Fraction(1, 8)),                 # ms = 50, 50 + 14 = 64
+    ([2, 0, 0, 0], 3, Fraction(1, 2)),            # ms = 1
+    ([3, -3, 3, -3], 7, Fraction(1, 4)),          # ms = 9
+    ([1, 2, 2], 1, Fraction(1, 2)),               # ms = 3
+    ([0.5, 0.5, 0.5, 0.5, 0.5, 0.5, 0.5, 0.5], 0.75, Fraction(1, 1)),  # ms = 1/4
+]
+
+
+def check_exact_rational_rows(o):
+    for row, eps, rr in _EXACT_FWD:
+        H = len(row)
+        ms = sum(Fraction(v) ** 2 for v in row) / H
+        assert (ms + Fraction(eps)) * rr * rr == 1  # the case really is exact
+        w = [1.5, -2.0, 0.25, 4.0, 1.0, 0.5, 2.0, -1.0][:H]
+        for dt in ("f32", "f16", "bf16"):
+            x = _storage(np.array([row], dtype=np.float64), dt)
+            wv = _storage(np.array(w), dt)
+            y, r = o.fwd(x, wv, eps, dt)
+            assert r[0] == float(rr), (row, dt, r[0])
+            exp = np.array([float(Fraction(v) * rr * Fraction(wj)) for v, wj in zip(row, w)])
+            assert np.array_equal(y[0], exp), (row, dt, y[0], exp)
+            y0, _ = o.fwd(x, None, eps, dt)
+            exp0 = np.array([float(Fraction(v) * rr) for v in row])
+            assert np.array_equal(y0[0], exp0)
+
+
+def check_constant_and_zero_rows(o):
+    rng = _rng(2)
+    for H in (1, 3, 64, 257, 4096):
+        for eps in (1e-6, 1e-5, 0.5):
+            c = float(np.float32(rng.uniform(-4, 4)))
+            x = np.full((2, H), c, dtype=np.float32)
+            x[1] = 0.0
+            w = rng.uniform(0.5, 1.5, H).astype(np.float32)
+            y, r = o.fwd(x, w, eps, "f32")
+            r_exp = 1.0 / np.sqrt(c * c + eps)
+            # a float64 sum of H terms is within (H-1) units of 2^-53 of exact
+            tol = 4 * H * 2.0 ** -53 + 1e-15
+            assert abs(r[0] - r_exp) <= tol * r_exp
+            assert np.allclose(y[0], c * r_exp * w.astype(np.float64), rtol=tol, atol=0)
+            assert abs(r[1] - eps ** -0.5) <= 1e-15 * eps ** -0.5
+            assert np.all(y[1] == 0.0)
+
+
+def check_h1_closed_form(o):
+    # H = 1: y = x / sqrt(x^2 + eps) * w, so y^2 + eps * rrms^2 = w^2 and
+    # sign(y) = sign(x * w), over every finite bfloat16 value below 2^63
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = _bf16_values(bits)
+    keep = np.isfinite(vals) & (np.abs(vals) < 2.0 ** 63)
+    x = bits[keep].reshape(-1, 1)
+    eps = 1e-6
+    y, r = o.fwd(x, None, eps, "bf16")
+    xv = vals[keep]
+    assert np.allclose(y[:, 0] ** 2 + eps * r ** 2, 1.0, rtol=0, atol=1e-14)
+    nz = xv != 0
+    assert np.array_equal(np.sign(y[nz, 0]), np.sign(xv[nz]))
+    assert np.all(y[~nz, 0] == 0)
+
+
+def check_weightless_mean_square(o):
+    # mean_j(y_ij^2) = ms/(ms+eps), i.e. mean(y^2) + eps*rrms^2 = 1 per row
+    rng = _rng(3)
+    for dt in ("f32", "f16", "bf16"):
+        for H in (1, 7, 512, 2049):
+            xv = rng.standard_normal((5, H)) * np.array([[1e-3], [1.0], [30.0], [0.01], [2.0]])
+            x = _storage(_round_like(xv, dt), dt)
+            for eps in (1e-6, 1e-2):
+                y, r = o.fwd(x, None, eps, dt)
+                lhs = (y ** 2).mean(axis=1) + eps * r ** 2
+                assert np.allclose(lhs, 1.0, rtol=0, atol=1e-13), (dt, H, lhs)
+
+
+def _round_like(v, dt):
+    if dt == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if dt == "f16":
+        return v.astype(np.float16).astype(np.float64)
+    if dt == "bf16":
+        return _bf16_values(_bf16_bits_from_f32(v.astype(np.float32)))
+    return v
+
+
+def check_weight_indexed_by_column(o):
+    # y(w)_ij = y(None)_ij * w_j for every row: the weight broadcasts over rows
+    rng = _rng(4)
+    for dt in ("f32", "bf16"):
+        H = 33
+        x = _storage(_round_like(rng.standard_normal((6, H)), dt), dt)
+        w = _storage(_round_like(rng.uniform(0.5, 2.0, H) * rng.choice([-1, 1], H), dt), dt)
+        y, _ = o.fwd(x, w, 1e-5, dt)
+        y0, _ = o.fwd(x, None, 1e-5, dt)
+        wd = w.astype(np.float64) if dt != "bf16" else _bf16_values(w)
+        assert np.allclose(y, y0 * wd[None, :], rtol=1e-15, atol=0)
+    # fp32 weight with 16-bit x gives the same numbers as the same weight values
+    x = _storage(_round_like(rng.standard_normal((3, 16)), "bf16"), "bf16")
+    w16 = _storage(_round_like(rng.uniform(0.5, 2, 16), "bf16"), "bf16")
+    w32 = _bf16_values(w16).astype(np.float32)
+    a, _ = o.fwd(x, w16, 1e-5, "bf16", "bf16")
+    b, _ = o.fwd(x, w32, 1e-5, "bf16", "f32")
+    assert np.array_equal(a, b)
+
+
+def check_scale_law(o):
+    # y(2^k x) / y(x) = sqrt((ms + eps) / (ms + eps * 4^-k)) with ms = ms(x)
+    rng = _rng(5)
+    H = 300
+    xv = rng.standard_normal((4, H))
+    x = xv.copy()
+    eps = 1e-3
+    _, r1 = o.fwd(x, None, eps, "f64")
+    ms = (xv ** 2).mean(axis=1)
+    for k in (-3, 1, 5):
+        y2, _ = o.fwd(x * 2.0 ** k, None, eps, "f64")
+        y1, _ = o.fwd(x, None, eps, "f64")
+        ratio = np.sqrt((ms + eps) / (ms + eps * 4.0 ** (-k)))
+        assert np.allclose(y2, y1 * ratio[:, None], rtol=1e-13, atol=0)
+
+
+def check_permutation_and_strides(o):
+    rng = _rng(6)
+    H = 97
+    xv = _round_like(rng.standard_normal((8, H)), "bf16")
+    x = _storage(xv, "bf16")
+    w = _storage(_round_like(rng.uniform(0.5, 1.5, H), "bf16"), "bf16")
+    y, r = o.fwd(x, w, 1e-5, "bf16")
+    perm = rng.permutation(H)
+    yp, rp = o.fwd(np.ascontiguousarray(x[:, perm]), np.ascontiguousarray(w[perm]), 1e-5, "bf16")
+    assert np.allclose(yp, y[:, perm], rtol=1e-15, atol=0)
+    assert np.allclose(rp, r, rtol=1e-15, atol=0)
+    # rows taken from a padded buffer (row stride > H) give the same numbers
+    pad = np.zeros((8, H + 11), dtype=np.uint16)
+    pad[:, :H] = x
+    pad[:, H:] = 0x7F80  # +inf in the padding must never be read
+    ys, rs = o.fwd(pad[:, :H], w, 1e-5, "bf16")
+    assert np.array_equal(ys, y) and np.array_equal(rs, r)
+    # each row alone equals the same row within the batch
+    for i in (0, 5):
+        y1, r1 = o.fwd(x[i:i + 1], w, 1e-5, "bf16")
+        assert np.array_equal(y1[0], y[i]) and r1[0] == r[i]
+
+
+def check_fp16_large_values(o):
+    # 256^2 = 65536 is above the largest float16 (65504); the definition
+    # squares exactly, so a row of +-256 is a constant-magnitude row
+    x = np.array([[256.0, -256.0, 256.0, -256.0], [300.0, 0, 0, 0]], dtype=np.float16)
+    y, r = o.fwd(x, None, 1e-6, "f16")
+    assert np.all(np.isfinite(y))
+    assert np.allclose(np.abs(y[0]), 256.0 / np.sqrt(65536.0 + 1e-6), rtol=1e-15)
+    assert abs(y[1, 0] - 300.0 / np.sqrt(300.0 ** 2 / 4 + 1e-6)) < 1e-14
+
+
+def check_decimal_bruteforce(o):
+    getcontext().prec = 60
+    rng = _rng(7)
+    for dt in ("f32", "f16", "bf16"):
+        for H in (1, 2, 3, 5):
+            xv = _round_like(rng.standard_normal((3, H)) * rng.choice([1e-2, 1.0, 100.0], (3, 1)), dt)
+            wv = _round_like(rng.uniform(0.5, 1.5, H), dt)
+            eps = 1e-5
+            y, r = o.fwd(_storage(xv, dt), _storage(wv, dt), eps, dt)
+            for i in range(3):
+                ss = sum(Decimal(float(v)) ** 2 for v in xv[i])
+                rd = 1 / (ss / H + Decimal(eps)).sqrt()
+                assert abs(Decimal(float(r[i])) - rd) <= rd * Decimal("1e-15")
+                for j in range(H):
+                    yd = Decimal(float(xv[i, j])) * rd * Decimal(float(wv[j]))
+                    assert abs(Decimal(float(y[i, j])) - yd) <= abs(yd) * Decimal("1e-15") + Decimal("1e-300")
+
+
+# ---------------------------------------------------------------------------
+# fused residual
+# ---------------------------------------------------------------------------
+
+def check_residual_identities(o):
+    import torch
+    rng = _rng(8)
+    for dt in ("bf16", "f16", "f32"):
+        H = 130
+        xv = _round_like(rng.standard_normal((6, H)), dt)
+        rv = _round_like(rng.standard_normal((6, H)) * 3, dt)
+        x, res = _storage(xv, dt), _storage(rv, dt)
+        w = _storage(_round_like(rng.uniform(0.5, 1.5, H), dt), dt)
+        y, h, r = o.fwd_residual(x, res, w, 1e-5, dt)
+        # the sum is exact in float64 for these formats
+        assert np.array_equal(h, xv + rv)
+        # rounding the sum: torch adds in float32 and rounds to the format;
+        # the float32 step is harmless (24 >= 2p+2 for p = 8 and 11)
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+        ref = (torch.from_numpy(xv.astype(np.float32)) + torch.from_numpy(rv.astype(np.float32))).to(tdt)
+        enc = o.encode(h, dt)
+        if dt == "bf16":
+            assert np.array_equal(enc, ref.view(torch.int16).numpy().view(np.uint16))
+        elif dt == "f16":
+            assert np.array_equal(enc.view(np.uint16), ref.view(torch.int16).numpy().view(np.uint16))
+        # y is the plain forward applied to the unrounded sum
+        wd = _bf16_values(w) if dt == "bf16" else w.astype(np.float64)
+        y2, r2 = o.fwd(h, wd, 1e-5, "f64")
+        assert np.array_equal(y, y2) and np.array_equal(r, r2)
+        # x and residual play symmetric roles
+        ys, hs, rs = o.fwd_residual(res, x, w, 1e-5, dt)
+        assert np.array_equal(ys, y) and np.array_equal(hs, h) and np.array_equal(rs, r)
+        # a zero residual reduces to the plain forward
+        yz, hz, rz = o.fwd_residual(x, _storage(np.zeros_like(xv), dt), w, 1e-5, dt)
+        yp, rp = o.fwd(x, w, 1e-5, dt)
+        assert np.array_equal(yz, yp) and np.array_equal(rz, rp) and np.array_equal(hz, xv)
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def check_bwd_exact_case(o):
+    # x = [6, 8], eps = 14 -> rrms = 1/8 exactly; w = 1, dy = [1, 0].
+    # Differentiating y_1 = x_1 * (ms + eps)^-1/2 with ms = (x_1^2 + x_2^2)/2:
+    #   dy_1/dx_1 = r (1 - x_1^2 r^2 / 2) = 23/256,  dy_1/dx_2 = -x_1 x_2 r^3 / 2 = -3/64
+    # and dw_j = dy_j * x_j * r = [3/4, 0].
+    x = np.array([[6.0, 8.0]], dtype=np.float32)
+    dy = np.array([[1.0, 0.0]], dtype=np.float32)
+    w = np.array([1.0, 1.0], dtype=np.float32)
+    _, r = o.fwd(x, w, 14.0, "f32")
+    dx, dw, _ = o.bwd(dy, x, w, r, "f32")
+    assert np.array_equal(dx[0], np.array([23 / 256, -3 / 64]))
+    assert np.array_equal(dw, np.array([0.75, 0.0]))
+
+
+def _loss(o, xv, wv, dyv, eps):
+    y, _ = o.fwd(xv, wv, eps, "f64")
+    return float((dyv * y).sum())
+
+
+def check_bwd_finite_differences(o):
+    rng = _rng(9)
+    for (M, H) in ((1, 1), (2, 2), (3, 3), (2, 16), (4, 257)):
+        eps = 1e-2
+        xv = rng.standard_normal((M, H))
+        wv = rng.uniform(0.5, 1.5, H)
+        dyv = rng.standard_normal((M, H))
+        _, r = o.fwd(xv, wv, eps, "f64")
+        dx, dw, _ = o.bwd(dyv, xv, wv, r, "f64")
+        hstep = 1e-5
+        cols = range(H) if H <= 16 else rng.choice(H, 12, replace=False)
+        fdx = np.zeros((M, H))
+        for i in range(M):
+            for j in cols:
+                xp = xv.copy(); xp[i, j] += hstep
+                xm = xv.copy(); xm[i, j] -= hstep
+                fdx[i, j] = (_loss(o, xp, wv, dyv, eps) - _loss(o, xm, wv, dyv, eps)) / (2 * hstep)
+        sel = np.zeros((M, H), dtype=bool)
+        sel[:, list(cols)] = True
+        scale = np.abs(dx).max()
+        assert np.all(np.abs(fdx[sel] - dx[sel]) <= 1e-7 * scale + 1e-9), (M, H)
+        for j in cols:
+            wp = wv.copy(); wp[j] += hstep
+            wm = wv.copy(); wm[j] -= hstep
+            fdw = (_loss(o, xv, wp, dyv, eps) - _loss(o, xv, wm, dyv, eps)) / (2 * hstep)
+            assert abs(fdw - dw[j]) <= 1e-7 * np.abs(dw).max() + 1e-9, (M, H, j)
+        # weightless backward is the w = 1 backward
+        _, r0 = o.fwd(xv, None, eps, "f64")
+        dx0, dw0, _ = o.bwd(dyv, xv, None, r0, "f64")
+        dx1, _, _ = o.bwd(dyv, xv, np.ones(H), r0, "f64")
+        assert dw0 is None and np.array_equal(dx0, dx1)
+
+
+def check_bwd_identities(o):
+    # with c_i = sum_j dy_ij w_j x_ij r_i:
+    #   sum_j x_ij dx_ij = c_i * eps / (ms_i + eps)   (dx is orthogonal to x as eps -> 0)
+    #   sum_j w_j dw_j   = sum_i c_i
+    rng = _rng(10)
+    M, H = 7, 300
+    eps = 1e-3
+    xv = rng.standard_normal((M, H)) * rng.uniform(0.1, 3, (M, 1))
+    wv = rng.uniform(0.5, 1.5, H)
+    dyv = rng.standard_normal((M, H))
+    _, r = o.fwd(xv, wv, eps, "f64")
+    dx, dw, _ = o.bwd(dyv, xv, wv, r, "f64")
+    ms = (xv ** 2).mean(axis=1)
+    c = (dyv * wv[None, :] * xv * r[:, None]).sum(axis=1)
+    assert np.allclose((xv * dx).sum(axis=1), c * eps / (ms + eps), rtol=1e-10, atol=1e-12)
+    assert abs((wv * dw).sum() - c.sum()) <= 1e-11 * np.abs(c).sum()
+
+
+def check_bwd_special_cases(o):
+    rng = _rng(11)
+    H, eps = 64, 1e-2
+    # one row: dw is dy * xn elementwise
+    xv = rng.standard_normal((1, H))
+    wv = rng.uniform(0.5, 1.5, H)
+    dyv = rng.standard_normal((1, H))
+    _, r = o.fwd(xv, wv, eps, "f64")
+    _, dw, _ = o.bwd(dyv, xv, wv, r, "f64")
+    assert np.allclose(dw, dyv[0] * xv[0] * r[0], rtol=1e-15, atol=0)
+    # weightless with dy = y: dx = x * r^2 * eps / (ms + eps)
+    xv = rng.standard_normal((3, H))
+    y, r = o.fwd(xv, None, eps, "f64")
+    dx, _, _ = o.bwd(y, xv, None, r, "f64")
+    ms = (xv ** 2).mean(axis=1)
+    exp = xv * (r ** 2 * eps / (ms + eps))[:, None]
+    assert np.allclose(dx, exp, rtol=1e-11, atol=1e-15)
+    # the saved rrms is used as given, not recomputed from x
+    dxa, _, _ = o.bwd(y, xv, None, r, "f64")
+    dxb, _, _ = o.bwd(y, xv, None, r * 2.0, "f64")
+    assert not np.allclose(dxa, dxb)
+
+
+def check_bwd_linearity_and_rows(o):
+    rng = _rng(12)
+    M, H = 5, 40
+    xv = rng.standard_normal((M, H))
+    wv = rng.uniform(0.5, 1.5, H)
+    d1, d2 = rng.standard_normal((M, H)), rng.standard_normal((M, H))
+    _, r = o.fwd(xv, wv, 1e-5, "f64")
+    a1, w1, _ = o.bwd(d1, xv, wv, r, "f64")
+    a2, w2, _ = o.bwd(d2, xv, wv, r, "f64")
+    a3, w3, _ = o.bwd(2 * d1 - 3 * d2, xv, wv, r, "f64")
+    assert np.allclose(a3, 2 * a1 - 3 * a2, rtol=1e-12, atol=1e-13)
+    assert np.allclose(w3, 2 * w1 - 3 * w2, rtol=1e-12, atol=1e-13)
+    # dw sums over rows: the rows' separate dw add up to the batch's
+    parts = sum(o.bwd(d1[i:i + 1], xv[i:i + 1], wv, r[i:i + 1], "f64")[1] for i in range(M))
+    assert np.allclose(parts, w1, rtol=1e-13, atol=1e-14)
+    # dx of one row does not depend on the other rows
+    a_row, _, _ = o.bwd(d1[2:3], xv[2:3], wv, r[2:3], "f64")
+    assert np.array_equal(a_row[0], a1[2])
+
+
+ALL_CHECKS = [
+    check_decode_all_16bit_patterns,
+    check_encode_matches_libraries,
+    check_encode_ties_by_hand,
+    check_exact_rational_rows,
+    check_constant_and_zero_rows,
+    check_h1_closed_form,
+    check_weightless_mean_square,
+    check_weight_indexed_by_column,
+    check_scale_law,
+    check_permutation_and_strides,
+    check_fp16_large_values,
+    check_decimal_bruteforce,
+    check_residual_identities,
+    check_bwd_exact_case,
+    check_bwd_finite_differences,
+    check_bwd_identities,
+    check_bwd_special_cases,
+    check_bwd_linearity_and_rows,
+]

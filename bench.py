@@ -1,0 +1,273 @@
+"""Throughput of the gfx950 RMSNorm library on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one launch of the library on one batch of seeded synthetic input
+already resident in HBM.  Batches rotate over enough buffer sets (>= 1 GiB per
+cycle) that no step finds its data in the last-level cache.  W untimed steps,
+then exactly K steps between two synchronisations, timed with HIP events on
+the stream the kernels are launched on.  One JSON line is printed.
+
+Workloads (default: the forward at bf16 M=8192 H=4096):
+  fwd_bf16_8192x4096, fwd_f32_64x512, fwd_bf16_32768x2048, fwd_bf16_32768x2048_noweight,
+  fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144
+
+The CPU baseline is the float64 oracle run on the host over a sample of the
+same workload (reported beside the GPU figure, never a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "RMSNorm fwd achieved HBM GB/s (% of peak) + rows/s, bf16 M=8192 H=4096"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+ROTATION_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources; a stored traffic measurement applies only to
+    the kernels it was taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_normalization_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, or None when absent or taken on other kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(kind, M, H, esize, wsize, weighted):
+    """Bytes the method must move once: inputs, weight, outputs, rrms if used."""
+    mat = M * H * esize
+    w = H * wsize if weighted else 0
+    if kind == "fwd":
+        return 2 * mat + w
+    if kind == "fwd_residual":
+        return 4 * mat + w
+    if kind == "bwd":
+        # x, dy read; dx written; rrms read; w read; dw written (float32)
+        return 3 * mat + M * 4 + w + H * 4
+    raise ValueError(kind)
+
+
+WORKLOADS = {
+    "fwd_bf16_8192x4096": ("fwd_bf16_8192x4096", True),
+    "fwd_f32_64x512": ("fwd_f32_64x512", True),
+    "fwd_bf16_32768x2048": ("fwd_bf16_32768x2048", True),
+    "fwd_bf16_32768x2048_noweight": ("fwd_bf16_32768x2048", False),
+    "fwd_f16_32768x2048_outliers": ("fwd_f16_32768x2048_outliers", True),
+    "fwd_residual_bf16_16384x8192": ("fwd_residual_bf16_16384x8192", True),
+    "bwd_bf16_8192x6144": ("bwd_bf16_8192x6144", True),
+}
+
+
+def cpu_baseline(spec, kind, weighted, seconds):
+    """The oracle as it stands, single-threaded, over the workload's rows
+    repeated until `seconds` have passed; reported in GB/s of the same
+    algorithmic bytes."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    rows = min(spec["M"], 1024)
+    d = synthetic.make_inputs(spec["name"], rows=rows)
+    w = d["w"] if weighted else None
+    eps = float(np.float32(spec["eps"]))
+    if kind == "bwd":
+        _, r = oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
+        r32 = r.astype(np.float32)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        if kind == "fwd":
+            oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
+        elif kind == "fwd_residual":
+            oracle.fwd_residual(d["x"], d["r"], w, eps, d["dtype"], d["wdtype"])
+        else:
+            oracle.bwd(d["dy"], d["x"], w, r32, d["dtype"], d["wdtype"])
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    es = synthetic.element_size(d["dtype"])
+    ws = synthetic.element_size(d["wdtype"])
+    nbytes = algorithmic_bytes(kind, rows, spec["H"], es, ws, weighted) * passes
+    return {
+        "value": round(nbytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {rows} of {spec['M']} rows, {passes} passes in {el:.1f} s, float64, one thread",
+        "rows_per_s": round(rows * passes / el, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="fwd_bf16_8192x4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0 skips it)")
+    ap.add_argument("--geom", default="", help="development: forced launch geometry 'vpt,wpr,rpw,grid'")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="also run a plain device copy of known size (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows shard across GPUs with no "
+              "communication, so per-GPU throughput is the one-GPU figure)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import transformer_normalization_amd as tn
+
+    if not os.path.exists(tn.LIB_PATH):
+        from transformer_normalization_amd import build as hipbuild
+        hipbuild.build()
+    tn.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    name, weighted = WORKLOADS[args.workload]
+    spec = dict(synthetic.WORKLOADS[name])
+    spec["name"] = name
+    kind = spec["kind"]
+    if args.geom:
+        parts = [int(v) for v in args.geom.split(",")]
+        tn.set_geometry("bwd" if kind == "bwd" else "fwd", *parts)
+
+    dev = torch.device("cuda:0")
+    d = synthetic.make_inputs(name)
+    dt = d["dtype"]
+    M, H = spec["M"], spec["H"]
+    es, ws = synthetic.element_size(dt), synthetic.element_size(d["wdtype"])
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+
+    def up(a, fmt):
+        a = np.ascontiguousarray(a)
+        if fmt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    per_set = algorithmic_bytes(kind, M, H, es, ws, weighted)
+    nsets = max(2, -(-ROTATION_BYTES // per_set))
+    x0 = up(d["x"], dt)
+    w = up(d["w"], d["wdtype"]) if weighted else None
+    sets = []
+    for i in range(nsets):
+        s = {"x": x0 if i == 0 else x0.clone(), "y": torch.empty_like(x0)}
+        if kind == "fwd_residual":
+            r0 = up(d["r"], dt) if i == 0 else sets[0]["r"].clone()
+            s.update(r=r0, ro=torch.empty_like(x0))
+        if kind == "bwd":
+            dy0 = up(d["dy"], dt) if i == 0 else sets[0]["dy"].clone()
+            s.update(dy=dy0)
+        sets.append(s)
+    del d
+    eps = spec["eps"]
+    if kind == "bwd":
+        rr = torch.empty(M, dtype=torch.float32, device=dev)
+        tn.rmsnorm_fwd(sets[0]["x"], w, eps, rrms=rr)
+        dw = torch.empty(H, dtype=torch.float32, device=dev)
+        wsp = torch.empty(tn.rmsnorm_bwd_workspace_bytes(M, H), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % nsets]
+        if kind == "fwd":
+            tn.rmsnorm_fwd(s["x"], w, eps, out=s["y"])
+        elif kind == "fwd_residual":
+            tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
+        else:
+            tn.rmsnorm_bwd(s["dy"], s["x"], w, rr, dx=s["y"], dw=dw, workspace=wsp)
+
+    for i in range(args.warmup):
+        step(i)
+    if args.copy_reference:
+        for _ in range(5):
+            sets[1]["y"].copy_(sets[0]["x"])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    gbs = per_set / (ms * 1e-3) / 1e9
+
+    traffic = stored_traffic(args.workload)
+    result = {
+        "metric": METRIC if args.workload == "fwd_bf16_8192x4096" else f"RMSNorm {args.workload} achieved HBM GB/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "H": H, "eps": eps,
+                   "weight": spec["wdtype"] if weighted else None, "buffer_sets": nsets,
+                   "bytes_per_step": per_set},
+        "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "rows_per_s": round(M / (ms * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if args.geom:
+        result["config"]["geom"] = args.geom
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(spec, kind, weighted, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * rmsnorm.h -- C ABI of the MI355X (gfx950) RMSNorm library.
+ *
+ * RMSNorm over the trailing (hidden) dimension of an (M, H) row-major matrix:
+ *
+ *     y[i, j] = x[i, j] * rrms[i] * w[j],   rrms[i] = 1 / sqrt(sum_j x[i, j]^2 / H + eps)
+ *
+ * as defined on the page "Skill: Write a Triton RMSNorm Kernel" (ahel.ai),
+ * section "Purpose" and "Required reasoning process" steps 1-10: the mean
+ * divides by the full row length H, eps sits inside the square root, the
+ * weight has shape (H,) and is indexed by column only, there is no bias and
+ * no mean subtraction, squares and sums are taken in float32 whatever the
+ * storage format.  The weightless form (w == NULL, y = x * rrms) follows the
+ * page "rocm-kernels" (skillselion.com), "Core Kernel Implementations",
+ * RMSNorm, where LTX-Video's norms carry no weight.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are row-major (M, H) with unit stride along H.  *_stride
+ *    arguments are the distance between consecutive rows, in ELEMENTS, and
+ *    must be >= H.  Rows may be padded (stride > H) or be a strided view.
+ *  - Every data pointer is a DEVICE pointer on the current HIP device
+ *    (hipGetDevice).  The caller owns all memory.  The library never
+ *    allocates, frees or synchronises; it only validates the arguments and
+ *    enqueues kernels on `stream` (0 = the null stream), so results are ready
+ *    when that stream reaches them.
+ *  - x_dtype is the storage format of every (M, H) matrix of a call; outputs
+ *    are written in that same format, rounded to nearest even.  w_dtype is
+ *    the weight's format: either x_dtype or RMSN_F32.  rrms and dw are
+ *    always float32.
+ *  - M == 0 is valid and enqueues nothing (after the other arguments pass
+ *    validation).
+ *  - An output may be the very same buffer as an input of the same shape
+ *    (same pointer and same stride; e.g. y == x): every element is read
+ *    before it is written.  Any other overlap between an output and another
+ *    buffer of the call is rejected with RMSN_ERR_INVALID_ARG.
+ *  - Argument errors are detected on the host before any HIP call, so they
+ *    are reported without touching the device.  RMSN_ERR_HIP reports a failed
+ *    device query or kernel launch (asynchronous faults surface later, on
+ *    the stream, as with any HIP kernel).  rmsnorm_last_error() returns a
+ *    message for the most recent failure on the calling thread.
+ *  - All entry points are thread-safe and keep no state between calls,
+ *    apart from a per-device cache of the compute-unit count.
+ *  - Results do not depend on the stream, on timing or on other calls: the
+ *    same inputs give the same bits on the same device.
+ */
+#ifndef RMSNORM_H
+#define RMSNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMSN_F32 = 0,  /* IEEE binary32 */
+    RMSN_F16 = 1,  /* IEEE binary16 */
+    RMSN_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+} rmsn_dtype_t;
+
+typedef enum {
+    RMSN_OK = 0,
+    RMSN_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size/stride/eps, overlap */
+    RMSN_ERR_UNSUPPORTED = 2, /* dtype combination, H too large, device not gfx950 */
+    RMSN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    RMSN_ERR_HIP = 4          /* device query or kernel launch failed */
+} rmsn_status_t;
+
+/*
+ * Forward RMSNorm ("Skill: Write a Triton RMSNorm Kernel", "Required reasoning
+ * process" steps 1-10; weightless form: "rocm-kernels", "Core Kernel
+ * Implementations").
+ *
+ *   x     (M, H) input, rows x_stride elements apart.
+ *   w     (H,) weight, contiguous, or NULL for the weightless norm.
+ *   y     (M, H) output, rows y_stride elements apart; may equal x (same
+ *         pointer and stride).
+ *   rrms  (M,) float32 output of the per-row 1/sqrt(mean(x^2) + eps) -- the
+ *         statistic the backward pass reads (step 10) -- or NULL.
+ *   eps   > 0 and finite; added inside the square root.
+ *   H     >= 1 and <= 2^30.
+ */
+rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *w, void *y,
+                          int64_t y_stride, float *rrms, int64_t M, int64_t H, float eps,
+                          rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream);
+
+/*
+ * Fused residual pre-norm ("Skill: Write a Triton RMSNorm Kernel", "Use this
+ * when" and "Kernel design rules": the residual is added in float32 after
+ * both inputs are widened and before squaring; the post-add sum may be
+ * written back as the next residual stream).
+ *
+ *   h[i, j]            = float32(x[i, j]) + float32(residual[i, j])
+ *   residual_out[i, j] = h[i, j] rounded to x_dtype (nearest even)
+ *   y                  = RMSNorm of the UNROUNDED h, as rmsnorm_fwd
+ *
+ *   residual      (M, H) input, rows r_stride apart.
+ *   residual_out  (M, H) output, rows ro_stride apart, or NULL to skip the
+ *                 write-back; may equal residual or x (same pointer/stride).
+ *   y, w, rrms, eps, M, H  as rmsnorm_fwd; y may equal x or residual.
+ */
+rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, const void *residual,
+                                   int64_t r_stride, const void *w, void *y, int64_t y_stride,
+                                   void *residual_out, int64_t ro_stride, float *rrms, int64_t M,
+                                   int64_t H, float eps, rmsn_dtype_t x_dtype,
+                                   rmsn_dtype_t w_dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace rmsnorm_bwd needs for (M, H) when a weight
+ * gradient is requested (0 when M <= 0 or H <= 0).  The value depends only on
+ * M and H, never on the device, so it can be sized once per shape.
+ */
+size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t H);
+
+/*
+ * Backward RMSNorm ("Skill: Write a Triton RMSNorm Kernel", "Required
+ * reasoning process" step 12, and "Correctness requirements": the saved rrms
+ * is read, never recomputed).  With xn = x * rrms[i] and g = dy * w:
+ *
+ *   dx[i, j] = rrms[i] * g[i, j] - xn[i, j] * (rrms[i] / H) * sum_j g[i, j] * xn[i, j]
+ *   dw[j]    = sum_i dy[i, j] * xn[i, j]          (shape (H,), float32)
+ *
+ *   dy, x     (M, H) inputs, rows dy_stride / x_stride apart.
+ *   w         (H,) weight, or NULL for the weightless norm (then g = dy and dw
+ *             must be NULL).
+ *   rrms      (M,) float32 saved by the forward pass.
+ *   dx        (M, H) output in x_dtype, rows dx_stride apart; may equal dy or
+ *             x (same pointer and stride).
+ *   dw        (H,) float32 output, OVERWRITTEN (not accumulated), or NULL to
+ *             skip the weight gradient.  The column sums are reduced in a
+ *             fixed order: no atomics, the same bits on every run.
+ *   workspace device scratch of at least rmsnorm_bwd_workspace_bytes(M, H)
+ *             bytes, 256-byte aligned, when dw != NULL (ignored otherwise).
+ *             Its contents on entry do not matter; it must not overlap any
+ *             other argument, and it must not be used by another call that
+ *             may run at the same time.
+ */
+rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void *x, int64_t x_stride,
+                          const void *w, const float *rrms, void *dx, int64_t dx_stride, float *dw,
+                          void *workspace, size_t workspace_bytes, int64_t M, int64_t H,
+                          rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream);
+
+/* Fixed text for a status code (never NULL). */
+const char *rmsnorm_status_string(rmsn_status_t status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char *rmsnorm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_H */

@@ -1,0 +1,40 @@
+/*
+ * rmsnorm_tuning.h -- development hook of librmsnorm.so for launch-geometry
+ * sweeps and for tests that must reach every kernel path at small sizes.
+ * Not needed for normal use: without it the library picks the geometry
+ * itself from H, the storage format and the device.
+ *
+ * The override changes which threads handle which elements, and therefore
+ * the order of the float32 sums, but never what is computed.  It is
+ * process-wide; set it only while no other thread is calling the library.
+ */
+#ifndef RMSNORM_TUNING_H
+#define RMSNORM_TUNING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * which = 0: forward and fused residual.  A row is owned by wpr waves of 64
+ *            threads, each thread holding vpt 16-byte vectors (single elements
+ *            when rows are not 16-byte aligned); third = rows per workgroup;
+ *            grid > 0 caps the number of workgroups (they then walk the rows
+ *            grid-stride), 0 = one workgroup per group of rows.
+ * which = 1: backward.  vpt and wpr as above (one row per workgroup at a
+ *            time); third = number of workgroups P, each owning a contiguous
+ *            block of rows and one row of dw partial sums (0 = default).
+ * vpt <= 0 or wpr <= 0 clears the override.  A tile too small for the row
+ * takes the two-pass path, which requires vpt = 4 (8 for single elements).
+ * An override the shape cannot use makes the call fail with
+ * RMSN_ERR_INVALID_ARG.
+ */
+void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_TUNING_H */

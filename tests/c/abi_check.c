@@ -1,0 +1,119 @@
+/* Plain C client of librmsnorm.so: checks that include/rmsnorm.h compiles as
+ * C and that argument errors are reported before any device work.  Pointers
+ * are never dereferenced: every call below fails validation on the host.
+ * Exit status 0 = all checks passed. */
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rmsnorm.h"
+#include "rmsnorm_tuning.h"
+
+static int failures = 0;
+
+static void expect(const char *what, rmsn_status_t got, rmsn_status_t want) {
+    if (got != want) {
+        printf("FAIL %s: got %s want %s (%s)\n", what, rmsnorm_status_string(got), rmsnorm_status_string(want),
+               rmsnorm_last_error());
+        ++failures;
+    } else if (want != RMSN_OK && rmsnorm_last_error()[0] == '\0') {
+        printf("FAIL %s: no error detail\n", what);
+        ++failures;
+    }
+}
+
+int main(void) {
+    /* fake, 256-byte aligned device addresses far apart; never dereferenced */
+    void *x = (void *)(uintptr_t)0x100000000ull;
+    void *y = (void *)(uintptr_t)0x200000000ull;
+    void *w = (void *)(uintptr_t)0x300000000ull;
+    void *r = (void *)(uintptr_t)0x400000000ull;
+    float *rr = (float *)(uintptr_t)0x500000000ull;
+    void *ws = (void *)(uintptr_t)0x600000000ull;
+    float *dw = (float *)(uintptr_t)0x700000000ull;
+    const int64_t M = 64, H = 4096;
+
+    expect("M == 0 is a no-op", rmsnorm_fwd(NULL, H, NULL, NULL, H, NULL, 0, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_OK);
+    if (rmsnorm_last_error()[0] != '\0') { printf("FAIL error detail not cleared\n"); ++failures; }
+    expect("x NULL", rmsnorm_fwd(NULL, H, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("y NULL", rmsnorm_fwd(x, H, w, NULL, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("H 0", rmsnorm_fwd(x, H, w, y, H, rr, M, 0, 1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("M < 0", rmsnorm_fwd(x, H, w, y, H, rr, -1, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("stride < H", rmsnorm_fwd(x, H - 1, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("eps 0", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 0.0f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("eps < 0", rmsnorm_fwd(x, H, w, y, H, rr, M, H, -1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("eps NaN", rmsnorm_fwd(x, H, w, y, H, rr, M, H, NAN, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("eps inf", rmsnorm_fwd(x, H, w, y, H, rr, M, H, INFINITY, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("bad dtype", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 1e-5f, (rmsn_dtype_t)7, RMSN_BF16, 0),
+           RMSN_ERR_UNSUPPORTED);
+    expect("w f16 with x bf16", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_F16, 0),
+           RMSN_ERR_UNSUPPORTED);
+    expect("H > 2^30", rmsnorm_fwd(x, (int64_t)1 << 31, w, y, (int64_t)1 << 31, rr, 1, (int64_t)1 << 31, 1e-5f,
+                                   RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_UNSUPPORTED);
+    expect("y partially overlaps x",
+           rmsnorm_fwd(x, H, w, (char *)x + 2 * H, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("y same start as x but other stride",
+           rmsnorm_fwd(x, H, w, x, 2 * H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("rrms inside x", rmsnorm_fwd(x, H, w, y, H, (float *)x, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("rrms inside y", rmsnorm_fwd(x, H, w, y, H, (float *)((char *)y + 64), M, H, 1e-5f, RMSN_BF16,
+                                        RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("stride overflow", rmsnorm_fwd(x, INT64_MAX / 2, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+
+    expect("residual NULL", rmsnorm_fwd_residual(x, H, NULL, H, w, y, H, r, H, rr, M, H, 1e-5f, RMSN_BF16,
+                                                 RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("residual_out overlaps y", rmsnorm_fwd_residual(x, H, r, H, w, y, H, (char *)y + 16, H, rr, M, H, 1e-5f,
+                                                           RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("residual_out == y", rmsnorm_fwd_residual(x, H, r, H, w, y, H, y, H, rr, M, H, 1e-5f, RMSN_BF16,
+                                                     RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("r_stride < H", rmsnorm_fwd_residual(x, H, r, 8, w, y, H, NULL, 0, rr, M, H, 1e-5f, RMSN_BF16,
+                                                RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("residual M == 0", rmsnorm_fwd_residual(NULL, H, NULL, H, NULL, NULL, H, NULL, H, NULL, 0, H, 1e-5f,
+                                                   RMSN_F16, RMSN_F32, 0), RMSN_OK);
+
+    size_t need = rmsnorm_bwd_workspace_bytes(M, H);
+    if (need != (size_t)M * H * 4) { printf("FAIL workspace size %zu\n", need); ++failures; }
+    if (rmsnorm_bwd_workspace_bytes(1 << 20, 6144) != (size_t)1024 * 6144 * 4) {
+        printf("FAIL workspace cap\n"); ++failures;
+    }
+    if (rmsnorm_bwd_workspace_bytes(0, H) != 0 || rmsnorm_bwd_workspace_bytes(M, 0) != 0) {
+        printf("FAIL empty workspace\n"); ++failures;
+    }
+    expect("dw without w", rmsnorm_bwd(r, H, x, H, NULL, rr, y, H, dw, ws, need, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("workspace NULL", rmsnorm_bwd(r, H, x, H, w, rr, y, H, dw, NULL, need, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_WORKSPACE);
+    expect("workspace small", rmsnorm_bwd(r, H, x, H, w, rr, y, H, dw, ws, need - 1, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_WORKSPACE);
+    expect("workspace misaligned", rmsnorm_bwd(r, H, x, H, w, rr, y, H, dw, (char *)ws + 4, need, M, H, RMSN_BF16,
+                                               RMSN_BF16, 0), RMSN_ERR_WORKSPACE);
+    expect("rrms NULL", rmsnorm_bwd(r, H, x, H, w, NULL, y, H, dw, ws, need, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("dw overlaps workspace", rmsnorm_bwd(r, H, x, H, w, rr, y, H, (float *)ws, ws, need, M, H, RMSN_BF16,
+                                                RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("dx overlaps rrms", rmsnorm_bwd(r, H, x, H, w, (float *)y, y, H, dw, ws, need, M, H, RMSN_BF16,
+                                           RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("workspace overlaps x", rmsnorm_bwd(r, H, x, H, w, rr, y, H, dw, x, need, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("bwd M == 0 without dw", rmsnorm_bwd(NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, NULL, 0, 0, H,
+                                                RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
+
+    /* a geometry that cannot cover the row is rejected before the device */
+    rmsnorm_tuning_set_geometry(0, 3, 1, 1, 0);
+    expect("override too small", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    rmsnorm_tuning_set_geometry(0, 2, 32, 1, 0);
+    expect("override too many threads", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    rmsnorm_tuning_set_geometry(0, 0, 0, 0, 0);
+
+    if (strcmp(rmsnorm_status_string(RMSN_ERR_WORKSPACE), "RMSN_ERR_WORKSPACE") != 0) {
+        printf("FAIL status string\n"); ++failures;
+    }
+    printf("%s (%d failures)\n", failures ? "FAILED" : "ok", failures);
+    return failures ? 1 : 0;
+}

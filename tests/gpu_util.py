@@ -1,0 +1,115 @@
+"""Helpers for GPU tests: host <-> device transfers of stored bits and
+chunked comparison of library outputs against the float64 oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synthetic
+from tests import parity
+
+DEV = "cuda:0"
+
+
+def torch_dtype(dtype):
+    import torch
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+
+
+def to_dev(a, dtype):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t, dtype):
+    import torch
+    t = t.detach()
+    if dtype == "bf16":
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def check_out(rep, got, ref64, dtype, offset=0):
+    if dtype == "f32":
+        parity.check_f32(rep, got, ref64, offset)
+    else:
+        parity.check16(rep, got, ref64, dtype, oracle.encode, offset)
+    return rep
+
+
+def eps32(eps):
+    """The float32 value the library receives; the oracle uses the same."""
+    return float(np.float32(eps))
+
+
+def fwd_vs_oracle(x, w, y_host, rrms_host, eps, dtype, wdtype=None, chunk=2048, name="fwd"):
+    M, H = x.shape
+    rep_y, rep_r = parity.Report(f"{name} y"), parity.Report(f"{name} rrms")
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        yref, rref = oracle.fwd(x[r0:r1], w, eps32(eps), dtype, wdtype)
+        check_out(rep_y, y_host[r0:r1], yref, dtype, r0 * H)
+        if rrms_host is not None:
+            parity.check_f32(rep_r, rrms_host[r0:r1], rref, r0)
+    return rep_y, rep_r
+
+
+def residual_vs_oracle(x, r, w, y_host, ro_host, rrms_host, eps, dtype, wdtype=None, chunk=1024, name="residual"):
+    M, H = x.shape
+    rep_y, rep_ro, rep_r = (parity.Report(f"{name} y"), parity.Report(f"{name} residual_out"),
+                            parity.Report(f"{name} rrms"))
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        yref, href, rref = oracle.fwd_residual(x[r0:r1], r[r0:r1], w, eps32(eps), dtype, wdtype)
+        check_out(rep_y, y_host[r0:r1], yref, dtype, r0 * H)
+        if ro_host is not None:
+            hb = oracle.encode(href, dtype)
+            bad = (ro_host[r0:r1].view(np.uint16 if dtype != "f32" else np.uint32)
+                   != hb.view(np.uint16 if dtype != "f32" else np.uint32))
+            rep_ro.n += bad.size
+            rep_ro.merge_bad(bad, r0 * H)
+        if rrms_host is not None:
+            parity.check_f32(rep_r, rrms_host[r0:r1], rref, r0)
+    return rep_y, rep_ro, rep_r
+
+
+def bwd_vs_oracle(dy, x, w, rrms32, dx_host, dw_host, dtype, wdtype=None, chunk=1024, name="bwd"):
+    M, H = x.shape
+    rep_dx, rep_dw = parity.Report(f"{name} dx"), parity.Report(f"{name} dw")
+    dw_ref = np.zeros(H) if w is not None else None
+    colscale = np.zeros(H)
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        dxref, dwref, terms = oracle.bwd(dy[r0:r1], x[r0:r1], w, rrms32[r0:r1], dtype, wdtype)
+        if dtype == "f32":
+            parity.check_dx_f32(rep_dx, dx_host[r0:r1], dxref, terms, r0 * H)
+        else:
+            parity.check_dx16(rep_dx, dx_host[r0:r1], dxref, terms, dtype, oracle.encode, oracle.decode, r0 * H)
+        if w is not None:
+            dw_ref += dwref
+            xn = oracle.decode(x[r0:r1], dtype) * rrms32[r0:r1].astype(np.float64)[:, None]
+            colscale += np.abs(oracle.decode(dy[r0:r1], dtype) * xn).sum(axis=0)
+    if w is not None and dw_host is not None:
+        parity.check_dw(rep_dw, dw_host, dw_ref, colscale)
+    return rep_dx, rep_dw
+
+
+def assert_ok(*reports):
+    for r in reports:
+        print(r, flush=True)
+    bad = [str(r) for r in reports if not r.ok()]
+    assert not bad, "; ".join(bad)
+
+
+def inputs(seed, M, H, dtype, wdtype=None, xdist=(0.0, 1.0), weight=True, residual=False, dy=False):
+    d = {"x": synthetic.normal_tensor(seed, synthetic.STREAM_X, (M, H), dtype, *xdist)}
+    d["w"] = synthetic.normal_tensor(seed, synthetic.STREAM_W, (H,), wdtype or dtype, 1.0, 0.1) if weight else None
+    if residual:
+        d["r"] = synthetic.normal_tensor(seed, synthetic.STREAM_RESIDUAL, (M, H), dtype)
+    if dy:
+        d["dy"] = synthetic.normal_tensor(seed, synthetic.STREAM_DY, (M, H), dtype)
+    return d

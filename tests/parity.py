@@ -1,0 +1,116 @@
+"""Comparison rules between the GPU library's outputs and the float64 oracle.
+
+  * float32 outputs (y, dx in float32, rrms): |got - ref| <= 1e-5*|ref| + 1e-6.
+  * 16-bit outputs: the stored bits are at most one unit in the last place
+    away from the oracle's value rounded to nearest even (distance between
+    the two bit patterns on the ordered integer line; +0 and -0 are equal).
+  * residual write-back: bit-exact.
+  * dx (16-bit): one ulp as above, where an element whose two terms
+    rrms*g and xn*rrms*c/H nearly cancel may instead be within one ulp taken
+    at 2^-10 * (|rrms*g| + |xn*rrms*c/H|): no float32 evaluation can do better
+    on such elements.  The number of elements judged by that floor is reported.
+  * dw: |got - ref| <= 1e-3*|ref| + 1e-5 * sum_i |dy*xn| for each column (a
+    pure relative bound is ill-posed for columns whose sum crosses zero).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PREC = {"bf16": 8, "f16": 11}
+MIN_QUANTUM = {"bf16": 2.0 ** -133, "f16": 2.0 ** -24}
+
+
+def ordered16(bits):
+    b = np.asarray(bits).view(np.uint16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def ulp_distance16(a_bits, b_bits):
+    return np.abs(ordered16(a_bits) - ordered16(b_bits))
+
+
+def ulp_at(mag, dtype):
+    """One unit in the last place of the format at magnitude mag (>= 0)."""
+    p = PREC[dtype]
+    m = np.maximum(np.asarray(mag, dtype=np.float64), 1e-300)
+    return np.maximum(np.exp2(np.floor(np.log2(m)) - (p - 1)), MIN_QUANTUM[dtype])
+
+
+class Report:
+    def __init__(self, name):
+        self.name = name
+        self.n = 0
+        self.failed = 0
+        self.max_ulp = 0
+        self.floor_used = 0
+        self.max_rel = 0.0
+        self.first_bad = None
+
+    def merge_bad(self, bad_mask, offset=0):
+        nb = int(np.count_nonzero(bad_mask))
+        if nb and self.first_bad is None:
+            self.first_bad = offset + int(np.flatnonzero(bad_mask.ravel())[0])
+        self.failed += nb
+
+    def ok(self):
+        return self.failed == 0
+
+    def __str__(self):
+        return (f"{self.name}: {self.n} elements, {self.failed} failed, max ulp {self.max_ulp}, "
+                f"floor-judged {self.floor_used}, max rel {self.max_rel:.3g}, first bad {self.first_bad}")
+
+
+def check16(report, got_bits, ref64, dtype, encode, offset=0):
+    ref_bits = encode(ref64, dtype)
+    d = ulp_distance16(got_bits, ref_bits)
+    # NaN in the reference must be NaN on the GPU too
+    report.n += d.size
+    report.max_ulp = max(report.max_ulp, int(d.max()) if d.size else 0)
+    report.merge_bad(d > 1, offset)
+    return report
+
+
+def check_f32(report, got, ref64, offset=0):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref64)
+    bad = ~(err <= 1e-5 * np.abs(ref64) + 1e-6)
+    report.n += got.size
+    if got.size:
+        report.max_rel = max(report.max_rel, float((err / np.maximum(np.abs(ref64), 1e-30)).max()))
+    report.merge_bad(bad, offset)
+    return report
+
+
+def check_dx16(report, got_bits, ref64, terms, dtype, encode, decode, offset=0):
+    ref_bits = encode(ref64, dtype)
+    d = ulp_distance16(got_bits, ref_bits)
+    within = d <= 1
+    got = decode(got_bits, dtype)
+    floor_ok = np.abs(got - ref64) <= ulp_at(2.0 ** -10 * terms, dtype)
+    report.n += d.size
+    report.max_ulp = max(report.max_ulp, int(d.max()) if d.size else 0)
+    report.floor_used += int(np.count_nonzero(~within & floor_ok))
+    report.merge_bad(~(within | floor_ok), offset)
+    return report
+
+
+def check_dx_f32(report, got, ref64, terms, offset=0):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref64)
+    strict = err <= 1e-5 * np.abs(ref64) + 1e-6
+    relaxed = err <= 1e-5 * np.maximum(np.abs(ref64), 2.0 ** -10 * terms) + 1e-6
+    report.n += got.size
+    report.floor_used += int(np.count_nonzero(~strict & relaxed))
+    report.merge_bad(~relaxed, offset)
+    return report
+
+
+def check_dw(report, got, ref64, colscale):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref64)
+    bad = ~(err <= 1e-3 * np.abs(ref64) + 1e-5 * colscale)
+    report.n += got.size
+    report.max_rel = max(report.max_rel, float((err / np.maximum(np.abs(ref64), 1e-30)).max()))
+    report.merge_bad(bad)
+    return report

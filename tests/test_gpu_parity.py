@@ -1,0 +1,468 @@
+"""GPU parity: the HIP library, called through its C ABI (via the Python
+binding), against the float64 oracle on the same seeded inputs.
+
+Full-size workloads are compared element by element (the oracle handles them
+in row chunks).  Smaller cases cover the kernels' other paths: ragged and
+tiny H, single-element accesses for unaligned rows, strided rows, the two-pass
+path and the grid-stride loop (forced through the tuning hook), aliasing of
+outputs with inputs, guard regions around outputs, determinism and the
+method's exact invariants.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests import gpu_util as G
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import transformer_normalization_amd as tn  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _default_geometry():
+    tn.set_geometry("fwd")
+    tn.set_geometry("bwd")
+    yield
+    tn.set_geometry("fwd")
+    tn.set_geometry("bwd")
+
+
+def run_fwd(x, w, eps, dtype, wdtype=None):
+    xd = G.to_dev(x, dtype)
+    wd = None if w is None else G.to_dev(w, wdtype or dtype)
+    y, rr = tn.rmsnorm_fwd(xd, wd, eps, return_rrms=True)
+    torch.cuda.synchronize()
+    return G.to_host(y, dtype), rr.cpu().numpy()
+
+
+def run_residual(x, r, w, eps, dtype, wdtype=None):
+    xd, rd = G.to_dev(x, dtype), G.to_dev(r, dtype)
+    wd = None if w is None else G.to_dev(w, wdtype or dtype)
+    y, ro, rr = tn.rmsnorm_fwd_residual(xd, rd, wd, eps, return_rrms=True)
+    torch.cuda.synchronize()
+    return G.to_host(y, dtype), G.to_host(ro, dtype), rr.cpu().numpy()
+
+
+def run_bwd(dy, x, w, rrms32, dtype, wdtype=None):
+    dyd, xd = G.to_dev(dy, dtype), G.to_dev(x, dtype)
+    wd = None if w is None else G.to_dev(w, wdtype or dtype)
+    dx, dw = tn.rmsnorm_bwd(dyd, xd, wd, torch.from_numpy(rrms32).to(G.DEV))
+    torch.cuda.synchronize()
+    return G.to_host(dx, dtype), (None if dw is None else dw.cpu().numpy())
+
+
+def oracle_rrms32(x, w, eps, dtype, wdtype=None, chunk=2048):
+    """Per-row rrms from the oracle, rounded to float32 (the saved statistic)."""
+    out = np.empty(x.shape[0], dtype=np.float32)
+    for r0 in range(0, x.shape[0], chunk):
+        _, r = oracle.fwd(x[r0:r0 + chunk], w, G.eps32(eps), dtype, wdtype)
+        out[r0:r0 + chunk] = r.astype(np.float32)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads, full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["fwd_f32_64x512", "fwd_bf16_8192x4096"])
+def test_workload_fwd(name):
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    y, rr = run_fwd(d["x"], d["w"], d["eps"], d["dtype"], d["wdtype"])
+    G.assert_ok(*G.fwd_vs_oracle(d["x"], d["w"], y, rr, d["eps"], d["dtype"], d["wdtype"], name=name))
+
+
+@pytest.mark.parametrize("name", ["fwd_bf16_32768x2048", "fwd_f16_32768x2048_outliers"])
+@pytest.mark.parametrize("weighted", [True, False], ids=["weight", "weightless"])
+def test_workload_fwd_mix(name, weighted):
+    d = synthetic.make_inputs(name)
+    w = d["w"] if weighted else None
+    print(f"[gpu] {name} weighted={weighted}", flush=True)
+    y, rr = run_fwd(d["x"], w, d["eps"], d["dtype"], d["wdtype"])
+    G.assert_ok(*G.fwd_vs_oracle(d["x"], w, y, rr, d["eps"], d["dtype"], d["wdtype"], name=name))
+    if d["dtype"] == "f16":
+        # squares of the +-200..300 outliers exceed the float16 range; the
+        # outputs stay finite because the sums are float32
+        assert np.isfinite(y.astype(np.float32)).all()
+
+
+def test_workload_fwd_residual():
+    name = "fwd_residual_bf16_16384x8192"
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    y, ro, rr = run_residual(d["x"], d["r"], d["w"], d["eps"], d["dtype"], d["wdtype"])
+    G.assert_ok(*G.residual_vs_oracle(d["x"], d["r"], d["w"], y, ro, rr, d["eps"], d["dtype"], d["wdtype"],
+                                      name=name))
+
+
+def test_workload_bwd():
+    name = "bwd_bf16_8192x6144"
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    rr = oracle_rrms32(d["x"], d["w"], d["eps"], d["dtype"])
+    dx, dw = run_bwd(d["dy"], d["x"], d["w"], rr, d["dtype"])
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], rr, dx, dw, d["dtype"], name=name))
+
+
+def test_workload_bwd_chained_with_gpu_rrms():
+    """The GPU forward's own rrms feeds the GPU backward; the oracle backward
+    gets the same float32 rrms."""
+    name = "bwd_bf16_8192x6144"
+    d = synthetic.make_inputs(name, rows=2048)
+    _, rr = run_fwd(d["x"], d["w"], d["eps"], d["dtype"])
+    rr = rr.astype(np.float32)
+    dx, dw = run_bwd(d["dy"], d["x"], d["w"], rr, d["dtype"])
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], rr, dx, dw, d["dtype"], name=name + " chained"))
+
+
+# ---------------------------------------------------------------------------
+# shapes: ragged, tiny and long rows, every format
+# ---------------------------------------------------------------------------
+
+EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 3072, 4097, 5120, 6144, 8191, 12288,
+          16385, 32768, 65536]
+
+
+def _rows_for(H):
+    return 257 if H <= 8192 else 5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("H", EDGE_H)
+def test_edge_shapes_all_paths(dtype, H):
+    M = _rows_for(H)
+    d = G.inputs(1000 + H, M, H, dtype, residual=True, dy=True)
+    x, w, r, dy = d["x"], d["w"], d["r"], d["dy"]
+    print(f"[gpu] edge {dtype} M={M} H={H}", flush=True)
+    y, rr = run_fwd(x, w, 1e-5, dtype)
+    reps = list(G.fwd_vs_oracle(x, w, y, rr, 1e-5, dtype, name=f"fwd {dtype} H={H}"))
+    y2, ro, rr2 = run_residual(x, r, w, 1e-6, dtype)
+    reps += list(G.residual_vs_oracle(x, r, w, y2, ro, rr2, 1e-6, dtype, name=f"res {dtype} H={H}"))
+    r32 = oracle_rrms32(x, w, 1e-5, dtype)
+    dx, dw = run_bwd(dy, x, w, r32, dtype)
+    reps += list(G.bwd_vs_oracle(dy, x, w, r32, dx, dw, dtype, name=f"bwd {dtype} H={H}"))
+    G.assert_ok(*reps)
+
+
+@pytest.mark.parametrize("M", [1, 2, 255, 257])
+def test_row_counts(M):
+    H = 4096
+    d = G.inputs(7 + M, M, H, "bf16", residual=True, dy=True)
+    y, rr = run_fwd(d["x"], d["w"], 1e-5, "bf16")
+    reps = list(G.fwd_vs_oracle(d["x"], d["w"], y, rr, 1e-5, "bf16"))
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-5, "bf16")
+    dx, dw = run_bwd(d["dy"], d["x"], d["w"], r32, "bf16")
+    reps += list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, dx, dw, "bf16"))
+    G.assert_ok(*reps)
+
+
+def test_page_test_shapes():
+    """Shapes the pages test with: (1,1024,2048), (2,1024,2048), (2,4096,3072)
+    in float16 with a weight of ones, and (4,4096,4096) in bfloat16."""
+    import json
+    import os
+    spec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_cases.json")))
+    for case in spec["fwd_cases"]:
+        shape, dtype = tuple(case["shape"]), case["dtype"]
+        M, H = int(np.prod(shape[:-1])), shape[-1]
+        x = synthetic.normal_tensor(case["seed"], synthetic.STREAM_X, (M, H), dtype)
+        w = synthetic.encode(np.ones(H), dtype) if case["weight"] == "ones" else \
+            synthetic.normal_tensor(case["seed"], synthetic.STREAM_W, (H,), dtype, 1.0, 0.1)
+        y, rr = run_fwd(x, w, case["eps"], dtype)
+        G.assert_ok(*G.fwd_vs_oracle(x, w, y, rr, case["eps"], dtype, name=f"page {shape} {dtype}"))
+
+
+def test_float32_weight_with_16bit_x():
+    for dtype in ("bf16", "f16"):
+        d = G.inputs(31, 300, 4096, dtype, wdtype="f32", residual=True, dy=True)
+        y, rr = run_fwd(d["x"], d["w"], 1e-5, dtype, "f32")
+        reps = list(G.fwd_vs_oracle(d["x"], d["w"], y, rr, 1e-5, dtype, "f32"))
+        y2, ro, rr2 = run_residual(d["x"], d["r"], d["w"], 1e-5, dtype, "f32")
+        reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], y2, ro, rr2, 1e-5, dtype, "f32"))
+        r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype, "f32")
+        dx, dw = run_bwd(d["dy"], d["x"], d["w"], r32, dtype, "f32")
+        reps += list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, dx, dw, dtype, "f32"))
+        G.assert_ok(*reps)
+
+
+# ---------------------------------------------------------------------------
+# forced geometries: multi-row workgroups, grid-stride loop, two passes
+# ---------------------------------------------------------------------------
+
+FWD_GEOMS = [
+    (1, 8, 1, 0), (2, 4, 1, 0), (4, 2, 2, 0), (8, 1, 4, 0), (8, 1, 2, 0), (2, 4, 2, 0),
+    (2, 4, 1, 7),      # 7 workgroups walk 300 rows grid-stride (LDS parity reuse)
+    (8, 1, 4, 5),      # one wave per row, 4 rows per workgroup, grid-stride
+    (4, 1, 1, 0),      # 256 vectors per chunk < 512: two passes
+    (4, 1, 2, 3),      # two passes inside a grid-stride loop
+]
+
+
+@pytest.mark.parametrize("geom", FWD_GEOMS, ids=[str(g) for g in FWD_GEOMS])
+def test_forced_fwd_geometry(geom):
+    M, H = 300, 4096
+    d = G.inputs(55, M, H, "bf16", residual=True)
+    tn.set_geometry("fwd", *geom)
+    y, rr = run_fwd(d["x"], d["w"], 1e-5, "bf16")
+    reps = list(G.fwd_vs_oracle(d["x"], d["w"], y, rr, 1e-5, "bf16", name=f"fwd {geom}"))
+    y2, ro, rr2 = run_residual(d["x"], d["r"], d["w"], 1e-5, "bf16")
+    reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], y2, ro, rr2, 1e-5, "bf16", name=f"res {geom}"))
+    G.assert_ok(*reps)
+
+
+BWD_GEOMS = [(1, 8, 0), (2, 4, 0), (4, 2, 0), (2, 4, 1), (2, 4, 7), (2, 4, 300), (4, 1, 16), (4, 2, 3)]
+
+
+@pytest.mark.parametrize("geom", BWD_GEOMS, ids=[str(g) for g in BWD_GEOMS])
+def test_forced_bwd_geometry(geom):
+    M, H = 300, 4096
+    d = G.inputs(56, M, H, "bf16", dy=True)
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-6, "bf16")
+    tn.set_geometry("bwd", geom[0], geom[1], geom[2])
+    dx, dw = run_bwd(d["dy"], d["x"], d["w"], r32, "bf16")
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, dx, dw, "bf16", name=f"bwd {geom}"))
+
+
+def test_forced_geometry_rejected_when_it_cannot_fit():
+    tn.set_geometry("fwd", 3, 1, 1, 0)  # 192 vectors < 512 and vpt != 4: no two-pass tile
+    d = G.inputs(57, 4, 4096, "bf16")
+    with pytest.raises(tn.RMSNormError) as e:
+        run_fwd(d["x"], d["w"], 1e-5, "bf16")
+    assert e.value.status == 1
+
+
+# ---------------------------------------------------------------------------
+# layout: strides, alignment, aliasing, guard regions
+# ---------------------------------------------------------------------------
+
+def test_aligned_padding_is_bit_identical():
+    M, H, pad = 64, 4096, 64  # pad keeps 16-byte alignment of every row
+    d = G.inputs(61, M, H, "bf16", residual=True, dy=True)
+    base = G.to_dev(d["x"], "bf16")
+    wide = torch.zeros((M, H + pad), dtype=torch.bfloat16, device=G.DEV)
+    wide[:, :H] = base
+    y1 = tn.rmsnorm_fwd(base, G.to_dev(d["w"], "bf16"), 1e-5)
+    y2 = tn.rmsnorm_fwd(wide[:, :H], G.to_dev(d["w"], "bf16"), 1e-5)
+    out_wide = torch.zeros_like(wide)
+    y3 = tn.rmsnorm_fwd(base, G.to_dev(d["w"], "bf16"), 1e-5, out=out_wide[:, :H])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    assert torch.count_nonzero(out_wide[:, H:].view(torch.int16)) == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_misaligned_rows_use_single_elements(dtype):
+    M, H = 33, 4096
+    d = G.inputs(62, M, H, dtype, residual=True, dy=True)
+    for pad, offset in ((1, 0), (0, 1), (3, 1)):
+        buf = torch.zeros(offset + M * (H + pad), dtype=G.torch_dtype(dtype), device=G.DEV)
+        view = buf[offset:].view(M, H + pad)[:, :H]
+        view.copy_(G.to_dev(d["x"], dtype))
+        wd = G.to_dev(d["w"], dtype)
+        y, rr = tn.rmsnorm_fwd(view, wd, 1e-5, return_rrms=True)
+        rview = torch.zeros_like(buf)[offset:].view(M, H + pad)[:, :H]
+        rview.copy_(G.to_dev(d["r"], dtype))
+        y2, ro, rr2 = tn.rmsnorm_fwd_residual(view, rview, wd, 1e-5, return_rrms=True)
+        dyv = torch.zeros_like(buf)[offset:].view(M, H + pad)[:, :H]
+        dyv.copy_(G.to_dev(d["dy"], dtype))
+        r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype)
+        dx, dw = tn.rmsnorm_bwd(dyv, view, wd, torch.from_numpy(r32).to(G.DEV))
+        torch.cuda.synchronize()
+        reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(y, dtype), rr.cpu().numpy(), 1e-5, dtype,
+                                    name=f"fwd pad={pad} off={offset}"))
+        reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype), G.to_host(ro, dtype),
+                                          rr2.cpu().numpy(), 1e-5, dtype, name=f"res pad={pad} off={offset}"))
+        reps += list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx, dtype), dw.cpu().numpy(), dtype,
+                                     name=f"bwd pad={pad} off={offset}"))
+        G.assert_ok(*reps)
+
+
+def test_in_place_outputs():
+    M, H = 200, 6144
+    d = G.inputs(63, M, H, "bf16", residual=True, dy=True)
+    wd = G.to_dev(d["w"], "bf16")
+    ref_y = tn.rmsnorm_fwd(G.to_dev(d["x"], "bf16"), wd, 1e-5)
+    x = G.to_dev(d["x"], "bf16")
+    tn.rmsnorm_fwd(x, wd, 1e-5, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), ref_y.view(torch.int16))
+    # residual stream updated in place, y written over x
+    ref = tn.rmsnorm_fwd_residual(G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16"), wd, 1e-5)
+    x, r = G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16")
+    tn.rmsnorm_fwd_residual(x, r, wd, 1e-5, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(r.view(torch.int16), ref[1].view(torch.int16))
+    # dx written over dy
+    r32 = torch.from_numpy(oracle_rrms32(d["x"], d["w"], 1e-5, "bf16")).to(G.DEV)
+    dref, wref = tn.rmsnorm_bwd(G.to_dev(d["dy"], "bf16"), G.to_dev(d["x"], "bf16"), wd, r32)
+    dy = G.to_dev(d["dy"], "bf16")
+    _, dw = tn.rmsnorm_bwd(dy, G.to_dev(d["x"], "bf16"), wd, r32, dx=dy)
+    torch.cuda.synchronize()
+    assert torch.equal(dy.view(torch.int16), dref.view(torch.int16))
+    assert torch.equal(dw, wref)
+
+
+def test_in_place_two_pass():
+    M, H = 40, 4096
+    d = G.inputs(64, M, H, "bf16", residual=True)
+    wd = G.to_dev(d["w"], "bf16")
+    tn.set_geometry("fwd", 4, 1, 1, 0)  # two passes over 256-vector chunks
+    ref = tn.rmsnorm_fwd_residual(G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16"), wd, 1e-5)
+    x, r = G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16")
+    tn.rmsnorm_fwd_residual(x, r, wd, 1e-5, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(r.view(torch.int16), ref[1].view(torch.int16))
+
+
+GUARD = 4096
+
+
+def _guarded(shape, dtype, fill):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * GUARD,), fill, dtype=dtype, device=G.DEV)
+    return buf, buf[GUARD:GUARD + n].view(*shape)
+
+
+def test_guard_regions_untouched():
+    for (M, H) in ((17, 4097), (33, 4096), (9, 65536), (5, 3)):
+        d = G.inputs(65 + H, M, H, "bf16", residual=True, dy=True)
+        xd, rd, dyd, wd = (G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16"), G.to_dev(d["dy"], "bf16"),
+                           G.to_dev(d["w"], "bf16"))
+        sentinel = -1234.0
+        ybuf, y = _guarded((M, H), torch.bfloat16, sentinel)
+        robuf, ro = _guarded((M, H), torch.bfloat16, sentinel)
+        rrbuf, rr = _guarded((M,), torch.float32, sentinel)
+        dxbuf, dx = _guarded((M, H), torch.bfloat16, sentinel)
+        dwbuf, dw = _guarded((H,), torch.float32, sentinel)
+        tn.rmsnorm_fwd(xd, wd, 1e-5, out=y, rrms=rr)
+        tn.rmsnorm_fwd_residual(xd, rd, wd, 1e-5, out=torch.empty_like(xd), residual_out=ro)
+        tn.rmsnorm_bwd(dyd, xd, wd, rr, dx=dx, dw=dw)
+        torch.cuda.synchronize()
+        for buf in (ybuf, robuf, rrbuf, dxbuf, dwbuf):
+            head, tail = buf[:GUARD], buf[-GUARD:]
+            assert torch.all(head == sentinel) and torch.all(tail == sentinel), (M, H)
+
+
+# ---------------------------------------------------------------------------
+# determinism and exact invariants
+# ---------------------------------------------------------------------------
+
+def test_determinism():
+    d = synthetic.make_inputs("bwd_bf16_8192x6144", rows=1024)
+    xd, dyd, wd = G.to_dev(d["x"], "bf16"), G.to_dev(d["dy"], "bf16"), G.to_dev(d["w"], "bf16")
+    a = tn.rmsnorm_fwd(xd, wd, 1e-6, return_rrms=True)
+    b = tn.rmsnorm_fwd(xd, wd, 1e-6, return_rrms=True)
+    c = tn.rmsnorm_bwd(dyd, xd, wd, a[1])
+    e = tn.rmsnorm_bwd(dyd, xd, wd, a[1])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+    assert torch.equal(c[0].view(torch.int16), e[0].view(torch.int16)) and torch.equal(c[1], e[1])
+
+
+def test_weightless_equals_weight_of_ones():
+    for dtype in ("bf16", "f16", "f32"):
+        d = G.inputs(71, 128, 2048, dtype, xdist=(0.0, 2.0), residual=True)
+        xd = G.to_dev(d["x"], dtype)
+        ones = torch.ones(2048, dtype=G.torch_dtype(dtype), device=G.DEV)
+        a = tn.rmsnorm_fwd(xd, None, 1e-6)
+        b = tn.rmsnorm_fwd(xd, ones, 1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(-1).view(torch.uint8), b.view(-1).view(torch.uint8))
+
+
+def test_zero_residual_equals_plain_forward():
+    for dtype in ("bf16", "f16", "f32"):
+        d = G.inputs(72, 100, 4096, dtype)
+        xd, wd = G.to_dev(d["x"], dtype), G.to_dev(d["w"], dtype)
+        y, rr = tn.rmsnorm_fwd(xd, wd, 1e-5, return_rrms=True)
+        y2, ro, rr2 = tn.rmsnorm_fwd_residual(xd, torch.zeros_like(xd), wd, 1e-5, return_rrms=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(-1).view(torch.uint8), y2.view(-1).view(torch.uint8))
+        assert torch.equal(ro.view(-1).view(torch.uint8), xd.view(-1).view(torch.uint8))
+        assert torch.equal(rr, rr2)
+
+
+def test_residual_symmetric_in_x_and_r():
+    d = G.inputs(73, 64, 8192, "bf16", residual=True)
+    xd, rd, wd = G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16"), G.to_dev(d["w"], "bf16")
+    a = tn.rmsnorm_fwd_residual(xd, rd, wd, 1e-5)
+    b = tn.rmsnorm_fwd_residual(rd, xd, wd, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+def test_unit_rows_give_weight_exactly():
+    # rows of +-1 with eps = 1e-5: y = +-w * 0.999995..., which rounds back to w in bf16
+    H = 4096
+    rng = np.random.default_rng(5)
+    x = synthetic.encode(rng.choice([-1.0, 1.0], (16, H)), "bf16")
+    w = synthetic.normal_tensor(74, synthetic.STREAM_W, (H,), "bf16", 1.0, 0.1)
+    y, _ = run_fwd(x, w, 1e-5, "bf16")
+    expect = synthetic.encode(synthetic.decode(x, "bf16") * synthetic.decode(w, "bf16")[None, :], "bf16")
+    assert np.array_equal(y, expect)
+
+
+def test_scale_law_with_tiny_eps():
+    # eps = 1e-30 vanishes next to mean(x^2) in float32, so y(2^k x) = y(x)
+    d = G.inputs(75, 64, 4096, "bf16")
+    x = synthetic.decode(d["x"], "bf16")
+    y1, _ = run_fwd(d["x"], d["w"], 1e-30, "bf16")
+    for k in (-8, 3):
+        y2, _ = run_fwd(synthetic.encode(x * 2.0 ** k, "bf16"), d["w"], 1e-30, "bf16")
+        assert parity.ulp_distance16(y1, y2).max() <= 1
+
+
+def test_weightless_mean_square():
+    d = G.inputs(76, 256, 2048, "bf16", xdist=(0.0, 2.0))
+    y, rr = run_fwd(d["x"], None, 1e-6, "bf16")
+    yv = synthetic.decode(y, "bf16")
+    ms = (yv ** 2).mean(axis=1) + 1e-6 * rr.astype(np.float64) ** 2
+    assert np.all(np.abs(ms - 1.0) <= 2.0 ** -7)
+
+
+def test_constant_and_zero_rows():
+    H = 4096
+    x = np.zeros((3, H), dtype=np.float32)
+    x[0] = 0.75
+    x[1] = -3.0
+    y, rr = run_fwd(x, None, 1e-6, "f32")
+    assert np.all(y[2] == 0.0)
+    assert abs(rr[2] - 1000.0) <= 1e-5 * 1000.0
+    for i, c in ((0, 0.75), (1, -3.0)):
+        exp = c / np.sqrt(c * c + float(np.float32(1e-6)))
+        assert np.all(np.abs(y[i] - exp) <= 1e-5 * abs(exp) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_exhaustive_h1(dtype):
+    """H = 1 over every finite value of the format: y = x / sqrt(x^2 + eps)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = synthetic.decode(bits if dtype == "bf16" else bits.view(np.float16), dtype)
+    keep = np.isfinite(vals) & (np.abs(vals) < 2.0 ** 63)
+    x = (bits[keep] if dtype == "bf16" else bits[keep].view(np.float16)).reshape(-1, 1)
+    y, rr = run_fwd(x, None, 1e-6, dtype)
+    G.assert_ok(*G.fwd_vs_oracle(x, None, y, rr, 1e-6, dtype, name=f"H=1 {dtype}"))
+
+
+def test_empty_batch_is_a_no_op():
+    xd = torch.empty((0, 4096), dtype=torch.bfloat16, device=G.DEV)
+    y = tn.rmsnorm_fwd(xd, None, 1e-5)
+    assert y.shape == (0, 4096)
+    wd = torch.ones(4096, dtype=torch.bfloat16, device=G.DEV)
+    dx, dw = tn.rmsnorm_bwd(xd, xd, wd, torch.empty(0, dtype=torch.float32, device=G.DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw) == 0  # dw over zero rows is zero

@@ -1,0 +1,232 @@
+"""RMSNorm for AMD Instinct MI355X (gfx950): thin Python binding of librmsnorm.so.
+
+The functions below only marshal torch tensors into the C ABI declared in
+include/rmsnorm.h (device pointers, row strides in elements, dtype codes and
+the current HIP stream); every step of the computation runs in the library's
+HIP kernels.  There is no CPU fallback: without the built library the
+functions raise.
+
+    y = rmsnorm_fwd(x, w, eps)                       # w may be None
+    y, rrms = rmsnorm_fwd(x, w, eps, return_rrms=True)
+    y, res_out = rmsnorm_fwd_residual(x, residual, w, eps)
+    dx, dw = rmsnorm_bwd(dy, x, w, rrms)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "librmsnorm.so")
+
+RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
+STATUS = {0: "RMSN_OK", 1: "RMSN_ERR_INVALID_ARG", 2: "RMSN_ERR_UNSUPPORTED", 3: "RMSN_ERR_WORKSPACE",
+          4: "RMSN_ERR_HIP"}
+EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
+            "rmsnorm_status_string", "rmsnorm_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class RMSNormError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librmsnorm.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path == LIB_PATH:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m transformer_normalization_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+        lib.rmsnorm_fwd.argtypes = [vp, i64, vp, vp, i64, vp, i64, i64, f32, i32, i32, vp]
+        lib.rmsnorm_fwd.restype = i32
+        lib.rmsnorm_fwd_residual.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, i64, i64, f32, i32, i32, vp]
+        lib.rmsnorm_fwd_residual.restype = i32
+        lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
+        lib.rmsnorm_bwd_workspace_bytes.restype = sz
+        lib.rmsnorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32, i32, vp]
+        lib.rmsnorm_bwd.restype = i32
+        lib.rmsnorm_status_string.argtypes = [i32]
+        lib.rmsnorm_status_string.restype = ctypes.c_char_p
+        lib.rmsnorm_last_error.argtypes = []
+        lib.rmsnorm_last_error.restype = ctypes.c_char_p
+        lib.rmsnorm_tuning_set_geometry.argtypes = [i32, i32, i32, i32, i64]
+        lib.rmsnorm_tuning_set_geometry.restype = None
+        if path == LIB_PATH:
+            _lib = lib
+        return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise RMSNormError(status, lib.rmsnorm_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: RMSN_F32, torch.float16: RMSN_F16, torch.bfloat16: RMSN_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return m[t.dtype]
+
+
+def _rows(t, name):
+    """(M, H, row stride) of a tensor viewed as rows over its last dim."""
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have at least one dimension")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    H = t.shape[-1]
+    if t.numel() == 0:
+        return 0, H, max(H, 1)
+    if t.stride(-1) != 1 and H > 1:
+        raise ValueError(f"{name} must be contiguous along its last dimension")
+    if t.dim() == 1:
+        return 1, H, H
+    lead = t.shape[:-1]
+    # leading dims must collapse into one row stride
+    stride = t.stride(-2)
+    expect = stride
+    for d in range(t.dim() - 2, -1, -1):
+        if t.shape[d] != 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}'s leading dimensions cannot be viewed as rows with one stride")
+        expect *= t.shape[d]
+    M = 1
+    for s in lead:
+        M *= s
+    if M == 1:
+        stride = max(stride, H)
+    return M, H, stride
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def rmsnorm_fwd(x, weight=None, eps: float = 1e-6, out=None, rrms=None, return_rrms: bool = False):
+    """y = x * rsqrt(mean(x^2, -1) + eps) * weight over the last dim of x.
+
+    out (same shape and dtype as x, may be x itself) and rrms (float32, one
+    value per row) are optional preallocated outputs."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _, _, ys = _rows(out, "out")
+    if return_rrms and rrms is None:
+        rrms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if rrms is not None and (rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous()):
+        raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
+    wcode = _dtype_code(weight) if weight is not None else _dtype_code(x)
+    if weight is not None and (weight.numel() != H or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous tensor of H elements")
+    st = lib.rmsnorm_fwd(_ptr(x), xs, _ptr(weight), _ptr(out), ys, _ptr(rrms), M, H, float(eps), _dtype_code(x),
+                         wcode, _stream(x))
+    _check(lib, st)
+    return (out, rrms) if return_rrms else out
+
+
+def rmsnorm_fwd_residual(x, residual, weight=None, eps: float = 1e-6, out=None, residual_out=None, rrms=None,
+                         return_rrms: bool = False, write_residual: bool = True):
+    """h = x + residual (float32), residual_out = h in x's dtype, y = RMSNorm(h).
+
+    Returns (y, residual_out) (plus rrms when return_rrms).  residual_out may
+    be `residual` itself for an in-place update of the residual stream."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if residual.shape != x.shape or residual.dtype != x.dtype:
+        raise ValueError("residual must match x in shape and dtype")
+    _, _, rs = _rows(residual, "residual")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    _, _, ys = _rows(out, "out")
+    if write_residual and residual_out is None:
+        residual_out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    ros = 0
+    if residual_out is not None:
+        if residual_out.shape != x.shape or residual_out.dtype != x.dtype:
+            raise ValueError("residual_out must match x in shape and dtype")
+        _, _, ros = _rows(residual_out, "residual_out")
+    if return_rrms and rrms is None:
+        rrms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if rrms is not None and (rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous()):
+        raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
+    wcode = _dtype_code(weight) if weight is not None else _dtype_code(x)
+    if weight is not None and (weight.numel() != H or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous tensor of H elements")
+    st = lib.rmsnorm_fwd_residual(_ptr(x), xs, _ptr(residual), rs, _ptr(weight), _ptr(out), ys, _ptr(residual_out),
+                                  ros, _ptr(rrms), M, H, float(eps), _dtype_code(x), wcode, _stream(x))
+    _check(lib, st)
+    res = (out, residual_out)
+    return res + (rrms,) if return_rrms else res
+
+
+def rmsnorm_bwd_workspace_bytes(M: int, H: int) -> int:
+    return int(load_library().rmsnorm_bwd_workspace_bytes(M, H))
+
+
+def rmsnorm_bwd(dy, x, weight, rrms, dx=None, dw=None, workspace=None, want_dw: bool = True):
+    """Gradients of RMSNorm from the saved per-row rrms.
+
+    Returns (dx, dw); dw (float32, shape (H,)) is None for a weightless norm
+    or when want_dw is False.  dx may be dy or x itself."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    _, _, dys = _rows(dy, "dy")
+    if dx is None:
+        dx = torch.empty_like(x, memory_format=torch.contiguous_format)
+    _, _, dxs = _rows(dx, "dx")
+    if rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous():
+        raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
+    if weight is not None and (weight.numel() != H or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous tensor of H elements")
+    if weight is not None and want_dw and dw is None:
+        dw = torch.empty(H, dtype=torch.float32, device=x.device)
+    if weight is None:
+        dw = None
+    ws_bytes = 0
+    if dw is not None:
+        need = int(lib.rmsnorm_bwd_workspace_bytes(M, H))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    wcode = _dtype_code(weight) if weight is not None else _dtype_code(x)
+    st = lib.rmsnorm_bwd(_ptr(dy), dys, _ptr(x), xs, _ptr(weight), _ptr(rrms), _ptr(dx), dxs, _ptr(dw),
+                         _ptr(workspace), ws_bytes, M, H, _dtype_code(x), wcode, _stream(x))
+    _check(lib, st)
+    return dx, dw
+
+
+def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: int = 0) -> None:
+    """Development hook (include/rmsnorm_tuning.h): force the launch geometry
+    of the forward ("fwd") or backward ("bwd") kernels; vpt=0 restores the
+    library's own choice."""
+    code = {"fwd": 0, "bwd": 1}[which]
+    load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))

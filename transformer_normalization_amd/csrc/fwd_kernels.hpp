@@ -1,0 +1,213 @@
+// fwd_kernels.hpp -- gfx950 forward RMSNorm and fused residual pre-norm.
+//
+// What is computed ("Skill: Write a Triton RMSNorm Kernel", "Required
+// reasoning process" steps 1-11 and "Kernel design rules"):
+//   h      = x                     (plain form)
+//   h      = float32(x) + float32(r)  (fused residual; r_out = RNE(h))
+//   rrms   = rsqrt(sum(h*h) * (1/H) + eps)     in float32, eps inside the root
+//   y      = (h * rrms) * w                     (w = 1 when weightless)
+//
+// Layout of the work on the device:
+//   * A "row group" of 64*wpr threads (wpr whole waves) owns one row at a
+//     time; a workgroup holds rpw row groups.  Workgroups walk the rows
+//     grid-stride: row group `slot` of workgroup b takes rows
+//     (b + it*gridDim.x)*rpw + slot for it = 0 .. iters-1.  iters is the same
+//     for every thread, so the workgroup barriers inside row_sum are reached
+//     uniformly; rows past M are processed as zeros and never stored.
+//   * Thread t of a row group owns the VEC-element vectors t, t+64*wpr, ...,
+//     t+(VPT-1)*64*wpr of the row, so a wave's load is 64 consecutive 16-byte
+//     vectors (1 KiB) and the columns a thread owns never change between
+//     rows; the weight is loaded once into registers.
+//   * Resident path (the row fits: nvec <= 64*wpr*VPT): the row is loaded
+//     once, stays in registers through the reduction and is scaled and
+//     stored from registers -- one HBM read and one write per element
+//     ("Required reasoning process", step 3, the persistent pattern).
+//   * Two-pass path (longer rows): pass 1 sums squares chunk by chunk, pass 2
+//     reloads each chunk with the same bounds and scales it (step 11).
+//   * The reduction is a per-thread float32 sum over the thread's elements in
+//     column order, then a DPP wave sum and, for wpr > 1, a fixed-order sum
+//     of the wave totals through LDS.  The tree depends only on (H, VEC, VPT,
+//     wpr), never on strides, alignment of rows or timing.
+#pragma once
+
+#include "numerics.hpp"
+
+namespace rmsn {
+
+struct FwdParams {
+    const void *x;
+    const void *r;   // residual (fused form only)
+    const void *w;   // may be null (weightless)
+    void *y;
+    void *ro;        // residual_out, may be null
+    float *rrms;     // may be null
+    int64_t xs, rs, ys, ros;  // row strides, elements
+    int64_t M;
+    int64_t iters;   // row-group iterations per workgroup
+    int H;
+    int nvec;        // vectors of VEC elements per row
+    int wpr;         // waves per row group
+    int rpw;         // row groups per workgroup
+    int nchunks;     // two-pass: chunks of 64*wpr*VPT vectors
+    float eps;
+    float inv_h;     // float32(1/H)
+};
+
+template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, int MAXT>
+__global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
+    __shared__ float red[2][16];
+    const int row_threads = 64 * p.wpr;
+    const int slot = threadIdx.x / row_threads;
+    const int t = threadIdx.x - slot * row_threads;
+    const int wave_in_row = t >> 6;
+    const int64_t gstride = (int64_t)gridDim.x;
+
+    if constexpr (!TWO_PASS) {
+        // Loaded data stays packed in registers and is widened at each use
+        // (one VALU op per element), which halves the register footprint of
+        // 16-bit formats; every widening of an element gives the same float.
+        Raw<WDT, VEC> wr[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int v = t + k * row_threads;
+            if (p.w != nullptr && v < p.nvec)
+                wr[k].load(p.w, (int64_t)v * VEC);
+            else
+                wr[k].fill_one();
+        }
+
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
+            Raw<XDT, VEC> xr[VPT];
+            Raw<XDT, VEC> rr[RESID ? VPT : 1];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int v = t + k * row_threads;
+                if (valid && v < p.nvec) {
+                    xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
+                    if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
+                } else {
+                    xr[k].zero();
+                    if constexpr (RESID) rr[k].zero();
+                }
+            }
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                float hv[VEC];
+                xr[k].widen_to(hv);
+                if constexpr (RESID) {
+                    float rv[VEC];
+                    rr[k].widen_to(rv);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                    const int v = t + k * row_threads;
+                    if (p.ro != nullptr && valid && v < p.nvec)
+                        store_elems<XDT, VEC>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                }
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(hv[e], hv[e], acc);
+            }
+            const float ss = row_sum(acc, p.wpr, wave_in_row, &red[it & 1][slot * p.wpr]);
+            const float rs = fast_rsqrt(ss * p.inv_h + p.eps);
+            if (p.rrms != nullptr && valid && t == 0) p.rrms[row] = rs;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                xr[k].opaque();
+                if constexpr (RESID) rr[k].opaque();
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int v = t + k * row_threads;
+                if (valid && v < p.nvec) {
+                    float hv[VEC], wv[VEC], o[VEC];
+                    xr[k].widen_to(hv);
+                    if constexpr (RESID) {
+                        float rv[VEC];
+                        rr[k].widen_to(rv);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                    }
+                    wr[k].widen_to(wv);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                    store_elems<XDT, VEC>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                }
+            }
+        }
+    } else {
+        const int chunk = row_threads * VPT;
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
+            // pass 1: sum of squares, chunk by chunk
+            float acc = 0.0f;
+            for (int c = 0; c < p.nchunks; ++c) {
+                Raw<XDT, VEC> xr[VPT];
+                Raw<XDT, VEC> rr[RESID ? VPT : 1];
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (valid && v < p.nvec) {
+                        xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
+                        if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
+                    } else {
+                        xr[k].zero();
+                        if constexpr (RESID) rr[k].zero();
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    float hv[VEC];
+                    xr[k].widen_to(hv);
+                    if constexpr (RESID) {
+                        float rv[VEC];
+                        rr[k].widen_to(rv);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(hv[e], hv[e], acc);
+                }
+            }
+            const float ss = row_sum(acc, p.wpr, wave_in_row, &red[it & 1][slot * p.wpr]);
+            const float rs = fast_rsqrt(ss * p.inv_h + p.eps);
+            if (p.rrms != nullptr && valid && t == 0) p.rrms[row] = rs;
+            // pass 2: reload each chunk with the same bounds, scale, store.
+            // Every element is read and then written by the same thread, so an
+            // output that is the same buffer as an input is safe.
+            for (int c = 0; c < p.nchunks; ++c) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (valid && v < p.nvec) {
+                        float hv[VEC], wv[VEC];
+                        load_elems<XDT, VEC>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                        if constexpr (RESID) {
+                            float rv[VEC];
+                            load_elems<XDT, VEC>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                        }
+                        if (p.w != nullptr) {
+                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
+                        }
+                        if constexpr (RESID) {
+                            if (p.ro != nullptr) store_elems<XDT, VEC>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                        }
+                        float o[VEC];
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                        store_elems<XDT, VEC>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace rmsn

@@ -1,0 +1,675 @@
+// rmsnorm_api.hip -- host side of the gfx950 RMSNorm library: argument
+// validation, launch geometry and the extern "C" entry points declared in
+// include/rmsnorm.h.
+//
+// Nothing here allocates, frees or synchronises.  Argument errors are found
+// before the first HIP call.  The only HIP calls are hipGetDevice,
+// hipDeviceGetAttribute / hipGetDeviceProperties (once per device, cached)
+// and hipLaunchKernel.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "bwd_kernels.hpp"
+#include "fwd_kernels.hpp"
+#include "rmsnorm.h"
+#include "rmsnorm_tuning.h"
+
+namespace {
+
+using namespace rmsn;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+
+thread_local char g_last_error[512] = "";
+
+rmsn_status_t fail(rmsn_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rmsn_status_t ok() {
+    g_last_error[0] = '\0';
+    return RMSN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// device facts (read once per device; a failed read is an error, never a guess)
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    std::once_flag once;
+    rmsn_status_t status = RMSN_ERR_HIP;
+    int cus = 0;
+    char detail[256] = "";
+};
+
+DeviceInfo g_devices[kMaxDevices];
+
+rmsn_status_t device_info(int *cus) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RMSN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(RMSN_ERR_HIP, "device index %d out of range", dev);
+    DeviceInfo &d = g_devices[dev];
+    std::call_once(d.once, [&d, dev]() {
+        int n = 0;
+        hipError_t err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess || n <= 0) {
+            snprintf(d.detail, sizeof d.detail, "reading the compute-unit count of device %d failed: %s", dev,
+                     hipGetErrorString(err));
+            d.status = RMSN_ERR_HIP;
+            return;
+        }
+        hipDeviceProp_t prop;
+        err = hipGetDeviceProperties(&prop, dev);
+        if (err != hipSuccess) {
+            snprintf(d.detail, sizeof d.detail, "reading the properties of device %d failed: %s", dev,
+                     hipGetErrorString(err));
+            d.status = RMSN_ERR_HIP;
+            return;
+        }
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            snprintf(d.detail, sizeof d.detail, "device %d is %s; this library is built for gfx950 only", dev,
+                     prop.gcnArchName);
+            d.status = RMSN_ERR_UNSUPPORTED;
+            return;
+        }
+        d.cus = n;
+        d.status = RMSN_OK;
+    });
+    if (d.status != RMSN_OK) return fail(d.status, "%s", d.detail);
+    *cus = d.cus;
+    return RMSN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks
+// ---------------------------------------------------------------------------
+
+int dtype_bytes(rmsn_dtype_t t) { return t == RMSN_F32 ? 4 : 2; }
+bool dtype_valid(int t) { return t == RMSN_F32 || t == RMSN_F16 || t == RMSN_BF16; }
+
+constexpr int64_t kMaxH = int64_t(1) << 30;
+
+// A buffer as a byte range [lo, hi) plus what identifies "the same buffer".
+struct Region {
+    const char *name;
+    uintptr_t base;
+    int64_t stride;  // elements, 0 for vectors
+    int64_t rows;
+    int64_t cols;
+    int ebytes;
+    bool present;
+    uintptr_t lo() const { return base; }
+    uintptr_t hi() const { return base + (uintptr_t)(((rows - 1) * stride + cols) * ebytes); }
+    bool overlaps(const Region &o) const { return lo() < o.hi() && o.lo() < hi(); }
+    bool same(const Region &o) const {
+        return base == o.base && stride == o.stride && rows == o.rows && cols == o.cols && ebytes == o.ebytes;
+    }
+};
+
+Region mat(const char *name, const void *p, int64_t stride, int64_t M, int64_t H, int eb) {
+    return Region{name, (uintptr_t)p, stride, M, H, eb, p != nullptr};
+}
+Region vec(const char *name, const void *p, int64_t n, int eb) {
+    return Region{name, (uintptr_t)p, 0, 1, n, eb, p != nullptr};
+}
+
+// outputs must not overlap each other; an output may overlap an input only
+// by being exactly the same buffer
+rmsn_status_t check_overlap(const Region *outs, int nout, const Region *ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        if (!outs[i].present) continue;
+        for (int j = i + 1; j < nout; ++j)
+            if (outs[j].present && outs[i].overlaps(outs[j]))
+                return fail(RMSN_ERR_INVALID_ARG, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+        for (int j = 0; j < nin; ++j)
+            if (ins[j].present && outs[i].overlaps(ins[j]) && !outs[i].same(ins[j]))
+                return fail(RMSN_ERR_INVALID_ARG, "output %s partially overlaps input %s", outs[i].name,
+                            ins[j].name);
+    }
+    return RMSN_OK;
+}
+
+rmsn_status_t check_common(int64_t M, int64_t H, rmsn_dtype_t xdt, const void *w, rmsn_dtype_t wdt) {
+    if (!dtype_valid(xdt)) return fail(RMSN_ERR_UNSUPPORTED, "x_dtype %d is not RMSN_F32/F16/BF16", (int)xdt);
+    if (w != nullptr && !(wdt == xdt || wdt == RMSN_F32))
+        return fail(RMSN_ERR_UNSUPPORTED, "w_dtype %d must equal x_dtype %d or be RMSN_F32", (int)wdt, (int)xdt);
+    if (M < 0) return fail(RMSN_ERR_INVALID_ARG, "M = %lld is negative", (long long)M);
+    if (H < 1) return fail(RMSN_ERR_INVALID_ARG, "H = %lld must be >= 1", (long long)H);
+    if (H > kMaxH) return fail(RMSN_ERR_UNSUPPORTED, "H = %lld exceeds 2^30", (long long)H);
+    return RMSN_OK;
+}
+
+rmsn_status_t check_stride(const char *name, int64_t stride, int64_t M, int64_t H, int eb) {
+    if (stride < H) return fail(RMSN_ERR_INVALID_ARG, "%s = %lld is smaller than H = %lld", name, (long long)stride,
+                                (long long)H);
+    // the last byte of the matrix must be addressable without overflow
+    if (M > 1 && (stride > (INT64_MAX / eb) / (M - 1)))
+        return fail(RMSN_ERR_INVALID_ARG, "%s * M overflows", name);
+    return RMSN_OK;
+}
+
+rmsn_status_t check_eps(float eps) {
+    if (!(eps > 0.0f) || !std::isfinite(eps))
+        return fail(RMSN_ERR_INVALID_ARG, "eps = %g must be positive and finite", (double)eps);
+    return RMSN_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// geometry
+// ---------------------------------------------------------------------------
+
+// Launch-geometry override for tuning and for tests that must reach the
+// grid-stride and two-pass paths at small sizes.  Set through
+// rmsnorm_tuning_set_geometry() (include/rmsnorm_tuning.h) or, once per
+// process at first use, from the environment:
+//   RMSN_FWD_GEOM="vpt,wpr,rpw,grid"   (grid 0 = one workgroup per row group)
+//   RMSN_BWD_GEOM="vpt,wpr,P"
+struct Override {
+    bool set = false;
+    int a = 0, b = 0, c = 0;
+    int64_t d = 0;
+};
+
+std::mutex g_override_mu;
+Override g_override[2];
+std::atomic<bool> g_override_any{false};
+std::once_flag g_override_env_once;
+
+Override parse_override(const char *var) {
+    Override o;
+    const char *s = getenv(var);
+    if (s == nullptr || *s == '\0') return o;
+    long long v[4] = {0, 0, 0, 0};
+    int n = sscanf(s, "%lld,%lld,%lld,%lld", &v[0], &v[1], &v[2], &v[3]);
+    if (n >= 2) {
+        o.set = true;
+        o.a = (int)v[0];
+        o.b = (int)v[1];
+        o.c = (int)v[2];
+        o.d = v[3];
+    }
+    return o;
+}
+
+Override get_override(int which) {
+    std::call_once(g_override_env_once, []() {
+        std::lock_guard<std::mutex> lk(g_override_mu);
+        g_override[0] = parse_override("RMSN_FWD_GEOM");
+        g_override[1] = parse_override("RMSN_BWD_GEOM");
+        g_override_any.store(g_override[0].set || g_override[1].set);
+    });
+    if (!g_override_any.load(std::memory_order_relaxed)) return Override{};
+    std::lock_guard<std::mutex> lk(g_override_mu);
+    return g_override[which];
+}
+
+// vectors per thread available as kernel instantiations
+enum class Kind { Fwd, FwdResid, Bwd };
+constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
+constexpr int kBwdVecVpt[] = {1, 2, 3, 4, 6};
+constexpr int kScalarVpt[] = {1, 2, 4, 8};
+// largest workgroup each register tile may use (the kernels' launch bounds)
+int max_threads_for(Kind kind, int vpt, int vec) {
+    return kind == Kind::Bwd ? bwd_max_threads(vpt * vec) : fwd_max_threads(vpt * vec, kind == Kind::FwdResid);
+}
+
+struct Geom {
+    int vec;      // elements per access (16 bytes / element, or 1)
+    int vpt;      // accesses per thread per chunk
+    int wpr;      // waves per row group
+    int rpw;      // row groups per workgroup
+    int nvec;     // accesses per row
+    int nchunks;  // 1 = resident
+    bool two_pass;
+};
+
+// Pick (vpt, wpr) so that 64*wpr*vpt covers nvec with the least idle slots,
+// preferring `pref` elements per thread; rows longer than the largest tile
+// use two passes.
+Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
+    Geom g{};
+    g.vec = vec;
+    g.nvec = (H + vec - 1) / vec;
+    const int *set = vec == 1 ? kScalarVpt : kind == Kind::Bwd ? kBwdVecVpt : kFwdVecVpt;
+    const int nset = vec == 1 ? 4 : kind == Kind::Bwd ? 5 : 6;
+    double best = 1e30;
+    for (int i = 0; i < nset; ++i) {
+        const int vpt = set[i];
+        const int maxw = max_threads_for(kind, vpt, vec) / 64;
+        const int wpr = (g.nvec + 64 * vpt - 1) / (64 * vpt);
+        if (wpr > maxw) continue;
+        const double slots = 64.0 * wpr * vpt;
+        const double idle = (slots - g.nvec) / slots;
+        const double pref = std::fabs(std::log2((double)(vpt * vec) / pref_elems));
+        const double cost = 8.0 * idle + pref;
+        if (cost < best) {
+            best = cost;
+            g.vpt = vpt;
+            g.wpr = wpr;
+        }
+    }
+    if (best < 1e30) {
+        g.nchunks = 1;
+        g.two_pass = false;
+    } else {
+        g.vpt = vec > 1 ? 4 : 8;
+        g.wpr = 16;
+        const int chunk = 64 * g.wpr * g.vpt;
+        g.nchunks = (g.nvec + chunk - 1) / chunk;
+        g.two_pass = true;
+    }
+    g.rpw = 1;
+    while (g.rpw * g.wpr < 4 && 64 * g.wpr * g.rpw * 2 <= max_threads_for(kind, g.vpt, g.vec)) g.rpw *= 2;
+    return g;
+}
+
+// ---------------------------------------------------------------------------
+// kernel tables
+// ---------------------------------------------------------------------------
+
+typedef void (*fwd_fn)(const FwdParams);
+typedef void (*bwd_fn)(const BwdParams);
+
+template <int XDT, int WDT, int VEC, bool RESID>
+fwd_fn fwd_kernel_for(int vpt, bool two_pass) {
+    if (two_pass) {
+        constexpr int V = VEC > 1 ? 4 : 8;
+        return rmsnorm_fwd_kernel<XDT, WDT, VEC, V, RESID, true, 1024>;
+    }
+    switch (vpt) {
+    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, RESID, false, fwd_max_threads(1 * VEC, RESID)>;
+    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, RESID, false, fwd_max_threads(2 * VEC, RESID)>;
+    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, RESID, false, fwd_max_threads(4 * VEC, RESID)>;
+    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, RESID, false, fwd_max_threads(8 * VEC, RESID)>;
+    default: break;
+    }
+    if constexpr (VEC > 1) {
+        switch (vpt) {
+        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, RESID, false, fwd_max_threads(3 * VEC, RESID)>;
+        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, RESID, false, fwd_max_threads(6 * VEC, RESID)>;
+        default: break;
+        }
+    }
+    return nullptr;
+}
+
+template <int XDT, int WDT, bool RESID>
+fwd_fn fwd_kernel_vec(int vec, int vpt, bool two_pass) {
+    constexpr int V = 16 / Fmt<XDT>::bytes;
+    return vec == 1 ? fwd_kernel_for<XDT, WDT, 1, RESID>(vpt, two_pass)
+                    : fwd_kernel_for<XDT, WDT, V, RESID>(vpt, two_pass);
+}
+
+template <bool RESID>
+fwd_fn fwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
+    const bool wf32 = (wdt == RMSN_F32);
+    switch (xdt) {
+    case RMSN_F32: return fwd_kernel_vec<DT_F32, DT_F32, RESID>(vec, vpt, two_pass);
+    case RMSN_F16:
+        return wf32 ? fwd_kernel_vec<DT_F16, DT_F32, RESID>(vec, vpt, two_pass)
+                    : fwd_kernel_vec<DT_F16, DT_F16, RESID>(vec, vpt, two_pass);
+    case RMSN_BF16:
+        return wf32 ? fwd_kernel_vec<DT_BF16, DT_F32, RESID>(vec, vpt, two_pass)
+                    : fwd_kernel_vec<DT_BF16, DT_BF16, RESID>(vec, vpt, two_pass);
+    }
+    return nullptr;
+}
+
+template <int XDT, int WDT, int VEC>
+bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
+    if (two_pass) {
+        constexpr int V = VEC > 1 ? 4 : 8;
+        return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, true, 1024>;
+    }
+    switch (vpt) {
+    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, false, bwd_max_threads(1 * VEC)>;
+    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, false, bwd_max_threads(2 * VEC)>;
+    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, false, bwd_max_threads(4 * VEC)>;
+    default: break;
+    }
+    if constexpr (VEC == 1) {
+        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, false, bwd_max_threads(8 * VEC)>;
+    }
+    if constexpr (VEC > 1) {
+        switch (vpt) {
+        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, bwd_max_threads(3 * VEC)>;
+        case 6: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 6, false, bwd_max_threads(6 * VEC)>;
+        default: break;
+        }
+    }
+    return nullptr;
+}
+
+template <int XDT, int WDT>
+bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass) {
+    constexpr int V = 16 / Fmt<XDT>::bytes;
+    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1>(vpt, two_pass) : bwd_kernel_for<XDT, WDT, V>(vpt, two_pass);
+}
+
+bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
+    const bool wf32 = (wdt == RMSN_F32);
+    switch (xdt) {
+    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32>(vec, vpt, two_pass);
+    case RMSN_F16:
+        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32>(vec, vpt, two_pass) : bwd_kernel_vec<DT_F16, DT_F16>(vec, vpt, two_pass);
+    case RMSN_BF16:
+        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32>(vec, vpt, two_pass)
+                    : bwd_kernel_vec<DT_BF16, DT_BF16>(vec, vpt, two_pass);
+    }
+    return nullptr;
+}
+
+rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what) {
+    hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+    if (e != hipSuccess) return fail(RMSN_ERR_HIP, "launching %s failed: %s", what, hipGetErrorString(e));
+    return RMSN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward (plain and fused residual)
+// ---------------------------------------------------------------------------
+
+rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int64_t rs, const void *w, void *y,
+                       int64_t ys, void *ro, int64_t ros, float *rrms, int64_t M, int64_t H, float eps,
+                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
+    rmsn_status_t st = check_common(M, H, xdt, w, wdt);
+    if (st != RMSN_OK) return st;
+    if ((st = check_eps(eps)) != RMSN_OK) return st;
+    const int eb = dtype_bytes(xdt);
+    if ((st = check_stride("x_stride", xs, M, H, eb)) != RMSN_OK) return st;
+    if ((st = check_stride("y_stride", ys, M, H, eb)) != RMSN_OK) return st;
+    if (resid) {
+        if ((st = check_stride("r_stride", rs, M, H, eb)) != RMSN_OK) return st;
+        if (ro != nullptr && (st = check_stride("ro_stride", ros, M, H, eb)) != RMSN_OK) return st;
+    }
+    if (M == 0) return RMSN_OK;
+    if (x == nullptr) return fail(RMSN_ERR_INVALID_ARG, "x is NULL");
+    if (y == nullptr) return fail(RMSN_ERR_INVALID_ARG, "y is NULL");
+    if (resid && r == nullptr) return fail(RMSN_ERR_INVALID_ARG, "residual is NULL");
+
+    const int wb = w ? dtype_bytes(wdt) : 0;
+    Region ins[3] = {mat("x", x, xs, M, H, eb), mat("residual", resid ? r : nullptr, rs, M, H, eb),
+                     vec("w", w, H, wb ? wb : 1)};
+    Region outs[3] = {mat("y", y, ys, M, H, eb), mat("residual_out", resid ? ro : nullptr, ros, M, H, eb),
+                      vec("rrms", rrms, M, 4)};
+    // rrms and w must not be "the same buffer" as a matrix: compare ranges only
+    if ((st = check_overlap(outs, 3, ins, 3)) != RMSN_OK) return st;
+    if (rrms != nullptr) {
+        for (const Region &in : ins)
+            if (in.present && outs[2].overlaps(in))
+                return fail(RMSN_ERR_INVALID_ARG, "rrms overlaps input %s", in.name);
+    }
+
+    // vector path: every row start 16-byte aligned and H a whole number of vectors
+    const int vecw = 16 / eb;
+    bool vec_ok = (H % vecw) == 0 && aligned16(x) && aligned16(y) && (xs * eb) % 16 == 0 && (ys * eb) % 16 == 0 &&
+                  (w == nullptr || aligned16(w));
+    if (resid)
+        vec_ok = vec_ok && aligned16(r) && (rs * eb) % 16 == 0 &&
+                 (ro == nullptr || (aligned16(ro) && (ros * eb) % 16 == 0));
+
+    const Kind kind = resid ? Kind::FwdResid : Kind::Fwd;
+    Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
+    int64_t grid = (M + g.rpw - 1) / g.rpw;
+    const Override ov = get_override(0);
+    if (ov.set) {
+        Geom o = g;
+        o.vpt = ov.a;
+        o.wpr = ov.b;
+        o.rpw = ov.c > 0 ? ov.c : 1;
+        const int maxt = max_threads_for(kind, o.vpt, o.vec);
+        if (o.vpt < 1 || o.wpr < 1 || o.wpr * o.rpw * 64 > maxt || o.wpr * o.rpw > 16)
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: bad tile vpt %d wpr %d rpw %d (max %d threads)",
+                        o.vpt, o.wpr, o.rpw, maxt);
+        const int chunk = 64 * o.wpr * o.vpt;
+        o.nchunks = (o.nvec + chunk - 1) / chunk;
+        o.two_pass = o.nchunks > 1;
+        if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+        g = o;
+        grid = (M + g.rpw - 1) / g.rpw;
+        if (ov.d > 0 && ov.d < grid) grid = ov.d;
+    }
+    const int64_t groups = (M + g.rpw - 1) / g.rpw;
+    if (grid > INT32_MAX) grid = INT32_MAX;
+    const int64_t iters = (groups + grid - 1) / grid;
+
+    fwd_fn fn = resid ? fwd_lookup<true>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass)
+                      : fwd_lookup<false>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass);
+    if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
+    int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
+    if ((st = device_info(&cus)) != RMSN_OK) return st;
+
+    FwdParams p;
+    p.x = x;
+    p.r = r;
+    p.w = w;
+    p.y = y;
+    p.ro = ro;
+    p.rrms = rrms;
+    p.xs = xs;
+    p.rs = rs;
+    p.ys = ys;
+    p.ros = ros;
+    p.M = M;
+    p.iters = iters;
+    p.H = (int)H;
+    p.nvec = g.nvec;
+    p.wpr = g.wpr;
+    p.rpw = g.rpw;
+    p.nchunks = g.nchunks;
+    p.eps = eps;
+    p.inv_h = (float)(1.0 / (double)H);
+    void *args[] = {&p};
+    return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
+                  resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd");
+}
+
+constexpr int64_t kMaxPartials = 1024;
+
+size_t bwd_workspace(int64_t M, int64_t H) {
+    if (M <= 0 || H <= 0 || H > kMaxH) return 0;
+    const int64_t P = M < kMaxPartials ? M : kMaxPartials;
+    return (size_t)P * (size_t)H * sizeof(float);
+}
+
+rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, const void *w, const float *rrms,
+                       void *dx, int64_t dxs, float *dw, void *ws, size_t ws_bytes, int64_t M, int64_t H,
+                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
+    rmsn_status_t st = check_common(M, H, xdt, w, wdt);
+    if (st != RMSN_OK) return st;
+    const int eb = dtype_bytes(xdt);
+    if ((st = check_stride("dy_stride", dys, M, H, eb)) != RMSN_OK) return st;
+    if ((st = check_stride("x_stride", xs, M, H, eb)) != RMSN_OK) return st;
+    if ((st = check_stride("dx_stride", dxs, M, H, eb)) != RMSN_OK) return st;
+    if (dw != nullptr && w == nullptr)
+        return fail(RMSN_ERR_INVALID_ARG, "dw requested for a weightless norm (w is NULL)");
+    if (M > 0) {
+        if (dy == nullptr) return fail(RMSN_ERR_INVALID_ARG, "dy is NULL");
+        if (x == nullptr) return fail(RMSN_ERR_INVALID_ARG, "x is NULL");
+        if (rrms == nullptr) return fail(RMSN_ERR_INVALID_ARG, "rrms is NULL");
+        if (dx == nullptr) return fail(RMSN_ERR_INVALID_ARG, "dx is NULL");
+    }
+    const size_t need = bwd_workspace(M, H);
+    if (dw != nullptr && M > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(RMSN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0,
+                        need);
+        if (!aligned16(ws)) return fail(RMSN_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    }
+    const int wb = w ? dtype_bytes(wdt) : 1;
+    if (M > 0) {
+        Region ins[4] = {mat("dy", dy, dys, M, H, eb), mat("x", x, xs, M, H, eb), vec("w", w, H, wb),
+                         vec("rrms", rrms, M, 4)};
+        Region outs[3] = {mat("dx", dx, dxs, M, H, eb), vec("dw", dw, H, 4),
+                          vec("workspace", dw ? ws : nullptr, (int64_t)need, 1)};
+        if ((st = check_overlap(outs, 3, ins, 4)) != RMSN_OK) return st;
+        for (int i = 1; i < 3; ++i)
+            for (const Region &in : ins)
+                if (outs[i].present && in.present && outs[i].overlaps(in))
+                    return fail(RMSN_ERR_INVALID_ARG, "%s overlaps input %s", outs[i].name, in.name);
+        // dx may be the same buffer as dy or x, but never w or rrms
+        if (outs[0].overlaps(ins[2]) && ins[2].present) return fail(RMSN_ERR_INVALID_ARG, "dx overlaps w");
+        if (outs[0].overlaps(ins[3])) return fail(RMSN_ERR_INVALID_ARG, "dx overlaps rrms");
+    } else if (dw == nullptr) {
+        return RMSN_OK;
+    }
+
+    if (M == 0) {  // dw of zero rows is zero
+        int cus = 0;
+        if ((st = device_info(&cus)) != RMSN_OK) return st;
+        const float *none = nullptr;
+        int P = 0, Hi = (int)H;
+        void *args[] = {(void *)&none, &P, &Hi, &dw};
+        return launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + 63) / 64)), dim3(1024), args,
+                      stream, "rmsnorm_dw_finalize");
+    }
+
+    const int vecw = 16 / eb;
+    const bool vec_ok = (H % vecw) == 0 && aligned16(dy) && aligned16(x) && aligned16(dx) &&
+                        (dys * eb) % 16 == 0 && (xs * eb) % 16 == 0 && (dxs * eb) % 16 == 0 &&
+                        (w == nullptr || aligned16(w));
+    Geom g = pick_row_geom(Kind::Bwd, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 24);
+    int64_t P = 0;  // 0: chosen from the device below
+    const Override ov = get_override(1);
+    if (ov.set) {
+        Geom o = g;
+        o.vpt = ov.a;
+        o.wpr = ov.b;
+        const int maxt = max_threads_for(Kind::Bwd, o.vpt, o.vec);
+        if (o.vpt < 1 || o.wpr < 1 || o.wpr * 64 > maxt)
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: bad tile vpt %d wpr %d", o.vpt, o.wpr);
+        const int chunk = 64 * o.wpr * o.vpt;
+        o.nchunks = (o.nvec + chunk - 1) / chunk;
+        o.two_pass = o.nchunks > 1;
+        if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+        g = o;
+        if (ov.c > 0) P = ov.c;
+    }
+    bwd_fn fn = bwd_lookup(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass);
+    if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
+    int cus = 0;
+    if ((st = device_info(&cus)) != RMSN_OK) return st;
+    if (P <= 0) P = 2 * (int64_t)cus;
+    if (P > kMaxPartials) P = kMaxPartials;
+    if (P > M) P = M;
+    const int64_t rows_per = (M + P - 1) / P;
+    P = (M + rows_per - 1) / rows_per;
+
+    BwdParams p;
+    p.dy = dy;
+    p.x = x;
+    p.w = w;
+    p.rrms = rrms;
+    p.dx = dx;
+    p.partial = dw != nullptr ? static_cast<float *>(ws) : nullptr;
+    p.dys = dys;
+    p.xs = xs;
+    p.dxs = dxs;
+    p.M = M;
+    p.rows_per_wg = rows_per;
+    p.H = (int)H;
+    p.nvec = g.nvec;
+    p.wpr = g.wpr;
+    p.nchunks = g.nchunks;
+    p.inv_h = (float)(1.0 / (double)H);
+    void *args[] = {&p};
+    if ((st = launch((const void *)fn, dim3((unsigned)P), dim3(64 * g.wpr), args, stream, "rmsnorm_bwd")) != RMSN_OK)
+        return st;
+    if (dw != nullptr) {
+        const float *part = p.partial;
+        int Pi = (int)P, Hi = (int)H;
+        void *fargs[] = {(void *)&part, &Pi, &Hi, &dw};
+        if ((st = launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + 63) / 64)), dim3(1024), fargs,
+                         stream, "rmsnorm_dw_finalize")) != RMSN_OK)
+            return st;
+    }
+    return RMSN_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+#define RMSN_API __attribute__((visibility("default")))
+
+extern "C" {
+
+RMSN_API rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *w, void *y, int64_t y_stride, float *rrms,
+                          int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
+                          hipStream_t stream) {
+    rmsn_status_t s = fwd_impl(false, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
+                               x_dtype, w_dtype, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, const void *residual, int64_t r_stride,
+                                   const void *w, void *y, int64_t y_stride, void *residual_out,
+                                   int64_t ro_stride, float *rrms, int64_t M, int64_t H, float eps,
+                                   rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream) {
+    rmsn_status_t s = fwd_impl(true, x, x_stride, residual, r_stride, w, y, y_stride, residual_out, ro_stride,
+                               rrms, M, H, eps, x_dtype, w_dtype, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t H) { return bwd_workspace(M, H); }
+
+RMSN_API rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void *x, int64_t x_stride, const void *w,
+                          const float *rrms, void *dx, int64_t dx_stride, float *dw, void *workspace,
+                          size_t workspace_bytes, int64_t M, int64_t H, rmsn_dtype_t x_dtype,
+                          rmsn_dtype_t w_dtype, hipStream_t stream) {
+    rmsn_status_t s = bwd_impl(dy, dy_stride, x, x_stride, w, rrms, dx, dx_stride, dw, workspace, workspace_bytes,
+                               M, H, x_dtype, w_dtype, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API const char *rmsnorm_status_string(rmsn_status_t s) {
+    switch (s) {
+    case RMSN_OK: return "RMSN_OK";
+    case RMSN_ERR_INVALID_ARG: return "RMSN_ERR_INVALID_ARG";
+    case RMSN_ERR_UNSUPPORTED: return "RMSN_ERR_UNSUPPORTED";
+    case RMSN_ERR_WORKSPACE: return "RMSN_ERR_WORKSPACE";
+    case RMSN_ERR_HIP: return "RMSN_ERR_HIP";
+    }
+    return "RMSN_UNKNOWN_STATUS";
+}
+
+RMSN_API const char *rmsnorm_last_error(void) { return g_last_error; }
+
+RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid) {
+    get_override(0);  // the environment is read first, so a later call wins
+    std::lock_guard<std::mutex> lk(g_override_mu);
+    if (which < 0 || which > 1) return;
+    Override o;
+    o.set = vpt > 0 && wpr > 0;
+    o.a = vpt;
+    o.b = wpr;
+    o.c = third;
+    o.d = grid;
+    g_override[which] = o;
+    g_override_any.store(g_override[0].set || g_override[1].set);
+}
+
+}  // extern "C"

@@ -33,6 +33,14 @@ extern "C" {
  */
 void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid);
 
+/*
+ * Streaming accesses: the (M, H) inputs and outputs can be read and written
+ * with non-temporal hints, which keep them out of the caches.  mode < 0 (the
+ * default) streams when a call moves at least 64 MiB of such data, 0 never,
+ * > 0 always.  Results are identical either way.
+ */
+void rmsnorm_tuning_set_streaming(int mode);
+
 #ifdef __cplusplus
 }
 #endif

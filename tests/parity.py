@@ -9,6 +9,10 @@
     rrms*g and xn*rrms*c/H nearly cancel may instead be within one ulp taken
     at 2^-10 * (|rrms*g| + |xn*rrms*c/H|): no float32 evaluation can do better
     on such elements.  The number of elements judged by that floor is reported.
+  * dx (float32): |got - ref| <= 1e-5*max(|ref|, 2^-4 * terms) + 1e-6, with
+    terms = |rrms*g| + |xn*rrms*c/H|.  Evaluating the difference of two terms
+    of size T in float32 costs about 4 * 2^-24 * T; 1e-5 * 2^-4 * T is ten
+    times that.  (Rows with H = 1 cancel to dx = rrms*g*eps/(x^2+eps).)
   * dw: |got - ref| <= 1e-3*|ref| + 1e-5 * sum_i |dy*xn| for each column (a
     pure relative bound is ill-posed for columns whose sum crosses zero).
 """
@@ -99,7 +103,7 @@ def check_dx_f32(report, got, ref64, terms, offset=0):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref64)
     strict = err <= 1e-5 * np.abs(ref64) + 1e-6
-    relaxed = err <= 1e-5 * np.maximum(np.abs(ref64), 2.0 ** -10 * terms) + 1e-6
+    relaxed = err <= 1e-5 * np.maximum(np.abs(ref64), 2.0 ** -4 * terms) + 1e-6
     report.n += got.size
     report.floor_used += int(np.count_nonzero(~strict & relaxed))
     report.merge_bad(~relaxed, offset)

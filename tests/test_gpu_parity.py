@@ -32,9 +32,11 @@ import transformer_normalization_amd as tn  # noqa: E402
 def _default_geometry():
     tn.set_geometry("fwd")
     tn.set_geometry("bwd")
+    tn.set_streaming(-1)
     yield
     tn.set_geometry("fwd")
     tn.set_geometry("bwd")
+    tn.set_streaming(-1)
 
 
 def run_fwd(x, w, eps, dtype, wdtype=None):
@@ -208,11 +210,13 @@ FWD_GEOMS = [
 ]
 
 
+@pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
 @pytest.mark.parametrize("geom", FWD_GEOMS, ids=[str(g) for g in FWD_GEOMS])
-def test_forced_fwd_geometry(geom):
+def test_forced_fwd_geometry(geom, stream):
     M, H = 300, 4096
     d = G.inputs(55, M, H, "bf16", residual=True)
     tn.set_geometry("fwd", *geom)
+    tn.set_streaming(stream)
     y, rr = run_fwd(d["x"], d["w"], 1e-5, "bf16")
     reps = list(G.fwd_vs_oracle(d["x"], d["w"], y, rr, 1e-5, "bf16", name=f"fwd {geom}"))
     y2, ro, rr2 = run_residual(d["x"], d["r"], d["w"], 1e-5, "bf16")
@@ -223,12 +227,14 @@ def test_forced_fwd_geometry(geom):
 BWD_GEOMS = [(1, 8, 0), (2, 4, 0), (4, 2, 0), (2, 4, 1), (2, 4, 7), (2, 4, 300), (4, 1, 16), (4, 2, 3)]
 
 
+@pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
 @pytest.mark.parametrize("geom", BWD_GEOMS, ids=[str(g) for g in BWD_GEOMS])
-def test_forced_bwd_geometry(geom):
+def test_forced_bwd_geometry(geom, stream):
     M, H = 300, 4096
     d = G.inputs(56, M, H, "bf16", dy=True)
     r32 = oracle_rrms32(d["x"], d["w"], 1e-6, "bf16")
     tn.set_geometry("bwd", geom[0], geom[1], geom[2])
+    tn.set_streaming(stream)
     dx, dw = run_bwd(d["dy"], d["x"], d["w"], r32, "bf16")
     G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, dx, dw, "bf16", name=f"bwd {geom}"))
 
@@ -261,8 +267,10 @@ def test_aligned_padding_is_bit_identical():
     assert torch.count_nonzero(out_wide[:, H:].view(torch.int16)) == 0
 
 
+@pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_misaligned_rows_use_single_elements(dtype):
+def test_misaligned_rows_use_single_elements(dtype, stream):
+    tn.set_streaming(stream)
     M, H = 33, 4096
     d = G.inputs(62, M, H, dtype, residual=True, dy=True)
     for pad, offset in ((1, 0), (0, 1), (3, 1)):
@@ -359,6 +367,21 @@ def test_guard_regions_untouched():
 # ---------------------------------------------------------------------------
 # determinism and exact invariants
 # ---------------------------------------------------------------------------
+
+def test_streaming_does_not_change_bits():
+    d = synthetic.make_inputs("bwd_bf16_8192x6144", rows=2048)
+    xd, dyd, wd = G.to_dev(d["x"], "bf16"), G.to_dev(d["dy"], "bf16"), G.to_dev(d["w"], "bf16")
+    outs = []
+    for mode in (0, 1):
+        tn.set_streaming(mode)
+        y, rr = tn.rmsnorm_fwd(xd, wd, 1e-6, return_rrms=True)
+        y2, ro = tn.rmsnorm_fwd_residual(xd, dyd, wd, 1e-6)
+        dx, dw = tn.rmsnorm_bwd(dyd, xd, wd, rr)
+        torch.cuda.synchronize()
+        outs.append([t.view(-1).view(torch.uint8).clone() for t in (y, rr, y2, ro, dx, dw)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
 
 def test_determinism():
     d = synthetic.make_inputs("bwd_bf16_8192x6144", rows=1024)

@@ -62,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_last_error.restype = ctypes.c_char_p
         lib.rmsnorm_tuning_set_geometry.argtypes = [i32, i32, i32, i32, i64]
         lib.rmsnorm_tuning_set_geometry.restype = None
+        lib.rmsnorm_tuning_set_streaming.argtypes = [i32]
+        lib.rmsnorm_tuning_set_streaming.restype = None
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -230,3 +232,9 @@ def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: i
     library's own choice."""
     code = {"fwd": 0, "bwd": 1}[which]
     load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))
+
+
+def set_streaming(mode: int = -1) -> None:
+    """Development hook (include/rmsnorm_tuning.h): -1 lets the library decide
+    by size whether to stream inputs/outputs past the caches, 0 never, 1 always."""
+    load_library().rmsnorm_tuning_set_streaming(int(mode))

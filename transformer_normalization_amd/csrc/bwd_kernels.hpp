@@ -17,6 +17,9 @@
 // pass 2 reloads x and dy, writes dx and adds dy*xn into the workgroup's own
 // workspace row (no other workgroup touches it, so no atomics).
 //
+// NT kernels stream x, dy and dx past the caches (non-temporal accesses);
+// weight, rrms and the partial sums use ordinary cached accesses.
+//
 // Kernel 2 (rmsnorm_dw_finalize): dw[j] = sum_p partial[p][j] in a fixed
 // order (16 interleaved slices of p, then the 16 slice sums in slice order),
 // so dw has the same bits on every run ("dweight ... is a separate kernel
@@ -44,7 +47,7 @@ struct BwdParams {
     float inv_h;
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool TWO_PASS, int MAXT>
+template <int XDT, int WDT, int VEC, int VPT, bool TWO_PASS, bool NT, int MAXT>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;  // == blockDim.x
@@ -76,8 +79,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
                 if (v < p.nvec) {
-                    xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
-                    dr[k].load(p.dy, row * p.dys + (int64_t)v * VEC);
+                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                    dr[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
                 } else {
                     xr[k].zero();
                     dr[k].zero();
@@ -114,7 +117,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     o[e] = rs * (dv[e] * wv[e]) - xn * s;
                     dwa[k][e] = __builtin_fmaf(dv[e], xn, dwa[k][e]);
                 }
-                if (v < p.nvec) store_elems<XDT, VEC>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                if (v < p.nvec) store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
             }
         }
         if (part != nullptr) {
@@ -140,6 +143,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     const int v = c * chunk + t + k * row_threads;
                     if (v < p.nvec) {
                         float xv[VEC], dv[VEC], wv[VEC];
+                        // cached: pass 2 reads the same chunk again
                         load_elems<XDT, VEC>(p.x, row * p.xs + (int64_t)v * VEC, xv);
                         load_elems<XDT, VEC>(p.dy, row * p.dys + (int64_t)v * VEC, dv);
                         if (p.w != nullptr) {
@@ -161,8 +165,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     const int v = c * chunk + t + k * row_threads;
                     if (v < p.nvec) {
                         float xv[VEC], dv[VEC], wv[VEC], o[VEC];
-                        load_elems<XDT, VEC>(p.x, row * p.xs + (int64_t)v * VEC, xv);
-                        load_elems<XDT, VEC>(p.dy, row * p.dys + (int64_t)v * VEC, dv);
+                        load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, xv);
+                        load_elems<XDT, VEC, NT>(p.dy, row * p.dys + (int64_t)v * VEC, dv);
                         if (p.w != nullptr) {
                             load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
                         } else {
@@ -175,7 +179,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                             xn[e] = xv[e] * rs;
                             o[e] = rs * (dv[e] * wv[e]) - xn[e] * s;
                         }
-                        store_elems<XDT, VEC>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                        store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
                         if (part != nullptr) {
                             float pa[VEC];
                             load_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);

@@ -24,6 +24,8 @@
 //     ("Required reasoning process", step 3, the persistent pattern).
 //   * Two-pass path (longer rows): pass 1 sums squares chunk by chunk, pass 2
 //     reloads each chunk with the same bounds and scales it (step 11).
+//   * NT kernels stream x, r, y and r_out past the caches (non-temporal
+//     accesses); the weight and rrms use ordinary cached accesses.
 //   * The reduction is a per-thread float32 sum over the thread's elements in
 //     column order, then a DPP wave sum and, for wpr > 1, a fixed-order sum
 //     of the wave totals through LDS.  The tree depends only on (H, VEC, VPT,
@@ -53,7 +55,7 @@ struct FwdParams {
     float inv_h;     // float32(1/H)
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, int MAXT>
+template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT>
 __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;
@@ -85,8 +87,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
                 if (valid && v < p.nvec) {
-                    xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
-                    if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
+                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                    if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
                 } else {
                     xr[k].zero();
                     if constexpr (RESID) rr[k].zero();
@@ -104,7 +106,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                     const int v = t + k * row_threads;
                     if (p.ro != nullptr && valid && v < p.nvec)
-                        store_elems<XDT, VEC>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
                 }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(hv[e], hv[e], acc);
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     wr[k].widen_to(wv);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
-                    store_elems<XDT, VEC>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                 }
             }
         }
@@ -150,6 +152,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
                     if (valid && v < p.nvec) {
+                        // cached: pass 2 reads the same chunk again
                         xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
                         if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
                     } else {
@@ -183,10 +186,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     const int v = c * chunk + t + k * row_threads;
                     if (valid && v < p.nvec) {
                         float hv[VEC], wv[VEC];
-                        load_elems<XDT, VEC>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                        load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, hv);
                         if constexpr (RESID) {
                             float rv[VEC];
-                            load_elems<XDT, VEC>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+                            load_elems<XDT, VEC, NT>(p.r, row * p.rs + (int64_t)v * VEC, rv);
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                         }
@@ -197,12 +200,12 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                             for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
                         }
                         if constexpr (RESID) {
-                            if (p.ro != nullptr) store_elems<XDT, VEC>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                            if (p.ro != nullptr) store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
                         }
                         float o[VEC];
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
-                        store_elems<XDT, VEC>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                     }
                 }
             }

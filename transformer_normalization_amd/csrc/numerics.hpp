@@ -108,7 +108,7 @@ __device__ __forceinline__ uint32_t pack_word<DT_BF16>(const float *in) {
 // N * bytes is either a multiple of 16 (one or more 16-byte accesses, which
 // need 16-byte aligned addresses) or N == 1 (one element).
 
-template <int DT, int N>
+template <int DT, int N, bool NT = false>
 __device__ __forceinline__ void load_elems(const void *base, int64_t elem, float *out) {
     constexpr int ES = Fmt<DT>::bytes;
     constexpr int BYTES = N * ES;
@@ -117,17 +117,28 @@ __device__ __forceinline__ void load_elems(const void *base, int64_t elem, float
         constexpr int PER_WORD = 4 / ES;
 #pragma unroll
         for (int c = 0; c < BYTES / 16; ++c) {
-            u32x4 raw = *reinterpret_cast<const u32x4 *>(p + 16 * c);
+            const u32x4 *q = reinterpret_cast<const u32x4 *>(p + 16 * c);
+            u32x4 raw;
+            if constexpr (NT)
+                raw = __builtin_nontemporal_load(q);
+            else
+                raw = *q;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) unpack_word<DT>(raw[q], out + (c * 4 + q) * PER_WORD);
+            for (int w = 0; w < 4; ++w) unpack_word<DT>(raw[w], out + (c * 4 + w) * PER_WORD);
         }
     } else {
         static_assert(N == 1, "sub-16-byte accesses are single elements");
-        out[0] = widen<DT>(*reinterpret_cast<const typename Fmt<DT>::T *>(p));
+        const typename Fmt<DT>::T *q = reinterpret_cast<const typename Fmt<DT>::T *>(p);
+        if constexpr (NT)
+            out[0] = widen<DT>(__builtin_nontemporal_load(q));
+        else
+            out[0] = widen<DT>(*q);
     }
 }
 
-template <int DT, int N>
+// NT = true marks a streaming access (non-temporal: the line is not kept in
+// the caches), for data each kernel touches exactly once.
+template <int DT, int N, bool NT = false>
 __device__ __forceinline__ void store_elems(void *base, int64_t elem, const float *in) {
     constexpr int ES = Fmt<DT>::bytes;
     constexpr int BYTES = N * ES;
@@ -139,11 +150,17 @@ __device__ __forceinline__ void store_elems(void *base, int64_t elem, const floa
             u32x4 raw;
 #pragma unroll
             for (int q = 0; q < 4; ++q) raw[q] = pack_word<DT>(in + (c * 4 + q) * PER_WORD);
-            *reinterpret_cast<u32x4 *>(p + 16 * c) = raw;
+            if constexpr (NT)
+                __builtin_nontemporal_store(raw, reinterpret_cast<u32x4 *>(p + 16 * c));
+            else
+                *reinterpret_cast<u32x4 *>(p + 16 * c) = raw;
         }
     } else {
         static_assert(N == 1, "sub-16-byte accesses are single elements");
-        *reinterpret_cast<typename Fmt<DT>::T *>(p) = narrow<DT>(in[0]);
+        if constexpr (NT)
+            __builtin_nontemporal_store(narrow<DT>(in[0]), reinterpret_cast<typename Fmt<DT>::T *>(p));
+        else
+            *reinterpret_cast<typename Fmt<DT>::T *>(p) = narrow<DT>(in[0]);
     }
 }
 
@@ -156,17 +173,27 @@ struct Raw {
     static constexpr int CHUNKS = VEC ? (N * ES) / 16 : 1;
     u32x4 v[CHUNKS];
 
+    template <bool NT = false>
     __device__ __forceinline__ void load(const void *base, int64_t elem) {
         const char *p = static_cast<const char *>(base) + elem * ES;
         if constexpr (VEC) {
 #pragma unroll
-            for (int c = 0; c < CHUNKS; ++c) v[c] = *reinterpret_cast<const u32x4 *>(p + 16 * c);
+            for (int c = 0; c < CHUNKS; ++c) {
+                const u32x4 *q = reinterpret_cast<const u32x4 *>(p + 16 * c);
+                if constexpr (NT)
+                    v[c] = __builtin_nontemporal_load(q);
+                else
+                    v[c] = *q;
+            }
         } else {
             static_assert(N == 1, "sub-16-byte accesses are single elements");
-            if constexpr (DT == DT_F32)
-                v[0][0] = __builtin_bit_cast(uint32_t, *reinterpret_cast<const float *>(p));
-            else
-                v[0][0] = *reinterpret_cast<const uint16_t *>(p);
+            if constexpr (DT == DT_F32) {
+                const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+                v[0][0] = NT ? __builtin_nontemporal_load(q) : *q;
+            } else {
+                const uint16_t *q = reinterpret_cast<const uint16_t *>(p);
+                v[0][0] = NT ? __builtin_nontemporal_load(q) : *q;
+            }
         }
     }
     __device__ __forceinline__ void zero() {

@@ -289,93 +289,117 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
 typedef void (*fwd_fn)(const FwdParams);
 typedef void (*bwd_fn)(const BwdParams);
 
-template <int XDT, int WDT, int VEC, bool RESID>
+template <int XDT, int WDT, int VEC, bool RESID, bool NT>
 fwd_fn fwd_kernel_for(int vpt, bool two_pass) {
     if (two_pass) {
         constexpr int V = VEC > 1 ? 4 : 8;
-        return rmsnorm_fwd_kernel<XDT, WDT, VEC, V, RESID, true, 1024>;
+        return rmsnorm_fwd_kernel<XDT, WDT, VEC, V, RESID, true, NT, 1024>;
     }
     switch (vpt) {
-    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, RESID, false, fwd_max_threads(1 * VEC, RESID)>;
-    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, RESID, false, fwd_max_threads(2 * VEC, RESID)>;
-    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, RESID, false, fwd_max_threads(4 * VEC, RESID)>;
-    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, RESID, false, fwd_max_threads(8 * VEC, RESID)>;
+    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, RESID, false, NT, fwd_max_threads(1 * VEC, RESID)>;
+    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, RESID, false, NT, fwd_max_threads(2 * VEC, RESID)>;
+    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, RESID, false, NT, fwd_max_threads(4 * VEC, RESID)>;
+    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, RESID, false, NT, fwd_max_threads(8 * VEC, RESID)>;
     default: break;
     }
     if constexpr (VEC > 1) {
         switch (vpt) {
-        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, RESID, false, fwd_max_threads(3 * VEC, RESID)>;
-        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, RESID, false, fwd_max_threads(6 * VEC, RESID)>;
+        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, RESID, false, NT, fwd_max_threads(3 * VEC, RESID)>;
+        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, RESID, false, NT, fwd_max_threads(6 * VEC, RESID)>;
         default: break;
         }
     }
     return nullptr;
 }
 
-template <int XDT, int WDT, bool RESID>
+template <int XDT, int WDT, bool RESID, bool NT>
 fwd_fn fwd_kernel_vec(int vec, int vpt, bool two_pass) {
     constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? fwd_kernel_for<XDT, WDT, 1, RESID>(vpt, two_pass)
-                    : fwd_kernel_for<XDT, WDT, V, RESID>(vpt, two_pass);
+    return vec == 1 ? fwd_kernel_for<XDT, WDT, 1, RESID, NT>(vpt, two_pass)
+                    : fwd_kernel_for<XDT, WDT, V, RESID, NT>(vpt, two_pass);
+}
+
+template <bool RESID, bool NT>
+fwd_fn fwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
+    const bool wf32 = (wdt == RMSN_F32);
+    switch (xdt) {
+    case RMSN_F32: return fwd_kernel_vec<DT_F32, DT_F32, RESID, NT>(vec, vpt, two_pass);
+    case RMSN_F16:
+        return wf32 ? fwd_kernel_vec<DT_F16, DT_F32, RESID, NT>(vec, vpt, two_pass)
+                    : fwd_kernel_vec<DT_F16, DT_F16, RESID, NT>(vec, vpt, two_pass);
+    case RMSN_BF16:
+        return wf32 ? fwd_kernel_vec<DT_BF16, DT_F32, RESID, NT>(vec, vpt, two_pass)
+                    : fwd_kernel_vec<DT_BF16, DT_BF16, RESID, NT>(vec, vpt, two_pass);
+    }
+    return nullptr;
 }
 
 template <bool RESID>
-fwd_fn fwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
-    const bool wf32 = (wdt == RMSN_F32);
-    switch (xdt) {
-    case RMSN_F32: return fwd_kernel_vec<DT_F32, DT_F32, RESID>(vec, vpt, two_pass);
-    case RMSN_F16:
-        return wf32 ? fwd_kernel_vec<DT_F16, DT_F32, RESID>(vec, vpt, two_pass)
-                    : fwd_kernel_vec<DT_F16, DT_F16, RESID>(vec, vpt, two_pass);
-    case RMSN_BF16:
-        return wf32 ? fwd_kernel_vec<DT_BF16, DT_F32, RESID>(vec, vpt, two_pass)
-                    : fwd_kernel_vec<DT_BF16, DT_BF16, RESID>(vec, vpt, two_pass);
-    }
-    return nullptr;
+fwd_fn fwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
+    return nt ? fwd_lookup_nt<RESID, true>(xdt, wdt, vec, vpt, two_pass)
+              : fwd_lookup_nt<RESID, false>(xdt, wdt, vec, vpt, two_pass);
 }
 
-template <int XDT, int WDT, int VEC>
+template <int XDT, int WDT, int VEC, bool NT>
 bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
     if (two_pass) {
         constexpr int V = VEC > 1 ? 4 : 8;
-        return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, true, 1024>;
+        return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, true, NT, 1024>;
     }
     switch (vpt) {
-    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, false, bwd_max_threads(1 * VEC)>;
-    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, false, bwd_max_threads(2 * VEC)>;
-    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, false, bwd_max_threads(4 * VEC)>;
+    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, false, NT, bwd_max_threads(1 * VEC)>;
+    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, false, NT, bwd_max_threads(2 * VEC)>;
+    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, false, NT, bwd_max_threads(4 * VEC)>;
     default: break;
     }
     if constexpr (VEC == 1) {
-        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, false, bwd_max_threads(8 * VEC)>;
+        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, false, NT, bwd_max_threads(8 * VEC)>;
     }
     if constexpr (VEC > 1) {
         switch (vpt) {
-        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, bwd_max_threads(3 * VEC)>;
-        case 6: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 6, false, bwd_max_threads(6 * VEC)>;
+        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, NT, bwd_max_threads(3 * VEC)>;
+        case 6: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 6, false, NT, bwd_max_threads(6 * VEC)>;
         default: break;
         }
     }
     return nullptr;
 }
 
-template <int XDT, int WDT>
+template <int XDT, int WDT, bool NT>
 bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass) {
     constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1>(vpt, two_pass) : bwd_kernel_for<XDT, WDT, V>(vpt, two_pass);
+    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1, NT>(vpt, two_pass) : bwd_kernel_for<XDT, WDT, V, NT>(vpt, two_pass);
 }
 
-bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
+template <bool NT>
+bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
     const bool wf32 = (wdt == RMSN_F32);
     switch (xdt) {
-    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32>(vec, vpt, two_pass);
+    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32, NT>(vec, vpt, two_pass);
     case RMSN_F16:
-        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32>(vec, vpt, two_pass) : bwd_kernel_vec<DT_F16, DT_F16>(vec, vpt, two_pass);
+        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32, NT>(vec, vpt, two_pass)
+                    : bwd_kernel_vec<DT_F16, DT_F16, NT>(vec, vpt, two_pass);
     case RMSN_BF16:
-        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_BF16, DT_BF16>(vec, vpt, two_pass);
+        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, NT>(vec, vpt, two_pass)
+                    : bwd_kernel_vec<DT_BF16, DT_BF16, NT>(vec, vpt, two_pass);
     }
     return nullptr;
+}
+
+bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
+    return nt ? bwd_lookup_nt<true>(xdt, wdt, vec, vpt, two_pass) : bwd_lookup_nt<false>(xdt, wdt, vec, vpt, two_pass);
+}
+
+// Streaming (non-temporal) accesses pay off when a call moves more data than
+// the caches could usefully keep for the next kernel; below that, ordinary
+// cached accesses leave the outputs in L2 / the last-level cache for the
+// consumer.  Mode -1 = decide by size, 0 = never, 1 = always.
+constexpr int64_t kStreamBytes = int64_t(64) << 20;
+std::atomic<int> g_stream_mode{-1};
+
+bool use_streaming(int64_t bytes_moved) {
+    const int mode = g_stream_mode.load(std::memory_order_relaxed);
+    return mode < 0 ? bytes_moved >= kStreamBytes : mode > 0;
 }
 
 rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what) {
@@ -453,8 +477,9 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
     if (grid > INT32_MAX) grid = INT32_MAX;
     const int64_t iters = (groups + grid - 1) / grid;
 
-    fwd_fn fn = resid ? fwd_lookup<true>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass)
-                      : fwd_lookup<false>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass);
+    const bool nt = use_streaming((resid ? (ro ? 4 : 3) : 2) * M * H * eb);
+    fwd_fn fn = resid ? fwd_lookup<true>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
+                      : fwd_lookup<false>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -566,7 +591,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         g = o;
         if (ov.c > 0) P = ov.c;
     }
-    bwd_fn fn = bwd_lookup(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass);
+    const bool nt = use_streaming(3 * M * H * eb);
+    bwd_fn fn = bwd_lookup(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -657,6 +683,8 @@ RMSN_API const char *rmsnorm_status_string(rmsn_status_t s) {
 }
 
 RMSN_API const char *rmsnorm_last_error(void) { return g_last_error; }
+
+RMSN_API void rmsnorm_tuning_set_streaming(int mode) { g_stream_mode.store(mode < 0 ? -1 : mode > 0 ? 1 : 0); }
 
 RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid) {
     get_override(0);  // the environment is read first, so a later call wins

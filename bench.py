@@ -34,15 +34,22 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30
 
 
-def kernel_source_digest() -> str:
-    """Digest of the HIP sources; a stored traffic measurement applies only to
-    the kernels it was taken on."""
+KERNEL_SOURCES = {
+    "fwd": ("numerics.hpp", "fwd_kernels.hpp", "rmsnorm_api.hip"),
+    "fwd_residual": ("numerics.hpp", "fwd_kernels.hpp", "rmsnorm_api.hip"),
+    "bwd": ("numerics.hpp", "bwd_kernels.hpp", "rmsnorm_api.hip"),
+}
+
+
+def kernel_source_digest(kind: str) -> str:
+    """Digest of the HIP sources a kind of call runs (kernels and the host code
+    that picks their launch geometry); a stored traffic measurement applies
+    only to the sources it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_normalization_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in KERNEL_SOURCES[kind]:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -57,7 +64,9 @@ def stored_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_digest") != kernel_source_digest():
+    name, _ = WORKLOADS[workload]
+    import synthetic
+    if fields.get("kernel_source_digest") != kernel_source_digest(synthetic.WORKLOADS[name]["kind"]):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -132,6 +141,62 @@ def cpu_baseline(spec, kind, weighted, seconds):
     }
 
 
+def summarize_pmc(fetch_csv, write_csv, workload):
+    """Text summary of HBM traffic per launch of the workload's dominant
+    kernel from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch), each scaled by what the same counter reads for the plain
+    device copies of the x tensor (known size) in the same run."""
+    import csv
+    import statistics
+
+    import synthetic
+
+    name, weighted = WORKLOADS[workload]
+    spec = synthetic.WORKLOADS[name]
+    es = synthetic.element_size(spec["dtype"])
+    ws = synthetic.element_size(spec["wdtype"])
+    known_kib = spec["M"] * spec["H"] * es / 1024.0
+    kernel_key = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel",
+                  "bwd": "rmsnorm_bwd_kernel"}[spec["kind"]]
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        kern = [float(r["Counter_Value"]) for r in rows if kernel_key in r["Kernel_Name"]]
+        copies = [(int(r["Grid_Size"]), float(r["Counter_Value"])) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"]]
+        big = max(g for g, _ in copies)
+        ref = [v for g, v in copies if g == big]
+        kname = next(r["Kernel_Name"] for r in rows if kernel_key in r["Kernel_Name"])
+        return statistics.mean(kern), len(kern), statistics.mean(ref), len(ref), kname
+
+    f_k, f_n, f_ref, f_rn, kname = read(fetch_csv, "FETCH_SIZE")
+    w_k, w_n, w_ref, w_rn, _ = read(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = known_kib / f_ref, known_kib / w_ref
+    hbm = (f_k * f_scale + w_k * w_scale) * 1024.0
+    alg = algorithmic_bytes(spec["kind"], spec["M"], spec["H"], es, ws, weighted)
+    lines = [
+        f"# HBM traffic per launch of {kname}",
+        f"# workload {workload}: M={spec['M']} H={spec['H']} {spec['dtype']}",
+        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
+        f"#   python3 bench.py --workload {workload} --cpu-seconds 0 --steps 20 --warmup 10 --copy-reference",
+        "# each scaled by the same counter's reading for device copies of the x tensor",
+        f"# ({known_kib:.0f} KiB read and written per copy) in the same run; summary made by",
+        f"#   python3 bench.py --workload {workload} --summarize-pmc <fetch csv> <write csv>",
+        f"kernel_source_digest: {kernel_source_digest(spec['kind'])}",
+        f"kernel_dispatches: {f_n} (fetch run), {w_n} (write run)",
+        f"fetch_size_kib_per_launch: {f_k:.2f}",
+        f"write_size_kib_per_launch: {w_k:.2f}",
+        f"copy_fetch_size_kib: {f_ref:.2f} over {f_rn} copies",
+        f"copy_write_size_kib: {w_ref:.2f} over {w_rn} copies",
+        f"fetch_scale: {f_scale:.5f}",
+        f"write_scale: {w_scale:.5f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {hbm / alg:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,7 +207,13 @@ def main():
     ap.add_argument("--geom", default="", help="development: forced launch geometry 'vpt,wpr,rpw,grid'")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain device copy of known size (for scaling HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc counter_collection.csv files")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows shard across GPUs with no "
@@ -176,7 +247,6 @@ def main():
     dt = d["dtype"]
     M, H = spec["M"], spec["H"]
     es, ws = synthetic.element_size(dt), synthetic.element_size(d["wdtype"])
-    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
 
     def up(a, fmt):
         a = np.ascontiguousarray(a)

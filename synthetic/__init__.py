@@ -3,7 +3,7 @@
 This module draws numbers and encodes them into storage formats. It holds none
 of the normalisation arithmetic: no squares, no means, no reciprocal roots.
 
-Generator (a reading: the pages name no seeds and no generator):
+Generator (a reading: the pages name no seeds and no generator), in _gen.c:
   * SplitMix64 in counter form.  The stream for (seed, stream id) starts from
     key = mix64(seed * GOLDEN + stream + 1); its i-th output is
     mix64(key + (i + 1) * GOLDEN), where mix64 is Steele, Lea and Flood's
@@ -22,11 +22,12 @@ outlier mask = 4, outlier value = 5.
 
 from __future__ import annotations
 
-import numpy as np
+import ctypes
+import os
+import subprocess
+import threading
 
-GOLDEN = np.uint64(0x9E3779B97F4A7C15)
-_M1 = np.uint64(0xBF58476D1CE4E5B9)
-_M2 = np.uint64(0x94D049BB133111EB)
+import numpy as np
 
 STREAM_X = 0
 STREAM_W = 1
@@ -38,57 +39,49 @@ STREAM_OUTLIER_VALUE = 5
 # Storage formats, by name.  "bf16" arrays are returned as uint16 bit patterns.
 DTYPES = ("f32", "f16", "bf16")
 
-_CHUNK = 1 << 22
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "_gen.c")
+_LIB = os.path.join(_HERE, "_libgen.so")
+_lock = threading.Lock()
+_lib = None
 
 
-def _mix64(z: np.ndarray) -> np.ndarray:
-    with np.errstate(over="ignore"):
-        z = (z ^ (z >> np.uint64(30))) * _M1
-        z = (z ^ (z >> np.uint64(27))) * _M2
-        return z ^ (z >> np.uint64(31))
+def build(force: bool = True) -> str:
+    """Compile the generator (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                        "-Wall", "-Werror", _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
 
 
-def _key(seed: int, stream: int) -> np.uint64:
-    with np.errstate(over="ignore"):
-        s = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) * GOLDEN + np.uint64(stream + 1)
-    return _mix64(np.array([s], dtype=np.uint64))[0]
+def _gen():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            u64, i32, i64, dp, vp = ctypes.c_uint64, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+            lib.syn_uniform.argtypes = [u64, i32, i64, i64, vp]
+            lib.syn_normal.argtypes = [u64, i32, i64, i64, dp, dp, vp]
+            lib.syn_outliers.argtypes = [u64, i32, i32, i64, i64, dp, dp, dp, vp]
+            _lib = lib
+    return _lib
 
 
-def raw_bits(seed: int, stream: int, start: int, count: int) -> np.ndarray:
-    """Outputs start .. start+count-1 of the counter stream, as uint64."""
-    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return _mix64(_key(seed, stream) + idx * GOLDEN)
-
-
-def uniform(seed: int, stream: int, n: int) -> np.ndarray:
-    """n float64 uniforms in [0, 1)."""
+def uniform(seed: int, stream: int, n: int, start: int = 0) -> np.ndarray:
+    """n float64 uniforms in [0, 1): positions start .. start+n-1 of the stream."""
     out = np.empty(n, dtype=np.float64)
-    for s in range(0, n, _CHUNK):
-        c = min(_CHUNK, n - s)
-        out[s:s + c] = (raw_bits(seed, stream, s, c) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    _gen().syn_uniform(seed, stream, start, n, out.ctypes.data)
     return out
 
 
-def normal(seed: int, stream: int, n: int, mean: float = 0.0, std: float = 1.0) -> np.ndarray:
+def normal(seed: int, stream: int, n: int, mean: float = 0.0, std: float = 1.0, start: int = 0) -> np.ndarray:
     """n float64 draws from N(mean, std**2) (std is the standard deviation)."""
     out = np.empty(n, dtype=np.float64)
-    npairs = (n + 1) // 2
-    for s in range(0, npairs, _CHUNK // 2):
-        c = min(_CHUNK // 2, npairs - s)
-        b = raw_bits(seed, stream, 2 * s, 2 * c) >> np.uint64(11)
-        u0 = b[0::2].astype(np.float64) * (2.0 ** -53)
-        u1 = b[1::2].astype(np.float64) * (2.0 ** -53)
-        rad = np.sqrt(-2.0 * np.log1p(-u0))
-        theta = (2.0 * np.pi) * u1
-        pair = np.empty(2 * c, dtype=np.float64)
-        pair[0::2] = rad * np.cos(theta)
-        pair[1::2] = rad * np.sin(theta)
-        lo, hi = 2 * s, min(2 * s + 2 * c, n)
-        out[lo:hi] = pair[: hi - lo]
-    if mean != 0.0 or std != 1.0:
-        out *= std
-        out += mean
+    _gen().syn_normal(seed, stream, start, n, float(mean), float(std), out.ctypes.data)
     return out
 
 
@@ -139,18 +132,8 @@ def with_outliers(seed: int, shape, dtype: str, mean: float, std: float,
     is replaced by sign * U(lo, hi), the sign +1 or -1 with equal odds."""
     n = int(np.prod(shape))
     v = normal(seed, STREAM_X, n, mean, std)
-    pick = uniform(seed, STREAM_OUTLIER_MASK, n) < frac
-    idx = np.nonzero(pick)[0]
-    if idx.size:
-        # value stream: output 2i decides the sign, output 2i+1 the magnitude
-        # (drawn only where needed, from the same counter positions each time)
-        key = _key(seed, STREAM_OUTLIER_VALUE)
-        with np.errstate(over="ignore"):
-            bs = _mix64(key + (2 * idx.astype(np.uint64) + np.uint64(1)) * GOLDEN)
-            bm = _mix64(key + (2 * idx.astype(np.uint64) + np.uint64(2)) * GOLDEN)
-        us = (bs >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
-        um = (bm >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
-        v[idx] = np.where(us < 0.5, 1.0, -1.0) * (lo + (hi - lo) * um)
+    _gen().syn_outliers(seed, STREAM_OUTLIER_MASK, STREAM_OUTLIER_VALUE, 0, n, float(frac), float(lo), float(hi),
+                        v.ctypes.data)
     return encode(v, dtype).reshape(shape)
 
 

@@ -72,52 +72,102 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dwa[k][e] = 0.0f;
         }
-        int parity = 0;
-        for (int64_t row = row0; row < row1; ++row, parity ^= 1) {
-            Raw<XDT, VEC> xr[VPT], dr[VPT];
+        // Software pipeline: the loads of rows row+1 .. row+PF are in flight
+        // while row is reduced and stored (the barrier in row_sum waits on
+        // LDS only).  The rows' saved rrms values are read 64 at a time, one
+        // per lane, and taken with v_readlane, so that no vector load inside
+        // the loop makes the in-order memory counter wait for the prefetch.
+        // depth 2 for small tiles, 1 where three rows would not fit the
+        // register budget (packed 32-bit words of x and dy per row)
+        constexpr int WORDS = 2 * VPT * VEC * Fmt<XDT>::bytes / 4;
+        constexpr int PF = WORDS <= 16 ? 2 : 1;
+        Raw<XDT, VEC> xb[PF + 1][VPT], db[PF + 1][VPT];
+        const int lane = t & 63;
+        // rows in chunks of 64: one rrms value per lane for the chunk, loaded
+        // before the chunk's row loads so that no wait inside the row loop
+        // depends on a load issued after a prefetch
+        for (int64_t base = row0; base < row1; base += 64) {
+            const int64_t cend = base + 64 < row1 ? base + 64 : row1;
+            float rr_lane = (base + lane < cend) ? p.rrms[base + lane] : 0.0f;
+            asm volatile("" : "+v"(rr_lane));  // complete it now, before the row loads
+            // Row loads inside the steady-state loop are unconditional, so the
+            // compiler can count them in order and wait only for the oldest;
+            // vector indices past the row are clamped to its last vector
+            // (same addresses within one wave access: no extra traffic) and
+            // masked at use.
+            auto load_row = [&](int64_t row, Raw<XDT, VEC> *xd, Raw<XDT, VEC> *dd) {
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int v = t + k * row_threads;
-                if (v < p.nvec) {
-                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
-                    dr[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
-                } else {
-                    xr[k].zero();
-                    dr[k].zero();
+                for (int k = 0; k < VPT; ++k) {
+                    const int vv = t + k * row_threads;
+                    const int v = vv < p.nvec ? vv : p.nvec - 1;
+                    xd[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                    dd[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
+                }
+            };
+            auto process_row = [&](int64_t row, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr) {
+                const float rs = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rr_lane), (int)(row - base)));
+                float acc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    float xv[VEC], dv[VEC], wv[VEC];
+                    xr[k].widen_to(xv);
+                    dr[k].widen_to(dv);
+                    wr[k].widen_to(wv);
+                    float part = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) part = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, part);
+                    if (t + k * row_threads < p.nvec) acc += part;
+                }
+                const float c = row_sum(acc, p.wpr, wave, &red[(row - row0) & 1][0]);
+                const float s = (c * p.inv_h) * rs;
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    xr[k].opaque();
+                    dr[k].opaque();
+                }
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = t + k * row_threads;
+                    float xv[VEC], dv[VEC], wv[VEC], o[VEC];
+                    xr[k].widen_to(xv);
+                    dr[k].widen_to(dv);
+                    wr[k].widen_to(wv);
+                    if (v < p.nvec) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const float xn = xv[e] * rs;
+                            o[e] = rs * (dv[e] * wv[e]) - xn * s;
+                            dwa[k][e] = __builtin_fmaf(dv[e], xn, dwa[k][e]);
+                        }
+                        store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                    }
+                }
+            };
+            // prologue: unconditional too (a chunk shorter than PF rows reads
+            // its last row again rather than branching)
+#pragma unroll
+            for (int j = 0; j < PF; ++j) load_row(base + j < cend ? base + j : cend - 1, xb[j], db[j]);
+            // Steady state, unrolled by PF+1 so that row r always lives in
+            // slot (r - base) % (PF+1) (copying registers whose loads are in
+            // flight would wait for them).  It runs while every prefetched row
+            // exists, so its loads need no condition.
+            int64_t row = base;
+            for (; row + 2 * PF < cend; row += PF + 1) {
+#pragma unroll
+                for (int u = 0; u <= PF; ++u) {
+                    load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)]);
+                    process_row(row + u, xb[u], db[u]);
                 }
             }
-            const float rs = p.rrms[row];
-            float acc = 0.0f;
+            // the last rows (at most 2*PF), with conditional prefetch
 #pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                float xv[VEC], dv[VEC], wv[VEC];
-                xr[k].widen_to(xv);
-                dr[k].widen_to(dv);
-                wr[k].widen_to(wv);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, acc);
-            }
-            const float c = row_sum(acc, p.wpr, wave, &red[parity][0]);
-            const float s = (c * p.inv_h) * rs;
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                xr[k].opaque();
-                dr[k].opaque();
-            }
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) {
-                const int v = t + k * row_threads;
-                float xv[VEC], dv[VEC], wv[VEC], o[VEC];
-                xr[k].widen_to(xv);
-                dr[k].widen_to(dv);
-                wr[k].widen_to(wv);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float xn = xv[e] * rs;
-                    o[e] = rs * (dv[e] * wv[e]) - xn * s;
-                    dwa[k][e] = __builtin_fmaf(dv[e], xn, dwa[k][e]);
+            for (int u = 0; u < 2 * PF; ++u) {
+                if (row + u < cend) {
+                    if (row + u + PF < cend)
+                        load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)]);
+                    process_row(row + u, xb[u % (PF + 1)], db[u % (PF + 1)]);
                 }
-                if (v < p.nvec) store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
             }
         }
         if (part != nullptr) {
@@ -205,7 +255,17 @@ __global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restr
     const int col = blockIdx.x * 64 + lane;
     float acc = 0.0f;
     if (col < H) {
-        for (int q = s; q < P; q += 16) acc += partial[(int64_t)q * H + col];
+        // batches of 8 independent loads, then 8 adds in increasing q: the
+        // same order as one add per load, without one memory latency per add
+        int q = s;
+        for (; q + 16 * 7 < P; q += 16 * 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(q + 16 * j) * H + col];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += v[j];
+        }
+        for (; q < P; q += 16) acc += partial[(int64_t)q * H + col];
     }
     sums[s][lane] = acc;
     __syncthreads();

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rmsn {
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
@@ -164,14 +166,17 @@ __device__ __forceinline__ void store_elems(void *base, int64_t elem, const floa
     }
 }
 
-// Raw (still packed) 16-byte loads, so that all of a row's loads can be
-// issued before any of them is widened.
+// Raw (still packed) loads, so that all of a row's loads can be issued
+// before any of them is widened.  Vector tiles hold CHUNKS 16-byte words;
+// single-element tiles hold one 32-bit word.
 template <int DT, int N>
 struct Raw {
     static constexpr int ES = Fmt<DT>::bytes;
     static constexpr bool VEC = (N * ES) % 16 == 0;
     static constexpr int CHUNKS = VEC ? (N * ES) / 16 : 1;
-    u32x4 v[CHUNKS];
+    static_assert(VEC || N == 1, "sub-16-byte accesses are single elements");
+    using Word = typename std::conditional<VEC, u32x4, uint32_t>::type;
+    Word v[CHUNKS];
 
     template <bool NT = false>
     __device__ __forceinline__ void load(const void *base, int64_t elem) {
@@ -185,20 +190,13 @@ struct Raw {
                 else
                     v[c] = *q;
             }
+        } else if constexpr (DT == DT_F32) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+            v[0] = NT ? __builtin_nontemporal_load(q) : *q;
         } else {
-            static_assert(N == 1, "sub-16-byte accesses are single elements");
-            if constexpr (DT == DT_F32) {
-                const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-                v[0][0] = NT ? __builtin_nontemporal_load(q) : *q;
-            } else {
-                const uint16_t *q = reinterpret_cast<const uint16_t *>(p);
-                v[0][0] = NT ? __builtin_nontemporal_load(q) : *q;
-            }
+            const uint16_t *q = reinterpret_cast<const uint16_t *>(p);
+            v[0] = NT ? __builtin_nontemporal_load(q) : *q;
         }
-    }
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) v[c] = u32x4{0u, 0u, 0u, 0u};
     }
     // Hide the value from the optimiser so that widening it again after a
     // reduction is recomputed from these packed registers instead of keeping
@@ -217,7 +215,21 @@ struct Raw {
         else
             one = 0x3F803F80u;
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) v[c] = u32x4{one, one, one, one};
+        for (int c = 0; c < CHUNKS; ++c) {
+            if constexpr (VEC)
+                v[c] = u32x4{one, one, one, one};
+            else
+                v[c] = one;
+        }
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+            if constexpr (VEC)
+                v[c] = u32x4{0u, 0u, 0u, 0u};
+            else
+                v[c] = 0u;
+        }
     }
     __device__ __forceinline__ void widen_to(float *out) const {
         if constexpr (VEC) {
@@ -226,11 +238,10 @@ struct Raw {
             for (int c = 0; c < CHUNKS; ++c)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) unpack_word<DT>(v[c][q], out + (c * 4 + q) * PER_WORD);
+        } else if constexpr (DT == DT_F32) {
+            out[0] = __builtin_bit_cast(float, v[0]);
         } else {
-            if constexpr (DT == DT_F32)
-                out[0] = __builtin_bit_cast(float, v[0][0]);
-            else
-                out[0] = widen<DT>((uint16_t)v[0][0]);
+            out[0] = widen<DT>((uint16_t)v[0]);
         }
     }
 };

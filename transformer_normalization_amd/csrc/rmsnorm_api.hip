@@ -225,7 +225,7 @@ Override get_override(int which) {
 // vectors per thread available as kernel instantiations
 enum class Kind { Fwd, FwdResid, Bwd };
 constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
-constexpr int kBwdVecVpt[] = {1, 2, 3, 4, 6};
+constexpr int kBwdVecVpt[] = {1, 2, 3, 4};
 constexpr int kScalarVpt[] = {1, 2, 4, 8};
 // largest workgroup each register tile may use (the kernels' launch bounds)
 int max_threads_for(Kind kind, int vpt, int vec) {
@@ -250,7 +250,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     g.vec = vec;
     g.nvec = (H + vec - 1) / vec;
     const int *set = vec == 1 ? kScalarVpt : kind == Kind::Bwd ? kBwdVecVpt : kFwdVecVpt;
-    const int nset = vec == 1 ? 4 : kind == Kind::Bwd ? 5 : 6;
+    const int nset = vec == 1 ? 4 : kind == Kind::Bwd ? 4 : 6;
     double best = 1e30;
     for (int i = 0; i < nset; ++i) {
         const int vpt = set[i];
@@ -358,7 +358,6 @@ bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
     if constexpr (VEC > 1) {
         switch (vpt) {
         case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, NT, bwd_max_threads(3 * VEC)>;
-        case 6: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 6, false, NT, bwd_max_threads(6 * VEC)>;
         default: break;
         }
     }
@@ -573,7 +572,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     const bool vec_ok = (H % vecw) == 0 && aligned16(dy) && aligned16(x) && aligned16(dx) &&
                         (dys * eb) % 16 == 0 && (xs * eb) % 16 == 0 && (dxs * eb) % 16 == 0 &&
                         (w == nullptr || aligned16(w));
-    Geom g = pick_row_geom(Kind::Bwd, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 24);
+    Geom g = pick_row_geom(Kind::Bwd, (int)H, vec_ok ? vecw : 1, 8);
     int64_t P = 0;  // 0: chosen from the device below
     const Override ov = get_override(1);
     if (ov.set) {
@@ -596,7 +595,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
-    if (P <= 0) P = 2 * (int64_t)cus;
+    // three workgroups per CU: enough rows in flight to cover memory latency
+    // while the dw partial sums stay a small fraction of the traffic
+    if (P <= 0) P = 3 * (int64_t)cus;
     if (P > kMaxPartials) P = kMaxPartials;
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;

@@ -245,34 +245,37 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 }
 
 // dw[j] = sum over p of partial[p][j]: 64 columns x 16 slices per workgroup
-// of 1024 threads.  Thread (col, s) sums p = s, s+16, ... in increasing p;
-// the 16 slice sums are then added in slice order.
+// of 1024 threads (a wave reads 256 contiguous bytes of one partial row).
+// Thread (col, s) sums p = s, s+16, ... in increasing p, loading 8 at a time
+// before adding; the 16 slice sums of a column are then added in slice
+// order.  The order is fixed, so dw has the same bits on every run.
+constexpr int kFinCols = 64;
+constexpr int kFinSlices = 16;
+
 __global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restrict__ partial, int P, int H,
                                                             float *__restrict__ dw) {
-    __shared__ float sums[16][64];
-    const int lane = threadIdx.x & 63;
-    const int s = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + lane;
+    __shared__ float sums[kFinSlices][kFinCols];
+    const int c = threadIdx.x % kFinCols;
+    const int s = threadIdx.x / kFinCols;
+    const int col = blockIdx.x * kFinCols + c;
     float acc = 0.0f;
     if (col < H) {
-        // batches of 8 independent loads, then 8 adds in increasing q: the
-        // same order as one add per load, without one memory latency per add
         int q = s;
-        for (; q + 16 * 7 < P; q += 16 * 8) {
+        for (; q + kFinSlices * 7 < P; q += kFinSlices * 8) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(q + 16 * j) * H + col];
+            for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(q + kFinSlices * j) * H + col];
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc += v[j];
         }
-        for (; q < P; q += 16) acc += partial[(int64_t)q * H + col];
+        for (; q < P; q += kFinSlices) acc += partial[(int64_t)q * H + col];
     }
-    sums[s][lane] = acc;
+    sums[s][c] = acc;
     __syncthreads();
     if (s == 0 && col < H) {
-        float tot = sums[0][lane];
+        float tot = sums[0][c];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) tot += sums[i][lane];
+        for (int i = 1; i < kFinSlices; ++i) tot += sums[i][c];
         dw[col] = tot;
     }
 }

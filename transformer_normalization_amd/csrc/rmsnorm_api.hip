@@ -564,7 +564,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *none = nullptr;
         int P = 0, Hi = (int)H;
         void *args[] = {(void *)&none, &P, &Hi, &dw};
-        return launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + 63) / 64)), dim3(1024), args,
+        return launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), args,
                       stream, "rmsnorm_dw_finalize");
     }
 
@@ -595,9 +595,10 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
-    // three workgroups per CU: enough rows in flight to cover memory latency
-    // while the dw partial sums stay a small fraction of the traffic
-    if (P <= 0) P = 3 * (int64_t)cus;
+    // four workgroups per CU: on gfx950 the row loop gains more from the extra
+    // rows in flight than the dw partial sums (P x H x 4 bytes, written and
+    // read once) cost
+    if (P <= 0) P = 4 * (int64_t)cus;
     if (P > kMaxPartials) P = kMaxPartials;
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;
@@ -627,7 +628,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *part = p.partial;
         int Pi = (int)P, Hi = (int)H;
         void *fargs[] = {(void *)&part, &Pi, &Hi, &dw};
-        if ((st = launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + 63) / 64)), dim3(1024), fargs,
+        if ((st = launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), fargs,
                          stream, "rmsnorm_dw_finalize")) != RMSN_OK)
             return st;
     }

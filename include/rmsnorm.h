@@ -29,7 +29,8 @@
  *    the weight's format: either x_dtype or RMSN_F32.  rrms and dw are
  *    always float32.
  *  - M == 0 is valid and enqueues nothing (after the other arguments pass
- *    validation).
+ *    validation), except that rmsnorm_bwd with dw != NULL writes dw = 0,
+ *    the sum over zero rows.
  *  - An output may be the very same buffer as an input of the same shape
  *    (same pointer and same stride; e.g. y == x): every element is read
  *    before it is written.  Any other overlap between an output and another
@@ -111,8 +112,10 @@ rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, const void *
 
 /*
  * Bytes of device workspace rmsnorm_bwd needs for (M, H) when a weight
- * gradient is requested (0 when M <= 0 or H <= 0).  The value depends only on
- * M and H, never on the device, so it can be sized once per shape.
+ * gradient is requested (0 when M <= 0 or H <= 0): min(M, Pmax(H)) * H * 4,
+ * where Pmax(H) = clamp(8 MiB / (4 H), 1024, 8192) is the most float32 rows
+ * of partial column sums a call may use.  The value depends only on M and H,
+ * never on the device, so it can be sized once per shape.
  */
 size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t H);
 
@@ -134,7 +137,8 @@ size_t rmsnorm_bwd_workspace_bytes(int64_t M, int64_t H);
  *             skip the weight gradient.  The column sums are reduced in a
  *             fixed order: no atomics, the same bits on every run.
  *   workspace device scratch of at least rmsnorm_bwd_workspace_bytes(M, H)
- *             bytes, 256-byte aligned, when dw != NULL (ignored otherwise).
+ *             bytes, 16-byte aligned (hipMalloc and torch allocations are),
+ *             when dw != NULL (ignored otherwise).
  *             Its contents on entry do not matter; it must not overlap any
  *             other argument, and it must not be used by another call that
  *             may run at the same time.

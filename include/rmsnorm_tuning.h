@@ -24,8 +24,10 @@ extern "C" {
  *            grid > 0 caps the number of workgroups (they then walk the rows
  *            grid-stride), 0 = one workgroup per group of rows.
  * which = 1: backward.  vpt and wpr as above (one row per workgroup at a
- *            time); third = number of workgroups P, each owning a contiguous
- *            block of rows and one row of dw partial sums (0 = default).
+ *            time); third = number of workgroups P, each owning one row of
+ *            dw partial sums (0 = default); grid selects which rows a
+ *            workgroup owns: 0 = default, 1 = interleaved (b, b+P, ...),
+ *            2 = a contiguous block.
  * vpt <= 0 or wpr <= 0 clears the override.  A tile too small for the row
  * takes the two-pass path, which requires vpt = 4 (8 for single elements).
  * An override the shape cannot use makes the call fail with

@@ -224,7 +224,9 @@ def test_forced_fwd_geometry(geom, stream):
     G.assert_ok(*reps)
 
 
-BWD_GEOMS = [(1, 8, 0), (2, 4, 0), (4, 2, 0), (2, 4, 1), (2, 4, 7), (2, 4, 300), (4, 1, 16), (4, 2, 3)]
+# (vpt, wpr, P, row order: 0 default, 1 interleaved, 2 contiguous blocks)
+BWD_GEOMS = [(1, 8, 0, 0), (2, 4, 0, 0), (4, 2, 0, 0), (2, 4, 1, 0), (2, 4, 7, 1), (2, 4, 7, 2), (2, 4, 300, 0),
+             (1, 8, 37, 2), (4, 1, 16, 1), (4, 1, 16, 2), (4, 2, 3, 2), (1, 8, 1000, 1)]
 
 
 @pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
@@ -233,7 +235,7 @@ def test_forced_bwd_geometry(geom, stream):
     M, H = 300, 4096
     d = G.inputs(56, M, H, "bf16", dy=True)
     r32 = oracle_rrms32(d["x"], d["w"], 1e-6, "bf16")
-    tn.set_geometry("bwd", geom[0], geom[1], geom[2])
+    tn.set_geometry("bwd", geom[0], geom[1], geom[2], geom[3])
     tn.set_streaming(stream)
     dx, dw = run_bwd(d["dy"], d["x"], d["w"], r32, "bf16")
     G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, dx, dw, "bf16", name=f"bwd {geom}"))

@@ -8,9 +8,9 @@
 //   dx = rrms * g - xn * ((c * (1/H)) * rrms)
 //   dw[j] = sum over rows of dy * xn
 //
-// Kernel 1 (rmsnorm_bwd_kernel): workgroup b owns the contiguous block of
-// rows [b*rows_per_wg, (b+1)*rows_per_wg) and walks it one row at a time with
-// all 64*wpr threads.  The columns a thread owns are fixed (vector v = t +
+// Kernel 1 (rmsnorm_bwd_kernel): workgroup b owns the rows b, b+P, b+2P, ...
+// (or, optionally, a contiguous block of rows) and walks them one row at a
+// time with all 64*wpr threads.  The columns a thread owns are fixed (vector v = t +
 // k*64*wpr), so it keeps the weight and its dw partial sums in registers for
 // the whole block and, at the end, writes its float32 partials to row b of the
 // workspace `partial` (P x H).  Longer rows use two passes: pass 1 forms c,
@@ -39,7 +39,8 @@ struct BwdParams {
     float *partial;      // P x H float32, or null when dw is not wanted
     int64_t dys, xs, dxs;  // row strides, elements
     int64_t M;
-    int64_t rows_per_wg;
+    int64_t rows_per_wg;  // contiguous order: rows of one workgroup
+    int interleave;       // 1: workgroup b owns rows b, b+P, b+2P, ...
     int H;
     int nvec;
     int wpr;
@@ -53,8 +54,19 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     const int row_threads = 64 * p.wpr;  // == blockDim.x
     const int t = threadIdx.x;
     const int wave = t >> 6;
-    const int64_t row0 = (int64_t)blockIdx.x * p.rows_per_wg;
-    const int64_t row1 = row0 + p.rows_per_wg < p.M ? row0 + p.rows_per_wg : p.M;
+    // The workgroup's rows are start + j*step for j = 0 .. nsteps-1: either a
+    // contiguous block, or interleaved with the other workgroups so that the
+    // rows in flight across the GPU at any moment are neighbours in memory.
+    int64_t start, step, nsteps;
+    if (p.interleave) {
+        start = blockIdx.x;
+        step = gridDim.x;
+        nsteps = (p.M - start + step - 1) / step;
+    } else {
+        start = (int64_t)blockIdx.x * p.rows_per_wg;
+        step = 1;
+        nsteps = start + p.rows_per_wg < p.M ? p.rows_per_wg : p.M - start;
+    }
     float *part = p.partial != nullptr ? p.partial + (int64_t)blockIdx.x * p.H : nullptr;
 
     if constexpr (!TWO_PASS) {
@@ -86,16 +98,17 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // rows in chunks of 64: one rrms value per lane for the chunk, loaded
         // before the chunk's row loads so that no wait inside the row loop
         // depends on a load issued after a prefetch
-        for (int64_t base = row0; base < row1; base += 64) {
-            const int64_t cend = base + 64 < row1 ? base + 64 : row1;
-            float rr_lane = (base + lane < cend) ? p.rrms[base + lane] : 0.0f;
+        for (int64_t base = 0; base < nsteps; base += 64) {
+            const int64_t cend = base + 64 < nsteps ? base + 64 : nsteps;
+            float rr_lane = (base + lane < cend) ? p.rrms[start + (base + lane) * step] : 0.0f;
             asm volatile("" : "+v"(rr_lane));  // complete it now, before the row loads
             // Row loads inside the steady-state loop are unconditional, so the
             // compiler can count them in order and wait only for the oldest;
             // vector indices past the row are clamped to its last vector
             // (same addresses within one wave access: no extra traffic) and
             // masked at use.
-            auto load_row = [&](int64_t row, Raw<XDT, VEC> *xd, Raw<XDT, VEC> *dd) {
+            auto load_row = [&](int64_t j, Raw<XDT, VEC> *xd, Raw<XDT, VEC> *dd) {
+                const int64_t row = start + j * step;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int vv = t + k * row_threads;
@@ -104,9 +117,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     dd[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
                 }
             };
-            auto process_row = [&](int64_t row, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr) {
+            auto process_row = [&](int64_t j, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr) {
+                const int64_t row = start + j * step;
                 const float rs = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rr_lane), (int)(row - base)));
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rr_lane), (int)(j - base)));
                 float acc = 0.0f;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
@@ -119,7 +133,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     for (int e = 0; e < VEC; ++e) part = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, part);
                     if (t + k * row_threads < p.nvec) acc += part;
                 }
-                const float c = row_sum(acc, p.wpr, wave, &red[(row - row0) & 1][0]);
+                const float c = row_sum(acc, p.wpr, wave, &red[j & 1][0]);
                 const float s = (c * p.inv_h) * rs;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
@@ -152,7 +166,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             // slot (r - base) % (PF+1) (copying registers whose loads are in
             // flight would wait for them).  It runs while every prefetched row
             // exists, so its loads need no condition.
-            int64_t row = base;
+            int64_t row = base;  // step index
             for (; row + 2 * PF < cend; row += PF + 1) {
 #pragma unroll
                 for (int u = 0; u <= PF; ++u) {
@@ -184,7 +198,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             for (int v = t; v < p.nvec; v += row_threads) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, z);
         }
         int parity = 0;
-        for (int64_t row = row0; row < row1; ++row, parity ^= 1) {
+        for (int64_t j = 0; j < nsteps; ++j, parity ^= 1) {
+            const int64_t row = start + j * step;
             const float rs = p.rrms[row];
             float acc = 0.0f;
             for (int c = 0; c < p.nchunks; ++c) {

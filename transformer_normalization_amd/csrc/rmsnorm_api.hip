@@ -508,11 +508,20 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
                   resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd");
 }
 
-constexpr int64_t kMaxPartials = 1024;
+// Most dw partial rows a backward call may use: 1024, or more for short rows
+// (up to 8 MiB of partial sums, at most 8192 rows).  Depends on H only, so
+// the workspace size is known without a device.
+int64_t max_partials(int64_t H) {
+    int64_t p = (int64_t(8) << 20) / (4 * H);
+    if (p < 1024) p = 1024;
+    if (p > 8192) p = 8192;
+    return p;
+}
 
 size_t bwd_workspace(int64_t M, int64_t H) {
     if (M <= 0 || H <= 0 || H > kMaxH) return 0;
-    const int64_t P = M < kMaxPartials ? M : kMaxPartials;
+    const int64_t cap = max_partials(H);
+    const int64_t P = M < cap ? M : cap;
     return (size_t)P * (size_t)H * sizeof(float);
 }
 
@@ -574,6 +583,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
                         (w == nullptr || aligned16(w));
     Geom g = pick_row_geom(Kind::Bwd, (int)H, vec_ok ? vecw : 1, 8);
     int64_t P = 0;  // 0: chosen from the device below
+    // rows interleaved across workgroups: the rows in flight at any moment are
+    // neighbours in memory, as in the forward's one-row-per-workgroup grid
+    bool interleave = true;
     const Override ov = get_override(1);
     if (ov.set) {
         Geom o = g;
@@ -589,17 +601,21 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
             return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
         g = o;
         if (ov.c > 0) P = ov.c;
+        if (ov.d == 1) interleave = true;
+        if (ov.d == 2) interleave = false;
     }
     const bool nt = use_streaming(3 * M * H * eb);
     bwd_fn fn = bwd_lookup(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
-    // four workgroups per CU: on gfx950 the row loop gains more from the extra
-    // rows in flight than the dw partial sums (P x H x 4 bytes, written and
-    // read once) cost
-    if (P <= 0) P = 4 * (int64_t)cus;
-    if (P > kMaxPartials) P = kMaxPartials;
+    // About 12 waves per CU with whole workgroups (one 12-wave workgroup per CU
+    // at H = 6144 bf16), rows interleaved: measured fastest on gfx950 for the
+    // row loop, and it keeps the dw partial sums (P x H x 4 bytes, written and
+    // read once) near the minimum that fills the device.  A grid that is not
+    // a multiple of the CU count leaves a tail of CUs with an extra block.
+    if (P <= 0) P = (int64_t)cus * (g.wpr >= 12 ? 1 : 12 / g.wpr);
+    if (P > max_partials(H)) P = max_partials(H);
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;
     P = (M + rows_per - 1) / rows_per;
@@ -616,6 +632,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     p.dxs = dxs;
     p.M = M;
     p.rows_per_wg = rows_per;
+    p.interleave = interleave ? 1 : 0;
     p.H = (int)H;
     p.nvec = g.nvec;
     p.wpr = g.wpr;

@@ -35,9 +35,9 @@ ROTATION_BYTES = 1 << 30
 
 
 KERNEL_SOURCES = {
-    "fwd": ("numerics.hpp", "fwd_kernels.hpp", "rmsnorm_api.hip"),
-    "fwd_residual": ("numerics.hpp", "fwd_kernels.hpp", "rmsnorm_api.hip"),
-    "bwd": ("numerics.hpp", "bwd_kernels.hpp", "rmsnorm_api.hip"),
+    "fwd": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd.hip", "rmsnorm_api.hip"),
+    "fwd_residual": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd_residual.hip", "rmsnorm_api.hip"),
+    "bwd": ("numerics.hpp", "bwd_kernels.hpp", "kernels_bwd.hip", "rmsnorm_api.hip"),
 }
 
 

@@ -266,33 +266,6 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 // order.  The order is fixed, so dw has the same bits on every run.
 constexpr int kFinCols = 64;
 constexpr int kFinSlices = 16;
-
-__global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restrict__ partial, int P, int H,
-                                                            float *__restrict__ dw) {
-    __shared__ float sums[kFinSlices][kFinCols];
-    const int c = threadIdx.x % kFinCols;
-    const int s = threadIdx.x / kFinCols;
-    const int col = blockIdx.x * kFinCols + c;
-    float acc = 0.0f;
-    if (col < H) {
-        int q = s;
-        for (; q + kFinSlices * 7 < P; q += kFinSlices * 8) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(q + kFinSlices * j) * H + col];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc += v[j];
-        }
-        for (; q < P; q += kFinSlices) acc += partial[(int64_t)q * H + col];
-    }
-    sums[s][c] = acc;
-    __syncthreads();
-    if (s == 0 && col < H) {
-        float tot = sums[0][c];
-#pragma unroll
-        for (int i = 1; i < kFinSlices; ++i) tot += sums[i][c];
-        dw[col] = tot;
-    }
-}
+// (defined in kernels_bwd.hip)
 
 }  // namespace rmsn

@@ -17,8 +17,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "bwd_kernels.hpp"
-#include "fwd_kernels.hpp"
+#include "kernel_tables.hpp"
 #include "rmsnorm.h"
 #include "rmsnorm_tuning.h"
 
@@ -286,109 +285,6 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
 // kernel tables
 // ---------------------------------------------------------------------------
 
-typedef void (*fwd_fn)(const FwdParams);
-typedef void (*bwd_fn)(const BwdParams);
-
-template <int XDT, int WDT, int VEC, bool RESID, bool NT>
-fwd_fn fwd_kernel_for(int vpt, bool two_pass) {
-    if (two_pass) {
-        constexpr int V = VEC > 1 ? 4 : 8;
-        return rmsnorm_fwd_kernel<XDT, WDT, VEC, V, RESID, true, NT, 1024>;
-    }
-    switch (vpt) {
-    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, RESID, false, NT, fwd_max_threads(1 * VEC, RESID)>;
-    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, RESID, false, NT, fwd_max_threads(2 * VEC, RESID)>;
-    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, RESID, false, NT, fwd_max_threads(4 * VEC, RESID)>;
-    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, RESID, false, NT, fwd_max_threads(8 * VEC, RESID)>;
-    default: break;
-    }
-    if constexpr (VEC > 1) {
-        switch (vpt) {
-        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, RESID, false, NT, fwd_max_threads(3 * VEC, RESID)>;
-        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, RESID, false, NT, fwd_max_threads(6 * VEC, RESID)>;
-        default: break;
-        }
-    }
-    return nullptr;
-}
-
-template <int XDT, int WDT, bool RESID, bool NT>
-fwd_fn fwd_kernel_vec(int vec, int vpt, bool two_pass) {
-    constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? fwd_kernel_for<XDT, WDT, 1, RESID, NT>(vpt, two_pass)
-                    : fwd_kernel_for<XDT, WDT, V, RESID, NT>(vpt, two_pass);
-}
-
-template <bool RESID, bool NT>
-fwd_fn fwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
-    const bool wf32 = (wdt == RMSN_F32);
-    switch (xdt) {
-    case RMSN_F32: return fwd_kernel_vec<DT_F32, DT_F32, RESID, NT>(vec, vpt, two_pass);
-    case RMSN_F16:
-        return wf32 ? fwd_kernel_vec<DT_F16, DT_F32, RESID, NT>(vec, vpt, two_pass)
-                    : fwd_kernel_vec<DT_F16, DT_F16, RESID, NT>(vec, vpt, two_pass);
-    case RMSN_BF16:
-        return wf32 ? fwd_kernel_vec<DT_BF16, DT_F32, RESID, NT>(vec, vpt, two_pass)
-                    : fwd_kernel_vec<DT_BF16, DT_BF16, RESID, NT>(vec, vpt, two_pass);
-    }
-    return nullptr;
-}
-
-template <bool RESID>
-fwd_fn fwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
-    return nt ? fwd_lookup_nt<RESID, true>(xdt, wdt, vec, vpt, two_pass)
-              : fwd_lookup_nt<RESID, false>(xdt, wdt, vec, vpt, two_pass);
-}
-
-template <int XDT, int WDT, int VEC, bool NT>
-bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
-    if (two_pass) {
-        constexpr int V = VEC > 1 ? 4 : 8;
-        return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, true, NT, 1024>;
-    }
-    switch (vpt) {
-    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, false, NT, bwd_max_threads(1 * VEC)>;
-    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, false, NT, bwd_max_threads(2 * VEC)>;
-    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, false, NT, bwd_max_threads(4 * VEC)>;
-    default: break;
-    }
-    if constexpr (VEC == 1) {
-        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, false, NT, bwd_max_threads(8 * VEC)>;
-    }
-    if constexpr (VEC > 1) {
-        switch (vpt) {
-        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, NT, bwd_max_threads(3 * VEC)>;
-        default: break;
-        }
-    }
-    return nullptr;
-}
-
-template <int XDT, int WDT, bool NT>
-bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass) {
-    constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1, NT>(vpt, two_pass) : bwd_kernel_for<XDT, WDT, V, NT>(vpt, two_pass);
-}
-
-template <bool NT>
-bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
-    const bool wf32 = (wdt == RMSN_F32);
-    switch (xdt) {
-    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32, NT>(vec, vpt, two_pass);
-    case RMSN_F16:
-        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_F16, DT_F16, NT>(vec, vpt, two_pass);
-    case RMSN_BF16:
-        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_BF16, DT_BF16, NT>(vec, vpt, two_pass);
-    }
-    return nullptr;
-}
-
-bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
-    return nt ? bwd_lookup_nt<true>(xdt, wdt, vec, vpt, two_pass) : bwd_lookup_nt<false>(xdt, wdt, vec, vpt, two_pass);
-}
-
 // Streaming (non-temporal) accesses pay off when a call moves more data than
 // the caches could usefully keep for the next kernel; below that, ordinary
 // cached accesses leave the outputs in L2 / the last-level cache for the
@@ -477,8 +373,8 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
     const int64_t iters = (groups + grid - 1) / grid;
 
     const bool nt = use_streaming((resid ? (ro ? 4 : 3) : 2) * M * H * eb);
-    fwd_fn fn = resid ? fwd_lookup<true>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
-                      : fwd_lookup<false>(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
+    fwd_fn fn = resid ? fwd_lookup_resid(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
+                      : fwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -573,7 +469,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *none = nullptr;
         int P = 0, Hi = (int)H;
         void *args[] = {(void *)&none, &P, &Hi, &dw};
-        return launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), args,
+        return launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), args,
                       stream, "rmsnorm_dw_finalize");
     }
 
@@ -645,7 +541,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *part = p.partial;
         int Pi = (int)P, Hi = (int)H;
         void *fargs[] = {(void *)&part, &Pi, &Hi, &dw};
-        if ((st = launch((const void *)rmsnorm_dw_finalize, dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), fargs,
+        if ((st = launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), fargs,
                          stream, "rmsnorm_dw_finalize")) != RMSN_OK)
             return st;
     }

@@ -75,7 +75,9 @@ class Oracle:
         lib.orc_fwd.argtypes = [vp, i64, vp, i32, i32, i64, i64, dp, vp, vp]
         lib.orc_fwd_residual.argtypes = [vp, i64, vp, i64, vp, i32, i32, i64, i64, dp, vp, vp, vp]
         lib.orc_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
-        for f in (lib.orc_decode, lib.orc_encode, lib.orc_fwd, lib.orc_fwd_residual, lib.orc_bwd):
+        lib.orc_adaln_fwd.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i32, i32, i64, i64, dp, vp, vp]
+        for f in (lib.orc_decode, lib.orc_encode, lib.orc_fwd, lib.orc_fwd_residual, lib.orc_bwd,
+                  lib.orc_adaln_fwd):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -150,6 +152,30 @@ class Oracle:
         return dx, dw, terms
 
 
+    def adaln_fwd(self, x, w, scale, shift, rows_per_cond: int, eps: float, dtype: str,
+                  wdtype: str | None = None, cdtype: str | None = None):
+        """-> (y float64 (M, H), rrms float64 (M,)).  scale and shift are
+        (ceil(M / rows_per_cond), H); row i uses conditioning row i // rows_per_cond."""
+        x, xs = _rows(x, dtype)
+        sc, css = _rows(scale, cdtype or dtype)
+        sh, chs = _rows(shift, cdtype or dtype)
+        M, H = x.shape
+        if sc.shape != sh.shape or sc.shape[1] != H or sc.shape[0] * rows_per_cond < M:
+            raise ValueError("scale/shift must be (ceil(M / rows_per_cond), H)")
+        if css != chs:
+            sc, sh = np.ascontiguousarray(sc), np.ascontiguousarray(sh)
+            css = H
+        wv = None if w is None else _vec(w, wdtype or dtype)
+        y = np.empty((M, H), dtype=np.float64)
+        r = np.empty(M, dtype=np.float64)
+        rc = self.lib.orc_adaln_fwd(_ptr(x), xs, _ptr(wv), _ptr(sc), _ptr(sh), css, int(rows_per_cond),
+                                    CODES[dtype], CODES[wdtype or dtype], CODES[cdtype or dtype], M, H, float(eps),
+                                    _ptr(y), _ptr(r))
+        if rc != 0:
+            raise ValueError("orc_adaln_fwd rejected its arguments")
+        return y, r
+
+
 def default() -> Oracle:
     """The oracle built from rmsnorm_oracle.c (rebuilt when the source is newer)."""
     global _default
@@ -179,3 +205,7 @@ def fwd_residual(x, res, w, eps, dtype, wdtype=None):
 
 def bwd(dy, x, w, rrms, dtype, wdtype=None, want_dw=True):
     return default().bwd(dy, x, w, rrms, dtype, wdtype, want_dw)
+
+
+def adaln_fwd(x, w, scale, shift, rows_per_cond, eps, dtype, wdtype=None, cdtype=None):
+    return default().adaln_fwd(x, w, scale, shift, rows_per_cond, eps, dtype, wdtype, cdtype)

@@ -22,6 +22,9 @@
  *   - The weightless form (no weight, LTX-Video's elementwise_affine=False)
  *     is the page "rocm-kernels" (skillselion.com), "Core Kernel
  *     Implementations", RMSNorm: out = x * rms_inv when there is no weight.
+ *   - AdaLN: the same page, "Core Kernel Implementations", 4. AdaLN, and its
+ *     "Template 4": norm(x) * weight * (1 + scale) + shift, with scale and
+ *     shift one row per token ([B, S, H]) or one row per batch ([B, 1, H]).
  *
  * Everything is computed in IEEE float64 from exactly decoded inputs, one row
  * at a time, in the plain left-to-right order of the definition.  Rounding to
@@ -248,6 +251,37 @@ int orc_bwd(const void *dy, int64_t dy_stride, const void *x, int64_t x_stride,
             dx[i * H + j] = t1 - t2;
             if (dx_terms) dx_terms[i * H + j] = fabs(t1) + fabs(t2);
             if (dw) dw[j] += dyv * xn;
+        }
+    }
+    return 0;
+}
+
+/* ---- AdaLN-RMSNorm --------------------------------------------------------
+ * y_ij = x_ij * rrms_i * w_j * (1 + scale_cj) + shift_cj, with c = i / rows_per_cond
+ * (rows_per_cond = 1: one conditioning row per row; = S: one per batch of S
+ * rows).  scale and shift rows are cond_stride elements apart, in c_dt.
+ */
+int orc_adaln_fwd(const void *x, int64_t x_stride, const void *w, const void *scale, const void *shift,
+                  int64_t cond_stride, int64_t rows_per_cond, int x_dt, int w_dt, int c_dt, int64_t M, int64_t H,
+                  double eps, double *y, double *rrms) {
+    if (!orc_valid_code(x_dt) || !orc_valid_code(c_dt) || (w && !orc_valid_code(w_dt))) return -1;
+    if (M < 0 || H < 1 || x_stride < H || cond_stride < H || rows_per_cond < 1 || !(eps > 0.0)) return -1;
+    if (M > 0 && (!x || !y || !scale || !shift)) return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = load_elem(x, x_dt, i * x_stride + j);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        if (rrms) rrms[i] = r;
+        const int64_t c = i / rows_per_cond;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = load_elem(x, x_dt, i * x_stride + j);
+            double wj = w ? load_elem(w, w_dt, j) : 1.0;
+            double sc = load_elem(scale, c_dt, c * cond_stride + j);
+            double sh = load_elem(shift, c_dt, c * cond_stride + j);
+            y[i * H + j] = v * r * wj * (1.0 + sc) + sh;
         }
     }
     return 0;

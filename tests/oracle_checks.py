@@ -462,6 +462,84 @@ def check_bwd_linearity_and_rows(o):
     assert np.array_equal(a_row[0], a1[2])
 
 
+# ---------------------------------------------------------------------------
+# AdaLN
+# ---------------------------------------------------------------------------
+
+def check_adaln_exact_case(o):
+    # x = [6, 8], eps = 14 -> rrms = 1/8, xn = [3/4, 1]; w = 1;
+    # y = xn * (1 + scale) + shift with scale = [1, -1/2], shift = [1/4, 2]
+    x = np.array([[6.0, 8.0]], dtype=np.float32)
+    sc = np.array([[1.0, -0.5]], dtype=np.float32)
+    sh = np.array([[0.25, 2.0]], dtype=np.float32)
+    y, r = o.adaln_fwd(x, np.ones(2, np.float32), sc, sh, 1, 14.0, "f32")
+    assert r[0] == 0.125 and np.array_equal(y[0], np.array([1.75, 2.5]))
+
+
+def check_adaln_reduces_to_rmsnorm(o):
+    rng = _rng(20)
+    M, H = 6, 40
+    for dt in ("bf16", "f16", "f32"):
+        x = _storage(_round_like(rng.standard_normal((M, H)), dt), dt)
+        w = _storage(_round_like(rng.uniform(0.5, 1.5, H), dt), dt)
+        zeros = _storage(np.zeros((M, H)), dt)
+        y0, r0 = o.fwd(x, w, 1e-5, dt)
+        # zero conditioning is the plain norm, exactly
+        y, r = o.adaln_fwd(x, w, zeros, zeros, 1, 1e-5, dt)
+        assert np.array_equal(y, y0) and np.array_equal(r, r0)
+        # scale = -1 leaves the shift alone, exactly
+        sh = _storage(_round_like(rng.standard_normal((M, H)), dt), dt)
+        minus1 = _storage(-np.ones((M, H)), dt)
+        y, _ = o.adaln_fwd(x, w, minus1, sh, 1, 1e-5, dt)
+        shv = _bf16_values(sh) if dt == "bf16" else sh.astype(np.float64)
+        assert np.array_equal(y, shv)
+        # y - shift = (plain norm) * (1 + scale)
+        sc = _storage(_round_like(rng.standard_normal((M, H)) * 0.3, dt), dt)
+        scv = _bf16_values(sc) if dt == "bf16" else sc.astype(np.float64)
+        y, _ = o.adaln_fwd(x, w, sc, sh, 1, 1e-5, dt)
+        assert np.allclose(y - shv, y0 * (1.0 + scv), rtol=1e-12, atol=1e-14)
+
+
+def check_adaln_broadcast_rows(o):
+    # one conditioning row per batch of S rows equals that row repeated S times
+    rng = _rng(21)
+    B, S, H = 3, 5, 24
+    x = _storage(_round_like(rng.standard_normal((B * S, H)), "bf16"), "bf16")
+    w = _storage(_round_like(rng.uniform(0.5, 1.5, H), "bf16"), "bf16")
+    sc = _storage(_round_like(rng.standard_normal((B, H)) * 0.2, "bf16"), "bf16")
+    sh = _storage(_round_like(rng.standard_normal((B, H)) * 0.2, "bf16"), "bf16")
+    yb, rb = o.adaln_fwd(x, w, sc, sh, S, 1e-6, "bf16")
+    yf, rf = o.adaln_fwd(x, w, np.repeat(sc, S, axis=0), np.repeat(sh, S, axis=0), 1, 1e-6, "bf16")
+    assert np.array_equal(yb, yf) and np.array_equal(rb, rf)
+    # the conditioning row is chosen by batch: a change in batch 1's row moves
+    # only rows S..2S-1
+    sc2 = sc.copy()
+    sc2[1] = _storage(_round_like(rng.standard_normal(H), "bf16"), "bf16")
+    y2, _ = o.adaln_fwd(x, w, sc2, sh, S, 1e-6, "bf16")
+    changed = np.any(y2 != yb, axis=1)
+    assert np.array_equal(changed, np.repeat([False, True, False], S))
+
+
+def check_adaln_decimal(o):
+    getcontext().prec = 60
+    rng = _rng(22)
+    H = 3
+    x = _round_like(rng.standard_normal((2, H)), "f32")
+    w = _round_like(rng.uniform(0.5, 1.5, H), "f32")
+    sc = _round_like(rng.standard_normal((2, H)), "f32")
+    sh = _round_like(rng.standard_normal((2, H)), "f32")
+    y, _ = o.adaln_fwd(x.astype(np.float32), w.astype(np.float32), sc.astype(np.float32), sh.astype(np.float32),
+                       1, 1e-5, "f32")
+    for i in range(2):
+        ss = sum(Decimal(float(v)) ** 2 for v in x[i])
+        r = 1 / (ss / H + Decimal(float(np.float32(1e-5)))).sqrt()
+        for j in range(H):
+            t = Decimal(float(x[i, j])) * r * Decimal(float(w[j])) * (1 + Decimal(float(sc[i, j])))
+            e = t + Decimal(float(sh[i, j]))
+            # float64 rounding is relative to the terms, which may cancel
+            assert abs(Decimal(float(y[i, j])) - e) <= (abs(t) + abs(Decimal(float(sh[i, j])))) * Decimal("1e-15")
+
+
 ALL_CHECKS = [
     check_decode_all_16bit_patterns,
     check_encode_matches_libraries,
@@ -481,4 +559,8 @@ ALL_CHECKS = [
     check_bwd_identities,
     check_bwd_special_cases,
     check_bwd_linearity_and_rows,
+    check_adaln_exact_case,
+    check_adaln_reduces_to_rmsnorm,
+    check_adaln_broadcast_rows,
+    check_adaln_decimal,
 ]

@@ -37,6 +37,13 @@ MUTANTS = [
     ("bwd_dw_uses_x_not_xn", "if (dw) dw[j] += dyv * xn;", "if (dw) dw[j] += dyv * xv;", 0),
     ("bwd_dw_includes_weight", "if (dw) dw[j] += dyv * xn;", "if (dw) dw[j] += g * xn;", 0),
     ("bwd_extra_rrms", "double t1 = r * g;", "double t1 = r * r * g;", 0),
+    ("adaln_scale_without_one", "double sc = load_elem(scale, c_dt, c * cond_stride + j);",
+     "double sc = load_elem(scale, c_dt, c * cond_stride + j) - 1.0;", 0),
+    ("adaln_scale_shift_swapped", "y[i * H + j] = v * r * wj * (1.0 + sc) + sh;",
+     "y[i * H + j] = v * r * wj * (1.0 + sh) + sc;", 0),
+    ("adaln_shift_inside", "y[i * H + j] = v * r * wj * (1.0 + sc) + sh;",
+     "y[i * H + j] = v * r * (wj * (1.0 + sc) + sh);", 0),
+    ("adaln_cond_row_per_row", "const int64_t c = i / rows_per_cond;", "const int64_t c = i % rows_per_cond;", 0),
     ("round_half_away", "double q = rint(a / quantum);", "double q = round(a / quantum);", 0),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);", 0),
     ("f16_no_subnormal_quantum", "if (lead < emin) lead = emin;", "if (lead < emin - 30) lead = emin - 30;", 0),

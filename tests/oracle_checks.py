@@ -532,7 +532,7 @@ def check_adaln_decimal(o):
                        1, 1e-5, "f32")
     for i in range(2):
         ss = sum(Decimal(float(v)) ** 2 for v in x[i])
-        r = 1 / (ss / H + Decimal(float(np.float32(1e-5)))).sqrt()
+        r = 1 / (ss / H + Decimal(1e-5)).sqrt()  # the oracle was given the float64 1e-5
         for j in range(H):
             t = Decimal(float(x[i, j])) * r * Decimal(float(w[j])) * (1 + Decimal(float(sc[i, j])))
             e = t + Decimal(float(sh[i, j]))

@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "fwd": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd.hip", "rmsnorm_api.hip"),
     "fwd_residual": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd_residual.hip", "rmsnorm_api.hip"),
     "bwd": ("numerics.hpp", "bwd_kernels.hpp", "kernels_bwd.hip", "rmsnorm_api.hip"),
+    "adaln": ("numerics.hpp", "fwd_kernels.hpp", "kernels_adaln.hip", "rmsnorm_api.hip"),
 }
 
 
@@ -74,7 +75,7 @@ def stored_traffic(workload: str):
         return None
 
 
-def algorithmic_bytes(kind, M, H, esize, wsize, weighted):
+def algorithmic_bytes(kind, M, H, esize, wsize, weighted, cond_rows=0):
     """Bytes the method must move once: inputs, weight, outputs, rrms if used."""
     mat = M * H * esize
     w = H * wsize if weighted else 0
@@ -85,6 +86,9 @@ def algorithmic_bytes(kind, M, H, esize, wsize, weighted):
     if kind == "bwd":
         # x, dy read; dx written; rrms read; w read; dw written (float32)
         return 3 * mat + M * 4 + w + H * 4
+    if kind == "adaln":
+        # x read, y written, w and the scale/shift rows read once
+        return 2 * mat + w + 2 * cond_rows * H * wsize
     raise ValueError(kind)
 
 
@@ -96,6 +100,8 @@ WORKLOADS = {
     "fwd_f16_32768x2048_outliers": ("fwd_f16_32768x2048_outliers", True),
     "fwd_residual_bf16_16384x8192": ("fwd_residual_bf16_16384x8192", True),
     "bwd_bf16_8192x6144": ("bwd_bf16_8192x6144", True),
+    "adaln_bf16_2x4096x2048_batchcond": ("adaln_bf16_2x4096x2048_batchcond", True),
+    "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
 }
 
 
@@ -120,6 +126,9 @@ def cpu_baseline(spec, kind, weighted, seconds):
     while True:
         if kind == "fwd":
             oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
+        elif kind == "adaln":
+            oracle.adaln_fwd(d["x"], w, d["scale"], d["shift"], d["rows_per_cond"], eps, d["dtype"], d["wdtype"],
+                             d["wdtype"])
         elif kind == "fwd_residual":
             oracle.fwd_residual(d["x"], d["r"], w, eps, d["dtype"], d["wdtype"])
         else:
@@ -130,7 +139,8 @@ def cpu_baseline(spec, kind, weighted, seconds):
             break
     es = synthetic.element_size(d["dtype"])
     ws = synthetic.element_size(d["wdtype"])
-    nbytes = algorithmic_bytes(kind, rows, spec["H"], es, ws, weighted) * passes
+    crows = d["scale"].shape[0] if kind == "adaln" else 0
+    nbytes = algorithmic_bytes(kind, rows, spec["H"], es, ws, weighted, crows) * passes
     return {
         "value": round(nbytes / el / 1e9, 4),
         "unit": "GB/s",
@@ -156,7 +166,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     es = synthetic.element_size(spec["dtype"])
     ws = synthetic.element_size(spec["wdtype"])
     known_kib = spec["M"] * spec["H"] * es / 1024.0
-    kernel_key = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel",
+    kernel_key = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
                   "bwd": "rmsnorm_bwd_kernel"}[spec["kind"]]
 
     def read(path, counter):
@@ -173,7 +183,8 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     w_k, w_n, w_ref, w_rn, _ = read(write_csv, "WRITE_SIZE")
     f_scale, w_scale = known_kib / f_ref, known_kib / w_ref
     hbm = (f_k * f_scale + w_k * w_scale) * 1024.0
-    alg = algorithmic_bytes(spec["kind"], spec["M"], spec["H"], es, ws, weighted)
+    crows = -(-spec["M"] // spec.get("rows_per_cond", 1)) if spec["kind"] == "adaln" else 0
+    alg = algorithmic_bytes(spec["kind"], spec["M"], spec["H"], es, ws, weighted, crows)
     lines = [
         f"# HBM traffic per launch of {kname}",
         f"# workload {workload}: M={spec['M']} H={spec['H']} {spec['dtype']}",
@@ -254,7 +265,8 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    per_set = algorithmic_bytes(kind, M, H, es, ws, weighted)
+    crows = d["scale"].shape[0] if kind == "adaln" else 0
+    per_set = algorithmic_bytes(kind, M, H, es, ws, weighted, crows)
     nsets = max(2, -(-ROTATION_BYTES // per_set))
     x0 = up(d["x"], dt)
     w = up(d["w"], d["wdtype"]) if weighted else None
@@ -267,6 +279,12 @@ def main():
         if kind == "bwd":
             dy0 = up(d["dy"], dt) if i == 0 else sets[0]["dy"].clone()
             s.update(dy=dy0)
+        if kind == "adaln":
+            rpc = spec["rows_per_cond"]
+            shape = (M // rpc, 1, H) if rpc > 1 else (1, M, H)
+            sc0 = up(d["scale"], d["wdtype"]).view(*shape) if i == 0 else sets[0]["scale"].clone()
+            sh0 = up(d["shift"], d["wdtype"]).view(*shape) if i == 0 else sets[0]["shift"].clone()
+            s.update(scale=sc0, shift=sh0, x=s["x"].view(shape[0], -1, H), y=s["y"].view(shape[0], -1, H))
         sets.append(s)
     del d
     eps = spec["eps"]
@@ -283,6 +301,8 @@ def main():
             tn.rmsnorm_fwd(s["x"], w, eps, out=s["y"])
         elif kind == "fwd_residual":
             tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
+        elif kind == "adaln":
+            tn.rmsnorm_adaln_fwd(s["x"], w, s["scale"], s["shift"], eps, out=s["y"])
         else:
             tn.rmsnorm_bwd(s["dy"], s["x"], w, rr, dx=s["y"], dw=dw, workspace=wsp)
 

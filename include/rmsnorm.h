@@ -111,6 +111,30 @@ rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, const void *
                                    rmsn_dtype_t w_dtype, hipStream_t stream);
 
 /*
+ * AdaLN-RMSNorm, the DiT conditioning step fused with the norm ("rocm-kernels",
+ * "Core Kernel Implementations", 4. AdaLN, and "Triton kernel templates",
+ * Template 4: norm(x) * weight * (1 + scale) + shift):
+ *
+ *   y[i, j] = (x[i, j] * rrms[i]) * w[j] * (1 + scale[c, j]) + shift[c, j],
+ *   c = i / rows_per_cond
+ *
+ * rows_per_cond = 1 gives one conditioning row per row ([B, S, H] scale and
+ * shift); rows_per_cond = S gives one per batch of S rows ([B, 1, H]).
+ *
+ *   scale, shift  (ceil(M / rows_per_cond), H), rows cond_stride elements
+ *                 apart (both tensors share the stride, as when they are two
+ *                 slices of one modulation tensor).
+ *   w             (H,) weight or NULL.
+ *   param_dtype   format of w, scale and shift: x_dtype or RMSN_F32.
+ *   x, y, rrms, eps, M, H  as rmsnorm_fwd; the product with (1 + scale) and
+ *                 the addition of shift are one float32 fused multiply-add.
+ */
+rmsn_status_t rmsnorm_adaln_fwd(const void *x, int64_t x_stride, const void *w, const void *scale,
+                                const void *shift, int64_t cond_stride, int64_t rows_per_cond, void *y,
+                                int64_t y_stride, float *rrms, int64_t M, int64_t H, float eps,
+                                rmsn_dtype_t x_dtype, rmsn_dtype_t param_dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace rmsnorm_bwd needs for (M, H) when a weight
  * gradient is requested (0 when M <= 0 or H <= 0): min(M, Pmax(H)) * H * 4,
  * where Pmax(H) = clamp(8 MiB / (4 H), 1024, 8192) is the most float32 rows

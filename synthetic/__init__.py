@@ -17,7 +17,7 @@ Generator (a reading: the pages name no seeds and no generator), in _gen.c:
     harmless because float32 keeps 24 >= 2*8 + 2 significand bits.
 
 Stream ids: x = 0, weight = 1, residual = 2, upstream gradient = 3,
-outlier mask = 4, outlier value = 5.
+outlier mask = 4, outlier value = 5, AdaLN scale = 6, AdaLN shift = 7.
 """
 
 from __future__ import annotations
@@ -35,6 +35,8 @@ STREAM_RESIDUAL = 2
 STREAM_DY = 3
 STREAM_OUTLIER_MASK = 4
 STREAM_OUTLIER_VALUE = 5
+STREAM_SCALE = 6
+STREAM_SHIFT = 7
 
 # Storage formats, by name.  "bf16" arrays are returned as uint16 bit patterns.
 DTYPES = ("f32", "f16", "bf16")
@@ -156,6 +158,14 @@ WORKLOADS = {
                                          x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1004),
     "bwd_bf16_8192x6144": dict(kind="bwd", M=8192, H=6144, dtype="bf16", wdtype="bf16",
                                x=(0.0, 1.0), w=(1.0, 0.1), dy=(0.0, 1.0), eps=1e-6, seed=1005),
+    # DiT-style AdaLN on 2 x 4096 tokens of width 2048 (LTX-Video's hidden
+    # size); scale/shift per batch ([B, 1, H]) and per token ([B, S, H])
+    "adaln_bf16_2x4096x2048_batchcond": dict(kind="adaln", M=8192, H=2048, dtype="bf16", wdtype="bf16",
+                                             x=(0.0, 1.0), w=(1.0, 0.1), cond=(0.0, 0.5), rows_per_cond=4096,
+                                             eps=1e-6, seed=1006),
+    "adaln_bf16_2x4096x2048_tokencond": dict(kind="adaln", M=8192, H=2048, dtype="bf16", wdtype="bf16",
+                                             x=(0.0, 1.0), w=(1.0, 0.1), cond=(0.0, 0.5), rows_per_cond=1,
+                                             eps=1e-6, seed=1007),
 }
 
 
@@ -179,5 +189,10 @@ def make_inputs(name: str, rows: int | None = None) -> dict:
         out["r"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["r"]), dt).reshape(m, H)
     if "dy" in spec:
         out["dy"] = encode(normal(seed, STREAM_DY, n, *spec["dy"]), dt).reshape(m, H)
+    if "cond" in spec:
+        rpc = spec["rows_per_cond"]
+        C = (M + rpc - 1) // rpc if rows is None else (m + rpc - 1) // rpc
+        out["scale"] = encode(normal(seed, STREAM_SCALE, C * H, *spec["cond"]), wdt).reshape(C, H)
+        out["shift"] = encode(normal(seed, STREAM_SHIFT, C * H, *spec["cond"]), wdt).reshape(C, H)
     return out
 

@@ -75,6 +75,20 @@ int main(void) {
     expect("residual M == 0", rmsnorm_fwd_residual(NULL, H, NULL, H, NULL, NULL, H, NULL, H, NULL, 0, H, 1e-5f,
                                                    RMSN_F16, RMSN_F32, 0), RMSN_OK);
 
+    void *sc = (void *)(uintptr_t)0x800000000ull, *sh = (void *)(uintptr_t)0x900000000ull;
+    expect("adaln scale NULL", rmsnorm_adaln_fwd(x, H, w, NULL, sh, H, 1, y, H, rr, M, H, 1e-5f, RMSN_BF16,
+                                                 RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("adaln rows_per_cond 0", rmsnorm_adaln_fwd(x, H, w, sc, sh, H, 0, y, H, rr, M, H, 1e-5f, RMSN_BF16,
+                                                      RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("adaln cond_stride < H", rmsnorm_adaln_fwd(x, H, w, sc, sh, H - 8, 1, y, H, rr, M, H, 1e-5f, RMSN_BF16,
+                                                      RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("adaln param f16 with x bf16", rmsnorm_adaln_fwd(x, H, NULL, sc, sh, H, 1, y, H, rr, M, H, 1e-5f,
+                                                            RMSN_BF16, RMSN_F16, 0), RMSN_ERR_UNSUPPORTED);
+    expect("adaln y overlaps shift", rmsnorm_adaln_fwd(x, H, w, sc, sh, H, 1, (char *)sh + 32, H, rr, M, H, 1e-5f,
+                                                       RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("adaln M == 0", rmsnorm_adaln_fwd(NULL, H, NULL, NULL, NULL, H, 1, NULL, H, NULL, 0, H, 1e-5f, RMSN_BF16,
+                                             RMSN_F32, 0), RMSN_OK);
+
     size_t need = rmsnorm_bwd_workspace_bytes(M, H);
     if (need != (size_t)M * H * 4) { printf("FAIL workspace size %zu\n", need); ++failures; }
     if (rmsnorm_bwd_workspace_bytes(1 << 20, 6144) != (size_t)1024 * 6144 * 4) {

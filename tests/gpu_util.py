@@ -113,3 +113,28 @@ def inputs(seed, M, H, dtype, wdtype=None, xdist=(0.0, 1.0), weight=True, residu
     if dy:
         d["dy"] = synthetic.normal_tensor(seed, synthetic.STREAM_DY, (M, H), dtype)
     return d
+
+
+def adaln_vs_oracle(x, w, scale, shift, rows_per_cond, y_host, rrms_host, eps, dtype, pdtype=None, chunk=2048,
+                    name="adaln"):
+    M, H = x.shape
+    rep_y, rep_r = parity.Report(f"{name} y"), parity.Report(f"{name} rrms")
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        # conditioning rows of this chunk, re-based so that row r0 maps to 0
+        c0 = r0 // rows_per_cond
+        c1 = (r1 - 1) // rows_per_cond + 1
+        if rows_per_cond > 1 and r0 % rows_per_cond:
+            raise ValueError("chunk must start at a conditioning boundary")
+        yref, rref = oracle.adaln_fwd(x[r0:r1], w, scale[c0:c1], shift[c0:c1], rows_per_cond, eps32(eps), dtype,
+                                      pdtype, pdtype)
+        # y = a + shift may cancel: judge against the size of its two terms,
+        # as for dx (a = norm * w * (1 + scale))
+        shv = oracle.decode(np.repeat(shift[c0:c1], rows_per_cond, axis=0)[: r1 - r0], pdtype or dtype)
+        terms = np.abs(yref - shv) + np.abs(shv)
+        if dtype == "f32":
+            parity.check_dx_f32(rep_y, y_host[r0:r1], yref, terms, r0 * H)
+        else:
+            parity.check_dx16(rep_y, y_host[r0:r1], yref, terms, dtype, oracle.encode, oracle.decode, r0 * H)
+        parity.check_f32(rep_r, rrms_host[r0:r1], rref, r0)
+    return rep_y, rep_r

@@ -13,6 +13,8 @@
     terms = |rrms*g| + |xn*rrms*c/H|.  Evaluating the difference of two terms
     of size T in float32 costs about 4 * 2^-24 * T; 1e-5 * 2^-4 * T is ten
     times that.  (Rows with H = 1 cancel to dx = rrms*g*eps/(x^2+eps).)
+  * AdaLN output y = a + shift (a = norm * w * (1 + scale)) is judged like
+    dx, with terms = |a| + |shift|: the final addition can cancel.
   * dw: |got - ref| <= 1e-3*|ref| + 1e-5 * sum_i |dy*xn| for each column (a
     pure relative bound is ill-posed for columns whose sum crosses zero).
 """

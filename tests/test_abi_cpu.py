@@ -43,7 +43,7 @@ def declared_functions():
 
 def test_headers_declare_the_api():
     names = declared_functions()
-    for n in ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
+    for n in ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_adaln_fwd", "rmsnorm_bwd", "rmsnorm_bwd_workspace_bytes",
               "rmsnorm_status_string", "rmsnorm_last_error", "rmsnorm_tuning_set_geometry",
               "rmsnorm_tuning_set_streaming"):
         assert n in names, n

@@ -9,6 +9,7 @@ functions raise.
     y = rmsnorm_fwd(x, w, eps)                       # w may be None
     y, rrms = rmsnorm_fwd(x, w, eps, return_rrms=True)
     y, res_out = rmsnorm_fwd_residual(x, residual, w, eps)
+    y = rmsnorm_adaln_fwd(x, w, scale, shift, eps)  # scale/shift [B,S,H] or [B,1,H]
     dx, dw = rmsnorm_bwd(dy, x, w, rrms)
 """
 
@@ -24,8 +25,8 @@ LIB_PATH = os.path.join(PKG, "librmsnorm.so")
 RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
 STATUS = {0: "RMSN_OK", 1: "RMSN_ERR_INVALID_ARG", 2: "RMSN_ERR_UNSUPPORTED", 3: "RMSN_ERR_WORKSPACE",
           4: "RMSN_ERR_HIP"}
-EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_bwd_workspace_bytes", "rmsnorm_bwd",
-            "rmsnorm_status_string", "rmsnorm_last_error")
+EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_adaln_fwd", "rmsnorm_bwd_workspace_bytes",
+            "rmsnorm_bwd", "rmsnorm_status_string", "rmsnorm_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -52,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_fwd.restype = i32
         lib.rmsnorm_fwd_residual.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp, i64, i64, f32, i32, i32, vp]
         lib.rmsnorm_fwd_residual.restype = i32
+        lib.rmsnorm_adaln_fwd.argtypes = [vp, i64, vp, vp, vp, i64, i64, vp, i64, vp, i64, i64, f32, i32, i32, vp]
+        lib.rmsnorm_adaln_fwd.restype = i32
         lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
         lib.rmsnorm_bwd_workspace_bytes.restype = sz
         lib.rmsnorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32, i32, vp]
@@ -185,6 +188,52 @@ def rmsnorm_fwd_residual(x, residual, weight=None, eps: float = 1e-6, out=None, 
     _check(lib, st)
     res = (out, residual_out)
     return res + (rrms,) if return_rrms else res
+
+
+def rmsnorm_adaln_fwd(x, weight, scale, shift, eps: float = 1e-6, out=None, rrms=None, return_rrms: bool = False):
+    """AdaLN-RMSNorm: (x * rrms) * weight * (1 + scale) + shift over the last dim.
+
+    x is (..., S, H) or (M, H).  scale and shift are either per row (same
+    leading shape as x, or (M, H)) or per batch ((B, 1, H) for x of shape
+    (B, S, H)); they must share one format (x's or float32, the weight's too)
+    and one row stride, as slices of one modulation tensor do."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if scale.shape != shift.shape:
+        raise ValueError("scale and shift must have the same shape")
+    if scale.dtype != shift.dtype:
+        raise ValueError("scale and shift must have the same dtype")
+    if scale.shape[-1] != H:
+        raise ValueError("scale/shift last dim must be H")
+    if scale.numel() == M * H or (M == 0 and scale.numel() == 0):
+        rows_per_cond = 1
+    elif x.dim() >= 2 and scale.dim() == x.dim() and scale.shape[-2] == 1 and \
+            tuple(scale.shape[:-2]) == tuple(x.shape[:-2]):
+        rows_per_cond = x.shape[-2]
+    else:
+        raise ValueError("scale/shift must be per row (shape of x) or per batch ([..., 1, H])")
+    C, _, cs = _rows(scale, "scale")
+    _, _, hs = _rows(shift, "shift")
+    if C > 1 and cs != hs:
+        raise ValueError("scale and shift must have the same row stride")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    _, _, ys = _rows(out, "out")
+    if return_rrms and rrms is None:
+        rrms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if rrms is not None and (rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous()):
+        raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
+    pcode = _dtype_code(scale)
+    if weight is not None:
+        if weight.numel() != H or not weight.is_contiguous():
+            raise ValueError("weight must be a contiguous tensor of H elements")
+        if weight.dtype != scale.dtype:
+            raise ValueError("weight, scale and shift must share one dtype")
+    st = lib.rmsnorm_adaln_fwd(_ptr(x), xs, _ptr(weight), _ptr(scale), _ptr(shift), cs, rows_per_cond, _ptr(out),
+                               ys, _ptr(rrms), M, H, float(eps), _dtype_code(x), pcode, _stream(x))
+    _check(lib, st)
+    return (out, rrms) if return_rrms else out
 
 
 def rmsnorm_bwd_workspace_bytes(M: int, H: int) -> int:

@@ -6,6 +6,9 @@
 //   h      = float32(x) + float32(r)  (fused residual; r_out = RNE(h))
 //   rrms   = rsqrt(sum(h*h) * (1/H) + eps)     in float32, eps inside the root
 //   y      = (h * rrms) * w                     (w = 1 when weightless)
+//   y      = fma((h * rrms) * w, 1 + scale, shift)   (AdaLN: "rocm-kernels",
+//            "Core Kernel Implementations", 4. AdaLN; scale and shift come from
+//            conditioning row i / rows_per_cond, in the weight's format)
 //
 // Layout of the work on the device:
 //   * A "row group" of 64*wpr threads (wpr whole waves) owns one row at a
@@ -53,10 +56,20 @@ struct FwdParams {
     int nchunks;     // two-pass: chunks of 64*wpr*VPT vectors
     float eps;
     float inv_h;     // float32(1/H)
+    // AdaLN conditioning: scale and shift rows (parameter format), row i uses
+    // conditioning row i / rows_per_cond
+    const void *scale;
+    const void *shift;
+    int64_t cs;            // conditioning row stride, elements
+    int64_t rows_per_cond;
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT>
+enum : int { MODE_PLAIN = 0, MODE_RESID = 1, MODE_ADALN = 2 };
+
+template <int XDT, int WDT, int VEC, int VPT, int MODE, bool TWO_PASS, bool NT, int MAXT>
 __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
+    constexpr bool RESID = MODE == MODE_RESID;
+    constexpr bool ADALN = MODE == MODE_ADALN;
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;
     const int slot = threadIdx.x / row_threads;
@@ -78,11 +91,16 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                 wr[k].fill_one();
         }
 
+        // AdaLN conditioning rows stay in registers while consecutive rows of
+        // this row group use the same one (rows of one batch)
+        Raw<WDT, VEC> scr[ADALN ? VPT : 1], shr[ADALN ? VPT : 1];
+        int64_t have_crow = -1;
         for (int64_t it = 0; it < p.iters; ++it) {
             const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
             const bool valid = row < p.M;
             Raw<XDT, VEC> xr[VPT];
             Raw<XDT, VEC> rr[RESID ? VPT : 1];
+            const int64_t crow = ADALN ? row / p.rows_per_cond : 0;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
@@ -92,6 +110,23 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                 } else {
                     xr[k].zero();
                     if constexpr (RESID) rr[k].zero();
+                }
+            }
+            if constexpr (ADALN) {
+                if (valid && crow != have_crow) {
+#pragma unroll
+                    for (int k = 0; k < VPT; ++k) {
+                        const int v = t + k * row_threads;
+                        if (v < p.nvec) {
+                            // cached: a conditioning row serves rows_per_cond rows
+                            scr[k].load(p.scale, crow * p.cs + (int64_t)v * VEC);
+                            shr[k].load(p.shift, crow * p.cs + (int64_t)v * VEC);
+                        } else {
+                            scr[k].zero();
+                            shr[k].zero();
+                        }
+                    }
+                    have_crow = crow;
                 }
             }
             float acc = 0.0f;
@@ -132,8 +167,16 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                         for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                     }
                     wr[k].widen_to(wv);
+                    if constexpr (ADALN) {
+                        float sc[VEC], sh[VEC];
+                        scr[k].widen_to(sc);
+                        shr[k].widen_to(sh);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                        for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] * rs) * wv[e], 1.0f + sc[e], sh[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                    }
                     store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                 }
             }
@@ -203,8 +246,18 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                             if (p.ro != nullptr) store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
                         }
                         float o[VEC];
+                        if constexpr (ADALN) {
+                            const int64_t crow = row / p.rows_per_cond;
+                            float sc[VEC], sh[VEC];
+                            load_elems<WDT, VEC>(p.scale, crow * p.cs + (int64_t)v * VEC, sc);
+                            load_elems<WDT, VEC>(p.shift, crow * p.cs + (int64_t)v * VEC, sh);
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                            for (int e = 0; e < VEC; ++e)
+                                o[e] = __builtin_fmaf((hv[e] * rs) * wv[e], 1.0f + sc[e], sh[e]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+                        }
                         store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                     }
                 }

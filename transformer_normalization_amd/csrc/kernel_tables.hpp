@@ -1,6 +1,7 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
-// (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_bwd.hip) so that they
+// (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
+// kernels_bwd.hip) so that they
 // compile in parallel; the host code only sees these functions.
 #pragma once
 
@@ -17,6 +18,8 @@ typedef void (*bwd_fn)(const BwdParams);
 // accesses per thread; nt: streaming accesses)
 fwd_fn fwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
+// AdaLN: wdt is the format of the weight, scale and shift
+fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 const void *dw_finalize_kernel();
 

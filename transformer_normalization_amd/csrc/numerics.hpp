@@ -297,8 +297,9 @@ __device__ __forceinline__ float fast_rsqrt(float v) { return __builtin_amdgcn_r
 // waves of a SIMD) to hold the tile without spilling.  The host geometry uses
 // the same functions.  The forward keeps x (and the residual) packed; the
 // backward keeps x, dy and w packed plus float32 dw partial sums.
-constexpr int fwd_max_threads(int elems, bool resid) {
-    return resid ? (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256) : (elems <= 32 ? 1024 : 512);
+constexpr int fwd_max_threads(int elems, int mode) {  // mode: 0 plain, 1 residual, 2 AdaLN
+    return mode == 0 ? (elems <= 32 ? 1024 : 512)
+                     : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);
 }
 constexpr int bwd_max_threads(int elems) { return elems <= 16 ? 1024 : elems <= 32 ? 512 : 256; }
 

@@ -222,13 +222,16 @@ Override get_override(int which) {
 }
 
 // vectors per thread available as kernel instantiations
-enum class Kind { Fwd, FwdResid, Bwd };
+enum class Kind { Fwd, FwdResid, FwdAdaln, Bwd };
 constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
 constexpr int kBwdVecVpt[] = {1, 2, 3, 4};
 constexpr int kScalarVpt[] = {1, 2, 4, 8};
 // largest workgroup each register tile may use (the kernels' launch bounds)
 int max_threads_for(Kind kind, int vpt, int vec) {
-    return kind == Kind::Bwd ? bwd_max_threads(vpt * vec) : fwd_max_threads(vpt * vec, kind == Kind::FwdResid);
+    return kind == Kind::Bwd        ? bwd_max_threads(vpt * vec)
+           : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID)
+           : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN)
+                                    : fwd_max_threads(vpt * vec, MODE_PLAIN);
 }
 
 struct Geom {
@@ -307,10 +310,21 @@ rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStre
 // forward (plain and fused residual)
 // ---------------------------------------------------------------------------
 
-rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int64_t rs, const void *w, void *y,
+// Conditioning rows of an AdaLN call (scale and shift share the layout).
+struct Cond {
+    const void *scale = nullptr;
+    const void *shift = nullptr;
+    int64_t cs = 0;             // row stride, elements
+    int64_t rows_per_cond = 1;  // x rows per conditioning row
+};
+
+// mode: MODE_PLAIN, MODE_RESID or MODE_ADALN.  For AdaLN, wdt is the format of
+// the weight, scale and shift.
+rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64_t rs, const void *w, void *y,
                        int64_t ys, void *ro, int64_t ros, float *rrms, int64_t M, int64_t H, float eps,
-                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
-    rmsn_status_t st = check_common(M, H, xdt, w, wdt);
+                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, const Cond &cond, hipStream_t stream) {
+    const bool resid = mode == MODE_RESID, adaln = mode == MODE_ADALN;
+    rmsn_status_t st = check_common(M, H, xdt, (w || adaln) ? (const void *)1 : nullptr, wdt);
     if (st != RMSN_OK) return st;
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     const int eb = dtype_bytes(xdt);
@@ -320,18 +334,29 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
         if ((st = check_stride("r_stride", rs, M, H, eb)) != RMSN_OK) return st;
         if (ro != nullptr && (st = check_stride("ro_stride", ros, M, H, eb)) != RMSN_OK) return st;
     }
+    int64_t crows = 0;
+    const int pb = dtype_bytes(wdt);
+    if (adaln) {
+        if (cond.rows_per_cond < 1)
+            return fail(RMSN_ERR_INVALID_ARG, "rows_per_cond = %lld must be >= 1", (long long)cond.rows_per_cond);
+        crows = (M + cond.rows_per_cond - 1) / cond.rows_per_cond;
+        if ((st = check_stride("cond_stride", cond.cs, crows, H, pb)) != RMSN_OK) return st;
+    }
     if (M == 0) return RMSN_OK;
     if (x == nullptr) return fail(RMSN_ERR_INVALID_ARG, "x is NULL");
     if (y == nullptr) return fail(RMSN_ERR_INVALID_ARG, "y is NULL");
     if (resid && r == nullptr) return fail(RMSN_ERR_INVALID_ARG, "residual is NULL");
+    if (adaln && (cond.scale == nullptr || cond.shift == nullptr))
+        return fail(RMSN_ERR_INVALID_ARG, "scale and shift must not be NULL");
 
-    const int wb = w ? dtype_bytes(wdt) : 0;
-    Region ins[3] = {mat("x", x, xs, M, H, eb), mat("residual", resid ? r : nullptr, rs, M, H, eb),
-                     vec("w", w, H, wb ? wb : 1)};
+    const int wb = w ? dtype_bytes(wdt) : 1;
+    Region ins[5] = {mat("x", x, xs, M, H, eb), mat("residual", resid ? r : nullptr, rs, M, H, eb),
+                     vec("w", w, H, wb), mat("scale", adaln ? cond.scale : nullptr, cond.cs, crows, H, pb),
+                     mat("shift", adaln ? cond.shift : nullptr, cond.cs, crows, H, pb)};
     Region outs[3] = {mat("y", y, ys, M, H, eb), mat("residual_out", resid ? ro : nullptr, ros, M, H, eb),
                       vec("rrms", rrms, M, 4)};
-    // rrms and w must not be "the same buffer" as a matrix: compare ranges only
-    if ((st = check_overlap(outs, 3, ins, 3)) != RMSN_OK) return st;
+    if ((st = check_overlap(outs, 3, ins, 5)) != RMSN_OK) return st;
+    // rrms is never "the same buffer" as an input: compare ranges only
     if (rrms != nullptr) {
         for (const Region &in : ins)
             if (in.present && outs[2].overlaps(in))
@@ -345,8 +370,10 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
     if (resid)
         vec_ok = vec_ok && aligned16(r) && (rs * eb) % 16 == 0 &&
                  (ro == nullptr || (aligned16(ro) && (ros * eb) % 16 == 0));
+    if (adaln)
+        vec_ok = vec_ok && aligned16(cond.scale) && aligned16(cond.shift) && (cond.cs * pb) % 16 == 0;
 
-    const Kind kind = resid ? Kind::FwdResid : Kind::Fwd;
+    const Kind kind = resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     const Override ov = get_override(0);
@@ -372,9 +399,12 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
     if (grid > INT32_MAX) grid = INT32_MAX;
     const int64_t iters = (groups + grid - 1) / grid;
 
-    const bool nt = use_streaming((resid ? (ro ? 4 : 3) : 2) * M * H * eb);
-    fwd_fn fn = resid ? fwd_lookup_resid(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
-                      : fwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
+    const int64_t streamed = (resid ? (ro ? 4 : 3) : 2) * M * H * eb;
+    const bool nt = use_streaming(streamed);
+    const rmsn_dtype_t kwdt = (w || adaln) ? wdt : xdt;
+    fwd_fn fn = resid   ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
+                : adaln ? fwd_lookup_adaln(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
+                        : fwd_lookup_plain(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -399,9 +429,13 @@ rmsn_status_t fwd_impl(bool resid, const void *x, int64_t xs, const void *r, int
     p.nchunks = g.nchunks;
     p.eps = eps;
     p.inv_h = (float)(1.0 / (double)H);
+    p.scale = cond.scale;
+    p.shift = cond.shift;
+    p.cs = cond.cs;
+    p.rows_per_cond = cond.rows_per_cond;
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
-                  resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd");
+                  resid ? "rmsnorm_fwd_residual" : adaln ? "rmsnorm_adaln_fwd" : "rmsnorm_fwd");
 }
 
 // Most dw partial rows a backward call may use: 1024, or more for short rows
@@ -561,8 +595,8 @@ extern "C" {
 RMSN_API rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *w, void *y, int64_t y_stride, float *rrms,
                           int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
                           hipStream_t stream) {
-    rmsn_status_t s = fwd_impl(false, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
-                               x_dtype, w_dtype, stream);
+    rmsn_status_t s = fwd_impl(MODE_PLAIN, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
+                               x_dtype, w_dtype, Cond{}, stream);
     return s == RMSN_OK ? ok() : s;
 }
 
@@ -570,8 +604,22 @@ RMSN_API rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, con
                                    const void *w, void *y, int64_t y_stride, void *residual_out,
                                    int64_t ro_stride, float *rrms, int64_t M, int64_t H, float eps,
                                    rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream) {
-    rmsn_status_t s = fwd_impl(true, x, x_stride, residual, r_stride, w, y, y_stride, residual_out, ro_stride,
-                               rrms, M, H, eps, x_dtype, w_dtype, stream);
+    rmsn_status_t s = fwd_impl(MODE_RESID, x, x_stride, residual, r_stride, w, y, y_stride, residual_out, ro_stride,
+                               rrms, M, H, eps, x_dtype, w_dtype, Cond{}, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t rmsnorm_adaln_fwd(const void *x, int64_t x_stride, const void *w, const void *scale,
+                                         const void *shift, int64_t cond_stride, int64_t rows_per_cond, void *y,
+                                         int64_t y_stride, float *rrms, int64_t M, int64_t H, float eps,
+                                         rmsn_dtype_t x_dtype, rmsn_dtype_t param_dtype, hipStream_t stream) {
+    Cond c;
+    c.scale = scale;
+    c.shift = shift;
+    c.cs = cond_stride;
+    c.rows_per_cond = rows_per_cond;
+    rmsn_status_t s = fwd_impl(MODE_ADALN, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
+                               x_dtype, param_dtype, c, stream);
     return s == RMSN_OK ? ok() : s;
 }
 

@@ -33,7 +33,7 @@ _default = None
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle with gcc (IEEE float64, no contraction, no fast-math)."""
     if force or not os.path.exists(out):
-        tmp = out + ".tmp"
+        tmp = f"{out}.{os.getpid()}.tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
                "-fno-fast-math", "-Wall", "-Wextra", "-Werror", src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
@@ -76,8 +76,9 @@ class Oracle:
         lib.orc_fwd_residual.argtypes = [vp, i64, vp, i64, vp, i32, i32, i64, i64, dp, vp, vp, vp]
         lib.orc_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
         lib.orc_adaln_fwd.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i32, i32, i64, i64, dp, vp, vp]
+        lib.orc_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
         for f in (lib.orc_decode, lib.orc_encode, lib.orc_fwd, lib.orc_fwd_residual, lib.orc_bwd,
-                  lib.orc_adaln_fwd):
+                  lib.orc_adaln_fwd, lib.orc_bwd_residual):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -176,6 +177,31 @@ class Oracle:
         return y, r
 
 
+    def bwd_residual(self, dy, h, dres, w, rrms, dtype: str, wdtype: str | None = None, want_dw: bool = True):
+        """-> (dh float64 (M, H), dw or None, dh_terms): gradient reaching both
+        inputs of the fused residual add; dres (gradient on residual_out) may be
+        None.  dh_terms adds |dres| to the norm's two terms."""
+        h, hs = _rows(h, dtype)
+        dy, dys = _rows(dy, dtype)
+        M, H = h.shape
+        if dres is not None:
+            dres, drs = _rows(dres, dtype)
+            if dres.shape != h.shape:
+                raise ValueError("dres shape differs")
+        else:
+            drs = H
+        wv = None if w is None else _vec(w, wdtype or dtype)
+        r = np.ascontiguousarray(np.asarray(rrms).astype(np.float64))
+        dh = np.empty((M, H), dtype=np.float64)
+        terms = np.empty((M, H), dtype=np.float64)
+        dw = np.empty(H, dtype=np.float64) if (want_dw and w is not None) else None
+        rc = self.lib.orc_bwd_residual(_ptr(dy), dys, _ptr(h), hs, _ptr(dres), drs, _ptr(wv), _ptr(r),
+                                       CODES[dtype], CODES[wdtype or dtype], M, H, _ptr(dh), _ptr(dw), _ptr(terms))
+        if rc != 0:
+            raise ValueError("orc_bwd_residual rejected its arguments")
+        return dh, dw, terms
+
+
 def default() -> Oracle:
     """The oracle built from rmsnorm_oracle.c (rebuilt when the source is newer)."""
     global _default
@@ -209,3 +235,7 @@ def bwd(dy, x, w, rrms, dtype, wdtype=None, want_dw=True):
 
 def adaln_fwd(x, w, scale, shift, rows_per_cond, eps, dtype, wdtype=None, cdtype=None):
     return default().adaln_fwd(x, w, scale, shift, rows_per_cond, eps, dtype, wdtype, cdtype)
+
+
+def bwd_residual(dy, h, dres, w, rrms, dtype, wdtype=None, want_dw=True):
+    return default().bwd_residual(dy, h, dres, w, rrms, dtype, wdtype, want_dw)

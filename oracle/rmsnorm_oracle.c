@@ -22,6 +22,11 @@
  *   - The weightless form (no weight, LTX-Video's elementwise_affine=False)
  *     is the page "rocm-kernels" (skillselion.com), "Core Kernel
  *     Implementations", RMSNorm: out = x * rms_inv when there is no weight.
+ *   - Backward of the fused residual pre-norm (h = x + r, y = RMSNorm(h), and
+ *     h written back as the next residual stream): both x and r receive
+ *     dh = d(norm)/dh . dy + d(residual_out), the gradient of y through the
+ *     norm plus the gradient arriving on the residual stream (the chain rule
+ *     through the sum; the page only states the forward fusion).
  *   - AdaLN: the same page, "Core Kernel Implementations", 4. AdaLN, and its
  *     "Template 4": norm(x) * weight * (1 + scale) + shift, with scale and
  *     shift one row per token ([B, S, H]) or one row per batch ([B, 1, H]).
@@ -283,6 +288,28 @@ int orc_adaln_fwd(const void *x, int64_t x_stride, const void *w, const void *sc
             double sh = load_elem(shift, c_dt, c * cond_stride + j);
             y[i * H + j] = v * r * wj * (1.0 + sc) + sh;
         }
+    }
+    return 0;
+}
+
+/* ---- backward of the fused residual pre-norm -------------------------------
+ * dh_ij = (orc_bwd dx of dy through the norm of h)_ij + dres_ij, where h is
+ * the post-add stream (as stored, h_stride apart) and dres the gradient that
+ * arrives on the residual-stream output (NULL = 0).  dw as orc_bwd.
+ */
+int orc_bwd_residual(const void *dy, int64_t dy_stride, const void *h, int64_t h_stride, const void *dres,
+                     int64_t dres_stride, const void *w, const double *rrms, int x_dt, int w_dt, int64_t M,
+                     int64_t H, double *dh, double *dw, double *dh_terms) {
+    int rc = orc_bwd(dy, dy_stride, h, h_stride, w, rrms, x_dt, w_dt, M, H, dh, dw, dh_terms);
+    if (rc != 0) return rc;
+    if (dres) {
+        if (dres_stride < H) return -1;
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < H; ++j) {
+                double d = load_elem(dres, x_dt, i * dres_stride + j);
+                dh[i * H + j] += d;
+                if (dh_terms) dh_terms[i * H + j] += fabs(d);
+            }
     }
     return 0;
 }

@@ -51,7 +51,7 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile the generator (gcc, OpenMP)."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+        tmp = f"{_LIB}.{os.getpid()}.tmp"
         subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
                         "-Wall", "-Werror", _SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)

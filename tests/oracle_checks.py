@@ -540,6 +540,59 @@ def check_adaln_decimal(o):
             assert abs(Decimal(float(y[i, j])) - e) <= (abs(t) + abs(Decimal(float(sh[i, j])))) * Decimal("1e-15")
 
 
+# ---------------------------------------------------------------------------
+# backward of the fused residual pre-norm
+# ---------------------------------------------------------------------------
+
+def check_bwd_residual_finite_differences(o):
+    # L(x, r, w) = sum(dy * y) + sum(g * h) with h = x + r, y = RMSNorm(h):
+    # dL/dx = dL/dr = dh, dL/dw = dw
+    rng = _rng(30)
+    for (M, H) in ((1, 1), (2, 3), (3, 16), (2, 64)):
+        eps = 1e-2
+        xv, rv = rng.standard_normal((M, H)), rng.standard_normal((M, H))
+        wv = rng.uniform(0.5, 1.5, H)
+        dyv, gv = rng.standard_normal((M, H)), rng.standard_normal((M, H))
+
+        def loss(x, r, w):
+            y, h, _ = o.fwd_residual(x, r, w, eps, "f64")
+            return float((dyv * y).sum() + (gv * h).sum())
+
+        _, hh, rr = o.fwd_residual(xv, rv, wv, eps, "f64")
+        dh, dw, _ = o.bwd_residual(dyv, hh, gv, wv, rr, "f64")
+        step = 1e-5
+        scale = np.abs(dh).max()
+        for i in range(M):
+            for j in range(H):
+                for which in (0, 1):
+                    a = [xv.copy(), rv.copy()]
+                    b = [xv.copy(), rv.copy()]
+                    a[which][i, j] += step
+                    b[which][i, j] -= step
+                    fd = (loss(a[0], a[1], wv) - loss(b[0], b[1], wv)) / (2 * step)
+                    assert abs(fd - dh[i, j]) <= 1e-7 * scale + 1e-9, (M, H, i, j, which)
+        for j in range(H):
+            wp, wm = wv.copy(), wv.copy()
+            wp[j] += step
+            wm[j] -= step
+            fd = (loss(xv, rv, wp) - loss(xv, rv, wm)) / (2 * step)
+            assert abs(fd - dw[j]) <= 1e-7 * np.abs(dw).max() + 1e-9
+
+
+def check_bwd_residual_reduces_to_bwd(o):
+    rng = _rng(31)
+    M, H = 4, 50
+    h = rng.standard_normal((M, H))
+    w = rng.uniform(0.5, 1.5, H)
+    dy, g = rng.standard_normal((M, H)), rng.standard_normal((M, H))
+    _, r = o.fwd(h, w, 1e-5, "f64")
+    dx, dw, _ = o.bwd(dy, h, w, r, "f64")
+    dh0, dw0, _ = o.bwd_residual(dy, h, None, w, r, "f64")
+    assert np.array_equal(dh0, dx) and np.array_equal(dw0, dw)
+    dh1, dw1, _ = o.bwd_residual(dy, h, g, w, r, "f64")
+    assert np.allclose(dh1 - g, dx, rtol=1e-14, atol=1e-15) and np.array_equal(dw1, dw)
+
+
 ALL_CHECKS = [
     check_decode_all_16bit_patterns,
     check_encode_matches_libraries,
@@ -563,4 +616,6 @@ ALL_CHECKS = [
     check_adaln_reduces_to_rmsnorm,
     check_adaln_broadcast_rows,
     check_adaln_decimal,
+    check_bwd_residual_finite_differences,
+    check_bwd_residual_reduces_to_bwd,
 ]

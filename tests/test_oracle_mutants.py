@@ -44,6 +44,8 @@ MUTANTS = [
     ("adaln_shift_inside", "y[i * H + j] = v * r * wj * (1.0 + sc) + sh;",
      "y[i * H + j] = v * r * (wj * (1.0 + sc) + sh);", 0),
     ("adaln_cond_row_per_row", "const int64_t c = i / rows_per_cond;", "const int64_t c = i % rows_per_cond;", 0),
+    ("bwd_residual_grad_dropped", "                dh[i * H + j] += d;", "                dh[i * H + j] += 0.0 * d;", 0),
+    ("bwd_residual_grad_subtracted", "                dh[i * H + j] += d;", "                dh[i * H + j] -= d;", 0),
     ("round_half_away", "double q = rint(a / quantum);", "double q = round(a / quantum);", 0),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);", 0),
     ("f16_no_subnormal_quantum", "if (lead < emin) lead = emin;", "if (lead < emin - 30) lead = emin - 30;", 0),

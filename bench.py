@@ -10,7 +10,8 @@ the stream the kernels are launched on.  One JSON line is printed.
 
 Workloads (default: the forward at bf16 M=8192 H=4096):
   fwd_bf16_8192x4096, fwd_f32_64x512, fwd_bf16_32768x2048, fwd_bf16_32768x2048_noweight,
-  fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144
+  fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144,
+  bwd_residual_bf16_16384x8192, adaln_bf16_2x4096x2048_batchcond, adaln_bf16_2x4096x2048_tokencond
 
 The CPU baseline is the float64 oracle run on the host over a sample of the
 same workload (reported beside the GPU figure, never a target).
@@ -34,11 +35,14 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30
 
 
+_FWD = ("numerics.hpp", "fwd_kernels.hpp", "fwd_table.hpp", "kernel_tables.hpp")
+_BWD = ("numerics.hpp", "bwd_kernels.hpp", "bwd_table.hpp", "kernel_tables.hpp", "kernels_bwd.hip")
 KERNEL_SOURCES = {
-    "fwd": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd.hip", "rmsnorm_api.hip"),
-    "fwd_residual": ("numerics.hpp", "fwd_kernels.hpp", "kernels_fwd_residual.hip", "rmsnorm_api.hip"),
-    "bwd": ("numerics.hpp", "bwd_kernels.hpp", "kernels_bwd.hip", "rmsnorm_api.hip"),
-    "adaln": ("numerics.hpp", "fwd_kernels.hpp", "kernels_adaln.hip", "rmsnorm_api.hip"),
+    "fwd": _FWD + ("kernels_fwd.hip", "rmsnorm_api.hip"),
+    "fwd_residual": _FWD + ("kernels_fwd_residual.hip", "rmsnorm_api.hip"),
+    "bwd": _BWD + ("rmsnorm_api.hip",),
+    "bwd_residual": _BWD + ("kernels_bwd_residual.hip", "rmsnorm_api.hip"),
+    "adaln": _FWD + ("kernels_adaln.hip", "rmsnorm_api.hip"),
 }
 
 
@@ -86,6 +90,9 @@ def algorithmic_bytes(kind, M, H, esize, wsize, weighted, cond_rows=0):
     if kind == "bwd":
         # x, dy read; dx written; rrms read; w read; dw written (float32)
         return 3 * mat + M * 4 + w + H * 4
+    if kind == "bwd_residual":
+        # as bwd, plus the residual-stream gradient read
+        return 4 * mat + M * 4 + w + H * 4
     if kind == "adaln":
         # x read, y written, w and the scale/shift rows read once
         return 2 * mat + w + 2 * cond_rows * H * wsize
@@ -100,6 +107,7 @@ WORKLOADS = {
     "fwd_f16_32768x2048_outliers": ("fwd_f16_32768x2048_outliers", True),
     "fwd_residual_bf16_16384x8192": ("fwd_residual_bf16_16384x8192", True),
     "bwd_bf16_8192x6144": ("bwd_bf16_8192x6144", True),
+    "bwd_residual_bf16_16384x8192": ("bwd_residual_bf16_16384x8192", True),
     "adaln_bf16_2x4096x2048_batchcond": ("adaln_bf16_2x4096x2048_batchcond", True),
     "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
 }
@@ -118,7 +126,7 @@ def cpu_baseline(spec, kind, weighted, seconds):
     d = synthetic.make_inputs(spec["name"], rows=rows)
     w = d["w"] if weighted else None
     eps = float(np.float32(spec["eps"]))
-    if kind == "bwd":
+    if kind in ("bwd", "bwd_residual"):
         _, r = oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
         r32 = r.astype(np.float32)
     t0 = time.perf_counter()
@@ -131,6 +139,8 @@ def cpu_baseline(spec, kind, weighted, seconds):
                              d["wdtype"])
         elif kind == "fwd_residual":
             oracle.fwd_residual(d["x"], d["r"], w, eps, d["dtype"], d["wdtype"])
+        elif kind == "bwd_residual":
+            oracle.bwd_residual(d["dy"], d["x"], d["dres"], w, r32, d["dtype"], d["wdtype"])
         else:
             oracle.bwd(d["dy"], d["x"], w, r32, d["dtype"], d["wdtype"])
         passes += 1
@@ -167,7 +177,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     ws = synthetic.element_size(spec["wdtype"])
     known_kib = spec["M"] * spec["H"] * es / 1024.0
     kernel_key = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
-                  "bwd": "rmsnorm_bwd_kernel"}[spec["kind"]]
+                  "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel"}[spec["kind"]]
 
     def read(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -251,7 +261,7 @@ def main():
     kind = spec["kind"]
     if args.geom:
         parts = [int(v) for v in args.geom.split(",")]
-        tn.set_geometry("bwd" if kind == "bwd" else "fwd", *parts)
+        tn.set_geometry("bwd" if kind.startswith("bwd") else "fwd", *parts)
 
     dev = torch.device("cuda:0")
     d = synthetic.make_inputs(name)
@@ -276,9 +286,12 @@ def main():
         if kind == "fwd_residual":
             r0 = up(d["r"], dt) if i == 0 else sets[0]["r"].clone()
             s.update(r=r0, ro=torch.empty_like(x0))
-        if kind == "bwd":
+        if kind in ("bwd", "bwd_residual"):
             dy0 = up(d["dy"], dt) if i == 0 else sets[0]["dy"].clone()
             s.update(dy=dy0)
+        if kind == "bwd_residual":
+            g0 = up(d["dres"], dt) if i == 0 else sets[0]["dres"].clone()
+            s.update(dres=g0)
         if kind == "adaln":
             rpc = spec["rows_per_cond"]
             shape = (M // rpc, 1, H) if rpc > 1 else (1, M, H)
@@ -288,7 +301,7 @@ def main():
         sets.append(s)
     del d
     eps = spec["eps"]
-    if kind == "bwd":
+    if kind in ("bwd", "bwd_residual"):
         rr = torch.empty(M, dtype=torch.float32, device=dev)
         tn.rmsnorm_fwd(sets[0]["x"], w, eps, rrms=rr)
         dw = torch.empty(H, dtype=torch.float32, device=dev)
@@ -303,6 +316,8 @@ def main():
             tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
         elif kind == "adaln":
             tn.rmsnorm_adaln_fwd(s["x"], w, s["scale"], s["shift"], eps, out=s["y"])
+        elif kind == "bwd_residual":
+            tn.rmsnorm_bwd_residual(s["dy"], s["x"], s["dres"], w, rr, dh=s["y"], dw=dw, workspace=wsp)
         else:
             tn.rmsnorm_bwd(s["dy"], s["x"], w, rr, dx=s["y"], dw=dw, workspace=wsp)
 

@@ -172,6 +172,37 @@ rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void *x, int6
                           void *workspace, size_t workspace_bytes, int64_t M, int64_t H,
                           rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream);
 
+/*
+ * Backward of the fused residual pre-norm.  Its forward (rmsnorm_fwd_residual)
+ * computes h = x + residual, y = RMSNorm(h) and writes h back as the next
+ * residual stream, so h reaches the loss twice: through y and through
+ * residual_out.  By the chain rule through the sum, x and residual receive the
+ * same gradient
+ *
+ *   dh[i, j] = dx[i, j] (as rmsnorm_bwd, with h in place of x) + dres[i, j]
+ *
+ * formed in float32 and rounded once.  (The page "Skill: Write a Triton
+ * RMSNorm Kernel" gives the forward fusion, "Use this when" and "Kernel design
+ * rules", and the norm's backward, step 12; the added term is the derivative
+ * of the residual write-back.)
+ *
+ *   h         (M, H) the residual_out the forward wrote (the post-add stream
+ *             as stored), rows h_stride apart.  The forward's rrms was
+ *             computed from the unrounded sum; for float32 the two agree.
+ *   dres      (M, H) gradient arriving on residual_out, rows dres_stride
+ *             apart, or NULL when residual_out feeds nothing (then this call
+ *             is rmsnorm_bwd).
+ *   dh        (M, H) output, rows dh_stride apart; may equal dy, h or dres
+ *             (same pointer and stride).
+ *   dy, w, rrms, dw, workspace, workspace_bytes, M, H, dtypes
+ *             as rmsnorm_bwd (the workspace size is the same).
+ */
+rmsn_status_t rmsnorm_bwd_residual(const void *dy, int64_t dy_stride, const void *h, int64_t h_stride,
+                                   const void *dres, int64_t dres_stride, const void *w, const float *rrms,
+                                   void *dh, int64_t dh_stride, float *dw, void *workspace,
+                                   size_t workspace_bytes, int64_t M, int64_t H, rmsn_dtype_t x_dtype,
+                                   rmsn_dtype_t w_dtype, hipStream_t stream);
+
 /* Fixed text for a status code (never NULL). */
 const char *rmsnorm_status_string(rmsn_status_t status);
 

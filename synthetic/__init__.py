@@ -158,6 +158,12 @@ WORKLOADS = {
                                          x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1004),
     "bwd_bf16_8192x6144": dict(kind="bwd", M=8192, H=6144, dtype="bf16", wdtype="bf16",
                                x=(0.0, 1.0), w=(1.0, 0.1), dy=(0.0, 1.0), eps=1e-6, seed=1005),
+    # backward of the residual pre-norm above: h is the stored post-add
+    # stream (x + r of two N(0, 1) draws has std sqrt(2)); dres is the
+    # gradient arriving on it, drawn from the residual stream
+    "bwd_residual_bf16_16384x8192": dict(kind="bwd_residual", M=16384, H=8192, dtype="bf16", wdtype="bf16",
+                                         x=(0.0, 2.0 ** 0.5), w=(1.0, 0.1), dy=(0.0, 1.0), dres=(0.0, 1.0),
+                                         eps=1e-5, seed=1008),
     # DiT-style AdaLN on 2 x 4096 tokens of width 2048 (LTX-Video's hidden
     # size); scale/shift per batch ([B, 1, H]) and per token ([B, S, H])
     "adaln_bf16_2x4096x2048_batchcond": dict(kind="adaln", M=8192, H=2048, dtype="bf16", wdtype="bf16",
@@ -187,6 +193,8 @@ def make_inputs(name: str, rows: int | None = None) -> dict:
     out["w"] = encode(normal(seed, STREAM_W, H, *spec["w"]), wdt)
     if "r" in spec:
         out["r"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["r"]), dt).reshape(m, H)
+    if "dres" in spec:
+        out["dres"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["dres"]), dt).reshape(m, H)
     if "dy" in spec:
         out["dy"] = encode(normal(seed, STREAM_DY, n, *spec["dy"]), dt).reshape(m, H)
     if "cond" in spec:

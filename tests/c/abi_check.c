@@ -116,6 +116,21 @@ int main(void) {
     expect("bwd M == 0 without dw", rmsnorm_bwd(NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, NULL, 0, 0, H,
                                                 RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
 
+    void *g = (void *)(uintptr_t)0xa00000000ull;
+    expect("bwd_residual dres_stride < H", rmsnorm_bwd_residual(r, H, x, H, g, H - 8, w, rr, y, H, dw, ws, need, M,
+                                                                H, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("bwd_residual dh partially overlaps dres",
+           rmsnorm_bwd_residual(r, H, x, H, g, H, w, rr, (char *)g + 16, H, dw, ws, need, M, H, RMSN_BF16,
+                                RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("bwd_residual workspace overlaps dres",
+           rmsnorm_bwd_residual(r, H, x, H, g, H, w, rr, y, H, dw, g, need, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("bwd_residual workspace small",
+           rmsnorm_bwd_residual(r, H, x, H, g, H, w, rr, y, H, dw, ws, need - 16, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_WORKSPACE);
+    expect("bwd_residual M == 0", rmsnorm_bwd_residual(NULL, H, NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, NULL, 0,
+                                                       0, H, RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
+
     /* a geometry that cannot cover the row is rejected before the device */
     rmsnorm_tuning_set_geometry(0, 3, 1, 1, 0);
     expect("override too small", rmsnorm_fwd(x, H, w, y, H, rr, M, H, 1e-5f, RMSN_BF16, RMSN_BF16, 0),

@@ -98,6 +98,31 @@ def bwd_vs_oracle(dy, x, w, rrms32, dx_host, dw_host, dtype, wdtype=None, chunk=
     return rep_dx, rep_dw
 
 
+def bwd_residual_vs_oracle(dy, h, dres, w, rrms32, dh_host, dw_host, dtype, wdtype=None, chunk=1024,
+                          name="bwd_residual"):
+    """dh = norm backward through h + dres: dres joins the terms that set the
+    cancellation floor (dh may cancel between the norm's gradient and dres)."""
+    M, H = h.shape
+    rep_dh, rep_dw = parity.Report(f"{name} dh"), parity.Report(f"{name} dw")
+    dw_ref = np.zeros(H) if w is not None else None
+    colscale = np.zeros(H)
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        g = None if dres is None else dres[r0:r1]
+        dhref, dwref, terms = oracle.bwd_residual(dy[r0:r1], h[r0:r1], g, w, rrms32[r0:r1], dtype, wdtype)
+        if dtype == "f32":
+            parity.check_dx_f32(rep_dh, dh_host[r0:r1], dhref, terms, r0 * H)
+        else:
+            parity.check_dx16(rep_dh, dh_host[r0:r1], dhref, terms, dtype, oracle.encode, oracle.decode, r0 * H)
+        if w is not None:
+            dw_ref += dwref
+            xn = oracle.decode(h[r0:r1], dtype) * rrms32[r0:r1].astype(np.float64)[:, None]
+            colscale += np.abs(oracle.decode(dy[r0:r1], dtype) * xn).sum(axis=0)
+    if w is not None and dw_host is not None:
+        parity.check_dw(rep_dw, dw_host, dw_ref, colscale)
+    return rep_dh, rep_dw
+
+
 def assert_ok(*reports):
     for r in reports:
         print(r, flush=True)
@@ -106,6 +131,8 @@ def assert_ok(*reports):
 
 
 def inputs(seed, M, H, dtype, wdtype=None, xdist=(0.0, 1.0), weight=True, residual=False, dy=False):
+    """Seeded host arrays: x, w (or None), and optionally r (the residual
+    stream, which the backward tests also use as dres) and dy."""
     d = {"x": synthetic.normal_tensor(seed, synthetic.STREAM_X, (M, H), dtype, *xdist)}
     d["w"] = synthetic.normal_tensor(seed, synthetic.STREAM_W, (H,), wdtype or dtype, 1.0, 0.1) if weight else None
     if residual:

@@ -593,6 +593,91 @@ def check_bwd_residual_reduces_to_bwd(o):
     assert np.allclose(dh1 - g, dx, rtol=1e-14, atol=1e-15) and np.array_equal(dw1, dw)
 
 
+# ---------------------------------------------------------------------------
+# RoPE apply ("rocm-kernels", Core Kernel Implementations 2 and Template 2)
+# ---------------------------------------------------------------------------
+
+def check_rope_hand_example(o):
+    # head_dim 4: pairs (0, 2) and (1, 3); the table's last two columns are
+    # never read (filled with 9)
+    x = np.array([1.0, 3.0, 2.0, 5.0]).reshape(1, 1, 1, 4)
+    c = np.array([[0.5, 0.25, 9.0, 9.0]])
+    sn = np.array([[0.75, -1.0, 9.0, 9.0]])
+    # out0 = x0*c - x1*s, out1 = x0*s + x1*c, worked by hand
+    assert np.array_equal(o.rope(x, c, sn, "f64")[0, 0, 0], [-1.0, 5.75, 1.75, -1.75])
+    # transposed: s -> -s
+    assert np.array_equal(o.rope(x, c, sn, "f64", transpose=True)[0, 0, 0], [2.0, -4.25, 0.25, 4.25])
+    # half-width tables give the same result
+    assert np.array_equal(o.rope(x, c[:, :2], sn[:, :2], "f64")[0, 0, 0], [-1.0, 5.75, 1.75, -1.75])
+
+
+def check_rope_quarter_turns_by_position(o):
+    # token s of every batch turns by s quarter turns: cos/sin in {0, +-1}, so
+    # each output is exactly +-x0 or +-x1; this fixes which table row each
+    # flat row (b * S + s) reads
+    B, S, NH, D = 3, 5, 2, 6
+    rng = _rng(40)
+    x = rng.standard_normal((B, S, NH, D))
+    ang = np.arange(S)
+    c = np.repeat(np.array([1.0, 0.0, -1.0, 0.0])[ang % 4][:, None], D, axis=1)
+    sn = np.repeat(np.array([0.0, 1.0, 0.0, -1.0])[ang % 4][:, None], D, axis=1)
+    out = o.rope(x, c, sn, "f64")
+    h = D // 2
+    x0, x1 = x[..., :h], x[..., h:]
+    for s in range(S):
+        q = s % 4
+        want0 = [x0, -x1, -x0, x1][q][:, s]
+        want1 = [x1, x0, -x1, -x0][q][:, s]
+        assert np.array_equal(out[:, s, :, :h], want0) and np.array_equal(out[:, s, :, h:], want1), s
+
+
+def check_rope_rotation_invariants(o):
+    # each (j, j + D/2) pair is rotated by its angle: the pair's norm is kept,
+    # two rotations compose to the rotation by the summed angle, and the
+    # transposed rotation undoes the rotation
+    rng = _rng(41)
+    B, S, NH, D = 2, 7, 3, 16
+    x = rng.standard_normal((B, S, NH, D))
+    t1, t2 = rng.uniform(-np.pi, np.pi, (S, D // 2)), rng.uniform(-np.pi, np.pi, (S, D // 2))
+    y = o.rope(x, np.cos(t1), np.sin(t1), "f64")
+    h = D // 2
+    n_in = x[..., :h] ** 2 + x[..., h:] ** 2
+    n_out = y[..., :h] ** 2 + y[..., h:] ** 2
+    assert np.allclose(n_out, n_in, rtol=1e-14, atol=0)
+    z = o.rope(y, np.cos(t2), np.sin(t2), "f64")
+    z2 = o.rope(x, np.cos(t1 + t2), np.sin(t1 + t2), "f64")
+    assert np.allclose(z, z2, rtol=0, atol=1e-13)
+    back = o.rope(y, np.cos(t1), np.sin(t1), "f64", transpose=True)
+    assert np.allclose(back, x, rtol=0, atol=1e-14)
+    # the angle's complex form: (x0 + i x1) * exp(i t)
+    zc = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * t1)[None, :, None, :]
+    assert np.allclose(y[..., :h], zc.real, rtol=0, atol=1e-14) and np.allclose(y[..., h:], zc.imag, rtol=0,
+                                                                                 atol=1e-14)
+
+
+def check_rope_batches_and_strides(o):
+    # batches are independent and read the same table rows; a padded view
+    # (head and row strides) gives the same values as its contiguous copy
+    rng = _rng(42)
+    B, S, NH, D = 3, 4, 2, 8
+    x = rng.standard_normal((B, S, NH, D))
+    t = rng.uniform(-np.pi, np.pi, (S, D))
+    c, sn = np.cos(t), np.sin(t)
+    full = o.rope(x, c, sn, "f64")
+    for b in range(B):
+        assert np.array_equal(full[b], o.rope(x[b:b + 1], c, sn, "f64")[0])
+    big = np.zeros((B, S, NH + 1, D + 3))
+    big[:, :, :NH, :D] = x
+    assert np.array_equal(o.rope(big[:, :, :NH, :D], c, sn, "f64"), full)
+    # bf16 storage: decode is exact, the result is the float64 rotation of
+    # the decoded values
+    xb = o.encode(x, "bf16")
+    cb, sb = o.encode(c, "bf16"), o.encode(sn, "bf16")
+    got = o.rope(xb, cb, sb, "bf16")
+    want = o.rope(o.decode(xb, "bf16"), o.decode(cb, "bf16"), o.decode(sb, "bf16"), "f64")
+    assert np.array_equal(got, want)
+
+
 ALL_CHECKS = [
     check_decode_all_16bit_patterns,
     check_encode_matches_libraries,
@@ -618,4 +703,8 @@ ALL_CHECKS = [
     check_adaln_decimal,
     check_bwd_residual_finite_differences,
     check_bwd_residual_reduces_to_bwd,
+    check_rope_hand_example,
+    check_rope_quarter_turns_by_position,
+    check_rope_rotation_invariants,
+    check_rope_batches_and_strides,
 ]

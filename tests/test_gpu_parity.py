@@ -118,13 +118,14 @@ def test_workload_bwd():
 
 def test_workload_bwd_chained_with_gpu_rrms():
     """The GPU forward's own rrms feeds the GPU backward; the oracle backward
-    gets the same float32 rrms."""
+    gets the oracle forward's rrms rounded to float32 (the two differ by at
+    most a float32 rounding, far below the outputs' tolerance)."""
     name = "bwd_bf16_8192x6144"
     d = synthetic.make_inputs(name, rows=2048)
     _, rr = run_fwd(d["x"], d["w"], d["eps"], d["dtype"])
-    rr = rr.astype(np.float32)
-    dx, dw = run_bwd(d["dy"], d["x"], d["w"], rr, d["dtype"])
-    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], rr, dx, dw, d["dtype"], name=name + " chained"))
+    dx, dw = run_bwd(d["dy"], d["x"], d["w"], rr.astype(np.float32), d["dtype"])
+    ro = oracle_rrms32(d["x"], d["w"], d["eps"], d["dtype"])
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], ro, dx, dw, d["dtype"], name=name + " chained"))
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,334 @@
+"""GPU parity of the training path: the backward of the fused residual
+pre-norm (rmsnorm_bwd_residual) against the float64 oracle, and the
+torch.autograd layer (transformer_normalization_amd.autograd) against the
+oracle and against the C-ABI calls it is meant to make.
+
+Tolerances as for the plain backward: dh within 1 ulp of the oracle rounded to
+the output format, the ulp taken at no less than 2^-10 of the sum of the
+magnitudes of dh's terms (the norm's two terms and dres), since dh may cancel;
+float32 outputs within 1e-5 relative above the same kind of floor; dw within
+1e-3 relative plus 1e-5 of the column's sum of |dy * xn|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import transformer_normalization_amd as tn  # noqa: E402
+from transformer_normalization_amd import autograd as ag  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _default_geometry():
+    tn.set_geometry("fwd")
+    tn.set_geometry("bwd")
+    tn.set_streaming(-1)
+    yield
+    tn.set_geometry("fwd")
+    tn.set_geometry("bwd")
+    tn.set_streaming(-1)
+
+
+def oracle_rrms32(x, w, eps, dtype, wdtype=None, chunk=2048):
+    out = np.empty(x.shape[0], dtype=np.float32)
+    for r0 in range(0, x.shape[0], chunk):
+        _, r = oracle.fwd(x[r0:r0 + chunk], w, G.eps32(eps), dtype, wdtype)
+        out[r0:r0 + chunk] = r.astype(np.float32)
+    return out
+
+
+def run_bwd_residual(dy, h, dres, w, rrms32, dtype, wdtype=None):
+    dyd, hd = G.to_dev(dy, dtype), G.to_dev(h, dtype)
+    gd = None if dres is None else G.to_dev(dres, dtype)
+    wd = None if w is None else G.to_dev(w, wdtype or dtype)
+    dh, dw = tn.rmsnorm_bwd_residual(dyd, hd, gd, wd, torch.from_numpy(rrms32).to(G.DEV))
+    torch.cuda.synchronize()
+    return G.to_host(dh, dtype), (None if dw is None else dw.cpu().numpy())
+
+
+def case(seed, M, H, dtype, wdtype=None, eps=1e-5):
+    d = G.inputs(seed, M, H, dtype, wdtype, residual=True, dy=True)
+    d["rr"] = oracle_rrms32(d["x"], d["w"], eps, dtype, wdtype)
+    return d
+
+
+# ---------------------------------------------------------------------------
+# rmsnorm_bwd_residual
+# ---------------------------------------------------------------------------
+
+def test_workload_bwd_residual():
+    name = "bwd_residual_bf16_16384x8192"
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    rr = oracle_rrms32(d["x"], d["w"], d["eps"], d["dtype"])
+    dh, dw = run_bwd_residual(d["dy"], d["x"], d["dres"], d["w"], rr, d["dtype"])
+    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], d["x"], d["dres"], d["w"], rr, dh, dw, d["dtype"], name=name))
+
+
+RES_H = [1, 7, 64, 65, 513, 2049, 4096, 6144, 8191, 16385, 65536]
+
+
+@pytest.mark.parametrize("with_dres", [True, False], ids=["dres", "no_dres"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("H", RES_H)
+def test_bwd_residual_shapes(H, dtype, with_dres):
+    M = 257 if H <= 8192 else 5
+    print(f"[gpu] bwd_residual {dtype} M={M} H={H} dres={with_dres}", flush=True)
+    d = case(2000 + H, M, H, dtype)
+    g = d["r"] if with_dres else None
+    dh, dw = run_bwd_residual(d["dy"], d["x"], g, d["w"], d["rr"], dtype)
+    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], d["x"], g, d["w"], d["rr"], dh, dw, dtype,
+                                          name=f"bwd_residual {dtype} H={H}"))
+
+
+def test_bwd_residual_float32_weight_and_weightless():
+    d = case(71, 300, 2048, "bf16", "f32")
+    dh, dw = run_bwd_residual(d["dy"], d["x"], d["r"], d["w"], d["rr"], "bf16", "f32")
+    reps = list(G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], d["rr"], dh, dw, "bf16", "f32",
+                                         name="f32 weight"))
+    rr0 = oracle_rrms32(d["x"], None, 1e-5, "bf16")
+    dh0, dw0 = run_bwd_residual(d["dy"], d["x"], d["r"], None, rr0, "bf16")
+    assert dw0 is None
+    reps += list(G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], None, rr0, dh0, None, "bf16", name="weightless"))
+    G.assert_ok(*reps)
+
+
+# (vpt, wpr, P, row order: 0 default, 1 interleaved, 2 contiguous blocks)
+RES_GEOMS = [(1, 8, 0, 0), (2, 4, 0, 0), (4, 2, 0, 0), (2, 4, 7, 1), (2, 4, 7, 2), (1, 8, 37, 2), (4, 1, 16, 1)]
+
+
+@pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
+@pytest.mark.parametrize("geom", RES_GEOMS, ids=[str(g) for g in RES_GEOMS])
+def test_bwd_residual_forced_geometry(geom, stream):
+    d = case(72, 300, 4096, "bf16")
+    tn.set_geometry("bwd", *geom)
+    tn.set_streaming(stream)
+    dh, dw = run_bwd_residual(d["dy"], d["x"], d["r"], d["w"], d["rr"], "bf16")
+    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], d["rr"], dh, dw, "bf16",
+                                          name=f"geom {geom} stream {stream}"))
+
+
+def test_bwd_residual_two_pass_streaming_identical():
+    d = case(73, 6, 65536, "bf16")
+    tn.set_streaming(0)
+    a = run_bwd_residual(d["dy"], d["x"], d["r"], d["w"], d["rr"], "bf16")
+    tn.set_streaming(1)
+    b = run_bwd_residual(d["dy"], d["x"], d["r"], d["w"], d["rr"], "bf16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_residual_misaligned_rows(dtype):
+    """Rows that are not 16-byte aligned (odd H, and a dres view with a pad of
+    one element) take the single-element path."""
+    M, H = 129, 4097
+    d = case(74, M, H, dtype)
+    dyd, hd, wd = G.to_dev(d["dy"], dtype), G.to_dev(d["x"], dtype), G.to_dev(d["w"], dtype)
+    big = torch.zeros((M, H + 1), dtype=G.torch_dtype(dtype), device=G.DEV)
+    big[:, 1:] = G.to_dev(d["r"], dtype)
+    gd = big[:, 1:]
+    dh, dw = tn.rmsnorm_bwd_residual(dyd, hd, gd, wd, torch.from_numpy(d["rr"]).to(G.DEV))
+    torch.cuda.synchronize()
+    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], d["rr"], G.to_host(dh, dtype),
+                                          dw.cpu().numpy(), dtype, name=f"misaligned {dtype}"))
+
+
+@pytest.mark.parametrize("H", [4096, 65536])
+def test_bwd_residual_in_place(H):
+    """dh may be dres, dy or h itself (same buffer and stride); the bits equal
+    those of a separate output."""
+    M = 64 if H <= 8192 else 4
+    d = case(75, M, H, "bf16")
+    rr = torch.from_numpy(d["rr"]).to(G.DEV)
+    dyd, hd, gd, wd = (G.to_dev(d[k], "bf16") for k in ("dy", "x", "r", "w"))
+    ref, dwr = tn.rmsnorm_bwd_residual(dyd, hd, gd, wd, rr)
+    for alias in ("dres", "dy", "h"):
+        a = {"dres": gd.clone(), "dy": dyd.clone(), "h": hd.clone()}
+        out = a[alias]
+        dh, dw = tn.rmsnorm_bwd_residual(a["dy"], a["h"], a["dres"], wd, rr, dh=out)
+        assert dh.data_ptr() == out.data_ptr()
+        assert torch.equal(dh.view(torch.int16), ref.view(torch.int16)), alias
+        assert torch.equal(dw, dwr), alias
+
+
+def test_bwd_residual_without_dres_is_plain_backward():
+    d = case(76, 200, 6144, "bf16")
+    rr = torch.from_numpy(d["rr"]).to(G.DEV)
+    dyd, hd, gd, wd = (G.to_dev(d[k], "bf16") for k in ("dy", "x", "r", "w"))
+    a, dwa = tn.rmsnorm_bwd(dyd, hd, wd, rr)
+    b, dwb = tn.rmsnorm_bwd_residual(dyd, hd, None, wd, rr)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(dwa, dwb)
+    # a zero dres adds exactly zero (+0 and -0 compare equal)
+    c, dwc = tn.rmsnorm_bwd_residual(dyd, hd, torch.zeros_like(gd), wd, rr)
+    assert torch.equal(a.float(), c.float()) and torch.equal(dwa, dwc)
+
+
+def test_bwd_residual_deterministic():
+    d = case(77, 1000, 6144, "bf16")
+    runs = [run_bwd_residual(d["dy"], d["x"], d["r"], d["w"], d["rr"], "bf16") for _ in range(3)]
+    for dh, dw in runs[1:]:
+        assert np.array_equal(dh, runs[0][0]) and np.array_equal(dw, runs[0][1])
+
+
+def test_bwd_residual_empty_batch():
+    H = 512
+    e = torch.empty((0, H), dtype=torch.bfloat16, device=G.DEV)
+    w = torch.ones(H, dtype=torch.bfloat16, device=G.DEV)
+    dh, dw = tn.rmsnorm_bwd_residual(e, e, e, w, torch.empty(0, device=G.DEV))
+    torch.cuda.synchronize()
+    assert dh.shape == (0, H) and torch.equal(dw, torch.zeros(H, device=G.DEV))
+
+
+# ---------------------------------------------------------------------------
+# torch.autograd layer
+# ---------------------------------------------------------------------------
+
+def _leaf(a, dtype, grad=True):
+    return G.to_dev(a, dtype).requires_grad_(grad)
+
+
+def test_autograd_rms_norm_makes_the_abi_calls():
+    """Gradients through rms_norm are bit-identical to rmsnorm_fwd followed by
+    rmsnorm_bwd on the saved rrms, and match the oracle."""
+    M, H = 257, 4096
+    d = G.inputs(80, M, H, "bf16", dy=True)
+    x, w = _leaf(d["x"], "bf16"), _leaf(d["w"], "bf16")
+    gy = G.to_dev(d["dy"], "bf16")
+    y = ag.rms_norm(x, w, 1e-5)
+    (y.float() * gy.float()).sum().backward()
+    # the incoming gradient of a float32 product sum is gy in float32, cast back to bf16 exactly
+    y2, rr = tn.rmsnorm_fwd(x.detach(), w.detach(), 1e-5, return_rrms=True)
+    dx, dw = tn.rmsnorm_bwd(gy, x.detach(), w.detach(), rr)
+    assert torch.equal(y.detach().view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(x.grad.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(w.grad.float(), dw.to(torch.bfloat16).float())
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-5, "bf16")
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(x.grad, "bf16"), dw.cpu().numpy(), "bf16",
+                                 name="autograd rms_norm"))
+
+
+def test_autograd_fused_add_vs_oracle():
+    """loss = sum(gy * y) + sum(gh * h): x and residual both receive dh, the
+    weight dw cast to its format.  The gradients are the ABI's outputs for the
+    forward's own h and rrms (bit for bit) and match the oracle's, which gets
+    its own h and float32 rrms."""
+    M, H, eps = 300, 4096, 1e-5
+    d = G.inputs(81, M, H, "bf16", residual=True, dy=True)
+    gh_host = synthetic.normal_tensor(81, synthetic.STREAM_SHIFT, (M, H), "bf16")
+    x, r, w = _leaf(d["x"], "bf16"), _leaf(d["r"], "bf16"), _leaf(d["w"], "bf16")
+    gy, gh = G.to_dev(d["dy"], "bf16"), G.to_dev(gh_host, "bf16")
+    y, h = ag.fused_add_rms_norm(x, r, w, eps)
+    ((y.float() * gy.float()).sum() + (h.float() * gh.float()).sum()).backward()
+    assert torch.equal(x.grad.view(torch.int16), r.grad.view(torch.int16))
+    with torch.no_grad():
+        _, hm, rrm = tn.rmsnorm_fwd_residual(x, r, w, eps, return_rrms=True)
+        dh, dw = tn.rmsnorm_bwd_residual(gy, hm, gh, w, rrm)
+    assert torch.equal(x.grad.view(torch.int16), dh.view(torch.int16))
+    assert torch.equal(w.grad, dw.to(torch.bfloat16))
+    # parity: h is the rounded sum bit for bit; dh and the float32 dw are
+    # within tolerance of the oracle
+    _, href, rref = oracle.fwd_residual(d["x"], d["r"], d["w"], G.eps32(eps), "bf16")
+    h_host = oracle.encode(href, "bf16")
+    assert np.array_equal(G.to_host(h, "bf16"), h_host)
+    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], h_host, gh_host, d["w"], rref.astype(np.float32),
+                                          G.to_host(x.grad, "bf16"), dw.cpu().numpy(), "bf16",
+                                          name="autograd fused_add"))
+
+
+def test_autograd_fused_add_only_residual_stream_used():
+    M, H = 64, 2048
+    d = G.inputs(82, M, H, "bf16", residual=True, dy=True)
+    x, r, w = _leaf(d["x"], "bf16"), _leaf(d["r"], "bf16"), _leaf(d["w"], "bf16")
+    gh = G.to_dev(d["dy"], "bf16")
+    _, h = ag.fused_add_rms_norm(x, r, w, 1e-5)
+    (h.float() * gh.float()).sum().backward()
+    assert torch.equal(x.grad.view(torch.int16), gh.view(torch.int16))
+    assert torch.equal(r.grad.view(torch.int16), gh.view(torch.int16))
+    assert torch.equal(w.grad, torch.zeros_like(w))
+
+
+def test_autograd_two_layer_chain_matches_abi_sequence():
+    """Two pre-norm blocks sharing the residual stream: the autograd result is
+    bit-identical to the C-ABI backward calls made by hand in reverse order."""
+    M, H, eps = 128, 4096, 1e-5
+    s = [synthetic.normal_tensor(83, k, (M, H), "bf16") for k in range(6)]
+    w1h, w2h = (synthetic.normal_tensor(84 + i, synthetic.STREAM_W, (H,), "bf16", 1.0, 0.1) for i in range(2))
+    r0, x1, x2 = (_leaf(a, "bf16") for a in s[:3])
+    gy1, gy2, gh2 = (G.to_dev(a, "bf16") for a in s[3:])
+    w1, w2 = _leaf(w1h, "bf16"), _leaf(w2h, "bf16")
+    y1, h1 = ag.fused_add_rms_norm(x1, r0, w1, eps)
+    y2, h2 = ag.fused_add_rms_norm(x2, h1, w2, eps)
+    ((y1.float() * gy1.float()).sum() + (y2.float() * gy2.float()).sum() + (h2.float() * gh2.float()).sum()).backward()
+    with torch.no_grad():
+        _, h1m, rr1 = tn.rmsnorm_fwd_residual(x1, r0, w1, eps, return_rrms=True)
+        _, h2m, rr2 = tn.rmsnorm_fwd_residual(x2, h1m, w2, eps, return_rrms=True)
+        dh2, dw2 = tn.rmsnorm_bwd_residual(gy2, h2m, gh2, w2, rr2)
+        dh1, dw1 = tn.rmsnorm_bwd_residual(gy1, h1m, dh2, w1, rr1)
+    torch.cuda.synchronize()
+    for got, want in ((x2.grad, dh2), (x1.grad, dh1), (r0.grad, dh1)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert torch.equal(w1.grad, dw1.to(torch.bfloat16)) and torch.equal(w2.grad, dw2.to(torch.bfloat16))
+
+
+def test_autograd_expanded_and_transposed_gradients():
+    """y.sum() hands back an expanded gradient of ones; the layer copies it
+    into a row-contiguous buffer before the kernel reads it."""
+    M, H = 96, 1024
+    d = G.inputs(85, M, H, "f32")
+    x, w = _leaf(d["x"], "f32"), _leaf(d["w"], "f32")
+    ag.rms_norm(x, w, 1e-6).sum().backward()
+    ones = np.ones((M, H), dtype=np.float32)
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-6, "f32")
+    G.assert_ok(*G.bwd_vs_oracle(ones, d["x"], d["w"], r32, x.grad.cpu().numpy(), w.grad.cpu().numpy(), "f32",
+                                 name="expanded grad"))
+    x2 = _leaf(d["x"], "f32")
+    gT = torch.from_numpy(np.ascontiguousarray(d["x"].T)).to(G.DEV)  # (H, M), used transposed
+    (ag.rms_norm(x2, None, 1e-6) * gT.t()).sum().backward()
+    r0 = oracle_rrms32(d["x"], None, 1e-6, "f32")
+    rep, _ = G.bwd_vs_oracle(d["x"], d["x"], None, r0, x2.grad.cpu().numpy(), None, "f32", name="transposed grad")
+    G.assert_ok(rep)
+
+
+def test_module_shapes_dtypes_and_weightless():
+    B, T, H = 2, 33, 2048
+    xh = synthetic.normal_tensor(86, synthetic.STREAM_X, (B * T, H), "bf16")
+    norm = ag.RMSNorm(H, eps=1e-6, device=G.DEV, dtype=torch.float32)
+    x = G.to_dev(xh, "bf16").view(B, T, H).requires_grad_(True)
+    y = norm(x)
+    assert y.shape == (B, T, H) and y.dtype == torch.bfloat16
+    y.float().pow(2).sum().backward()
+    assert x.grad.shape == x.shape and x.grad.dtype == torch.bfloat16
+    assert norm.weight.grad.shape == (H,) and norm.weight.grad.dtype == torch.float32
+    r = torch.zeros_like(x)
+    y2, h = norm(x.detach(), r)
+    assert torch.equal(h.view(torch.int16), x.detach().view(torch.int16))
+    assert torch.equal(y2.view(torch.int16), y.detach().view(torch.int16))
+    plain = ag.RMSNorm(H, eps=1e-6, elementwise_affine=False)
+    assert plain.weight is None
+    xw = G.to_dev(xh, "bf16").requires_grad_(True)
+    yw = plain(xw)
+    rr = oracle_rrms32(xh, None, 1e-6, "bf16")
+    G.assert_ok(*G.fwd_vs_oracle(xh, None, G.to_host(yw, "bf16"), rr, 1e-6, "bf16", name="module weightless"))
+    gy = synthetic.normal_tensor(87, synthetic.STREAM_DY, (B * T, H), "bf16")
+    (yw.float() * G.to_dev(gy, "bf16").float()).sum().backward()
+    rep, _ = G.bwd_vs_oracle(gy, xh, None, rr, G.to_host(xw.grad, "bf16"), None, "bf16", name="module weightless bwd")
+    G.assert_ok(rep)
+
+
+def test_frozen_weight_skips_dw():
+    M, H = 32, 512
+    d = G.inputs(88, M, H, "bf16")
+    x, w = _leaf(d["x"], "bf16"), _leaf(d["w"], "bf16", grad=False)
+    ag.rms_norm(x, w, 1e-5).float().sum().backward()
+    assert x.grad is not None and w.grad is None

@@ -46,6 +46,18 @@ MUTANTS = [
     ("adaln_cond_row_per_row", "const int64_t c = i / rows_per_cond;", "const int64_t c = i % rows_per_cond;", 0),
     ("bwd_residual_grad_dropped", "                dh[i * H + j] += d;", "                dh[i * H + j] += 0.0 * d;", 0),
     ("bwd_residual_grad_subtracted", "                dh[i * H + j] += d;", "                dh[i * H + j] -= d;", 0),
+    ("rope_pairs_neighbours", "double x1 = load_elem(x, x_dt, base + j + half);",
+     "double x1 = load_elem(x, x_dt, base + (j + 1) % head_dim);", 0),
+    ("rope_out0_sign", "o[j] = x0 * c - x1 * sn;", "o[j] = x0 * c + x1 * sn;", 0),
+    ("rope_out1_terms_swapped", "o[j + half] = x0 * sn + x1 * c;", "o[j + half] = x0 * c + x1 * sn;", 0),
+    ("rope_cos_from_sin_table", "double c = load_elem(cos_t, t_dt,", "double c = load_elem(cos_t ? sin_t : cos_t, t_dt,",
+     0),
+    ("rope_table_row_is_batch", "const int64_t srow = r % seq_len;", "const int64_t srow = r / seq_len;", 0),
+    ("rope_table_row_clamped", "const int64_t srow = r % seq_len;",
+     "const int64_t srow = r < seq_len ? r : seq_len - 1;", 0),
+    ("rope_table_second_half", "double c = load_elem(cos_t, t_dt, srow * table_stride + j);",
+     "double c = load_elem(cos_t, t_dt, srow * table_stride + j + half);", 0),
+    ("rope_transpose_ignored", "if (transpose) sn = -sn;", "if (transpose > 1) sn = -sn;", 0),
     ("round_half_away", "double q = rint(a / quantum);", "double q = round(a / quantum);", 0),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);", 0),
     ("f16_no_subnormal_quantum", "if (lead < emin) lead = emin;", "if (lead < emin - 30) lead = emin - 30;", 0),

@@ -11,6 +11,10 @@ functions raise.
     y, res_out = rmsnorm_fwd_residual(x, residual, w, eps)
     y = rmsnorm_adaln_fwd(x, w, scale, shift, eps)  # scale/shift [B,S,H] or [B,1,H]
     dx, dw = rmsnorm_bwd(dy, x, w, rrms)
+    dh, dw = rmsnorm_bwd_residual(dy, res_out, dres, w, rrms)  # grad of x and residual
+
+transformer_normalization_amd.autograd wraps these as torch.autograd
+Functions and nn.Modules for training.
 """
 
 from __future__ import annotations
@@ -26,7 +30,7 @@ RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
 STATUS = {0: "RMSN_OK", 1: "RMSN_ERR_INVALID_ARG", 2: "RMSN_ERR_UNSUPPORTED", 3: "RMSN_ERR_WORKSPACE",
           4: "RMSN_ERR_HIP"}
 EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_adaln_fwd", "rmsnorm_bwd_workspace_bytes",
-            "rmsnorm_bwd", "rmsnorm_status_string", "rmsnorm_last_error")
+            "rmsnorm_bwd", "rmsnorm_bwd_residual", "rmsnorm_status_string", "rmsnorm_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -58,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
         lib.rmsnorm_bwd_workspace_bytes.restype = sz
         lib.rmsnorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32, i32, vp]
+        lib.rmsnorm_bwd_residual.restype = i32
+        lib.rmsnorm_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32,
+                                             i32, vp]
         lib.rmsnorm_bwd.restype = i32
         lib.rmsnorm_status_string.argtypes = [i32]
         lib.rmsnorm_status_string.restype = ctypes.c_char_p
@@ -240,19 +247,22 @@ def rmsnorm_bwd_workspace_bytes(M: int, H: int) -> int:
     return int(load_library().rmsnorm_bwd_workspace_bytes(M, H))
 
 
-def rmsnorm_bwd(dy, x, weight, rrms, dx=None, dw=None, workspace=None, want_dw: bool = True):
-    """Gradients of RMSNorm from the saved per-row rrms.
-
-    Returns (dx, dw); dw (float32, shape (H,)) is None for a weightless norm
-    or when want_dw is False.  dx may be dy or x itself."""
+def _bwd(dy, x, dres, weight, rrms, dx, dw, workspace, want_dw):
     torch = _torch()
     lib = load_library()
     M, H, xs = _rows(x, "x")
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise ValueError("dy must match x in shape and dtype")
     _, _, dys = _rows(dy, "dy")
+    drs = 0
+    if dres is not None:
+        if dres.shape != x.shape or dres.dtype != x.dtype:
+            raise ValueError("dres must match x in shape and dtype")
+        _, _, drs = _rows(dres, "dres")
     if dx is None:
         dx = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if dx.shape != x.shape or dx.dtype != x.dtype:
+        raise ValueError("dx must match x in shape and dtype")
     _, _, dxs = _rows(dx, "dx")
     if rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous():
         raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
@@ -269,10 +279,34 @@ def rmsnorm_bwd(dy, x, weight, rrms, dx=None, dw=None, workspace=None, want_dw: 
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
         ws_bytes = workspace.numel() * workspace.element_size()
     wcode = _dtype_code(weight) if weight is not None else _dtype_code(x)
-    st = lib.rmsnorm_bwd(_ptr(dy), dys, _ptr(x), xs, _ptr(weight), _ptr(rrms), _ptr(dx), dxs, _ptr(dw),
-                         _ptr(workspace), ws_bytes, M, H, _dtype_code(x), wcode, _stream(x))
+    if dres is None:
+        st = lib.rmsnorm_bwd(_ptr(dy), dys, _ptr(x), xs, _ptr(weight), _ptr(rrms), _ptr(dx), dxs, _ptr(dw),
+                             _ptr(workspace), ws_bytes, M, H, _dtype_code(x), wcode, _stream(x))
+    else:
+        st = lib.rmsnorm_bwd_residual(_ptr(dy), dys, _ptr(x), xs, _ptr(dres), drs, _ptr(weight), _ptr(rrms),
+                                      _ptr(dx), dxs, _ptr(dw), _ptr(workspace), ws_bytes, M, H, _dtype_code(x), wcode,
+                                      _stream(x))
     _check(lib, st)
     return dx, dw
+
+
+def rmsnorm_bwd(dy, x, weight, rrms, dx=None, dw=None, workspace=None, want_dw: bool = True):
+    """Gradients of RMSNorm from the saved per-row rrms.
+
+    Returns (dx, dw); dw (float32, shape (H,)) is None for a weightless norm
+    or when want_dw is False.  dx may be dy or x itself."""
+    return _bwd(dy, x, None, weight, rrms, dx, dw, workspace, want_dw)
+
+
+def rmsnorm_bwd_residual(dy, residual_out, dres, weight, rrms, dh=None, dw=None, workspace=None,
+                         want_dw: bool = True):
+    """Gradients of the fused residual pre-norm (rmsnorm_fwd_residual).
+
+    residual_out is the post-add stream h the forward wrote; dres is the
+    gradient arriving on it (None when it feeds nothing).  Returns (dh, dw):
+    dh = norm backward through h + dres is the gradient of both x and the
+    residual input.  dh may be dy, residual_out or dres itself."""
+    return _bwd(dy, residual_out, dres, weight, rrms, dh, dw, workspace, want_dw)
 
 
 def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: int = 0) -> None:

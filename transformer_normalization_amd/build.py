@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librmsnorm.so")
-SOURCES = ["rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_adaln.hip", "kernels_bwd.hip"]
+SOURCES = ["rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_adaln.hip", "kernels_bwd.hip",
+           "kernels_bwd_residual.hip"]
 ARCH = "gfx950"
 
 

@@ -7,6 +7,10 @@
 //   c  = sum over the row of g * xn
 //   dx = rrms * g - xn * ((c * (1/H)) * rrms)
 //   dw[j] = sum over rows of dy * xn
+// With RES (the backward of the fused residual pre-norm, whose forward
+// writes h = x + r back as the next residual stream), x is that stored h and
+// the gradient arriving on the residual stream, dres, is added before the
+// single rounding: dh = dx + dres, the gradient of both x and r.
 //
 // Kernel 1 (rmsnorm_bwd_kernel): workgroup b owns the rows b, b+P, b+2P, ...
 // (or, optionally, a contiguous block of rows) and walks them one row at a
@@ -35,9 +39,10 @@ struct BwdParams {
     const void *x;
     const void *w;       // may be null (weightless)
     const float *rrms;
+    const void *dres;     // RES: gradient on the residual-stream output
     void *dx;
     float *partial;      // P x H float32, or null when dw is not wanted
-    int64_t dys, xs, dxs;  // row strides, elements
+    int64_t dys, xs, dxs, drs;  // row strides, elements
     int64_t M;
     int64_t rows_per_wg;  // contiguous order: rows of one workgroup
     int interleave;       // 1: workgroup b owns rows b, b+P, b+2P, ...
@@ -48,7 +53,7 @@ struct BwdParams {
     float inv_h;
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool TWO_PASS, bool NT, int MAXT>
+template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;  // == blockDim.x
@@ -90,10 +95,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // per lane, and taken with v_readlane, so that no vector load inside
         // the loop makes the in-order memory counter wait for the prefetch.
         // depth 2 for small tiles, 1 where three rows would not fit the
-        // register budget (packed 32-bit words of x and dy per row)
-        constexpr int WORDS = 2 * VPT * VEC * Fmt<XDT>::bytes / 4;
+        // register budget (32-bit words holding x, dy and dres of one row)
+        constexpr int WORDS = (RES ? 3 : 2) * VPT * (int)(sizeof(Raw<XDT, VEC>) / 4);
         constexpr int PF = WORDS <= 16 ? 2 : 1;
-        Raw<XDT, VEC> xb[PF + 1][VPT], db[PF + 1][VPT];
+        Raw<XDT, VEC> xb[PF + 1][VPT], db[PF + 1][VPT], gb[RES ? PF + 1 : 1][VPT];
         const int lane = t & 63;
         // rows in chunks of 64: one rrms value per lane for the chunk, loaded
         // before the chunk's row loads so that no wait inside the row loop
@@ -107,7 +112,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             // vector indices past the row are clamped to its last vector
             // (same addresses within one wave access: no extra traffic) and
             // masked at use.
-            auto load_row = [&](int64_t j, Raw<XDT, VEC> *xd, Raw<XDT, VEC> *dd) {
+            auto load_row = [&](int64_t j, Raw<XDT, VEC> *xd, Raw<XDT, VEC> *dd, Raw<XDT, VEC> *gd) {
                 const int64_t row = start + j * step;
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
@@ -115,9 +120,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     const int v = vv < p.nvec ? vv : p.nvec - 1;
                     xd[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
                     dd[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
+                    if constexpr (RES) gd[k].template load<NT>(p.dres, row * p.drs + (int64_t)v * VEC);
                 }
             };
-            auto process_row = [&](int64_t j, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr) {
+            auto process_row = [&](int64_t j, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr, Raw<XDT, VEC> *gr) {
                 const int64_t row = start + j * step;
                 const float rs = __builtin_bit_cast(
                     float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rr_lane), (int)(j - base)));
@@ -139,6 +145,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     xr[k].opaque();
                     dr[k].opaque();
+                    if constexpr (RES) gr[k].opaque();
                 }
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
@@ -154,6 +161,12 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                             o[e] = rs * (dv[e] * wv[e]) - xn * s;
                             dwa[k][e] = __builtin_fmaf(dv[e], xn, dwa[k][e]);
                         }
+                        if constexpr (RES) {
+                            float gv[VEC];
+                            gr[k].widen_to(gv);
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) o[e] += gv[e];
+                        }
                         store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
                     }
                 }
@@ -161,7 +174,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             // prologue: unconditional too (a chunk shorter than PF rows reads
             // its last row again rather than branching)
 #pragma unroll
-            for (int j = 0; j < PF; ++j) load_row(base + j < cend ? base + j : cend - 1, xb[j], db[j]);
+            for (int j = 0; j < PF; ++j) load_row(base + j < cend ? base + j : cend - 1, xb[j], db[j], gb[RES ? j : 0]);
             // Steady state, unrolled by PF+1 so that row r always lives in
             // slot (r - base) % (PF+1) (copying registers whose loads are in
             // flight would wait for them).  It runs while every prefetched row
@@ -170,8 +183,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             for (; row + 2 * PF < cend; row += PF + 1) {
 #pragma unroll
                 for (int u = 0; u <= PF; ++u) {
-                    load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)]);
-                    process_row(row + u, xb[u], db[u]);
+                    load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)],
+                             gb[RES ? (u + PF) % (PF + 1) : 0]);
+                    process_row(row + u, xb[u], db[u], gb[RES ? u : 0]);
                 }
             }
             // the last rows (at most 2*PF), with conditional prefetch
@@ -179,8 +193,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             for (int u = 0; u < 2 * PF; ++u) {
                 if (row + u < cend) {
                     if (row + u + PF < cend)
-                        load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)]);
-                    process_row(row + u, xb[u % (PF + 1)], db[u % (PF + 1)]);
+                        load_row(row + u + PF, xb[(u + PF) % (PF + 1)], db[(u + PF) % (PF + 1)],
+                                 gb[RES ? (u + PF) % (PF + 1) : 0]);
+                    process_row(row + u, xb[u % (PF + 1)], db[u % (PF + 1)], gb[RES ? u % (PF + 1) : 0]);
                 }
             }
         }
@@ -243,6 +258,12 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                         for (int e = 0; e < VEC; ++e) {
                             xn[e] = xv[e] * rs;
                             o[e] = rs * (dv[e] * wv[e]) - xn[e] * s;
+                        }
+                        if constexpr (RES) {
+                            float gv[VEC];
+                            load_elems<XDT, VEC, NT>(p.dres, row * p.drs + (int64_t)v * VEC, gv);
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) o[e] += gv[e];
                         }
                         store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
                         if (part != nullptr) {

@@ -1,8 +1,8 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
-// kernels_bwd.hip) so that they
-// compile in parallel; the host code only sees these functions.
+// kernels_bwd.hip, kernels_bwd_residual.hip) so that they compile in
+// parallel; the host code only sees these functions.
 #pragma once
 
 #include "bwd_kernels.hpp"
@@ -20,7 +20,9 @@ fwd_fn fwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bo
 fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 // AdaLN: wdt is the format of the weight, scale and shift
 fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
-bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
+bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
+// the backward of the fused residual pre-norm (adds the residual-stream gradient)
+bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 const void *dw_finalize_kernel();
 
 }  // namespace rmsn

@@ -1,5 +1,6 @@
-// kernels_bwd.hip -- instantiations of the backward kernels (bwd_kernels.hpp).
-#include "kernel_tables.hpp"
+// kernels_bwd.hip -- instantiations of the backward kernels (bwd_kernels.hpp)
+// and the dw finalize kernel.
+#include "bwd_table.hpp"
 
 namespace rmsn {
 
@@ -31,59 +32,9 @@ __global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restr
     }
 }
 
-
-namespace {
-
-template <int XDT, int WDT, int VEC, bool NT>
-bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
-    if (two_pass) {
-        constexpr int V = VEC > 1 ? 4 : 8;
-        return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, true, NT, 1024>;
-    }
-    switch (vpt) {
-    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, false, NT, bwd_max_threads(1 * VEC)>;
-    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, false, NT, bwd_max_threads(2 * VEC)>;
-    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, false, NT, bwd_max_threads(4 * VEC)>;
-    default: break;
-    }
-    if constexpr (VEC == 1) {
-        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, false, NT, bwd_max_threads(8 * VEC)>;
-    }
-    if constexpr (VEC > 1) {
-        switch (vpt) {
-        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, false, NT, bwd_max_threads(3 * VEC)>;
-        default: break;
-        }
-    }
-    return nullptr;
-}
-
-template <int XDT, int WDT, bool NT>
-bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass) {
-    constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1, NT>(vpt, two_pass) : bwd_kernel_for<XDT, WDT, V, NT>(vpt, two_pass);
-}
-
-template <bool NT>
-bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
-    const bool wf32 = (wdt == RMSN_F32);
-    switch (xdt) {
-    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32, NT>(vec, vpt, two_pass);
-    case RMSN_F16:
-        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_F16, DT_F16, NT>(vec, vpt, two_pass);
-    case RMSN_BF16:
-        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_BF16, DT_BF16, NT>(vec, vpt, two_pass);
-    }
-    return nullptr;
-}
-
-
-}  // namespace
-
-bwd_fn bwd_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
-    return nt ? bwd_lookup_nt<true>(xdt, wdt, vec, vpt, two_pass) : bwd_lookup_nt<false>(xdt, wdt, vec, vpt, two_pass);
+bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
+    return nt ? tables::bwd_lookup_nt<false, true>(xdt, wdt, vec, vpt, two_pass)
+              : tables::bwd_lookup_nt<false, false>(xdt, wdt, vec, vpt, two_pass);
 }
 
 const void *dw_finalize_kernel() { return (const void *)rmsnorm_dw_finalize; }

@@ -222,13 +222,14 @@ Override get_override(int which) {
 }
 
 // vectors per thread available as kernel instantiations
-enum class Kind { Fwd, FwdResid, FwdAdaln, Bwd };
+enum class Kind { Fwd, FwdResid, FwdAdaln, Bwd, BwdRes };
 constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
 constexpr int kBwdVecVpt[] = {1, 2, 3, 4};
 constexpr int kScalarVpt[] = {1, 2, 4, 8};
 // largest workgroup each register tile may use (the kernels' launch bounds)
 int max_threads_for(Kind kind, int vpt, int vec) {
     return kind == Kind::Bwd        ? bwd_max_threads(vpt * vec)
+           : kind == Kind::BwdRes   ? bwd_max_threads(vpt * vec, true)
            : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID)
            : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN)
                                     : fwd_max_threads(vpt * vec, MODE_PLAIN);
@@ -251,8 +252,9 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     Geom g{};
     g.vec = vec;
     g.nvec = (H + vec - 1) / vec;
-    const int *set = vec == 1 ? kScalarVpt : kind == Kind::Bwd ? kBwdVecVpt : kFwdVecVpt;
-    const int nset = vec == 1 ? 4 : kind == Kind::Bwd ? 4 : 6;
+    const bool bwd = kind == Kind::Bwd || kind == Kind::BwdRes;
+    const int *set = vec == 1 ? kScalarVpt : bwd ? kBwdVecVpt : kFwdVecVpt;
+    const int nset = vec == 1 ? 4 : bwd ? 4 : 6;
     double best = 1e30;
     for (int i = 0; i < nset; ++i) {
         const int vpt = set[i];
@@ -455,15 +457,19 @@ size_t bwd_workspace(int64_t M, int64_t H) {
     return (size_t)P * (size_t)H * sizeof(float);
 }
 
-rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, const void *w, const float *rrms,
-                       void *dx, int64_t dxs, float *dw, void *ws, size_t ws_bytes, int64_t M, int64_t H,
-                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
+// dres == nullptr: the plain backward; otherwise the backward of the fused
+// residual pre-norm, which adds dres (rows drs apart) to dx.
+rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, const void *dres, int64_t drs,
+                       const void *w, const float *rrms, void *dx, int64_t dxs, float *dw, void *ws, size_t ws_bytes,
+                       int64_t M, int64_t H, rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
     rmsn_status_t st = check_common(M, H, xdt, w, wdt);
     if (st != RMSN_OK) return st;
     const int eb = dtype_bytes(xdt);
+    const bool res = dres != nullptr;
     if ((st = check_stride("dy_stride", dys, M, H, eb)) != RMSN_OK) return st;
     if ((st = check_stride("x_stride", xs, M, H, eb)) != RMSN_OK) return st;
     if ((st = check_stride("dx_stride", dxs, M, H, eb)) != RMSN_OK) return st;
+    if (res && (st = check_stride("dres_stride", drs, M, H, eb)) != RMSN_OK) return st;
     if (dw != nullptr && w == nullptr)
         return fail(RMSN_ERR_INVALID_ARG, "dw requested for a weightless norm (w is NULL)");
     if (M > 0) {
@@ -481,16 +487,16 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     }
     const int wb = w ? dtype_bytes(wdt) : 1;
     if (M > 0) {
-        Region ins[4] = {mat("dy", dy, dys, M, H, eb), mat("x", x, xs, M, H, eb), vec("w", w, H, wb),
-                         vec("rrms", rrms, M, 4)};
+        Region ins[5] = {mat("dy", dy, dys, M, H, eb), mat("x", x, xs, M, H, eb), vec("w", w, H, wb),
+                         vec("rrms", rrms, M, 4), mat("dres", dres, drs, M, H, eb)};
         Region outs[3] = {mat("dx", dx, dxs, M, H, eb), vec("dw", dw, H, 4),
                           vec("workspace", dw ? ws : nullptr, (int64_t)need, 1)};
-        if ((st = check_overlap(outs, 3, ins, 4)) != RMSN_OK) return st;
+        if ((st = check_overlap(outs, 3, ins, 5)) != RMSN_OK) return st;
         for (int i = 1; i < 3; ++i)
             for (const Region &in : ins)
                 if (outs[i].present && in.present && outs[i].overlaps(in))
                     return fail(RMSN_ERR_INVALID_ARG, "%s overlaps input %s", outs[i].name, in.name);
-        // dx may be the same buffer as dy or x, but never w or rrms
+        // dx may be the same buffer as dy, x or dres, but never w or rrms
         if (outs[0].overlaps(ins[2]) && ins[2].present) return fail(RMSN_ERR_INVALID_ARG, "dx overlaps w");
         if (outs[0].overlaps(ins[3])) return fail(RMSN_ERR_INVALID_ARG, "dx overlaps rrms");
     } else if (dw == nullptr) {
@@ -510,8 +516,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     const int vecw = 16 / eb;
     const bool vec_ok = (H % vecw) == 0 && aligned16(dy) && aligned16(x) && aligned16(dx) &&
                         (dys * eb) % 16 == 0 && (xs * eb) % 16 == 0 && (dxs * eb) % 16 == 0 &&
-                        (w == nullptr || aligned16(w));
-    Geom g = pick_row_geom(Kind::Bwd, (int)H, vec_ok ? vecw : 1, 8);
+                        (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && (drs * eb) % 16 == 0));
+    const Kind kind = res ? Kind::BwdRes : Kind::Bwd;
+    Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, 8);
     int64_t P = 0;  // 0: chosen from the device below
     // rows interleaved across workgroups: the rows in flight at any moment are
     // neighbours in memory, as in the forward's one-row-per-workgroup grid
@@ -521,7 +528,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         Geom o = g;
         o.vpt = ov.a;
         o.wpr = ov.b;
-        const int maxt = max_threads_for(Kind::Bwd, o.vpt, o.vec);
+        const int maxt = max_threads_for(kind, o.vpt, o.vec);
         if (o.vpt < 1 || o.wpr < 1 || o.wpr * 64 > maxt)
             return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: bad tile vpt %d wpr %d", o.vpt, o.wpr);
         const int chunk = 64 * o.wpr * o.vpt;
@@ -534,8 +541,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (ov.d == 1) interleave = true;
         if (ov.d == 2) interleave = false;
     }
-    const bool nt = use_streaming(3 * M * H * eb);
-    bwd_fn fn = bwd_lookup(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
+    const bool nt = use_streaming((res ? 4 : 3) * M * H * eb);
+    bwd_fn fn = res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
+                    : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -555,11 +563,13 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     p.x = x;
     p.w = w;
     p.rrms = rrms;
+    p.dres = dres;
     p.dx = dx;
     p.partial = dw != nullptr ? static_cast<float *>(ws) : nullptr;
     p.dys = dys;
     p.xs = xs;
     p.dxs = dxs;
+    p.drs = drs;
     p.M = M;
     p.rows_per_wg = rows_per;
     p.interleave = interleave ? 1 : 0;
@@ -569,7 +579,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     p.nchunks = g.nchunks;
     p.inv_h = (float)(1.0 / (double)H);
     void *args[] = {&p};
-    if ((st = launch((const void *)fn, dim3((unsigned)P), dim3(64 * g.wpr), args, stream, "rmsnorm_bwd")) != RMSN_OK)
+    if ((st = launch((const void *)fn, dim3((unsigned)P), dim3(64 * g.wpr), args, stream,
+                     res ? "rmsnorm_bwd_residual" : "rmsnorm_bwd")) != RMSN_OK)
         return st;
     if (dw != nullptr) {
         const float *part = p.partial;
@@ -629,8 +640,18 @@ RMSN_API rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void
                           const float *rrms, void *dx, int64_t dx_stride, float *dw, void *workspace,
                           size_t workspace_bytes, int64_t M, int64_t H, rmsn_dtype_t x_dtype,
                           rmsn_dtype_t w_dtype, hipStream_t stream) {
-    rmsn_status_t s = bwd_impl(dy, dy_stride, x, x_stride, w, rrms, dx, dx_stride, dw, workspace, workspace_bytes,
-                               M, H, x_dtype, w_dtype, stream);
+    rmsn_status_t s = bwd_impl(dy, dy_stride, x, x_stride, nullptr, 0, w, rrms, dx, dx_stride, dw, workspace,
+                               workspace_bytes, M, H, x_dtype, w_dtype, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t rmsnorm_bwd_residual(const void *dy, int64_t dy_stride, const void *h, int64_t h_stride,
+                                            const void *dres, int64_t dres_stride, const void *w, const float *rrms,
+                                            void *dh, int64_t dh_stride, float *dw, void *workspace,
+                                            size_t workspace_bytes, int64_t M, int64_t H, rmsn_dtype_t x_dtype,
+                                            rmsn_dtype_t w_dtype, hipStream_t stream) {
+    rmsn_status_t s = bwd_impl(dy, dy_stride, h, h_stride, dres, dres_stride, w, rrms, dh, dh_stride, dw, workspace,
+                               workspace_bytes, M, H, x_dtype, w_dtype, stream);
     return s == RMSN_OK ? ok() : s;
 }
 

@@ -77,8 +77,9 @@ class Oracle:
         lib.orc_bwd.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
         lib.orc_adaln_fwd.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i32, i32, i64, i64, dp, vp, vp]
         lib.orc_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
+        lib.orc_rope.argtypes = [vp, i64, i64, vp, vp, i64, i32, i32, i64, i64, i64, i64, i32, vp]
         for f in (lib.orc_decode, lib.orc_encode, lib.orc_fwd, lib.orc_fwd_residual, lib.orc_bwd,
-                  lib.orc_adaln_fwd, lib.orc_bwd_residual):
+                  lib.orc_adaln_fwd, lib.orc_bwd_residual, lib.orc_rope):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -202,6 +203,38 @@ class Oracle:
         return dh, dw, terms
 
 
+    def rope(self, x, cos, sin, dtype: str, tdtype: str | None = None, transpose: bool = False):
+        """Rotate-half RoPE of x (batch, seq_len, heads, head_dim) with
+        (seq_len, >= head_dim/2) cos and sin tables -> float64 array of x's
+        shape.  x may be any view whose last axis is contiguous and whose
+        (heads, head_dim) block of a token row has one head stride."""
+        x = np.asarray(x)
+        if x.dtype != np.dtype(_NP[dtype]):
+            raise TypeError(f"expected {_NP[dtype]} storage for {dtype}, got {x.dtype}")
+        if x.ndim != 4:
+            raise ValueError("x must be (batch, seq_len, heads, head_dim)")
+        B, S, NH, D = x.shape
+        it = x.itemsize
+        if (x.strides[3] != it or x.strides[2] % it or x.strides[1] % it or x.strides[0] != S * x.strides[1]
+                or x.strides[2] < D * it or x.strides[1] < NH * x.strides[2]):
+            x = np.ascontiguousarray(x)
+        hs, rs = x.strides[2] // it, x.strides[1] // it
+        td = tdtype or dtype
+        cos, sin = np.asarray(cos), np.asarray(sin)
+        for t in (cos, sin):
+            if t.dtype != np.dtype(_NP[td]):
+                raise TypeError(f"expected {_NP[td]} table storage for {td}, got {t.dtype}")
+        if cos.shape != sin.shape or cos.ndim != 2 or cos.shape[0] != S:
+            raise ValueError("cos and sin must both be (seq_len, >= head_dim/2)")
+        cos, sin = np.ascontiguousarray(cos), np.ascontiguousarray(sin)
+        out = np.empty((B, S, NH, D), dtype=np.float64)
+        rc = self.lib.orc_rope(_ptr(x), rs, hs, _ptr(cos), _ptr(sin), cos.shape[1], CODES[dtype], CODES[td], B, S,
+                               NH, D, 1 if transpose else 0, _ptr(out))
+        if rc != 0:
+            raise ValueError("orc_rope rejected its arguments")
+        return out
+
+
 def default() -> Oracle:
     """The oracle built from rmsnorm_oracle.c (rebuilt when the source is newer)."""
     global _default
@@ -239,3 +272,7 @@ def adaln_fwd(x, w, scale, shift, rows_per_cond, eps, dtype, wdtype=None, cdtype
 
 def bwd_residual(dy, h, dres, w, rrms, dtype, wdtype=None, want_dw=True):
     return default().bwd_residual(dy, h, dres, w, rrms, dtype, wdtype, want_dw)
+
+
+def rope(x, cos, sin, dtype, tdtype=None, transpose=False):
+    return default().rope(x, cos, sin, dtype, tdtype, transpose)

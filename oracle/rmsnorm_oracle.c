@@ -30,6 +30,15 @@
  *   - AdaLN: the same page, "Core Kernel Implementations", 4. AdaLN, and its
  *     "Template 4": norm(x) * weight * (1 + scale) + shift, with scale and
  *     shift one row per token ([B, S, H]) or one row per batch ([B, 1, H]).
+ *   - RoPE apply (the same page, "Core Kernel Implementations", 2. RoPE 3D,
+ *     and "Triton kernel templates", Template 2): q or k of shape
+ *     [batch, seq_len, heads, head_dim] is rotated pairwise in the
+ *     rotate-half layout, element j with element j + head_dim/2, by the angle
+ *     whose cos and sin sit at column j of the token's row of [seq_len,
+ *     head_dim] tables; with the batch folded into the rows, the table row is
+ *     the flat row index modulo seq_len.  Only the first head_dim/2 columns of
+ *     a table row are read.  The transposed rotation (sin negated) is the
+ *     gradient of the rotation with respect to its input, and its inverse.
  *
  * Everything is computed in IEEE float64 from exactly decoded inputs, one row
  * at a time, in the plain left-to-right order of the definition.  Rounding to
@@ -310,6 +319,45 @@ int orc_bwd_residual(const void *dy, int64_t dy_stride, const void *h, int64_t h
                 dh[i * H + j] += d;
                 if (dh_terms) dh_terms[i * H + j] += fabs(d);
             }
+    }
+    return 0;
+}
+
+/* ---- RoPE apply (rotate-half) ------------------------------------------------
+ * x: rows = batch * seq_len token rows, row r at r * x_row_stride, head h at
+ * + h * x_head_stride, head_dim contiguous elements.  cos and sin: seq_len
+ * rows table_stride apart (>= head_dim / 2 columns read).  out: float64,
+ * contiguous (rows, heads, head_dim).  For each token row r, head h and
+ * j < head_dim / 2, with s = r mod seq_len:
+ *   out[r][h][j]            = x0 * c - x1 * sn
+ *   out[r][h][j + half]     = x0 * sn + x1 * c
+ * where x0 = x[r][h][j], x1 = x[r][h][j + half], c = cos[s][j], sn = sin[s][j]
+ * (sn = -sin[s][j] when transpose != 0).
+ */
+int orc_rope(const void *x, int64_t x_row_stride, int64_t x_head_stride, const void *cos_t, const void *sin_t,
+             int64_t table_stride, int x_dt, int t_dt, int64_t batch, int64_t seq_len, int64_t heads,
+             int64_t head_dim, int transpose, double *out) {
+    if (!orc_valid_code(x_dt) || !orc_valid_code(t_dt) || batch < 0 || seq_len < 1 || heads < 1 ||
+        head_dim < 2 || head_dim % 2 != 0)
+        return -1;
+    const int64_t half = head_dim / 2;
+    if (table_stride < half || x_head_stride < head_dim || x_row_stride < heads * x_head_stride) return -1;
+    const int64_t rows = batch * seq_len;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t srow = r % seq_len;
+        for (int64_t h = 0; h < heads; ++h) {
+            const int64_t base = r * x_row_stride + h * x_head_stride;
+            double *o = out + (r * heads + h) * head_dim;
+            for (int64_t j = 0; j < half; ++j) {
+                double x0 = load_elem(x, x_dt, base + j);
+                double x1 = load_elem(x, x_dt, base + j + half);
+                double c = load_elem(cos_t, t_dt, srow * table_stride + j);
+                double sn = load_elem(sin_t, t_dt, srow * table_stride + j);
+                if (transpose) sn = -sn;
+                o[j] = x0 * c - x1 * sn;
+                o[j + half] = x0 * sn + x1 * c;
+            }
+        }
     }
     return 0;
 }

@@ -1,17 +1,24 @@
 """Throughput of the gfx950 RMSNorm library on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--graph]
 
-A step is one launch of the library on one batch of seeded synthetic input
-already resident in HBM.  Batches rotate over enough buffer sets (>= 1 GiB per
-cycle) that no step finds its data in the last-level cache.  W untimed steps,
-then exactly K steps between two synchronisations, timed with HIP events on
-the stream the kernels are launched on.  One JSON line is printed.
+A step is one library call (the whole hot path of the workload: the forward
+kernel, or the backward kernel and its dw finalize, or the RoPE kernel) on
+one batch of seeded synthetic input already resident in HBM.  Batches rotate
+over enough buffer sets (>= 1 GiB per cycle) that no step finds its data in
+the last-level cache.  W untimed steps, then exactly K steps between two
+synchronisations, timed with HIP events on the stream the kernels are
+launched on.  One JSON line is printed.
 
 Workloads (default: the forward at bf16 M=8192 H=4096):
   fwd_bf16_8192x4096, fwd_f32_64x512, fwd_bf16_32768x2048, fwd_bf16_32768x2048_noweight,
   fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144,
-  bwd_residual_bf16_16384x8192, adaln_bf16_2x4096x2048_batchcond, adaln_bf16_2x4096x2048_tokencond
+  bwd_residual_bf16_16384x8192, adaln_bf16_2x4096x2048_batchcond, adaln_bf16_2x4096x2048_tokencond,
+  rope_bf16_2x8064x32x64, rope_bf16_2x4096x32x128
+
+--graph captures the timed steps in HIP graphs (blocks of steps, replayed) so
+that host launch overhead cannot leave the GPU idle between short kernels;
+the kernels and their arguments are the same as in eager launches.
 
 The CPU baseline is the float64 oracle run on the host over a sample of the
 same workload (reported beside the GPU figure, never a target).
@@ -22,6 +29,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -33,7 +41,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 METRIC = "RMSNorm fwd achieved HBM GB/s (% of peak) + rows/s, bf16 M=8192 H=4096"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30
-
+GRAPH_BLOCK = 100  # steps per captured graph
 
 _FWD = ("numerics.hpp", "fwd_kernels.hpp", "fwd_table.hpp", "kernel_tables.hpp")
 _BWD = ("numerics.hpp", "bwd_kernels.hpp", "bwd_table.hpp", "kernel_tables.hpp", "kernels_bwd.hip")
@@ -43,6 +51,25 @@ KERNEL_SOURCES = {
     "bwd": _BWD + ("rmsnorm_api.hip",),
     "bwd_residual": _BWD + ("kernels_bwd_residual.hip", "rmsnorm_api.hip"),
     "adaln": _FWD + ("kernels_adaln.hip", "rmsnorm_api.hip"),
+    "rope": ("numerics.hpp", "rope_kernels.hpp", "kernel_tables.hpp", "kernels_rope.hip", "rope_api.hip"),
+}
+# the kernel whose launches the counters describe
+KERNEL_KEY = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
+              "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel"}
+
+WORKLOADS = {
+    "fwd_bf16_8192x4096": ("fwd_bf16_8192x4096", True),
+    "fwd_f32_64x512": ("fwd_f32_64x512", True),
+    "fwd_bf16_32768x2048": ("fwd_bf16_32768x2048", True),
+    "fwd_bf16_32768x2048_noweight": ("fwd_bf16_32768x2048", False),
+    "fwd_f16_32768x2048_outliers": ("fwd_f16_32768x2048_outliers", True),
+    "fwd_residual_bf16_16384x8192": ("fwd_residual_bf16_16384x8192", True),
+    "bwd_bf16_8192x6144": ("bwd_bf16_8192x6144", True),
+    "bwd_residual_bf16_16384x8192": ("bwd_residual_bf16_16384x8192", True),
+    "adaln_bf16_2x4096x2048_batchcond": ("adaln_bf16_2x4096x2048_batchcond", True),
+    "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
+    "rope_bf16_2x8064x32x64": ("rope_bf16_2x8064x32x64", True),
+    "rope_bf16_2x4096x32x128": ("rope_bf16_2x4096x32x128", True),
 }
 
 
@@ -79,10 +106,24 @@ def stored_traffic(workload: str):
         return None
 
 
-def algorithmic_bytes(kind, M, H, esize, wsize, weighted, cond_rows=0):
-    """Bytes the method must move once: inputs, weight, outputs, rrms if used."""
-    mat = M * H * esize
-    w = H * wsize if weighted else 0
+def _size(fmt):
+    return 4 if fmt == "f32" else 2
+
+
+def algorithmic_bytes(spec, weighted, rows=None):
+    """Bytes the method must move once per step: inputs, weight, outputs,
+    rrms if used; for RoPE, x and out plus the first half of each table row.
+    rows (positions, for RoPE) restricts the count to a leading sample."""
+    kind = spec["kind"]
+    if kind == "rope":
+        B, NH, D = spec["B"], spec["NH"], spec["D"]
+        S = spec["S"] if rows is None else rows
+        return 2 * B * S * NH * D * _size(spec["dtype"]) + 2 * S * (D // 2) * _size(spec["tdtype"])
+    M = spec["M"] if rows is None else rows
+    H = spec["H"]
+    mat = M * H * _size(spec["dtype"])
+    wsz = _size(spec["wdtype"])
+    w = H * wsz if weighted else 0
     if kind == "fwd":
         return 2 * mat + w
     if kind == "fwd_residual":
@@ -95,44 +136,53 @@ def algorithmic_bytes(kind, M, H, esize, wsize, weighted, cond_rows=0):
         return 4 * mat + M * 4 + w + H * 4
     if kind == "adaln":
         # x read, y written, w and the scale/shift rows read once
-        return 2 * mat + w + 2 * cond_rows * H * wsize
+        cond_rows = -(-M // spec["rows_per_cond"])
+        return 2 * mat + w + 2 * cond_rows * H * wsz
     raise ValueError(kind)
 
 
-WORKLOADS = {
-    "fwd_bf16_8192x4096": ("fwd_bf16_8192x4096", True),
-    "fwd_f32_64x512": ("fwd_f32_64x512", True),
-    "fwd_bf16_32768x2048": ("fwd_bf16_32768x2048", True),
-    "fwd_bf16_32768x2048_noweight": ("fwd_bf16_32768x2048", False),
-    "fwd_f16_32768x2048_outliers": ("fwd_f16_32768x2048_outliers", True),
-    "fwd_residual_bf16_16384x8192": ("fwd_residual_bf16_16384x8192", True),
-    "bwd_bf16_8192x6144": ("bwd_bf16_8192x6144", True),
-    "bwd_residual_bf16_16384x8192": ("bwd_residual_bf16_16384x8192", True),
-    "adaln_bf16_2x4096x2048_batchcond": ("adaln_bf16_2x4096x2048_batchcond", True),
-    "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
-}
+def x_bytes(spec):
+    """Size of the x tensor (the device copy of known size)."""
+    if spec["kind"] == "rope":
+        return spec["B"] * spec["S"] * spec["NH"] * spec["D"] * _size(spec["dtype"])
+    return spec["M"] * spec["H"] * _size(spec["dtype"])
 
 
-def cpu_baseline(spec, kind, weighted, seconds):
-    """The oracle as it stands, single-threaded, over the workload's rows
-    repeated until `seconds` have passed; reported in GB/s of the same
-    algorithmic bytes."""
+def step_rows(spec):
+    """Rows (token rows for RoPE) one step processes."""
+    return spec["B"] * spec["S"] if spec["kind"] == "rope" else spec["M"]
+
+
+def cpu_baseline(spec, weighted, seconds):
+    """The oracle as it stands, single-threaded, over a leading sample of the
+    workload repeated until `seconds` have passed; reported in GB/s of the
+    same algorithmic bytes."""
     import numpy as np
 
     import oracle
     import synthetic
 
-    rows = min(spec["M"], 1024)
-    d = synthetic.make_inputs(spec["name"], rows=rows)
-    w = d["w"] if weighted else None
-    eps = float(np.float32(spec["eps"]))
-    if kind in ("bwd", "bwd_residual"):
-        _, r = oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
-        r32 = r.astype(np.float32)
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        if kind == "fwd":
+    kind = spec["kind"]
+    if kind == "rope":
+        n = min(spec["S"], 256)
+        d = synthetic.make_inputs(spec["name"], rows=n)
+        sample = f"first {n} of {spec['S']} positions of each of {spec['B']} batches"
+        rows = spec["B"] * n
+    else:
+        n = min(spec["M"], 1024)
+        d = synthetic.make_inputs(spec["name"], rows=n)
+        sample = f"first {n} of {spec['M']} rows"
+        rows = n
+        w = d["w"] if weighted else None
+        eps = float(np.float32(spec["eps"]))
+        if kind in ("bwd", "bwd_residual"):
+            _, r = oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
+            r32 = r.astype(np.float32)
+
+    def once():
+        if kind == "rope":
+            oracle.rope(d["x"], d["cos"], d["sin"], d["dtype"], d["tdtype"])
+        elif kind == "fwd":
             oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
         elif kind == "adaln":
             oracle.adaln_fwd(d["x"], w, d["scale"], d["shift"], d["rows_per_cond"], eps, d["dtype"], d["wdtype"],
@@ -143,20 +193,22 @@ def cpu_baseline(spec, kind, weighted, seconds):
             oracle.bwd_residual(d["dy"], d["x"], d["dres"], w, r32, d["dtype"], d["wdtype"])
         else:
             oracle.bwd(d["dy"], d["x"], w, r32, d["dtype"], d["wdtype"])
+
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        once()
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    es = synthetic.element_size(d["dtype"])
-    ws = synthetic.element_size(d["wdtype"])
-    crows = d["scale"].shape[0] if kind == "adaln" else 0
-    nbytes = algorithmic_bytes(kind, rows, spec["H"], es, ws, weighted, crows) * passes
+    nbytes = algorithmic_bytes(spec, weighted, n) * passes
     return {
         "value": round(nbytes / el / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {rows} of {spec['M']} rows, {passes} passes in {el:.1f} s, float64, one thread",
+        "sample": f"{sample}, {passes} passes in {el:.1f} s, float64, one thread",
         "rows_per_s": round(rows * passes / el, 1),
     }
 
@@ -173,11 +225,8 @@ def summarize_pmc(fetch_csv, write_csv, workload):
 
     name, weighted = WORKLOADS[workload]
     spec = synthetic.WORKLOADS[name]
-    es = synthetic.element_size(spec["dtype"])
-    ws = synthetic.element_size(spec["wdtype"])
-    known_kib = spec["M"] * spec["H"] * es / 1024.0
-    kernel_key = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
-                  "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel"}[spec["kind"]]
+    known_kib = x_bytes(spec) / 1024.0
+    kernel_key = KERNEL_KEY[spec["kind"]]
 
     def read(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -193,11 +242,12 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     w_k, w_n, w_ref, w_rn, _ = read(write_csv, "WRITE_SIZE")
     f_scale, w_scale = known_kib / f_ref, known_kib / w_ref
     hbm = (f_k * f_scale + w_k * w_scale) * 1024.0
-    crows = -(-spec["M"] // spec.get("rows_per_cond", 1)) if spec["kind"] == "adaln" else 0
-    alg = algorithmic_bytes(spec["kind"], spec["M"], spec["H"], es, ws, weighted, crows)
+    alg = algorithmic_bytes(spec, weighted)
+    shape = (f"B={spec['B']} S={spec['S']} heads={spec['NH']} head_dim={spec['D']}" if spec["kind"] == "rope"
+             else f"M={spec['M']} H={spec['H']}")
     lines = [
         f"# HBM traffic per launch of {kname}",
-        f"# workload {workload}: M={spec['M']} H={spec['H']} {spec['dtype']}",
+        f"# workload {workload}: {shape} {spec['dtype']}",
         "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
         f"#   python3 bench.py --workload {workload} --cpu-seconds 0 --steps 20 --warmup 10 --copy-reference",
         "# each scaled by the same counter's reading for device copies of the x tensor",
@@ -218,6 +268,78 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     return "\n".join(lines) + "\n"
 
 
+def setup_steps(spec, weighted, dev, per_step):
+    """Device buffers for the workload, rotated over >= ROTATION_BYTES, and
+    step(i), which launches step i on the current stream and allocates
+    nothing.  Returns (step, number of buffer sets, x of set 0, and a buffer
+    of x's size to copy it into for the copy reference)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    import transformer_normalization_amd as tn
+
+    kind = spec["kind"]
+    d = synthetic.make_inputs(spec["name"])
+    dt = d["dtype"]
+
+    def up(a, fmt):
+        a = np.ascontiguousarray(a)
+        if fmt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    nsets = max(2, -(-ROTATION_BYTES // per_step))
+    x0 = up(d["x"], dt)
+    sets = []
+    for i in range(nsets):
+        s = {"x": x0 if i == 0 else x0.clone(), "y": torch.empty_like(x0)}
+        for key in {"fwd_residual": ("r",), "bwd": ("dy",), "bwd_residual": ("dy", "dres")}.get(kind, ()):
+            s[key] = up(d[key], dt) if i == 0 else sets[0][key].clone()
+        if kind == "fwd_residual":
+            s["ro"] = torch.empty_like(x0)
+        sets.append(s)
+    copy_src, copy_dst = sets[0]["x"], sets[1]["y"]
+
+    if kind == "rope":
+        cos, sin = up(d["cos"], d["tdtype"]), up(d["sin"], d["tdtype"])
+
+        def step(i):
+            s = sets[i % nsets]
+            tn.rope_apply(s["x"], cos, sin, out=s["y"])
+        return step, nsets, copy_src, copy_dst
+
+    eps = spec["eps"]
+    M, H = spec["M"], spec["H"]
+    w = up(d["w"], d["wdtype"]) if weighted else None
+    if kind == "adaln":
+        rpc = spec["rows_per_cond"]
+        shape = (M // rpc, 1, H) if rpc > 1 else (1, M, H)
+        sc, sh = up(d["scale"], d["wdtype"]).view(*shape), up(d["shift"], d["wdtype"]).view(*shape)
+        for i, s in enumerate(sets):
+            s.update(scale=sc if i == 0 else sc.clone(), shift=sh if i == 0 else sh.clone(),
+                     x=s["x"].view(shape[0], -1, H), y=s["y"].view(shape[0], -1, H))
+    if kind in ("bwd", "bwd_residual"):
+        rr = torch.empty(M, dtype=torch.float32, device=dev)
+        tn.rmsnorm_fwd(sets[0]["x"], w, eps, rrms=rr)
+        dw = torch.empty(H, dtype=torch.float32, device=dev)
+        wsp = torch.empty(tn.rmsnorm_bwd_workspace_bytes(M, H), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % nsets]
+        if kind == "fwd":
+            tn.rmsnorm_fwd(s["x"], w, eps, out=s["y"])
+        elif kind == "fwd_residual":
+            tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
+        elif kind == "adaln":
+            tn.rmsnorm_adaln_fwd(s["x"], w, s["scale"], s["shift"], eps, out=s["y"])
+        elif kind == "bwd_residual":
+            tn.rmsnorm_bwd_residual(s["dy"], s["x"], s["dres"], w, rr, dh=s["y"], dw=dw, workspace=wsp)
+        else:
+            tn.rmsnorm_bwd(s["dy"], s["x"], w, rr, dx=s["y"], dw=dw, workspace=wsp)
+    return step, nsets, copy_src, copy_dst
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +347,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="fwd_bf16_8192x4096", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0 skips it)")
+    ap.add_argument("--graph", action="store_true", help="launch the timed steps from captured HIP graphs")
     ap.add_argument("--geom", default="", help="development: forced launch geometry 'vpt,wpr,rpw,grid'")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain device copy of known size (for scaling HBM counters)")
@@ -240,8 +363,10 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows shard across GPUs with no "
               "communication, so per-GPU throughput is the one-GPU figure)", file=sys.stderr)
         sys.exit(2)
+    if args.graph and args.steps % GRAPH_BLOCK:
+        print(f"--graph times whole blocks of {GRAPH_BLOCK} steps: --steps must be a multiple", file=sys.stderr)
+        sys.exit(2)
 
-    import numpy as np
     import torch
 
     import synthetic
@@ -264,84 +389,64 @@ def main():
         tn.set_geometry("bwd" if kind.startswith("bwd") else "fwd", *parts)
 
     dev = torch.device("cuda:0")
-    d = synthetic.make_inputs(name)
-    dt = d["dtype"]
-    M, H = spec["M"], spec["H"]
-    es, ws = synthetic.element_size(dt), synthetic.element_size(d["wdtype"])
-
-    def up(a, fmt):
-        a = np.ascontiguousarray(a)
-        if fmt == "bf16":
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    crows = d["scale"].shape[0] if kind == "adaln" else 0
-    per_set = algorithmic_bytes(kind, M, H, es, ws, weighted, crows)
-    nsets = max(2, -(-ROTATION_BYTES // per_set))
-    x0 = up(d["x"], dt)
-    w = up(d["w"], d["wdtype"]) if weighted else None
-    sets = []
-    for i in range(nsets):
-        s = {"x": x0 if i == 0 else x0.clone(), "y": torch.empty_like(x0)}
-        if kind == "fwd_residual":
-            r0 = up(d["r"], dt) if i == 0 else sets[0]["r"].clone()
-            s.update(r=r0, ro=torch.empty_like(x0))
-        if kind in ("bwd", "bwd_residual"):
-            dy0 = up(d["dy"], dt) if i == 0 else sets[0]["dy"].clone()
-            s.update(dy=dy0)
-        if kind == "bwd_residual":
-            g0 = up(d["dres"], dt) if i == 0 else sets[0]["dres"].clone()
-            s.update(dres=g0)
-        if kind == "adaln":
-            rpc = spec["rows_per_cond"]
-            shape = (M // rpc, 1, H) if rpc > 1 else (1, M, H)
-            sc0 = up(d["scale"], d["wdtype"]).view(*shape) if i == 0 else sets[0]["scale"].clone()
-            sh0 = up(d["shift"], d["wdtype"]).view(*shape) if i == 0 else sets[0]["shift"].clone()
-            s.update(scale=sc0, shift=sh0, x=s["x"].view(shape[0], -1, H), y=s["y"].view(shape[0], -1, H))
-        sets.append(s)
-    del d
-    eps = spec["eps"]
-    if kind in ("bwd", "bwd_residual"):
-        rr = torch.empty(M, dtype=torch.float32, device=dev)
-        tn.rmsnorm_fwd(sets[0]["x"], w, eps, rrms=rr)
-        dw = torch.empty(H, dtype=torch.float32, device=dev)
-        wsp = torch.empty(tn.rmsnorm_bwd_workspace_bytes(M, H), dtype=torch.uint8, device=dev)
+    per_step = algorithmic_bytes(spec, weighted)
+    step, nsets, copy_src, copy_dst = setup_steps(spec, weighted, dev, per_step)
     torch.cuda.synchronize()
-
-    def step(i):
-        s = sets[i % nsets]
-        if kind == "fwd":
-            tn.rmsnorm_fwd(s["x"], w, eps, out=s["y"])
-        elif kind == "fwd_residual":
-            tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
-        elif kind == "adaln":
-            tn.rmsnorm_adaln_fwd(s["x"], w, s["scale"], s["shift"], eps, out=s["y"])
-        elif kind == "bwd_residual":
-            tn.rmsnorm_bwd_residual(s["dy"], s["x"], s["dres"], w, rr, dh=s["y"], dw=dw, workspace=wsp)
-        else:
-            tn.rmsnorm_bwd(s["dy"], s["x"], w, rr, dx=s["y"], dw=dw, workspace=wsp)
 
     for i in range(args.warmup):
         step(i)
     if args.copy_reference:
         for _ in range(5):
-            sets[1]["y"].copy_(sets[0]["x"])
+            copy_dst.copy_(copy_src)
     torch.cuda.synchronize()
+
+    graphs = []
+    if args.graph:
+        # block b holds steps b*GRAPH_BLOCK .. (b+1)*GRAPH_BLOCK-1, so the
+        # buffer rotation is that of eager launches; blocks whose first step
+        # falls on the same buffer set share one graph
+        distinct = nsets // math.gcd(nsets, GRAPH_BLOCK)
+        distinct = min(distinct, args.steps // GRAPH_BLOCK)
+        cap = torch.cuda.Stream(dev)
+        for b in range(distinct):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(b * GRAPH_BLOCK, (b + 1) * GRAPH_BLOCK):
+                    step(i)
+            graphs.append(g)
+        for g in graphs:  # one untimed replay of each
+            g.replay()
+        torch.cuda.synchronize()
+
     stream = torch.cuda.current_stream(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    if graphs:
+        for b in range(args.steps // GRAPH_BLOCK):
+            graphs[b % len(graphs)].replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
-    gbs = per_set / (ms * 1e-3) / 1e9
+    gbs = per_step / (ms * 1e-3) / 1e9
+    rows = step_rows(spec)
 
     traffic = stored_traffic(args.workload)
+    if kind == "rope":
+        config = {"workload": args.workload, "batch": spec["B"], "seq_len": spec["S"], "heads": spec["NH"],
+                  "head_dim": spec["D"], "table_dtype": spec["tdtype"]}
+    else:
+        config = {"workload": args.workload, "M": spec["M"], "H": spec["H"], "eps": spec["eps"],
+                  "weight": spec["wdtype"] if weighted else None}
+    config.update(buffer_sets=nsets, bytes_per_step=per_step, launch="graph" if graphs else "eager")
+    if args.geom:
+        config["geom"] = args.geom
     result = {
-        "metric": METRIC if args.workload == "fwd_bf16_8192x4096" else f"RMSNorm {args.workload} achieved HBM GB/s",
+        "metric": METRIC if args.workload == "fwd_bf16_8192x4096" else f"{args.workload} achieved HBM GB/s",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -351,13 +456,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dt,
+        "dtype": spec["dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "H": H, "eps": eps,
-                   "weight": spec["wdtype"] if weighted else None, "buffer_sets": nsets,
-                   "bytes_per_step": per_set},
+        "config": config,
         "pct_of_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "rows_per_s": round(M / (ms * 1e-3), 1),
+        "rows_per_s": round(rows / (ms * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 2),
@@ -367,10 +470,8 @@ def main():
             "traffic": traffic,
         },
     }
-    if args.geom:
-        result["config"]["geom"] = args.geom
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(spec, kind, weighted, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(spec, weighted, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -1,7 +1,10 @@
 """Seeded synthetic inputs shared by the oracle-side tests and the GPU-side tests.
 
 This module draws numbers and encodes them into storage formats. It holds none
-of the normalisation arithmetic: no squares, no means, no reciprocal roots.
+of the methods' arithmetic: no squares, no means, no reciprocal roots, no
+rotation.  RoPE's cos/sin tables are inputs to the rotation (a position
+embedding prepares them); here they are the cosines and sines of uniformly
+drawn angles.
 
 Generator (a reading: the pages name no seeds and no generator), in _gen.c:
   * SplitMix64 in counter form.  The stream for (seed, stream id) starts from
@@ -17,7 +20,8 @@ Generator (a reading: the pages name no seeds and no generator), in _gen.c:
     harmless because float32 keeps 24 >= 2*8 + 2 significand bits.
 
 Stream ids: x = 0, weight = 1, residual = 2, upstream gradient = 3,
-outlier mask = 4, outlier value = 5, AdaLN scale = 6, AdaLN shift = 7.
+outlier mask = 4, outlier value = 5, AdaLN scale = 6, AdaLN shift = 7,
+RoPE angle = 8.
 """
 
 from __future__ import annotations
@@ -37,6 +41,7 @@ STREAM_OUTLIER_MASK = 4
 STREAM_OUTLIER_VALUE = 5
 STREAM_SCALE = 6
 STREAM_SHIFT = 7
+STREAM_ANGLE = 8
 
 # Storage formats, by name.  "bf16" arrays are returned as uint16 bit patterns.
 DTYPES = ("f32", "f16", "bf16")
@@ -128,6 +133,16 @@ def normal_tensor(seed: int, stream: int, shape, dtype: str, mean: float = 0.0, 
     return encode(normal(seed, stream, n, mean, std), dtype).reshape(shape)
 
 
+def rope_tables(seed: int, seq_len: int, head_dim: int, dtype: str):
+    """(cos, sin) tables [seq_len, head_dim] of angles drawn uniformly in
+    [0, 2 pi), one per (position, pair), repeated in both halves of a row as
+    in the rotate-half layout; each value rounded once to dtype."""
+    half = head_dim // 2
+    ang = 2.0 * np.pi * uniform(seed, STREAM_ANGLE, seq_len * half).reshape(seq_len, half)
+    ang = np.concatenate([ang, ang], axis=1)
+    return encode(np.cos(ang), dtype), encode(np.sin(ang), dtype)
+
+
 def with_outliers(seed: int, shape, dtype: str, mean: float, std: float,
                   frac: float, lo: float, hi: float) -> np.ndarray:
     """N(mean, std) draws where each element independently (probability frac)
@@ -164,6 +179,13 @@ WORKLOADS = {
     "bwd_residual_bf16_16384x8192": dict(kind="bwd_residual", M=16384, H=8192, dtype="bf16", wdtype="bf16",
                                          x=(0.0, 2.0 ** 0.5), w=(1.0, 0.1), dy=(0.0, 1.0), dres=(0.0, 1.0),
                                          eps=1e-5, seed=1008),
+    # RoPE apply on video tokens: 2 clips of 21 x 16 x 24 latent patches
+    # (8064 positions), 32 heads of 64 (hidden 2048), float32 tables
+    "rope_bf16_2x8064x32x64": dict(kind="rope", B=2, S=8064, NH=32, D=64, dtype="bf16", tdtype="f32",
+                                   x=(0.0, 1.0), seed=1009),
+    # head_dim 128 (32 heads of a 4096-wide model), tables in bfloat16
+    "rope_bf16_2x4096x32x128": dict(kind="rope", B=2, S=4096, NH=32, D=128, dtype="bf16", tdtype="bf16",
+                                    x=(0.0, 1.0), seed=1010),
     # DiT-style AdaLN on 2 x 4096 tokens of width 2048 (LTX-Video's hidden
     # size); scale/shift per batch ([B, 1, H]) and per token ([B, S, H])
     "adaln_bf16_2x4096x2048_batchcond": dict(kind="adaln", M=8192, H=2048, dtype="bf16", wdtype="bf16",
@@ -179,6 +201,8 @@ def make_inputs(name: str, rows: int | None = None) -> dict:
     """Host arrays for a named workload.  rows, if given, keeps the first rows
     rows of every (M, H) tensor (the draws of those rows are unchanged)."""
     spec = dict(WORKLOADS[name])
+    if spec["kind"] == "rope":
+        return _rope_inputs(spec, rows)
     M, H, dt, wdt, seed = spec["M"], spec["H"], spec["dtype"], spec["wdtype"], spec["seed"]
     m = M if rows is None else min(rows, M)
     out = dict(spec)
@@ -204,3 +228,21 @@ def make_inputs(name: str, rows: int | None = None) -> dict:
         out["shift"] = encode(normal(seed, STREAM_SHIFT, C * H, *spec["cond"]), wdt).reshape(C, H)
     return out
 
+
+
+def _rope_inputs(spec: dict, positions: int | None) -> dict:
+    """x [B, S, NH, D] and its tables; positions, if given, keeps the first
+    positions of every batch (their draws are unchanged)."""
+    B, S, NH, D, seed = spec["B"], spec["S"], spec["NH"], spec["D"], spec["seed"]
+    m = S if positions is None else min(positions, S)
+    out = dict(spec)
+    out["S"] = m
+    per = NH * D
+    x = np.empty((B, m, NH, D), dtype=np.dtype({"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[spec["dtype"]]))
+    for b in range(B):
+        v = normal(seed, STREAM_X, m * per, *spec["x"], start=b * S * per)
+        x[b] = encode(v, spec["dtype"]).reshape(m, NH, D)
+    out["x"] = x
+    cos, sin = rope_tables(seed, S, D, spec["tdtype"])
+    out["cos"], out["sin"] = cos[:m], sin[:m]
+    return out

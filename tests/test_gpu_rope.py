@@ -1,0 +1,289 @@
+"""GPU parity of the RoPE apply step (rope_apply) against the float64 oracle,
+and of its autograd wrapper.
+
+Each output is a difference or sum of two products, which may cancel: it is
+judged within 1 ulp of the oracle rounded to the output format, the ulp taken
+at no less than 2^-10 of the sum of the two products' magnitudes (float32:
+within 1e-5 relative above a floor of 2^-4 of that sum), as for dx of the
+norm.  Quarter-turn tables (cos, sin in {0, +-1}) make every output an exact
+copy or negation of an input, so those cases are compared bit for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests import gpu_util as G
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import transformer_normalization_amd as tn  # noqa: E402
+from transformer_normalization_amd import autograd as ag  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _default_streaming():
+    tn.set_streaming(-1)
+    yield
+    tn.set_streaming(-1)
+
+
+def rope_terms(x, cos, sin, dtype, tdtype):
+    """Per output element, the sum of the magnitudes of its two products."""
+    D = x.shape[-1]
+    h = D // 2
+    xd = oracle.decode(x, dtype)
+    c = oracle.decode(np.ascontiguousarray(cos[:, :h]), tdtype)[None, :, None, :]
+    s = oracle.decode(np.ascontiguousarray(sin[:, :h]), tdtype)[None, :, None, :]
+    x0, x1 = xd[..., :h], xd[..., h:]
+    return np.concatenate([np.abs(x0 * c) + np.abs(x1 * s), np.abs(x0 * s) + np.abs(x1 * c)], axis=-1)
+
+
+def rope_vs_oracle(x, cos, sin, got, dtype, tdtype, transpose=False, name="rope"):
+    ref = oracle.rope(x, cos, sin, dtype, tdtype, transpose)
+    terms = rope_terms(x, cos, sin, dtype, tdtype)
+    rep = parity.Report(name)
+    n = ref.shape[-1] * ref.shape[-2]
+    ref, terms, got = ref.reshape(-1, n), terms.reshape(-1, n), np.ascontiguousarray(got).reshape(-1, n)
+    if dtype == "f32":
+        parity.check_dx_f32(rep, got, ref, terms)
+    else:
+        parity.check_dx16(rep, got, ref, terms, dtype, oracle.encode, oracle.decode)
+    return rep
+
+
+def tables(seed, S, D, tdtype, width=None):
+    c, s = synthetic.rope_tables(seed, S, D, tdtype)
+    if width is not None:
+        c, s = np.ascontiguousarray(c[:, :width]), np.ascontiguousarray(s[:, :width])
+    return c, s
+
+
+def run(x, cos, sin, dtype, tdtype, transpose=False):
+    out = tn.rope_apply(G.to_dev(x, dtype), G.to_dev(cos, tdtype), G.to_dev(sin, tdtype), transpose=transpose)
+    torch.cuda.synchronize()
+    return G.to_host(out, dtype)
+
+
+def rand_x(seed, shape, dtype):
+    return synthetic.normal_tensor(seed, synthetic.STREAM_X, shape, dtype)
+
+
+# ---------------------------------------------------------------------------
+# workloads, full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["rope_bf16_2x8064x32x64", "rope_bf16_2x4096x32x128"])
+def test_workload_rope(name):
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    got = run(d["x"], d["cos"], d["sin"], d["dtype"], d["tdtype"])
+    G.assert_ok(rope_vs_oracle(d["x"], d["cos"], d["sin"], got, d["dtype"], d["tdtype"], name=name))
+
+
+# ---------------------------------------------------------------------------
+# shapes and formats
+# ---------------------------------------------------------------------------
+
+SHAPES = [(1, 1, 1, 2), (2, 3, 1, 8), (3, 5, 3, 14), (2, 257, 32, 64), (1, 33, 7, 72), (2, 19, 4, 128),
+          (3, 9, 2, 256), (1, 4, 300, 64), (2, 3, 2, 1000)]
+
+
+@pytest.mark.parametrize("transpose", [False, True], ids=["fwd", "transposed"])
+@pytest.mark.parametrize("dtype,tdtype", [("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32"),
+                                          ("f32", "f32")])
+@pytest.mark.parametrize("shape", SHAPES, ids=["x".join(map(str, s)) for s in SHAPES])
+def test_rope_shapes(shape, dtype, tdtype, transpose):
+    B, S, NH, D = shape
+    print(f"[gpu] rope {shape} {dtype}/{tdtype} transpose={transpose}", flush=True)
+    x = rand_x(3000 + D + NH, shape, dtype)
+    c, s = tables(3000 + S, S, D, tdtype)
+    got = run(x, c, s, dtype, tdtype, transpose)
+    G.assert_ok(rope_vs_oracle(x, c, s, got, dtype, tdtype, transpose, name=f"rope {shape} {dtype}/{tdtype}"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_quarter_turns_are_exact(dtype):
+    """cos, sin in {0, +-1} per position: outputs are exact copies or
+    negations of the inputs, bit for bit, and fix the position each batch row
+    reads (row b * S + s reads table row s)."""
+    B, S, NH, D = 3, 9, 4, 64
+    x = rand_x(31, (B, S, NH, D), dtype)
+    q = np.arange(S) % 4
+    c = np.repeat(np.array([1.0, 0.0, -1.0, 0.0])[q][:, None], D, axis=1)
+    s = np.repeat(np.array([0.0, 1.0, 0.0, -1.0])[q][:, None], D, axis=1)
+    cb, sb = oracle.encode(c, dtype), oracle.encode(s, dtype)
+    got = run(x, cb, sb, dtype, dtype)
+    want = oracle.encode(oracle.rope(x, cb, sb, dtype), dtype)
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_batches_read_the_same_table_rows():
+    B, S, NH, D = 4, 37, 8, 64
+    x = rand_x(32, (B, S, NH, D), "bf16")
+    c, s = tables(32, S, D, "f32")
+    full = run(x, c, s, "bf16", "f32")
+    for b in range(B):
+        one = run(np.ascontiguousarray(x[b:b + 1]), c, s, "bf16", "f32")
+        assert np.array_equal(full[b:b + 1], one), b
+
+
+def test_half_width_tables_equal_full_width():
+    B, S, NH, D = 2, 50, 4, 128
+    x = rand_x(33, (B, S, NH, D), "bf16")
+    c, s = tables(33, S, D, "bf16")
+    a = run(x, c, s, "bf16", "bf16")
+    b = run(x, np.ascontiguousarray(c[:, :D // 2]), np.ascontiguousarray(s[:, :D // 2]), "bf16", "bf16")
+    assert np.array_equal(a, b)
+    # the second half of a table row is never read
+    c2, s2 = c.copy(), s.copy()
+    c2[:, D // 2:] = oracle.encode(np.full((S, D // 2), 7.0), "bf16")
+    assert np.array_equal(run(x, c2, s2, "bf16", "bf16"), a)
+
+
+def test_strided_views_and_in_place():
+    """q sliced from a fused [B, S, 3, NH, D] projection (row stride 3*NH*D,
+    head stride D), a padded head layout, and in-place application."""
+    B, S, NH, D = 2, 64, 8, 64
+    qkv_h = rand_x(34, (B, S, 3, NH, D), "bf16")
+    c, s = tables(34, S, D, "f32")
+    cd, sd = G.to_dev(c, "f32"), G.to_dev(s, "f32")
+    qkv = G.to_dev(qkv_h, "bf16")
+    q = qkv[:, :, 0]
+    ref = run(np.ascontiguousarray(qkv_h[:, :, 0]), c, s, "bf16", "f32")
+    out = tn.rope_apply(q, cd, sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.to_host(out, "bf16"), ref)
+    # in place on the strided slice: the other two slices stay untouched
+    k_before = qkv[:, :, 1].clone()
+    r = tn.rope_apply(q, cd, sd, out=q)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == q.data_ptr()
+    assert np.array_equal(G.to_host(qkv[:, :, 0], "bf16"), ref)
+    assert torch.equal(qkv[:, :, 1].view(torch.int16), k_before.view(torch.int16))
+    # padded heads: head stride D + 8
+    big = torch.zeros((B, S, NH, D + 8), dtype=torch.bfloat16, device=G.DEV)
+    big[..., :D] = G.to_dev(np.ascontiguousarray(qkv_h[:, :, 0]), "bf16")
+    out2 = tn.rope_apply(big[..., :D], cd, sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.to_host(out2, "bf16"), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_misaligned_rows_use_single_elements(dtype):
+    """head_dim/2 not a multiple of the vector width, and a view starting one
+    element into its buffer, take the single-element path; values as the
+    vector path's."""
+    B, S, NH, D = 2, 21, 3, 70
+    x = rand_x(35, (B, S, NH, D), dtype)
+    c, s = tables(35, S, D, "f32")
+    got = run(x, c, s, dtype, "f32")
+    G.assert_ok(rope_vs_oracle(x, c, s, got, dtype, "f32", name=f"odd half {dtype}"))
+    D2 = 64
+    x2 = rand_x(36, (B, S, NH, D2), dtype)
+    c2, s2 = tables(36, S, D2, "f32")
+    flat = torch.zeros(B * S * NH * D2 + 1, dtype=G.torch_dtype(dtype), device=G.DEV)
+    view = flat[1:].view(B, S, NH, D2)
+    view.copy_(G.to_dev(x2, dtype))
+    out = tn.rope_apply(view, G.to_dev(c2, "f32"), G.to_dev(s2, "f32"))
+    torch.cuda.synchronize()
+    assert np.array_equal(G.to_host(out, dtype), run(x2, c2, s2, dtype, "f32"))
+
+
+def test_streaming_does_not_change_bits():
+    d = synthetic.make_inputs("rope_bf16_2x8064x32x64", rows=512)
+    tn.set_streaming(0)
+    a = run(d["x"], d["cos"], d["sin"], "bf16", "f32")
+    tn.set_streaming(1)
+    b = run(d["x"], d["cos"], d["sin"], "bf16", "f32")
+    assert np.array_equal(a, b)
+
+
+def test_transpose_inverts_within_rounding():
+    B, S, NH, D = 2, 40, 4, 64
+    x = rand_x(37, (B, S, NH, D), "f32")
+    c, s = tables(37, S, D, "f32")
+    y = tn.rope_apply(G.to_dev(x, "f32"), G.to_dev(c, "f32"), G.to_dev(s, "f32"))
+    z = tn.rope_apply(y, G.to_dev(c, "f32"), G.to_dev(s, "f32"), transpose=True)
+    torch.cuda.synchronize()
+    assert np.allclose(z.cpu().numpy(), x, rtol=0, atol=1e-5)
+
+
+def test_guard_regions_untouched():
+    B, S, NH, D = 2, 17, 3, 64
+    x = rand_x(38, (B, S, NH, D), "bf16")
+    c, s = tables(38, S, D, "bf16")
+    n = B * S * NH * D
+    buf = torch.full((n + 256,), 1.5, dtype=torch.bfloat16, device=G.DEV)
+    out = buf[128:128 + n].view(B, S, NH, D)
+    tn.rope_apply(G.to_dev(x, "bf16"), G.to_dev(c, "bf16"), G.to_dev(s, "bf16"), out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:128] == 1.5) and torch.all(buf[128 + n:] == 1.5)
+
+
+def test_rejects_bad_arguments():
+    x = torch.zeros((2, 4, 2, 64), dtype=torch.bfloat16, device=G.DEV)
+    c = torch.zeros((4, 64), dtype=torch.float32, device=G.DEV)
+    with pytest.raises(tn.RMSNormError):
+        tn.rope_apply(x[..., :63], c, c)  # odd head_dim
+    with pytest.raises(ValueError):
+        tn.rope_apply(x, c[:3], c[:3])  # table rows != seq_len
+    # an output that partially overlaps the input
+    n = x.numel()
+    buf = torch.zeros(n + 64, dtype=torch.bfloat16, device=G.DEV)
+    with pytest.raises(tn.RMSNormError):
+        tn.rope_apply(buf[:n].view(x.shape), c, c, out=buf[64:64 + n].view(x.shape))
+    # an output over a table (the table is a float32 view of out's memory)
+    tab = torch.zeros(n, dtype=torch.bfloat16, device=G.DEV)
+    ct = tab[:512].view(torch.float32).view(4, 64)
+    with pytest.raises(tn.RMSNormError):
+        tn.rope_apply(x, ct, c, out=tab.view(x.shape))
+    h16 = torch.zeros((4, 64), dtype=torch.float16, device=G.DEV)
+    with pytest.raises(tn.RMSNormError):
+        tn.rope_apply(x, h16, h16)  # f16 tables for bf16 x
+
+
+def test_empty_batch():
+    x = torch.empty((0, 5, 2, 64), dtype=torch.bfloat16, device=G.DEV)
+    c = torch.zeros((5, 64), dtype=torch.bfloat16, device=G.DEV)
+    out = tn.rope_apply(x, c, c)
+    torch.cuda.synchronize()
+    assert out.shape == x.shape
+
+
+def test_deterministic():
+    d = synthetic.make_inputs("rope_bf16_2x4096x32x128", rows=300)
+    runs = [run(d["x"], d["cos"], d["sin"], "bf16", "bf16") for _ in range(3)]
+    assert all(np.array_equal(runs[0], r) for r in runs[1:])
+
+
+# ---------------------------------------------------------------------------
+# autograd
+# ---------------------------------------------------------------------------
+
+def test_autograd_rope_gradient_is_transposed_rotation():
+    B, S, NH, D = 2, 65, 8, 64
+    x_h = rand_x(39, (B, S, NH, D), "bf16")
+    g_h = synthetic.normal_tensor(39, synthetic.STREAM_DY, (B, S, NH, D), "bf16")
+    c, s = tables(39, S, D, "f32")
+    cd, sd = G.to_dev(c, "f32"), G.to_dev(s, "f32")
+    x = G.to_dev(x_h, "bf16").requires_grad_(True)
+    g = G.to_dev(g_h, "bf16")
+    y = ag.rope_3d(x, cd, sd)
+    (y.float() * g.float()).sum().backward()
+    assert np.array_equal(G.to_host(y, "bf16"), run(x_h, c, s, "bf16", "f32"))
+    want = tn.rope_apply(g, cd, sd, transpose=True)
+    assert torch.equal(x.grad.view(torch.int16), want.view(torch.int16))
+    G.assert_ok(rope_vs_oracle(g_h, c, s, G.to_host(x.grad, "bf16"), "bf16", "f32", transpose=True,
+                               name="rope grad"))
+    cg = cd.clone().requires_grad_(True)
+    with pytest.raises(NotImplementedError):
+        ag.rope_3d(G.to_dev(x_h, "bf16"), cg, sd).float().sum().backward()

@@ -12,6 +12,7 @@ functions raise.
     y = rmsnorm_adaln_fwd(x, w, scale, shift, eps)  # scale/shift [B,S,H] or [B,1,H]
     dx, dw = rmsnorm_bwd(dy, x, w, rrms)
     dh, dw = rmsnorm_bwd_residual(dy, res_out, dres, w, rrms)  # grad of x and residual
+    q = rope_apply(q, cos, sin)                      # q [B, S, heads, head_dim], cos/sin [S, head_dim]
 
 transformer_normalization_amd.autograd wraps these as torch.autograd
 Functions and nn.Modules for training.
@@ -30,7 +31,7 @@ RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
 STATUS = {0: "RMSN_OK", 1: "RMSN_ERR_INVALID_ARG", 2: "RMSN_ERR_UNSUPPORTED", 3: "RMSN_ERR_WORKSPACE",
           4: "RMSN_ERR_HIP"}
 EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_adaln_fwd", "rmsnorm_bwd_workspace_bytes",
-            "rmsnorm_bwd", "rmsnorm_bwd_residual", "rmsnorm_status_string", "rmsnorm_last_error")
+            "rmsnorm_bwd", "rmsnorm_bwd_residual", "rmsnorm_status_string", "rmsnorm_last_error", "rope_apply")
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
         lib.rmsnorm_bwd_workspace_bytes.restype = sz
         lib.rmsnorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32, i32, vp]
+        lib.rope_apply.restype = i32
+        lib.rope_apply.argtypes = [vp, i64, i64, vp, vp, i64, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.rmsnorm_bwd_residual.restype = i32
         lib.rmsnorm_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32,
                                              i32, vp]
@@ -307,6 +310,56 @@ def rmsnorm_bwd_residual(dy, residual_out, dres, weight, rrms, dh=None, dw=None,
     dh = norm backward through h + dres is the gradient of both x and the
     residual input.  dh may be dy, residual_out or dres itself."""
     return _bwd(dy, residual_out, dres, weight, rrms, dh, dw, workspace, want_dw)
+
+
+def _heads_view(t, name):
+    """(batch, seq_len, heads, head_dim, row stride, head stride) of a
+    [batch, seq_len, heads, head_dim] tensor whose batch and position axes
+    collapse into rows of one stride (token b, s is row b * seq_len + s)."""
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [batch, seq_len, heads, head_dim]")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    B, S, NH, D = t.shape
+    hs = t.stride(2) if NH > 1 else D
+    span = (NH - 1) * hs + D  # elements of one token row
+    if t.numel() == 0:
+        return B, S, NH, D, max(span, 1), max(hs, 1)
+    if t.stride(3) != 1 and D > 1:
+        raise ValueError(f"{name} must be contiguous along head_dim")
+    if S > 1:
+        rs = t.stride(1)
+        if B > 1 and t.stride(0) != S * rs:
+            raise ValueError(f"{name}'s batch and position axes cannot be viewed as rows with one stride")
+    else:
+        rs = t.stride(0) if B > 1 else span
+    return B, S, NH, D, rs, hs
+
+
+def rope_apply(x, cos, sin, out=None, transpose: bool = False):
+    """Rotate-half RoPE of x [batch, seq_len, heads, head_dim] by per-position
+    cos/sin tables [seq_len, >= head_dim/2] (x's dtype or float32); token b, s
+    reads table row s.  out may be x itself (in place).  transpose rotates by
+    the negated angles (the inverse, and the gradient with respect to x)."""
+    torch = _torch()
+    lib = load_library()
+    B, S, NH, D, xrs, xhs = _heads_view(x, "x")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _, _, _, _, ors, ohs = _heads_view(out, "out")
+    if cos.shape != sin.shape or cos.dtype != sin.dtype or cos.dim() != 2 or cos.shape[0] != S:
+        raise ValueError("cos and sin must both be [seq_len, >= head_dim/2] tensors of one dtype")
+    if cos.shape[1] < D // 2:
+        raise ValueError("cos/sin rows must hold at least head_dim/2 entries")
+    if cos.stride(1) != 1 or sin.stride(1) != 1 or (S > 1 and cos.stride(0) != sin.stride(0)):
+        raise ValueError("cos and sin must be row-contiguous with one row stride")
+    ts = cos.stride(0) if S > 1 else cos.shape[1]
+    st = lib.rope_apply(_ptr(x), xrs, xhs, _ptr(cos), _ptr(sin), ts, _ptr(out), ors, ohs, B, S, NH, D,
+                        1 if transpose else 0, _dtype_code(x), _dtype_code(cos), _stream(x))
+    _check(lib, st)
+    return out
 
 
 def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: int = 0) -> None:

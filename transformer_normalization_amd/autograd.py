@@ -5,6 +5,10 @@ library's C ABI.
     y, h = fused_add_rms_norm(x, residual, weight, eps)  # h = x + residual
     norm = RMSNorm(4096, eps=1e-5, device="cuda", dtype=torch.bfloat16)
     y = norm(x);  y, h = norm(x, residual)
+    q = rope_3d(q, cos, sin)                            # differentiable in q
+
+RoPE's backward is the transposed rotation (the same kernel with the sine
+negated); the tables are constants (no gradient).
 
 The forward saves the per-row float32 rrms the forward kernel writes, and the
 backward reads it instead of recomputing it (page "Skill: Write a Triton
@@ -24,9 +28,10 @@ from __future__ import annotations
 
 import torch
 
-from . import rmsnorm_bwd, rmsnorm_bwd_residual, rmsnorm_fwd, rmsnorm_fwd_residual
+from . import rmsnorm_bwd, rmsnorm_bwd_residual, rmsnorm_fwd, rmsnorm_fwd_residual, rope_apply
 
-__all__ = ["RMSNormFunction", "FusedAddRMSNormFunction", "rms_norm", "fused_add_rms_norm", "RMSNorm"]
+__all__ = ["RMSNormFunction", "FusedAddRMSNormFunction", "RoPEFunction", "rms_norm", "fused_add_rms_norm", "rope_3d",
+           "RMSNorm"]
 
 
 def _grad_like(g, ref):
@@ -92,6 +97,23 @@ class FusedAddRMSNormFunction(torch.autograd.Function):
         return gx, gr, dw, None
 
 
+class RoPEFunction(torch.autograd.Function):
+    """Rotate-half RoPE of q or k [batch, seq_len, heads, head_dim] by
+    [seq_len, head_dim] cos/sin tables (constants)."""
+
+    @staticmethod
+    def forward(ctx, x, cos, sin):
+        ctx.save_for_backward(cos, sin)
+        return rope_apply(x, cos, sin)
+
+    @staticmethod
+    def backward(ctx, dy):
+        cos, sin = ctx.saved_tensors
+        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
+            raise NotImplementedError("rope_3d has no gradient with respect to the cos/sin tables")
+        return rope_apply(_grad_like(dy, dy), cos, sin, transpose=True), None, None
+
+
 def rms_norm(x, weight=None, eps: float = 1e-6):
     """Differentiable RMSNorm over the last dimension of x."""
     return RMSNormFunction.apply(x, weight, eps)
@@ -100,6 +122,11 @@ def rms_norm(x, weight=None, eps: float = 1e-6):
 def fused_add_rms_norm(x, residual, weight=None, eps: float = 1e-6):
     """Differentiable fused residual pre-norm: returns (RMSNorm(x + residual), x + residual)."""
     return FusedAddRMSNormFunction.apply(x, residual, weight, eps)
+
+
+def rope_3d(x, cos, sin):
+    """Differentiable rotate-half RoPE (gradient with respect to x only)."""
+    return RoPEFunction.apply(x, cos, sin)
 
 
 class RMSNorm(torch.nn.Module):

@@ -19,8 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librmsnorm.so")
-SOURCES = ["rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_adaln.hip", "kernels_bwd.hip",
-           "kernels_bwd_residual.hip"]
+SOURCES = ["host_common.hip", "rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_adaln.hip", "kernels_bwd.hip",
+           "kernels_bwd_residual.hip", "rope_api.hip", "kernels_rope.hip"]
 ARCH = "gfx950"
 
 

@@ -1,18 +1,20 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
-// kernels_bwd.hip, kernels_bwd_residual.hip) so that they compile in
-// parallel; the host code only sees these functions.
+// kernels_bwd.hip, kernels_bwd_residual.hip, kernels_rope.hip) so that they
+// compile in parallel; the host code only sees these functions.
 #pragma once
 
 #include "bwd_kernels.hpp"
 #include "fwd_kernels.hpp"
 #include "rmsnorm.h"
+#include "rope_kernels.hpp"
 
 namespace rmsn {
 
 typedef void (*fwd_fn)(const FwdParams);
 typedef void (*bwd_fn)(const BwdParams);
+typedef void (*rope_fn)(const RopeParams);
 
 // nullptr when no instantiation matches (vec: elements per access; vpt:
 // accesses per thread; nt: streaming accesses)
@@ -24,5 +26,7 @@ bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bo
 // the backward of the fused residual pre-norm (adds the residual-stream gradient)
 bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 const void *dw_finalize_kernel();
+// vec: 16 / element size, or 1 for single elements; tdt: x's format or float32
+rope_fn rope_lookup(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool nt);
 
 }  // namespace rmsn

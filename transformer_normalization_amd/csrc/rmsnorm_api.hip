@@ -1,6 +1,6 @@
 // rmsnorm_api.hip -- host side of the gfx950 RMSNorm library: argument
 // validation, launch geometry and the extern "C" entry points declared in
-// include/rmsnorm.h.
+// include/rmsnorm.h (shared helpers: host_common.hpp).
 //
 // Nothing here allocates, frees or synchronises.  Argument errors are found
 // before the first HIP call.  The only HIP calls are hipGetDevice,
@@ -17,6 +17,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "host_common.hpp"
 #include "kernel_tables.hpp"
 #include "rmsnorm.h"
 #include "rmsnorm_tuning.h"
@@ -24,126 +25,13 @@
 namespace {
 
 using namespace rmsn;
+using namespace rmsn::host;
 
 // ---------------------------------------------------------------------------
-// errors
+// argument checks of the norm entry points
 // ---------------------------------------------------------------------------
-
-thread_local char g_last_error[512] = "";
-
-rmsn_status_t fail(rmsn_status_t s, const char *fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
-    va_end(ap);
-    return s;
-}
-
-rmsn_status_t ok() {
-    g_last_error[0] = '\0';
-    return RMSN_OK;
-}
-
-// ---------------------------------------------------------------------------
-// device facts (read once per device; a failed read is an error, never a guess)
-// ---------------------------------------------------------------------------
-
-constexpr int kMaxDevices = 64;
-
-struct DeviceInfo {
-    std::once_flag once;
-    rmsn_status_t status = RMSN_ERR_HIP;
-    int cus = 0;
-    char detail[256] = "";
-};
-
-DeviceInfo g_devices[kMaxDevices];
-
-rmsn_status_t device_info(int *cus) {
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(RMSN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= kMaxDevices) return fail(RMSN_ERR_HIP, "device index %d out of range", dev);
-    DeviceInfo &d = g_devices[dev];
-    std::call_once(d.once, [&d, dev]() {
-        int n = 0;
-        hipError_t err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err != hipSuccess || n <= 0) {
-            snprintf(d.detail, sizeof d.detail, "reading the compute-unit count of device %d failed: %s", dev,
-                     hipGetErrorString(err));
-            d.status = RMSN_ERR_HIP;
-            return;
-        }
-        hipDeviceProp_t prop;
-        err = hipGetDeviceProperties(&prop, dev);
-        if (err != hipSuccess) {
-            snprintf(d.detail, sizeof d.detail, "reading the properties of device %d failed: %s", dev,
-                     hipGetErrorString(err));
-            d.status = RMSN_ERR_HIP;
-            return;
-        }
-        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-            snprintf(d.detail, sizeof d.detail, "device %d is %s; this library is built for gfx950 only", dev,
-                     prop.gcnArchName);
-            d.status = RMSN_ERR_UNSUPPORTED;
-            return;
-        }
-        d.cus = n;
-        d.status = RMSN_OK;
-    });
-    if (d.status != RMSN_OK) return fail(d.status, "%s", d.detail);
-    *cus = d.cus;
-    return RMSN_OK;
-}
-
-// ---------------------------------------------------------------------------
-// argument checks
-// ---------------------------------------------------------------------------
-
-int dtype_bytes(rmsn_dtype_t t) { return t == RMSN_F32 ? 4 : 2; }
-bool dtype_valid(int t) { return t == RMSN_F32 || t == RMSN_F16 || t == RMSN_BF16; }
 
 constexpr int64_t kMaxH = int64_t(1) << 30;
-
-// A buffer as a byte range [lo, hi) plus what identifies "the same buffer".
-struct Region {
-    const char *name;
-    uintptr_t base;
-    int64_t stride;  // elements, 0 for vectors
-    int64_t rows;
-    int64_t cols;
-    int ebytes;
-    bool present;
-    uintptr_t lo() const { return base; }
-    uintptr_t hi() const { return base + (uintptr_t)(((rows - 1) * stride + cols) * ebytes); }
-    bool overlaps(const Region &o) const { return lo() < o.hi() && o.lo() < hi(); }
-    bool same(const Region &o) const {
-        return base == o.base && stride == o.stride && rows == o.rows && cols == o.cols && ebytes == o.ebytes;
-    }
-};
-
-Region mat(const char *name, const void *p, int64_t stride, int64_t M, int64_t H, int eb) {
-    return Region{name, (uintptr_t)p, stride, M, H, eb, p != nullptr};
-}
-Region vec(const char *name, const void *p, int64_t n, int eb) {
-    return Region{name, (uintptr_t)p, 0, 1, n, eb, p != nullptr};
-}
-
-// outputs must not overlap each other; an output may overlap an input only
-// by being exactly the same buffer
-rmsn_status_t check_overlap(const Region *outs, int nout, const Region *ins, int nin) {
-    for (int i = 0; i < nout; ++i) {
-        if (!outs[i].present) continue;
-        for (int j = i + 1; j < nout; ++j)
-            if (outs[j].present && outs[i].overlaps(outs[j]))
-                return fail(RMSN_ERR_INVALID_ARG, "outputs %s and %s overlap", outs[i].name, outs[j].name);
-        for (int j = 0; j < nin; ++j)
-            if (ins[j].present && outs[i].overlaps(ins[j]) && !outs[i].same(ins[j]))
-                return fail(RMSN_ERR_INVALID_ARG, "output %s partially overlaps input %s", outs[i].name,
-                            ins[j].name);
-    }
-    return RMSN_OK;
-}
 
 rmsn_status_t check_common(int64_t M, int64_t H, rmsn_dtype_t xdt, const void *w, rmsn_dtype_t wdt) {
     if (!dtype_valid(xdt)) return fail(RMSN_ERR_UNSUPPORTED, "x_dtype %d is not RMSN_F32/F16/BF16", (int)xdt);
@@ -155,22 +43,11 @@ rmsn_status_t check_common(int64_t M, int64_t H, rmsn_dtype_t xdt, const void *w
     return RMSN_OK;
 }
 
-rmsn_status_t check_stride(const char *name, int64_t stride, int64_t M, int64_t H, int eb) {
-    if (stride < H) return fail(RMSN_ERR_INVALID_ARG, "%s = %lld is smaller than H = %lld", name, (long long)stride,
-                                (long long)H);
-    // the last byte of the matrix must be addressable without overflow
-    if (M > 1 && (stride > (INT64_MAX / eb) / (M - 1)))
-        return fail(RMSN_ERR_INVALID_ARG, "%s * M overflows", name);
-    return RMSN_OK;
-}
-
 rmsn_status_t check_eps(float eps) {
     if (!(eps > 0.0f) || !std::isfinite(eps))
         return fail(RMSN_ERR_INVALID_ARG, "eps = %g must be positive and finite", (double)eps);
     return RMSN_OK;
 }
-
-bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
 // geometry
@@ -290,23 +167,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
 // kernel tables
 // ---------------------------------------------------------------------------
 
-// Streaming (non-temporal) accesses pay off when a call moves more data than
-// the caches could usefully keep for the next kernel; below that, ordinary
-// cached accesses leave the outputs in L2 / the last-level cache for the
-// consumer.  Mode -1 = decide by size, 0 = never, 1 = always.
-constexpr int64_t kStreamBytes = int64_t(64) << 20;
-std::atomic<int> g_stream_mode{-1};
 
-bool use_streaming(int64_t bytes_moved) {
-    const int mode = g_stream_mode.load(std::memory_order_relaxed);
-    return mode < 0 ? bytes_moved >= kStreamBytes : mode > 0;
-}
-
-rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what) {
-    hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
-    if (e != hipSuccess) return fail(RMSN_ERR_HIP, "launching %s failed: %s", what, hipGetErrorString(e));
-    return RMSN_OK;
-}
 
 // ---------------------------------------------------------------------------
 // forward (plain and fused residual)
@@ -666,9 +527,9 @@ RMSN_API const char *rmsnorm_status_string(rmsn_status_t s) {
     return "RMSN_UNKNOWN_STATUS";
 }
 
-RMSN_API const char *rmsnorm_last_error(void) { return g_last_error; }
+RMSN_API const char *rmsnorm_last_error(void) { return last_error(); }
 
-RMSN_API void rmsnorm_tuning_set_streaming(int mode) { g_stream_mode.store(mode < 0 ? -1 : mode > 0 ? 1 : 0); }
+RMSN_API void rmsnorm_tuning_set_streaming(int mode) { set_stream_mode(mode); }
 
 RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid) {
     get_override(0);  // the environment is read first, so a later call wins

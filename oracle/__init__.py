@@ -78,8 +78,9 @@ class Oracle:
         lib.orc_adaln_fwd.argtypes = [vp, i64, vp, vp, vp, i64, i64, i32, i32, i32, i64, i64, dp, vp, vp]
         lib.orc_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, vp, vp, vp]
         lib.orc_rope.argtypes = [vp, i64, i64, vp, vp, i64, i32, i32, i64, i64, i64, i64, i32, vp]
+        lib.orc_layernorm.argtypes = [vp, i64, vp, i64, vp, vp, i32, i32, i64, i64, dp, vp, vp, vp, vp]
         for f in (lib.orc_decode, lib.orc_encode, lib.orc_fwd, lib.orc_fwd_residual, lib.orc_bwd,
-                  lib.orc_adaln_fwd, lib.orc_bwd_residual, lib.orc_rope):
+                  lib.orc_adaln_fwd, lib.orc_bwd_residual, lib.orc_rope, lib.orc_layernorm):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -235,6 +236,31 @@ class Oracle:
         return out
 
 
+    def layernorm(self, x, residual, w, b, eps, dtype: str, wdtype: str | None = None):
+        """Residual + LayerNorm: -> (y, h, mean, rstd), float64.  residual, w
+        and b may each be None.  h is the exact sum x + residual (x when there
+        is no residual)."""
+        x, xs = _rows(x, dtype)
+        M, H = x.shape
+        rs = H
+        if residual is not None:
+            residual, rs = _rows(residual, dtype)
+            if residual.shape != x.shape:
+                raise ValueError("residual shape differs")
+        wd = wdtype or dtype
+        wv = None if w is None else _vec(w, wd)
+        bv = None if b is None else _vec(b, wd)
+        y = np.empty((M, H), dtype=np.float64)
+        h = np.empty((M, H), dtype=np.float64)
+        mean = np.empty(M, dtype=np.float64)
+        rstd = np.empty(M, dtype=np.float64)
+        rc = self.lib.orc_layernorm(_ptr(x), xs, _ptr(residual), rs, _ptr(wv), _ptr(bv), CODES[dtype], CODES[wd], M,
+                                    H, float(eps), _ptr(y), _ptr(h), _ptr(mean), _ptr(rstd))
+        if rc != 0:
+            raise ValueError("orc_layernorm rejected its arguments")
+        return y, h, mean, rstd
+
+
 def default() -> Oracle:
     """The oracle built from rmsnorm_oracle.c (rebuilt when the source is newer)."""
     global _default
@@ -276,3 +302,7 @@ def bwd_residual(dy, h, dres, w, rrms, dtype, wdtype=None, want_dw=True):
 
 def rope(x, cos, sin, dtype, tdtype=None, transpose=False):
     return default().rope(x, cos, sin, dtype, tdtype, transpose)
+
+
+def layernorm(x, residual, w, b, eps, dtype, wdtype=None):
+    return default().layernorm(x, residual, w, b, eps, dtype, wdtype)

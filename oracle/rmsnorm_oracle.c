@@ -39,6 +39,14 @@
  *     the flat row index modulo seq_len.  Only the first head_dim/2 columns of
  *     a table row are read.  The transposed rotation (sin negated) is the
  *     gradient of the rotation with respect to its input, and its inverse.
+ *   - Residual + LayerNorm (the page "SpeedROCm: shape-aware Triton
+ *     acceleration for Transformer inference", "How the solution addresses
+ *     the problem", item 4: each residual add fused with the LayerNorm that
+ *     consumes it, in a pre-LayerNorm transformer).  LayerNorm is the one the
+ *     page names among its runtime interfaces (torch.nn's): over the last
+ *     axis, mean and population (biased) variance, eps inside the square
+ *     root, then the optional elementwise weight and bias:
+ *       h = x + r,  y = (h - mean(h)) / sqrt(var(h) + eps) * w + b.
  *
  * Everything is computed in IEEE float64 from exactly decoded inputs, one row
  * at a time, in the plain left-to-right order of the definition.  Rounding to
@@ -50,6 +58,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F64 = 3 };
@@ -359,5 +368,44 @@ int orc_rope(const void *x, int64_t x_row_stride, int64_t x_head_stride, const v
             }
         }
     }
+    return 0;
+}
+
+/* ---- residual + LayerNorm --------------------------------------------------
+ * res may be NULL (plain LayerNorm: h = x); w and b may each be NULL (1 and
+ * 0).  Outputs: y (M, H) and, when non-NULL, h (M, H) (the exact sum, before
+ * any rounding to a storage format), mean (M,) and rstd (M,).
+ */
+int orc_layernorm(const void *x, int64_t x_stride, const void *res, int64_t r_stride, const void *w, const void *b,
+                  int x_dt, int w_dt, int64_t M, int64_t H, double eps, double *y, double *h_out, double *mean_out,
+                  double *rstd_out) {
+    if (!orc_valid_code(x_dt) || !orc_valid_code(w_dt) || M < 0 || H < 1 || x_stride < H ||
+        (res && r_stride < H) || !(eps >= 0.0))
+        return -1;
+    double *h = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!h) return -2;
+    for (int64_t i = 0; i < M; ++i) {
+        double sum = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = load_elem(x, x_dt, i * x_stride + j);
+            if (res) v += load_elem(res, x_dt, i * r_stride + j);
+            h[j] = v;
+            sum += v;
+        }
+        const double mean = sum / (double)H;
+        double sq = 0.0;
+        for (int64_t j = 0; j < H; ++j) sq += (h[j] - mean) * (h[j] - mean);
+        const double var = sq / (double)H;
+        const double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t j = 0; j < H; ++j) {
+            double wj = w ? load_elem(w, w_dt, j) : 1.0;
+            double bj = b ? load_elem(b, w_dt, j) : 0.0;
+            y[i * H + j] = (h[j] - mean) * rstd * wj + bj;
+            if (h_out) h_out[i * H + j] = h[j];
+        }
+        if (mean_out) mean_out[i] = mean;
+        if (rstd_out) rstd_out[i] = rstd;
+    }
+    free(h);
     return 0;
 }

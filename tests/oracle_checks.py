@@ -678,6 +678,71 @@ def check_rope_batches_and_strides(o):
     assert np.array_equal(got, want)
 
 
+# ---------------------------------------------------------------------------
+# residual + LayerNorm ("SpeedROCm", item 4; torch.nn's LayerNorm)
+# ---------------------------------------------------------------------------
+
+def check_layernorm_hand_example(o):
+    # row 1 2 3 4: mean 2.5, population variance 1.25; eps 2.75 makes
+    # var + eps = 4, so rstd = 1/2 and (h - mean) * rstd = -0.75 -0.25 0.25 0.75
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    w = np.array([1.0, 2.0, -1.0, 0.5])
+    b = np.array([0.5, 0.0, 1.0, -1.0])
+    y, h, mean, rstd = o.layernorm(x, None, w, b, 2.75, "f64")
+    assert np.array_equal(y[0], [-0.25, -0.5, 0.75, -0.625])
+    assert mean[0] == 2.5 and rstd[0] == 0.5 and np.array_equal(h, x)
+    # the same row split as x + residual
+    y2, h2, _, _ = o.layernorm(np.array([[0.5, 4.0, 3.0, -1.0]]), np.array([[0.5, -2.0, 0.0, 5.0]]), w, b, 2.75,
+                               "f64")
+    assert np.array_equal(y2, y) and np.array_equal(h2, x)
+
+
+def check_layernorm_matches_torch_float64(o):
+    torch = __import__("torch")
+    rng = _rng(50)
+    for (M, H, mu) in ((3, 1, 0.0), (4, 7, 0.0), (5, 64, 3.0), (2, 1000, -50.0)):
+        x = rng.standard_normal((M, H)) + mu
+        r = rng.standard_normal((M, H))
+        w, b = rng.uniform(0.5, 1.5, H), rng.standard_normal(H)
+        y, h, mean, rstd = o.layernorm(x, r, w, b, 1e-5, "f64")
+        t = torch.nn.functional.layer_norm(torch.from_numpy(x + r), (H,), torch.from_numpy(w), torch.from_numpy(b),
+                                           1e-5).numpy()
+        assert np.allclose(y, t, rtol=1e-12, atol=1e-12), (M, H)
+        t0 = torch.nn.functional.layer_norm(torch.from_numpy(x), (H,), None, None, 1e-5).numpy()
+        assert np.allclose(o.layernorm(x, None, None, None, 1e-5, "f64")[0], t0, rtol=1e-12, atol=1e-12)
+
+
+def check_layernorm_is_rmsnorm_of_centred_row(o):
+    # LayerNorm(h) = RMSNorm(h - mean(h)) with the same eps; mean(y) = 0 and
+    # mean(y^2) = var / (var + eps) without the affine part
+    rng = _rng(51)
+    M, H, eps = 6, 48, 1e-3
+    x = rng.standard_normal((M, H)) * 3 + 1
+    y, h, mean, rstd = o.layernorm(x, None, None, None, eps, "f64")
+    centred = x - x.mean(axis=1, keepdims=True)
+    yr, rr = o.fwd(centred, None, eps, "f64")
+    assert np.allclose(y, yr, rtol=1e-13, atol=1e-13) and np.allclose(rstd, rr, rtol=1e-13)
+    assert np.allclose(mean, x.mean(axis=1), rtol=1e-14, atol=1e-14)
+    assert np.all(np.abs(y.mean(axis=1)) < 1e-14)
+    var = 1.0 / rstd ** 2 - eps
+    assert np.allclose((y ** 2).mean(axis=1), var / (var + eps), rtol=1e-13)
+
+
+def check_layernorm_shift_and_scale(o):
+    # a constant added to a row changes nothing; scaling a row by k with eps
+    # scaled by k^2 changes nothing; a constant row gives exactly the bias
+    rng = _rng(52)
+    M, H = 4, 32
+    x = rng.standard_normal((M, H))
+    b = rng.standard_normal(H)
+    y0 = o.layernorm(x, None, None, b, 1e-4, "f64")[0]
+    assert np.allclose(o.layernorm(x + 1000.0, None, None, b, 1e-4, "f64")[0], y0, rtol=0, atol=1e-9)
+    assert np.allclose(o.layernorm(x * 8.0, None, None, b, 64e-4, "f64")[0], y0, rtol=0, atol=1e-12)
+    c = np.full((2, 64), 0.75)
+    assert np.array_equal(o.layernorm(c, None, np.full(64, 3.0), b[:1].repeat(64), 1e-5, "f64")[0],
+                          np.tile(b[:1].repeat(64), (2, 1)))
+
+
 ALL_CHECKS = [
     check_decode_all_16bit_patterns,
     check_encode_matches_libraries,
@@ -707,4 +772,8 @@ ALL_CHECKS = [
     check_rope_quarter_turns_by_position,
     check_rope_rotation_invariants,
     check_rope_batches_and_strides,
+    check_layernorm_hand_example,
+    check_layernorm_matches_torch_float64,
+    check_layernorm_is_rmsnorm_of_centred_row,
+    check_layernorm_shift_and_scale,
 ]

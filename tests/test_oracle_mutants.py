@@ -58,6 +58,18 @@ MUTANTS = [
     ("rope_table_second_half", "double c = load_elem(cos_t, t_dt, srow * table_stride + j);",
      "double c = load_elem(cos_t, t_dt, srow * table_stride + j + half);", 0),
     ("rope_transpose_ignored", "if (transpose) sn = -sn;", "if (transpose > 1) sn = -sn;", 0),
+    ("ln_no_mean_subtraction", "y[i * H + j] = (h[j] - mean) * rstd * wj + bj;",
+     "y[i * H + j] = (h[j] - 0.0 * mean) * rstd * wj + bj;", 0),
+    ("ln_unbiased_variance", "const double var = sq / (double)H;",
+     "const double var = sq / (double)(H > 1 ? H - 1 : 1);", 0),
+    ("ln_uncentred_variance", "for (int64_t j = 0; j < H; ++j) sq += (h[j] - mean) * (h[j] - mean);",
+     "for (int64_t j = 0; j < H; ++j) sq += h[j] * h[j];", 0),
+    ("ln_eps_outside_root", "const double rstd = 1.0 / sqrt(var + eps);",
+     "const double rstd = 1.0 / (sqrt(var) + eps);", 0),
+    ("ln_bias_before_weight", "y[i * H + j] = (h[j] - mean) * rstd * wj + bj;",
+     "y[i * H + j] = ((h[j] - mean) * rstd + bj) * wj;", 0),
+    ("ln_residual_ignored", "if (res) v += load_elem(res, x_dt, i * r_stride + j);",
+     "if (res) v += 0.0 * load_elem(res, x_dt, i * r_stride + j);", 0),
     ("round_half_away", "double q = rint(a / quantum);", "double q = round(a / quantum);", 0),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);", 0),
     ("f16_no_subnormal_quantum", "if (lead < emin) lead = emin;", "if (lead < emin - 30) lead = emin - 30;", 0),

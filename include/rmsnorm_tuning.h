@@ -28,6 +28,11 @@ extern "C" {
  *            dw partial sums (0 = default); grid selects which rows a
  *            workgroup owns: 0 = default, 1 = interleaved (b, b+P, ...),
  *            2 = a contiguous block.
+ * which = 2: RoPE apply.  vpt = wpr = 1 sets the override; third = 1 forces
+ *            the split layout (each thread reads both halves of a head)
+ *            instead of the lane exchange; grid > 0 caps the number of
+ *            workgroups along the positions (they then walk the position
+ *            blocks grid-stride), 0 = one workgroup per block.
  * vpt <= 0 or wpr <= 0 clears the override.  A tile too small for the row
  * takes the two-pass path, which requires vpt = 4 (8 for single elements).
  * An override the shape cannot use makes the call fail with

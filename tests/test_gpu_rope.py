@@ -32,8 +32,10 @@ from transformer_normalization_amd import autograd as ag  # noqa: E402
 @pytest.fixture(autouse=True)
 def _default_streaming():
     tn.set_streaming(-1)
+    tn.set_geometry("rope")
     yield
     tn.set_streaming(-1)
+    tn.set_geometry("rope")
 
 
 def rope_terms(x, cos, sin, dtype, tdtype):
@@ -93,8 +95,10 @@ def test_workload_rope(name):
 # shapes and formats
 # ---------------------------------------------------------------------------
 
+# head_dim 64/128/256/512 (16-bit) take the lane exchange; 48 and 96 the
+# split layout with vectors; 2, 14, 72 and 1000 (16-bit) single elements
 SHAPES = [(1, 1, 1, 2), (2, 3, 1, 8), (3, 5, 3, 14), (2, 257, 32, 64), (1, 33, 7, 72), (2, 19, 4, 128),
-          (3, 9, 2, 256), (1, 4, 300, 64), (2, 3, 2, 1000)]
+          (3, 9, 2, 256), (1, 4, 300, 64), (2, 3, 2, 1000), (2, 17, 5, 96), (1, 9, 3, 48), (2, 5, 3, 512)]
 
 
 @pytest.mark.parametrize("transpose", [False, True], ids=["fwd", "transposed"])
@@ -196,6 +200,21 @@ def test_misaligned_rows_use_single_elements(dtype):
     out = tn.rope_apply(view, G.to_dev(c2, "f32"), G.to_dev(s2, "f32"))
     torch.cuda.synchronize()
     assert np.array_equal(G.to_host(out, dtype), run(x2, c2, s2, dtype, "f32"))
+
+
+@pytest.mark.parametrize("geom", [(1, 1, 1, 0), (1, 1, 0, 7), (1, 1, 1, 5)], ids=["split", "grid7", "split_grid5"])
+@pytest.mark.parametrize("shape", [(2, 300, 8, 64), (3, 41, 4, 128)], ids=["d64", "d128"])
+def test_layouts_and_capped_grid_give_identical_bits(shape, geom):
+    """The split layout and a capped, grid-stride grid compute the same
+    float32 expressions as the default lane exchange: identical bits."""
+    B, S, NH, D = shape
+    x = rand_x(40, shape, "bf16")
+    c, s = tables(40, S, D, "f32")
+    ref = run(x, c, s, "bf16", "f32")
+    tn.set_geometry("rope", *geom)
+    got = run(x, c, s, "bf16", "f32")
+    assert np.array_equal(got, ref)
+    G.assert_ok(rope_vs_oracle(x, c, s, got, "bf16", "f32", name=f"rope geom {geom}"))
 
 
 def test_streaming_does_not_change_bits():

@@ -364,9 +364,9 @@ def rope_apply(x, cos, sin, out=None, transpose: bool = False):
 
 def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: int = 0) -> None:
     """Development hook (include/rmsnorm_tuning.h): force the launch geometry
-    of the forward ("fwd") or backward ("bwd") kernels; vpt=0 restores the
+    of the forward ("fwd"), backward ("bwd") or RoPE ("rope") kernels; vpt=0 restores the
     library's own choice."""
-    code = {"fwd": 0, "bwd": 1}[which]
+    code = {"fwd": 0, "bwd": 1, "rope": 2}[which]
     load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))
 
 

@@ -65,6 +65,16 @@ rmsn_status_t check_stride(const char *name, int64_t stride, int64_t rows, int64
 bool use_streaming(int64_t bytes_moved);
 void set_stream_mode(int mode);
 
+// Launch-geometry override (include/rmsnorm_tuning.h): which = 0 forward,
+// 1 backward, 2 RoPE; the meaning of a..d is the caller's.
+struct Override {
+    bool set = false;
+    int a = 0, b = 0, c = 0;
+    int64_t d = 0;
+};
+Override get_override(int which);
+void set_override(int which, int a, int b, int c, int64_t d);
+
 rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what);
 
 }  // namespace host

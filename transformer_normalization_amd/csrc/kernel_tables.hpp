@@ -1,12 +1,13 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
-// kernels_bwd.hip, kernels_bwd_residual.hip, kernels_rope.hip) so that they
-// compile in parallel; the host code only sees these functions.
+// kernels_bwd.hip, kernels_bwd_residual.hip, kernels_rope.hip, kernels_ln.hip)
+// so that they compile in parallel; the host code only sees these functions.
 #pragma once
 
 #include "bwd_kernels.hpp"
 #include "fwd_kernels.hpp"
+#include "ln_kernels.hpp"
 #include "rmsnorm.h"
 #include "rope_kernels.hpp"
 
@@ -15,6 +16,7 @@ namespace rmsn {
 typedef void (*fwd_fn)(const FwdParams);
 typedef void (*bwd_fn)(const BwdParams);
 typedef void (*rope_fn)(const RopeParams);
+typedef void (*ln_fn)(const LnParams);
 
 // nullptr when no instantiation matches (vec: elements per access; vpt:
 // accesses per thread; nt: streaming accesses)
@@ -26,7 +28,10 @@ bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bo
 // the backward of the fused residual pre-norm (adds the residual-stream gradient)
 bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 const void *dw_finalize_kernel();
-// vec: 16 / element size, or 1 for single elements; tdt: x's format or float32
-rope_fn rope_lookup(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool nt);
+// vec: 16 / element size, or 1 for single elements; tdt: x's format or
+// float32; xchg: the lane-exchange layout (vectors only)
+// LayerNorm forward, plain or fused with the residual add (resid)
+ln_fn ln_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt, bool resid);
+rope_fn rope_lookup(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool nt, bool xchg);
 
 }  // namespace rmsn

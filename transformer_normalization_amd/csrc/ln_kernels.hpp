@@ -1,0 +1,252 @@
+// ln_kernels.hpp -- gfx950 LayerNorm forward, plain and fused with the
+// residual add that precedes it in a pre-LayerNorm transformer block (the
+// page "SpeedROCm: shape-aware Triton acceleration for Transformer
+// inference", "How the solution addresses the problem", item 4).
+//
+// What is computed, all in float32 (torch.nn's LayerNorm semantics):
+//   h     = x, or float32(x) + float32(r) with r_out = RNE(h)
+//   mean  = sum(h) * (1/H)
+//   var   = sum((h - mean)^2) * (1/H)      (population variance, centred)
+//   rstd  = rsqrt(var + eps)
+//   y     = fma((h - mean) * rstd, w, b)    (w = 1, b = 0 when absent)
+//
+// The variance is taken about the computed mean in a second reduction, never
+// as mean(h^2) - mean^2, which cancels when |mean| >> std.
+//
+// Work layout as the RMSNorm forward (fwd_kernels.hpp): row groups of wpr
+// waves own a row at a time, rpw row groups per workgroup, grid-stride over
+// the rows with a uniform trip count; thread t owns the vectors t, t +
+// 64*wpr, ... of the row; weight and bias stay packed in registers.
+//   * Resident path: the row (and the residual) stays packed in registers
+//     for both reductions and the output -- one HBM read per input element
+//     and one write per output element.
+//   * Long rows: pass 1 sums h, pass 2 sums (h - mean)^2, pass 3 writes y
+//     (and r_out); passes 1 and 2 use cached loads.
+#pragma once
+
+#include "numerics.hpp"
+
+namespace rmsn {
+
+struct LnParams {
+    const void *x;
+    const void *r;    // residual (fused form only)
+    const void *w;    // may be null
+    const void *b;    // may be null
+    void *y;
+    void *ro;         // residual_out, may be null
+    float *mean;      // may be null
+    float *rstd;      // may be null
+    int64_t xs, rs, ys, ros;  // row strides, elements
+    int64_t M;
+    int64_t iters;    // row-group iterations per workgroup
+    int H;
+    int nvec;
+    int wpr;
+    int rpw;
+    int nchunks;
+    float eps;
+    float inv_h;
+};
+
+template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT>
+__global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
+    // one LDS area per reduction of a row; consecutive reductions alternate
+    // areas, so one barrier per reduction suffices (see row_sum)
+    __shared__ float red[2][16];
+    const int row_threads = 64 * p.wpr;
+    const int slot = threadIdx.x / row_threads;
+    const int t = threadIdx.x - slot * row_threads;
+    const int wave_in_row = t >> 6;
+    const int64_t gstride = (int64_t)gridDim.x;
+
+    if constexpr (!TWO_PASS) {
+        Raw<WDT, VEC> wr[VPT], br[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int v = t + k * row_threads;
+            if (p.w != nullptr && v < p.nvec)
+                wr[k].load(p.w, (int64_t)v * VEC);
+            else
+                wr[k].fill_one();
+            if (p.b != nullptr && v < p.nvec)
+                br[k].load(p.b, (int64_t)v * VEC);
+            else
+                br[k].zero();
+        }
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
+            Raw<XDT, VEC> xr[VPT];
+            Raw<XDT, VEC> rr[RESID ? VPT : 1];
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int v = t + k * row_threads;
+                if (valid && v < p.nvec) {
+                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                    if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
+                } else {
+                    xr[k].zero();
+                    if constexpr (RESID) rr[k].zero();
+                }
+            }
+            // h of vector k, widened (and summed with the residual) again at
+            // each use; every widening gives the same floats
+            auto widen_h = [&](int k, float *hv) {
+                xr[k].widen_to(hv);
+                if constexpr (RESID) {
+                    float rv[VEC];
+                    rr[k].widen_to(rv);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                }
+            };
+            float s1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                float hv[VEC];
+                widen_h(k, hv);
+                if constexpr (RESID) {
+                    const int v = t + k * row_threads;
+                    if (p.ro != nullptr && valid && v < p.nvec)
+                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                }
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s1 += hv[e];
+            }
+            const float mean = row_sum(s1, p.wpr, wave_in_row, &red[0][slot * p.wpr]) * p.inv_h;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                xr[k].opaque();
+                if constexpr (RESID) rr[k].opaque();
+            }
+            float s2 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int v = t + k * row_threads;
+                float hv[VEC];
+                widen_h(k, hv);
+                if (v < p.nvec) {  // padding lanes hold h = 0, not mean
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float d = hv[e] - mean;
+                        s2 = __builtin_fmaf(d, d, s2);
+                    }
+                }
+            }
+            const float var = row_sum(s2, p.wpr, wave_in_row, &red[1][slot * p.wpr]) * p.inv_h;
+            const float rs = fast_rsqrt(var + p.eps);
+            if (valid && t == 0) {
+                if (p.mean != nullptr) p.mean[row] = mean;
+                if (p.rstd != nullptr) p.rstd[row] = rs;
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                xr[k].opaque();
+                if constexpr (RESID) rr[k].opaque();
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int v = t + k * row_threads;
+                if (valid && v < p.nvec) {
+                    float hv[VEC], wv[VEC], bv[VEC], o[VEC];
+                    widen_h(k, hv);
+                    wr[k].widen_to(wv);
+                    br[k].widen_to(bv);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
+                    store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                }
+            }
+        }
+    } else {
+        const int chunk = row_threads * VPT;
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
+            // h of vector v (cached loads for the two reduction passes)
+            auto load_h = [&](int v, float *hv, auto nt_tag) {
+                constexpr bool LNT = decltype(nt_tag)::value;
+                load_elems<XDT, VEC, LNT>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                if constexpr (RESID) {
+                    float rv[VEC];
+                    load_elems<XDT, VEC, LNT>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                }
+            };
+            using cached = std::integral_constant<bool, false>;
+            using streamed = std::integral_constant<bool, NT>;
+            // pass 1: sum of h
+            float s1 = 0.0f;
+            for (int c = 0; c < p.nchunks; ++c) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (valid && v < p.nvec) {
+                        float hv[VEC];
+                        load_h(v, hv, cached{});
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) s1 += hv[e];
+                    }
+                }
+            }
+            const float mean = row_sum(s1, p.wpr, wave_in_row, &red[0][slot * p.wpr]) * p.inv_h;
+            // pass 2: sum of (h - mean)^2
+            float s2 = 0.0f;
+            for (int c = 0; c < p.nchunks; ++c) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (valid && v < p.nvec) {
+                        float hv[VEC];
+                        load_h(v, hv, cached{});
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const float d = hv[e] - mean;
+                            s2 = __builtin_fmaf(d, d, s2);
+                        }
+                    }
+                }
+            }
+            const float var = row_sum(s2, p.wpr, wave_in_row, &red[1][slot * p.wpr]) * p.inv_h;
+            const float rs = fast_rsqrt(var + p.eps);
+            if (valid && t == 0) {
+                if (p.mean != nullptr) p.mean[row] = mean;
+                if (p.rstd != nullptr) p.rstd[row] = rs;
+            }
+            // pass 3: reload, normalise, store (each element is read and
+            // written by the same thread, so in-place outputs are safe)
+            for (int c = 0; c < p.nchunks; ++c) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (valid && v < p.nvec) {
+                        float hv[VEC], wv[VEC], bv[VEC], o[VEC];
+                        load_h(v, hv, streamed{});
+                        if constexpr (RESID) {
+                            if (p.ro != nullptr) store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                        }
+                        if (p.w != nullptr) {
+                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
+                        }
+                        if (p.b != nullptr) {
+                            load_elems<WDT, VEC>(p.b, (int64_t)v * VEC, bv);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) bv[e] = 0.0f;
+                        }
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
+                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace rmsn

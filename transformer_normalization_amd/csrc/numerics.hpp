@@ -301,6 +301,8 @@ constexpr int fwd_max_threads(int elems, int mode) {  // mode: 0 plain, 1 residu
     return mode == 0 ? (elems <= 32 ? 1024 : 512)
                      : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);
 }
+// LayerNorm keeps x (and the residual) packed plus packed weight and bias
+constexpr int ln_max_threads(int elems) { return elems <= 16 ? 1024 : elems <= 32 ? 512 : 256; }
 // (res: the residual backward holds a third row tile, dres, in registers)
 constexpr int bwd_max_threads(int elems, bool res = false) {
     return res ? (elems <= 8 ? 1024 : elems <= 16 ? 512 : 256) : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);

@@ -1,6 +1,6 @@
 // rmsnorm_api.hip -- host side of the gfx950 RMSNorm library: argument
 // validation, launch geometry and the extern "C" entry points declared in
-// include/rmsnorm.h (shared helpers: host_common.hpp).
+// include/rmsnorm.h and include/layernorm.h (shared helpers: host_common.hpp).
 //
 // Nothing here allocates, frees or synchronises.  Argument errors are found
 // before the first HIP call.  The only HIP calls are hipGetDevice,
@@ -19,6 +19,7 @@
 
 #include "host_common.hpp"
 #include "kernel_tables.hpp"
+#include "layernorm.h"
 #include "rmsnorm.h"
 #include "rmsnorm_tuning.h"
 
@@ -53,53 +54,9 @@ rmsn_status_t check_eps(float eps) {
 // geometry
 // ---------------------------------------------------------------------------
 
-// Launch-geometry override for tuning and for tests that must reach the
-// grid-stride and two-pass paths at small sizes.  Set through
-// rmsnorm_tuning_set_geometry() (include/rmsnorm_tuning.h) or, once per
-// process at first use, from the environment:
-//   RMSN_FWD_GEOM="vpt,wpr,rpw,grid"   (grid 0 = one workgroup per row group)
-//   RMSN_BWD_GEOM="vpt,wpr,P"
-struct Override {
-    bool set = false;
-    int a = 0, b = 0, c = 0;
-    int64_t d = 0;
-};
-
-std::mutex g_override_mu;
-Override g_override[2];
-std::atomic<bool> g_override_any{false};
-std::once_flag g_override_env_once;
-
-Override parse_override(const char *var) {
-    Override o;
-    const char *s = getenv(var);
-    if (s == nullptr || *s == '\0') return o;
-    long long v[4] = {0, 0, 0, 0};
-    int n = sscanf(s, "%lld,%lld,%lld,%lld", &v[0], &v[1], &v[2], &v[3]);
-    if (n >= 2) {
-        o.set = true;
-        o.a = (int)v[0];
-        o.b = (int)v[1];
-        o.c = (int)v[2];
-        o.d = v[3];
-    }
-    return o;
-}
-
-Override get_override(int which) {
-    std::call_once(g_override_env_once, []() {
-        std::lock_guard<std::mutex> lk(g_override_mu);
-        g_override[0] = parse_override("RMSN_FWD_GEOM");
-        g_override[1] = parse_override("RMSN_BWD_GEOM");
-        g_override_any.store(g_override[0].set || g_override[1].set);
-    });
-    if (!g_override_any.load(std::memory_order_relaxed)) return Override{};
-    std::lock_guard<std::mutex> lk(g_override_mu);
-    return g_override[which];
-}
 
 // vectors per thread available as kernel instantiations
-enum class Kind { Fwd, FwdResid, FwdAdaln, Bwd, BwdRes };
+enum class Kind { Fwd, FwdResid, FwdAdaln, Ln, Bwd, BwdRes };
 constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
 constexpr int kBwdVecVpt[] = {1, 2, 3, 4};
 constexpr int kScalarVpt[] = {1, 2, 4, 8};
@@ -109,6 +66,7 @@ int max_threads_for(Kind kind, int vpt, int vec) {
            : kind == Kind::BwdRes   ? bwd_max_threads(vpt * vec, true)
            : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID)
            : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN)
+           : kind == Kind::Ln       ? ln_max_threads(vpt * vec)
                                     : fwd_max_threads(vpt * vec, MODE_PLAIN);
 }
 
@@ -181,13 +139,26 @@ struct Cond {
     int64_t rows_per_cond = 1;  // x rows per conditioning row
 };
 
-// mode: MODE_PLAIN, MODE_RESID or MODE_ADALN.  For AdaLN, wdt is the format of
-// the weight, scale and shift.
+// LayerNorm calls (modes kLn, kLnResid): the bias and the per-row mean
+// output; the rrms argument of fwd_impl then receives rstd.
+struct LnExtra {
+    const void *bias = nullptr;
+    float *mean = nullptr;
+};
+constexpr int kLn = 3, kLnResid = 4;  // host-side modes beside MODE_PLAIN/RESID/ADALN
+
+// mode: MODE_PLAIN, MODE_RESID, MODE_ADALN, kLn or kLnResid.  For AdaLN, wdt
+// is the format of the weight, scale and shift; for LayerNorm, of the weight
+// and bias.
 rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64_t rs, const void *w, void *y,
                        int64_t ys, void *ro, int64_t ros, float *rrms, int64_t M, int64_t H, float eps,
-                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, const Cond &cond, hipStream_t stream) {
-    const bool resid = mode == MODE_RESID, adaln = mode == MODE_ADALN;
-    rmsn_status_t st = check_common(M, H, xdt, (w || adaln) ? (const void *)1 : nullptr, wdt);
+                       rmsn_dtype_t xdt, rmsn_dtype_t wdt, const Cond &cond, const LnExtra &lnx,
+                       hipStream_t stream) {
+    const bool ln = mode == kLn || mode == kLnResid;
+    const bool resid = mode == MODE_RESID || mode == kLnResid, adaln = mode == MODE_ADALN;
+    const void *bias = ln ? lnx.bias : nullptr;
+    float *mean = ln ? lnx.mean : nullptr;
+    rmsn_status_t st = check_common(M, H, xdt, (w || adaln || bias) ? (const void *)1 : nullptr, wdt);
     if (st != RMSN_OK) return st;
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     const int eb = dtype_bytes(xdt);
@@ -213,17 +184,19 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         return fail(RMSN_ERR_INVALID_ARG, "scale and shift must not be NULL");
 
     const int wb = w ? dtype_bytes(wdt) : 1;
-    Region ins[5] = {mat("x", x, xs, M, H, eb), mat("residual", resid ? r : nullptr, rs, M, H, eb),
+    Region ins[6] = {mat("x", x, xs, M, H, eb), mat("residual", resid ? r : nullptr, rs, M, H, eb),
                      vec("w", w, H, wb), mat("scale", adaln ? cond.scale : nullptr, cond.cs, crows, H, pb),
-                     mat("shift", adaln ? cond.shift : nullptr, cond.cs, crows, H, pb)};
-    Region outs[3] = {mat("y", y, ys, M, H, eb), mat("residual_out", resid ? ro : nullptr, ros, M, H, eb),
-                      vec("rrms", rrms, M, 4)};
-    if ((st = check_overlap(outs, 3, ins, 5)) != RMSN_OK) return st;
-    // rrms is never "the same buffer" as an input: compare ranges only
-    if (rrms != nullptr) {
+                     mat("shift", adaln ? cond.shift : nullptr, cond.cs, crows, H, pb), vec("bias", bias, H, pb)};
+    Region outs[4] = {mat("y", y, ys, M, H, eb), mat("residual_out", resid ? ro : nullptr, ros, M, H, eb),
+                      vec(ln ? "rstd" : "rrms", rrms, M, 4), vec("mean", mean, M, 4)};
+    if ((st = check_overlap(outs, 4, ins, 6)) != RMSN_OK) return st;
+    // the per-row statistics are never "the same buffer" as an input: compare
+    // ranges only
+    for (int i = 2; i < 4; ++i) {
+        if (!outs[i].present) continue;
         for (const Region &in : ins)
-            if (in.present && outs[2].overlaps(in))
-                return fail(RMSN_ERR_INVALID_ARG, "rrms overlaps input %s", in.name);
+            if (in.present && outs[i].overlaps(in))
+                return fail(RMSN_ERR_INVALID_ARG, "%s overlaps input %s", outs[i].name, in.name);
     }
 
     // vector path: every row start 16-byte aligned and H a whole number of vectors
@@ -235,8 +208,9 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
                  (ro == nullptr || (aligned16(ro) && (ros * eb) % 16 == 0));
     if (adaln)
         vec_ok = vec_ok && aligned16(cond.scale) && aligned16(cond.shift) && (cond.cs * pb) % 16 == 0;
+    if (bias != nullptr) vec_ok = vec_ok && aligned16(bias);
 
-    const Kind kind = resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
+    const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     const Override ov = get_override(0);
@@ -264,12 +238,42 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     const int64_t streamed = (resid ? (ro ? 4 : 3) : 2) * M * H * eb;
     const bool nt = use_streaming(streamed);
-    const rmsn_dtype_t kwdt = (w || adaln) ? wdt : xdt;
+    const rmsn_dtype_t kwdt = (w || adaln || bias) ? wdt : xdt;
+    int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
+    if (ln) {
+        ln_fn fn = ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
+        if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
+        if ((st = device_info(&cus)) != RMSN_OK) return st;
+        LnParams p;
+        p.x = x;
+        p.r = r;
+        p.w = w;
+        p.b = bias;
+        p.y = y;
+        p.ro = ro;
+        p.mean = mean;
+        p.rstd = rrms;
+        p.xs = xs;
+        p.rs = rs;
+        p.ys = ys;
+        p.ros = ros;
+        p.M = M;
+        p.iters = iters;
+        p.H = (int)H;
+        p.nvec = g.nvec;
+        p.wpr = g.wpr;
+        p.rpw = g.rpw;
+        p.nchunks = g.nchunks;
+        p.eps = eps;
+        p.inv_h = (float)(1.0 / (double)H);
+        void *args[] = {&p};
+        return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
+                      resid ? "layernorm_fwd_residual" : "layernorm_fwd");
+    }
     fwd_fn fn = resid   ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                 : adaln ? fwd_lookup_adaln(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                         : fwd_lookup_plain(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
-    int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if ((st = device_info(&cus)) != RMSN_OK) return st;
 
     FwdParams p;
@@ -468,7 +472,7 @@ RMSN_API rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *
                           int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
                           hipStream_t stream) {
     rmsn_status_t s = fwd_impl(MODE_PLAIN, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
-                               x_dtype, w_dtype, Cond{}, stream);
+                               x_dtype, w_dtype, Cond{}, LnExtra{}, stream);
     return s == RMSN_OK ? ok() : s;
 }
 
@@ -477,7 +481,7 @@ RMSN_API rmsn_status_t rmsnorm_fwd_residual(const void *x, int64_t x_stride, con
                                    int64_t ro_stride, float *rrms, int64_t M, int64_t H, float eps,
                                    rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream) {
     rmsn_status_t s = fwd_impl(MODE_RESID, x, x_stride, residual, r_stride, w, y, y_stride, residual_out, ro_stride,
-                               rrms, M, H, eps, x_dtype, w_dtype, Cond{}, stream);
+                               rrms, M, H, eps, x_dtype, w_dtype, Cond{}, LnExtra{}, stream);
     return s == RMSN_OK ? ok() : s;
 }
 
@@ -491,7 +495,31 @@ RMSN_API rmsn_status_t rmsnorm_adaln_fwd(const void *x, int64_t x_stride, const 
     c.cs = cond_stride;
     c.rows_per_cond = rows_per_cond;
     rmsn_status_t s = fwd_impl(MODE_ADALN, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
-                               x_dtype, param_dtype, c, stream);
+                               x_dtype, param_dtype, c, LnExtra{}, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t layernorm_fwd(const void *x, int64_t x_stride, const void *w, const void *b, void *y,
+                                     int64_t y_stride, float *mean, float *rstd, int64_t M, int64_t H, float eps,
+                                     rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream) {
+    LnExtra e;
+    e.bias = b;
+    e.mean = mean;
+    rmsn_status_t s = fwd_impl(kLn, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rstd, M, H, eps, x_dtype,
+                               w_dtype, Cond{}, e, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t layernorm_fwd_residual(const void *x, int64_t x_stride, const void *residual, int64_t r_stride,
+                                              const void *w, const void *b, void *y, int64_t y_stride,
+                                              void *residual_out, int64_t ro_stride, float *mean, float *rstd,
+                                              int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype,
+                                              rmsn_dtype_t w_dtype, hipStream_t stream) {
+    LnExtra e;
+    e.bias = b;
+    e.mean = mean;
+    rmsn_status_t s = fwd_impl(kLnResid, x, x_stride, residual, r_stride, w, y, y_stride, residual_out, ro_stride,
+                               rstd, M, H, eps, x_dtype, w_dtype, Cond{}, e, stream);
     return s == RMSN_OK ? ok() : s;
 }
 
@@ -532,17 +560,7 @@ RMSN_API const char *rmsnorm_last_error(void) { return last_error(); }
 RMSN_API void rmsnorm_tuning_set_streaming(int mode) { set_stream_mode(mode); }
 
 RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid) {
-    get_override(0);  // the environment is read first, so a later call wins
-    std::lock_guard<std::mutex> lk(g_override_mu);
-    if (which < 0 || which > 1) return;
-    Override o;
-    o.set = vpt > 0 && wpr > 0;
-    o.a = vpt;
-    o.b = wpr;
-    o.c = third;
-    o.d = grid;
-    g_override[which] = o;
-    g_override_any.store(g_override[0].set || g_override[1].set);
+    set_override(which, vpt, wpr, third, grid);
 }
 
 }  // extern "C"

@@ -74,8 +74,14 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
                         ors % vecw == 0 && ohs % vecw == 0 && aligned16(cos_t) && aligned16(sin_t) &&
                         (ts * tb) % 16 == 0;
     const int vec = vec_ok ? vecw : 1;
+    const int64_t nvec = half / vec;
+    // lane exchange when a head's 2*nvec lanes are a power of two <= 64, so
+    // heads never straddle waves and partners are lane ^ nvec
+    bool xchg = vec > 1 && nvec <= 32 && (nvec & (nvec - 1)) == 0;
+    const Override ov = get_override(2);
+    if (ov.set && ov.c == 1) xchg = false;
     const bool nt = use_streaming(2 * rows * NH * D * eb);
-    rope_fn fn = rope_lookup(xdt, tdt, vec, nt);
+    rope_fn fn = rope_lookup(xdt, tdt, vec, nt, xchg);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no RoPE kernel for vec %d", vec);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -93,14 +99,16 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     p.S = S;
     p.B = B;
     p.half = (int)half;
-    p.nvec = (int)(half / vec);
-    p.items = (int)(NH * p.nvec);
+    p.nvec = (int)nvec;
+    p.items = (int)(NH * (xchg ? 2 * nvec : nvec));
     p.ipw = p.items < kRopeThreads ? p.items : kRopeThreads;
     p.tpw = kRopeThreads / p.ipw;
     p.sign = transpose ? -1.0f : 1.0f;
-    const int64_t gx = (S + p.tpw - 1) / p.tpw;
+    p.nblocks = (S + p.tpw - 1) / p.tpw;
+    int64_t gx = p.nblocks;
+    if (ov.set && ov.d > 0 && ov.d < gx) gx = ov.d;
+    if (gx > INT32_MAX) gx = INT32_MAX;  // the position blocks are walked grid-stride
     const int64_t gy = (p.items + p.ipw - 1) / p.ipw;
-    if (gx > INT32_MAX) return fail(RMSN_ERR_UNSUPPORTED, "seq_len = %lld is too large", (long long)S);
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)gx, (unsigned)gy), dim3(kRopeThreads), args, stream, "rope_apply");
 }

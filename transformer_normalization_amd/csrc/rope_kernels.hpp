@@ -6,16 +6,21 @@
 // rotated value written once; the cos/sin tables (seq_len rows) are read by
 // every head and every batch of a position, so they come from the caches.
 //
-// Work item = (position s, head h, vector v): a thread holds the VEC
-// elements j = v*VEC .. v*VEC+VEC-1 of the first half of head h and the
-// matching elements of the second half (two 16-byte accesses head_dim/2
-// apart), and the VEC table entries of those columns, which it loads once and
-// applies to every batch b of position s (rows b * seq_len + s).  Consecutive
-// lanes take consecutive vectors of one head, then the next head, so a wave's
-// two loads together cover a contiguous stretch of the token row.
+// Two layouts of the work, both applying a position's table entries (loaded
+// once per thread) to every batch b of that position (rows b * seq_len + s):
+//
+//  - lane exchange (XCHG, the default when a half head is a power-of-two
+//    number <= 32 of 16-byte vectors): lane k of a head's 2*nvec lanes holds
+//    vector k of the head, so every load and store instruction of a wave
+//    covers whole contiguous 128-byte lines; the partner element j + D/2 (or
+//    j - D/2) is fetched from lane k ^ nvec with ds_bpermute.
+//  - split (any other shape, and single elements): a thread holds the VEC
+//    elements j.. of the first half and the matching elements of the second
+//    half (two accesses head_dim/2 apart).
 //
 // Mapping: a workgroup of 256 threads covers `tpw` positions x `ipw` items;
 // blockIdx.y selects the block of items when one position has more than 256.
+// Position blocks are walked grid-stride, so a capped grid also works.
 #pragma once
 
 #include "numerics.hpp"
@@ -34,68 +39,135 @@ struct RopeParams {
     int64_t B;         // batch
     int half;          // head_dim / 2
     int nvec;          // vectors per half head (half / VEC)
-    int items;         // num_heads * nvec
+    int items;         // work items per position: num_heads * nvec (split), * 2 nvec (exchange)
     int ipw;           // items per workgroup row (<= 256)
     int tpw;           // positions per workgroup
+    int64_t nblocks;   // position blocks: ceil(S / tpw)
     float sign;        // +1, or -1 for the transposed rotation
 };
 
 constexpr int kRopeThreads = 256;
 
-template <int XDT, int TDT, int VEC, bool NT>
+// out0 = x0 c - x1 s and out1 = x0 s + x1 c, the first product fused
+__device__ __forceinline__ float rot_lo(float x0, float x1, float c, float sn) {
+    return __builtin_fmaf(x0, c, -(x1 * sn));
+}
+__device__ __forceinline__ float rot_hi(float x0, float x1, float c, float sn) {
+    return __builtin_fmaf(x0, sn, x1 * c);
+}
+
+template <int DT, int N>
+__device__ __forceinline__ Raw<DT, N> from_lane(const Raw<DT, N> &r, int byte_addr) {
+    Raw<DT, N> o;
+#pragma unroll
+    for (int c = 0; c < Raw<DT, N>::CHUNKS; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            o.v[c][w] = (uint32_t)__builtin_amdgcn_ds_bpermute(byte_addr, (int)r.v[c][w]);
+    return o;
+}
+
+template <int XDT, int TDT, int VEC, bool NT, bool XCHG>
 __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopeParams p) {
     const int t = threadIdx.x;
     const int lt = t / p.ipw;
     const int item = blockIdx.y * p.ipw + (t - lt * p.ipw);
-    const int64_t s = (int64_t)blockIdx.x * p.tpw + lt;
-    if (lt >= p.tpw || item >= p.items || s >= p.S) return;
-    const int h = item / p.nvec;
-    const int col = (item - h * p.nvec) * VEC;
-
-    float c[VEC], sn[VEC];
-    load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
-    load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) sn[e] *= p.sign;  // exact
-
-    const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + col;
-    const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + col;
+    // partners (exchange layout) share lt and both pass or both fail here
+    if (lt >= p.tpw || item >= p.items) return;
     const int64_t xstep = p.S * p.xrs;  // one batch further
     const int64_t ostep = p.S * p.ors;
-    // two batches per iteration: both rows' loads are issued before either
-    // row is stored (an output may be the input itself, but each thread
-    // reads its own elements of a row before writing them)
-    int64_t b = 0;
-    for (; b + 1 < p.B; b += 2) {
-        float x0[2][VEC], x1[2][VEC];
+
+    if constexpr (XCHG) {
+        static_assert(VEC > 1, "the exchange layout moves 16-byte vectors");
+        const int per_head = 2 * p.nvec;
+        const int h = item / per_head;
+        const int k = item - h * per_head;  // == t % per_head: heads are aligned to per_head lanes
+        const bool upper = k >= p.nvec;
+        const int col = (upper ? k - p.nvec : k) * VEC;  // table column
+        const int partner = ((t & 63) ^ p.nvec) << 2;   // ds_bpermute byte address
+        for (int64_t pb = blockIdx.x; pb < p.nblocks; pb += gridDim.x) {
+            const int64_t s = pb * p.tpw + lt;
+            if (s >= p.S) break;
+            float c[VEC], sn[VEC];
+            load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
+            load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep, x0[u]);
-            load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep + p.half, x1[u]);
-        }
+            for (int e = 0; e < VEC; ++e) sn[e] *= p.sign;  // exact
+            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
+            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + k * VEC;
+            auto finish = [&](const Raw<XDT, VEC> &mine, int64_t o) {
+                const Raw<XDT, VEC> theirs = from_lane(mine, partner);
+                float a[VEC], b[VEC], out[VEC];
+                mine.widen_to(a);
+                theirs.widen_to(b);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float o0[VEC], o1[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                o0[e] = __builtin_fmaf(x0[u][e], c[e], -(x1[u][e] * sn[e]));
-                o1[e] = __builtin_fmaf(x0[u][e], sn[e], x1[u][e] * c[e]);
+                for (int e = 0; e < VEC; ++e)
+                    out[e] = upper ? rot_hi(b[e], a[e], c[e], sn[e]) : rot_lo(a[e], b[e], c[e], sn[e]);
+                store_elems<XDT, VEC, NT>(p.out, o, out);
+            };
+            int64_t b = 0;
+            for (; b + 1 < p.B; b += 2) {
+                Raw<XDT, VEC> r0, r1;
+                r0.template load<NT>(p.x, xoff + b * xstep);
+                r1.template load<NT>(p.x, xoff + (b + 1) * xstep);
+                finish(r0, ooff + b * ostep);
+                finish(r1, ooff + (b + 1) * ostep);
             }
-            store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep, o0);
-            store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep + p.half, o1);
+            if (b < p.B) {
+                Raw<XDT, VEC> r0;
+                r0.template load<NT>(p.x, xoff + b * xstep);
+                finish(r0, ooff + b * ostep);
+            }
         }
-    }
-    if (b < p.B) {
-        float x0[VEC], x1[VEC], o0[VEC], o1[VEC];
-        load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep, x0);
-        load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep + p.half, x1);
+    } else {
+        const int h = item / p.nvec;
+        const int col = (item - h * p.nvec) * VEC;
+        for (int64_t pb = blockIdx.x; pb < p.nblocks; pb += gridDim.x) {
+            const int64_t s = pb * p.tpw + lt;
+            if (s >= p.S) break;
+            float c[VEC], sn[VEC];
+            load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
+            load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            o0[e] = __builtin_fmaf(x0[e], c[e], -(x1[e] * sn[e]));
-            o1[e] = __builtin_fmaf(x0[e], sn[e], x1[e] * c[e]);
+            for (int e = 0; e < VEC; ++e) sn[e] *= p.sign;  // exact
+            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + col;
+            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + col;
+            // two batches per iteration: both rows' loads are issued before
+            // either row is stored (an output may be the input itself, but
+            // each thread reads its own elements of a row before writing them)
+            int64_t b = 0;
+            for (; b + 1 < p.B; b += 2) {
+                float x0[2][VEC], x1[2][VEC];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep, x0[u]);
+                    load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep + p.half, x1[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float o0[VEC], o1[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        o0[e] = rot_lo(x0[u][e], x1[u][e], c[e], sn[e]);
+                        o1[e] = rot_hi(x0[u][e], x1[u][e], c[e], sn[e]);
+                    }
+                    store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep, o0);
+                    store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep + p.half, o1);
+                }
+            }
+            if (b < p.B) {
+                float x0[VEC], x1[VEC], o0[VEC], o1[VEC];
+                load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep, x0);
+                load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep + p.half, x1);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    o0[e] = rot_lo(x0[e], x1[e], c[e], sn[e]);
+                    o1[e] = rot_hi(x0[e], x1[e], c[e], sn[e]);
+                }
+                store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep, o0);
+                store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep + p.half, o1);
+            }
         }
-        store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep, o0);
-        store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep + p.half, o1);
     }
 }
 

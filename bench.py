@@ -14,7 +14,7 @@ Workloads (default: the forward at bf16 M=8192 H=4096):
   fwd_bf16_8192x4096, fwd_f32_64x512, fwd_bf16_32768x2048, fwd_bf16_32768x2048_noweight,
   fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144,
   bwd_residual_bf16_16384x8192, adaln_bf16_2x4096x2048_batchcond, adaln_bf16_2x4096x2048_tokencond,
-  rope_bf16_2x8064x32x64, rope_bf16_2x4096x32x128
+  rope_bf16_2x8064x32x64, rope_bf16_2x4096x32x128, ln_residual_f32_16384x1024
 
 --graph captures the timed steps in HIP graphs (blocks of steps, replayed) so
 that host launch overhead cannot leave the GPU idle between short kernels;
@@ -52,10 +52,12 @@ KERNEL_SOURCES = {
     "bwd_residual": _BWD + ("kernels_bwd_residual.hip", "rmsnorm_api.hip"),
     "adaln": _FWD + ("kernels_adaln.hip", "rmsnorm_api.hip"),
     "rope": ("numerics.hpp", "rope_kernels.hpp", "kernel_tables.hpp", "kernels_rope.hip", "rope_api.hip"),
+    "ln_residual": ("numerics.hpp", "ln_kernels.hpp", "kernel_tables.hpp", "kernels_ln.hip", "rmsnorm_api.hip"),
 }
 # the kernel whose launches the counters describe
 KERNEL_KEY = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
-              "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel"}
+              "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel",
+              "ln_residual": "layernorm_fwd_kernel"}
 
 WORKLOADS = {
     "fwd_bf16_8192x4096": ("fwd_bf16_8192x4096", True),
@@ -70,6 +72,7 @@ WORKLOADS = {
     "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
     "rope_bf16_2x8064x32x64": ("rope_bf16_2x8064x32x64", True),
     "rope_bf16_2x4096x32x128": ("rope_bf16_2x4096x32x128", True),
+    "ln_residual_f32_16384x1024": ("ln_residual_f32_16384x1024", True),
 }
 
 
@@ -128,6 +131,9 @@ def algorithmic_bytes(spec, weighted, rows=None):
         return 2 * mat + w
     if kind == "fwd_residual":
         return 4 * mat + w
+    if kind == "ln_residual":
+        # x, r read; y, residual_out written; weight and bias read once
+        return 4 * mat + 2 * w
     if kind == "bwd":
         # x, dy read; dx written; rrms read; w read; dw written (float32)
         return 3 * mat + M * 4 + w + H * 4
@@ -189,6 +195,8 @@ def cpu_baseline(spec, weighted, seconds):
                              d["wdtype"])
         elif kind == "fwd_residual":
             oracle.fwd_residual(d["x"], d["r"], w, eps, d["dtype"], d["wdtype"])
+        elif kind == "ln_residual":
+            oracle.layernorm(d["x"], d["r"], w, d["b"] if weighted else None, eps, d["dtype"], d["wdtype"])
         elif kind == "bwd_residual":
             oracle.bwd_residual(d["dy"], d["x"], d["dres"], w, r32, d["dtype"], d["wdtype"])
         else:
@@ -294,9 +302,10 @@ def setup_steps(spec, weighted, dev, per_step):
     sets = []
     for i in range(nsets):
         s = {"x": x0 if i == 0 else x0.clone(), "y": torch.empty_like(x0)}
-        for key in {"fwd_residual": ("r",), "bwd": ("dy",), "bwd_residual": ("dy", "dres")}.get(kind, ()):
+        for key in {"fwd_residual": ("r",), "ln_residual": ("r",), "bwd": ("dy",),
+                    "bwd_residual": ("dy", "dres")}.get(kind, ()):
             s[key] = up(d[key], dt) if i == 0 else sets[0][key].clone()
-        if kind == "fwd_residual":
+        if kind in ("fwd_residual", "ln_residual"):
             s["ro"] = torch.empty_like(x0)
         sets.append(s)
     copy_src, copy_dst = sets[0]["x"], sets[1]["y"]
@@ -312,6 +321,7 @@ def setup_steps(spec, weighted, dev, per_step):
     eps = spec["eps"]
     M, H = spec["M"], spec["H"]
     w = up(d["w"], d["wdtype"]) if weighted else None
+    bias = up(d["b"], d["wdtype"]) if weighted and "b" in d else None
     if kind == "adaln":
         rpc = spec["rows_per_cond"]
         shape = (M // rpc, 1, H) if rpc > 1 else (1, M, H)
@@ -331,6 +341,8 @@ def setup_steps(spec, weighted, dev, per_step):
             tn.rmsnorm_fwd(s["x"], w, eps, out=s["y"])
         elif kind == "fwd_residual":
             tn.rmsnorm_fwd_residual(s["x"], s["r"], w, eps, out=s["y"], residual_out=s["ro"])
+        elif kind == "ln_residual":
+            tn.layernorm_fwd_residual(s["x"], s["r"], w, bias, eps, out=s["y"], residual_out=s["ro"])
         elif kind == "adaln":
             tn.rmsnorm_adaln_fwd(s["x"], w, s["scale"], s["shift"], eps, out=s["y"])
         elif kind == "bwd_residual":

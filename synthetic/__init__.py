@@ -21,7 +21,7 @@ Generator (a reading: the pages name no seeds and no generator), in _gen.c:
 
 Stream ids: x = 0, weight = 1, residual = 2, upstream gradient = 3,
 outlier mask = 4, outlier value = 5, AdaLN scale = 6, AdaLN shift = 7,
-RoPE angle = 8.
+RoPE angle = 8, LayerNorm bias = 9.
 """
 
 from __future__ import annotations
@@ -42,6 +42,7 @@ STREAM_OUTLIER_VALUE = 5
 STREAM_SCALE = 6
 STREAM_SHIFT = 7
 STREAM_ANGLE = 8
+STREAM_BIAS = 9
 
 # Storage formats, by name.  "bf16" arrays are returned as uint16 bit patterns.
 DTYPES = ("f32", "f16", "bf16")
@@ -186,6 +187,11 @@ WORKLOADS = {
     # head_dim 128 (32 heads of a 4096-wide model), tables in bfloat16
     "rope_bf16_2x4096x32x128": dict(kind="rope", B=2, S=4096, NH=32, D=128, dtype="bf16", tdtype="bf16",
                                     x=(0.0, 1.0), seed=1010),
+    # residual + LayerNorm of a pre-LayerNorm transformer in float32 at
+    # d_model 1024 (the width of the largest published rows), 16384 tokens
+    "ln_residual_f32_16384x1024": dict(kind="ln_residual", M=16384, H=1024, dtype="f32", wdtype="f32",
+                                       x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), b=(0.0, 0.1), eps=1e-5,
+                                       seed=1011),
     # DiT-style AdaLN on 2 x 4096 tokens of width 2048 (LTX-Video's hidden
     # size); scale/shift per batch ([B, 1, H]) and per token ([B, S, H])
     "adaln_bf16_2x4096x2048_batchcond": dict(kind="adaln", M=8192, H=2048, dtype="bf16", wdtype="bf16",
@@ -217,6 +223,8 @@ def make_inputs(name: str, rows: int | None = None) -> dict:
     out["w"] = encode(normal(seed, STREAM_W, H, *spec["w"]), wdt)
     if "r" in spec:
         out["r"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["r"]), dt).reshape(m, H)
+    if "b" in spec:
+        out["b"] = encode(normal(seed, STREAM_BIAS, H, *spec["b"]), wdt)
     if "dres" in spec:
         out["dres"] = encode(normal(seed, STREAM_RESIDUAL, n, *spec["dres"]), dt).reshape(m, H)
     if "dy" in spec:

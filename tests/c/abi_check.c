@@ -6,8 +6,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "layernorm.h"
 #include "rmsnorm.h"
 #include "rmsnorm_tuning.h"
+#include "rope.h"
 
 static int failures = 0;
 
@@ -130,6 +132,41 @@ int main(void) {
            RMSN_ERR_WORKSPACE);
     expect("bwd_residual M == 0", rmsnorm_bwd_residual(NULL, H, NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, NULL, 0,
                                                        0, H, RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
+
+    /* LayerNorm */
+    expect("ln eps 0", layernorm_fwd(x, H, w, r, y, H, NULL, NULL, M, H, 0.0f, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("ln bias f16 with x bf16", layernorm_fwd(x, H, NULL, r, y, H, NULL, NULL, M, H, 1e-5f, RMSN_BF16,
+                                                    RMSN_F16, 0), RMSN_ERR_UNSUPPORTED);
+    expect("ln mean overlaps x", layernorm_fwd(x, H, w, NULL, y, H, (float *)x, NULL, M, H, 1e-5f, RMSN_BF16,
+                                               RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("ln y overlaps bias", layernorm_fwd(x, H, w, (char *)y + 64, y, H, NULL, NULL, M, H, 1e-5f, RMSN_BF16,
+                                               RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("ln residual NULL", layernorm_fwd_residual(x, H, NULL, H, w, NULL, y, H, NULL, 0, NULL, NULL, M, H, 1e-5f,
+                                                      RMSN_F32, RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("ln M == 0", layernorm_fwd_residual(NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, H, NULL, NULL, 0, H,
+                                               1e-5f, RMSN_F32, RMSN_F32, 0), RMSN_OK);
+
+    /* RoPE: x [2, 8, 4, 64] */
+    const int64_t rs = 4 * 64;
+    expect("rope odd head_dim", rope_apply(x, rs, 64, w, r, 64, y, rs, 64, 2, 8, 4, 63, 0, RMSN_BF16, RMSN_F32, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("rope head stride < head_dim", rope_apply(x, rs, 32, w, r, 64, y, rs, 64, 2, 8, 4, 64, 0, RMSN_BF16,
+                                                     RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("rope row stride too small", rope_apply(x, 3 * 64, 64, w, r, 64, y, rs, 64, 2, 8, 4, 64, 0, RMSN_BF16,
+                                                   RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("rope table stride < head_dim/2", rope_apply(x, rs, 64, w, r, 16, y, rs, 64, 2, 8, 4, 64, 0, RMSN_BF16,
+                                                        RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("rope f16 tables for bf16 x", rope_apply(x, rs, 64, w, r, 64, y, rs, 64, 2, 8, 4, 64, 0, RMSN_BF16,
+                                                    RMSN_F16, 0), RMSN_ERR_UNSUPPORTED);
+    expect("rope out over the cos table", rope_apply(x, rs, 64, w, r, 64, (char *)w + 16, rs, 64, 2, 8, 4, 64, 0,
+                                                     RMSN_BF16, RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("rope out partially over x", rope_apply(x, rs, 64, w, r, 64, (char *)x + 32, rs, 64, 2, 8, 4, 64, 0,
+                                                   RMSN_BF16, RMSN_F32, 0), RMSN_ERR_INVALID_ARG);
+    expect("rope seq_len 0", rope_apply(x, rs, 64, w, r, 64, y, rs, 64, 2, 0, 4, 64, 0, RMSN_BF16, RMSN_F32, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("rope batch 0", rope_apply(NULL, rs, 64, NULL, NULL, 64, NULL, rs, 64, 0, 8, 4, 64, 0, RMSN_BF16,
+                                      RMSN_F32, 0), RMSN_OK);
 
     /* a geometry that cannot cover the row is rejected before the device */
     rmsnorm_tuning_set_geometry(0, 3, 1, 1, 0);

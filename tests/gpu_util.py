@@ -123,6 +123,43 @@ def bwd_residual_vs_oracle(dy, h, dres, w, rrms32, dh_host, dw_host, dtype, wdty
     return rep_dh, rep_dw
 
 
+def ln_vs_oracle(x, r, w, b, y_host, ro_host, mean_host, rstd_host, eps, dtype, wdtype=None, chunk=2048,
+                 name="layernorm"):
+    """Residual + LayerNorm against the oracle.  y = (h - mean) * rstd * w + b
+    cancels twice (h - mean, and the bias), so its ulp floor is taken at the
+    size of the terms, (|h| + |mean|) * rstd * |w| + |b|.  residual_out is
+    bit-exact; mean within 1e-5 of mean(|h|) (a float32 sum of the row) and
+    rstd within 1e-5 relative."""
+    M, H = x.shape
+    reps = {k: parity.Report(f"{name} {k}") for k in ("y", "residual_out", "mean", "rstd")}
+    wd = wdtype or dtype
+    for r0 in range(0, M, chunk):
+        r1 = min(M, r0 + chunk)
+        rr = None if r is None else r[r0:r1]
+        yref, href, mref, sref = oracle.layernorm(x[r0:r1], rr, w, b, eps32(eps), dtype, wdtype)
+        wv = np.ones(H) if w is None else oracle.decode(w, wd)
+        bv = np.zeros(H) if b is None else oracle.decode(b, wd)
+        terms = (np.abs(href) + np.abs(mref)[:, None]) * sref[:, None] * np.abs(wv)[None, :] + np.abs(bv)[None, :]
+        if dtype == "f32":
+            parity.check_dx_f32(reps["y"], y_host[r0:r1], yref, terms, r0 * H)
+        else:
+            parity.check_dx16(reps["y"], y_host[r0:r1], yref, terms, dtype, oracle.encode, oracle.decode, r0 * H)
+        if ro_host is not None:
+            hb = oracle.encode(href, dtype)
+            view = np.uint16 if dtype != "f32" else np.uint32
+            bad = ro_host[r0:r1].view(view) != hb.view(view)
+            reps["residual_out"].n += bad.size
+            reps["residual_out"].merge_bad(bad, r0 * H)
+        if mean_host is not None:
+            scale = np.abs(href).mean(axis=1)
+            bad = np.abs(mean_host[r0:r1].astype(np.float64) - mref) > 1e-5 * scale + 1e-30
+            reps["mean"].n += bad.size
+            reps["mean"].merge_bad(bad, r0)
+        if rstd_host is not None:
+            parity.check_f32(reps["rstd"], rstd_host[r0:r1], sref, r0)
+    return tuple(reps.values())
+
+
 def assert_ok(*reports):
     for r in reports:
         print(r, flush=True)

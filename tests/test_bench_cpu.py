@@ -40,6 +40,8 @@ def test_algorithmic_bytes_of_the_named_workloads():
     # RoPE: x and out, plus half of each float32 table row
     assert bench.algorithmic_bytes(spec("rope_bf16_2x8064x32x64"), True) == \
         2 * 2 * 8064 * 32 * 64 * 2 + 2 * 8064 * 32 * 4
+    # residual + LayerNorm: x, r read, y and residual_out written, w and b once
+    assert bench.algorithmic_bytes(spec("ln_residual_f32_16384x1024"), True) == 4 * 16384 * 1024 * 4 + 2 * 1024 * 4
     # a leading sample scales the row-proportional part only
     s = spec("fwd_bf16_8192x4096")
     assert bench.algorithmic_bytes(s, True, rows=1024) == 2 * 1024 * 4096 * 2 + 4096 * 2

@@ -1,0 +1,228 @@
+"""GPU parity of the LayerNorm forward (layernorm_fwd, layernorm_fwd_residual)
+against the float64 oracle.
+
+y is judged within 1 ulp of the oracle rounded to the output format, the ulp
+taken at no less than 2^-10 of the size of its terms ((|h| + |mean|) * rstd *
+|w| + |b|; float32: 1e-5 relative above a floor of 2^-4 of that size), since
+h - mean and the bias may cancel; residual_out is bit-exact; the per-row mean
+is within 1e-5 of the row's mean |h| and rstd within 1e-5 relative.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synthetic
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import transformer_normalization_amd as tn  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _default_geometry():
+    tn.set_geometry("fwd")
+    tn.set_streaming(-1)
+    yield
+    tn.set_geometry("fwd")
+    tn.set_streaming(-1)
+
+
+def bias_of(seed, H, dtype, std=0.1):
+    return synthetic.normal_tensor(seed, synthetic.STREAM_BIAS, (H,), dtype, 0.0, std)
+
+
+def run_ln(x, r, w, b, eps, dtype, wdtype=None):
+    wd = wdtype or dtype
+    xd = G.to_dev(x, dtype)
+    wt = None if w is None else G.to_dev(w, wd)
+    bt = None if b is None else G.to_dev(b, wd)
+    if r is None:
+        y, mean, rstd = tn.layernorm_fwd(xd, wt, bt, eps, return_stats=True)
+        ro = None
+    else:
+        y, ro, mean, rstd = tn.layernorm_fwd_residual(xd, G.to_dev(r, dtype), wt, bt, eps, return_stats=True)
+    torch.cuda.synchronize()
+    return (G.to_host(y, dtype), None if ro is None else G.to_host(ro, dtype), mean.cpu().numpy(),
+            rstd.cpu().numpy())
+
+
+def check(x, r, w, b, eps, dtype, wdtype=None, name="ln"):
+    y, ro, mean, rstd = run_ln(x, r, w, b, eps, dtype, wdtype)
+    G.assert_ok(*G.ln_vs_oracle(x, r, w, b, y, ro, mean, rstd, eps, dtype, wdtype, name=name))
+    return y, ro
+
+
+def test_workload_ln_residual():
+    name = "ln_residual_f32_16384x1024"
+    d = synthetic.make_inputs(name)
+    print(f"[gpu] {name}", flush=True)
+    check(d["x"], d["r"], d["w"], d["b"], d["eps"], d["dtype"], d["wdtype"], name=name)
+
+
+LN_H = [1, 3, 8, 64, 65, 512, 1000, 1024, 2049, 4096, 8191, 12288, 16385, 65536]
+
+
+@pytest.mark.parametrize("resid", [True, False], ids=["residual", "plain"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("H", LN_H)
+def test_ln_shapes(H, dtype, resid):
+    M = 257 if H <= 8192 else 5
+    print(f"[gpu] ln {dtype} M={M} H={H} resid={resid}", flush=True)
+    d = G.inputs(4000 + H, M, H, dtype, residual=resid)
+    b = bias_of(4000 + H, H, dtype)
+    check(d["x"], d.get("r"), d["w"], b, 1e-5, dtype, name=f"ln {dtype} H={H}")
+
+
+@pytest.mark.parametrize("affine", ["none", "weight", "bias", "f32params"])
+def test_ln_optional_weight_and_bias(affine):
+    M, H = 300, 2048
+    d = G.inputs(41, M, H, "bf16", residual=True)
+    w, b, wd = d["w"], bias_of(41, H, "bf16"), None
+    if affine == "none":
+        w = b = None
+    elif affine == "weight":
+        b = None
+    elif affine == "bias":
+        w = None
+    else:
+        wd = "f32"
+        w = synthetic.normal_tensor(41, synthetic.STREAM_W, (H,), "f32", 1.0, 0.1)
+        b = bias_of(41, H, "f32")
+    check(d["x"], d["r"], w, b, 1e-5, "bf16", wd, name=f"ln affine {affine}")
+
+
+def test_ln_large_mean_offset():
+    """Rows whose mean is far larger than their spread: the centred second
+    reduction keeps the variance accurate."""
+    M, H = 256, 1024
+    x = synthetic.normal_tensor(42, synthetic.STREAM_X, (M, H), "f32", 100.0, 1.0)
+    y, _ = check(x, None, None, None, 1e-5, "f32", name="ln offset 100")
+    # the output has unit spread, not the offset's
+    assert abs(float(np.std(y)) - 1.0) < 1e-3
+
+
+def test_ln_constant_rows_give_the_bias():
+    M, H = 64, 1024
+    x = np.full((M, H), 0.75, dtype=np.float32)
+    w = synthetic.normal_tensor(43, synthetic.STREAM_W, (H,), "f32", 1.0, 0.1)
+    b = bias_of(43, H, "f32")
+    y, _, mean, rstd = run_ln(x, None, w, b, 1e-5, "f32")
+    assert np.array_equal(y, np.tile(b, (M, 1)))
+    assert np.all(mean == 0.75)
+
+
+# (vpt, wpr, rpw, grid): row tiles (exact, and with idle slots), several rows
+# per workgroup, and capped grids walking the rows grid-stride (long rows'
+# three-pass path is reached by the H = 65536 shapes)
+LN_GEOMS = [(1, 4, 1, 0), (2, 2, 2, 0), (4, 1, 4, 0), (2, 2, 1, 7), (4, 1, 1, 0), (8, 1, 1, 0), (4, 2, 2, 5)]
+
+
+@pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
+@pytest.mark.parametrize("geom", LN_GEOMS, ids=[str(g) for g in LN_GEOMS])
+def test_ln_forced_geometry(geom, stream):
+    M, H = 300, 2048
+    d = G.inputs(44, M, H, "bf16", residual=True)
+    b = bias_of(44, H, "bf16")
+    tn.set_geometry("fwd", *geom)
+    tn.set_streaming(stream)
+    check(d["x"], d["r"], d["w"], b, 1e-5, "bf16", name=f"ln geom {geom}")
+
+
+def test_ln_streaming_and_determinism():
+    d = G.inputs(45, 1000, 4096, "bf16", residual=True)
+    b = bias_of(45, 4096, "bf16")
+    runs = []
+    for mode in (0, 1, -1, -1):
+        tn.set_streaming(mode)
+        runs.append(run_ln(d["x"], d["r"], d["w"], b, 1e-5, "bf16"))
+    for r in runs[1:]:
+        for a, c in zip(runs[0], r):
+            assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_misaligned_and_strided_rows(dtype):
+    """Odd H, and a residual one element into its buffer, take single
+    elements (another reduction order: within tolerance of the oracle);
+    row strides padded by whole 16-byte vectors give the same bits as
+    contiguous rows."""
+    M, H = 129, 1023
+    d = G.inputs(46, M, H, dtype, residual=True)
+    b = bias_of(46, H, dtype)
+    check(d["x"], d["r"], d["w"], b, 1e-5, dtype, name=f"ln odd H {dtype}")
+    H = 1024
+    d = G.inputs(47, M, H, dtype, residual=True)
+    b = bias_of(47, H, dtype)
+    ref = run_ln(d["x"], d["r"], d["w"], b, 1e-5, dtype)
+    td = G.torch_dtype(dtype)
+    wt, bt = G.to_dev(d["w"], dtype), G.to_dev(b, dtype)
+    xb = torch.zeros((M, H + 8), dtype=td, device=G.DEV)
+    xb[:, :H] = G.to_dev(d["x"], dtype)
+    rb = torch.zeros((M, H + 16), dtype=td, device=G.DEV)
+    rb[:, :H] = G.to_dev(d["r"], dtype)
+    y, ro = tn.layernorm_fwd_residual(xb[:, :H], rb[:, :H], wt, bt, 1e-5)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.to_host(y, dtype), ref[0]) and np.array_equal(G.to_host(ro, dtype), ref[1])
+    flat = torch.zeros(M * H + 1, dtype=td, device=G.DEV)
+    rv = flat[1:].view(M, H)
+    rv.copy_(G.to_dev(d["r"], dtype))
+    y, ro, mean, rstd = tn.layernorm_fwd_residual(xb[:, :H], rv, wt, bt, 1e-5, return_stats=True)
+    torch.cuda.synchronize()
+    G.assert_ok(*G.ln_vs_oracle(d["x"], d["r"], d["w"], b, G.to_host(y, dtype), G.to_host(ro, dtype),
+                                mean.cpu().numpy(), rstd.cpu().numpy(), 1e-5, dtype, name=f"ln misaligned {dtype}"))
+
+
+@pytest.mark.parametrize("H", [4096, 65536])
+def test_ln_in_place(H):
+    M = 64 if H <= 8192 else 4
+    d = G.inputs(48, M, H, "bf16", residual=True)
+    b = bias_of(48, H, "bf16")
+    ref = run_ln(d["x"], d["r"], d["w"], b, 1e-5, "bf16")
+    x, r = G.to_dev(d["x"], "bf16"), G.to_dev(d["r"], "bf16")
+    w, bt = G.to_dev(d["w"], "bf16"), G.to_dev(b, "bf16")
+    # y over x, residual_out over residual: the usual in-place update
+    y, ro = tn.layernorm_fwd_residual(x, r, w, bt, 1e-5, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr() and ro.data_ptr() == r.data_ptr()
+    assert np.array_equal(G.to_host(x, "bf16"), ref[0]) and np.array_equal(G.to_host(r, "bf16"), ref[1])
+
+
+def test_ln_rejects_bad_arguments():
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=G.DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=G.DEV)
+    with pytest.raises(tn.RMSNormError):
+        tn.layernorm_fwd(x, w, None, 0.0)  # eps must be positive
+    with pytest.raises(tn.RMSNormError):
+        tn.layernorm_fwd(x, w.half(), None, 1e-5)  # float16 parameters for bfloat16 x
+    with pytest.raises(ValueError):
+        tn.layernorm_fwd(x, w, w.float(), 1e-5)  # weight and bias formats differ
+    buf = torch.zeros(4 * 64 + 8, dtype=torch.bfloat16, device=G.DEV)
+    with pytest.raises(tn.RMSNormError):
+        tn.layernorm_fwd(buf[:256].view(4, 64), w, None, 1e-5, out=buf[8:264].view(4, 64))
+
+
+def test_ln_empty_batch():
+    x = torch.empty((0, 512), dtype=torch.float32, device=G.DEV)
+    y = tn.layernorm_fwd(x, None, None, 1e-5)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512)
+
+
+def test_ln_guard_regions_untouched():
+    M, H = 33, 1000
+    d = G.inputs(49, M, H, "f32", residual=True)
+    n = M * H
+    yb = torch.full((n + 128,), 7.0, dtype=torch.float32, device=G.DEV)
+    rb = torch.full((n + 128,), 7.0, dtype=torch.float32, device=G.DEV)
+    tn.layernorm_fwd_residual(G.to_dev(d["x"], "f32"), G.to_dev(d["r"], "f32"), G.to_dev(d["w"], "f32"), None, 1e-5,
+                              out=yb[64:64 + n].view(M, H), residual_out=rb[64:64 + n].view(M, H))
+    torch.cuda.synchronize()
+    for t in (yb, rb):
+        assert torch.all(t[:64] == 7.0) and torch.all(t[64 + n:] == 7.0)

@@ -13,6 +13,7 @@ functions raise.
     dx, dw = rmsnorm_bwd(dy, x, w, rrms)
     dh, dw = rmsnorm_bwd_residual(dy, res_out, dres, w, rrms)  # grad of x and residual
     q = rope_apply(q, cos, sin)                      # q [B, S, heads, head_dim], cos/sin [S, head_dim]
+    y, h = layernorm_fwd_residual(x, residual, w, b, eps)   # residual + LayerNorm
 
 transformer_normalization_amd.autograd wraps these as torch.autograd
 Functions and nn.Modules for training.
@@ -31,7 +32,8 @@ RMSN_F32, RMSN_F16, RMSN_BF16 = 0, 1, 2
 STATUS = {0: "RMSN_OK", 1: "RMSN_ERR_INVALID_ARG", 2: "RMSN_ERR_UNSUPPORTED", 3: "RMSN_ERR_WORKSPACE",
           4: "RMSN_ERR_HIP"}
 EXPORTED = ("rmsnorm_fwd", "rmsnorm_fwd_residual", "rmsnorm_adaln_fwd", "rmsnorm_bwd_workspace_bytes",
-            "rmsnorm_bwd", "rmsnorm_bwd_residual", "rmsnorm_status_string", "rmsnorm_last_error", "rope_apply")
+            "rmsnorm_bwd", "rmsnorm_bwd_residual", "rmsnorm_status_string", "rmsnorm_last_error", "rope_apply",
+            "layernorm_fwd", "layernorm_fwd_residual")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +65,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_bwd_workspace_bytes.argtypes = [i64, i64]
         lib.rmsnorm_bwd_workspace_bytes.restype = sz
         lib.rmsnorm_bwd.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32, i32, vp]
+        lib.layernorm_fwd.restype = i32
+        lib.layernorm_fwd.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, i64, f32, i32, i32, vp]
+        lib.layernorm_fwd_residual.restype = i32
+        lib.layernorm_fwd_residual.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, i64, i64, f32, i32,
+                                               i32, vp]
         lib.rope_apply.restype = i32
         lib.rope_apply.argtypes = [vp, i64, i64, vp, vp, i64, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.rmsnorm_bwd_residual.restype = i32
@@ -310,6 +317,80 @@ def rmsnorm_bwd_residual(dy, residual_out, dres, weight, rrms, dh=None, dw=None,
     dh = norm backward through h + dres is the gradient of both x and the
     residual input.  dh may be dy, residual_out or dres itself."""
     return _bwd(dy, residual_out, dres, weight, rrms, dh, dw, workspace, want_dw)
+
+
+def _params(x, weight, bias, H):
+    """w_dtype code for an optional weight and bias (one format, x's or float32)."""
+    ref = weight if weight is not None else bias
+    for name, t in (("weight", weight), ("bias", bias)):
+        if t is not None and (t.numel() != H or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor of H elements")
+    if weight is not None and bias is not None and weight.dtype != bias.dtype:
+        raise ValueError("weight and bias must share one dtype")
+    return _dtype_code(ref) if ref is not None else _dtype_code(x)
+
+
+def _stats(x, M, given, want):
+    torch = _torch()
+    if want and given is None:
+        given = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if given is not None and (given.dtype != torch.float32 or given.numel() != M or not given.is_contiguous()):
+        raise ValueError("mean and rstd must be contiguous float32 tensors with one value per row")
+    return given
+
+
+def layernorm_fwd(x, weight=None, bias=None, eps: float = 1e-5, out=None, mean=None, rstd=None,
+                  return_stats: bool = False):
+    """LayerNorm over the last dim: (x - mean) / sqrt(var + eps) * weight + bias
+    (population variance; weight and bias optional).  Returns y, or
+    (y, mean, rstd) with return_stats."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _, _, ys = _rows(out, "out")
+    mean, rstd = _stats(x, M, mean, return_stats), _stats(x, M, rstd, return_stats)
+    wcode = _params(x, weight, bias, H)
+    st = lib.layernorm_fwd(_ptr(x), xs, _ptr(weight), _ptr(bias), _ptr(out), ys, _ptr(mean), _ptr(rstd), M, H,
+                           float(eps), _dtype_code(x), wcode, _stream(x))
+    _check(lib, st)
+    return (out, mean, rstd) if return_stats else out
+
+
+def layernorm_fwd_residual(x, residual, weight=None, bias=None, eps: float = 1e-5, out=None, residual_out=None,
+                           mean=None, rstd=None, return_stats: bool = False, write_residual: bool = True):
+    """h = x + residual (float32; written to residual_out in x's dtype) and
+    y = LayerNorm(h) of the unrounded sum.  Returns (y, residual_out), plus
+    (mean, rstd) with return_stats.  residual_out may be `residual` itself."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if residual.shape != x.shape or residual.dtype != x.dtype:
+        raise ValueError("residual must match x in shape and dtype")
+    _, _, rs = _rows(residual, "residual")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _, _, ys = _rows(out, "out")
+    if write_residual and residual_out is None:
+        residual_out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    ros = 0
+    if residual_out is not None:
+        if residual_out.shape != x.shape or residual_out.dtype != x.dtype:
+            raise ValueError("residual_out must match x in shape and dtype")
+        _, _, ros = _rows(residual_out, "residual_out")
+    mean, rstd = _stats(x, M, mean, return_stats), _stats(x, M, rstd, return_stats)
+    wcode = _params(x, weight, bias, H)
+    st = lib.layernorm_fwd_residual(_ptr(x), xs, _ptr(residual), rs, _ptr(weight), _ptr(bias), _ptr(out), ys,
+                                    _ptr(residual_out), ros, _ptr(mean), _ptr(rstd), M, H, float(eps),
+                                    _dtype_code(x), wcode, _stream(x))
+    _check(lib, st)
+    res = (out, residual_out)
+    return res + (mean, rstd) if return_stats else res
 
 
 def _heads_view(t, name):

@@ -105,12 +105,12 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     p.tpw = kRopeThreads / p.ipw;
     p.sign = transpose ? -1.0f : 1.0f;
     p.nblocks = (S + p.tpw - 1) / p.tpw;
-    int64_t gx = p.nblocks;
-    if (ov.set && ov.d > 0 && ov.d < gx) gx = ov.d;
-    if (gx > INT32_MAX) gx = INT32_MAX;  // the position blocks are walked grid-stride
-    const int64_t gy = (p.items + p.ipw - 1) / p.ipw;
+    p.iblocks = (p.items + p.ipw - 1) / p.ipw;
+    int64_t grid = p.nblocks * p.iblocks;
+    if (ov.set && ov.d > 0 && ov.d < grid) grid = ov.d;
+    if (grid > INT32_MAX) grid = INT32_MAX;  // the work is walked grid-stride
     void *args[] = {&p};
-    return launch((const void *)fn, dim3((unsigned)gx, (unsigned)gy), dim3(kRopeThreads), args, stream, "rope_apply");
+    return launch((const void *)fn, dim3((unsigned)grid), dim3(kRopeThreads), args, stream, "rope_apply");
 }
 
 }  // namespace

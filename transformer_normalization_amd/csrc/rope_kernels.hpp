@@ -18,9 +18,12 @@
 //    elements j.. of the first half and the matching elements of the second
 //    half (two accesses head_dim/2 apart).
 //
-// Mapping: a workgroup of 256 threads covers `tpw` positions x `ipw` items;
-// blockIdx.y selects the block of items when one position has more than 256.
-// Position blocks are walked grid-stride, so a capped grid also works.
+// Mapping: a workgroup of 256 threads covers `tpw` positions x `ipw` items.
+// When one position has more than 256 items it takes `iblocks` consecutive
+// workgroups, so neighbouring workgroups cover neighbouring bytes of a token
+// row (a position-major order would leave strided holes in each row).  The
+// (position block, item block) pairs are walked grid-stride, so a capped
+// grid also works.
 #pragma once
 
 #include "numerics.hpp"
@@ -43,6 +46,7 @@ struct RopeParams {
     int ipw;           // items per workgroup row (<= 256)
     int tpw;           // positions per workgroup
     int64_t nblocks;   // position blocks: ceil(S / tpw)
+    int iblocks;       // item blocks per position block: ceil(items / ipw)
     float sign;        // +1, or -1 for the transposed rotation
 };
 
@@ -71,23 +75,27 @@ template <int XDT, int TDT, int VEC, bool NT, bool XCHG>
 __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopeParams p) {
     const int t = threadIdx.x;
     const int lt = t / p.ipw;
-    const int item = blockIdx.y * p.ipw + (t - lt * p.ipw);
-    // partners (exchange layout) share lt and both pass or both fail here
-    if (lt >= p.tpw || item >= p.items) return;
+    const int it = t - lt * p.ipw;
+    if (lt >= p.tpw) return;
     const int64_t xstep = p.S * p.xrs;  // one batch further
     const int64_t ostep = p.S * p.ors;
+    const int64_t nwork = p.nblocks * p.iblocks;
 
     if constexpr (XCHG) {
         static_assert(VEC > 1, "the exchange layout moves 16-byte vectors");
         const int per_head = 2 * p.nvec;
-        const int h = item / per_head;
-        const int k = item - h * per_head;  // == t % per_head: heads are aligned to per_head lanes
-        const bool upper = k >= p.nvec;
-        const int col = (upper ? k - p.nvec : k) * VEC;  // table column
-        const int partner = ((t & 63) ^ p.nvec) << 2;   // ds_bpermute byte address
-        for (int64_t pb = blockIdx.x; pb < p.nblocks; pb += gridDim.x) {
+        const int partner = ((t & 63) ^ p.nvec) << 2;  // ds_bpermute byte address
+        for (int64_t wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
+            const int64_t pb = wk / p.iblocks;
+            const int item = (int)(wk - pb * p.iblocks) * p.ipw + it;
             const int64_t s = pb * p.tpw + lt;
-            if (s >= p.S) break;
+            // partners share the position and the item block: both go on or
+            // both skip (items is a multiple of per_head)
+            if (s >= p.S || item >= p.items) continue;
+            const int h = item / per_head;
+            const int k = item - h * per_head;  // == t % per_head: heads are aligned to per_head lanes
+            const bool upper = k >= p.nvec;
+            const int col = (upper ? k - p.nvec : k) * VEC;  // table column
             float c[VEC], sn[VEC];
             load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
             load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
@@ -120,11 +128,13 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             }
         }
     } else {
-        const int h = item / p.nvec;
-        const int col = (item - h * p.nvec) * VEC;
-        for (int64_t pb = blockIdx.x; pb < p.nblocks; pb += gridDim.x) {
+        for (int64_t wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
+            const int64_t pb = wk / p.iblocks;
+            const int item = (int)(wk - pb * p.iblocks) * p.ipw + it;
             const int64_t s = pb * p.tpw + lt;
-            if (s >= p.S) break;
+            if (s >= p.S || item >= p.items) continue;
+            const int h = item / p.nvec;
+            const int col = (item - h * p.nvec) * VEC;
             float c[VEC], sn[VEC];
             load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
             load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);

@@ -83,9 +83,6 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     const bool nt = use_streaming(2 * rows * NH * D * eb);
     rope_fn fn = rope_lookup(xdt, tdt, vec, nt, xchg);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no RoPE kernel for vec %d", vec);
-    int cus = 0;
-    if ((st = device_info(&cus)) != RMSN_OK) return st;
-
     RopeParams p;
     p.x = x;
     p.cos = cos_t;
@@ -106,9 +103,12 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     p.sign = transpose ? -1.0f : 1.0f;
     p.nblocks = (S + p.tpw - 1) / p.tpw;
     p.iblocks = (p.items + p.ipw - 1) / p.ipw;
+    if (p.nblocks > INT64_MAX / p.iblocks) return fail(RMSN_ERR_UNSUPPORTED, "seq_len = %lld is too large", (long long)S);
     int64_t grid = p.nblocks * p.iblocks;
     if (ov.set && ov.d > 0 && ov.d < grid) grid = ov.d;
     if (grid > INT32_MAX) grid = INT32_MAX;  // the work is walked grid-stride
+    int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
+    if ((st = device_info(&cus)) != RMSN_OK) return st;
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)grid), dim3(kRopeThreads), args, stream, "rope_apply");
 }

@@ -77,3 +77,17 @@ def test_graph_replays_match_eager():
         got.update(rr=_bits(rr), rr2=_bits(rr2), dw=_bits(dw), dw2=_bits(dw2))
         for k in want:
             assert torch.equal(got[k], want[k]), f"replay {rep}: {k}"
+
+
+def test_calls_run_on_the_current_stream():
+    """The binding hands the library the current stream of the tensor's
+    device, also inside `with torch.cuda.stream(...)`."""
+    x = torch.ones((64, 512), dtype=torch.bfloat16, device=G.DEV)
+    # (ctypes shows the null stream, handle 0, as None)
+    assert (tn._stream(x).value or 0) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream(G.DEV)
+    with torch.cuda.stream(side):
+        assert (tn._stream(x).value or 0) == side.cuda_stream
+        y = tn.rmsnorm_fwd(x, None, 1e-6)
+    side.synchronize()
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))  # rows of ones normalise to ones

@@ -49,6 +49,9 @@ class RMSNormError(RuntimeError):
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load librmsnorm.so (raises if it has not been built)."""
     global _lib
+    lib = _lib
+    if lib is not None and path == LIB_PATH:  # loaded: no lock on the per-call path
+        return lib
     with _lock:
         if _lib is not None and path == LIB_PATH:
             return _lib
@@ -99,16 +102,26 @@ def _torch():
     return torch
 
 
+_CODES = None
+
+
 def _dtype_code(t) -> int:
-    torch = _torch()
-    m = {torch.float32: RMSN_F32, torch.float16: RMSN_F16, torch.bfloat16: RMSN_BF16}
-    if t.dtype not in m:
+    global _CODES
+    if _CODES is None:
+        torch = _torch()
+        _CODES = {torch.float32: RMSN_F32, torch.float16: RMSN_F16, torch.bfloat16: RMSN_BF16}
+    code = _CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
-    return m[t.dtype]
+    return code
 
 
 def _rows(t, name):
     """(M, H, row stride) of a tensor viewed as rows over its last dim."""
+    if t.is_cuda and t.is_contiguous() and t.dim() >= 1:  # the common case, in a few calls
+        H = t.shape[-1]
+        n = t.numel()
+        return (n // H if H else 0), H, max(H, 1)
     if t.dim() < 1:
         raise ValueError(f"{name} must have at least one dimension")
     if not t.is_cuda:
@@ -137,7 +150,11 @@ def _rows(t, name):
 
 
 def _stream(t):
+    """The raw handle of the current HIP stream of t's device."""
     torch = _torch()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:  # the handle without building a Stream object
+        return ctypes.c_void_p(raw(t.device.index if t.device.index is not None else torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 

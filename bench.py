@@ -20,6 +20,10 @@ Workloads (default: the forward at bf16 M=8192 H=4096):
 that host launch overhead cannot leave the GPU idle between short kernels;
 the kernels and their arguments are the same as in eager launches.
 
+copy_ceiling times rmsnorm_tuning_copy moving the same bytes per step (half
+read, half written) with the kernels' access pattern and no arithmetic: the
+practical HBM ceiling of a transfer of that size, beside the 8 TB/s peak.
+
 The CPU baseline is the float64 oracle run on the host over a sample of the
 same workload (reported beside the GPU figure, never a target).
 """
@@ -257,7 +261,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
         f"# HBM traffic per launch of {kname}",
         f"# workload {workload}: {shape} {spec['dtype']}",
         "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs of",
-        f"#   python3 bench.py --workload {workload} --cpu-seconds 0 --steps 20 --warmup 10 --copy-reference",
+        f"#   python3 bench.py --workload {workload} --cpu-seconds 0 --no-ceiling --steps 20 --warmup 10 --copy-reference",
         "# each scaled by the same counter's reading for device copies of the x tensor",
         f"# ({known_kib:.0f} KiB read and written per copy) in the same run; summary made by",
         f"#   python3 bench.py --workload {workload} --summarize-pmc <fetch csv> <write csv>",
@@ -352,6 +356,36 @@ def setup_steps(spec, weighted, dev, per_step):
     return step, nsets, copy_src, copy_dst
 
 
+def copy_ceiling(per_step, dev, steps):
+    """The speed-of-light reference: rmsnorm_tuning_copy moving per_step
+    bytes (half read, half written) with the forward kernels' access pattern
+    and no arithmetic, over buffers rotated like the steps', timed the same
+    way."""
+    import torch
+
+    import transformer_normalization_amd as tn
+
+    half = max(16, (per_step // 2) // 16 * 16)
+    nsets = max(2, -(-ROTATION_BYTES // (2 * half)))
+    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nsets)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    for i in range(50):
+        tn.copy_reference(src[i % nsets], dst[i % nsets])
+    stream = torch.cuda.current_stream(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        tn.copy_reference(src[i % nsets], dst[i % nsets])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    gbs = 2 * half / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(ms, 6), "bytes": 2 * half,
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "kind": "16-byte non-temporal copy, 256-thread workgroups of 8 KiB (rmsnorm_tuning_copy)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +395,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0 skips it)")
     ap.add_argument("--graph", action="store_true", help="launch the timed steps from captured HIP graphs")
     ap.add_argument("--geom", default="", help="development: forced launch geometry 'vpt,wpr,rpw,grid'")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip timing the speed-of-light copy of the same bytes")
     ap.add_argument("--copy-reference", action="store_true",
                     help="also run a plain device copy of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -482,6 +518,9 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_ceiling:
+        result["copy_ceiling"] = copy_ceiling(per_step, dev, min(args.steps, 1000))
+        result["copy_ceiling"]["step_over_copy"] = round(gbs / result["copy_ceiling"]["value"], 4)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(spec, weighted, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -13,6 +13,8 @@
 
 #include <stdint.h>
 
+#include "rmsnorm.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -47,6 +49,17 @@ void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t
  * > 0 always.  Results are identical either way.
  */
 void rmsnorm_tuning_set_streaming(int mode);
+
+/*
+ * Speed-of-light reference for measurements: copies `bytes` from src to dst
+ * (device pointers, 16-byte aligned, bytes a multiple of 16, the two ranges
+ * disjoint) with the forward kernels' access pattern -- 256-thread
+ * workgroups, two 16-byte vectors per thread, non-temporal loads and stores
+ * -- and no arithmetic, so that a kernel's HBM rate can be compared with the
+ * rate of moving the same bytes in the same way.  Enqueued on `stream`;
+ * returns RMSN_ERR_INVALID_ARG for a bad argument.
+ */
+rmsn_status_t rmsnorm_tuning_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

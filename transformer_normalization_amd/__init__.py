@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.layernorm_fwd_residual.restype = i32
         lib.layernorm_fwd_residual.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, i64, vp, vp, i64, i64, f32, i32,
                                                i32, vp]
+        lib.rmsnorm_tuning_copy.restype = i32
+        lib.rmsnorm_tuning_copy.argtypes = [vp, vp, i64, vp]
         lib.rope_apply.restype = i32
         lib.rope_apply.argtypes = [vp, i64, i64, vp, vp, i64, vp, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.rmsnorm_bwd_residual.restype = i32
@@ -466,6 +468,20 @@ def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: i
     library's own choice."""
     code = {"fwd": 0, "bwd": 1, "rope": 2}[which]
     load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))
+
+
+def copy_reference(src, dst) -> None:
+    """Development hook (include/rmsnorm_tuning.h): copy src into dst (same
+    byte size, both contiguous device tensors) with the forward kernels'
+    access pattern and no arithmetic -- the speed-of-light reference for a
+    transfer of that size."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous tensors of the same byte size")
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("src and dst must be device tensors")
+    _check(lib, lib.rmsnorm_tuning_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
 
 
 def set_streaming(mode: int = -1) -> None:

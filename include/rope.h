@@ -21,12 +21,13 @@
  * (sn = -sin[s, j] when transpose != 0), in float32:
  *
  *   out[r, h, j]              = x0 * c - x1 * sn
- *   out[r, h, j + head_dim/2] = x0 * sn + x1 * c
+ *   out[r, h, j + head_dim/2] = x1 * c + x0 * sn
  *
- * each rounded once to x_dtype (nearest even); the first product of each line
- * is fused with the sum (one fma).  Only the first head_dim/2 columns of a
- * table row are read: the rotate-half layout repeats the same angles in both
- * halves, so [seq_len, head_dim/2] tables work too.  The transposed rotation
+ * each rounded once to x_dtype (nearest even); the product with c is fused
+ * with the sum (one fma each: fma(x0, c, x1 * -sn) and fma(x1, c, x0 * sn)).
+ * Only the first head_dim/2 columns of a table row are read: the rotate-half
+ * layout repeats the same angles in both halves, so [seq_len, head_dim/2]
+ * tables work too.  The transposed rotation
  * is the inverse rotation and the gradient of the rotation with respect to x.
  */
 #ifndef ROPE_H

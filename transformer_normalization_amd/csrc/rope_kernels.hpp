@@ -52,12 +52,14 @@ struct RopeParams {
 
 constexpr int kRopeThreads = 256;
 
-// out0 = x0 c - x1 s and out1 = x0 s + x1 c, the first product fused
+// out0 = x0 c - x1 s and out1 = x1 c + x0 s: each output is
+// fma(own, c, partner * s') with s' = -s for the first half and +s for the
+// second, so both halves (and both layouts) evaluate the same expression
 __device__ __forceinline__ float rot_lo(float x0, float x1, float c, float sn) {
-    return __builtin_fmaf(x0, c, -(x1 * sn));
+    return __builtin_fmaf(x0, c, x1 * -sn);
 }
 __device__ __forceinline__ float rot_hi(float x0, float x1, float c, float sn) {
-    return __builtin_fmaf(x0, sn, x1 * c);
+    return __builtin_fmaf(x1, c, x0 * sn);
 }
 
 template <int DT, int N>
@@ -99,19 +101,36 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             float c[VEC], sn[VEC];
             load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
             load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
+            // s' = +-s: the transposed rotation negates s, the first half
+            // of a head negates it again (exact)
+            const float sg = upper ? p.sign : -p.sign;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) sn[e] *= p.sign;  // exact
+            for (int e = 0; e < VEC; ++e) sn[e] *= sg;
             const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
             const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + k * VEC;
+            // one packed 32-bit word at a time keeps few values live
+            // (the kernel stays within 64 VGPRs: 8 waves per SIMD)
             auto finish = [&](const Raw<XDT, VEC> &mine, int64_t o) {
                 const Raw<XDT, VEC> theirs = from_lane(mine, partner);
-                float a[VEC], b[VEC], out[VEC];
-                mine.widen_to(a);
-                theirs.widen_to(b);
+                constexpr int PW = 4 / Fmt<XDT>::bytes;  // elements per word
+                u32x4 res;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    out[e] = upper ? rot_hi(b[e], a[e], c[e], sn[e]) : rot_lo(a[e], b[e], c[e], sn[e]);
-                store_elems<XDT, VEC, NT>(p.out, o, out);
+                for (int w = 0; w < 4; ++w) {
+                    float a[PW], b[PW], out[PW];
+                    unpack_word<XDT>(mine.v[0][w], a);
+                    unpack_word<XDT>(theirs.v[0][w], b);
+#pragma unroll
+                    for (int e = 0; e < PW; ++e) {
+                        const int j = w * PW + e;
+                        out[e] = __builtin_fmaf(a[e], c[j], b[e] * sn[j]);  // rot_lo / rot_hi of this half
+                    }
+                    res[w] = pack_word<XDT>(out);
+                }
+                u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<char *>(p.out) + o * Fmt<XDT>::bytes);
+                if constexpr (NT)
+                    __builtin_nontemporal_store(res, dst);
+                else
+                    *dst = res;
             };
             int64_t b = 0;
             for (; b + 1 < p.B; b += 2) {

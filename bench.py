@@ -215,12 +215,19 @@ def cpu_baseline(spec, weighted, seconds):
         if el >= seconds:
             break
     nbytes = algorithmic_bytes(spec, weighted, n) * passes
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {
         "value": round(nbytes / el / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"{sample}, {passes} passes in {el:.1f} s, float64, one thread",
+        "cpu": f"{cpu} ({os.cpu_count()} logical CPUs visible)",
         "rows_per_s": round(rows * passes / el, 1),
     }
 

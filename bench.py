@@ -401,7 +401,8 @@ def main():
     ap.add_argument("--workload", default="fwd_bf16_8192x4096", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0 skips it)")
     ap.add_argument("--graph", action="store_true", help="launch the timed steps from captured HIP graphs")
-    ap.add_argument("--geom", default="", help="development: forced launch geometry 'vpt,wpr,rpw,grid'")
+    ap.add_argument("--geom", default="",
+                    help="development: forced launch geometry, four integers as rmsnorm_tuning_set_geometry takes")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip timing the speed-of-light copy of the same bytes")
     ap.add_argument("--copy-reference", action="store_true",
@@ -441,7 +442,7 @@ def main():
     kind = spec["kind"]
     if args.geom:
         parts = [int(v) for v in args.geom.split(",")]
-        tn.set_geometry("bwd" if kind.startswith("bwd") else "fwd", *parts)
+        tn.set_geometry("bwd" if kind.startswith("bwd") else "rope" if kind == "rope" else "fwd", *parts)
 
     dev = torch.device("cuda:0")
     per_step = algorithmic_bytes(spec, weighted)

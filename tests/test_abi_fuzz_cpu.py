@@ -22,7 +22,6 @@ hypothesis = pytest.importorskip("hypothesis")
 from hypothesis import given, settings  # noqa: E402
 from hypothesis import strategies as st  # noqa: E402
 
-import transformer_normalization_amd as tn  # noqa: E402
 from tests.test_abi_cpu import _lib, _no_device_visible  # noqa: E402
 
 pytestmark = pytest.mark.skipif(not _no_device_visible(), reason="runs only where no GPU is visible")
@@ -35,10 +34,6 @@ BASES = [(k + 1) << 52 for k in range(8)]
 
 dtypes = st.sampled_from([0, 1, 2, 3, -1])
 eps_values = st.sampled_from([1e-5, 1e-6, 1.0, 0.0, -1e-5, float("nan"), float("inf")])
-
-
-def esize(dt):
-    return 4 if dt == 0 else 2
 
 
 @settings(max_examples=400, deadline=None)

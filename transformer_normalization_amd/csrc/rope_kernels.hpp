@@ -83,6 +83,11 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
     const int64_t ostep = p.S * p.ors;
     const int64_t nwork = p.nblocks * p.iblocks;
 
+    // Batches are taken two at a time.  The rows of a pair are requested
+    // before the table entries of the position, so the latency of the table
+    // loads overlaps that of the rows instead of adding to it (the tables are
+    // needed first, but a wait for them would otherwise hold back every row
+    // load behind it).  `two` depends only on the batch count: uniform.
     if constexpr (XCHG) {
         static_assert(VEC > 1, "the exchange layout moves 16-byte vectors");
         const int per_head = 2 * p.nvec;
@@ -98,6 +103,17 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             const int k = item - h * per_head;  // == t % per_head: heads are aligned to per_head lanes
             const bool upper = k >= p.nvec;
             const int col = (upper ? k - p.nvec : k) * VEC;  // table column
+            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
+            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + k * VEC;
+            Raw<XDT, VEC> r[2];
+            auto load_pair = [&](int64_t b, bool two) {
+                r[0].template load<NT>(p.x, xoff + b * xstep);
+                if (two)
+                    r[1].template load<NT>(p.x, xoff + (b + 1) * xstep);
+                else
+                    r[1].zero();
+            };
+            load_pair(0, p.B > 1);
             float c[VEC], sn[VEC];
             load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
             load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
@@ -106,8 +122,6 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             const float sg = upper ? p.sign : -p.sign;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) sn[e] *= sg;
-            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
-            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + k * VEC;
             // one packed 32-bit word at a time keeps few values live
             // (the kernel stays within 64 VGPRs: 8 waves per SIMD)
             auto finish = [&](const Raw<XDT, VEC> &mine, int64_t o) {
@@ -132,18 +146,13 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
                 else
                     *dst = res;
             };
-            int64_t b = 0;
-            for (; b + 1 < p.B; b += 2) {
-                Raw<XDT, VEC> r0, r1;
-                r0.template load<NT>(p.x, xoff + b * xstep);
-                r1.template load<NT>(p.x, xoff + (b + 1) * xstep);
-                finish(r0, ooff + b * ostep);
-                finish(r1, ooff + (b + 1) * ostep);
-            }
-            if (b < p.B) {
-                Raw<XDT, VEC> r0;
-                r0.template load<NT>(p.x, xoff + b * xstep);
-                finish(r0, ooff + b * ostep);
+            for (int64_t b = 0;;) {
+                const bool two = b + 1 < p.B;
+                finish(r[0], ooff + b * ostep);
+                if (two) finish(r[1], ooff + (b + 1) * ostep);
+                b += 2;
+                if (b >= p.B) break;
+                load_pair(b, b + 1 < p.B);
             }
         }
     } else {
@@ -154,47 +163,47 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             if (s >= p.S || item >= p.items) continue;
             const int h = item / p.nvec;
             const int col = (item - h * p.nvec) * VEC;
+            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + col;
+            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + col;
+            // each thread reads its own elements of a row before writing
+            // them, so an output may be the input itself
+            float x0[2][VEC], x1[2][VEC];
+            auto load_pair = [&](int64_t b, bool two) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (u == 0 || two) {
+                        load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep, x0[u]);
+                        load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep + p.half, x1[u]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) x0[u][e] = x1[u][e] = 0.0f;
+                    }
+                }
+            };
+            load_pair(0, p.B > 1);
             float c[VEC], sn[VEC];
             load_elems<TDT, VEC>(p.cos, s * p.ts + col, c);
             load_elems<TDT, VEC>(p.sin, s * p.ts + col, sn);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) sn[e] *= p.sign;  // exact
-            const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + col;
-            const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + col;
-            // two batches per iteration: both rows' loads are issued before
-            // either row is stored (an output may be the input itself, but
-            // each thread reads its own elements of a row before writing them)
-            int64_t b = 0;
-            for (; b + 1 < p.B; b += 2) {
-                float x0[2][VEC], x1[2][VEC];
+            for (int64_t b = 0;;) {
+                const bool two = b + 1 < p.B;
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep, x0[u]);
-                    load_elems<XDT, VEC, NT>(p.x, xoff + (b + u) * xstep + p.half, x1[u]);
-                }
+                    if (u == 0 || two) {
+                        float o0[VEC], o1[VEC];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    float o0[VEC], o1[VEC];
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        o0[e] = rot_lo(x0[u][e], x1[u][e], c[e], sn[e]);
-                        o1[e] = rot_hi(x0[u][e], x1[u][e], c[e], sn[e]);
+                        for (int e = 0; e < VEC; ++e) {
+                            o0[e] = rot_lo(x0[u][e], x1[u][e], c[e], sn[e]);
+                            o1[e] = rot_hi(x0[u][e], x1[u][e], c[e], sn[e]);
+                        }
+                        store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep, o0);
+                        store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep + p.half, o1);
                     }
-                    store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep, o0);
-                    store_elems<XDT, VEC, NT>(p.out, ooff + (b + u) * ostep + p.half, o1);
                 }
-            }
-            if (b < p.B) {
-                float x0[VEC], x1[VEC], o0[VEC], o1[VEC];
-                load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep, x0);
-                load_elems<XDT, VEC, NT>(p.x, xoff + b * xstep + p.half, x1);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    o0[e] = rot_lo(x0[e], x1[e], c[e], sn[e]);
-                    o1[e] = rot_hi(x0[e], x1[e], c[e], sn[e]);
-                }
-                store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep, o0);
-                store_elems<XDT, VEC, NT>(p.out, ooff + b * ostep + p.half, o1);
+                b += 2;
+                if (b >= p.B) break;
+                load_pair(b, b + 1 < p.B);
             }
         }
     }

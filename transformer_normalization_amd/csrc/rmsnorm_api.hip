@@ -315,6 +315,21 @@ int64_t max_partials(int64_t H) {
     return p;
 }
 
+// Row groups (workgroups) of the backward resident per CU.  Measured on
+// gfx950 over H = 256 .. 8192 and M = 4096 .. 131072 (bf16): the plain
+// backward is fastest with about 8 waves per CU when a row spans several
+// waves, and about 4 when a row is one wave (its reduction has no barrier)
+// -- more when that wave is partly idle; the residual form, whose rows carry
+// a third stream, with about 4.  More groups than that slow both kernels:
+// each adds a partial row for the finalize to sum and shortens the rows a
+// group streams between its prologue and its partial store.
+int bwd_groups_per_cu(bool res, int wpr, int nvec) {
+    if (res) return wpr >= 4 ? 1 : 4 / wpr;
+    if (wpr >= 2) return wpr >= 8 ? 1 : 8 / wpr;
+    const int active = nvec < 64 ? nvec : 64;  // busy lanes of the row's wave
+    return 4 * 64 / active;
+}
+
 size_t bwd_workspace(int64_t M, int64_t H) {
     if (M <= 0 || H <= 0 || H > kMaxH) return 0;
     const int64_t cap = max_partials(H);
@@ -412,12 +427,11 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
-    // About 12 waves per CU with whole workgroups (one 12-wave workgroup per CU
-    // at H = 6144 bf16), rows interleaved: measured fastest on gfx950 for the
-    // row loop, and it keeps the dw partial sums (P x H x 4 bytes, written and
-    // read once) near the minimum that fills the device.  A grid that is not
-    // a multiple of the CU count leaves a tail of CUs with an extra block.
-    if (P <= 0) P = (int64_t)cus * (g.wpr >= 12 ? 1 : 12 / g.wpr);
+    // Whole row groups per CU, rows interleaved (see bwd_groups_per_cu); the
+    // dw partial sums are P x H x 4 bytes, written and read once.  A grid that
+    // is not a multiple of the CU count leaves a tail of CUs with an extra
+    // block.
+    if (P <= 0) P = (int64_t)cus * bwd_groups_per_cu(res, g.wpr, g.nvec);
     if (P > max_partials(H)) P = max_partials(H);
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;

@@ -95,16 +95,19 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
         // this row group use the same one (rows of one batch)
         Raw<WDT, VEC> scr[ADALN ? VPT : 1], shr[ADALN ? VPT : 1];
         int64_t have_crow = -1;
-        for (int64_t it = 0; it < p.iters; ++it) {
+        // A row's loads are issued before the loop (first row) or at the end
+        // of the previous iteration, never behind a wait: loaded before a loop
+        // that uses them, the weights would otherwise be waited for in the
+        // loop's preheader, ahead of the first row's loads, and every
+        // workgroup would pay two memory latencies in a row.
+        Raw<XDT, VEC> xr[VPT];
+        Raw<XDT, VEC> rr[RESID ? VPT : 1];
+        auto load_row = [&](int64_t it) {
             const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
-            const bool valid = row < p.M;
-            Raw<XDT, VEC> xr[VPT];
-            Raw<XDT, VEC> rr[RESID ? VPT : 1];
-            const int64_t crow = ADALN ? row / p.rows_per_cond : 0;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
-                if (valid && v < p.nvec) {
+                if (row < p.M && v < p.nvec) {
                     xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
                     if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
                 } else {
@@ -112,8 +115,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     if constexpr (RESID) rr[k].zero();
                 }
             }
+            // the row's conditioning row travels with it (same wait), unless
+            // the previous row already used it
             if constexpr (ADALN) {
-                if (valid && crow != have_crow) {
+                const int64_t crow = row / p.rows_per_cond;
+                if (row < p.M && crow != have_crow) {
 #pragma unroll
                     for (int k = 0; k < VPT; ++k) {
                         const int v = t + k * row_threads;
@@ -129,6 +135,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     have_crow = crow;
                 }
             }
+        };
+        load_row(0);
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
@@ -180,6 +191,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                 }
             }
+            if (it + 1 < p.iters) load_row(it + 1);
         }
     } else {
         const int chunk = row_threads * VPT;

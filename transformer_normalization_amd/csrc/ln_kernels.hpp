@@ -74,15 +74,18 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
             else
                 br[k].zero();
         }
-        for (int64_t it = 0; it < p.iters; ++it) {
+        // a row's loads are issued before the loop (first row) or at the end
+        // of the previous iteration, never behind a wait: the weight and bias
+        // would otherwise be waited for in the loop's preheader, ahead of the
+        // first row's loads (two memory latencies in a row)
+        Raw<XDT, VEC> xr[VPT];
+        Raw<XDT, VEC> rr[RESID ? VPT : 1];
+        auto load_row = [&](int64_t it) {
             const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
-            const bool valid = row < p.M;
-            Raw<XDT, VEC> xr[VPT];
-            Raw<XDT, VEC> rr[RESID ? VPT : 1];
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
-                if (valid && v < p.nvec) {
+                if (row < p.M && v < p.nvec) {
                     xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
                     if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
                 } else {
@@ -90,6 +93,11 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                     if constexpr (RESID) rr[k].zero();
                 }
             }
+        };
+        load_row(0);
+        for (int64_t it = 0; it < p.iters; ++it) {
+            const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
+            const bool valid = row < p.M;
             // h of vector k, widened (and summed with the residual) again at
             // each use; every widening gives the same floats
             auto widen_h = [&](int k, float *hv) {
@@ -158,6 +166,7 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                     store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                 }
             }
+            if (it + 1 < p.iters) load_row(it + 1);
         }
     } else {
         const int chunk = row_threads * VPT;

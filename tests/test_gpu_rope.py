@@ -96,9 +96,12 @@ def test_workload_rope(name):
 # ---------------------------------------------------------------------------
 
 # head_dim 64/128/256/512 (16-bit) take the lane exchange; 48 and 96 the
-# split layout with vectors; 2, 14, 72 and 1000 (16-bit) single elements
+# split layout with vectors; 2, 14, 72 and 1000 (16-bit) single elements.
+# Batches are taken in pairs: 1 to 5 batches cover a lone batch, whole pairs,
+# and pairs followed by a last single batch, in each layout.
 SHAPES = [(1, 1, 1, 2), (2, 3, 1, 8), (3, 5, 3, 14), (2, 257, 32, 64), (1, 33, 7, 72), (2, 19, 4, 128),
-          (3, 9, 2, 256), (1, 4, 300, 64), (2, 3, 2, 1000), (2, 17, 5, 96), (1, 9, 3, 48), (2, 5, 3, 512)]
+          (3, 9, 2, 256), (1, 4, 300, 64), (2, 3, 2, 1000), (2, 17, 5, 96), (1, 9, 3, 48), (2, 5, 3, 512),
+          (5, 6, 2, 64), (4, 7, 3, 128), (5, 5, 3, 96), (4, 3, 2, 48), (5, 3, 1, 14)]
 
 
 @pytest.mark.parametrize("transpose", [False, True], ids=["fwd", "transposed"])

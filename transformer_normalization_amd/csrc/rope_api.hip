@@ -97,14 +97,23 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     p.B = B;
     p.half = (int)half;
     p.nvec = (int)nvec;
-    p.items = (int)(NH * (xchg ? 2 * nvec : nvec));
-    p.ipw = p.items < kRopeThreads ? p.items : kRopeThreads;
-    p.tpw = kRopeThreads / p.ipw;
+    const int64_t items = NH * (xchg ? 2 * nvec : nvec);
+    if (items > INT32_MAX - kRopeThreads)
+        return fail(RMSN_ERR_UNSUPPORTED, "num_heads * head_dim = %lld is too large", (long long)(NH * D));
+    p.items = (int)items;
     p.sign = transpose ? -1.0f : 1.0f;
-    p.nblocks = (S + p.tpw - 1) / p.tpw;
-    p.iblocks = (p.items + p.ipw - 1) / p.ipw;
-    if (p.nblocks > INT64_MAX / p.iblocks) return fail(RMSN_ERR_UNSUPPORTED, "seq_len = %lld is too large", (long long)S);
-    int64_t grid = p.nblocks * p.iblocks;
+    if (S > (INT64_MAX - kRopeThreads) / items)
+        return fail(RMSN_ERR_UNSUPPORTED, "seq_len = %lld is too large", (long long)S);
+    if (xchg) {
+        p.nwork = (S * items + kRopeThreads - 1) / kRopeThreads;
+        p.ipw = p.tpw = p.iblocks = 0;  // unused
+    } else {
+        p.ipw = p.items < kRopeThreads ? p.items : kRopeThreads;
+        p.tpw = kRopeThreads / p.ipw;
+        p.iblocks = (p.items + p.ipw - 1) / p.ipw;
+        p.nwork = ((S + p.tpw - 1) / p.tpw) * p.iblocks;  // no overflow: <= S * items + 255
+    }
+    int64_t grid = p.nwork;
     if (ov.set && ov.d > 0 && ov.d < grid) grid = ov.d;
     if (grid > INT32_MAX) grid = INT32_MAX;  // the work is walked grid-stride
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued

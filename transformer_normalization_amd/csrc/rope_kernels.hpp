@@ -18,12 +18,22 @@
 //    elements j.. of the first half and the matching elements of the second
 //    half (two accesses head_dim/2 apart).
 //
-// Mapping: a workgroup of 256 threads covers `tpw` positions x `ipw` items.
-// When one position has more than 256 items it takes `iblocks` consecutive
-// workgroups, so neighbouring workgroups cover neighbouring bytes of a token
-// row (a position-major order would leave strided holes in each row).  The
-// (position block, item block) pairs are walked grid-stride, so a capped
-// grid also works.
+// Mapping of the exchange layout: the (position, item) pairs are numbered
+// position-major, item fastest, and work unit u is the 256 pairs u*256 ..
+// u*256+255; thread t of a workgroup takes pair u*256 + t.  No thread idles
+// whatever the number of items per position (a position may span several
+// units, a unit several positions), neighbouring threads and workgroups
+// cover neighbouring bytes of a token row, and a head's lanes stay whole and
+// aligned inside one wave (the items of a position are a multiple of the
+// lanes of a head, which divide 64).
+//
+// Mapping of the split layout: a workgroup covers `tpw` positions x `ipw`
+// items; a position with more than 256 items takes `iblocks` consecutive
+// workgroups.  (The flat numbering measured slower here, by 2-11 %, even
+// though this mapping leaves threads idle when the items of a position are
+// not a divisor or multiple of 256.)
+//
+// Units are walked grid-stride in both, so a capped grid also works.
 #pragma once
 
 #include "numerics.hpp"
@@ -43,10 +53,10 @@ struct RopeParams {
     int half;          // head_dim / 2
     int nvec;          // vectors per half head (half / VEC)
     int items;         // work items per position: num_heads * nvec (split), * 2 nvec (exchange)
-    int ipw;           // items per workgroup row (<= 256)
-    int tpw;           // positions per workgroup
-    int64_t nblocks;   // position blocks: ceil(S / tpw)
-    int iblocks;       // item blocks per position block: ceil(items / ipw)
+    int64_t nwork;     // work units: ceil(S * items / 256) (exchange), nblocks * iblocks (split)
+    int ipw;           // split: items per workgroup row (<= 256)
+    int tpw;           // split: positions per workgroup
+    int iblocks;       // split: item blocks per position block, ceil(items / ipw)
     float sign;        // +1, or -1 for the transposed rotation
 };
 
@@ -76,12 +86,18 @@ __device__ __forceinline__ Raw<DT, N> from_lane(const Raw<DT, N> &r, int byte_ad
 template <int XDT, int TDT, int VEC, bool NT, bool XCHG>
 __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopeParams p) {
     const int t = threadIdx.x;
-    const int lt = t / p.ipw;
-    const int it = t - lt * p.ipw;
-    if (lt >= p.tpw) return;
     const int64_t xstep = p.S * p.xrs;  // one batch further
     const int64_t ostep = p.S * p.ors;
-    const int64_t nwork = p.nblocks * p.iblocks;
+    // pair u*256 + t as (position s, item); the division of the unit's first
+    // pair is uniform, the thread's offset from it is below items + 256
+    auto pair_of = [&](int64_t wk, int64_t &s, int &item) {
+        const int64_t first = wk * kRopeThreads;
+        const int64_t s0 = first / p.items;
+        const int idx = (int)(first - s0 * p.items) + t;
+        const int q = (int)((unsigned)idx / (unsigned)p.items);
+        s = s0 + q;
+        item = idx - q * p.items;
+    };
 
     // Batches are taken two at a time.  The rows of a pair are requested
     // before the table entries of the position, so the latency of the table
@@ -92,15 +108,15 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
         static_assert(VEC > 1, "the exchange layout moves 16-byte vectors");
         const int per_head = 2 * p.nvec;
         const int partner = ((t & 63) ^ p.nvec) << 2;  // ds_bpermute byte address
-        for (int64_t wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
-            const int64_t pb = wk / p.iblocks;
-            const int item = (int)(wk - pb * p.iblocks) * p.ipw + it;
-            const int64_t s = pb * p.tpw + lt;
-            // partners share the position and the item block: both go on or
-            // both skip (items is a multiple of per_head)
-            if (s >= p.S || item >= p.items) continue;
+        for (int64_t wk = blockIdx.x; wk < p.nwork; wk += gridDim.x) {
+            int64_t s;
+            int item;
+            pair_of(wk, s, item);
+            // partners share the position: both go on or both skip (items is
+            // a multiple of per_head)
+            if (s >= p.S) continue;
             const int h = item / per_head;
-            const int k = item - h * per_head;  // == t % per_head: heads are aligned to per_head lanes
+            const int k = item - h * per_head;  // == t % per_head: units start on head boundaries
             const bool upper = k >= p.nvec;
             const int col = (upper ? k - p.nvec : k) * VEC;  // table column
             const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
@@ -156,7 +172,10 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             }
         }
     } else {
-        for (int64_t wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
+        const int lt = t / p.ipw;
+        const int it = t - lt * p.ipw;
+        if (lt >= p.tpw) return;
+        for (int64_t wk = blockIdx.x; wk < p.nwork; wk += gridDim.x) {
             const int64_t pb = wk / p.iblocks;
             const int item = (int)(wk - pb * p.iblocks) * p.ipw + it;
             const int64_t s = pb * p.tpw + lt;

@@ -57,10 +57,17 @@
 extern "C" {
 #endif
 
+/* Both enums are int-sized, and their two range markers make every int value
+ * a valid value of the type (also in C++, where a value outside an enum's
+ * range is undefined): a caller may pass any int, and the library rejects
+ * the ones it does not know with RMSN_ERR_UNSUPPORTED instead of misbehaving.
+ * The markers are never valid arguments. */
 typedef enum {
     RMSN_F32 = 0,  /* IEEE binary32 */
     RMSN_F16 = 1,  /* IEEE binary16 */
-    RMSN_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+    RMSN_BF16 = 2, /* bfloat16 (upper half of a binary32) */
+    RMSN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    RMSN_DTYPE_RANGE_MAX_ = 2147483647
 } rmsn_dtype_t;
 
 typedef enum {
@@ -68,7 +75,9 @@ typedef enum {
     RMSN_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size/stride/eps, overlap */
     RMSN_ERR_UNSUPPORTED = 2, /* dtype combination, H too large, device not gfx950 */
     RMSN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-    RMSN_ERR_HIP = 4          /* device query or kernel launch failed */
+    RMSN_ERR_HIP = 4,         /* device query or kernel launch failed */
+    RMSN_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    RMSN_STATUS_RANGE_MAX_ = 2147483647
 } rmsn_status_t;
 
 /*

@@ -51,6 +51,7 @@ bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool 
     case RMSN_BF16:
         return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, RES, NT>(vec, vpt, two_pass)
                     : bwd_kernel_vec<DT_BF16, DT_BF16, RES, NT>(vec, vpt, two_pass);
+    default: break;  // any other value: no kernel
     }
     return nullptr;
 }

@@ -50,6 +50,7 @@ fwd_fn fwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool 
     case RMSN_BF16:
         return wf32 ? fwd_kernel_vec<DT_BF16, DT_F32, MODE, NT>(vec, vpt, two_pass)
                     : fwd_kernel_vec<DT_BF16, DT_BF16, MODE, NT>(vec, vpt, two_pass);
+    default: break;  // any other value: no kernel
     }
     return nullptr;
 }

@@ -94,6 +94,11 @@ rmsn_status_t device_info(int *cus) {
 // ---------------------------------------------------------------------------
 
 rmsn_status_t check_overlap(const Region *outs, int nout, const Region *ins, int nin) {
+    for (int k = 0; k < nout + nin; ++k) {
+        const Region &r = k < nout ? outs[k] : ins[k - nout];
+        if (r.present && !r.fits())
+            return fail(RMSN_ERR_INVALID_ARG, "%s extends past the end of the address space", r.name);
+    }
     for (int i = 0; i < nout; ++i) {
         if (!outs[i].present) continue;
         for (int j = i + 1; j < nout; ++j)

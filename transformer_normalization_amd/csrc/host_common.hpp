@@ -37,8 +37,15 @@ struct Region {
     int64_t cols;
     int ebytes;
     bool present;
-    uintptr_t lo() const { return base; }
-    uintptr_t hi() const { return base + (uintptr_t)(((rows - 1) * stride + cols) * ebytes); }
+    // Byte bounds in 128-bit arithmetic: no size the caller passes can
+    // overflow them (check_overlap rejects a region whose end passes 2^64
+    // before comparing any).  Regions have rows >= 1.
+    unsigned __int128 lo() const { return base; }
+    unsigned __int128 hi() const {
+        return (unsigned __int128)base +
+               (unsigned __int128)(((__int128)(rows - 1) * stride + cols) * (__int128)ebytes);
+    }
+    bool fits() const { return hi() <= ((unsigned __int128)1 << 64); }
     bool overlaps(const Region &o) const { return lo() < o.hi() && o.lo() < hi(); }
     bool same(const Region &o) const {
         return base == o.base && stride == o.stride && rows == o.rows && cols == o.cols && ebytes == o.ebytes;

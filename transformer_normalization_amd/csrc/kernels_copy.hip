@@ -38,6 +38,8 @@ extern "C" RMSN_API rmsn_status_t rmsnorm_tuning_copy(const void *src, void *dst
         return fail(RMSN_ERR_INVALID_ARG, "bytes = %lld must be a non-negative multiple of 16", (long long)bytes);
     if (!aligned16(src) || !aligned16(dst)) return fail(RMSN_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
     const Region a = vec("src", src, bytes, 1), b = vec("dst", dst, bytes, 1);
+    if (bytes > 0 && (!a.fits() || !b.fits()))
+        return fail(RMSN_ERR_INVALID_ARG, "src or dst extends past the end of the address space");
     if (bytes > 0 && a.overlaps(b)) return fail(RMSN_ERR_INVALID_ARG, "src and dst overlap");
     if (bytes == 0) return ok();
     const int64_t nvec = bytes / 16;

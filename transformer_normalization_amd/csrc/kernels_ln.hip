@@ -47,6 +47,7 @@ ln_fn ln_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool tw
     case RMSN_BF16:
         return wf32 ? ln_kernel_vec<DT_BF16, DT_F32, RES, NT>(vec, vpt, two_pass)
                     : ln_kernel_vec<DT_BF16, DT_BF16, RES, NT>(vec, vpt, two_pass);
+    default: break;  // any other value: no kernel
     }
     return nullptr;
 }

@@ -21,6 +21,7 @@ rope_fn rope_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool xchg) {
         return tf32 ? rope_for<DT_F16, DT_F32, NT>(vec, xchg) : rope_for<DT_F16, DT_F16, NT>(vec, xchg);
     case RMSN_BF16:
         return tf32 ? rope_for<DT_BF16, DT_F32, NT>(vec, xchg) : rope_for<DT_BF16, DT_BF16, NT>(vec, xchg);
+    default: break;  // any other value: no kernel
     }
     return nullptr;
 }

@@ -173,7 +173,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     if (adaln) {
         if (cond.rows_per_cond < 1)
             return fail(RMSN_ERR_INVALID_ARG, "rows_per_cond = %lld must be >= 1", (long long)cond.rows_per_cond);
-        crows = (M + cond.rows_per_cond - 1) / cond.rows_per_cond;
+        crows = M / cond.rows_per_cond + (M % cond.rows_per_cond != 0);  // ceil, without overflow
         if ((st = check_stride("cond_stride", cond.cs, crows, H, pb)) != RMSN_OK) return st;
     }
     if (M == 0) return RMSN_OK;
@@ -201,13 +201,13 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     // vector path: every row start 16-byte aligned and H a whole number of vectors
     const int vecw = 16 / eb;
-    bool vec_ok = (H % vecw) == 0 && aligned16(x) && aligned16(y) && (xs * eb) % 16 == 0 && (ys * eb) % 16 == 0 &&
+    bool vec_ok = (H % vecw) == 0 && aligned16(x) && aligned16(y) && xs % (16 / eb) == 0 && ys % (16 / eb) == 0 &&
                   (w == nullptr || aligned16(w));
     if (resid)
-        vec_ok = vec_ok && aligned16(r) && (rs * eb) % 16 == 0 &&
-                 (ro == nullptr || (aligned16(ro) && (ros * eb) % 16 == 0));
+        vec_ok = vec_ok && aligned16(r) && rs % (16 / eb) == 0 &&
+                 (ro == nullptr || (aligned16(ro) && ros % (16 / eb) == 0));
     if (adaln)
-        vec_ok = vec_ok && aligned16(cond.scale) && aligned16(cond.shift) && (cond.cs * pb) % 16 == 0;
+        vec_ok = vec_ok && aligned16(cond.scale) && aligned16(cond.shift) && cond.cs % (16 / pb) == 0;
     if (bias != nullptr) vec_ok = vec_ok && aligned16(bias);
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
@@ -215,6 +215,10 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     const Override ov = get_override(0);
     if (ov.set) {
+        // bounds first: the products below are then small
+        if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16 || ov.c < 0 || ov.c > 16)
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: tile vpt %d wpr %d rpw %d out of range", ov.a, ov.b,
+                        ov.c);
         Geom o = g;
         o.vpt = ov.a;
         o.wpr = ov.b;
@@ -395,8 +399,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
 
     const int vecw = 16 / eb;
     const bool vec_ok = (H % vecw) == 0 && aligned16(dy) && aligned16(x) && aligned16(dx) &&
-                        (dys * eb) % 16 == 0 && (xs * eb) % 16 == 0 && (dxs * eb) % 16 == 0 &&
-                        (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && (drs * eb) % 16 == 0));
+                        dys % (16 / eb) == 0 && xs % (16 / eb) == 0 && dxs % (16 / eb) == 0 &&
+                        (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && drs % (16 / eb) == 0));
     const Kind kind = res ? Kind::BwdRes : Kind::Bwd;
     Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, 8);
     int64_t P = 0;  // 0: chosen from the device below
@@ -405,6 +409,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     bool interleave = true;
     const Override ov = get_override(1);
     if (ov.set) {
+        if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16)
+            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: tile vpt %d wpr %d out of range", ov.a, ov.b);
         Geom o = g;
         o.vpt = ov.a;
         o.wpr = ov.b;
@@ -565,6 +571,7 @@ RMSN_API const char *rmsnorm_status_string(rmsn_status_t s) {
     case RMSN_ERR_UNSUPPORTED: return "RMSN_ERR_UNSUPPORTED";
     case RMSN_ERR_WORKSPACE: return "RMSN_ERR_WORKSPACE";
     case RMSN_ERR_HIP: return "RMSN_ERR_HIP";
+    default: break;
     }
     return "RMSN_UNKNOWN_STATUS";
 }

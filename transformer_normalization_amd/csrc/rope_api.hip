@@ -46,7 +46,8 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
         return fail(RMSN_ERR_INVALID_ARG, "head_dim = %lld must be even and >= 2", (long long)D);
     if (D > kMaxHeadDim) return fail(RMSN_ERR_UNSUPPORTED, "head_dim = %lld exceeds 65536", (long long)D);
     if (NH > kMaxRowElems / D)
-        return fail(RMSN_ERR_UNSUPPORTED, "num_heads * head_dim = %lld exceeds 2^24", (long long)(NH * D));
+        return fail(RMSN_ERR_UNSUPPORTED, "num_heads * head_dim = %lld * %lld exceeds 2^24", (long long)NH,
+                    (long long)D);
     if (B > INT64_MAX / S) return fail(RMSN_ERR_INVALID_ARG, "batch * seq_len overflows");
     const int64_t rows = B * S;
     const int64_t half = D / 2;
@@ -72,7 +73,7 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     const int vecw = 16 / eb;
     const bool vec_ok = half % vecw == 0 && aligned16(x) && aligned16(out) && xrs % vecw == 0 && xhs % vecw == 0 &&
                         ors % vecw == 0 && ohs % vecw == 0 && aligned16(cos_t) && aligned16(sin_t) &&
-                        (ts * tb) % 16 == 0;
+                        ts % (16 / tb) == 0;
     const int vec = vec_ok ? vecw : 1;
     const int64_t nvec = half / vec;
     // lane exchange when a head's 2*nvec lanes are a power of two <= 64, so

@@ -164,6 +164,13 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
             for (int k = 0; k < VPT; ++k) {
                 xr[k].opaque();
                 if constexpr (RESID) rr[k].opaque();
+                // the weight (and AdaLN's rows) too: widened before the
+                // reduction, their float32 copies would stay live across it
+                wr[k].opaque();
+                if constexpr (ADALN) {
+                    scr[k].opaque();
+                    shr[k].opaque();
+                }
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {

@@ -152,6 +152,10 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
             for (int k = 0; k < VPT; ++k) {
                 xr[k].opaque();
                 if constexpr (RESID) rr[k].opaque();
+                // weight and bias too: widened early, their float32 copies
+                // would stay live across both reductions
+                wr[k].opaque();
+                br[k].opaque();
             }
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {

@@ -90,6 +90,15 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     const bool bwd = kind == Kind::Bwd || kind == Kind::BwdRes;
     const int *set = vec == 1 ? kScalarVpt : bwd ? kBwdVecVpt : kFwdVecVpt;
     const int nset = vec == 1 ? 4 : bwd ? 4 : 6;
+    // Rows spread over more waves than `wcap` are avoided when a tile with
+    // more vectors per thread fits (measured on gfx950, bf16, 64 Mi-element
+    // calls: the forward and fused residual at H = 16384 ran 72 % of peak on
+    // 16-wave rows and 74.5-75 % on 8-11-wave rows; LayerNorm, with two
+    // reductions per row, 64 % on 16- and 8-wave rows and 73 % on 4-wave rows
+    // at H = 16384, while at H <= 8192 its tiles were within 1 %).  A
+    // penalty, not a limit: with no tile under the cap the row stays
+    // resident on the best tile over it.
+    const int wcap = kind == Kind::Ln ? (g.nvec > 1024 ? 4 : 16) : bwd ? 16 : 12;
     double best = 1e30;
     for (int i = 0; i < nset; ++i) {
         const int vpt = set[i];
@@ -99,7 +108,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
         const double slots = 64.0 * wpr * vpt;
         const double idle = (slots - g.nvec) / slots;
         const double pref = std::fabs(std::log2((double)(vpt * vec) / pref_elems));
-        const double cost = 8.0 * idle + pref;
+        const double cost = 8.0 * idle + pref + (wpr > wcap ? 4.0 : 0.0);
         if (cost < best) {
             best = cost;
             g.vpt = vpt;

@@ -132,8 +132,10 @@ def test_workload_bwd_chained_with_gpu_rrms():
 # shapes: ragged, tiny and long rows, every format
 # ---------------------------------------------------------------------------
 
-EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 3072, 4097, 5120, 6144, 8191, 12288,
-          16385, 32768, 65536]
+# 16384 takes a tile capped below 16 waves per row (16-bit: 3 x 11 plain,
+# 4 x 8 residual; float32: 6 x 11), and so does 8192 in float32 (3 x 11)
+EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 3072, 4097, 5120, 6144, 8191, 8192, 12288,
+          16384, 16385, 32768, 65536]
 
 
 def _rows_for(H):

@@ -95,8 +95,9 @@ def test_workload_rope(name):
 # shapes and formats
 # ---------------------------------------------------------------------------
 
-# head_dim 64/128/256/512 (16-bit) take the lane exchange; 48 and 96 the
-# split layout with vectors; 2, 14, 72 and 1000 (16-bit) single elements.
+# head_dim 64/128/256/512 (16-bit) take the lane exchange, 48 and 96 the
+# exchange in padded lane groups (6 and 12 lanes of 8 and 16); 2, 14, 72 and
+# 1000 (16-bit) single elements.
 # Batches are taken in pairs: 1 to 5 batches cover a lone batch, whole pairs,
 # and pairs followed by a last single batch, in each layout.
 SHAPES = [(1, 1, 1, 2), (2, 3, 1, 8), (3, 5, 3, 14), (2, 257, 32, 64), (1, 33, 7, 72), (2, 19, 4, 128),
@@ -206,7 +207,8 @@ def test_misaligned_rows_use_single_elements(dtype):
 
 
 @pytest.mark.parametrize("geom", [(1, 1, 1, 0), (1, 1, 0, 7), (1, 1, 1, 5)], ids=["split", "grid7", "split_grid5"])
-@pytest.mark.parametrize("shape", [(2, 300, 8, 64), (3, 41, 4, 128)], ids=["d64", "d128"])
+@pytest.mark.parametrize("shape", [(2, 300, 8, 64), (3, 41, 4, 128), (2, 37, 5, 96), (3, 29, 3, 80), (1, 50, 6, 48)],
+                         ids=["d64", "d128", "d96_padded", "d80_padded", "d48_padded"])
 def test_layouts_and_capped_grid_give_identical_bits(shape, geom):
     """The split layout and a capped, grid-stride grid compute the same
     float32 expressions as the default lane exchange: identical bits."""

@@ -76,9 +76,12 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
                         ts % (16 / tb) == 0;
     const int vec = vec_ok ? vecw : 1;
     const int64_t nvec = half / vec;
-    // lane exchange when a head's 2*nvec lanes are a power of two <= 64, so
-    // heads never straddle waves and partners are lane ^ nvec
-    bool xchg = vec > 1 && nvec <= 32 && (nvec & (nvec - 1)) == 0;
+    // lane exchange when a head's 2*nvec lanes fit a wave: each head takes a
+    // power-of-two group of lanes (padding lanes idle), so heads never
+    // straddle waves
+    bool xchg = vec > 1 && nvec <= 32;
+    int group = 1;
+    while (group < 2 * nvec) group *= 2;
     const Override ov = get_override(2);
     if (ov.set && ov.c == 1) xchg = false;
     const bool nt = use_streaming(2 * rows * NH * D * eb);
@@ -98,7 +101,8 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     p.B = B;
     p.half = (int)half;
     p.nvec = (int)nvec;
-    const int64_t items = NH * (xchg ? 2 * nvec : nvec);
+    p.group = group;
+    const int64_t items = NH * (xchg ? group : nvec);
     if (items > INT32_MAX - kRopeThreads)
         return fail(RMSN_ERR_UNSUPPORTED, "num_heads * head_dim = %lld is too large", (long long)(NH * D));
     p.items = (int)items;

@@ -9,12 +9,13 @@
 // Two layouts of the work, both applying a position's table entries (loaded
 // once per thread) to every batch b of that position (rows b * seq_len + s):
 //
-//  - lane exchange (XCHG, the default when a half head is a power-of-two
-//    number <= 32 of 16-byte vectors): lane k of a head's 2*nvec lanes holds
-//    vector k of the head, so every load and store instruction of a wave
-//    covers whole contiguous 128-byte lines; the partner element j + D/2 (or
-//    j - D/2) is fetched from lane k ^ nvec with ds_bpermute.
-//  - split (any other shape, and single elements): a thread holds the VEC
+//  - lane exchange (XCHG, the default when a half head is at most 32 16-byte
+//    vectors): a head takes a group of `group` lanes, 2*nvec rounded up to a
+//    power of two; lane k < 2*nvec of the group holds vector k of the head
+//    (lanes above stay idle), so every load and store instruction of a wave
+//    covers whole contiguous runs of a head; the partner element j + D/2 (or
+//    j - D/2) is fetched from lane k + nvec (or k - nvec) with ds_bpermute.
+//  - split (single elements, and longer heads): a thread holds the VEC
 //    elements j.. of the first half and the matching elements of the second
 //    half (two accesses head_dim/2 apart).
 //
@@ -25,7 +26,7 @@
 // units, a unit several positions), neighbouring threads and workgroups
 // cover neighbouring bytes of a token row, and a head's lanes stay whole and
 // aligned inside one wave (the items of a position are a multiple of the
-// lanes of a head, which divide 64).
+// group, which divides 64).
 //
 // Mapping of the split layout: a workgroup covers `tpw` positions x `ipw`
 // items; a position with more than 256 items takes `iblocks` consecutive
@@ -52,7 +53,8 @@ struct RopeParams {
     int64_t B;         // batch
     int half;          // head_dim / 2
     int nvec;          // vectors per half head (half / VEC)
-    int items;         // work items per position: num_heads * nvec (split), * 2 nvec (exchange)
+    int group;         // exchange: lanes per head, 2 * nvec rounded up to a power of two (<= 64)
+    int items;         // work items per position: num_heads * nvec (split), * group (exchange)
     int64_t nwork;     // work units: ceil(S * items / 256) (exchange), nblocks * iblocks (split)
     int ipw;           // split: items per workgroup row (<= 256)
     int tpw;           // split: positions per workgroup
@@ -106,8 +108,13 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
     // load behind it).  `two` depends only on the batch count: uniform.
     if constexpr (XCHG) {
         static_assert(VEC > 1, "the exchange layout moves 16-byte vectors");
-        const int per_head = 2 * p.nvec;
-        const int partner = ((t & 63) ^ p.nvec) << 2;  // ds_bpermute byte address
+        const int per_head = p.group;
+        // lane k of a group (the same for every unit: units start on group
+        // boundaries) and its partner, k + nvec or k - nvec
+        const int k = t & (per_head - 1);
+        const bool upper = k >= p.nvec;
+        const int partner = ((t & 63) + (upper ? -p.nvec : p.nvec)) << 2;  // ds_bpermute byte address
+        if (k >= 2 * p.nvec) return;  // padding lane of the group: no element
         for (int64_t wk = blockIdx.x; wk < p.nwork; wk += gridDim.x) {
             int64_t s;
             int item;
@@ -116,8 +123,6 @@ __global__ void __launch_bounds__(kRopeThreads) rope_apply_kernel(const RopePara
             // a multiple of per_head)
             if (s >= p.S) continue;
             const int h = item / per_head;
-            const int k = item - h * per_head;  // == t % per_head: units start on head boundaries
-            const bool upper = k >= p.nvec;
             const int col = (upper ? k - p.nvec : k) * VEC;  // table column
             const int64_t xoff = s * p.xrs + (int64_t)h * p.xhs + k * VEC;
             const int64_t ooff = s * p.ors + (int64_t)h * p.ohs + k * VEC;

@@ -127,3 +127,55 @@ def test_rope_past_2_31_elements():
                                 np.abs(xv[..., :h] * sv) + np.abs(xv[..., h:] * cv)], axis=-1)
         parity.check_dx16(rep, got, want, terms.reshape(len(pos), NH * D), "bf16", oracle.encode, oracle.decode)
         G.assert_ok(rep)
+
+
+def test_fused_residual_past_2_31_elements():
+    d = G.inputs(7003, R, H, "bf16", residual=True)
+    x, r = repeated(d["x"], "bf16"), repeated(d["r"], "bf16")
+    w = G.to_dev(d["w"], "bf16")
+    y, ro = tn.rmsnorm_fwd_residual(x, r, w, 1e-5)
+    del x, r
+    torch.cuda.synchronize()
+    rows = sample_rows()
+    idx = torch.from_numpy(rows).to(G.DEV)
+    yref, href, _ = oracle.fwd_residual(d["x"], d["r"], d["w"], G.eps32(1e-5), "bf16")
+    rep = parity.Report("fused residual y past 2^31")
+    parity.check16(rep, G.to_host(y[idx], "bf16"), yref[rows % R], "bf16", oracle.encode)
+    assert np.array_equal(G.to_host(ro[idx], "bf16"), oracle.encode(href[rows % R], "bf16"))
+    G.assert_ok(rep)
+
+
+def test_layernorm_residual_past_2_31_elements():
+    import synthetic
+    d = G.inputs(7004, R, H, "bf16", residual=True)
+    b = synthetic.normal_tensor(7004, synthetic.STREAM_BIAS, (H,), "bf16", 0.0, 0.1)
+    x, r = repeated(d["x"], "bf16"), repeated(d["r"], "bf16")
+    y, ro = tn.layernorm_fwd_residual(x, r, G.to_dev(d["w"], "bf16"), G.to_dev(b, "bf16"), 1e-5)
+    del x, r
+    torch.cuda.synchronize()
+    rows = sample_rows()
+    idx = torch.from_numpy(rows).to(G.DEV)
+    yref, href, _, _ = oracle.layernorm(d["x"], d["r"], d["w"], b, G.eps32(1e-5), "bf16")
+    rep = parity.Report("layernorm y past 2^31")
+    parity.check16(rep, G.to_host(y[idx], "bf16"), yref[rows % R], "bf16", oracle.encode)
+    assert np.array_equal(G.to_host(ro[idx], "bf16"), oracle.encode(href[rows % R], "bf16"))
+    G.assert_ok(rep)
+
+
+def test_adaln_past_2_31_elements():
+    """Per-token conditioning rows repeated like x, so conditioning row i is
+    block row i mod R as well (64-bit offsets in the conditioning rows too)."""
+    import synthetic
+    d = G.inputs(7005, R, H, "bf16")
+    sc = synthetic.normal_tensor(7005, synthetic.STREAM_SCALE, (R, H), "bf16", 0.0, 0.5)
+    sh = synthetic.normal_tensor(7005, synthetic.STREAM_SHIFT, (R, H), "bf16", 0.0, 0.5)
+    x, scd, shd = repeated(d["x"], "bf16"), repeated(sc, "bf16"), repeated(sh, "bf16")
+    y = tn.rmsnorm_adaln_fwd(x.view(1, M, H), G.to_dev(d["w"], "bf16"), scd.view(1, M, H), shd.view(1, M, H), 1e-6)
+    del x, scd, shd
+    torch.cuda.synchronize()
+    rows = sample_rows()
+    idx = torch.from_numpy(rows).to(G.DEV)
+    yref, _ = oracle.adaln_fwd(d["x"], d["w"], sc, sh, 1, G.eps32(1e-6), "bf16")
+    rep = parity.Report("adaln y past 2^31")
+    parity.check16(rep, G.to_host(y.view(M, H)[idx], "bf16"), yref[rows % R], "bf16", oracle.encode)
+    G.assert_ok(rep)

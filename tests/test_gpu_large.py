@@ -179,3 +179,28 @@ def test_adaln_past_2_31_elements():
     rep = parity.Report("adaln y past 2^31")
     parity.check16(rep, G.to_host(y.view(M, H)[idx], "bf16"), yref[rows % R], "bf16", oracle.encode)
     G.assert_ok(rep)
+
+
+def test_backward_residual_past_2_31_elements():
+    d = G.inputs(7006, R, H, "bf16", residual=True, dy=True)
+    dy, h, dres = repeated(d["dy"], "bf16"), repeated(d["x"], "bf16"), repeated(d["r"], "bf16")
+    w = G.to_dev(d["w"], "bf16")
+    _, r = oracle.fwd(d["x"], d["w"], G.eps32(1e-5), "bf16")
+    r32 = r.astype(np.float32)
+    rr = torch.from_numpy(np.resize(r32, M)).to(G.DEV)
+    dh, dw = tn.rmsnorm_bwd_residual(dy, h, dres, w, rr)
+    del dy, h, dres
+    torch.cuda.synchronize()
+    rows = sample_rows()
+    dhref, dwref1, terms = oracle.bwd_residual(d["dy"], d["x"], d["r"], d["w"], r32, "bf16")
+    rep_dh = parity.Report("residual bwd dh past 2^31")
+    parity.check_dx16(rep_dh, G.to_host(dh[torch.from_numpy(rows).to(G.DEV)], "bf16"), dhref[rows % R],
+                      terms[rows % R], "bf16", oracle.encode, oracle.decode)
+    # dw over all M rows: block row k occurs full + (k < rest) times
+    full, rest = divmod(M, R)
+    _, dw_rest, _ = oracle.bwd_residual(d["dy"][:rest], d["x"][:rest], d["r"][:rest], d["w"], r32[:rest], "bf16")
+    xn = oracle.decode(d["x"], "bf16") * r32.astype(np.float64)[:, None]
+    per_row = np.abs(oracle.decode(d["dy"], "bf16") * xn)
+    rep_dw = parity.Report("residual bwd dw past 2^31")
+    parity.check_dw(rep_dw, dw.cpu().numpy(), full * dwref1 + dw_rest, full * per_row.sum(axis=0) + per_row[:rest].sum(axis=0))
+    G.assert_ok(rep_dh, rep_dw)

@@ -274,7 +274,7 @@ def test_aligned_padding_is_bit_identical():
 
 @pytest.mark.parametrize("stream", [0, 1], ids=["cached", "streaming"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_misaligned_rows_use_single_elements(dtype, stream):
+def test_misaligned_rows(dtype, stream):
     tn.set_streaming(stream)
     M, H = 33, 4096
     d = G.inputs(62, M, H, dtype, residual=True, dy=True)
@@ -299,6 +299,99 @@ def test_misaligned_rows_use_single_elements(dtype, stream):
         reps += list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx, dtype), dw.cpu().numpy(), dtype,
                                      name=f"bwd pad={pad} off={offset}"))
         G.assert_ok(*reps)
+
+
+def _sentinel_view(M, H, pad, offset, dtype, fill):
+    """(M, H) view at element `offset` of a buffer with rows of H + pad,
+    every element first set to `fill`."""
+    buf = torch.full((offset + M * (H + pad) + 16,), fill, dtype=G.torch_dtype(dtype), device=G.DEV)
+    return buf, buf[offset:offset + M * (H + pad)].view(M, H + pad)[:, :H]
+
+
+def _untouched(buf, view, fill):
+    """Every element of buf outside `view` still holds `fill`."""
+    mask = torch.ones(buf.numel(), dtype=torch.bool, device=buf.device)
+    off = view.storage_offset() - buf.storage_offset()
+    rows = torch.arange(view.shape[0], device=buf.device)[:, None] * view.stride(0)
+    cols = torch.arange(view.shape[1], device=buf.device)[None, :]
+    mask[(off + rows + cols).reshape(-1)] = False
+    return bool(torch.all(buf[mask] == fill))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_misaligned_views_same_bits_at_any_offset(dtype):
+    """Rows off the 16-byte grid go through LDS on a vector tile that depends
+    on H only, so every layout of the same rows -- any element offset of x,
+    the residual and the outputs, any row pitch -- gives the same bits, at
+    parity with the oracle, for the plain and the fused residual forward;
+    the elements around the output rows (pads, the buffer's head and tail)
+    are never written."""
+    M, H = 37, 4096
+    d = G.inputs(66, M, H, dtype, residual=True)
+    xd, rd, wd = G.to_dev(d["x"], dtype), G.to_dev(d["r"], dtype), G.to_dev(d["w"], dtype)
+    bits = (lambda t: t.view(torch.int32)) if dtype == "f32" else (lambda t: t.view(torch.int16))
+    first = None
+    for pad, xoff, yoff in ((1, 0, 1), (0, 1, 3), (3, 1, 0), (5, 7, 2), (8, 3, 5)):
+        print(f"[gpu] staged views {dtype} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
+        _, xv = _sentinel_view(M, H, pad, xoff, dtype, 0.0)
+        _, rv = _sentinel_view(M, H, pad, xoff + 1, dtype, 0.0)
+        xv.copy_(xd)
+        rv.copy_(rd)
+        ybuf, yv = _sentinel_view(M, H, pad + 2, yoff, dtype, -77.0)
+        robuf, rov = _sentinel_view(M, H, pad, yoff + 1, dtype, -77.0)
+        _, rr = tn.rmsnorm_fwd(xv, wd, 1e-5, out=yv, return_rrms=True)
+        y2, _, rr2 = tn.rmsnorm_fwd_residual(xv, rv, wd, 1e-6, residual_out=rov, return_rrms=True)
+        torch.cuda.synchronize()
+        got = (bits(yv.contiguous()), rr, bits(y2), bits(rov.contiguous()), rr2)
+        assert _untouched(ybuf, yv, -77.0) and _untouched(robuf, rov, -77.0), (pad, xoff, yoff)
+        if first is None:
+            first = got
+            reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(yv.contiguous(), dtype), rr.cpu().numpy(), 1e-5,
+                                        dtype, name=f"fwd {dtype} staged view"))
+            reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype),
+                                              G.to_host(rov.contiguous(), dtype), rr2.cpu().numpy(), 1e-6, dtype,
+                                              name=f"res {dtype} staged view"))
+            G.assert_ok(*reps)
+        else:
+            for a, b in zip(got, first):
+                assert torch.equal(a, b), (pad, xoff, yoff)
+
+
+@pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("H", [5, 13, 63, 129, 1001, 4097, 6143, 8190, 12289])
+def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
+    """Ragged H (rows off the 16-byte grid by their length) in padded
+    layouts: parity with the oracle for the plain and fused residual forward,
+    and the pads between output rows never written; the forced element-wise
+    tile gives results at parity too."""
+    M = 41 if H <= 8192 else 9
+    d = G.inputs(67 + H, M, H, dtype, wdtype=wdtype, residual=True)
+    wd = G.to_dev(d["w"], wdtype)
+    xd, rd = G.to_dev(d["x"], dtype), G.to_dev(d["r"], dtype)
+    print(f"[gpu] ragged {dtype}/{wdtype} H={H}", flush=True)
+    ybuf, yv = _sentinel_view(M, H, 3, 1, dtype, -77.0)
+    robuf, rov = _sentinel_view(M, H, 1, 2, dtype, -77.0)
+    _, rr = tn.rmsnorm_fwd(xd, wd, 1e-5, out=yv, return_rrms=True)
+    y2, _, rr2 = tn.rmsnorm_fwd_residual(xd, rd, wd, 1e-6, residual_out=rov, return_rrms=True)
+    torch.cuda.synchronize()
+    reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(yv.contiguous(), dtype), rr.cpu().numpy(), 1e-5, dtype,
+                                wdtype=wdtype, name=f"fwd {dtype} H={H}"))
+    reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype), G.to_host(rov.contiguous(), dtype),
+                                      rr2.cpu().numpy(), 1e-6, dtype, wdtype=wdtype, name=f"res {dtype} H={H}"))
+    G.assert_ok(*reps)
+    assert _untouched(ybuf, yv, -77.0) and _untouched(robuf, rov, -77.0)
+    # the element-wise tile, forced: a resident tile of single elements
+    vpt = 8
+    wpr = max(1, -(-H // (64 * vpt)))
+    if wpr <= 16:
+        tn.set_geometry("fwd", vpt, wpr, 1, 0)
+        try:
+            y3, rr3 = tn.rmsnorm_fwd(xd, wd, 1e-5, return_rrms=True)
+            torch.cuda.synchronize()
+        finally:
+            tn.set_geometry("fwd", 0, 0, 0, 0)
+        G.assert_ok(*G.fwd_vs_oracle(d["x"], d["w"], G.to_host(y3, dtype), rr3.cpu().numpy(), 1e-5, dtype,
+                                     wdtype=wdtype, name=f"fwd element tile {dtype} H={H}"))
 
 
 def test_in_place_outputs():

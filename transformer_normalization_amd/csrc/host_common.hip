@@ -195,8 +195,9 @@ void set_override(int which, int a, int b, int c, int64_t d) {
     g_override_any.store(g_override[0].set || g_override[1].set || g_override[2].set);
 }
 
-rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what) {
-    hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what,
+                     size_t shmem) {
+    hipError_t e = hipLaunchKernel(fn, grid, block, args, shmem, stream);
     if (e != hipSuccess) return fail(RMSN_ERR_HIP, "launching %s failed: %s", what, hipGetErrorString(e));
     return RMSN_OK;
 }

@@ -26,6 +26,7 @@ rmsn_status_t device_info(int *cus);
 inline int dtype_bytes(rmsn_dtype_t t) { return t == RMSN_F32 ? 4 : 2; }
 inline bool dtype_valid(int t) { return t == RMSN_F32 || t == RMSN_F16 || t == RMSN_BF16; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned_to(const void *p, int bytes) { return ((uintptr_t)p % (uintptr_t)bytes) == 0; }
 
 // A buffer as the byte range spanned by `rows` rows of `cols` elements,
 // `stride` elements apart, plus what identifies "the same buffer".
@@ -82,7 +83,9 @@ struct Override {
 Override get_override(int which);
 void set_override(int which, int a, int b, int c, int64_t d);
 
-rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what);
+// shmem: dynamic LDS bytes per workgroup
+rmsn_status_t launch(const void *fn, dim3 grid, dim3 block, void **args, hipStream_t stream, const char *what,
+                     size_t shmem = 0);
 
 }  // namespace host
 }  // namespace rmsn

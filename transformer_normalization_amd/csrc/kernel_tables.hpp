@@ -1,7 +1,7 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
-// kernels_bwd.hip, kernels_bwd_residual.hip, kernels_rope.hip, kernels_ln.hip)
+// kernels_fwd_staged*.hip, kernels_bwd.hip, kernels_bwd_residual.hip, kernels_rope.hip, kernels_ln.hip)
 // so that they compile in parallel; the host code only sees these functions.
 #pragma once
 
@@ -10,6 +10,7 @@
 #include "ln_kernels.hpp"
 #include "rmsnorm.h"
 #include "rope_kernels.hpp"
+#include "staged_kernels.hpp"
 
 namespace rmsn {
 
@@ -22,6 +23,10 @@ typedef void (*ln_fn)(const LnParams);
 // accesses per thread; nt: streaming accesses)
 fwd_fn fwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
+// the forward for rows off the 16-byte grid (staged through LDS); vpt:
+// column vectors per thread, as the aligned tile
+fwd_fn fwd_staged_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt);
+fwd_fn fwd_staged_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt);
 // AdaLN: wdt is the format of the weight, scale and shift
 fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);

@@ -130,6 +130,39 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     return g;
 }
 
+// Tile of the staged forward (rows off the 16-byte grid).  There a lane
+// without a vector costs no memory traffic, and the fewer waves a row takes,
+// the more rows a CU holds in flight, so the cost is the row's waves plus
+// 8 x the idle share of its slots, over vpt <= 6 (the register tile of 8 lowers
+// the waves a SIMD holds); two rows share a workgroup only when a row takes a
+// single wave.  Measured on gfx950 (64 Mi-element calls): bf16 H = 4097 ran
+// 59.5 % of peak on 3 x 3 (54.8 % on the aligned path's 3 x 3 with two rows
+// per workgroup), H = 2050 58.5 % on 6 x 1 (39.2 % on 1 x 5), float32
+// H = 4097 64.6 % on 6 x 3 (59.9 % on 2 x 9).  two_pass is set when no tile
+// holds the row.
+Geom pick_staged_geom(Kind kind, int H, int vec) {
+    static const int kStagedVpt[] = {1, 2, 3, 4, 6};
+    Geom g{};
+    g.vec = vec;
+    g.nvec = (H + vec - 1) / vec;
+    double best = 1e30;
+    for (int vpt : kStagedVpt) {
+        const int wpr = (g.nvec + 64 * vpt - 1) / (64 * vpt);
+        if (wpr > max_threads_for(kind, vpt, vec) / 64) continue;
+        const double slots = 64.0 * wpr * vpt;
+        const double cost = wpr + 8.0 * (slots - g.nvec) / slots;
+        if (cost < best) {
+            best = cost;
+            g.vpt = vpt;
+            g.wpr = wpr;
+        }
+    }
+    g.two_pass = best >= 1e30;
+    g.nchunks = 1;
+    g.rpw = g.wpr == 1 ? 2 : 1;
+    return g;
+}
+
 // ---------------------------------------------------------------------------
 // kernel tables
 // ---------------------------------------------------------------------------
@@ -220,9 +253,29 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     if (bias != nullptr) vec_ok = vec_ok && aligned16(bias);
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
-    Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
-    int64_t grid = (M + g.rpw - 1) / g.rpw;
     const Override ov = get_override(0);
+    // Rows off the 16-byte grid, plain and fused residual forms: staged
+    // through LDS on a vector tile, when the weight is 16-byte aligned, every
+    // row pointer is element-aligned, a row holds at least 1 KiB (below that
+    // the element-wise tile measured faster: bf16 H = 257 ran 35.6 % of peak
+    // element-wise, 31.3 % staged; H = 520 65.5 % and 69.5 %) and the row
+    // fits the register tile and the LDS budget.  Otherwise, or with a forced
+    // geometry, the element-wise tile.
+    Geom g{};
+    int64_t lds = 0;
+    bool staged = false;
+    if (!vec_ok && !ov.set && (mode == MODE_PLAIN || mode == MODE_RESID) && H * eb >= 1024 &&
+        (w == nullptr || aligned16(w)) && aligned_to(x, eb) && aligned_to(y, eb) &&
+        (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb))))) {
+        g = pick_staged_geom(kind, (int)H, vecw);
+        lds = (int64_t)g.rpw * (resid ? 2 : 1) * staged_buffer_bytes(g.nvec);
+        staged = !g.two_pass && lds <= kStagedMaxLds;
+    }
+    if (!staged) {
+        g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
+        lds = 0;
+    }
+    int64_t grid = (M + g.rpw - 1) / g.rpw;
     if (ov.set) {
         // bounds first: the products below are then small
         if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16 || ov.c < 0 || ov.c > 16)
@@ -283,7 +336,9 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                       resid ? "layernorm_fwd_residual" : "layernorm_fwd");
     }
-    fwd_fn fn = resid   ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
+    fwd_fn fn = staged  ? (resid ? fwd_staged_lookup_resid(xdt, kwdt, g.vpt, nt)
+                                 : fwd_staged_lookup_plain(xdt, kwdt, g.vpt, nt))
+                : resid ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                 : adaln ? fwd_lookup_adaln(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                         : fwd_lookup_plain(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
@@ -313,6 +368,29 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     p.shift = cond.shift;
     p.cs = cond.cs;
     p.rows_per_cond = cond.rows_per_cond;
+    if (staged) {
+        // one row group per workgroup: launches of at most INT32_MAX
+        // workgroups, each on rows [r0, r0 + rows)
+        const int64_t max_rows = (int64_t)INT32_MAX * g.rpw;
+        for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
+            const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
+            FwdParams q = p;
+            q.x = static_cast<const char *>(x) + r0 * xs * eb;
+            q.y = static_cast<char *>(y) + r0 * ys * eb;
+            if (resid) {
+                q.r = static_cast<const char *>(r) + r0 * rs * eb;
+                if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
+            }
+            if (rrms != nullptr) q.rrms = rrms + r0;
+            q.M = rows;
+            q.iters = 1;
+            void *qargs[] = {&q};
+            if ((st = launch((const void *)fn, dim3((unsigned)((rows + g.rpw - 1) / g.rpw)), dim3(64 * g.wpr * g.rpw),
+                             qargs, stream, resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd", (size_t)lds)) != RMSN_OK)
+                return st;
+        }
+        return RMSN_OK;
+    }
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                   resid ? "rmsnorm_fwd_residual" : adaln ? "rmsnorm_adaln_fwd" : "rmsnorm_fwd");

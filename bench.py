@@ -57,11 +57,22 @@ KERNEL_SOURCES = {
     "adaln": _FWD + ("kernels_adaln.hip", "rmsnorm_api.hip"),
     "rope": ("numerics.hpp", "rope_kernels.hpp", "kernel_tables.hpp", "kernels_rope.hip", "rope_api.hip"),
     "ln_residual": ("numerics.hpp", "ln_kernels.hpp", "kernel_tables.hpp", "kernels_ln.hip", "rmsnorm_api.hip"),
+    "fwd_staged": ("numerics.hpp", "fwd_kernels.hpp", "staged_kernels.hpp", "kernel_tables.hpp",
+                   "kernels_fwd_staged_plain.hip", "rmsnorm_api.hip"),
 }
 # the kernel whose launches the counters describe
 KERNEL_KEY = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
               "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel",
-              "ln_residual": "layernorm_fwd_kernel"}
+              "ln_residual": "layernorm_fwd_kernel", "fwd_staged": "rmsnorm_fwd_staged_kernel"}
+
+
+def kernel_kind(spec) -> str:
+    """The kernel family a workload's calls run: its kind, except that a
+    forward on contiguous rows whose byte length is not a multiple of 16 (so
+    that rows leave the 16-byte grid) runs the LDS-staged forward."""
+    if spec["kind"] == "fwd" and (spec["H"] * _size(spec["dtype"])) % 16:
+        return "fwd_staged"
+    return spec["kind"]
 
 WORKLOADS = {
     "fwd_bf16_8192x4096": ("fwd_bf16_8192x4096", True),
@@ -76,6 +87,7 @@ WORKLOADS = {
     "adaln_bf16_2x4096x2048_tokencond": ("adaln_bf16_2x4096x2048_tokencond", True),
     "rope_bf16_2x8064x32x64": ("rope_bf16_2x8064x32x64", True),
     "rope_bf16_2x4096x32x128": ("rope_bf16_2x4096x32x128", True),
+    "fwd_bf16_8192x4097": ("fwd_bf16_8192x4097", True),
     "ln_residual_f32_16384x1024": ("ln_residual_f32_16384x1024", True),
 }
 
@@ -105,7 +117,7 @@ def stored_traffic(workload: str):
             fields[k.strip()] = v.strip()
     name, _ = WORKLOADS[workload]
     import synthetic
-    if fields.get("kernel_source_digest") != kernel_source_digest(synthetic.WORKLOADS[name]["kind"]):
+    if fields.get("kernel_source_digest") != kernel_source_digest(kernel_kind(synthetic.WORKLOADS[name])):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -245,7 +257,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
     name, weighted = WORKLOADS[workload]
     spec = synthetic.WORKLOADS[name]
     known_kib = x_bytes(spec) / 1024.0
-    kernel_key = KERNEL_KEY[spec["kind"]]
+    kernel_key = KERNEL_KEY[kernel_kind(spec)]
 
     def read(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
@@ -272,7 +284,7 @@ def summarize_pmc(fetch_csv, write_csv, workload):
         "# each scaled by the same counter's reading for device copies of the x tensor",
         f"# ({known_kib:.0f} KiB read and written per copy) in the same run; summary made by",
         f"#   python3 bench.py --workload {workload} --summarize-pmc <fetch csv> <write csv>",
-        f"kernel_source_digest: {kernel_source_digest(spec['kind'])}",
+        f"kernel_source_digest: {kernel_source_digest(kernel_kind(spec))}",
         f"kernel_dispatches: {f_n} (fetch run), {w_n} (write run)",
         f"fetch_size_kib_per_launch: {f_k:.2f}",
         f"write_size_kib_per_launch: {w_k:.2f}",

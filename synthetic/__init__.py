@@ -170,6 +170,9 @@ WORKLOADS = {
     "fwd_f16_32768x2048_outliers": dict(kind="fwd", M=32768, H=2048, dtype="f16", wdtype="f16",
                                         x=(0.0, 2.0), w=(1.0, 0.1), eps=1e-6, seed=1013,
                                         outliers=(0.01, 200.0, 300.0)),
+    # a ragged row length: rows of 8194 bytes leave the 16-byte grid
+    "fwd_bf16_8192x4097": dict(kind="fwd", M=8192, H=4097, dtype="bf16", wdtype="bf16",
+                               x=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1014),
     "fwd_residual_bf16_16384x8192": dict(kind="fwd_residual", M=16384, H=8192, dtype="bf16", wdtype="bf16",
                                          x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1004),
     "bwd_bf16_8192x6144": dict(kind="bwd", M=8192, H=6144, dtype="bf16", wdtype="bf16",

@@ -53,6 +53,28 @@ def test_workload_adaln(name):
                                    chunk=4096, name=name))
 
 
+@pytest.mark.parametrize("B,S", [(3, 6000), (3, 6001), (16, 1100)])
+def test_per_batch_rows_walked_by_each_row_group(B, S):
+    """Per-batch conditioning on a large grid: each row group walks 4 rows
+    a quarter of the call apart, so its rows cross batch boundaries (the
+    conditioning rows are reloaded there) and the last iteration runs past
+    M (ragged: 3 x 6001 rows is an odd number of two-row groups).  Parity
+    with the oracle and the same bits as the one-row-per-row-group grid of
+    the same tile."""
+    H, dt = 2048, "bf16"
+    M = B * S
+    d = G.inputs(470 + S, M, H, dt)
+    sc = synthetic.normal_tensor(470 + S, synthetic.STREAM_SCALE, (B, H), dt, 0.0, 0.5)
+    sh = synthetic.normal_tensor(470 + S, synthetic.STREAM_SHIFT, (B, H), dt, 0.0, 0.5)
+    print(f"[gpu] adaln per-batch walk B={B} S={S}", flush=True)
+    y, rr = run(d["x"], d["w"], sc, sh, B, S, 1e-6, dt)
+    G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, S, y, rr, 1e-6, dt, chunk=S * max(1, 4096 // S),
+                                   name=f"adaln walk {B}x{S}"))
+    tn.set_geometry("fwd", 2, 2, 2, 0)  # the same tile, one row per row group
+    y1, rr1 = run(d["x"], d["w"], sc, sh, B, S, 1e-6, dt)
+    assert np.array_equal(y, y1) and np.array_equal(rr, rr1)
+
+
 @pytest.mark.parametrize("pdtype", ["same", "f32"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 3072, 4097, 8192, 16384, 20000])  # 16384: capped tile

@@ -21,11 +21,10 @@
 //     aligned path's tree for the tile; the tile depends on H only, so any
 //     two layouts of the same rows (offsets, row pitches) give the same bits.
 //     Elements past H count as 0, as the aligned path's padding vectors do.
-//   * The row is read from LDS twice (for the sum, then for the outputs)
-//     instead of being held in registers, so a thread holds little more than
-//     the weight: more rows are in flight per CU.  Each thread writes its
-//     outputs over its own input bytes in LDS, then the output row is copied
-//     out: every aligned 16-byte block lying wholly inside it with one
+//   * A thread holds its packed vectors (and the weight) in registers from
+//     the sum to the outputs, as the aligned path does.  Each thread writes
+//     its outputs over its own input bytes in LDS, then the output row is
+//     copied out: every aligned 16-byte block lying wholly inside it with one
 //     16-byte store (its bytes joined from LDS as above), and the at most two
 //     blocks it shares with its neighbours element by element, so nothing
 //     outside the row is written.
@@ -202,24 +201,24 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
         }
     }
 
-    // pass 1: sum of squares
+    // pass 1: sum of squares; the packed vectors stay in registers for pass 2
     float acc = 0.0f;
+    Raw<XDT, VEC> xr[VPT], rr[RESID ? VPT : 1];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
-        Raw<XDT, VEC> xr, rr;
         if (v < p.nvec) {
-            xr.v[0] = lds_read16(lx, dx + 16 * v);
-            if constexpr (RESID) rr.v[0] = lds_read16(lr, dr + 16 * v);
+            xr[k].v[0] = lds_read16(lx, dx + 16 * v);
+            if constexpr (RESID) rr[k].v[0] = lds_read16(lr, dr + 16 * v);
         } else {
-            xr.zero();
-            if constexpr (RESID) rr.zero();
+            xr[k].zero();
+            if constexpr (RESID) rr[k].zero();
         }
         float hv[VEC];
-        xr.widen_to(hv);
+        xr[k].widen_to(hv);
         if constexpr (RESID) {
             float rv[VEC];
-            rr.widen_to(rv);
+            rr[k].widen_to(rv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
         }
@@ -230,7 +229,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
     const float rs = fast_rsqrt(ss * p.inv_h + p.eps);
     if (p.rrms != nullptr && valid && t == 0) p.rrms[row] = rs;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) wr[k].opaque();
+    for (int k = 0; k < VPT; ++k) {
+        wr[k].opaque();
+        xr[k].opaque();
+        if constexpr (RESID) rr[k].opaque();
+    }
 
     // pass 2: outputs over the thread's own input bytes (values past H stay
     // in the buffer and are never copied out)
@@ -238,15 +241,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
         if (v < p.nvec) {
-            Raw<XDT, VEC> xr;
-            xr.v[0] = lds_read16(lx, dx + 16 * v);
             float hv[VEC], wv[VEC], o[VEC];
-            xr.widen_to(hv);
+            xr[k].widen_to(hv);
             if constexpr (RESID) {
-                Raw<XDT, VEC> rr;
-                rr.v[0] = lds_read16(lr, dr + 16 * v);
                 float rv[VEC];
-                rr.widen_to(rv);
+                rr[k].widen_to(rv);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                 if (p.ro != nullptr) {

@@ -202,3 +202,24 @@ def adaln_vs_oracle(x, w, scale, shift, rows_per_cond, y_host, rrms_host, eps, d
             parity.check_dx16(rep_y, y_host[r0:r1], yref, terms, dtype, oracle.encode, oracle.decode, r0 * H)
         parity.check_f32(rep_r, rrms_host[r0:r1], rref, r0)
     return rep_y, rep_r
+
+
+def sentinel_view(M, H, pad, offset, dtype, fill):
+    """(M, H) view at element `offset` of a buffer with rows of H + pad,
+    every element first set to `fill`."""
+    import torch
+
+    buf = torch.full((offset + M * (H + pad) + 16,), fill, dtype=torch_dtype(dtype), device=DEV)
+    return buf, buf[offset:offset + M * (H + pad)].view(M, H + pad)[:, :H]
+
+
+def untouched(buf, view, fill):
+    """Every element of buf outside `view` still holds `fill`."""
+    import torch
+
+    mask = torch.ones(buf.numel(), dtype=torch.bool, device=buf.device)
+    off = view.storage_offset() - buf.storage_offset()
+    rows = torch.arange(view.shape[0], device=buf.device)[:, None] * view.stride(0)
+    cols = torch.arange(view.shape[1], device=buf.device)[None, :]
+    mask[(off + rows + cols).reshape(-1)] = False
+    return bool(torch.all(buf[mask] == fill))

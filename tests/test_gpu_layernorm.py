@@ -150,10 +150,10 @@ def test_ln_streaming_and_determinism():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ln_misaligned_and_strided_rows(dtype):
-    """Odd H, and a residual one element into its buffer, take single
-    elements (another reduction order: within tolerance of the oracle);
-    row strides padded by whole 16-byte vectors give the same bits as
-    contiguous rows."""
+    """Odd H, and a residual one element into its buffer, leave the
+    16-byte grid (another tile and reduction order: within tolerance of the
+    oracle); row strides padded by whole 16-byte vectors give the same bits
+    as contiguous rows."""
     M, H = 129, 1023
     d = G.inputs(46, M, H, dtype, residual=True)
     b = bias_of(46, H, dtype)
@@ -178,6 +178,56 @@ def test_ln_misaligned_and_strided_rows(dtype):
     torch.cuda.synchronize()
     G.assert_ok(*G.ln_vs_oracle(d["x"], d["r"], d["w"], b, G.to_host(y, dtype), G.to_host(ro, dtype),
                                 mean.cpu().numpy(), rstd.cpu().numpy(), 1e-5, dtype, name=f"ln misaligned {dtype}"))
+
+
+@pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
+@pytest.mark.parametrize("H", [600, 2049, 4096, 6143])
+def test_ln_rows_off_the_grid(dtype, wdtype, H):
+    """Rows off the 16-byte grid (ragged H, or views at element offsets)
+    go through LDS on a tile that depends on H only: every layout gives the
+    same bits, at parity with the oracle, and nothing around the output rows
+    is written; the forced element-wise tile is at parity too."""
+    M = 67
+    d = G.inputs(5100 + H, M, H, dtype, wdtype=wdtype, residual=True)
+    b = bias_of(5100 + H, H, wdtype)
+    wt, bt = G.to_dev(d["w"], wdtype), G.to_dev(b, wdtype)
+    first = None
+    for pad, xoff, yoff in ((1, 1, 0), (0, 3, 1), (5, 0, 7), (8, 1, 1)):
+        print(f"[gpu] ln staged {dtype}/{wdtype} H={H} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
+        _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
+        _, rv = G.sentinel_view(M, H, pad + 1, xoff + 2, dtype, 0.0)
+        xv.copy_(G.to_dev(d["x"], dtype))
+        rv.copy_(G.to_dev(d["r"], dtype))
+        ybuf, yv = G.sentinel_view(M, H, pad + 3, yoff, dtype, -77.0)
+        robuf, rov = G.sentinel_view(M, H, pad, yoff + 1, dtype, -77.0)
+        _, _, mean, rstd = tn.layernorm_fwd_residual(xv, rv, wt, bt, 1e-5, out=yv, residual_out=rov,
+                                                     return_stats=True)
+        y2 = tn.layernorm_fwd(xv, wt, bt, 1e-5)
+        torch.cuda.synchronize()
+        assert G.untouched(ybuf, yv, -77.0) and G.untouched(robuf, rov, -77.0), (pad, xoff, yoff)
+        got = [G.to_host(yv.contiguous(), dtype), G.to_host(rov.contiguous(), dtype), mean.cpu().numpy(),
+               rstd.cpu().numpy(), G.to_host(y2, dtype)]
+        if first is None:
+            first = got
+            G.assert_ok(*G.ln_vs_oracle(d["x"], d["r"], d["w"], b, got[0], got[1], got[2], got[3], 1e-5, dtype,
+                                        wdtype, name=f"ln staged {dtype} H={H}"))
+            G.assert_ok(*G.ln_vs_oracle(d["x"], None, d["w"], b, got[4], None, None, None, 1e-5, dtype, wdtype,
+                                        name=f"ln staged plain {dtype} H={H}"))
+        else:
+            for a, c in zip(got, first):
+                assert np.array_equal(a, c), (pad, xoff, yoff)
+    # ragged H: the contiguous call leaves the grid too, and a forced tile
+    # keeps it on single elements
+    vpt = 8
+    wpr = -(-H // (64 * vpt))
+    if (H * (4 if dtype == "f32" else 2)) % 16 and 64 * wpr <= 512:
+        tn.set_geometry("fwd", vpt, wpr, 1, 0)
+        try:
+            y3, ro3, m3, r3 = run_ln(d["x"], d["r"], d["w"], b, 1e-5, dtype, wdtype)
+        finally:
+            tn.set_geometry("fwd")
+        G.assert_ok(*G.ln_vs_oracle(d["x"], d["r"], d["w"], b, y3, ro3, m3, r3, 1e-5, dtype, wdtype,
+                                    name=f"ln element tile {dtype} H={H}"))
 
 
 @pytest.mark.parametrize("H", [4096, 65536])

@@ -301,23 +301,6 @@ def test_misaligned_rows(dtype, stream):
         G.assert_ok(*reps)
 
 
-def _sentinel_view(M, H, pad, offset, dtype, fill):
-    """(M, H) view at element `offset` of a buffer with rows of H + pad,
-    every element first set to `fill`."""
-    buf = torch.full((offset + M * (H + pad) + 16,), fill, dtype=G.torch_dtype(dtype), device=G.DEV)
-    return buf, buf[offset:offset + M * (H + pad)].view(M, H + pad)[:, :H]
-
-
-def _untouched(buf, view, fill):
-    """Every element of buf outside `view` still holds `fill`."""
-    mask = torch.ones(buf.numel(), dtype=torch.bool, device=buf.device)
-    off = view.storage_offset() - buf.storage_offset()
-    rows = torch.arange(view.shape[0], device=buf.device)[:, None] * view.stride(0)
-    cols = torch.arange(view.shape[1], device=buf.device)[None, :]
-    mask[(off + rows + cols).reshape(-1)] = False
-    return bool(torch.all(buf[mask] == fill))
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_misaligned_views_same_bits_at_any_offset(dtype):
     """Rows off the 16-byte grid go through LDS on a vector tile that depends
@@ -333,17 +316,17 @@ def test_misaligned_views_same_bits_at_any_offset(dtype):
     first = None
     for pad, xoff, yoff in ((1, 0, 1), (0, 1, 3), (3, 1, 0), (5, 7, 2), (8, 3, 5)):
         print(f"[gpu] staged views {dtype} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
-        _, xv = _sentinel_view(M, H, pad, xoff, dtype, 0.0)
-        _, rv = _sentinel_view(M, H, pad, xoff + 1, dtype, 0.0)
+        _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
+        _, rv = G.sentinel_view(M, H, pad, xoff + 1, dtype, 0.0)
         xv.copy_(xd)
         rv.copy_(rd)
-        ybuf, yv = _sentinel_view(M, H, pad + 2, yoff, dtype, -77.0)
-        robuf, rov = _sentinel_view(M, H, pad, yoff + 1, dtype, -77.0)
+        ybuf, yv = G.sentinel_view(M, H, pad + 2, yoff, dtype, -77.0)
+        robuf, rov = G.sentinel_view(M, H, pad, yoff + 1, dtype, -77.0)
         _, rr = tn.rmsnorm_fwd(xv, wd, 1e-5, out=yv, return_rrms=True)
         y2, _, rr2 = tn.rmsnorm_fwd_residual(xv, rv, wd, 1e-6, residual_out=rov, return_rrms=True)
         torch.cuda.synchronize()
         got = (bits(yv.contiguous()), rr, bits(y2), bits(rov.contiguous()), rr2)
-        assert _untouched(ybuf, yv, -77.0) and _untouched(robuf, rov, -77.0), (pad, xoff, yoff)
+        assert G.untouched(ybuf, yv, -77.0) and G.untouched(robuf, rov, -77.0), (pad, xoff, yoff)
         if first is None:
             first = got
             reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(yv.contiguous(), dtype), rr.cpu().numpy(), 1e-5,
@@ -369,8 +352,8 @@ def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
     wd = G.to_dev(d["w"], wdtype)
     xd, rd = G.to_dev(d["x"], dtype), G.to_dev(d["r"], dtype)
     print(f"[gpu] ragged {dtype}/{wdtype} H={H}", flush=True)
-    ybuf, yv = _sentinel_view(M, H, 3, 1, dtype, -77.0)
-    robuf, rov = _sentinel_view(M, H, 1, 2, dtype, -77.0)
+    ybuf, yv = G.sentinel_view(M, H, 3, 1, dtype, -77.0)
+    robuf, rov = G.sentinel_view(M, H, 1, 2, dtype, -77.0)
     _, rr = tn.rmsnorm_fwd(xd, wd, 1e-5, out=yv, return_rrms=True)
     y2, _, rr2 = tn.rmsnorm_fwd_residual(xd, rd, wd, 1e-6, residual_out=rov, return_rrms=True)
     torch.cuda.synchronize()
@@ -379,7 +362,7 @@ def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
     reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype), G.to_host(rov.contiguous(), dtype),
                                       rr2.cpu().numpy(), 1e-6, dtype, wdtype=wdtype, name=f"res {dtype} H={H}"))
     G.assert_ok(*reps)
-    assert _untouched(ybuf, yv, -77.0) and _untouched(robuf, rov, -77.0)
+    assert G.untouched(ybuf, yv, -77.0) and G.untouched(robuf, rov, -77.0)
     # the element-wise tile, forced: a resident tile of single elements
     vpt = 8
     wpr = max(1, -(-H // (64 * vpt)))

@@ -15,7 +15,6 @@ fwd_fn staged_for(int vpt) {
     case 3: return rmsnorm_fwd_staged_kernel<XDT, WDT, 3, R, NT, fwd_max_threads(3 * V, R ? 1 : 0)>;
     case 4: return rmsnorm_fwd_staged_kernel<XDT, WDT, 4, R, NT, fwd_max_threads(4 * V, R ? 1 : 0)>;
     case 6: return rmsnorm_fwd_staged_kernel<XDT, WDT, 6, R, NT, fwd_max_threads(6 * V, R ? 1 : 0)>;
-    case 8: return rmsnorm_fwd_staged_kernel<XDT, WDT, 8, R, NT, fwd_max_threads(8 * V, R ? 1 : 0)>;
     default: return nullptr;
     }
 }

@@ -173,6 +173,27 @@ Geom pick_staged_geom(Kind kind, int H, int vec) {
 // forward (plain and fused residual)
 // ---------------------------------------------------------------------------
 
+// The staged kernels take one row group per workgroup and have no row loop:
+// a call is split into launches of at most INT32_MAX workgroups, each on rows
+// [r0, r0 + rows) through pointers that `shift` moves to row r0.
+template <class Params, class Shift>
+rmsn_status_t launch_row_chunks(const void *fn, const Params &p, int64_t M, const Geom &g, int64_t lds,
+                                hipStream_t stream, const char *what, Shift shift) {
+    const int64_t max_rows = (int64_t)INT32_MAX * g.rpw;
+    for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
+        const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
+        Params q = p;
+        shift(q, r0);
+        q.M = rows;
+        q.iters = 1;
+        void *args[] = {&q};
+        const rmsn_status_t st = launch(fn, dim3((unsigned)((rows + g.rpw - 1) / g.rpw)), dim3(64 * g.wpr * g.rpw),
+                                        args, stream, what, (size_t)lds);
+        if (st != RMSN_OK) return st;
+    }
+    return RMSN_OK;
+}
+
 // Conditioning rows of an AdaLN call (scale and shift share the layout).
 struct Cond {
     const void *scale = nullptr;
@@ -254,8 +275,9 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     const Override ov = get_override(0);
-    // Rows off the 16-byte grid, plain and fused residual forms: staged
-    // through LDS on a vector tile, when the weight is 16-byte aligned, every
+    // Rows off the 16-byte grid, RMSNorm and LayerNorm, plain and fused
+    // residual forms: staged through LDS on a vector tile, when the weight
+    // (and bias) is 16-byte aligned, every
     // row pointer is element-aligned, a row holds at least 1 KiB (below that
     // the element-wise tile measured faster: bf16 H = 257 ran 35.6 % of peak
     // element-wise, 31.3 % staged; H = 520 65.5 % and 69.5 %) and the row
@@ -264,8 +286,8 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     Geom g{};
     int64_t lds = 0;
     bool staged = false;
-    if (!vec_ok && !ov.set && (mode == MODE_PLAIN || mode == MODE_RESID) && H * eb >= 1024 &&
-        (w == nullptr || aligned16(w)) && aligned_to(x, eb) && aligned_to(y, eb) &&
+    if (!vec_ok && !ov.set && !adaln && H * eb >= 1024 && (w == nullptr || aligned16(w)) &&
+        (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
         (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb))))) {
         g = pick_staged_geom(kind, (int)H, vecw);
         lds = (int64_t)g.rpw * (resid ? 2 : 1) * staged_buffer_bytes(g.nvec);
@@ -307,7 +329,8 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     const rmsn_dtype_t kwdt = (w || adaln || bias) ? wdt : xdt;
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if (ln) {
-        ln_fn fn = ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
+        ln_fn fn = staged ? ln_staged_lookup(xdt, kwdt, g.vpt, nt, resid)
+                          : ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
         if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
         if ((st = device_info(&cus)) != RMSN_OK) return st;
         LnParams p;
@@ -332,6 +355,18 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         p.nchunks = g.nchunks;
         p.eps = eps;
         p.inv_h = (float)(1.0 / (double)H);
+        if (staged)
+            return launch_row_chunks((const void *)fn, p, M, g, lds, stream,
+                                     resid ? "layernorm_fwd_residual" : "layernorm_fwd", [&](LnParams &q, int64_t r0) {
+                                         q.x = static_cast<const char *>(x) + r0 * xs * eb;
+                                         q.y = static_cast<char *>(y) + r0 * ys * eb;
+                                         if (resid) {
+                                             q.r = static_cast<const char *>(r) + r0 * rs * eb;
+                                             if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
+                                         }
+                                         if (mean != nullptr) q.mean = mean + r0;
+                                         if (rrms != nullptr) q.rstd = rrms + r0;
+                                     });
         void *args[] = {&p};
         return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                       resid ? "layernorm_fwd_residual" : "layernorm_fwd");
@@ -381,29 +416,17 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     p.shift = cond.shift;
     p.cs = cond.cs;
     p.rows_per_cond = cond.rows_per_cond;
-    if (staged) {
-        // one row group per workgroup: launches of at most INT32_MAX
-        // workgroups, each on rows [r0, r0 + rows)
-        const int64_t max_rows = (int64_t)INT32_MAX * g.rpw;
-        for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
-            const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
-            FwdParams q = p;
-            q.x = static_cast<const char *>(x) + r0 * xs * eb;
-            q.y = static_cast<char *>(y) + r0 * ys * eb;
-            if (resid) {
-                q.r = static_cast<const char *>(r) + r0 * rs * eb;
-                if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
-            }
-            if (rrms != nullptr) q.rrms = rrms + r0;
-            q.M = rows;
-            q.iters = 1;
-            void *qargs[] = {&q};
-            if ((st = launch((const void *)fn, dim3((unsigned)((rows + g.rpw - 1) / g.rpw)), dim3(64 * g.wpr * g.rpw),
-                             qargs, stream, resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd", (size_t)lds)) != RMSN_OK)
-                return st;
-        }
-        return RMSN_OK;
-    }
+    if (staged)
+        return launch_row_chunks((const void *)fn, p, M, g, lds, stream, resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd",
+                                 [&](FwdParams &q, int64_t r0) {
+                                     q.x = static_cast<const char *>(x) + r0 * xs * eb;
+                                     q.y = static_cast<char *>(y) + r0 * ys * eb;
+                                     if (resid) {
+                                         q.r = static_cast<const char *>(r) + r0 * rs * eb;
+                                         if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
+                                     }
+                                     if (rrms != nullptr) q.rrms = rrms + r0;
+                                 });
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                   resid ? "rmsnorm_fwd_residual" : adaln ? "rmsnorm_adaln_fwd" : "rmsnorm_fwd");

@@ -1,11 +1,13 @@
-// staged_kernels.hpp -- gfx950 forward RMSNorm (plain and fused residual) for
-// rows that are not 16-byte aligned: H not a whole number of 16-byte
-// vectors, or a base or row stride off the 16-byte grid.
+// staged_kernels.hpp -- gfx950 forward RMSNorm and LayerNorm (plain and
+// fused residual) for rows that are not 16-byte aligned: H not a whole number
+// of 16-byte vectors, or a base or row stride off the 16-byte grid.
 //
-// What is computed is exactly the forward of fwd_kernels.hpp, resident tile:
-// the same float32 expressions in the same order ("Skill: Write a Triton
-// RMSNorm Kernel", "Required reasoning process" steps 1-11).  Only the
-// movement of the data differs:
+// What is computed is exactly the forward of fwd_kernels.hpp (and of
+// ln_kernels.hpp for LayerNorm), resident tile: the same float32 expressions
+// in the same order ("Skill: Write a Triton RMSNorm Kernel", "Required
+// reasoning process" steps 1-11; LayerNorm: "SpeedROCm: shape-aware Triton
+// acceleration for Transformer inference", "How the solution addresses the
+// problem", item 4).  Only the movement of the data differs:
 //   * A row group of 64*wpr threads owns one row; a workgroup holds rpw row
 //     groups, each with its own LDS buffers, and handles rpw consecutive rows
 //     (no loop over rows: straight-line code keeps few registers live; a
@@ -34,6 +36,7 @@
 #pragma once
 
 #include "fwd_kernels.hpp"
+#include "ln_kernels.hpp"
 
 namespace rmsn {
 
@@ -144,13 +147,32 @@ __device__ __forceinline__ void unstage_row(const unsigned char *l, int src, voi
     }
 }
 
+// The weight (and bias) of a staged kernel as column vectors: a 16-byte
+// chunk is loaded only if it holds an element below H.
+template <int WDT, int VEC, int VPT>
+__device__ __forceinline__ void load_param_staged(Raw<WDT, VEC> *pr, const void *param, int t, int row_threads,
+                                                  int nvec, int H) {
+    constexpr int WPC = 16 / Fmt<WDT>::bytes;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int v = t + k * row_threads;
+        if (param != nullptr && v < nvec) {
+#pragma unroll
+            for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c) {
+                const int j0 = v * VEC + c * WPC;
+                if (j0 < H)
+                    pr[k].v[c] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(param) +
+                                                                   (int64_t)j0 * Fmt<WDT>::bytes);
+            }
+        }
+    }
+}
+
 template <int XDT, int WDT, int VPT, bool RESID, bool NT, int MAXT>
 __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParams p) {
     constexpr int ES = Fmt<XDT>::bytes;
     constexpr int VEC = 16 / ES;
-    constexpr int WES = Fmt<WDT>::bytes;
-    constexpr int WPC = 16 / WES;  // weight elements per 16-byte chunk
-    constexpr int BLK = VPT + 1;   // a row spans at most nvec + 1 <= 64*wpr*VPT + 1 blocks
+    constexpr int BLK = VPT + 1;  // a row spans at most nvec + 1 <= 64*wpr*VPT + 1 blocks
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red[16];
     const int row_threads = 64 * p.wpr;
@@ -173,18 +195,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
 
     Raw<WDT, VEC> wr[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = t + k * row_threads;
-        wr[k].fill_one();
-        if (p.w != nullptr && v < p.nvec) {
-#pragma unroll
-            for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c) {
-                const int j0 = v * VEC + c * WPC;
-                if (j0 < p.H)
-                    wr[k].v[c] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.w) + (int64_t)j0 * WES);
-            }
-        }
-    }
+    for (int k = 0; k < VPT; ++k) wr[k].fill_one();
+    load_param_staged<WDT, VEC, VPT>(wr, p.w, t, row_threads, p.nvec, p.H);
 
     sx.store(lx, t, row_threads);
     if constexpr (RESID) sr.store(lr, t, row_threads);
@@ -258,6 +270,154 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
             wr[k].widen_to(wv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
+            u32x4 q;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));
+            lds_write16(lx, dx + 16 * v, q);
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        unstage_row<XDT, NT, BLK>(lx, dx, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
+        if constexpr (RESID)
+            if (p.ro != nullptr)
+                unstage_row<XDT, NT, BLK>(lr, dr, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
+                                          row_threads);
+    }
+}
+
+// LayerNorm (plain or fused with the residual add) on rows off the 16-byte
+// grid: the staging of rmsnorm_fwd_staged_kernel around the two reductions
+// of layernorm_fwd_kernel.  Elements past H read as 0, which adds nothing to
+// the sum; the centred sum skips them.
+template <int XDT, int WDT, int VPT, bool RESID, bool NT, int MAXT>
+__global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnParams p) {
+    constexpr int ES = Fmt<XDT>::bytes;
+    constexpr int VEC = 16 / ES;
+    constexpr int BLK = VPT + 1;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float red[2][16];
+    const int row_threads = 64 * p.wpr;
+    const int slot = threadIdx.x / row_threads;
+    const int t = threadIdx.x - slot * row_threads;
+    const int wave_in_row = t >> 6;
+    const int64_t buf = staged_buffer_bytes(p.nvec);
+    unsigned char *lx = smem + (RESID ? 2 : 1) * slot * buf;
+    unsigned char *lr = lx + buf;
+    const int64_t row_bytes = (int64_t)p.H * ES;
+
+    const int64_t row = (int64_t)blockIdx.x * p.rpw + slot;
+    const bool valid = row < p.M;
+    Staged<NT, BLK> sx;
+    Staged<NT, RESID ? BLK : 1> sr;
+    sx.load(static_cast<const char *>(p.x) + row * p.xs * ES, valid, row_bytes, t, row_threads);
+    if constexpr (RESID) sr.load(static_cast<const char *>(p.r) + row * p.rs * ES, valid, row_bytes, t, row_threads);
+
+    Raw<WDT, VEC> wr[VPT], br[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        wr[k].fill_one();
+        br[k].zero();
+    }
+    load_param_staged<WDT, VEC, VPT>(wr, p.w, t, row_threads, p.nvec, p.H);
+    load_param_staged<WDT, VEC, VPT>(br, p.b, t, row_threads, p.nvec, p.H);
+
+    sx.store(lx, t, row_threads);
+    if constexpr (RESID) sr.store(lr, t, row_threads);
+    const int dx = sx.delta;
+    const int dr = RESID ? sr.delta : 0;
+    __syncthreads();
+    if (t == (p.nvec - 1) % row_threads) {
+        for (int off = (int)row_bytes; off < 16 * p.nvec; off += ES) {
+            *reinterpret_cast<typename Fmt<XDT>::T *>(lx + dx + off) = 0;
+            if constexpr (RESID) *reinterpret_cast<typename Fmt<XDT>::T *>(lr + dr + off) = 0;
+        }
+    }
+
+    Raw<XDT, VEC> xr[VPT], rr[RESID ? VPT : 1];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int v = t + k * row_threads;
+        if (v < p.nvec) {
+            xr[k].v[0] = lds_read16(lx, dx + 16 * v);
+            if constexpr (RESID) rr[k].v[0] = lds_read16(lr, dr + 16 * v);
+        } else {
+            xr[k].zero();
+            if constexpr (RESID) rr[k].zero();
+        }
+    }
+    auto widen_h = [&](int k, float *hv) {
+        xr[k].widen_to(hv);
+        if constexpr (RESID) {
+            float rv[VEC];
+            rr[k].widen_to(rv);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+        }
+    };
+    float s1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        float hv[VEC];
+        widen_h(k, hv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) s1 += hv[e];
+    }
+    const float mean = row_sum(s1, p.wpr, wave_in_row, &red[0][slot * p.wpr]) * p.inv_h;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        xr[k].opaque();
+        if constexpr (RESID) rr[k].opaque();
+    }
+    float s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int v = t + k * row_threads;
+        float hv[VEC];
+        widen_h(k, hv);
+        if (v < p.nvec) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if (v * VEC + e < p.H) {  // elements past H are 0, not mean
+                    const float d = hv[e] - mean;
+                    s2 = __builtin_fmaf(d, d, s2);
+                }
+            }
+        }
+    }
+    const float var = row_sum(s2, p.wpr, wave_in_row, &red[1][slot * p.wpr]) * p.inv_h;
+    const float rs = fast_rsqrt(var + p.eps);
+    if (valid && t == 0) {
+        if (p.mean != nullptr) p.mean[row] = mean;
+        if (p.rstd != nullptr) p.rstd[row] = rs;
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        xr[k].opaque();
+        if constexpr (RESID) rr[k].opaque();
+        wr[k].opaque();
+        br[k].opaque();
+    }
+
+    // outputs over the thread's own input bytes, then copied out
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int v = t + k * row_threads;
+        if (v < p.nvec) {
+            float hv[VEC], wv[VEC], bv[VEC], o[VEC];
+            widen_h(k, hv);
+            if constexpr (RESID) {
+                if (p.ro != nullptr) {
+                    u32x4 q;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(hv + w * (4 / ES));
+                    lds_write16(lr, dr + 16 * v, q);
+                }
+            }
+            wr[k].widen_to(wv);
+            br[k].widen_to(bv);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
             u32x4 q;
 #pragma unroll
             for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));

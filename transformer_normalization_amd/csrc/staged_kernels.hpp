@@ -113,6 +113,22 @@ struct Staged {
     }
 };
 
+// Elements past H read as 0: bytes [H*ES, nvec*16) of the row's last vector
+// (at LDS offset delta) are read by the vector's owner alone -- a
+// neighbour's read of a shared dword uses only its own bytes -- so that
+// thread clears them, for x and (RESID) the residual, after the barrier that
+// follows staging and before its own reads.
+template <int XDT, bool RESID>
+__device__ __forceinline__ void zero_tail(unsigned char *lx, int dx, unsigned char *lr, int dr, int64_t row_bytes,
+                                          int nvec, int t, int row_threads) {
+    using T = typename Fmt<XDT>::T;
+    if (t != (nvec - 1) % row_threads) return;
+    for (int off = (int)row_bytes; off < 16 * nvec; off += Fmt<XDT>::bytes) {
+        *reinterpret_cast<T *>(lx + dx + off) = 0;
+        if constexpr (RESID) *reinterpret_cast<T *>(lr + dr + off) = 0;
+    }
+}
+
 // Copy the row held in l at byte offset `src` (row byte i at l + src + i) to
 // the row at `row`: whole aligned blocks with 16-byte stores, the blocks
 // shared with the neighbours element by element.  At most BLK blocks per
@@ -203,15 +219,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
     const int dx = sx.delta;
     const int dr = RESID ? sr.delta : 0;
     __syncthreads();
-    // Elements past H read as 0: bytes [H*ES, nvec*16) of the last vector
-    // are read by its owner alone (a neighbour's read of a shared dword uses
-    // only its own bytes), which clears them first.
-    if (t == (p.nvec - 1) % row_threads) {
-        for (int off = (int)row_bytes; off < 16 * p.nvec; off += ES) {
-            *reinterpret_cast<typename Fmt<XDT>::T *>(lx + dx + off) = 0;
-            if constexpr (RESID) *reinterpret_cast<typename Fmt<XDT>::T *>(lr + dr + off) = 0;
-        }
-    }
+    zero_tail<XDT, RESID>(lx, dx, lr, dr, row_bytes, p.nvec, t, row_threads);
 
     // pass 1: sum of squares; the packed vectors stay in registers for pass 2
     float acc = 0.0f;
@@ -327,12 +335,7 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
     const int dx = sx.delta;
     const int dr = RESID ? sr.delta : 0;
     __syncthreads();
-    if (t == (p.nvec - 1) % row_threads) {
-        for (int off = (int)row_bytes; off < 16 * p.nvec; off += ES) {
-            *reinterpret_cast<typename Fmt<XDT>::T *>(lx + dx + off) = 0;
-            if constexpr (RESID) *reinterpret_cast<typename Fmt<XDT>::T *>(lr + dr + off) = 0;
-        }
-    }
+    zero_tail<XDT, RESID>(lx, dx, lr, dr, row_bytes, p.nvec, t, row_threads);
 
     Raw<XDT, VEC> xr[VPT], rr[RESID ? VPT : 1];
 #pragma unroll

@@ -4,8 +4,8 @@
 
 namespace rmsn {
 
-__global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restrict__ partial, int P, int H,
-                                                            float *__restrict__ dw) {
+__global__ void __launch_bounds__(kFinCols * kFinSlices) rmsnorm_dw_finalize(const float *__restrict__ partial, int P,
+                                                                             int H, float *__restrict__ dw) {
     __shared__ float sums[kFinSlices][kFinCols];
     const int c = threadIdx.x % kFinCols;
     const int s = threadIdx.x / kFinCols;
@@ -13,12 +13,12 @@ __global__ void __launch_bounds__(1024) rmsnorm_dw_finalize(const float *__restr
     float acc = 0.0f;
     if (col < H) {
         int q = s;
-        for (; q + kFinSlices * 7 < P; q += kFinSlices * 8) {
-            float v[8];
+        for (; q + kFinSlices * (kFinBatch - 1) < P; q += kFinSlices * kFinBatch) {
+            float v[kFinBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(q + kFinSlices * j) * H + col];
+            for (int j = 0; j < kFinBatch; ++j) v[j] = partial[(int64_t)(q + kFinSlices * j) * H + col];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc += v[j];
+            for (int j = 0; j < kFinBatch; ++j) acc += v[j];
         }
         for (; q < P; q += kFinSlices) acc += partial[(int64_t)q * H + col];
     }

@@ -516,7 +516,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *none = nullptr;
         int P = 0, Hi = (int)H;
         void *args[] = {(void *)&none, &P, &Hi, &dw};
-        return launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), args,
+        return launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinSlices), args,
                       stream, "rmsnorm_dw_finalize");
     }
 
@@ -594,7 +594,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *part = p.partial;
         int Pi = (int)P, Hi = (int)H;
         void *fargs[] = {(void *)&part, &Pi, &Hi, &dw};
-        if ((st = launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(1024), fargs,
+        if ((st = launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinSlices), fargs,
                          stream, "rmsnorm_dw_finalize")) != RMSN_OK)
             return st;
     }

@@ -230,7 +230,7 @@ def test_ln_rows_off_the_grid(dtype, wdtype, H):
                                     name=f"ln element tile {dtype} H={H}"))
 
 
-@pytest.mark.parametrize("H", [4096, 65536])
+@pytest.mark.parametrize("H", [4096, 65536, 4097])  # 4097: rows off the 16-byte grid
 def test_ln_in_place(H):
     M = 64 if H <= 8192 else 4
     d = G.inputs(48, M, H, "bf16", residual=True)

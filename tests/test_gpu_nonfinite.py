@@ -62,9 +62,10 @@ def same_classes(got64, ref64, what):
     assert np.array_equal(got64[fin], ref64[fin]), f"{what}: finite values differ"
 
 
+@pytest.mark.parametrize("H", [4096, 4097], ids=["aligned", "staged"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_forward(dtype):
-    M, H = 16, 4096
+def test_forward(dtype, H):
+    M = 16
     d = G.inputs(501, M, H, dtype)
     x = plant(d["x"], dtype)
     y, rr = tn.rmsnorm_fwd(G.to_dev(x, dtype), G.to_dev(d["w"], dtype), 1e-5, return_rrms=True)
@@ -79,8 +80,9 @@ def test_forward(dtype):
     assert np.isnan(rrg[1]) and rrg[4] == 0.0 and rrg[9] == 0.0
 
 
-def test_fused_residual_nan_in_residual():
-    M, H, dt = 16, 2048, "bf16"
+@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "staged"])
+def test_fused_residual_nan_in_residual(H):
+    M, dt = 16, "bf16"
     d = G.inputs(502, M, H, dt, residual=True)
     r = plant(d["r"], dt)
     y, ro, rr = tn.rmsnorm_fwd_residual(G.to_dev(d["x"], dt), G.to_dev(r, dt), G.to_dev(d["w"], dt), 1e-5,
@@ -118,8 +120,9 @@ def test_backward_nan_in_dy():
     G.assert_ok(rep)
 
 
-def test_layernorm():
-    M, H, dt = 16, 2048, "bf16"
+@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "staged"])
+def test_layernorm(H):
+    M, dt = 16, "bf16"
     d = G.inputs(504, M, H, dt, residual=True)
     x = plant(d["x"], dt)
     b = synthetic.normal_tensor(504, synthetic.STREAM_BIAS, (H,), dt, 0.0, 0.1)

@@ -516,8 +516,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *none = nullptr;
         int P = 0, Hi = (int)H;
         void *args[] = {(void *)&none, &P, &Hi, &dw};
-        return launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinSlices), args,
-                      stream, "rmsnorm_dw_finalize");
+        return launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)),
+                      dim3(kFinCols * kFinSlices), args, stream, "rmsnorm_dw_finalize");
     }
 
     const int vecw = 16 / eb;
@@ -594,8 +594,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         const float *part = p.partial;
         int Pi = (int)P, Hi = (int)H;
         void *fargs[] = {(void *)&part, &Pi, &Hi, &dw};
-        if ((st = launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinSlices), fargs,
-                         stream, "rmsnorm_dw_finalize")) != RMSN_OK)
+        if ((st = launch(dw_finalize_kernel(), dim3((unsigned)((H + kFinCols - 1) / kFinCols)),
+                         dim3(kFinCols * kFinSlices), fargs, stream, "rmsnorm_dw_finalize")) != RMSN_OK)
             return st;
     }
     return RMSN_OK;
@@ -611,9 +611,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
 
 extern "C" {
 
-RMSN_API rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *w, void *y, int64_t y_stride, float *rrms,
-                          int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
-                          hipStream_t stream) {
+RMSN_API rmsn_status_t rmsnorm_fwd(const void *x, int64_t x_stride, const void *w, void *y, int64_t y_stride,
+                                   float *rrms, int64_t M, int64_t H, float eps, rmsn_dtype_t x_dtype,
+                                   rmsn_dtype_t w_dtype, hipStream_t stream) {
     rmsn_status_t s = fwd_impl(MODE_PLAIN, x, x_stride, nullptr, 0, w, y, y_stride, nullptr, 0, rrms, M, H, eps,
                                x_dtype, w_dtype, Cond{}, LnExtra{}, stream);
     return s == RMSN_OK ? ok() : s;

@@ -9,14 +9,15 @@
 // acceleration for Transformer inference", "How the solution addresses the
 // problem", item 4).  Only the movement of the data differs:
 //   * A row group of 64*wpr threads owns one row; a workgroup holds rpw row
-//     groups, each with its own LDS buffers, and handles rpw consecutive rows
-//     (no loop over rows: straight-line code keeps few registers live; a
-//     call with more than 2^31 - 1 workgroups is split into launches).  Each input row (x, and
-//     the residual) is copied into LDS as the aligned 16-byte blocks that
-//     hold its bytes -- every block loaded holds at least one byte of the
-//     row, so no load leaves the row's pages -- and the row's byte i then
-//     sits at LDS byte delta + i, delta being the row's offset in its first
-//     block.
+//     groups, each with its own LDS buffers, and handles rpw consecutive
+//     rows.  There is no loop over rows: straight-line code keeps few
+//     registers live, and the host splits a call of more than 2^31 - 1
+//     workgroups into launches.
+//   * Each input row (x, and the residual) is copied into LDS as the aligned
+//     16-byte blocks that hold its bytes -- every block loaded holds at least
+//     one byte of the row, so no load leaves the row's pages -- and the row's
+//     byte i then sits at LDS byte delta + i, delta being the row's offset in
+//     its first block.
 //   * Thread t takes the same column vectors as on the aligned path (VEC
 //     elements each: vectors t, t + 64*wpr, ...), read from LDS as five
 //     aligned dwords joined with v_alignbyte.  The sum of squares follows the
@@ -256,7 +257,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
     }
 
     // pass 2: outputs over the thread's own input bytes (values past H stay
-    // in the buffer and are never copied out)
+    // in the buffer and are never copied out).  A neighbour still reading
+    // its vector may read a dword this thread writes into, but it uses only
+    // its own bytes of it, which no other thread writes.
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;

@@ -140,6 +140,52 @@ def test_adaln_misaligned_rows():
     G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, 1, y, rr, 1e-6, "bf16", chunk=M, name="adaln H=2047"))
 
 
+@pytest.mark.parametrize("per_batch", [True, False], ids=["per_batch", "per_token"])
+@pytest.mark.parametrize("dtype,pdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
+@pytest.mark.parametrize("H", [2049, 4096])
+def test_adaln_rows_off_the_grid(H, dtype, pdtype, per_batch):
+    """Rows off the 16-byte grid (ragged H, x and the modulation at element
+    offsets; scale and shift as column slices of one modulation tensor, per
+    batch as [B, 1, H] views): the tile depends on H only, so every layout
+    gives the same bits, at parity with the oracle, and nothing around the
+    output rows is written."""
+    B, S = 3, 11
+    M = B * S
+    C = B if per_batch else M
+    d = G.inputs(5200 + H, M, H, dtype, wdtype=pdtype)
+    sc = synthetic.normal_tensor(5200 + H, synthetic.STREAM_SCALE, (C, H), pdtype, 0.0, 0.5)
+    sh = synthetic.normal_tensor(5200 + H, synthetic.STREAM_SHIFT, (C, H), pdtype, 0.0, 0.5)
+    wd = G.to_dev(d["w"], pdtype)
+    first = None
+    for pad, xoff, moff, yoff in ((1, 1, 0, 0), (0, 3, 1, 1), (5, 0, 3, 7), (8, 1, 2, 1)):
+        print(f"[gpu] adaln staged {dtype}/{pdtype} H={H} per_batch={per_batch} layout {pad},{xoff},{moff},{yoff}",
+              flush=True)
+        _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
+        xv.copy_(G.to_dev(d["x"], dtype))
+        # scale and shift: two column slices of one modulation tensor
+        _, mv = G.sentinel_view(C, 2 * H, pad, moff, pdtype, 0.0)
+        mv[:, :H].copy_(G.to_dev(sc, pdtype))
+        mv[:, H:].copy_(G.to_dev(sh, pdtype))
+        scv, shv = mv[:, :H], mv[:, H:]
+        if per_batch:
+            scv, shv = scv.unsqueeze(1), shv.unsqueeze(1)
+        else:
+            scv, shv = scv.view(B, S, H), shv.view(B, S, H)
+        ybuf, yv = G.sentinel_view(M, H, pad + 2, yoff, dtype, -77.0)
+        _, rr = tn.rmsnorm_adaln_fwd(xv.view(B, S, H), wd, scv, shv, 1e-6, out=yv.view(B, S, H),
+                                     return_rrms=True)
+        torch.cuda.synchronize()
+        assert G.untouched(ybuf, yv, -77.0)
+        got = (G.to_host(yv.contiguous(), dtype), rr.view(-1).cpu().numpy())
+        if first is None:
+            first = got
+            rpc = S if per_batch else 1
+            G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, rpc, got[0], got[1], 1e-6, dtype, pdtype,
+                                           chunk=M, name=f"adaln staged {dtype} H={H}"))
+        else:
+            assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1])
+
+
 def test_adaln_modulation_slices():
     """scale and shift as two column slices of one [B, 1, 6H] modulation tensor
     (DiT's six values per block), sharing its row stride."""

@@ -135,19 +135,20 @@ def _rows(t, name):
         raise ValueError(f"{name} must be contiguous along its last dimension")
     if t.dim() == 1:
         return 1, H, H
-    lead = t.shape[:-1]
-    # leading dims must collapse into one row stride
-    stride = t.stride(-2)
+    # leading dims of size > 1 must collapse into one row stride; a dim of
+    # size 1 has no meaningful stride (torch gives it any value) and is skipped
+    lead = [d for d in range(t.dim() - 1) if t.shape[d] != 1]
+    if not lead:
+        return 1, H, H
+    stride = t.stride(lead[-1])
     expect = stride
-    for d in range(t.dim() - 2, -1, -1):
-        if t.shape[d] != 1 and t.stride(d) != expect:
+    for d in reversed(lead):
+        if t.stride(d) != expect:
             raise ValueError(f"{name}'s leading dimensions cannot be viewed as rows with one stride")
         expect *= t.shape[d]
     M = 1
-    for s in lead:
-        M *= s
-    if M == 1:
-        stride = max(stride, H)
+    for d in lead:
+        M *= t.shape[d]
     return M, H, stride
 
 

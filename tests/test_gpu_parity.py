@@ -4,10 +4,9 @@ binding), against the float64 oracle on the same seeded inputs.
 Full-size workloads are compared element by element (the oracle handles them
 in row chunks).  Smaller cases cover the kernels' other paths: ragged and
 tiny H, unaligned rows (staged through LDS, or single elements when forced),
-strided rows, the two-pass
-path and the grid-stride loop (forced through the tuning hook), aliasing of
-outputs with inputs, guard regions around outputs, determinism and the
-method's exact invariants.
+strided rows, the two-pass path and the grid-stride loop (forced through the
+tuning hook), aliasing of outputs with inputs, guard regions around outputs,
+determinism and the method's exact invariants.
 """
 
 from __future__ import annotations

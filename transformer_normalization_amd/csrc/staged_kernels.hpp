@@ -19,18 +19,20 @@
 //     byte i then sits at LDS byte delta + i, delta being the row's offset in
 //     its first block.
 //   * Thread t takes the same column vectors as on the aligned path (VEC
-//     elements each: vectors t, t + 64*wpr, ...), read from LDS as five
-//     aligned dwords joined with v_alignbyte.  The sum of squares follows the
+//     elements each: vectors t, t + 64*wpr, ...), read from LDS as the two
+//     aligned 16-byte blocks that hold them, joined with v_alignbyte by the
+//     row's offset (the same in every lane, so every LDS access of a wave is
+//     a run of consecutive 16-byte blocks, free of bank conflicts).  The sum of squares follows the
 //     aligned path's tree for the tile; the tile depends on H only, so any
 //     two layouts of the same rows (offsets, row pitches) give the same bits.
 //     Elements past H count as 0, as the aligned path's padding vectors do.
 //   * A thread holds its packed vectors (and the weight) in registers from
-//     the sum to the outputs, as the aligned path does.  Each thread writes
-//     its outputs over its own input bytes in LDS, then the output row is
-//     copied out: every aligned 16-byte block lying wholly inside it with one
-//     16-byte store (its bytes joined from LDS as above), and the at most two
-//     blocks it shares with its neighbours element by element, so nothing
-//     outside the row is written.
+//     the sum to the outputs, as the aligned path does, and writes its output
+//     vector to the aligned slot 16 v of the input's buffer.  The output row
+//     is then copied out: every aligned 16-byte block lying wholly inside it
+//     with one 16-byte store (its bytes joined from LDS as above), and the at
+//     most two blocks it shares with its neighbours element by element, so
+//     nothing outside the row is written.
 //   * The weight (16-byte aligned) is read as column vectors; a 16-byte chunk
 //     is loaded only if it holds an element below H, so the load stays inside
 //     the weight's pages.
@@ -42,43 +44,38 @@
 namespace rmsn {
 
 // Bytes of one staging buffer for rows of nvec column vectors: the row's
-// bytes start at delta < 16 and end before 16 * (nvec + 1); every LDS read
-// (five dwords from a 4-byte boundary at or below a row byte) ends before
-// 16 * (nvec + 2).
+// bytes start at delta < 16 and end before 16 * (nvec + 1); a read of a
+// vector takes the block after the one holding its first byte, which ends by
+// 16 * (nvec + 1) too, and the buffer keeps one block of slack.
 __host__ __device__ constexpr int64_t staged_buffer_bytes(int64_t nvec) { return 16 * (nvec + 2); }
 // LDS the staged kernels may use per workgroup (rpw row groups, one buffer
 // each for the plain form, two for the fused residual)
 constexpr int64_t kStagedMaxLds = 60 * 1024;
 
-// 16 bytes at LDS byte offset `off` (any alignment): the five aligned dwords
-// that hold them, each output word shifted out of a neighbouring pair.
-__device__ __forceinline__ u32x4 lds_read16(const unsigned char *l, int off) {
-    const uint32_t *d = reinterpret_cast<const uint32_t *>(l + (off & ~3));
-    const uint32_t s = (uint32_t)(off & 3);
-    uint32_t w[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) w[i] = d[i];
+// 16 bytes at LDS byte offset blk*16 + sh (0 <= sh < 16, wave-uniform):
+// the two aligned 16-byte blocks that hold them, read with ds_read_b128
+// (consecutive lanes read consecutive blocks: no bank conflicts), and the
+// bytes picked with a wave-uniform shift.
+__device__ __forceinline__ u32x4 lds_read16_blocks(const unsigned char *l, int blk, int sh) {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(l + 16 * blk);
+    if (sh == 0) return a;
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(l + 16 * blk + 16);
+    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const uint32_t s = (uint32_t)(sh & 3);
     u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], s);
-    return r;
-}
-
-// 16 bytes to LDS byte offset `off`, a multiple of 2, writing no byte
-// outside [off, off + 16): dword stores when off is a multiple of 4, else a
-// halfword, three realigned dwords and a halfword.
-__device__ __forceinline__ void lds_write16(unsigned char *l, int off, u32x4 v) {
-    if ((off & 3) == 0) {
-        uint32_t *d = reinterpret_cast<uint32_t *>(l + off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = v[i];
-    } else {
-        *reinterpret_cast<uint16_t *>(l + off) = (uint16_t)v[0];
-        uint32_t *d = reinterpret_cast<uint32_t *>(l + off + 2);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) d[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2u);
-        *reinterpret_cast<uint16_t *>(l + off + 14) = (uint16_t)(v[3] >> 16);
+    switch (sh >> 2) {
+#define RMSN_PICK(Q)                                                                      \
+    case Q:                                                                               \
+        for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(w[Q + i + 1], w[Q + i], s); \
+        break;
+        RMSN_PICK(0)
+        RMSN_PICK(1)
+        RMSN_PICK(2)
+        default:
+        RMSN_PICK(3)
+#undef RMSN_PICK
     }
+    return r;
 }
 
 // The aligned blocks holding row bytes [a, a + row_bytes): b = t + i*nthreads
@@ -140,7 +137,7 @@ __device__ __forceinline__ void unstage_row(const unsigned char *l, int src, voi
     constexpr int ES = Fmt<XDT>::bytes;
     using T = typename Fmt<XDT>::T;
     const uintptr_t a = reinterpret_cast<uintptr_t>(row);
-    const int d = (int)(a & 15u);
+    const int d = __builtin_amdgcn_readfirstlane((int)(a & 15u));  // one row per wave: the same in every lane
     unsigned char *base = reinterpret_cast<unsigned char *>(a - (uintptr_t)d);
     const int64_t end = d + row_bytes;
     const int nblk = (int)((end + 15) >> 4);
@@ -150,7 +147,8 @@ __device__ __forceinline__ void unstage_row(const unsigned char *l, int src, voi
         if (b >= nblk) continue;
         const int lo = 16 * b, hi = lo + 16;
         if (lo >= d && hi <= end) {
-            const u32x4 v = lds_read16(l, src + lo - d);
+            const int off = src + lo - d;  // = 16 * (off >> 4) + (off & 15), the shift wave-uniform
+            const u32x4 v = lds_read16_blocks(l, off >> 4, off & 15);
             u32x4 *dst = reinterpret_cast<u32x4 *>(base + lo);
             if constexpr (NT)
                 __builtin_nontemporal_store(v, dst);
@@ -217,8 +215,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
 
     sx.store(lx, t, row_threads);
     if constexpr (RESID) sr.store(lr, t, row_threads);
-    const int dx = sx.delta;
-    const int dr = RESID ? sr.delta : 0;
+    const int dx = __builtin_amdgcn_readfirstlane(sx.delta);  // the same in every lane of the wave
+    const int dr = RESID ? __builtin_amdgcn_readfirstlane(sr.delta) : 0;
     __syncthreads();
     zero_tail<XDT, RESID>(lx, dx, lr, dr, row_bytes, p.nvec, t, row_threads);
 
@@ -229,8 +227,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
         if (v < p.nvec) {
-            xr[k].v[0] = lds_read16(lx, dx + 16 * v);
-            if constexpr (RESID) rr[k].v[0] = lds_read16(lr, dr + 16 * v);
+            xr[k].v[0] = lds_read16_blocks(lx, v, dx);
+            if constexpr (RESID) rr[k].v[0] = lds_read16_blocks(lr, v, dr);
         } else {
             xr[k].zero();
             if constexpr (RESID) rr[k].zero();
@@ -256,10 +254,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
         if constexpr (RESID) rr[k].opaque();
     }
 
-    // pass 2: outputs over the thread's own input bytes (values past H stay
-    // in the buffer and are never copied out).  A neighbour still reading
-    // its vector may read a dword this thread writes into, but it uses only
-    // its own bytes of it, which no other thread writes.
+    // pass 2: outputs at the aligned slot 16 v of the input's buffer (every
+    // read of the inputs ended before the reduction's barrier, or, for a
+    // one-wave row, before these writes in the wave's own order)
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
@@ -275,7 +272,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
                     u32x4 q;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(hv + w * (4 / ES));
-                    lds_write16(lr, dr + 16 * v, q);
+                    *reinterpret_cast<u32x4 *>(lr + 16 * v) = q;
                 }
             }
             wr[k].widen_to(wv);
@@ -284,15 +281,15 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
             u32x4 q;
 #pragma unroll
             for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));
-            lds_write16(lx, dx + 16 * v, q);
+            *reinterpret_cast<u32x4 *>(lx + 16 * v) = q;
         }
     }
     __syncthreads();
     if (valid) {
-        unstage_row<XDT, NT, BLK>(lx, dx, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
+        unstage_row<XDT, NT, BLK>(lx, 0, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
         if constexpr (RESID)
             if (p.ro != nullptr)
-                unstage_row<XDT, NT, BLK>(lr, dr, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
+                unstage_row<XDT, NT, BLK>(lr, 0, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
                                           row_threads);
     }
 }
@@ -335,8 +332,8 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
 
     sx.store(lx, t, row_threads);
     if constexpr (RESID) sr.store(lr, t, row_threads);
-    const int dx = sx.delta;
-    const int dr = RESID ? sr.delta : 0;
+    const int dx = __builtin_amdgcn_readfirstlane(sx.delta);  // the same in every lane of the wave
+    const int dr = RESID ? __builtin_amdgcn_readfirstlane(sr.delta) : 0;
     __syncthreads();
     zero_tail<XDT, RESID>(lx, dx, lr, dr, row_bytes, p.nvec, t, row_threads);
 
@@ -345,8 +342,8 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
         if (v < p.nvec) {
-            xr[k].v[0] = lds_read16(lx, dx + 16 * v);
-            if constexpr (RESID) rr[k].v[0] = lds_read16(lr, dr + 16 * v);
+            xr[k].v[0] = lds_read16_blocks(lx, v, dx);
+            if constexpr (RESID) rr[k].v[0] = lds_read16_blocks(lr, v, dr);
         } else {
             xr[k].zero();
             if constexpr (RESID) rr[k].zero();
@@ -405,7 +402,8 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
         br[k].opaque();
     }
 
-    // outputs over the thread's own input bytes, then copied out
+    // outputs at the aligned slot 16 v of the input's buffer (as the RMSNorm
+    // kernel), then copied out
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int v = t + k * row_threads;
@@ -417,7 +415,7 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
                     u32x4 q;
 #pragma unroll
                     for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(hv + w * (4 / ES));
-                    lds_write16(lr, dr + 16 * v, q);
+                    *reinterpret_cast<u32x4 *>(lr + 16 * v) = q;
                 }
             }
             wr[k].widen_to(wv);
@@ -427,15 +425,15 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnPara
             u32x4 q;
 #pragma unroll
             for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));
-            lds_write16(lx, dx + 16 * v, q);
+            *reinterpret_cast<u32x4 *>(lx + 16 * v) = q;
         }
     }
     __syncthreads();
     if (valid) {
-        unstage_row<XDT, NT, BLK>(lx, dx, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
+        unstage_row<XDT, NT, BLK>(lx, 0, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
         if constexpr (RESID)
             if (p.ro != nullptr)
-                unstage_row<XDT, NT, BLK>(lr, dr, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
+                unstage_row<XDT, NT, BLK>(lr, 0, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
                                           row_threads);
     }
 }

@@ -457,6 +457,35 @@ int bwd_groups_per_cu(bool res, int wpr, int nvec) {
     return 4 * 64 / active;
 }
 
+// The backward on rows off the 16-byte grid (single elements), H >= 512:
+// 4 elements per thread when the row fits 16 waves, else 8, and more
+// workgroups than the vector tile takes -- ceil(16 / wpr) per CU at 4
+// elements per thread, one at 8.  Measured on gfx950 over H = 513 ... 8191
+// (bf16, 2^25-element calls, plain and residual): plain H = 1025 ran
+// 39.6 % of peak against 24.5 % on the vector tile's rule, H = 2050
+// 44.6 % against 32.3 %, H = 513 35.2 % against 16.3 %; residual 43-49 %
+// against 28-37 %; at H >= 4097 both rules take 8 x wpr on one workgroup per
+// CU.  two_pass is set when no tile holds the row.
+Geom pick_bwd_elem_geom(Kind kind, int H, int *groups_per_cu) {
+    Geom g{};
+    g.vec = 1;
+    g.nvec = H;
+    g.rpw = 1;
+    g.nchunks = 1;
+    g.two_pass = false;
+    for (int vpt : {4, 8}) {
+        const int wpr = (H + 64 * vpt - 1) / (64 * vpt);
+        if (wpr <= max_threads_for(kind, vpt, 1) / 64 && wpr <= 16) {
+            g.vpt = vpt;
+            g.wpr = wpr;
+            *groups_per_cu = vpt == 4 ? (16 + wpr - 1) / wpr : 1;
+            return g;
+        }
+    }
+    g.two_pass = true;
+    return g;
+}
+
 size_t bwd_workspace(int64_t M, int64_t H) {
     if (M <= 0 || H <= 0 || H > kMaxH) return 0;
     const int64_t cap = max_partials(H);
@@ -526,6 +555,14 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
                         (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && drs % (16 / eb) == 0));
     const Kind kind = res ? Kind::BwdRes : Kind::Bwd;
     Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, 8);
+    int elem_groups = 0;  // workgroups per CU of the single-element rule, 0: the vector tile's rule
+    if (!vec_ok && H >= 512) {
+        const Geom e = pick_bwd_elem_geom(kind, (int)H, &elem_groups);
+        if (e.two_pass)
+            elem_groups = 0;
+        else
+            g = e;
+    }
     int64_t P = 0;  // 0: chosen from the device below
     // rows interleaved across workgroups: the rows in flight at any moment are
     // neighbours in memory, as in the forward's one-row-per-workgroup grid
@@ -546,6 +583,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
             return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
         g = o;
+        elem_groups = 0;
         if (ov.c > 0) P = ov.c;
         if (ov.d == 1) interleave = true;
         if (ov.d == 2) interleave = false;
@@ -560,7 +598,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     // dw partial sums are P x H x 4 bytes, written and read once.  A grid that
     // is not a multiple of the CU count leaves a tail of CUs with an extra
     // block.
-    if (P <= 0) P = (int64_t)cus * bwd_groups_per_cu(res, g.wpr, g.nvec);
+    if (P <= 0) P = (int64_t)cus * (elem_groups > 0 ? elem_groups : bwd_groups_per_cu(res, g.wpr, g.nvec));
     if (P > max_partials(H)) P = max_partials(H);
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;

@@ -18,8 +18,10 @@
 // k*64*wpr), so it keeps the weight and its dw partial sums in registers for
 // the whole block and, at the end, writes its float32 partials to row b of the
 // workspace `partial` (P x H).  Longer rows use two passes: pass 1 forms c,
-// pass 2 reloads x and dy, writes dx and adds dy*xn into the workgroup's own
-// workspace row (no other workgroup touches it, so no atomics).
+// pass 2 reloads x and dy, writes dx and adds dy*xn into the dw partial sums
+// -- registers for the first chunks of single-element rows, else the
+// workgroup's own workspace row (no other workgroup touches it, so no
+// atomics).
 //
 // NT kernels stream x, dy and dx past the caches (non-temporal accesses);
 // weight, rrms and the partial sums use ordinary cached accesses.
@@ -208,19 +210,39 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         }
     } else {
         const int chunk = row_threads * VPT;
+        // Single-element rows keep the dw partial sums of their first RCH
+        // chunks in registers across the workgroup's rows and store them once;
+        // the sums of later chunks (and every chunk of vector rows, whose
+        // sums would take too many registers) are added into the workgroup's
+        // workspace row at each row.  Either way each column adds its rows in
+        // row order, so dw has the same bits.
+        constexpr int RCH = VEC == 1 ? 4 : 0;
+        float dwr[RCH > 0 ? RCH : 1][VPT][VEC];
+#pragma unroll
+        for (int c = 0; c < (RCH > 0 ? RCH : 1); ++c)
+#pragma unroll
+            for (int k = 0; k < VPT; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) dwr[c][k][e] = 0.0f;
         if (part != nullptr) {
             const float z[VEC] = {};
-            for (int v = t; v < p.nvec; v += row_threads) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, z);
+            for (int v = RCH * chunk + t; v < p.nvec; v += row_threads)
+                store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, z);
         }
         int parity = 0;
         for (int64_t j = 0; j < nsteps; ++j, parity ^= 1) {
             const int64_t row = start + j * step;
             const float rs = p.rrms[row];
+            // the column offsets are recomputed in every row from an opaque
+            // copy of t: hoisted out of the row loop, those of all the
+            // unrolled chunks would stay live (over 100 VGPRs)
+            int tc = t;
+            asm volatile("" : "+v"(tc));
             float acc = 0.0f;
             for (int c = 0; c < p.nchunks; ++c) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
-                    const int v = c * chunk + t + k * row_threads;
+                    const int v = c * chunk + tc + k * row_threads;
                     if (v < p.nvec) {
                         float xv[VEC], dv[VEC], wv[VEC];
                         // cached: pass 2 reads the same chunk again
@@ -239,10 +261,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             }
             const float cs = row_sum(acc, p.wpr, wave, &red[parity][0]);
             const float s = (cs * p.inv_h) * rs;
-            for (int c = 0; c < p.nchunks; ++c) {
+            // pass 2 over chunk c; dw_add(k, e-array) receives dy * xn
+            auto pass2 = [&](int c, auto &&dw_add) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
-                    const int v = c * chunk + t + k * row_threads;
+                    const int v = c * chunk + tc + k * row_threads;
                     if (v < p.nvec) {
                         float xv[VEC], dv[VEC], wv[VEC], o[VEC];
                         load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, xv);
@@ -266,14 +289,39 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                             for (int e = 0; e < VEC; ++e) o[e] += gv[e];
                         }
                         store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
-                        if (part != nullptr) {
-                            float pa[VEC];
-                            load_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
-#pragma unroll
-                            for (int e = 0; e < VEC; ++e) pa[e] = __builtin_fmaf(dv[e], xn[e], pa[e]);
-                            store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
-                        }
+                        dw_add(k, v, dv, xn);
                     }
+                }
+            };
+#pragma unroll
+            for (int c = 0; c < RCH; ++c) {
+                if (c < p.nchunks)
+                    pass2(c, [&](int k, int, const float *dv, const float *xn) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) dwr[c][k][e] = __builtin_fmaf(dv[e], xn[e], dwr[c][k][e]);
+                    });
+                // one chunk's loads at a time: interleaving the unrolled
+                // chunks would hold all of their elements at once
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int c = RCH; c < p.nchunks; ++c)
+                pass2(c, [&](int, int v, const float *dv, const float *xn) {
+                    if (part != nullptr) {
+                        float pa[VEC];
+                        load_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) pa[e] = __builtin_fmaf(dv[e], xn[e], pa[e]);
+                        store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+                    }
+                });
+        }
+        if (part != nullptr) {
+#pragma unroll
+            for (int c = 0; c < RCH; ++c) {
+#pragma unroll
+                for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    if (c < p.nchunks && v < p.nvec) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, dwr[c][k]);
                 }
             }
         }

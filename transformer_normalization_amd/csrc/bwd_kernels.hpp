@@ -19,9 +19,8 @@
 // the whole block and, at the end, writes its float32 partials to row b of the
 // workspace `partial` (P x H).  Longer rows use two passes: pass 1 forms c,
 // pass 2 reloads x and dy, writes dx and adds dy*xn into the dw partial sums
-// -- registers for the first chunks of single-element rows, else the
-// workgroup's own workspace row (no other workgroup touches it, so no
-// atomics).
+// -- registers for the first chunks, the workgroup's own workspace row for
+// later ones (no other workgroup touches it, so no atomics).
 //
 // NT kernels stream x, dy and dx past the caches (non-temporal accesses);
 // weight, rrms and the partial sums use ordinary cached accesses.
@@ -210,13 +209,13 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         }
     } else {
         const int chunk = row_threads * VPT;
-        // Single-element rows keep the dw partial sums of their first RCH
-        // chunks in registers across the workgroup's rows and store them once;
-        // the sums of later chunks (and every chunk of vector rows, whose
-        // sums would take too many registers) are added into the workgroup's
+        // The dw partial sums of the first RCH chunks stay in registers
+        // across the workgroup's rows and are stored once (four chunks of
+        // single-element rows, one of vector rows, whose chunks hold 8x the
+        // columns); the sums of later chunks are added into the workgroup's
         // workspace row at each row.  Either way each column adds its rows in
         // row order, so dw has the same bits.
-        constexpr int RCH = VEC == 1 ? 4 : 0;
+        constexpr int RCH = VEC == 1 ? 4 : 1;
         float dwr[RCH > 0 ? RCH : 1][VPT][VEC];
 #pragma unroll
         for (int c = 0; c < (RCH > 0 ? RCH : 1); ++c)

@@ -210,12 +210,12 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     } else {
         const int chunk = row_threads * VPT;
         // The dw partial sums of the first RCH chunks stay in registers
-        // across the workgroup's rows and are stored once (four chunks of
-        // single-element rows, one of vector rows, whose chunks hold 8x the
-        // columns); the sums of later chunks are added into the workgroup's
-        // workspace row at each row.  Either way each column adds its rows in
-        // row order, so dw has the same bits.
-        constexpr int RCH = VEC == 1 ? 4 : 1;
+        // across the workgroup's rows and are stored once (32 floats per
+        // thread: four chunks of single elements, two of float32 vectors, one
+        // of 16-bit vectors); the sums of later chunks are added into the
+        // workgroup's workspace row at each row.  Either way each column adds
+        // its rows in row order, so dw has the same bits.
+        constexpr int RCH = 32 / (VPT * VEC) > 0 ? 32 / (VPT * VEC) : 1;
         float dwr[RCH > 0 ? RCH : 1][VPT][VEC];
 #pragma unroll
         for (int c = 0; c < (RCH > 0 ? RCH : 1); ++c)

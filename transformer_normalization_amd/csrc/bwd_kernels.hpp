@@ -210,12 +210,13 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     } else {
         const int chunk = row_threads * VPT;
         // The dw partial sums of the first RCH chunks stay in registers
-        // across the workgroup's rows and are stored once (32 floats per
-        // thread: four chunks of single elements, two of float32 vectors, one
-        // of 16-bit vectors); the sums of later chunks are added into the
-        // workgroup's workspace row at each row.  Either way each column adds
-        // its rows in row order, so dw has the same bits.
-        constexpr int RCH = 32 / (VPT * VEC) > 0 ? 32 / (VPT * VEC) : 1;
+        // across the workgroup's rows and are stored once (64 floats per
+        // thread: eight chunks of single elements, four of float32 vectors,
+        // two of 16-bit vectors -- rows up to 65536 elements; 78-110 VGPRs
+        // at 1024 threads, no spills); the sums of later chunks are added
+        // into the workgroup's workspace row at each row.  Either way each
+        // column adds its rows in row order, so dw has the same bits.
+        constexpr int RCH = 64 / (VPT * VEC) > 0 ? 64 / (VPT * VEC) : 1;
         float dwr[RCH > 0 ? RCH : 1][VPT][VEC];
 #pragma unroll
         for (int c = 0; c < (RCH > 0 ? RCH : 1); ++c)

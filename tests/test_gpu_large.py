@@ -38,19 +38,59 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def repeated(block, dtype):
-    """(M, H) device tensor whose row i is block row i mod R."""
+def repeated(block, dtype, m=M):
+    """(m, H') device tensor whose row i is block row i mod R (H' = the block's width)."""
     b = G.to_dev(block, dtype)
-    out = torch.empty((M, H), dtype=b.dtype, device=G.DEV)
-    full = M // R
-    out[: full * R].view(full, R, H).copy_(b.unsqueeze(0).expand(full, R, H))
-    out[full * R:] = b[: M - full * R]
+    h = b.shape[1]
+    out = torch.empty((m, h), dtype=b.dtype, device=G.DEV)
+    full = m // R
+    out[: full * R].view(full, R, h).copy_(b.unsqueeze(0).expand(full, R, h))
+    out[full * R:] = b[: m - full * R]
     return out
 
 
-def sample_rows():
-    rows = list(range(0, 3)) + list(range(BOUNDARY - 3, BOUNDARY + 3)) + list(range(M - 3, M))
+def sample_rows(m=M, boundary=BOUNDARY):
+    rows = list(range(0, 3)) + list(range(boundary - 3, boundary + 3)) + list(range(m - 3, m))
     return np.array(sorted(set(rows)))
+
+
+# Rows off the 16-byte grid (8194 bytes each) take the LDS-staged kernels; the
+# row that holds element 2^31 starts below it and ends above it.
+HS = 4097
+MS = (1 << 31) // HS + 5        # 524165 rows
+BOUNDARY_S = (1 << 31) // HS    # the row that crosses 2^31 elements
+
+
+@pytest.mark.parametrize("op", ["fwd", "residual", "layernorm"])
+def test_staged_rows_past_2_31_elements(op):
+    import synthetic
+    d = G.inputs(7007, R, HS, "bf16", residual=True)
+    x, w = repeated(d["x"], "bf16", MS), G.to_dev(d["w"], "bf16")
+    rows = sample_rows(MS, BOUNDARY_S)
+    idx = torch.from_numpy(rows).to(G.DEV)
+    rep = parity.Report(f"staged {op} y past 2^31")
+    if op == "fwd":
+        y, rr = tn.rmsnorm_fwd(x, w, 1e-5, return_rrms=True)
+        del x
+        torch.cuda.synchronize()
+        yref, rref = oracle.fwd(d["x"], d["w"], G.eps32(1e-5), "bf16")
+        rep_r = parity.Report("staged fwd rrms past 2^31")
+        parity.check_f32(rep_r, rr.cpu().numpy()[rows], rref[rows % R])
+        G.assert_ok(rep_r)
+    else:
+        r = repeated(d["r"], "bf16", MS)
+        if op == "residual":
+            y, ro = tn.rmsnorm_fwd_residual(x, r, w, 1e-5)
+            yref, href, _ = oracle.fwd_residual(d["x"], d["r"], d["w"], G.eps32(1e-5), "bf16")
+        else:
+            b = synthetic.normal_tensor(7007, synthetic.STREAM_BIAS, (HS,), "bf16", 0.0, 0.1)
+            y, ro = tn.layernorm_fwd_residual(x, r, w, G.to_dev(b, "bf16"), 1e-5)
+            yref, href, _, _ = oracle.layernorm(d["x"], d["r"], d["w"], b, G.eps32(1e-5), "bf16")
+        del x, r
+        torch.cuda.synchronize()
+        assert np.array_equal(G.to_host(ro[idx], "bf16"), oracle.encode(href[rows % R], "bf16"))
+    parity.check16(rep, G.to_host(y[idx], "bf16"), yref[rows % R], "bf16", oracle.encode)
+    G.assert_ok(rep)
 
 
 def test_forward_past_2_31_elements():

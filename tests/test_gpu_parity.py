@@ -577,3 +577,56 @@ def test_empty_batch_is_a_no_op():
     dx, dw = tn.rmsnorm_bwd(xd, xd, wd, torch.empty(0, dtype=torch.float32, device=G.DEV))
     torch.cuda.synchronize()
     assert torch.count_nonzero(dw) == 0  # dw over zero rows is zero
+
+
+@pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("H", [1, 5, 13, 63, 129, 1001, 4096, 4097, 6143, 8190, 12289])
+def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
+    """The backward on rows off the 16-byte grid (16-byte vectors read and
+    written at each row's byte offset): dy, x, dres and dx each at their own
+    element offset in padded buffers, so the four tensors' rows sit at
+    different offsets within their 16-byte blocks.  Parity with the oracle for
+    the plain and the residual backward, the pads and the buffers' heads and
+    tails never written, and dx written in place over dy with the same bits;
+    the forced single-element tile is at parity too."""
+    M = 41 if H <= 8192 else 9
+    d = G.inputs(68 + H, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype, wdtype)
+    rr = torch.from_numpy(r32).to(G.DEV)
+    wd = G.to_dev(d["w"], wdtype)
+    print(f"[gpu] bwd off the grid {dtype}/{wdtype} H={H}", flush=True)
+    _, dyv = G.sentinel_view(M, H, 1, 1, dtype, 0.0)
+    _, xv = G.sentinel_view(M, H, 3, 2, dtype, 0.0)
+    _, gv = G.sentinel_view(M, H, 2, 3, dtype, 0.0)
+    dyv.copy_(G.to_dev(d["dy"], dtype))
+    xv.copy_(G.to_dev(d["x"], dtype))
+    gv.copy_(G.to_dev(d["r"], dtype))
+    dxbuf, dxv = G.sentinel_view(M, H, 5, 5, dtype, -77.0)
+    dhbuf, dhv = G.sentinel_view(M, H, 1, 0, dtype, -77.0)
+    _, dw = tn.rmsnorm_bwd(dyv, xv, wd, rr, dx=dxv)
+    _, dw2 = tn.rmsnorm_bwd_residual(dyv, xv, gv, wd, rr, dh=dhv)
+    torch.cuda.synchronize()
+    assert G.untouched(dxbuf, dxv, -77.0) and G.untouched(dhbuf, dhv, -77.0)
+    reps = list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dxv.contiguous(), dtype), dw.cpu().numpy(),
+                                dtype, wdtype=wdtype, name=f"bwd {dtype}/{wdtype} H={H}"))
+    reps += list(G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], r32, G.to_host(dhv.contiguous(), dtype),
+                                          dw2.cpu().numpy(), dtype, wdtype=wdtype, name=f"bwd_res {dtype} H={H}"))
+    G.assert_ok(*reps)
+    # in place over dy: the same bits
+    dx_in, _ = tn.rmsnorm_bwd(dyv, xv, wd, rr, dx=dyv)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.contiguous().view(torch.int32)) if dtype == "f32" else \
+        (lambda t: t.contiguous().view(torch.int16))
+    assert dx_in.data_ptr() == dyv.data_ptr() and torch.equal(bits(dyv), bits(dxv))
+    # the single-element tile, forced (contiguous rows of a ragged H only:
+    # rows on the grid keep the vector tile)
+    wpr = max(1, -(-H // (64 * 8)))
+    if wpr <= 16 and (H * (4 if dtype == "f32" else 2)) % 16:
+        tn.set_geometry("bwd", 8, wpr, 0, 0)
+        try:
+            dx3, dw3 = tn.rmsnorm_bwd(G.to_dev(d["dy"], dtype), G.to_dev(d["x"], dtype), wd, rr)
+            torch.cuda.synchronize()
+        finally:
+            tn.set_geometry("bwd")
+        G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx3, dtype), dw3.cpu().numpy(), dtype,
+                                     wdtype=wdtype, name=f"bwd element tile {dtype} H={H}"))

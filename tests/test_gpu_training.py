@@ -131,7 +131,8 @@ def test_bwd_residual_two_pass_streaming_identical():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_residual_misaligned_rows(dtype):
     """Rows that are not 16-byte aligned (odd H, and a dres view with a pad of
-    one element) take the single-element path."""
+    one element, so dres rows sit at other offsets than dy's and h's) take
+    16-byte vectors at each tensor's own row offset."""
     M, H = 129, 4097
     d = case(74, M, H, dtype)
     dyd, hd, wd = G.to_dev(d["dy"], dtype), G.to_dev(d["x"], dtype), G.to_dev(d["w"], dtype)

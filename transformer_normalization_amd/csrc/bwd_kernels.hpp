@@ -22,6 +22,10 @@
 // -- registers for the first chunks, the workgroup's own workspace row for
 // later ones (no other workgroup touches it, so no atomics).
 //
+// MIS kernels take rows off the 16-byte grid (a start that is not 16-byte
+// aligned, or a length that is not a whole number of vectors) in the same
+// 16-byte vectors, read and written at the row's byte offset (below).
+//
 // NT kernels stream x, dy and dx past the caches (non-temporal accesses);
 // weight, rrms and the partial sums use ordinary cached accesses.
 //
@@ -54,8 +58,41 @@ struct BwdParams {
     float inv_h;
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT>
+// ---- rows off the 16-byte grid -----------------------------------------------
+// Vector v of a row holds the row's bytes [16v, 16v + 16) and is read and
+// written with one 16-byte access at the row's own byte offset: gfx9 runs
+// global memory in unaligned mode, where such an access at any element-aligned
+// address is one instruction.  When the row's last vector is only partly
+// inside the row, its lane takes the row's last 16 bytes instead (columns
+// H - VEC .. H - 1): the leading `dup` columns of that window are also the
+// previous vector's, for which it computes and writes the same values; its
+// row-sum terms take them with a weight of zero, and its dw partial sums for
+// them are not stored.  No access leaves the row.
+
+// 16 bytes at an address that is only element-aligned
+typedef uint32_t u32x4_elem_aligned __attribute__((ext_vector_type(4), aligned(2)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_at(const char *a) {
+    const u32x4_elem_aligned *q = reinterpret_cast<const u32x4_elem_aligned *>(a);
+    const u32x4_elem_aligned v = NT ? __builtin_nontemporal_load(q) : *q;
+    return u32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16_at(char *a, u32x4 v) {
+    u32x4_elem_aligned *q = reinterpret_cast<u32x4_elem_aligned *>(a);
+    const u32x4_elem_aligned u = {v[0], v[1], v[2], v[3]};
+    if constexpr (NT)
+        __builtin_nontemporal_store(u, q);
+    else
+        *q = u;
+}
+
+template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
+    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: one-pass vector tiles");
+    // (rows off the grid: at least 16 bytes long, so that the last 16 bytes lie inside the row)
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;  // == blockDim.x
     const int t = threadIdx.x;
@@ -80,15 +117,46 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // only the dw partial sums are float32 registers.
         Raw<WDT, VEC> wr[VPT];
         float dwa[VPT][VEC];
+        // rows off the grid: column of the thread's window, and how many of
+        // its leading columns are the previous vector's (last vector only)
+        int col0[VPT], dup[VPT];
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int v = t + k * row_threads;
-            if (p.w != nullptr && v < p.nvec)
-                wr[k].load(p.w, (int64_t)v * VEC);
-            else
+            col0[k] = MIS && v * VEC > p.H - VEC ? p.H - VEC : v * VEC;
+            dup[k] = MIS ? v * VEC - col0[k] : 0;
+            if (p.w != nullptr && v < p.nvec) {
+                if constexpr (MIS) {
+                    constexpr int WES = Fmt<WDT>::bytes;
+#pragma unroll
+                    for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+                        wr[k].v[c] = load16_at<false>(static_cast<const char *>(p.w) + (int64_t)col0[k] * WES + 16 * c);
+                } else {
+                    wr[k].load(p.w, (int64_t)v * VEC);
+                }
+            } else {
                 wr[k].fill_one();
+            }
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dwa[k][e] = 0.0f;
+        }
+        // the weights of the row-sum terms: w, with the window's leading
+        // columns zeroed off the grid (fma(0, y, part) == part)
+        Raw<WDT, VEC> wsum[MIS ? VPT : 1];
+        if constexpr (MIS) {
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                constexpr int PER_WORD = 4 / Fmt<WDT>::bytes;
+                float f[VEC];
+                wr[k].widen_to(f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (e < dup[k]) f[e] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wsum[k].v[c][q] = pack_word<WDT>(f + (c * 4 + q) * PER_WORD);
+            }
         }
         // Software pipeline: the loads of rows row+1 .. row+PF are in flight
         // while row is reduced and stored (the barrier in row_sum waits on
@@ -100,6 +168,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         constexpr int WORDS = (RES ? 3 : 2) * VPT * (int)(sizeof(Raw<XDT, VEC>) / 4);
         constexpr int PF = WORDS <= 16 ? 2 : 1;
         Raw<XDT, VEC> xb[PF + 1][VPT], db[PF + 1][VPT], gb[RES ? PF + 1 : 1][VPT];
+        constexpr int ES = Fmt<XDT>::bytes;
         const int lane = t & 63;
         // rows in chunks of 64: one rrms value per lane for the chunk, loaded
         // before the chunk's row loads so that no wait inside the row loop
@@ -119,9 +188,17 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     const int vv = t + k * row_threads;
                     const int v = vv < p.nvec ? vv : p.nvec - 1;
-                    xd[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
-                    dd[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
-                    if constexpr (RES) gd[k].template load<NT>(p.dres, row * p.drs + (int64_t)v * VEC);
+                    if constexpr (MIS) {
+                        const int64_t o = (int64_t)(vv < p.nvec ? col0[k] : p.H - VEC) * ES;
+                        xd[k].v[0] = load16_at<NT>(static_cast<const char *>(p.x) + row * p.xs * ES + o);
+                        dd[k].v[0] = load16_at<NT>(static_cast<const char *>(p.dy) + row * p.dys * ES + o);
+                        if constexpr (RES)
+                            gd[k].v[0] = load16_at<NT>(static_cast<const char *>(p.dres) + row * p.drs * ES + o);
+                    } else {
+                        xd[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                        dd[k].template load<NT>(p.dy, row * p.dys + (int64_t)v * VEC);
+                        if constexpr (RES) gd[k].template load<NT>(p.dres, row * p.drs + (int64_t)v * VEC);
+                    }
                 }
             };
             auto process_row = [&](int64_t j, Raw<XDT, VEC> *xr, Raw<XDT, VEC> *dr, Raw<XDT, VEC> *gr) {
@@ -134,7 +211,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     float xv[VEC], dv[VEC], wv[VEC];
                     xr[k].widen_to(xv);
                     dr[k].widen_to(dv);
-                    wr[k].widen_to(wv);
+                    if constexpr (MIS)
+                        wsum[k].widen_to(wv);
+                    else
+                        wr[k].widen_to(wv);
                     float part = 0.0f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) part = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, part);
@@ -168,7 +248,13 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) o[e] += gv[e];
                         }
-                        store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                        if constexpr (MIS) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(o + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.dx) + (row * p.dxs + col0[k]) * ES, raw);
+                        } else
+                            store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
                     }
                 }
             };
@@ -204,7 +290,14 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 #pragma unroll
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
-                if (v < p.nvec) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, dwa[k]);
+                if constexpr (MIS) {
+                    // the workspace rows are H floats apart, so off the grid too
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (v < p.nvec && e >= dup[k]) part[(int64_t)col0[k] + e] = dwa[k][e];
+                } else {
+                    if (v < p.nvec) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, dwa[k]);
+                }
             }
         }
     } else {

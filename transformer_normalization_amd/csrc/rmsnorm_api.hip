@@ -554,9 +554,23 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
                         dys % (16 / eb) == 0 && xs % (16 / eb) == 0 && dxs % (16 / eb) == 0 &&
                         (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && drs % (16 / eb) == 0));
     const Kind kind = res ? Kind::BwdRes : Kind::Bwd;
+    const Override ov = get_override(1);
     Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, 8);
     int elem_groups = 0;  // workgroups per CU of the single-element rule, 0: the vector tile's rule
-    if (!vec_ok && H >= 512) {
+    // Rows off the grid take 16-byte vectors at their byte offset when every
+    // row start is element-aligned, w is 16-byte aligned and the row holds at
+    // least 16 bytes and fits one pass; a forced geometry keeps the
+    // single-element tile.
+    bool mis = false;
+    if (!vec_ok && !ov.set && H * eb >= 16 && aligned_to(dy, eb) && aligned_to(x, eb) && aligned_to(dx, eb) &&
+        (!res || aligned_to(dres, eb)) && (w == nullptr || aligned16(w))) {
+        const Geom m = pick_row_geom(kind, (int)H, vecw, 8);
+        if (!m.two_pass) {
+            g = m;
+            mis = true;
+        }
+    }
+    if (!vec_ok && !mis && H >= 512) {
         const Geom e = pick_bwd_elem_geom(kind, (int)H, &elem_groups);
         if (e.two_pass)
             elem_groups = 0;
@@ -567,7 +581,6 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     // rows interleaved across workgroups: the rows in flight at any moment are
     // neighbours in memory, as in the forward's one-row-per-workgroup grid
     bool interleave = true;
-    const Override ov = get_override(1);
     if (ov.set) {
         if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16)
             return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: tile vpt %d wpr %d out of range", ov.a, ov.b);
@@ -589,8 +602,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (ov.d == 2) interleave = false;
     }
     const bool nt = use_streaming((res ? 4 : 3) * M * H * eb);
-    bwd_fn fn = res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
-                    : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
+    bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, res, nt)
+                : res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
+                      : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;

@@ -587,8 +587,9 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
     element offset in padded buffers, so the four tensors' rows sit at
     different offsets within their 16-byte blocks.  Parity with the oracle for
     the plain and the residual backward, the pads and the buffers' heads and
-    tails never written, and dx written in place over dy with the same bits;
-    the forced single-element tile is at parity too."""
+    tails never written, dx written in place over dy with the same bits, and,
+    for an H of whole vectors, the bits of the contiguous (aligned) run; the
+    forced single-element tile is at parity too."""
     M = 41 if H <= 8192 else 9
     d = G.inputs(68 + H, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
     r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype, wdtype)
@@ -612,11 +613,17 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
     reps += list(G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], r32, G.to_host(dhv.contiguous(), dtype),
                                           dw2.cpu().numpy(), dtype, wdtype=wdtype, name=f"bwd_res {dtype} H={H}"))
     G.assert_ok(*reps)
+    bits = (lambda t: t.contiguous().view(torch.int32)) if dtype == "f32" else \
+        (lambda t: t.contiguous().view(torch.int16))
+    if (H * (4 if dtype == "f32" else 2)) % 16 == 0:
+        # whole vectors: the views run the aligned path's tile, so the bits
+        # of the contiguous (aligned) run
+        dxa, dwa = tn.rmsnorm_bwd(G.to_dev(d["dy"], dtype), G.to_dev(d["x"], dtype), wd, rr)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(dxv), bits(dxa)) and torch.equal(dw, dwa)
     # in place over dy: the same bits
     dx_in, _ = tn.rmsnorm_bwd(dyv, xv, wd, rr, dx=dyv)
     torch.cuda.synchronize()
-    bits = (lambda t: t.contiguous().view(torch.int32)) if dtype == "f32" else \
-        (lambda t: t.contiguous().view(torch.int16))
     assert dx_in.data_ptr() == dyv.data_ptr() and torch.equal(bits(dyv), bits(dxv))
     # the single-element tile, forced (contiguous rows of a ragged H only:
     # rows on the grid keep the vector tile)
@@ -630,3 +637,49 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
             tn.set_geometry("bwd")
         G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx3, dtype), dw3.cpu().numpy(), dtype,
                                      wdtype=wdtype, name=f"bwd element tile {dtype} H={H}"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("H", [8, 15, 63, 64, 128, 255, 256, 257, 384, 511])
+def test_fwd_short_rows_off_the_grid(dtype, H):
+    """Rows under 1 KiB off the 16-byte grid (from 512 bytes: 16-byte vectors
+    at each row's byte offset; shorter rows: the element-wise tile): x, the
+    residual and the outputs at different element offsets in padded buffers,
+    for the plain and fused residual forward -- parity with the oracle, the
+    pads never written, in place over x and over the residual with the same
+    bits, and, for an H of whole vectors from 512 bytes, the bits of the
+    contiguous (aligned) run."""
+    M = 300
+    d = G.inputs(90 + H, M, H, dtype, residual=True)
+    wd = G.to_dev(d["w"], dtype)
+    print(f"[gpu] short rows off the grid {dtype} H={H}", flush=True)
+    _, xv = G.sentinel_view(M, H, 1, 1, dtype, 0.0)
+    _, rv = G.sentinel_view(M, H, 2, 3, dtype, 0.0)
+    xv.copy_(G.to_dev(d["x"], dtype))
+    rv.copy_(G.to_dev(d["r"], dtype))
+    ybuf, yv = G.sentinel_view(M, H, 3, 2, dtype, -77.0)
+    robuf, rov = G.sentinel_view(M, H, 1, 5, dtype, -77.0)
+    _, rr = tn.rmsnorm_fwd(xv, wd, 1e-5, out=yv, return_rrms=True)
+    y2, _, rr2 = tn.rmsnorm_fwd_residual(xv, rv, wd, 1e-6, residual_out=rov, return_rrms=True)
+    torch.cuda.synchronize()
+    assert G.untouched(ybuf, yv, -77.0) and G.untouched(robuf, rov, -77.0)
+    reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(yv.contiguous(), dtype), rr.cpu().numpy(), 1e-5, dtype,
+                                name=f"fwd {dtype} H={H}"))
+    reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype), G.to_host(rov.contiguous(), dtype),
+                                      rr2.cpu().numpy(), 1e-6, dtype, name=f"res {dtype} H={H}"))
+    G.assert_ok(*reps)
+    bits = (lambda t: t.contiguous().view(torch.int32)) if dtype == "f32" else \
+        (lambda t: t.contiguous().view(torch.int16))
+    row_bytes = H * (4 if dtype == "f32" else 2)
+    if row_bytes % 16 == 0 and 512 <= row_bytes < 1024:
+        ya = tn.rmsnorm_fwd(G.to_dev(d["x"], dtype), wd, 1e-5)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(yv), bits(ya))
+    # in place: y over x, residual_out over the residual
+    y_first, ro_first = bits(yv).clone(), bits(rov).clone()
+    y3, _ = tn.rmsnorm_fwd_residual(xv, rv, wd, 1e-6, residual_out=rv)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(rv), ro_first) and torch.equal(bits(y3), bits(y2))
+    tn.rmsnorm_fwd(xv, wd, 1e-5, out=xv)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(xv), y_first)

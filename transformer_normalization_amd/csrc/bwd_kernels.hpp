@@ -69,26 +69,6 @@ struct BwdParams {
 // row-sum terms take them with a weight of zero, and its dw partial sums for
 // them are not stored.  No access leaves the row.
 
-// 16 bytes at an address that is only element-aligned
-typedef uint32_t u32x4_elem_aligned __attribute__((ext_vector_type(4), aligned(2)));
-
-template <bool NT>
-__device__ __forceinline__ u32x4 load16_at(const char *a) {
-    const u32x4_elem_aligned *q = reinterpret_cast<const u32x4_elem_aligned *>(a);
-    const u32x4_elem_aligned v = NT ? __builtin_nontemporal_load(q) : *q;
-    return u32x4{v[0], v[1], v[2], v[3]};
-}
-
-template <bool NT>
-__device__ __forceinline__ void store16_at(char *a, u32x4 v) {
-    u32x4_elem_aligned *q = reinterpret_cast<u32x4_elem_aligned *>(a);
-    const u32x4_elem_aligned u = {v[0], v[1], v[2], v[3]};
-    if constexpr (NT)
-        __builtin_nontemporal_store(u, q);
-    else
-        *q = u;
-}
-
 template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: one-pass vector tiles");

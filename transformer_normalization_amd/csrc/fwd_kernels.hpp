@@ -27,6 +27,15 @@
 //     ("Required reasoning process", step 3, the persistent pattern).
 //   * Two-pass path (longer rows): pass 1 sums squares chunk by chunk, pass 2
 //     reloads each chunk with the same bounds and scales it (step 11).
+//   * MIS kernels (resident path only) take rows off the 16-byte grid (a
+//     start that is not 16-byte aligned, or a length that is not a whole
+//     number of vectors) in the same 16-byte vectors, each read and written
+//     with one access at the row's own byte offset.  When a row's last vector
+//     is only partly inside the row, its lane takes the row's last 16 bytes
+//     instead (columns H - VEC .. H - 1): the window's leading `dup` columns
+//     are also the previous vector's, for which it computes and writes the
+//     same values, and they are left out of its sum of squares.  Every lane
+//     runs the same code, and no access leaves the row.
 //   * NT kernels stream x, r, y and r_out past the caches (non-temporal
 //     accesses); the weight and rrms use ordinary cached accesses.
 //   * The reduction is a per-thread float32 sum over the thread's elements in
@@ -66,8 +75,11 @@ struct FwdParams {
 
 enum : int { MODE_PLAIN = 0, MODE_RESID = 1, MODE_ADALN = 2 };
 
-template <int XDT, int WDT, int VEC, int VPT, int MODE, bool TWO_PASS, bool NT, int MAXT>
+template <int XDT, int WDT, int VEC, int VPT, int MODE, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
+    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: resident vector tiles");
+    constexpr int ES = Fmt<XDT>::bytes;
+    constexpr int WES = Fmt<WDT>::bytes;
     constexpr bool RESID = MODE == MODE_RESID;
     constexpr bool ADALN = MODE == MODE_ADALN;
     __shared__ float red[2][16];
@@ -82,13 +94,25 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
         // (one VALU op per element), which halves the register footprint of
         // 16-bit formats; every widening of an element gives the same float.
         Raw<WDT, VEC> wr[VPT];
+        // rows off the grid: first column of the thread's window, and how
+        // many of its leading columns are the previous vector's
+        int col0[VPT], dup[VPT];
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int v = t + k * row_threads;
-            if (p.w != nullptr && v < p.nvec)
-                wr[k].load(p.w, (int64_t)v * VEC);
-            else
+            col0[k] = MIS && v * VEC > p.H - VEC ? p.H - VEC : v * VEC;
+            dup[k] = MIS ? v * VEC - col0[k] : 0;
+            if (p.w != nullptr && v < p.nvec) {
+                if constexpr (MIS) {
+#pragma unroll
+                    for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+                        wr[k].v[c] = load16_at<false>(static_cast<const char *>(p.w) + (int64_t)col0[k] * WES + 16 * c);
+                } else {
+                    wr[k].load(p.w, (int64_t)v * VEC);
+                }
+            } else {
                 wr[k].fill_one();
+            }
         }
 
         // AdaLN conditioning rows stay in registers while consecutive rows of
@@ -108,8 +132,14 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
                 if (row < p.M && v < p.nvec) {
-                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
-                    if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
+                    if constexpr (MIS) {
+                        xr[k].v[0] = load16_at<NT>(static_cast<const char *>(p.x) + (row * p.xs + col0[k]) * ES);
+                        if constexpr (RESID)
+                            rr[k].v[0] = load16_at<NT>(static_cast<const char *>(p.r) + (row * p.rs + col0[k]) * ES);
+                    } else {
+                        xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                        if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
+                    }
                 } else {
                     xr[k].zero();
                     if constexpr (RESID) rr[k].zero();
@@ -125,8 +155,17 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                         const int v = t + k * row_threads;
                         if (v < p.nvec) {
                             // cached: a conditioning row serves rows_per_cond rows
-                            scr[k].load(p.scale, crow * p.cs + (int64_t)v * VEC);
-                            shr[k].load(p.shift, crow * p.cs + (int64_t)v * VEC);
+                            if constexpr (MIS) {
+#pragma unroll
+                                for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c) {
+                                    const int64_t o = (crow * p.cs + col0[k]) * WES + 16 * c;
+                                    scr[k].v[c] = load16_at<false>(static_cast<const char *>(p.scale) + o);
+                                    shr[k].v[c] = load16_at<false>(static_cast<const char *>(p.shift) + o);
+                                }
+                            } else {
+                                scr[k].load(p.scale, crow * p.cs + (int64_t)v * VEC);
+                                shr[k].load(p.shift, crow * p.cs + (int64_t)v * VEC);
+                            }
                         } else {
                             scr[k].zero();
                             shr[k].zero();
@@ -151,11 +190,22 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                     const int v = t + k * row_threads;
-                    if (p.ro != nullptr && valid && v < p.nvec)
-                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                    if (p.ro != nullptr && valid && v < p.nvec) {
+                        if constexpr (MIS) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(hv + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.ro) + (row * p.ros + col0[k]) * ES, raw);
+                        } else {
+                            store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                        }
+                    }
                 }
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(hv[e], hv[e], acc);
+                for (int e = 0; e < VEC; ++e) {
+                    const float he = MIS && e < dup[k] ? 0.0f : hv[e];
+                    acc = __builtin_fmaf(he, he, acc);
+                }
             }
             const float ss = row_sum(acc, p.wpr, wave_in_row, &red[it & 1][slot * p.wpr]);
             const float rs = fast_rsqrt(ss * p.inv_h + p.eps);
@@ -195,7 +245,14 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
                     }
-                    store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    if constexpr (MIS) {
+                        u32x4 raw;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(o + q * (4 / ES));
+                        store16_at<NT>(static_cast<char *>(p.y) + (row * p.ys + col0[k]) * ES, raw);
+                    } else {
+                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    }
                 }
             }
             if (it + 1 < p.iters) load_row(it + 1);

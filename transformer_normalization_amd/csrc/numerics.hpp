@@ -246,6 +246,32 @@ struct Raw {
     }
 };
 
+// ---- 16-byte vectors at element-aligned addresses ---------------------------
+// gfx9 runs global memory in unaligned mode: a 16-byte access at any
+// element-aligned address is one global_load_dwordx4 / global_store_dwordx4.
+// (Rows off the 16-byte grid: the kernels that use these keep every access
+// inside the row.)
+
+// 16 bytes at an address that is only element-aligned
+typedef uint32_t u32x4_elem_aligned __attribute__((ext_vector_type(4), aligned(2)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_at(const char *a) {
+    const u32x4_elem_aligned *q = reinterpret_cast<const u32x4_elem_aligned *>(a);
+    const u32x4_elem_aligned v = NT ? __builtin_nontemporal_load(q) : *q;
+    return u32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16_at(char *a, u32x4 v) {
+    u32x4_elem_aligned *q = reinterpret_cast<u32x4_elem_aligned *>(a);
+    const u32x4_elem_aligned u = {v[0], v[1], v[2], v[3]};
+    if constexpr (NT)
+        __builtin_nontemporal_store(u, q);
+    else
+        *q = u;
+}
+
 // ---- reductions -------------------------------------------------------------
 
 template <int CTRL>

@@ -184,16 +184,17 @@ def test_ln_misaligned_and_strided_rows(dtype):
 @pytest.mark.parametrize("H", [600, 2049, 4096, 6143])
 def test_ln_rows_off_the_grid(dtype, wdtype, H):
     """Rows off the 16-byte grid (ragged H, or views at element offsets)
-    go through LDS on a tile that depends on H only: every layout gives the
-    same bits, at parity with the oracle, and nothing around the output rows
-    is written; the forced element-wise tile is at parity too."""
+    are read and written in 16-byte vectors at each row's byte offset, on a
+    tile that depends on H only: every layout gives the same bits, at parity
+    with the oracle, and nothing around the output rows is written; the
+    forced element-wise tile is at parity too."""
     M = 67
     d = G.inputs(5100 + H, M, H, dtype, wdtype=wdtype, residual=True)
     b = bias_of(5100 + H, H, wdtype)
     wt, bt = G.to_dev(d["w"], wdtype), G.to_dev(b, wdtype)
     first = None
     for pad, xoff, yoff in ((1, 1, 0), (0, 3, 1), (5, 0, 7), (8, 1, 1)):
-        print(f"[gpu] ln staged {dtype}/{wdtype} H={H} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
+        print(f"[gpu] ln off the grid {dtype}/{wdtype} H={H} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
         _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
         _, rv = G.sentinel_view(M, H, pad + 1, xoff + 2, dtype, 0.0)
         xv.copy_(G.to_dev(d["x"], dtype))
@@ -210,9 +211,9 @@ def test_ln_rows_off_the_grid(dtype, wdtype, H):
         if first is None:
             first = got
             G.assert_ok(*G.ln_vs_oracle(d["x"], d["r"], d["w"], b, got[0], got[1], got[2], got[3], 1e-5, dtype,
-                                        wdtype, name=f"ln staged {dtype} H={H}"))
+                                        wdtype, name=f"ln off the grid {dtype} H={H}"))
             G.assert_ok(*G.ln_vs_oracle(d["x"], None, d["w"], b, got[4], None, None, None, 1e-5, dtype, wdtype,
-                                        name=f"ln staged plain {dtype} H={H}"))
+                                        name=f"ln off the grid plain {dtype} H={H}"))
         else:
             for a, c in zip(got, first):
                 assert np.array_equal(a, c), (pad, xoff, yoff)

@@ -3,7 +3,7 @@
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
 // kernels_fwd_staged*.hip, kernels_fwd_mis.hip, kernels_bwd.hip, kernels_bwd_residual.hip, kernels_bwd_mis.hip,
 // kernels_rope.hip, kernels_ln.hip,
-// kernels_ln_staged.hip)
+// kernels_ln_mis.hip)
 // so that they compile in parallel; the host code only sees these functions.
 #pragma once
 
@@ -45,8 +45,9 @@ const void *dw_finalize_kernel();
 // float32; xchg: the lane-exchange layout (vectors only)
 // LayerNorm forward, plain or fused with the residual add (resid)
 ln_fn ln_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt, bool resid);
-// LayerNorm for rows off the 16-byte grid (staged through LDS)
-ln_fn ln_staged_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt, bool resid);
+// LayerNorm for rows off the 16-byte grid, resident, in 16-byte vectors at
+// the row's byte offset
+ln_fn ln_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt, bool resid);
 rope_fn rope_lookup(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool nt, bool xchg);
 
 }  // namespace rmsn

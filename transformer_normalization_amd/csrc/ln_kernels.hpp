@@ -49,8 +49,17 @@ struct LnParams {
     float inv_h;
 };
 
-template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT>
+// MIS (resident path only): rows off the 16-byte grid in the same 16-byte
+// vectors, each read and written with one access at the row's own byte
+// offset; a row's last vector, when only partly inside the row, is the window
+// over the row's last 16 bytes, whose leading `dup` columns (the previous
+// vector's, written again with the same values) are left out of both sums
+// (fwd_kernels.hpp).
+template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
+    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: resident vector tiles");
+    constexpr int ES = Fmt<XDT>::bytes;
+    constexpr int WES = Fmt<WDT>::bytes;
     // one LDS area per reduction of a row; consecutive reductions alternate
     // areas, so one barrier per reduction suffices (see row_sum)
     __shared__ float red[2][16];
@@ -62,17 +71,32 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
 
     if constexpr (!TWO_PASS) {
         Raw<WDT, VEC> wr[VPT], br[VPT];
+        int col0[VPT], dup[VPT];
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int v = t + k * row_threads;
-            if (p.w != nullptr && v < p.nvec)
-                wr[k].load(p.w, (int64_t)v * VEC);
-            else
-                wr[k].fill_one();
-            if (p.b != nullptr && v < p.nvec)
-                br[k].load(p.b, (int64_t)v * VEC);
-            else
-                br[k].zero();
+            col0[k] = MIS && v * VEC > p.H - VEC ? p.H - VEC : v * VEC;
+            dup[k] = MIS ? v * VEC - col0[k] : 0;
+            if constexpr (MIS) {
+#pragma unroll
+                for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c) {
+                    const int64_t o = (int64_t)col0[k] * WES + 16 * c;
+                    wr[k].v[c] = p.w != nullptr && v < p.nvec ? load16_at<false>(static_cast<const char *>(p.w) + o)
+                                                               : u32x4{0u, 0u, 0u, 0u};
+                    br[k].v[c] = p.b != nullptr && v < p.nvec ? load16_at<false>(static_cast<const char *>(p.b) + o)
+                                                               : u32x4{0u, 0u, 0u, 0u};
+                }
+                if (p.w == nullptr || v >= p.nvec) wr[k].fill_one();
+            } else {
+                if (p.w != nullptr && v < p.nvec)
+                    wr[k].load(p.w, (int64_t)v * VEC);
+                else
+                    wr[k].fill_one();
+                if (p.b != nullptr && v < p.nvec)
+                    br[k].load(p.b, (int64_t)v * VEC);
+                else
+                    br[k].zero();
+            }
         }
         // a row's loads are issued before the loop (first row) or at the end
         // of the previous iteration, never behind a wait: the weight and bias
@@ -86,13 +110,26 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
             for (int k = 0; k < VPT; ++k) {
                 const int v = t + k * row_threads;
                 if (row < p.M && v < p.nvec) {
-                    xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
-                    if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
+                    if constexpr (MIS) {
+                        xr[k].v[0] = load16_at<NT>(static_cast<const char *>(p.x) + (row * p.xs + col0[k]) * ES);
+                        if constexpr (RESID)
+                            rr[k].v[0] = load16_at<NT>(static_cast<const char *>(p.r) + (row * p.rs + col0[k]) * ES);
+                    } else {
+                        xr[k].template load<NT>(p.x, row * p.xs + (int64_t)v * VEC);
+                        if constexpr (RESID) rr[k].template load<NT>(p.r, row * p.rs + (int64_t)v * VEC);
+                    }
                 } else {
                     xr[k].zero();
                     if constexpr (RESID) rr[k].zero();
                 }
             }
+        };
+        // 16 bytes of float32 values, in x's format, written at column col0[k]
+        auto store_window = [&](void *base, int64_t row_off, int k, const float *vals) {
+            u32x4 raw;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(vals + q * (4 / ES));
+            store16_at<NT>(static_cast<char *>(base) + (row_off + col0[k]) * ES, raw);
         };
         load_row(0);
         for (int64_t it = 0; it < p.iters; ++it) {
@@ -116,11 +153,15 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                 widen_h(k, hv);
                 if constexpr (RESID) {
                     const int v = t + k * row_threads;
-                    if (p.ro != nullptr && valid && v < p.nvec)
-                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                    if (p.ro != nullptr && valid && v < p.nvec) {
+                        if constexpr (MIS)
+                            store_window(p.ro, row * p.ros, k, hv);
+                        else
+                            store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                    }
                 }
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) s1 += hv[e];
+                for (int e = 0; e < VEC; ++e) s1 += MIS && e < dup[k] ? 0.0f : hv[e];
             }
             const float mean = row_sum(s1, p.wpr, wave_in_row, &red[0][slot * p.wpr]) * p.inv_h;
 #pragma unroll
@@ -137,7 +178,7 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                 if (v < p.nvec) {  // padding lanes hold h = 0, not mean
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float d = hv[e] - mean;
+                        const float d = MIS && e < dup[k] ? 0.0f : hv[e] - mean;
                         s2 = __builtin_fmaf(d, d, s2);
                     }
                 }
@@ -167,7 +208,10 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                     br[k].widen_to(bv);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
-                    store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                    if constexpr (MIS)
+                        store_window(p.y, row * p.ys, k, o);
+                    else
+                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
                 }
             }
             if (it + 1 < p.iters) load_row(it + 1);

@@ -275,26 +275,28 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     const Override ov = get_override(0);
-    // Rows off the 16-byte grid, RMSNorm and LayerNorm, plain and fused
-    // residual forms: staged through LDS on a vector tile, when the weight
-    // (and bias) is 16-byte aligned, every
-    // row pointer is element-aligned, a row holds at least 1 KiB (below that
-    // the element-wise tile measured faster: bf16 H = 257 ran 35.6 % of peak
-    // element-wise, 31.3 % staged; H = 520 65.5 % and 69.5 %) and the row
-    // fits the register tile and the LDS budget.  Otherwise, or with a forced
-    // geometry, the element-wise tile.
+    // RMSNorm rows off the 16-byte grid, plain and fused residual forms:
+    // staged through LDS on a vector tile, when the weight is 16-byte
+    // aligned, every row pointer is element-aligned, a row holds at least
+    // 1 KiB (below that the element-wise tile measured faster: bf16 H = 257
+    // ran 35.6 % of peak element-wise, 31.3 % staged; H = 520 65.5 % and
+    // 69.5 %) and the row fits the register tile and the LDS budget.
+    // LayerNorm takes the unaligned vectors below at every length (measured
+    // on gfx950 against the staged tile: float32 fused residual H = 1023
+    // 70.5 % against 63.7 %, bf16 H = 4097 55.5 % and 51.9 %, f16 fused
+    // residual H = 2049 54.3 % and 51.9 %).
     Geom g{};
     int64_t lds = 0;
     bool staged = false;
-    if (!vec_ok && !ov.set && !adaln && H * eb >= 1024 && (w == nullptr || aligned16(w)) &&
+    if (!vec_ok && !ov.set && !adaln && !ln && H * eb >= 1024 && (w == nullptr || aligned16(w)) &&
         (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
         (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb))))) {
         g = pick_staged_geom(kind, (int)H, vecw);
         lds = (int64_t)g.rpw * (resid ? 2 : 1) * staged_buffer_bytes(g.nvec);
         staged = !g.two_pass && lds <= kStagedMaxLds;
     }
-    // RMSNorm rows off the grid that are not staged (AdaLN, rows under 1 KiB)
-    // take 16-byte vectors at each row's byte offset on the aligned tile, when
+    // Rows off the grid that are not staged (AdaLN and LayerNorm at any
+    // length, RMSNorm rows under 1 KiB) take 16-byte vectors at each row's byte offset on the aligned tile, when
     // every row start is element-aligned, the parameters are 16-byte aligned
     // (AdaLN's conditioning rows: element-aligned), the row holds at least 512
     // bytes and fits the resident tile.  Measured on gfx950 against the
@@ -303,7 +305,8 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     // vectors leave most of a wave idle).  From 1 KiB the LDS-staged tile
     // measured better or within 3 %: H = 2049 58.7 % staged, 48.2 % here.
     bool mis = false;
-    if (!staged && !vec_ok && !ov.set && !ln && H * eb >= 512 && (w == nullptr || aligned16(w)) &&
+    if (!staged && !vec_ok && !ov.set && H * eb >= 512 && (w == nullptr || aligned16(w)) &&
+        (bias == nullptr || aligned16(bias)) &&
         aligned_to(x, eb) && aligned_to(y, eb) &&
         (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb)))) &&
         (!adaln || (aligned_to(cond.scale, pb) && aligned_to(cond.shift, pb)))) {
@@ -349,8 +352,8 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     const rmsn_dtype_t kwdt = (w || adaln || bias) ? wdt : xdt;
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if (ln) {
-        ln_fn fn = staged ? ln_staged_lookup(xdt, kwdt, g.vpt, nt, resid)
-                          : ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
+        ln_fn fn = mis ? ln_mis_lookup(xdt, kwdt, g.vpt, nt, resid)
+                       : ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
         if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
         if ((st = device_info(&cus)) != RMSN_OK) return st;
         LnParams p;
@@ -375,18 +378,6 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         p.nchunks = g.nchunks;
         p.eps = eps;
         p.inv_h = (float)(1.0 / (double)H);
-        if (staged)
-            return launch_row_chunks((const void *)fn, p, M, g, lds, stream,
-                                     resid ? "layernorm_fwd_residual" : "layernorm_fwd", [&](LnParams &q, int64_t r0) {
-                                         q.x = static_cast<const char *>(x) + r0 * xs * eb;
-                                         q.y = static_cast<char *>(y) + r0 * ys * eb;
-                                         if (resid) {
-                                             q.r = static_cast<const char *>(r) + r0 * rs * eb;
-                                             if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
-                                         }
-                                         if (mean != nullptr) q.mean = mean + r0;
-                                         if (rrms != nullptr) q.rstd = rrms + r0;
-                                     });
         void *args[] = {&p};
         return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                       resid ? "layernorm_fwd_residual" : "layernorm_fwd");

@@ -1,13 +1,10 @@
-// staged_kernels.hpp -- gfx950 forward RMSNorm and LayerNorm (plain and
-// fused residual) for rows that are not 16-byte aligned: H not a whole number
-// of 16-byte vectors, or a base or row stride off the 16-byte grid.
+// staged_kernels.hpp -- gfx950 forward RMSNorm (plain and fused residual)
+// for rows that are not 16-byte aligned: H not a whole number of 16-byte
+// vectors, or a base or row stride off the 16-byte grid.
 //
-// What is computed is exactly the forward of fwd_kernels.hpp (and of
-// ln_kernels.hpp for LayerNorm), resident tile: the same float32 expressions
-// in the same order ("Skill: Write a Triton RMSNorm Kernel", "Required
-// reasoning process" steps 1-11; LayerNorm: "SpeedROCm: shape-aware Triton
-// acceleration for Transformer inference", "How the solution addresses the
-// problem", item 4).  Only the movement of the data differs:
+// What is computed is exactly the forward of fwd_kernels.hpp, resident tile:
+// the same float32 expressions in the same order ("Skill: Write a Triton
+// RMSNorm Kernel", "Required reasoning process" steps 1-11).  Only the movement of the data differs:
 //   * A row group of 64*wpr threads owns one row; a workgroup holds rpw row
 //     groups, each with its own LDS buffers, and handles rpw consecutive
 //     rows.  There is no loop over rows: straight-line code keeps few
@@ -39,7 +36,6 @@
 #pragma once
 
 #include "fwd_kernels.hpp"
-#include "ln_kernels.hpp"
 
 namespace rmsn {
 
@@ -278,150 +274,6 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_staged_kernel(const FwdParam
             wr[k].widen_to(wv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
-            u32x4 q;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));
-            *reinterpret_cast<u32x4 *>(lx + 16 * v) = q;
-        }
-    }
-    __syncthreads();
-    if (valid) {
-        unstage_row<XDT, NT, BLK>(lx, 0, static_cast<char *>(p.y) + row * p.ys * ES, row_bytes, t, row_threads);
-        if constexpr (RESID)
-            if (p.ro != nullptr)
-                unstage_row<XDT, NT, BLK>(lr, 0, static_cast<char *>(p.ro) + row * p.ros * ES, row_bytes, t,
-                                          row_threads);
-    }
-}
-
-// LayerNorm (plain or fused with the residual add) on rows off the 16-byte
-// grid: the staging of rmsnorm_fwd_staged_kernel around the two reductions
-// of layernorm_fwd_kernel.  Elements past H read as 0, which adds nothing to
-// the sum; the centred sum skips them.
-template <int XDT, int WDT, int VPT, bool RESID, bool NT, int MAXT>
-__global__ void __launch_bounds__(MAXT) layernorm_fwd_staged_kernel(const LnParams p) {
-    constexpr int ES = Fmt<XDT>::bytes;
-    constexpr int VEC = 16 / ES;
-    constexpr int BLK = VPT + 1;
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float red[2][16];
-    const int row_threads = 64 * p.wpr;
-    const int slot = threadIdx.x / row_threads;
-    const int t = threadIdx.x - slot * row_threads;
-    const int wave_in_row = t >> 6;
-    const int64_t buf = staged_buffer_bytes(p.nvec);
-    unsigned char *lx = smem + (RESID ? 2 : 1) * slot * buf;
-    unsigned char *lr = lx + buf;
-    const int64_t row_bytes = (int64_t)p.H * ES;
-
-    const int64_t row = (int64_t)blockIdx.x * p.rpw + slot;
-    const bool valid = row < p.M;
-    Staged<NT, BLK> sx;
-    Staged<NT, RESID ? BLK : 1> sr;
-    sx.load(static_cast<const char *>(p.x) + row * p.xs * ES, valid, row_bytes, t, row_threads);
-    if constexpr (RESID) sr.load(static_cast<const char *>(p.r) + row * p.rs * ES, valid, row_bytes, t, row_threads);
-
-    Raw<WDT, VEC> wr[VPT], br[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        wr[k].fill_one();
-        br[k].zero();
-    }
-    load_param_staged<WDT, VEC, VPT>(wr, p.w, t, row_threads, p.nvec, p.H);
-    load_param_staged<WDT, VEC, VPT>(br, p.b, t, row_threads, p.nvec, p.H);
-
-    sx.store(lx, t, row_threads);
-    if constexpr (RESID) sr.store(lr, t, row_threads);
-    const int dx = __builtin_amdgcn_readfirstlane(sx.delta);  // the same in every lane of the wave
-    const int dr = RESID ? __builtin_amdgcn_readfirstlane(sr.delta) : 0;
-    __syncthreads();
-    zero_tail<XDT, RESID>(lx, dx, lr, dr, row_bytes, p.nvec, t, row_threads);
-
-    Raw<XDT, VEC> xr[VPT], rr[RESID ? VPT : 1];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = t + k * row_threads;
-        if (v < p.nvec) {
-            xr[k].v[0] = lds_read16_blocks(lx, v, dx);
-            if constexpr (RESID) rr[k].v[0] = lds_read16_blocks(lr, v, dr);
-        } else {
-            xr[k].zero();
-            if constexpr (RESID) rr[k].zero();
-        }
-    }
-    auto widen_h = [&](int k, float *hv) {
-        xr[k].widen_to(hv);
-        if constexpr (RESID) {
-            float rv[VEC];
-            rr[k].widen_to(rv);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
-        }
-    };
-    float s1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        float hv[VEC];
-        widen_h(k, hv);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s1 += hv[e];
-    }
-    const float mean = row_sum(s1, p.wpr, wave_in_row, &red[0][slot * p.wpr]) * p.inv_h;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        xr[k].opaque();
-        if constexpr (RESID) rr[k].opaque();
-    }
-    float s2 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = t + k * row_threads;
-        float hv[VEC];
-        widen_h(k, hv);
-        if (v < p.nvec) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                if (v * VEC + e < p.H) {  // elements past H are 0, not mean
-                    const float d = hv[e] - mean;
-                    s2 = __builtin_fmaf(d, d, s2);
-                }
-            }
-        }
-    }
-    const float var = row_sum(s2, p.wpr, wave_in_row, &red[1][slot * p.wpr]) * p.inv_h;
-    const float rs = fast_rsqrt(var + p.eps);
-    if (valid && t == 0) {
-        if (p.mean != nullptr) p.mean[row] = mean;
-        if (p.rstd != nullptr) p.rstd[row] = rs;
-    }
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        xr[k].opaque();
-        if constexpr (RESID) rr[k].opaque();
-        wr[k].opaque();
-        br[k].opaque();
-    }
-
-    // outputs at the aligned slot 16 v of the input's buffer (as the RMSNorm
-    // kernel), then copied out
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = t + k * row_threads;
-        if (v < p.nvec) {
-            float hv[VEC], wv[VEC], bv[VEC], o[VEC];
-            widen_h(k, hv);
-            if constexpr (RESID) {
-                if (p.ro != nullptr) {
-                    u32x4 q;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(hv + w * (4 / ES));
-                    *reinterpret_cast<u32x4 *>(lr + 16 * v) = q;
-                }
-            }
-            wr[k].widen_to(wv);
-            br[k].widen_to(bv);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
             u32x4 q;
 #pragma unroll
             for (int w = 0; w < 4; ++w) q[w] = pack_word<XDT>(o + w * (4 / ES));

@@ -57,21 +57,21 @@ KERNEL_SOURCES = {
     "adaln": _FWD + ("kernels_adaln.hip", "rmsnorm_api.hip"),
     "rope": ("numerics.hpp", "rope_kernels.hpp", "kernel_tables.hpp", "kernels_rope.hip", "rope_api.hip"),
     "ln_residual": ("numerics.hpp", "ln_kernels.hpp", "kernel_tables.hpp", "kernels_ln.hip", "rmsnorm_api.hip"),
-    "fwd_staged": ("numerics.hpp", "fwd_kernels.hpp", "staged_kernels.hpp", "kernel_tables.hpp",
-                   "kernels_fwd_staged_plain.hip", "rmsnorm_api.hip"),
+    "fwd_offgrid": _FWD + ("kernels_fwd_mis.hip", "rmsnorm_api.hip"),
 }
 # the kernel whose launches the counters describe
 KERNEL_KEY = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
               "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel",
-              "ln_residual": "layernorm_fwd_kernel", "fwd_staged": "rmsnorm_fwd_staged_kernel"}
+              "ln_residual": "layernorm_fwd_kernel", "fwd_offgrid": "rmsnorm_fwd_kernel"}
 
 
 def kernel_kind(spec) -> str:
     """The kernel family a workload's calls run: its kind, except that a
     forward on contiguous rows whose byte length is not a multiple of 16 (so
-    that rows leave the 16-byte grid) runs the LDS-staged forward."""
+    that rows leave the 16-byte grid) runs the forward's instantiations for
+    rows off the grid (16-byte vectors at each row's byte offset)."""
     if spec["kind"] == "fwd" and (spec["H"] * _size(spec["dtype"])) % 16:
-        return "fwd_staged"
+        return "fwd_offgrid"
     return spec["kind"]
 
 WORKLOADS = {

@@ -54,10 +54,10 @@ def test_every_bench_workload_names_a_kernel_and_sources():
         assert len(bench.kernel_source_digest(kind)) == 16
 
 
-def test_ragged_forward_runs_the_staged_kernel():
+def test_ragged_forward_runs_the_off_grid_kernels():
     # rows of 8194 bytes leave the 16-byte grid; rows of 8192 bytes do not
-    assert bench.kernel_kind(spec("fwd_bf16_8192x4097")) == "fwd_staged"
-    assert bench.KERNEL_KEY["fwd_staged"] == "rmsnorm_fwd_staged_kernel"
+    assert bench.kernel_kind(spec("fwd_bf16_8192x4097")) == "fwd_offgrid"
+    assert bench.KERNEL_KEY["fwd_offgrid"] == "rmsnorm_fwd_kernel"
     assert bench.kernel_kind(spec("fwd_bf16_8192x4096")) == "fwd"
     assert bench.kernel_kind(spec("fwd_f32_64x512")) == "fwd"
     assert bench.algorithmic_bytes(spec("fwd_bf16_8192x4097"), True) == 2 * 8192 * 4097 * 2 + 4097 * 2

@@ -158,7 +158,7 @@ def test_adaln_rows_off_the_grid(H, dtype, pdtype, per_batch):
     wd = G.to_dev(d["w"], pdtype)
     first = None
     for pad, xoff, moff, yoff in ((1, 1, 0, 0), (0, 3, 1, 1), (5, 0, 3, 7), (8, 1, 2, 1)):
-        print(f"[gpu] adaln staged {dtype}/{pdtype} H={H} per_batch={per_batch} layout {pad},{xoff},{moff},{yoff}",
+        print(f"[gpu] adaln off-grid {dtype}/{pdtype} H={H} per_batch={per_batch} layout {pad},{xoff},{moff},{yoff}",
               flush=True)
         _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
         xv.copy_(G.to_dev(d["x"], dtype))
@@ -181,7 +181,7 @@ def test_adaln_rows_off_the_grid(H, dtype, pdtype, per_batch):
             first = got
             rpc = S if per_batch else 1
             G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, rpc, got[0], got[1], 1e-6, dtype, pdtype,
-                                           chunk=M, name=f"adaln staged {dtype} H={H}"))
+                                           chunk=M, name=f"adaln off-grid {dtype} H={H}"))
         else:
             assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1])
 

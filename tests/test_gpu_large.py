@@ -54,7 +54,7 @@ def sample_rows(m=M, boundary=BOUNDARY):
     return np.array(sorted(set(rows)))
 
 
-# Rows off the 16-byte grid (8194 bytes each) take the LDS-staged kernels; the
+# Rows off the 16-byte grid (8194 bytes each) take the kernels for such rows; the
 # row that holds element 2^31 starts below it and ends above it.
 HS = 4097
 MS = (1 << 31) // HS + 5        # 524165 rows
@@ -62,19 +62,19 @@ BOUNDARY_S = (1 << 31) // HS    # the row that crosses 2^31 elements
 
 
 @pytest.mark.parametrize("op", ["fwd", "residual", "layernorm"])
-def test_staged_rows_past_2_31_elements(op):
+def test_off_grid_rows_past_2_31_elements(op):
     import synthetic
     d = G.inputs(7007, R, HS, "bf16", residual=True)
     x, w = repeated(d["x"], "bf16", MS), G.to_dev(d["w"], "bf16")
     rows = sample_rows(MS, BOUNDARY_S)
     idx = torch.from_numpy(rows).to(G.DEV)
-    rep = parity.Report(f"staged {op} y past 2^31")
+    rep = parity.Report(f"off-grid {op} y past 2^31")
     if op == "fwd":
         y, rr = tn.rmsnorm_fwd(x, w, 1e-5, return_rrms=True)
         del x
         torch.cuda.synchronize()
         yref, rref = oracle.fwd(d["x"], d["w"], G.eps32(1e-5), "bf16")
-        rep_r = parity.Report("staged fwd rrms past 2^31")
+        rep_r = parity.Report("off-grid fwd rrms past 2^31")
         parity.check_f32(rep_r, rr.cpu().numpy()[rows], rref[rows % R])
         G.assert_ok(rep_r)
     else:

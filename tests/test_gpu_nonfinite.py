@@ -62,7 +62,7 @@ def same_classes(got64, ref64, what):
     assert np.array_equal(got64[fin], ref64[fin]), f"{what}: finite values differ"
 
 
-@pytest.mark.parametrize("H", [4096, 4097], ids=["aligned", "staged"])
+@pytest.mark.parametrize("H", [4096, 4097], ids=["aligned", "off_grid"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_forward(dtype, H):
     M = 16
@@ -80,7 +80,7 @@ def test_forward(dtype, H):
     assert np.isnan(rrg[1]) and rrg[4] == 0.0 and rrg[9] == 0.0
 
 
-@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "staged"])
+@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "off_grid"])
 def test_fused_residual_nan_in_residual(H):
     M, dt = 16, "bf16"
     d = G.inputs(502, M, H, dt, residual=True)
@@ -120,7 +120,7 @@ def test_backward_nan_in_dy():
     G.assert_ok(rep)
 
 
-@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "staged"])
+@pytest.mark.parametrize("H", [2048, 2049], ids=["aligned", "off_grid"])
 def test_layernorm(H):
     M, dt = 16, "bf16"
     d = G.inputs(504, M, H, dt, residual=True)

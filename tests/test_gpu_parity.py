@@ -3,7 +3,7 @@ binding), against the float64 oracle on the same seeded inputs.
 
 Full-size workloads are compared element by element (the oracle handles them
 in row chunks).  Smaller cases cover the kernels' other paths: ragged and
-tiny H, unaligned rows (staged through LDS, or single elements when forced),
+tiny H, unaligned rows (16-byte vectors at the row offset, or single elements when forced),
 strided rows, the two-pass path and the grid-stride loop (forced through the
 tuning hook), aliasing of outputs with inputs, guard regions around outputs,
 determinism and the method's exact invariants.
@@ -76,7 +76,7 @@ def oracle_rrms32(x, w, eps, dtype, wdtype=None, chunk=2048):
 # the named workloads, full size
 # ---------------------------------------------------------------------------
 
-# fwd_bf16_8192x4097: rows of 8194 bytes, the LDS-staged forward at full
+# fwd_bf16_8192x4097: rows of 8194 bytes, the forward for rows off the grid at full
 # size (with streaming accesses, as bench.py times it)
 @pytest.mark.parametrize("name", ["fwd_f32_64x512", "fwd_bf16_8192x4096", "fwd_bf16_8192x4097"])
 def test_workload_fwd(name):
@@ -305,8 +305,8 @@ def test_misaligned_rows(dtype, stream):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_misaligned_views_same_bits_at_any_offset(dtype):
-    """Rows off the 16-byte grid go through LDS on a vector tile that depends
-    on H only, so every layout of the same rows -- any element offset of x,
+    """Rows off the 16-byte grid take 16-byte vectors at each row's byte
+    offset on a vector tile that depends on H only, so every layout of the same rows -- any element offset of x,
     the residual and the outputs, any row pitch -- gives the same bits, at
     parity with the oracle, for the plain and the fused residual forward;
     the elements around the output rows (pads, the buffer's head and tail)
@@ -317,7 +317,7 @@ def test_misaligned_views_same_bits_at_any_offset(dtype):
     bits = (lambda t: t.view(torch.int32)) if dtype == "f32" else (lambda t: t.view(torch.int16))
     first = None
     for pad, xoff, yoff in ((1, 0, 1), (0, 1, 3), (3, 1, 0), (5, 7, 2), (8, 3, 5)):
-        print(f"[gpu] staged views {dtype} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
+        print(f"[gpu] off-grid views {dtype} pad={pad} xoff={xoff} yoff={yoff}", flush=True)
         _, xv = G.sentinel_view(M, H, pad, xoff, dtype, 0.0)
         _, rv = G.sentinel_view(M, H, pad, xoff + 1, dtype, 0.0)
         xv.copy_(xd)
@@ -332,10 +332,10 @@ def test_misaligned_views_same_bits_at_any_offset(dtype):
         if first is None:
             first = got
             reps = list(G.fwd_vs_oracle(d["x"], d["w"], G.to_host(yv.contiguous(), dtype), rr.cpu().numpy(), 1e-5,
-                                        dtype, name=f"fwd {dtype} staged view"))
+                                        dtype, name=f"fwd {dtype} off-grid view"))
             reps += list(G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y2, dtype),
                                               G.to_host(rov.contiguous(), dtype), rr2.cpu().numpy(), 1e-6, dtype,
-                                              name=f"res {dtype} staged view"))
+                                              name=f"res {dtype} off-grid view"))
             G.assert_ok(*reps)
         else:
             for a, b in zip(got, first):
@@ -379,7 +379,7 @@ def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
                                      wdtype=wdtype, name=f"fwd element tile {dtype} H={H}"))
 
 
-@pytest.mark.parametrize("H", [6144, 4097], ids=["aligned", "staged"])
+@pytest.mark.parametrize("H", [6144, 4097], ids=["aligned", "off_grid"])
 def test_in_place_outputs(H):
     """y written over x, residual_out over the residual, dx over dy.  At
     H = 4097 the rows are off the 16-byte grid: a row's edge blocks are

@@ -19,8 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librmsnorm.so")
-SOURCES = ["host_common.hip", "rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_fwd_staged_plain.hip",
-           "kernels_fwd_staged_resid.hip", "kernels_adaln.hip", "kernels_bwd.hip",
+SOURCES = ["host_common.hip", "rmsnorm_api.hip", "kernels_fwd.hip", "kernels_fwd_residual.hip", "kernels_adaln.hip", "kernels_bwd.hip",
            "kernels_bwd_residual.hip", "kernels_bwd_mis.hip", "kernels_fwd_mis.hip", "rope_api.hip", "kernels_rope.hip", "kernels_ln.hip", "kernels_ln_mis.hip",
            "kernels_copy.hip"]
 ARCH = "gfx950"

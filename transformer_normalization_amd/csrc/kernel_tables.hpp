@@ -1,7 +1,7 @@
 // kernel_tables.hpp -- lookup of kernel instantiations by format and tile.
 // Each kernel family is instantiated in its own translation unit
 // (kernels_fwd.hip, kernels_fwd_residual.hip, kernels_adaln.hip,
-// kernels_fwd_staged*.hip, kernels_fwd_mis.hip, kernels_bwd.hip, kernels_bwd_residual.hip, kernels_bwd_mis.hip,
+// kernels_fwd_mis.hip, kernels_bwd.hip, kernels_bwd_residual.hip, kernels_bwd_mis.hip,
 // kernels_rope.hip, kernels_ln.hip,
 // kernels_ln_mis.hip)
 // so that they compile in parallel; the host code only sees these functions.
@@ -12,7 +12,6 @@
 #include "ln_kernels.hpp"
 #include "rmsnorm.h"
 #include "rope_kernels.hpp"
-#include "staged_kernels.hpp"
 
 namespace rmsn {
 
@@ -25,10 +24,6 @@ typedef void (*ln_fn)(const LnParams);
 // accesses per thread; nt: streaming accesses)
 fwd_fn fwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
-// the forward for rows off the 16-byte grid (staged through LDS); vpt:
-// column vectors per thread, as the aligned tile
-fwd_fn fwd_staged_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt);
-fwd_fn fwd_staged_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt);
 // the resident forward for rows off the 16-byte grid (16-byte vectors at the
 // row's byte offset; mode: MODE_PLAIN, MODE_RESID or MODE_ADALN)
 fwd_fn fwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, int mode, bool nt);

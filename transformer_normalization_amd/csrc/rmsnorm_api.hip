@@ -130,23 +130,23 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     return g;
 }
 
-// Tile of the staged forward (rows off the 16-byte grid).  There a lane
-// without a vector costs no memory traffic, and the fewer waves a row takes,
-// the more rows a CU holds in flight, so the cost is the row's waves plus
-// 8 x the idle share of its slots, over vpt <= 6 (the register tile of 8 lowers
-// the waves a SIMD holds); two rows share a workgroup only when a row takes a
-// single wave.  Measured on gfx950 (64 Mi-element calls): bf16 H = 4097 ran
-// 59.5 % of peak on 3 x 3 (54.8 % on the aligned path's 3 x 3 with two rows
-// per workgroup), H = 2050 58.5 % on 6 x 1 (39.2 % on 1 x 5), float32
-// H = 4097 64.6 % on 6 x 3 (59.9 % on 2 x 9).  two_pass is set when no tile
-// holds the row.
-Geom pick_staged_geom(Kind kind, int H, int vec) {
-    static const int kStagedVpt[] = {1, 2, 3, 4, 6};
+// Tile of the RMSNorm forward on rows off the 16-byte grid from 1 KiB (16-byte
+// vectors at the row's byte offset).  A lane without a vector costs no memory
+// traffic, and the fewer waves a row takes, the more rows a CU holds in
+// flight, so the cost is the row's waves plus 8 x the idle share of its slots,
+// over vpt <= 6; rows of at most three waves share a workgroup in pairs.
+// Measured on gfx950 (bf16, 2^25 elements) against the vector tile rule and
+// against the LDS staging this replaced: H = 2049 64.8 % (48.2 % on the vector
+// rule, 58.5 % staged), H = 4097 63.7 % (61.3 % staged; one row per
+// workgroup: 60.1 %), H = 6143 64.5 % (58.7 % staged), fused residual
+// H = 6143 68.7 % (58.4 % staged).
+Geom pick_offgrid_geom(Kind kind, int H, int vec) {
+    static const int kOffgridVpt[] = {1, 2, 3, 4, 6};
     Geom g{};
     g.vec = vec;
     g.nvec = (H + vec - 1) / vec;
     double best = 1e30;
-    for (int vpt : kStagedVpt) {
+    for (int vpt : kOffgridVpt) {
         const int wpr = (g.nvec + 64 * vpt - 1) / (64 * vpt);
         if (wpr > max_threads_for(kind, vpt, vec) / 64) continue;
         const double slots = 64.0 * wpr * vpt;
@@ -159,7 +159,7 @@ Geom pick_staged_geom(Kind kind, int H, int vec) {
     }
     g.two_pass = best >= 1e30;
     g.nchunks = 1;
-    g.rpw = g.wpr == 1 ? 2 : 1;
+    g.rpw = g.wpr <= 3 && 64 * g.wpr * 2 <= max_threads_for(kind, g.vpt, vec) ? 2 : 1;
     return g;
 }
 
@@ -172,27 +172,6 @@ Geom pick_staged_geom(Kind kind, int H, int vec) {
 // ---------------------------------------------------------------------------
 // forward (plain and fused residual)
 // ---------------------------------------------------------------------------
-
-// The staged kernels take one row group per workgroup and have no row loop:
-// a call is split into launches of at most INT32_MAX workgroups, each on rows
-// [r0, r0 + rows) through pointers that `shift` moves to row r0.
-template <class Params, class Shift>
-rmsn_status_t launch_row_chunks(const void *fn, const Params &p, int64_t M, const Geom &g, int64_t lds,
-                                hipStream_t stream, const char *what, Shift shift) {
-    const int64_t max_rows = (int64_t)INT32_MAX * g.rpw;
-    for (int64_t r0 = 0; r0 < M; r0 += max_rows) {
-        const int64_t rows = M - r0 < max_rows ? M - r0 : max_rows;
-        Params q = p;
-        shift(q, r0);
-        q.M = rows;
-        q.iters = 1;
-        void *args[] = {&q};
-        const rmsn_status_t st = launch(fn, dim3((unsigned)((rows + g.rpw - 1) / g.rpw)), dim3(64 * g.wpr * g.rpw),
-                                        args, stream, what, (size_t)lds);
-        if (st != RMSN_OK) return st;
-    }
-    return RMSN_OK;
-}
 
 // Conditioning rows of an AdaLN call (scale and shift share the layout).
 struct Cond {
@@ -275,51 +254,32 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     const Override ov = get_override(0);
-    // RMSNorm rows off the 16-byte grid, plain and fused residual forms:
-    // staged through LDS on a vector tile, when the weight is 16-byte
-    // aligned, every row pointer is element-aligned, a row holds at least
-    // 1 KiB (below that the element-wise tile measured faster: bf16 H = 257
-    // ran 35.6 % of peak element-wise, 31.3 % staged; H = 520 65.5 % and
-    // 69.5 %) and the row fits the register tile and the LDS budget.
-    // LayerNorm takes the unaligned vectors below at every length (measured
-    // on gfx950 against the staged tile: float32 fused residual H = 1023
-    // 70.5 % against 63.7 %, bf16 H = 4097 55.5 % and 51.9 %, f16 fused
-    // residual H = 2049 54.3 % and 51.9 %).
+    // Rows off the 16-byte grid take 16-byte vectors at each row's byte
+    // offset (one unaligned access per vector), when every row start is
+    // element-aligned, the weight (and bias) is 16-byte aligned (AdaLN's
+    // conditioning rows: element-aligned), the row holds at least 512 bytes
+    // and fits the resident tile: RMSNorm rows from 1 KiB on the off-grid tile
+    // rule, shorter rows, AdaLN and LayerNorm on the aligned rule.  Measured on
+    // gfx950 against the element-wise tile (bf16, 2^25 elements): H = 257
+    // 49.5 % against 37.4 % of peak, H = 511 68.9 % and 56.3 %, but H = 127
+    // 27.8 % and 31.3 % (16 vectors leave most of a wave idle); LayerNorm
+    // against the LDS staging it replaced: float32 fused residual H = 1023
+    // 70.5 % against 63.7 %, bf16 H = 4097 55.5 % and 51.9 %.  Otherwise, or
+    // with a forced geometry, the element-wise tile.
     Geom g{};
-    int64_t lds = 0;
-    bool staged = false;
-    if (!vec_ok && !ov.set && !adaln && !ln && H * eb >= 1024 && (w == nullptr || aligned16(w)) &&
-        (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
-        (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb))))) {
-        g = pick_staged_geom(kind, (int)H, vecw);
-        lds = (int64_t)g.rpw * (resid ? 2 : 1) * staged_buffer_bytes(g.nvec);
-        staged = !g.two_pass && lds <= kStagedMaxLds;
-    }
-    // Rows off the grid that are not staged (AdaLN and LayerNorm at any
-    // length, RMSNorm rows under 1 KiB) take 16-byte vectors at each row's byte offset on the aligned tile, when
-    // every row start is element-aligned, the parameters are 16-byte aligned
-    // (AdaLN's conditioning rows: element-aligned), the row holds at least 512
-    // bytes and fits the resident tile.  Measured on gfx950 against the
-    // element-wise tile (bf16, 2^25 elements): H = 257 49.5 % against 37.4 %
-    // of peak, H = 511 68.9 % and 56.3 %, but H = 127 27.8 % and 31.3 % (16
-    // vectors leave most of a wave idle).  From 1 KiB the LDS-staged tile
-    // measured better or within 3 %: H = 2049 58.7 % staged, 48.2 % here.
     bool mis = false;
-    if (!staged && !vec_ok && !ov.set && H * eb >= 512 && (w == nullptr || aligned16(w)) &&
-        (bias == nullptr || aligned16(bias)) &&
-        aligned_to(x, eb) && aligned_to(y, eb) &&
+    if (!vec_ok && !ov.set && H * eb >= 512 && (w == nullptr || aligned16(w)) &&
+        (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
         (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb)))) &&
         (!adaln || (aligned_to(cond.scale, pb) && aligned_to(cond.shift, pb)))) {
-        const Geom m = pick_row_geom(kind, (int)H, vecw, eb == 4 ? 8 : 16);
+        Geom m = !ln && !adaln && H * eb >= 1024 ? pick_offgrid_geom(kind, (int)H, vecw) : Geom{};
+        if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, (int)H, vecw, eb == 4 ? 8 : 16);
         if (!m.two_pass) {
             g = m;
             mis = true;
         }
     }
-    if (!staged && !mis) {
-        g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
-        lds = 0;
-    }
+    if (!mis) g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     if (ov.set) {
         // bounds first: the products below are then small
@@ -382,9 +342,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                       resid ? "layernorm_fwd_residual" : "layernorm_fwd");
     }
-    fwd_fn fn = staged  ? (resid ? fwd_staged_lookup_resid(xdt, kwdt, g.vpt, nt)
-                                 : fwd_staged_lookup_plain(xdt, kwdt, g.vpt, nt))
-                : mis   ? fwd_mis_lookup(xdt, kwdt, g.vpt, mode, nt)
+    fwd_fn fn = mis     ? fwd_mis_lookup(xdt, kwdt, g.vpt, mode, nt)
                 : resid ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                 : adaln ? fwd_lookup_adaln(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                         : fwd_lookup_plain(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt);
@@ -428,17 +386,6 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     p.shift = cond.shift;
     p.cs = cond.cs;
     p.rows_per_cond = cond.rows_per_cond;
-    if (staged)
-        return launch_row_chunks((const void *)fn, p, M, g, lds, stream, resid ? "rmsnorm_fwd_residual" : "rmsnorm_fwd",
-                                 [&](FwdParams &q, int64_t r0) {
-                                     q.x = static_cast<const char *>(x) + r0 * xs * eb;
-                                     q.y = static_cast<char *>(y) + r0 * ys * eb;
-                                     if (resid) {
-                                         q.r = static_cast<const char *>(r) + r0 * rs * eb;
-                                         if (ro != nullptr) q.ro = static_cast<char *>(ro) + r0 * ros * eb;
-                                     }
-                                     if (rrms != nullptr) q.rrms = rrms + r0;
-                                 });
     void *args[] = {&p};
     return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                   resid ? "rmsnorm_fwd_residual" : adaln ? "rmsnorm_adaln_fwd" : "rmsnorm_fwd");

@@ -43,6 +43,20 @@ extern "C" {
 void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid);
 
 /*
+ * Host only (touches no device): the tile a call takes with no forced
+ * geometry.  op: 0 RMSNorm forward, 1 fused residual, 2 AdaLN, 3 LayerNorm,
+ * 4 backward, 5 residual backward.  layout 0: every row start 16-byte
+ * aligned; 1: row starts only element-aligned (parameters 16-byte aligned).
+ * Writes out[0] elements per access, out[1] accesses per thread, out[2] waves
+ * per row, out[3] rows per workgroup, out[4] 1 when rows off the 16-byte grid
+ * take 16-byte vectors at each row's byte offset (0: single elements or rows
+ * on the grid), out[5] 1 when the row takes the multi-pass path (out[1] and
+ * out[2] are then 0).  RMSN_ERR_INVALID_ARG for a bad op, layout, H or a NULL
+ * out; RMSN_ERR_UNSUPPORTED for an unknown format or H > 2^30.
+ */
+rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dtype, int layout, int32_t out[6]);
+
+/*
  * Streaming accesses: the (M, H) inputs and outputs can be read and written
  * with non-temporal hints, which keep them out of the caches.  mode < 0 (the
  * default) streams when a call moves at least 64 MiB of such data, 0 never,

@@ -382,9 +382,13 @@ def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
 @pytest.mark.parametrize("H", [6144, 4097], ids=["aligned", "off_grid"])
 def test_in_place_outputs(H):
     """y written over x, residual_out over the residual, dx over dy.  At
-    H = 4097 the rows are off the 16-byte grid: a row's edge blocks are
-    shared with its neighbours, whose workgroups read and write their own
-    bytes of them concurrently."""
+    H = 4097 (bf16) the rows are off the 16-byte grid and take 16-byte
+    vectors at the row's byte offset on a 3-wave row (3 vectors per thread):
+    the row's last vector, 512, is a window over the row's last 16 bytes,
+    held by thread 128 (wave 2), and its leading 7 columns are also vector
+    511's, held by thread 127 (wave 1).  Only the order of every aligned-away
+    store after all of the row's loads keeps the in-place result equal to
+    the out-of-place one there."""
     M = 200
     d = G.inputs(63, M, H, "bf16", residual=True, dy=True)
     wd = G.to_dev(d["w"], "bf16")

@@ -145,10 +145,13 @@ def test_bwd_residual_misaligned_rows(dtype):
                                           dw.cpu().numpy(), dtype, name=f"misaligned {dtype}"))
 
 
-@pytest.mark.parametrize("H", [4096, 65536])
+@pytest.mark.parametrize("H", [4096, 65536, 4097])
 def test_bwd_residual_in_place(H):
     """dh may be dres, dy or h itself (same buffer and stride); the bits equal
-    those of a separate output."""
+    those of a separate output.  H = 4097 (bf16): rows off the 16-byte grid,
+    where the row's last vector is a window whose leading columns belong to
+    a lane of another wave (the kernel waits for its dres loads before the
+    row barrier)."""
     M = 64 if H <= 8192 else 4
     d = case(75, M, H, "bf16")
     rr = torch.from_numpy(d["rr"]).to(G.DEV)

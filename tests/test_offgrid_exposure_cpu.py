@@ -1,0 +1,119 @@
+"""Rows off the 16-byte grid: which shapes put the row's last (window) vector
+in another wave than the vector before it.
+
+Off the grid, a row's last vector, when only partly inside the row, is read
+and written as a window over the row's last 16 bytes.  Its leading columns
+are also the previous vector's.  When the two vectors sit in different waves
+of the row, nothing but the row barrier orders one wave's stores against the
+other wave's loads of those columns.  An output that is the very same buffer
+as an input (the ABI allows it) is then safe only because every aligned-away
+store is made after every load of the row has returned: the kernels store
+residual_out (forward, LayerNorm) and dh (residual backward) after the row's
+reductions, and the residual backward waits for its dres loads before the
+row barrier.
+
+This test needs no GPU: it asks the library for the tile each call takes
+(rmsnorm_tuning_tile) and lists the exposed shapes, H <= 8192 in every
+format.  The in-place GPU tests run the listed worked case, bf16 H = 4097.
+"""
+
+from __future__ import annotations
+
+import os
+
+import pytest
+
+import transformer_normalization_amd as tn
+from transformer_normalization_amd import build as hipbuild
+
+OPS = ("fwd", "fwd_residual", "adaln", "layernorm", "bwd", "bwd_residual")
+ES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def _lib():
+    if not os.path.exists(tn.LIB_PATH):
+        hipbuild.build()
+    return tn.load_library()
+
+
+def _exposed(H: int, vec: int, wpr: int) -> bool:
+    """Whether the window vector and the vector before it are in different
+    waves: thread t of a row group of 64*wpr threads holds vectors t, t +
+    64*wpr, ...; its wave is t // 64."""
+    nvec = -(-H // vec)
+    if H % vec == 0 or nvec < 2:
+        return False  # no partial vector, or no neighbour
+    row_threads = 64 * wpr
+    wave = lambda v: (v % row_threads) // 64
+    return wave(nvec - 1) != wave(nvec - 2)
+
+
+def exposure_table(hmax: int = 8192):
+    _lib()
+    rows = []
+    for dt, es in ES.items():
+        vec = 16 // es
+        for op in OPS:
+            for H in range(2, hmax + 1):
+                if H % vec == 0:
+                    continue
+                t = tn.tile(op, H, dt, off_grid=True)
+                if t["mis"] and _exposed(H, t["vec"], t["wpr"]):
+                    rows.append((op, dt, H, t["vpt"], t["wpr"]))
+    return rows
+
+
+def test_exposure_rule_matches_mapping():
+    # the closed form: exposed iff wpr > 1 and the window vector is lane 0 of
+    # a wave, i.e. (nvec - 1) % 64 == 0
+    for vec in (4, 8):
+        for wpr in (1, 2, 3, 4, 8):
+            for H in range(2, 4 * 64 * vec * wpr):
+                nvec = -(-H // vec)
+                want = H % vec != 0 and nvec >= 2 and wpr > 1 and (nvec - 1) % 64 == 0
+                assert _exposed(H, vec, wpr) == want, (vec, wpr, H)
+
+
+def test_worked_case_is_exposed():
+    # bf16 H = 4097 fused residual: vectors 511 and 512 (the window) are
+    # threads 127 and 128 of a 3-wave row, waves 1 and 2
+    t = tn.tile("fwd_residual", 4097, "bf16", off_grid=True)
+    assert t["mis"] and (t["vpt"], t["wpr"]) == (3, 3)
+    assert _exposed(4097, 8, 3)
+
+
+def test_exposure_table(capsys):
+    rows = exposure_table()
+    by_op = {}
+    for op, dt, H, vpt, wpr in rows:
+        by_op.setdefault((op, dt), []).append(H)
+    with capsys.disabled():
+        print("\noff-grid shapes (H <= 8192) whose window vector is in another wave than its neighbour:")
+        for (op, dt), hs in sorted(by_op.items()):
+            print(f"  {op:13s} {dt:5s} {len(hs):3d} H: {hs}")
+    # the exposure only arises for rows of several waves whose last vector
+    # starts a wave; every row whose length leaves H % vec != 0 and nvec - 1
+    # a multiple of 64 and that takes a multi-wave tile is listed
+    assert ("fwd_residual", "bf16", 4097, 3, 3) in rows
+    for op, dt, H, vpt, wpr in rows:
+        vec = 16 // ES[dt]
+        assert wpr > 1 and (-(-H // vec) - 1) % 64 == 0
+
+
+@pytest.mark.parametrize("args", [(-1, 64, 2, 0), (6, 64, 2, 0), (0, 64, 2, 2), (0, 0, 2, 0), (0, 64, 9, 0)])
+def test_tile_query_rejects_bad_arguments(args):
+    import ctypes
+    lib = _lib()
+    out = (ctypes.c_int32 * 6)()
+    op, H, dt, layout = args
+    assert lib.rmsnorm_tuning_tile(op, H, dt, layout, out) != 0
+
+
+def test_tile_query_aligned_rows():
+    # the headline forward: bf16 rows of 4096 on the grid take 2 vectors per
+    # thread over 4 waves, one row per workgroup
+    t = tn.tile("fwd", 4096, "bf16", off_grid=False)
+    assert (t["vec"], t["vpt"], t["wpr"], t["mis"], t["multi_pass"]) == (8, 2, 4, False, False)
+    t = tn.tile("bwd", 6144, "bf16", off_grid=False)
+    assert t["vec"] == 8 and not t["mis"] and not t["multi_pass"]
+    assert 64 * t["wpr"] * t["vpt"] >= 768

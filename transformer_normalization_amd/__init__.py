@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_tuning_set_geometry.restype = None
         lib.rmsnorm_tuning_set_streaming.argtypes = [i32]
         lib.rmsnorm_tuning_set_streaming.restype = None
+        lib.rmsnorm_tuning_tile.argtypes = [i32, i64, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+        lib.rmsnorm_tuning_tile.restype = i32
         if path == LIB_PATH:
             _lib = lib
         return lib
@@ -469,6 +471,22 @@ def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: i
     library's own choice."""
     code = {"fwd": 0, "bwd": 1, "rope": 2}[which]
     load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))
+
+
+_TILE_OPS = {"fwd": 0, "fwd_residual": 1, "adaln": 2, "layernorm": 3, "bwd": 4, "bwd_residual": 5}
+_DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+def tile(op: str, H: int, dtype: str, off_grid: bool) -> dict:
+    """Development hook (include/rmsnorm_tuning.h), host only: the register
+    tile the library picks for `op` at row length H in `dtype` ("f32", "f16",
+    "bf16"), for rows on the 16-byte grid (off_grid False) or rows whose
+    starts are only element-aligned (True)."""
+    lib = load_library()
+    out = (ctypes.c_int32 * 6)()
+    _check(lib, lib.rmsnorm_tuning_tile(_TILE_OPS[op], int(H), _DTYPE_NAMES[dtype], 1 if off_grid else 0, out))
+    return {"vec": out[0], "vpt": out[1], "wpr": out[2], "rpw": out[3], "mis": bool(out[4]),
+            "multi_pass": bool(out[5])}
 
 
 def copy_reference(src, dst) -> None:

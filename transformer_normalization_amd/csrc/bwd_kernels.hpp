@@ -200,6 +200,16 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     for (int e = 0; e < VEC; ++e) part = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, part);
                     if (t + k * row_threads < p.nvec) acc += part;
                 }
+                // Off the grid, the window lane's leading columns are another
+                // lane's too, possibly in another wave, and dh may be the same
+                // buffer as dres.  x and dy have returned here (the row sum
+                // used them), but nothing else waits for dres before another
+                // wave stores over it: take it now, so that every load of the
+                // row has returned, in every wave, before any store of dh.
+                if constexpr (MIS && RES) {
+#pragma unroll
+                    for (int k = 0; k < VPT; ++k) gr[k].opaque();
+                }
                 const float c = row_sum(acc, p.wpr, wave, &red[j & 1][0]);
                 const float s = (c * p.inv_h) * rs;
 #pragma unroll

@@ -189,17 +189,12 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     rr[k].widen_to(rv);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                    // Aligned rows: each element is read and written by one
+                    // thread, so r_out may go out now.  Off the grid it waits
+                    // for the row barrier (below).
                     const int v = t + k * row_threads;
-                    if (p.ro != nullptr && valid && v < p.nvec) {
-                        if constexpr (MIS) {
-                            u32x4 raw;
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(hv + q * (4 / ES));
-                            store16_at<NT>(static_cast<char *>(p.ro) + (row * p.ros + col0[k]) * ES, raw);
-                        } else {
-                            store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
-                        }
-                    }
+                    if (!MIS && p.ro != nullptr && valid && v < p.nvec)
+                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
                 }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
@@ -233,6 +228,23 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                         rr[k].widen_to(rv);
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
+                    }
+                    if constexpr (RESID && MIS) {
+                        // Off the grid, the window lane's leading columns are
+                        // another lane's too, possibly in another wave.  When
+                        // r_out is the same buffer as x or r, a store of them
+                        // made before the window lane's load returned would
+                        // change what it reads.  Here every load of the row
+                        // has returned (the sum of squares used each one), in
+                        // every wave of the row: several waves passed the
+                        // row barrier, and a one-wave row issues its stores
+                        // after its own loads.
+                        if (p.ro != nullptr) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(hv + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.ro) + (row * p.ros + col0[k]) * ES, raw);
+                        }
                     }
                     wr[k].widen_to(wv);
                     if constexpr (ADALN) {

@@ -151,14 +151,13 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
             for (int k = 0; k < VPT; ++k) {
                 float hv[VEC];
                 widen_h(k, hv);
-                if constexpr (RESID) {
+                // Aligned rows: each element is read and written by one
+                // thread, so r_out may go out now.  Off the grid it waits for
+                // the row's reductions (below).
+                if constexpr (RESID && !MIS) {
                     const int v = t + k * row_threads;
-                    if (p.ro != nullptr && valid && v < p.nvec) {
-                        if constexpr (MIS)
-                            store_window(p.ro, row * p.ros, k, hv);
-                        else
-                            store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
-                    }
+                    if (p.ro != nullptr && valid && v < p.nvec)
+                        store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
                 }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) s1 += MIS && e < dup[k] ? 0.0f : hv[e];
@@ -204,6 +203,15 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                 if (valid && v < p.nvec) {
                     float hv[VEC], wv[VEC], bv[VEC], o[VEC];
                     widen_h(k, hv);
+                    // Off the grid, the window lane's leading columns are
+                    // another lane's too, possibly in another wave; r_out may
+                    // be the same buffer as x or r.  Every load of the row has
+                    // returned here (both sums used each one), in every wave
+                    // of the row, so this store cannot change what any lane
+                    // reads.
+                    if constexpr (RESID && MIS) {
+                        if (p.ro != nullptr) store_window(p.ro, row * p.ros, k, hv);
+                    }
                     wr[k].widen_to(wv);
                     br[k].widen_to(bv);
 #pragma unroll

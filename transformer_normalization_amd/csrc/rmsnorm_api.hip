@@ -163,6 +163,32 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
     return g;
 }
 
+// The forward family's tile with no forced geometry (vec_ok, mis_ok as for
+// bwd_tile; mis_ok also needs the bias and AdaLN's conditioning rows
+// aligned).  Rows off the 16-byte grid take 16-byte vectors at each row's
+// byte offset when the row holds at least 512 bytes and fits the resident
+// tile: RMSNorm rows from 1 KiB on the off-grid tile rule, shorter rows,
+// AdaLN and LayerNorm on the aligned rule.  Measured on gfx950 against the
+// element-wise tile (bf16, 2^25 elements): H = 257 49.5 % against 37.4 % of
+// peak, H = 511 68.9 % and 56.3 %, but H = 127 27.8 % and 31.3 % (16 vectors
+// leave most of a wave idle); LayerNorm against the LDS staging it replaced:
+// float32 fused residual H = 1023 70.5 % against 63.7 %, bf16 H = 4097 55.5 %
+// and 51.9 %.  Otherwise the element-wise tile.
+Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
+    const int vecw = 16 / eb;
+    const bool rms = kind == Kind::Fwd || kind == Kind::FwdResid;
+    *mis = false;
+    if (!vec_ok && mis_ok && H * eb >= 512) {
+        Geom m = rms && H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
+        if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
+        if (!m.two_pass) {
+            *mis = true;
+            return m;
+        }
+    }
+    return pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
+}
+
 // ---------------------------------------------------------------------------
 // kernel tables
 // ---------------------------------------------------------------------------
@@ -254,37 +280,19 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
 
     const Kind kind = ln ? Kind::Ln : resid ? Kind::FwdResid : adaln ? Kind::FwdAdaln : Kind::Fwd;
     const Override ov = get_override(0);
-    // Rows off the 16-byte grid take 16-byte vectors at each row's byte
-    // offset (one unaligned access per vector), when every row start is
-    // element-aligned, the weight (and bias) is 16-byte aligned (AdaLN's
-    // conditioning rows: element-aligned), the row holds at least 512 bytes
-    // and fits the resident tile: RMSNorm rows from 1 KiB on the off-grid tile
-    // rule, shorter rows, AdaLN and LayerNorm on the aligned rule.  Measured on
-    // gfx950 against the element-wise tile (bf16, 2^25 elements): H = 257
-    // 49.5 % against 37.4 % of peak, H = 511 68.9 % and 56.3 %, but H = 127
-    // 27.8 % and 31.3 % (16 vectors leave most of a wave idle); LayerNorm
-    // against the LDS staging it replaced: float32 fused residual H = 1023
-    // 70.5 % against 63.7 %, bf16 H = 4097 55.5 % and 51.9 %.  Otherwise, or
-    // with a forced geometry, the element-wise tile.
-    Geom g{};
+    // rows off the grid: every row start element-aligned, the weight (and
+    // bias) 16-byte aligned; a forced geometry keeps the element-wise tile
+    const bool mis_ok = !vec_ok && !ov.set && (w == nullptr || aligned16(w)) &&
+                        (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
+                        (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb)))) &&
+                        (!adaln || (aligned_to(cond.scale, pb) && aligned_to(cond.shift, pb)));
     bool mis = false;
-    if (!vec_ok && !ov.set && H * eb >= 512 && (w == nullptr || aligned16(w)) &&
-        (bias == nullptr || aligned16(bias)) && aligned_to(x, eb) && aligned_to(y, eb) &&
-        (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb)))) &&
-        (!adaln || (aligned_to(cond.scale, pb) && aligned_to(cond.shift, pb)))) {
-        Geom m = !ln && !adaln && H * eb >= 1024 ? pick_offgrid_geom(kind, (int)H, vecw) : Geom{};
-        if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, (int)H, vecw, eb == 4 ? 8 : 16);
-        if (!m.two_pass) {
-            g = m;
-            mis = true;
-        }
-    }
-    if (!mis) g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
+    Geom g = fwd_tile(kind, (int)H, eb, vec_ok, mis_ok, &mis);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     if (ov.set) {
         // bounds first: the products below are then small
         if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16 || ov.c < 0 || ov.c > 16)
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: tile vpt %d wpr %d rpw %d out of range", ov.a, ov.b,
+            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: tile vpt %d wpr %d rpw %d out of range", ov.a, ov.b,
                         ov.c);
         Geom o = g;
         o.vpt = ov.a;
@@ -292,13 +300,13 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         o.rpw = ov.c > 0 ? ov.c : 1;
         const int maxt = max_threads_for(kind, o.vpt, o.vec);
         if (o.vpt < 1 || o.wpr < 1 || o.wpr * o.rpw * 64 > maxt || o.wpr * o.rpw > 16)
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: bad tile vpt %d wpr %d rpw %d (max %d threads)",
+            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: bad tile vpt %d wpr %d rpw %d (max %d threads)",
                         o.vpt, o.wpr, o.rpw, maxt);
         const int chunk = 64 * o.wpr * o.vpt;
         o.nchunks = (o.nvec + chunk - 1) / chunk;
         o.two_pass = o.nchunks > 1;
         if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_FWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
         g = o;
         grid = (M + g.rpw - 1) / g.rpw;
         if (ov.d > 0 && ov.d < grid) grid = ov.d;
@@ -445,6 +453,35 @@ Geom pick_bwd_elem_geom(Kind kind, int H, int *groups_per_cu) {
     return g;
 }
 
+// The backward's tile with no forced geometry.  vec_ok: every row start is
+// 16-byte aligned and H a whole number of vectors.  mis_ok: otherwise, every
+// row start element-aligned and w 16-byte aligned.  Rows off the grid take
+// 16-byte vectors at their byte offset when the row holds at least 16 bytes
+// and fits one pass; otherwise rows from 512 elements take the single-element
+// rule (*elem_groups = its workgroups per CU), shorter ones the vector rule's
+// single-element tile.
+Geom bwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis, int *elem_groups) {
+    const int vecw = 16 / eb;
+    Geom g = pick_row_geom(kind, H, vec_ok ? vecw : 1, 8);
+    *mis = false;
+    *elem_groups = 0;
+    if (!vec_ok && mis_ok && H * eb >= 16) {
+        const Geom m = pick_row_geom(kind, H, vecw, 8);
+        if (!m.two_pass) {
+            g = m;
+            *mis = true;
+        }
+    }
+    if (!vec_ok && !*mis && H >= 512) {
+        const Geom e = pick_bwd_elem_geom(kind, H, elem_groups);
+        if (e.two_pass)
+            *elem_groups = 0;
+        else
+            g = e;
+    }
+    return g;
+}
+
 size_t bwd_workspace(int64_t M, int64_t H) {
     if (M <= 0 || H <= 0 || H > kMaxH) return 0;
     const int64_t cap = max_partials(H);
@@ -514,46 +551,29 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
                         (w == nullptr || aligned16(w)) && (!res || (aligned16(dres) && drs % (16 / eb) == 0));
     const Kind kind = res ? Kind::BwdRes : Kind::Bwd;
     const Override ov = get_override(1);
-    Geom g = pick_row_geom(kind, (int)H, vec_ok ? vecw : 1, 8);
+    const bool mis_ok = !vec_ok && !ov.set && aligned_to(dy, eb) && aligned_to(x, eb) && aligned_to(dx, eb) &&
+                        (!res || aligned_to(dres, eb)) && (w == nullptr || aligned16(w));
     int elem_groups = 0;  // workgroups per CU of the single-element rule, 0: the vector tile's rule
-    // Rows off the grid take 16-byte vectors at their byte offset when every
-    // row start is element-aligned, w is 16-byte aligned and the row holds at
-    // least 16 bytes and fits one pass; a forced geometry keeps the
-    // single-element tile.
     bool mis = false;
-    if (!vec_ok && !ov.set && H * eb >= 16 && aligned_to(dy, eb) && aligned_to(x, eb) && aligned_to(dx, eb) &&
-        (!res || aligned_to(dres, eb)) && (w == nullptr || aligned16(w))) {
-        const Geom m = pick_row_geom(kind, (int)H, vecw, 8);
-        if (!m.two_pass) {
-            g = m;
-            mis = true;
-        }
-    }
-    if (!vec_ok && !mis && H >= 512) {
-        const Geom e = pick_bwd_elem_geom(kind, (int)H, &elem_groups);
-        if (e.two_pass)
-            elem_groups = 0;
-        else
-            g = e;
-    }
+    Geom g = bwd_tile(kind, (int)H, eb, vec_ok, mis_ok, &mis, &elem_groups);
     int64_t P = 0;  // 0: chosen from the device below
     // rows interleaved across workgroups: the rows in flight at any moment are
     // neighbours in memory, as in the forward's one-row-per-workgroup grid
     bool interleave = true;
     if (ov.set) {
         if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16)
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: tile vpt %d wpr %d out of range", ov.a, ov.b);
+            return fail(RMSN_ERR_INVALID_ARG, "forced backward geometry: tile vpt %d wpr %d out of range", ov.a, ov.b);
         Geom o = g;
         o.vpt = ov.a;
         o.wpr = ov.b;
         const int maxt = max_threads_for(kind, o.vpt, o.vec);
         if (o.vpt < 1 || o.wpr < 1 || o.wpr * 64 > maxt)
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: bad tile vpt %d wpr %d", o.vpt, o.wpr);
+            return fail(RMSN_ERR_INVALID_ARG, "forced backward geometry: bad tile vpt %d wpr %d", o.vpt, o.wpr);
         const int chunk = 64 * o.wpr * o.vpt;
         o.nchunks = (o.nvec + chunk - 1) / chunk;
         o.two_pass = o.nchunks > 1;
         if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
-            return fail(RMSN_ERR_INVALID_ARG, "RMSN_BWD_GEOM: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+            return fail(RMSN_ERR_INVALID_ARG, "forced backward geometry: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
         g = o;
         elem_groups = 0;
         if (ov.c > 0) P = ov.c;
@@ -716,6 +736,29 @@ RMSN_API void rmsnorm_tuning_set_streaming(int mode) { set_stream_mode(mode); }
 
 RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t grid) {
     set_override(which, vpt, wpr, third, grid);
+}
+
+RMSN_API rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dtype, int layout, int32_t out[6]) {
+    if (out == nullptr) return fail(RMSN_ERR_INVALID_ARG, "out is NULL");
+    if (op < 0 || op > 5) return fail(RMSN_ERR_INVALID_ARG, "op = %d must be 0 .. 5", op);
+    if (layout != 0 && layout != 1) return fail(RMSN_ERR_INVALID_ARG, "layout = %d must be 0 or 1", layout);
+    rmsn_status_t st = check_common(0, H, x_dtype, nullptr, x_dtype);
+    if (st != RMSN_OK) return st;
+    static const Kind kinds[6] = {Kind::Fwd, Kind::FwdResid, Kind::FwdAdaln, Kind::Ln, Kind::Bwd, Kind::BwdRes};
+    const Kind kind = kinds[op];
+    const int eb = dtype_bytes(x_dtype);
+    const bool vec_ok = layout == 0 && H % (16 / eb) == 0;
+    bool mis = false;
+    int elem_groups = 0;
+    const Geom g = op >= 4 ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
+                           : fwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis);
+    out[0] = g.vec;
+    out[1] = g.two_pass ? 0 : g.vpt;
+    out[2] = g.two_pass ? 0 : g.wpr;
+    out[3] = op >= 4 ? 1 : g.rpw;
+    out[4] = mis ? 1 : 0;
+    out[5] = g.two_pass ? 1 : 0;
+    return ok();
 }
 
 }  // extern "C"

@@ -41,9 +41,14 @@
  *    the stream, as with any HIP kernel).  rmsnorm_last_error() returns a
  *    message for the most recent failure on the calling thread.
  *  - All entry points are thread-safe and keep no state between calls,
- *    apart from a per-device cache of the compute-unit count.
+ *    apart from a per-device cache of the compute-unit count.  The one
+ *    process-wide setting is the development override of rmsnorm_tuning.h,
+ *    which is off unless a caller sets it through that header's functions
+ *    (no environment variable or other input reaches it).
  *  - Results do not depend on the stream, on timing or on other calls: the
- *    same inputs give the same bits on the same device.
+ *    same inputs give the same bits on the same device.  A tile forced
+ *    through rmsnorm_tuning_set_geometry() changes the order of the float32
+ *    sums, and so may change bits, within the same tolerances.
  */
 #ifndef RMSNORM_H
 #define RMSNORM_H

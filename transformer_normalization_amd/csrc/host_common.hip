@@ -139,50 +139,22 @@ bool use_streaming(int64_t bytes_moved) {
 void set_stream_mode(int mode) { g_stream_mode.store(mode < 0 ? -1 : mode > 0 ? 1 : 0); }
 
 // Launch-geometry override for tuning and for tests that must reach the
-// grid-stride and two-pass paths at small sizes.  Set through
-// rmsnorm_tuning_set_geometry() (include/rmsnorm_tuning.h) or, once per
-// process at first use, from the environment:
-//   RMSN_FWD_GEOM="vpt,wpr,rpw,grid"   (grid 0 = one workgroup per row group)
-//   RMSN_BWD_GEOM="vpt,wpr,P,order"
-//   RMSN_ROPE_GEOM="1,1,0,grid"
+// grid-stride and two-pass paths at small sizes, set only through
+// rmsnorm_tuning_set_geometry() (include/rmsnorm_tuning.h): slot 0 forward,
+// 1 backward, 2 RoPE.  Nothing else (no environment variable) changes it.
 namespace {
 std::mutex g_override_mu;
 Override g_override[3];
 std::atomic<bool> g_override_any{false};
-std::once_flag g_override_env_once;
 }  // namespace
 
-static Override parse_override(const char *var) {
-    Override o;
-    const char *s = getenv(var);
-    if (s == nullptr || *s == '\0') return o;
-    long long v[4] = {0, 0, 0, 0};
-    int n = sscanf(s, "%lld,%lld,%lld,%lld", &v[0], &v[1], &v[2], &v[3]);
-    if (n >= 2) {
-        o.set = true;
-        o.a = (int)v[0];
-        o.b = (int)v[1];
-        o.c = (int)v[2];
-        o.d = v[3];
-    }
-    return o;
-}
-
 Override get_override(int which) {
-    std::call_once(g_override_env_once, []() {
-        std::lock_guard<std::mutex> lk(g_override_mu);
-        g_override[0] = parse_override("RMSN_FWD_GEOM");
-        g_override[1] = parse_override("RMSN_BWD_GEOM");
-        g_override[2] = parse_override("RMSN_ROPE_GEOM");
-        g_override_any.store(g_override[0].set || g_override[1].set || g_override[2].set);
-    });
     if (!g_override_any.load(std::memory_order_relaxed)) return Override{};
     std::lock_guard<std::mutex> lk(g_override_mu);
     return g_override[which];
 }
 
 void set_override(int which, int a, int b, int c, int64_t d) {
-    get_override(0);  // the environment is read first, so a later call wins
     std::lock_guard<std::mutex> lk(g_override_mu);
     if (which < 0 || which > 2) return;
     Override o;

@@ -25,7 +25,11 @@ read, half written) with the kernels' access pattern and no arithmetic: the
 practical HBM ceiling of a transfer of that size, beside the 8 TB/s peak.
 
 The CPU baseline is the float64 oracle run on the host over a sample of the
-same workload (reported beside the GPU figure, never a target).
+same workload, at one thread and at every thread the process may use (up to
+16), each the median of three runs (reported beside the GPU figure, never a
+target).  `spread` gives the per-step minimum, median, maximum and standard
+deviation from a second pass with an event after every step, and `device`
+what ran it.
 """
 
 from __future__ import annotations
@@ -46,6 +50,7 @@ METRIC = "RMSNorm fwd achieved HBM GB/s (% of peak) + rows/s, bf16 M=8192 H=4096
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 ROTATION_BYTES = 1 << 30
 GRAPH_BLOCK = 100  # steps per captured graph
+SPREAD_BLOCK = 20  # steps per timed block of the spread pass
 
 _FWD = ("numerics.hpp", "fwd_kernels.hpp", "fwd_table.hpp", "kernel_tables.hpp")
 _BWD = ("numerics.hpp", "bwd_kernels.hpp", "bwd_table.hpp", "kernel_tables.hpp", "kernels_bwd.hip")
@@ -175,10 +180,34 @@ def step_rows(spec):
     return spec["B"] * spec["S"] if spec["kind"] == "rope" else spec["M"]
 
 
-def cpu_baseline(spec, weighted, seconds):
-    """The oracle as it stands, single-threaded, over a leading sample of the
-    workload repeated until `seconds` have passed; reported in GB/s of the
-    same algorithmic bytes."""
+def host_threads() -> int:
+    """Threads the oracle may use: the CPUs this process may run on, capped
+    at 16 (one GPU's share of its host's cores)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
+def cpu_baseline(spec, weighted, seconds, runs=3):
+    """The oracle as it stands (float64 C through ctypes, which releases the
+    GIL), over a leading sample of the workload, at one thread and at
+    host_threads() threads; each thread takes a contiguous block of the
+    sample's rows (positions, for RoPE) per pass.  Each figure is the median
+    of `runs` independent runs, each repeating passes for about
+    seconds / (2 * runs); reported in GB/s of the same algorithmic bytes."""
+    import statistics
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
@@ -186,12 +215,12 @@ def cpu_baseline(spec, weighted, seconds):
 
     kind = spec["kind"]
     if kind == "rope":
-        n = min(spec["S"], 256)
+        n = min(spec["S"], 512)
         d = synthetic.make_inputs(spec["name"], rows=n)
         sample = f"first {n} of {spec['S']} positions of each of {spec['B']} batches"
         rows = spec["B"] * n
     else:
-        n = min(spec["M"], 1024)
+        n = min(spec["M"], 2048)
         d = synthetic.make_inputs(spec["name"], rows=n)
         sample = f"first {n} of {spec['M']} rows"
         rows = n
@@ -201,46 +230,79 @@ def cpu_baseline(spec, weighted, seconds):
             _, r = oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
             r32 = r.astype(np.float32)
 
-    def once():
+    def block(a, b):
+        """The oracle over sample rows [a, b) (positions, for RoPE)."""
         if kind == "rope":
-            oracle.rope(d["x"], d["cos"], d["sin"], d["dtype"], d["tdtype"])
+            oracle.rope(np.ascontiguousarray(d["x"][:, a:b]), d["cos"][a:b], d["sin"][a:b], d["dtype"], d["tdtype"])
         elif kind == "fwd":
-            oracle.fwd(d["x"], w, eps, d["dtype"], d["wdtype"])
+            oracle.fwd(d["x"][a:b], w, eps, d["dtype"], d["wdtype"])
         elif kind == "adaln":
-            oracle.adaln_fwd(d["x"], w, d["scale"], d["shift"], d["rows_per_cond"], eps, d["dtype"], d["wdtype"],
-                             d["wdtype"])
+            # row i reads conditioning row i // rpc: blocks are cut at the
+            # conditioning rows' boundaries so each call keeps that map
+            rpc = d["rows_per_cond"]
+            if rpc == 1:
+                oracle.adaln_fwd(d["x"][a:b], w, d["scale"][a:b], d["shift"][a:b], 1, eps, d["dtype"], d["wdtype"],
+                                 d["wdtype"])
+            else:
+                i = a
+                while i < b:
+                    c = i // rpc
+                    e = min(b, (c + 1) * rpc)
+                    oracle.adaln_fwd(d["x"][i:e], w, d["scale"][c:c + 1], d["shift"][c:c + 1], e - i, eps,
+                                     d["dtype"], d["wdtype"], d["wdtype"])
+                    i = e
         elif kind == "fwd_residual":
-            oracle.fwd_residual(d["x"], d["r"], w, eps, d["dtype"], d["wdtype"])
+            oracle.fwd_residual(d["x"][a:b], d["r"][a:b], w, eps, d["dtype"], d["wdtype"])
         elif kind == "ln_residual":
-            oracle.layernorm(d["x"], d["r"], w, d["b"] if weighted else None, eps, d["dtype"], d["wdtype"])
+            oracle.layernorm(d["x"][a:b], d["r"][a:b], w, d["b"] if weighted else None, eps, d["dtype"],
+                             d["wdtype"])
         elif kind == "bwd_residual":
-            oracle.bwd_residual(d["dy"], d["x"], d["dres"], w, r32, d["dtype"], d["wdtype"])
+            return oracle.bwd_residual(d["dy"][a:b], d["x"][a:b], d["dres"][a:b], w, r32[a:b], d["dtype"],
+                                       d["wdtype"])[1]
         else:
-            oracle.bwd(d["dy"], d["x"], w, r32, d["dtype"], d["wdtype"])
+            return oracle.bwd(d["dy"][a:b], d["x"][a:b], w, r32[a:b], d["dtype"], d["wdtype"])[1]
+        return None
 
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        once()
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    nbytes = algorithmic_bytes(spec, weighted, n) * passes
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
-    except OSError:
-        pass
+    nthreads = host_threads()
+    run_s = max(seconds, 0.0) / (2 * runs)
+    nbytes = algorithmic_bytes(spec, weighted, n)
+
+    def measure(threads):
+        bounds = [(n * i // threads, n * (i + 1) // threads) for i in range(threads)]
+        bounds = [(a, b) for a, b in bounds if b > a]
+        rates = []
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            for _ in range(runs):
+                passes = 0
+                t0 = time.perf_counter()
+                while True:
+                    parts = list(pool.map(lambda ab: block(*ab), bounds))
+                    if parts and parts[0] is not None:  # the backward's dw: the blocks' column sums added
+                        sum(parts[1:], parts[0].copy())
+                    passes += 1
+                    el = time.perf_counter() - t0
+                    if el >= run_s:
+                        break
+                rates.append((nbytes * passes / el, rows * passes / el, passes, el))
+        return rates
+
+    one = measure(1)
+    many = measure(nthreads) if nthreads > 1 else one
+    med = lambda rs, i: statistics.median(r[i] for r in rs)
     return {
-        "value": round(nbytes / el / 1e9, 4),
+        "value": round(med(many, 0) / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nthreads,
         "kind": "oracle",
-        "sample": f"{sample}, {passes} passes in {el:.1f} s, float64, one thread",
-        "cpu": f"{cpu} ({os.cpu_count()} logical CPUs visible)",
-        "rows_per_s": round(rows * passes / el, 1),
+        "sample": (f"{sample}; median of {runs} runs of about {run_s:.1f} s each, float64; "
+                   f"{nthreads} threads, each a contiguous block of the sample per pass"),
+        "rows_per_s": round(med(many, 1), 1),
+        "runs_gbs": [round(r[0] / 1e9, 4) for r in many],
+        "single_thread": {"value": round(med(one, 0) / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "rows_per_s": round(med(one, 1), 1), "runs_gbs": [round(r[0] / 1e9, 4) for r in one]},
+        "cpu": cpu_model(),
+        "nproc": os.cpu_count(),
+        "threads_available": nthreads,
     }
 
 
@@ -405,13 +467,32 @@ def copy_ceiling(per_step, dev, steps):
             "kind": "16-byte non-temporal copy, 256-thread workgroups of 8 KiB (rmsnorm_tuning_copy)"}
 
 
+def device_provenance(dev) -> dict:
+    """What ran the step: the device's architecture name and compute-unit
+    count as the runtime reports them, the HIP version torch was built
+    against, the installed ROCm release and the host's CPU count."""
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+        except OSError:
+            pass
+    return {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+            "hip": torch.version.hip, "rocm": rocm, "torch": torch.__version__, "host_nproc": os.cpu_count()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="fwd_bf16_8192x4096", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0 skips it)")
+    ap.add_argument("--cpu-seconds", type=float, default=18.0, help="oracle time budget, both thread counts together (0 skips it)")
     ap.add_argument("--graph", action="store_true", help="launch the timed steps from captured HIP graphs")
     ap.add_argument("--geom", default="",
                     help="development: forced launch geometry, four integers as rmsnorm_tuning_set_geometry takes")
@@ -503,6 +584,30 @@ def main():
     gbs = per_step / (ms * 1e-3) / 1e9
     rows = step_rows(spec)
 
+    # Spread: a second pass timed in blocks of SPREAD_BLOCK steps, an event
+    # at each block boundary (an event after every step adds its own cost to
+    # the step it follows: about 2.5 us on a 23 us forward), so each block
+    # gives one per-step time.
+    spread = None
+    n_blocks = min(args.steps // SPREAD_BLOCK, 50)
+    if not graphs and n_blocks >= 2:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_blocks + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for b in range(n_blocks):
+            for i in range(b * SPREAD_BLOCK, (b + 1) * SPREAD_BLOCK):
+                step(i)
+            evs[b + 1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(evs[b].elapsed_time(evs[b + 1]) / SPREAD_BLOCK for b in range(n_blocks))
+        mean = sum(per) / n_blocks
+        sd = (sum((v - mean) ** 2 for v in per) / (n_blocks - 1)) ** 0.5
+        med = per[n_blocks // 2] if n_blocks % 2 else 0.5 * (per[n_blocks // 2 - 1] + per[n_blocks // 2])
+        spread = {"blocks": n_blocks, "steps_per_block": SPREAD_BLOCK, "ms_min": round(per[0], 6),
+                  "ms_median": round(med, 6), "ms_max": round(per[-1], 6), "ms_mean": round(mean, 6),
+                  "ms_stddev": round(sd, 6), "gbs_at_median": round(per_step / (med * 1e-3) / 1e9, 2),
+                  "how": "per-step time of each block of a second eager pass, HIP events at block boundaries"}
+
     traffic = stored_traffic(args.workload)
     if kind == "rope":
         config = {"workload": args.workload, "batch": spec["B"], "seq_len": spec["S"], "heads": spec["NH"],
@@ -538,6 +643,9 @@ def main():
             "traffic": traffic,
         },
     }
+    if spread is not None:
+        result["spread"] = spread
+    result["device"] = device_provenance(dev)
     if not args.no_ceiling:
         result["copy_ceiling"] = copy_ceiling(per_step, dev, min(args.steps, 1000))
         result["copy_ceiling"]["step_over_copy"] = round(gbs / result["copy_ceiling"]["value"], 4)

@@ -160,9 +160,13 @@ def ln_vs_oracle(x, r, w, b, y_host, ro_host, mean_host, rstd_host, eps, dtype, 
     return tuple(reps.values())
 
 
-def assert_ok(*reports):
+def assert_ok(*reports, record=None):
+    """Fail on any failed element; `record` names a full-size workload whose
+    reports the session lists at its end."""
     for r in reports:
         print(r, flush=True)
+    if record is not None:
+        parity.record(record, *reports)
     bad = [str(r) for r in reports if not r.ok()]
     assert not bad, "; ".join(bad)
 

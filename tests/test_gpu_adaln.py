@@ -50,7 +50,7 @@ def test_workload_adaln(name):
     print(f"[gpu] {name}", flush=True)
     y, rr = run(d["x"], d["w"], d["scale"], d["shift"], B, S, d["eps"], d["dtype"], per_batch=rpc > 1)
     G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], d["scale"], d["shift"], rpc, y, rr, d["eps"], d["dtype"],
-                                   chunk=4096, name=name))
+                                   chunk=4096, name=name), record=name)
 
 
 @pytest.mark.parametrize("B,S", [(3, 6000), (3, 6001), (16, 1100)])

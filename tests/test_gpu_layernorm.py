@@ -53,9 +53,9 @@ def run_ln(x, r, w, b, eps, dtype, wdtype=None):
             rstd.cpu().numpy())
 
 
-def check(x, r, w, b, eps, dtype, wdtype=None, name="ln"):
+def check(x, r, w, b, eps, dtype, wdtype=None, name="ln", record=None):
     y, ro, mean, rstd = run_ln(x, r, w, b, eps, dtype, wdtype)
-    G.assert_ok(*G.ln_vs_oracle(x, r, w, b, y, ro, mean, rstd, eps, dtype, wdtype, name=name))
+    G.assert_ok(*G.ln_vs_oracle(x, r, w, b, y, ro, mean, rstd, eps, dtype, wdtype, name=name), record=record)
     return y, ro
 
 
@@ -63,7 +63,7 @@ def test_workload_ln_residual():
     name = "ln_residual_f32_16384x1024"
     d = synthetic.make_inputs(name)
     print(f"[gpu] {name}", flush=True)
-    check(d["x"], d["r"], d["w"], d["b"], d["eps"], d["dtype"], d["wdtype"], name=name)
+    check(d["x"], d["r"], d["w"], d["b"], d["eps"], d["dtype"], d["wdtype"], name=name, record=name)
 
 
 # 12288 and 16384 (16-bit) and 8192 (float32) take tiles capped at 4 waves per row

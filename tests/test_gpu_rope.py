@@ -88,7 +88,7 @@ def test_workload_rope(name):
     d = synthetic.make_inputs(name)
     print(f"[gpu] {name}", flush=True)
     got = run(d["x"], d["cos"], d["sin"], d["dtype"], d["tdtype"])
-    G.assert_ok(rope_vs_oracle(d["x"], d["cos"], d["sin"], got, d["dtype"], d["tdtype"], name=name))
+    G.assert_ok(rope_vs_oracle(d["x"], d["cos"], d["sin"], got, d["dtype"], d["tdtype"], name=name), record=name)
 
 
 # ---------------------------------------------------------------------------

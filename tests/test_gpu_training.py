@@ -73,7 +73,10 @@ def test_workload_bwd_residual():
     print(f"[gpu] {name}", flush=True)
     rr = oracle_rrms32(d["x"], d["w"], d["eps"], d["dtype"])
     dh, dw = run_bwd_residual(d["dy"], d["x"], d["dres"], d["w"], rr, d["dtype"])
-    G.assert_ok(*G.bwd_residual_vs_oracle(d["dy"], d["x"], d["dres"], d["w"], rr, dh, dw, d["dtype"], name=name))
+    rep_dh, rep_dw = G.bwd_residual_vs_oracle(d["dy"], d["x"], d["dres"], d["w"], rr, dh, dw, d["dtype"], name=name)
+    G.assert_ok(rep_dh, rep_dw, record=name)
+    assert rep_dh.floor_used <= 1e-4 * rep_dh.n, rep_dh
+    assert rep_dw.max_rel <= 1e-3, rep_dw
 
 
 RES_H = [1, 7, 64, 65, 513, 2049, 4096, 6144, 8191, 16385, 65536]

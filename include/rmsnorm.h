@@ -187,6 +187,30 @@ rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void *x, int6
                           rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype, hipStream_t stream);
 
 /*
+ * rmsnorm_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation, kernels and bits as rmsnorm_bwd, with no workspace
+ * argument: the dw partial rows live in a static device array of this
+ * library, 32 MiB, of which every device the library runs on holds one copy
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *
+ *   Arguments as rmsnorm_bwd.  The call needs P x H x 4 bytes of that array
+ *   when dw != NULL, with P the number of partial rows rmsnorm_bwd takes for
+ *   the shape on this device (256 for bf16 8192 x 6144 on a 256-CU MI355X: 6
+ *   MiB); a call needing more than 32 MiB is rejected with
+ *   RMSN_ERR_WORKSPACE before anything is enqueued.  With dw == NULL the
+ *   array is not used.
+ *   Every call on a device shares that device's array, and it keeps the last
+ *   call's partial rows; each call writes every row it reads, so nothing has
+ *   to be cleared.  Calls that may overlap in time on one device (other
+ *   streams, other threads) race on the array: order them on one stream.
+ */
+rmsn_status_t rmsnorm_bwd_noalloc(const void *dy, int64_t dy_stride, const void *x, int64_t x_stride,
+                                  const void *w, const float *rrms, void *dx, int64_t dx_stride, float *dw,
+                                  int64_t M, int64_t H, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
+                                  hipStream_t stream);
+
+/*
  * Backward of the fused residual pre-norm.  Its forward (rmsnorm_fwd_residual)
  * computes h = x + residual, y = RMSNorm(h) and writes h back as the next
  * residual stream, so h reaches the loss twice: through y and through

@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.rmsnorm_bwd_residual.argtypes = [vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, vp, vp, sz, i64, i64, i32,
                                              i32, vp]
         lib.rmsnorm_bwd.restype = i32
+        lib.rmsnorm_bwd_noalloc.argtypes = [vp, i64, vp, i64, vp, vp, vp, i64, vp, i64, i64, i32, i32, vp]
+        lib.rmsnorm_bwd_noalloc.restype = i32
         lib.rmsnorm_status_string.argtypes = [i32]
         lib.rmsnorm_status_string.restype = ctypes.c_char_p
         lib.rmsnorm_last_error.argtypes = []
@@ -328,6 +330,36 @@ def rmsnorm_bwd(dy, x, weight, rrms, dx=None, dw=None, workspace=None, want_dw: 
     Returns (dx, dw); dw (float32, shape (H,)) is None for a weightless norm
     or when want_dw is False.  dx may be dy or x itself."""
     return _bwd(dy, x, None, weight, rrms, dx, dw, workspace, want_dw)
+
+
+def rmsnorm_bwd_noalloc(dy, x, weight, rrms, dx, dw=None):
+    """rmsnorm_bwd for callers that cannot allocate (HIP graph capture,
+    serving loops): dx (and dw, float32 (H,), when weight is given) must be
+    passed in; the dw partial rows go to the library's static device scratch
+    (include/rmsnorm.h).  Calls that overlap in time on one device race on
+    that scratch.  Returns (dx, dw)."""
+    torch = _torch()
+    lib = load_library()
+    M, H, xs = _rows(x, "x")
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x in shape and dtype")
+    _, _, dys = _rows(dy, "dy")
+    if dx is None or dx.shape != x.shape or dx.dtype != x.dtype:
+        raise ValueError("dx must be given, matching x in shape and dtype")
+    _, _, dxs = _rows(dx, "dx")
+    if rrms.dtype != torch.float32 or rrms.numel() != M or not rrms.is_contiguous():
+        raise ValueError("rrms must be a contiguous float32 tensor with one value per row")
+    if weight is not None and (weight.numel() != H or not weight.is_contiguous()):
+        raise ValueError("weight must be a contiguous tensor of H elements")
+    if weight is None:
+        dw = None
+    elif dw is not None and (dw.dtype != torch.float32 or dw.numel() != H or not dw.is_contiguous()):
+        raise ValueError("dw must be a contiguous float32 tensor of H elements")
+    wcode = _dtype_code(weight) if weight is not None else _dtype_code(x)
+    st = lib.rmsnorm_bwd_noalloc(_ptr(dy), dys, _ptr(x), xs, _ptr(weight), _ptr(rrms), _ptr(dx), dxs, _ptr(dw), M, H,
+                                 _dtype_code(x), wcode, _stream(x))
+    _check(lib, st)
+    return dx, dw
 
 
 def rmsnorm_bwd_residual(dy, residual_out, dres, weight, rrms, dh=None, dw=None, workspace=None,

@@ -489,11 +489,55 @@ size_t bwd_workspace(int64_t M, int64_t H) {
     return (size_t)P * (size_t)H * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// static scratch of rmsnorm_bwd_noalloc
+// ---------------------------------------------------------------------------
+
+// The dw partial rows of rmsnorm_bwd_noalloc live here instead of a caller's
+// workspace: every device the library runs on holds one copy until the
+// process ends.  Each call writes every partial row it reads before reading
+// it, so nothing has to start at zero; calls that overlap on one device
+// share the array and race.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+    std::once_flag once;
+    hipError_t err = hipErrorUnknown;
+    void *ptr = nullptr;
+};
+ScratchSlot g_scratch[64];
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current.  In host code the array's name is only a
+// host-side stand-in; kernels receive this address.
+rmsn_status_t scratch_partials(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RMSN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(RMSN_ERR_HIP, "device index %d out of range", dev);
+    ScratchSlot &s = g_scratch[dev];
+    std::call_once(s.once, [&s]() {
+        void *p = nullptr;
+        s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (s.err == hipSuccess && p == nullptr) s.err = hipErrorInvalidSymbol;
+        if (s.err == hipSuccess) s.ptr = p;
+    });
+    if (s.err != hipSuccess)
+        return fail(RMSN_ERR_HIP, "looking up the scratch array on device %d failed: %s", dev,
+                    hipGetErrorString(s.err));
+    *out = s.ptr;
+    return RMSN_OK;
+}
+
 // dres == nullptr: the plain backward; otherwise the backward of the fused
 // residual pre-norm, which adds dres (rows drs apart) to dx.
+// use_scratch: the dw partial rows go to this library's static device array
+// (scratch_partials) instead of the caller's workspace, which is then ignored.
 rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, const void *dres, int64_t drs,
                        const void *w, const float *rrms, void *dx, int64_t dxs, float *dw, void *ws, size_t ws_bytes,
-                       int64_t M, int64_t H, rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream) {
+                       int64_t M, int64_t H, rmsn_dtype_t xdt, rmsn_dtype_t wdt, hipStream_t stream,
+                       bool use_scratch = false) {
     rmsn_status_t st = check_common(M, H, xdt, w, wdt);
     if (st != RMSN_OK) return st;
     const int eb = dtype_bytes(xdt);
@@ -510,8 +554,9 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (rrms == nullptr) return fail(RMSN_ERR_INVALID_ARG, "rrms is NULL");
         if (dx == nullptr) return fail(RMSN_ERR_INVALID_ARG, "dx is NULL");
     }
+    if (use_scratch) ws = nullptr;
     const size_t need = bwd_workspace(M, H);
-    if (dw != nullptr && M > 0) {
+    if (dw != nullptr && M > 0 && !use_scratch) {
         if (ws == nullptr || ws_bytes < need)
             return fail(RMSN_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0,
                         need);
@@ -596,6 +641,14 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;
     P = (M + rows_per - 1) / rows_per;
+    if (use_scratch && dw != nullptr) {
+        if ((uint64_t)P * (uint64_t)H * sizeof(float) > kScratchBytes)
+            return fail(RMSN_ERR_WORKSPACE,
+                        "the dw partial rows of this call (%lld x %lld float32) exceed the %zu-byte static scratch "
+                        "of rmsnorm_bwd_noalloc; call rmsnorm_bwd with a workspace",
+                        (long long)P, (long long)H, kScratchBytes);
+        if ((st = scratch_partials(&ws)) != RMSN_OK) return st;
+    }
 
     BwdParams p;
     p.dy = dy;
@@ -705,6 +758,15 @@ RMSN_API rmsn_status_t rmsnorm_bwd(const void *dy, int64_t dy_stride, const void
                           rmsn_dtype_t w_dtype, hipStream_t stream) {
     rmsn_status_t s = bwd_impl(dy, dy_stride, x, x_stride, nullptr, 0, w, rrms, dx, dx_stride, dw, workspace,
                                workspace_bytes, M, H, x_dtype, w_dtype, stream);
+    return s == RMSN_OK ? ok() : s;
+}
+
+RMSN_API rmsn_status_t rmsnorm_bwd_noalloc(const void *dy, int64_t dy_stride, const void *x, int64_t x_stride,
+                                           const void *w, const float *rrms, void *dx, int64_t dx_stride, float *dw,
+                                           int64_t M, int64_t H, rmsn_dtype_t x_dtype, rmsn_dtype_t w_dtype,
+                                           hipStream_t stream) {
+    rmsn_status_t s = bwd_impl(dy, dy_stride, x, x_stride, nullptr, 0, w, rrms, dx, dx_stride, dw, nullptr, 0, M,
+                               H, x_dtype, w_dtype, stream, true);
     return s == RMSN_OK ? ok() : s;
 }
 

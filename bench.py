@@ -437,19 +437,21 @@ def setup_steps(spec, weighted, dev, per_step):
     return step, nsets, copy_src, copy_dst
 
 
-def copy_ceiling(per_step, dev, steps):
+def copy_ceiling(per_step, dev, steps, offset=0):
     """The speed-of-light reference: rmsnorm_tuning_copy moving per_step
     bytes (half read, half written) with the forward kernels' access pattern
     and no arithmetic, over buffers rotated like the steps', timed the same
-    way."""
+    way.  offset > 0 starts both buffers that many bytes off the 16-byte
+    grid, so every access is an unaligned 16-byte one, as for rows off the
+    grid."""
     import torch
 
     import transformer_normalization_amd as tn
 
     half = max(16, (per_step // 2) // 16 * 16)
     nsets = max(2, -(-ROTATION_BYTES // (2 * half)))
-    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nsets)]
-    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    src = [torch.empty(half + 16, dtype=torch.uint8, device=dev).fill_(1)[offset:offset + half] for _ in range(nsets)]
+    dst = [torch.empty(half + 16, dtype=torch.uint8, device=dev)[offset:offset + half] for _ in range(nsets)]
     for i in range(50):
         tn.copy_reference(src[i % nsets], dst[i % nsets])
     stream = torch.cuda.current_stream(dev)
@@ -464,7 +466,8 @@ def copy_ceiling(per_step, dev, steps):
     gbs = 2 * half / (ms * 1e-3) / 1e9
     return {"value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(ms, 6), "bytes": 2 * half,
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "kind": "16-byte non-temporal copy, 256-thread workgroups of 8 KiB (rmsnorm_tuning_copy)"}
+            "kind": ("16-byte non-temporal copy, 256-thread workgroups of 8 KiB (rmsnorm_tuning_copy)"
+                     + (f", both buffers {offset} bytes off the 16-byte grid" if offset else ""))}
 
 
 def device_provenance(dev) -> dict:
@@ -649,6 +652,12 @@ def main():
     if not args.no_ceiling:
         result["copy_ceiling"] = copy_ceiling(per_step, dev, min(args.steps, 1000))
         result["copy_ceiling"]["step_over_copy"] = round(gbs / result["copy_ceiling"]["value"], 4)
+        if kernel_kind(spec) == "fwd_offgrid":
+            # rows off the grid make unaligned 16-byte accesses: the copy
+            # that makes the same ones
+            un = copy_ceiling(per_step, dev, min(args.steps, 1000), offset=2)
+            un["step_over_copy"] = round(gbs / un["value"], 4)
+            result["copy_ceiling_unaligned"] = un
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(spec, weighted, args.cpu_seconds)
     print(json.dumps(result), flush=True)

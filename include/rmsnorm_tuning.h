@@ -66,12 +66,15 @@ void rmsnorm_tuning_set_streaming(int mode);
 
 /*
  * Speed-of-light reference for measurements: copies `bytes` from src to dst
- * (device pointers, 16-byte aligned, bytes a multiple of 16, the two ranges
+ * (device pointers, 2-byte aligned, bytes a multiple of 16, the two ranges
  * disjoint) with the forward kernels' access pattern -- 256-thread
  * workgroups, two 16-byte vectors per thread, non-temporal loads and stores
  * -- and no arithmetic, so that a kernel's HBM rate can be compared with the
- * rate of moving the same bytes in the same way.  Enqueued on `stream`;
- * returns RMSN_ERR_INVALID_ARG for a bad argument.
+ * rate of moving the same bytes in the same way.  When src and dst are both
+ * 16-byte aligned every access is an aligned 16-byte one; otherwise every
+ * access is a 16-byte access at the element-aligned address, as the kernels
+ * for rows off the 16-byte grid make.  Enqueued on `stream`; returns
+ * RMSN_ERR_INVALID_ARG for a bad argument.
  */
 rmsn_status_t rmsnorm_tuning_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 

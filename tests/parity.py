@@ -63,6 +63,9 @@ class Report:
         self.floor_used = 0
         self.max_rel = 0.0
         self.first_bad = None
+        # float32 outputs and dw: the largest error as a fraction of the
+        # element's allowed error (<= 1 passes)
+        self.max_tol = 0.0
         # dw only: normwise error and well-conditioned columns
         self.err2 = 0.0
         self.ref2 = 0.0
@@ -83,7 +86,8 @@ class Report:
 
     def __str__(self):
         s = (f"{self.name}: {self.n} elements, {self.failed} failed, max ulp {self.max_ulp}, "
-             f"floor-judged {self.floor_used}, max rel {self.max_rel:.3g}, first bad {self.first_bad}")
+             f"floor-judged {self.floor_used}, max rel {self.max_rel:.3g}, "
+             f"max fraction of tolerance {self.max_tol:.3g}, first bad {self.first_bad}")
         if self.ref2 > 0:
             s += (f", normwise {self.normwise():.3g}, max rel over {self.wc_cols} well-conditioned columns "
                   f"{self.wc_max_rel:.3g}")
@@ -101,7 +105,7 @@ def record(workload: str, *reports: Report) -> None:
 def compact(r: Report) -> str:
     """One short line: elements, failed, max ulp, floor-judged, max relative
     error, and for dw the normwise and well-conditioned relative errors."""
-    s = f"{r.name}: n={r.n} fail={r.failed} ulp={r.max_ulp} floor={r.floor_used} rel={r.max_rel:.2g}"
+    s = f"{r.name}: n={r.n} fail={r.failed} ulp={r.max_ulp} floor={r.floor_used} rel={r.max_rel:.2g} tol={r.max_tol:.2g}"
     if r.ref2 > 0:
         s += f" norm={r.normwise():.2g} wc={r.wc_cols}:{r.wc_max_rel:.2g}"
     return s
@@ -124,10 +128,12 @@ def check16(report, got_bits, ref64, dtype, encode, offset=0):
 def check_f32(report, got, ref64, offset=0):
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref64)
-    bad = ~(err <= 1e-5 * np.abs(ref64) + 1e-6)
+    allowed = 1e-5 * np.abs(ref64) + 1e-6
+    bad = ~(err <= allowed)
     report.n += got.size
     if got.size:
         report.max_rel = max(report.max_rel, float((err / np.maximum(np.abs(ref64), 1e-30)).max()))
+        report.max_tol = max(report.max_tol, float(np.nanmax(err / allowed)))
     report.merge_bad(bad, offset)
     return report
 
@@ -150,10 +156,14 @@ def check_dx_f32(report, got, ref64, terms, offset=0):
     err = np.abs(got - ref64)
     strict = err <= 1e-5 * np.abs(ref64) + 1e-6
     relaxed = err <= 1e-5 * np.maximum(np.abs(ref64), 2.0 ** -4 * terms) + 1e-6
-    # relative error over the elements whose terms do not cancel
-    plain = np.abs(ref64) >= 2.0 ** -4 * terms
+    # relative error where the relative bound governs: terms that do not
+    # cancel, and |ref| >= 0.1 (below it the 1e-6 absolute term dominates)
+    plain = (np.abs(ref64) >= 2.0 ** -4 * terms) & (np.abs(ref64) >= 0.1)
     if np.any(plain):
-        report.max_rel = max(report.max_rel, float((err[plain] / np.maximum(np.abs(ref64[plain]), 1e-30)).max()))
+        report.max_rel = max(report.max_rel, float((err[plain] / np.abs(ref64[plain])).max()))
+    if got.size:
+        allowed = 1e-5 * np.maximum(np.abs(ref64), 2.0 ** -4 * terms) + 1e-6
+        report.max_tol = max(report.max_tol, float(np.nanmax(err / allowed)))
     report.n += got.size
     report.floor_used += int(np.count_nonzero(~strict & relaxed))
     report.merge_bad(~relaxed, offset)
@@ -167,6 +177,7 @@ def check_dw(report, got, ref64, colscale):
     rel = err / np.maximum(np.abs(ref64), 1e-30)
     report.n += got.size
     report.max_rel = max(report.max_rel, float(rel.max()))
+    report.max_tol = max(report.max_tol, float(np.nanmax(err / (1e-3 * np.abs(ref64) + 1e-5 * colscale))))
     report.err2 += float(np.sum(err * err))
     report.ref2 += float(np.sum(ref64 * ref64))
     wc = np.abs(ref64) >= 0.01 * colscale

@@ -130,11 +130,12 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     return g;
 }
 
-// Tile of the RMSNorm forward on rows off the 16-byte grid from 1 KiB (16-byte
-// vectors at the row's byte offset).  A lane without a vector costs no memory
-// traffic, and the fewer waves a row takes, the more rows a CU holds in
-// flight, so the cost is the row's waves plus 8 x the idle share of its slots,
-// over vpt <= 6; rows of at most three waves share a workgroup in pairs.
+// Tile of the RMSNorm forward (and 16-bit LayerNorm) on rows off the 16-byte
+// grid from 1 KiB (16-byte vectors at the row's byte offset).  A lane without
+// a vector costs no memory traffic, and the fewer waves a row takes, the more
+// rows a CU holds in flight, so the cost is the row's waves plus 8 x the idle
+// share of its slots, over vpt <= 6; rows of at most three waves share a
+// workgroup in pairs.
 // Measured on gfx950 (bf16, 2^25 elements) against the vector tile rule and
 // against the LDS staging this replaced: H = 2049 64.8 % (48.2 % on the vector
 // rule, 58.5 % staged), H = 4097 63.7 % (61.3 % staged; one row per
@@ -167,19 +168,25 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
 // bwd_tile; mis_ok also needs the bias and AdaLN's conditioning rows
 // aligned).  Rows off the 16-byte grid take 16-byte vectors at each row's
 // byte offset when the row holds at least 512 bytes and fits the resident
-// tile: RMSNorm rows from 1 KiB on the off-grid tile rule, shorter rows,
-// AdaLN and LayerNorm on the aligned rule.  Measured on gfx950 against the
-// element-wise tile (bf16, 2^25 elements): H = 257 49.5 % against 37.4 % of
-// peak, H = 511 68.9 % and 56.3 %, but H = 127 27.8 % and 31.3 % (16 vectors
-// leave most of a wave idle); LayerNorm against the LDS staging it replaced:
-// float32 fused residual H = 1023 70.5 % against 63.7 %, bf16 H = 4097 55.5 %
-// and 51.9 %.  Otherwise the element-wise tile.
+// tile: RMSNorm rows and 16-bit LayerNorm rows from 1 KiB on the off-grid
+// tile rule, shorter rows, AdaLN and float32 LayerNorm on the aligned rule.
+// Measured on gfx950 against the element-wise tile (bf16, 2^25 elements):
+// H = 257 49.5 % against 37.4 % of peak, H = 511 68.9 % and 56.3 %, but
+// H = 127 27.8 % and 31.3 % (16 vectors leave most of a wave idle);
+// LayerNorm against the LDS staging it replaced: float32 fused residual
+// H = 1023 70.5 % against 63.7 %, bf16 H = 4097 55.5 % and 51.9 %.
+// LayerNorm on the off-grid rule against the aligned one (2^25 elements or
+// more): bf16 H = 2049 57.3 % against 40.5 %, H = 6143 62.0 % against
+// 53.0 % (fused residual 64.8 % against 58.5 %), H = 4097 and 1025 within
+// 0.1 %; float32 H = 4097 the same, fused residual H = 1025 66.1 % against
+// 68.3 %, so float32 keeps the aligned rule.  Otherwise the element-wise
+// tile.
 Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
     const int vecw = 16 / eb;
-    const bool rms = kind == Kind::Fwd || kind == Kind::FwdResid;
+    const bool offrule = kind == Kind::Fwd || kind == Kind::FwdResid || (kind == Kind::Ln && eb == 2);
     *mis = false;
     if (!vec_ok && mis_ok && H * eb >= 512) {
-        Geom m = rms && H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
+        Geom m = offrule && H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
         if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
         if (!m.two_pass) {
             *mis = true;

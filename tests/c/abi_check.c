@@ -118,6 +118,40 @@ int main(void) {
     expect("bwd M == 0 without dw", rmsnorm_bwd(NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, NULL, 0, 0, H,
                                                 RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
 
+    /* the no-allocation backward validates as rmsnorm_bwd, with no workspace */
+    expect("noalloc dw without w", rmsnorm_bwd_noalloc(r, H, x, H, NULL, rr, y, H, dw, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("noalloc rrms NULL", rmsnorm_bwd_noalloc(r, H, x, H, w, NULL, y, H, dw, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("noalloc dx overlaps rrms", rmsnorm_bwd_noalloc(r, H, x, H, w, (float *)y, y, H, dw, M, H, RMSN_BF16,
+                                                           RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);
+    expect("noalloc stride < H", rmsnorm_bwd_noalloc(r, H - 1, x, H, w, rr, y, H, dw, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_INVALID_ARG);
+    expect("noalloc bad dtype", rmsnorm_bwd_noalloc(r, H, x, H, w, rr, y, H, dw, M, H, (rmsn_dtype_t)7, RMSN_BF16, 0),
+           RMSN_ERR_UNSUPPORTED);
+    expect("noalloc M == 0 without dw", rmsnorm_bwd_noalloc(NULL, H, NULL, H, NULL, NULL, NULL, H, NULL, 0, H,
+                                                            RMSN_BF16, RMSN_BF16, 0), RMSN_OK);
+    /* with valid arguments the call needs the device (the partial-row count
+       depends on its compute units): no device here, so a HIP error */
+    expect("noalloc needs the device", rmsnorm_bwd_noalloc(r, H, x, H, w, rr, y, H, dw, M, H, RMSN_BF16, RMSN_BF16, 0),
+           RMSN_ERR_HIP);
+
+    /* the tile query is host only */
+    {
+        int32_t t[6];
+        expect("tile query", rmsnorm_tuning_tile(0, 4096, RMSN_BF16, 0, t), RMSN_OK);
+        if (t[0] != 8 || t[1] * t[2] * 64 < 512 || t[4] != 0 || t[5] != 0) {
+            printf("FAIL tile query: vec %d vpt %d wpr %d mis %d multi %d\n", t[0], t[1], t[2], t[4], t[5]);
+            ++failures;
+        }
+        expect("tile query off grid", rmsnorm_tuning_tile(1, 4097, RMSN_BF16, 1, t), RMSN_OK);
+        if (t[4] != 1) { printf("FAIL tile query off grid: mis %d\n", t[4]); ++failures; }
+        expect("tile query NULL", rmsnorm_tuning_tile(0, 4096, RMSN_BF16, 0, NULL), RMSN_ERR_INVALID_ARG);
+        expect("tile query bad op", rmsnorm_tuning_tile(6, 4096, RMSN_BF16, 0, t), RMSN_ERR_INVALID_ARG);
+        expect("tile query H 0", rmsnorm_tuning_tile(0, 0, RMSN_BF16, 0, t), RMSN_ERR_INVALID_ARG);
+        expect("tile query bad dtype", rmsnorm_tuning_tile(0, 64, (rmsn_dtype_t)9, 0, t), RMSN_ERR_UNSUPPORTED);
+    }
+
     void *g = (void *)(uintptr_t)0xa00000000ull;
     expect("bwd_residual dres_stride < H", rmsnorm_bwd_residual(r, H, x, H, g, H - 8, w, rr, y, H, dw, ws, need, M,
                                                                 H, RMSN_BF16, RMSN_BF16, 0), RMSN_ERR_INVALID_ARG);

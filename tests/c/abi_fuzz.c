@@ -118,7 +118,7 @@ int main(int argc, char **argv) {
         /* sometimes force a launch geometry with extreme values first */
         if (next() % 8 == 0) rmsnorm_tuning_set_geometry(int_arg() % 4, int_arg(), int_arg(), int_arg(), size_arg());
         if (next() % 16 == 0) rmsnorm_tuning_set_streaming(int_arg());
-        switch (next() % 11) {
+        switch (next() % 13) {
         case 0:
             check("rmsnorm_fwd", rmsnorm_fwd(ptr_arg(), size_arg(), ptr_arg(), ptr_arg(), size_arg(), (float *)ptr_arg(),
                                              size_arg(), size_arg(), eps_arg(), dtype_arg(), dtype_arg(), NULL));
@@ -176,6 +176,18 @@ int main(int argc, char **argv) {
                 printf("FAIL rmsnorm_status_string: empty\n");
                 ++failures;
             }
+            break;
+        }
+        case 10:
+            check("rmsnorm_bwd_noalloc",
+                  rmsnorm_bwd_noalloc(ptr_arg(), size_arg(), ptr_arg(), size_arg(), ptr_arg(), (const float *)ptr_arg(),
+                                      ptr_arg(), size_arg(), (float *)ptr_arg(), size_arg(), size_arg(), dtype_arg(),
+                                      dtype_arg(), NULL));
+            break;
+        case 11: {
+            int32_t tile[6];
+            check("rmsnorm_tuning_tile", rmsnorm_tuning_tile(int_arg(), size_arg(), dtype_arg(), int_arg(),
+                                                             next() % 8 ? tile : NULL));
             break;
         }
         default:

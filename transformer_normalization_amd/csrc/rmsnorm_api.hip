@@ -185,8 +185,8 @@ Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
     const int vecw = 16 / eb;
     const bool offrule = kind == Kind::Fwd || kind == Kind::FwdResid || (kind == Kind::Ln && eb == 2);
     *mis = false;
-    if (!vec_ok && mis_ok && H * eb >= 512) {
-        Geom m = offrule && H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
+    if (!vec_ok && mis_ok && (int64_t)H * eb >= 512) {
+        Geom m = offrule && (int64_t)H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
         if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
         if (!m.two_pass) {
             *mis = true;
@@ -472,7 +472,7 @@ Geom bwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis, int
     Geom g = pick_row_geom(kind, H, vec_ok ? vecw : 1, 8);
     *mis = false;
     *elem_groups = 0;
-    if (!vec_ok && mis_ok && H * eb >= 16) {
+    if (!vec_ok && mis_ok && (int64_t)H * eb >= 16) {
         const Geom m = pick_row_geom(kind, H, vecw, 8);
         if (!m.two_pass) {
             g = m;

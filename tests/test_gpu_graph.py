@@ -36,12 +36,13 @@ def test_graph_replays_match_eager():
     ct, st = synthetic.rope_tables(91, S, D, "f32")
     cos, sin = G.to_dev(ct, "f32"), G.to_dev(st, "f32")
 
-    outs = {k: torch.empty_like(x) for k in ("y", "y2", "ro", "dx", "dh", "ya")}
+    outs = {k: torch.empty_like(x) for k in ("y", "y2", "ro", "dx", "dh", "ya", "dx3")}
     outs["q"] = torch.empty_like(q)
     rr = torch.empty(M, dtype=torch.float32, device=G.DEV)
     rr2 = torch.empty(M, dtype=torch.float32, device=G.DEV)
     dw = torch.empty(H, dtype=torch.float32, device=G.DEV)
     dw2 = torch.empty(H, dtype=torch.float32, device=G.DEV)
+    dw3 = torch.empty(H, dtype=torch.float32, device=G.DEV)
     ws = torch.empty(tn.rmsnorm_bwd_workspace_bytes(M, H), dtype=torch.uint8, device=G.DEV)
     ws2 = torch.empty_like(ws)
 
@@ -52,21 +53,26 @@ def test_graph_replays_match_eager():
         tn.rmsnorm_bwd_residual(dy, outs["ro"], r, w, rr2, dh=outs["dh"], dw=dw2, workspace=ws2)
         tn.rmsnorm_adaln_fwd(x, w, sc, sh, eps, out=outs["ya"])
         tn.rope_apply(q, cos, sin, out=outs["q"])
+        # the backward with its partial rows in the library's static scratch:
+        # nothing to allocate or clear inside the capture
+        tn.rmsnorm_bwd_noalloc(dy, x, w, rr, outs["dx3"], dw3)
 
     calls()  # eager, also caches the device facts before capture
     torch.cuda.synchronize()
     want = {k: _bits(v).clone() for k, v in outs.items()}
-    want.update(rr=_bits(rr).clone(), rr2=_bits(rr2).clone(), dw=_bits(dw).clone(), dw2=_bits(dw2).clone())
+    want.update(rr=_bits(rr).clone(), rr2=_bits(rr2).clone(), dw=_bits(dw).clone(), dw2=_bits(dw2).clone(),
+                dw3=_bits(dw3).clone())
+    assert torch.equal(want["dx3"], want["dx"]) and torch.equal(want["dw3"], want["dw"])
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream(G.DEV)
-    for t in list(outs.values()) + [rr, rr2, dw, dw2]:
+    for t in list(outs.values()) + [rr, rr2, dw, dw2, dw3]:
         t.fill_(0)
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=side):
         calls()
     for rep in range(3):
-        for t in list(outs.values()) + [rr, rr2, dw, dw2]:
+        for t in list(outs.values()) + [rr, rr2, dw, dw2, dw3]:
             t.fill_(0)
         # unrelated eager work between replays
         _ = (x.float() * 2).sum()
@@ -74,7 +80,7 @@ def test_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         got = {k: _bits(v) for k, v in outs.items()}
-        got.update(rr=_bits(rr), rr2=_bits(rr2), dw=_bits(dw), dw2=_bits(dw2))
+        got.update(rr=_bits(rr), rr2=_bits(rr2), dw=_bits(dw), dw2=_bits(dw2), dw3=_bits(dw3))
         for k in want:
             assert torch.equal(got[k], want[k]), f"replay {rep}: {k}"
 

@@ -485,7 +485,8 @@ def device_provenance(dev) -> dict:
         except OSError:
             pass
     return {"name": props.name, "gcnArchName": getattr(props, "gcnArchName", None),
-            "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+            "compute_units": props.multi_processor_count, "wave_size": getattr(props, "warp_size", None),
+            "hbm_bytes": props.total_memory,
             "hip": torch.version.hip, "rocm": rocm, "torch": torch.__version__, "host_nproc": os.cpu_count()}
 
 

@@ -513,7 +513,8 @@ struct ScratchSlot {
     hipError_t err = hipErrorUnknown;
     void *ptr = nullptr;
 };
-ScratchSlot g_scratch[64];
+constexpr int kScratchDevices = 64;  // device indices with a slot
+ScratchSlot g_scratch[kScratchDevices];
 
 // Device address of this device's copy of `scratch`, looked up once per
 // device with that device current.  In host code the array's name is only a
@@ -522,7 +523,7 @@ rmsn_status_t scratch_partials(void **out) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(RMSN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= 64) return fail(RMSN_ERR_HIP, "device index %d out of range", dev);
+    if (dev < 0 || dev >= kScratchDevices) return fail(RMSN_ERR_HIP, "device index %d out of range", dev);
     ScratchSlot &s = g_scratch[dev];
     std::call_once(s.once, [&s]() {
         void *p = nullptr;

@@ -56,8 +56,9 @@ extern "C" RMSN_API rmsn_status_t rmsnorm_tuning_copy(const void *src, void *dst
     rmsn_status_t st = device_info(&cus);
     if (st != RMSN_OK) return st;
     void *args[] = {(void *)&src, &dst, (void *)&nvec};
-    const void *fn = aligned16(src) && aligned16(dst) ? (const void *)rmsn::copy_reference_kernel<rmsn::u32x4>
-                                                      : (const void *)rmsn::copy_reference_kernel<rmsn::u32x4_elem_aligned>;
+    const bool grid16 = aligned16(src) && aligned16(dst);
+    const void *fn = grid16 ? (const void *)rmsn::copy_reference_kernel<rmsn::u32x4>
+                            : (const void *)rmsn::copy_reference_kernel<rmsn::u32x4_elem_aligned>;
     st = launch(fn, dim3((unsigned)grid), dim3(256), args, stream, "rmsnorm_tuning_copy");
     return st == RMSN_OK ? ok() : st;
 }

@@ -299,21 +299,23 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     if (ov.set) {
         // bounds first: the products below are then small
         if (ov.a < 1 || ov.a > 64 || ov.b < 1 || ov.b > 16 || ov.c < 0 || ov.c > 16)
-            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: tile vpt %d wpr %d rpw %d out of range", ov.a, ov.b,
-                        ov.c);
+            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: tile vpt %d wpr %d rpw %d out of range",
+                        ov.a, ov.b, ov.c);
         Geom o = g;
         o.vpt = ov.a;
         o.wpr = ov.b;
         o.rpw = ov.c > 0 ? ov.c : 1;
         const int maxt = max_threads_for(kind, o.vpt, o.vec);
         if (o.vpt < 1 || o.wpr < 1 || o.wpr * o.rpw * 64 > maxt || o.wpr * o.rpw > 16)
-            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: bad tile vpt %d wpr %d rpw %d (max %d threads)",
-                        o.vpt, o.wpr, o.rpw, maxt);
+            return fail(RMSN_ERR_INVALID_ARG,
+                        "forced forward geometry: bad tile vpt %d wpr %d rpw %d (max %d threads)", o.vpt, o.wpr,
+                        o.rpw, maxt);
         const int chunk = 64 * o.wpr * o.vpt;
         o.nchunks = (o.nvec + chunk - 1) / chunk;
         o.two_pass = o.nchunks > 1;
         if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
-            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+            return fail(RMSN_ERR_INVALID_ARG, "forced forward geometry: two-pass tiles need vpt %d",
+                        o.vec > 1 ? 4 : 8);
         g = o;
         grid = (M + g.rpw - 1) / g.rpw;
         if (ov.d > 0 && ov.d < grid) grid = ov.d;
@@ -626,7 +628,8 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         o.nchunks = (o.nvec + chunk - 1) / chunk;
         o.two_pass = o.nchunks > 1;
         if (o.two_pass && o.vpt != (o.vec > 1 ? 4 : 8))
-            return fail(RMSN_ERR_INVALID_ARG, "forced backward geometry: two-pass tiles need vpt %d", o.vec > 1 ? 4 : 8);
+            return fail(RMSN_ERR_INVALID_ARG, "forced backward geometry: two-pass tiles need vpt %d",
+                        o.vec > 1 ? 4 : 8);
         g = o;
         elem_groups = 0;
         if (ov.c > 0) P = ov.c;

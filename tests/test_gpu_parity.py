@@ -592,16 +592,20 @@ def test_empty_batch_is_a_no_op():
 
 
 @pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32"), ("bf16", "f32")])
-@pytest.mark.parametrize("H", [1, 5, 13, 63, 129, 1001, 4096, 4097, 6143, 8190, 12289])
+@pytest.mark.parametrize("H", [1, 5, 13, 63, 129, 1001, 4096, 4097, 6143, 8190, 12289, 16385, 30001, 70001])
 def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
     """The backward on rows off the 16-byte grid (16-byte vectors read and
     written at each row's byte offset): dy, x, dres and dx each at their own
     element offset in padded buffers, so the four tensors' rows sit at
     different offsets within their 16-byte blocks.  Parity with the oracle for
     the plain and the residual backward, the pads and the buffers' heads and
-    tails never written, dx written in place over dy with the same bits, and,
-    for an H of whole vectors, the bits of the contiguous (aligned) run; the
-    forced single-element tile is at parity too."""
+    tails never written, dx written in place over dy and dh over dres with the
+    same bits, and, for an H of whole vectors, the bits of the contiguous
+    (aligned) run; the forced single-element tile is at parity too.  Rows
+    longer than one tile (16-bit plain from 16385, residual from 8193,
+    float32 residual from 8193 and plain from 16385) take two passes; beyond
+    65536 columns their later chunks add into the workspace row at each row,
+    and at 70001 the row's last partial vector lies in such a chunk."""
     M = 41 if H <= 8192 else 9
     d = G.inputs(68 + H, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
     r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype, wdtype)
@@ -633,9 +637,11 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
         dxa, dwa = tn.rmsnorm_bwd(G.to_dev(d["dy"], dtype), G.to_dev(d["x"], dtype), wd, rr)
         torch.cuda.synchronize()
         assert torch.equal(bits(dxv), bits(dxa)) and torch.equal(dw, dwa)
-    # in place over dy: the same bits
+    # in place over dy, and dh over dres: the same bits
+    dh_in, _ = tn.rmsnorm_bwd_residual(dyv, xv, gv, wd, rr, dh=gv)
     dx_in, _ = tn.rmsnorm_bwd(dyv, xv, wd, rr, dx=dyv)
     torch.cuda.synchronize()
+    assert dh_in.data_ptr() == gv.data_ptr() and torch.equal(bits(gv), bits(dhv))
     assert dx_in.data_ptr() == dyv.data_ptr() and torch.equal(bits(dyv), bits(dxv))
     # the single-element tile, forced (contiguous rows of a ragged H only:
     # rows on the grid keep the vector tile)

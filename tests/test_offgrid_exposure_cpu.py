@@ -15,6 +15,11 @@ row barrier.
 This test needs no GPU: it asks the library for the tile each call takes
 (rmsnorm_tuning_tile) and lists the exposed shapes, H <= 8192 in every
 format.  The in-place GPU tests run the listed worked case, bf16 H = 4097.
+
+Backward rows longer than one tile take two passes; there the window is read
+in pass 1 only, and in pass 2 (dx stores, workspace updates) the lane of the
+last partial vector takes its own columns one by one, so no shape of that
+form is exposed.
 """
 
 from __future__ import annotations
@@ -117,3 +122,20 @@ def test_tile_query_aligned_rows():
     t = tn.tile("bwd", 6144, "bf16", off_grid=False)
     assert t["vec"] == 8 and not t["mis"] and not t["multi_pass"]
     assert 64 * t["wpr"] * t["vpt"] >= 768
+
+
+@pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16385), ("bwd", "f32", 16385), ("bwd", "bf16", 70001),
+                                     ("bwd_residual", "bf16", 8193), ("bwd_residual", "f16", 12289),
+                                     ("bwd_residual", "f32", 8193)])
+def test_long_backward_rows_off_the_grid_take_vectors(op, dt, H):
+    # rows longer than one tile: two passes in 16-byte vectors at each row's
+    # byte offset, not single elements
+    t = tn.tile(op, H, dt, off_grid=True)
+    assert t["multi_pass"] and t["mis"] and t["vec"] == 16 // ES[dt]
+
+
+@pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16383), ("bwd", "f32", 16383), ("bwd_residual", "bf16", 8191),
+                                     ("bwd_residual", "f32", 8191)])
+def test_longest_one_pass_backward_rows_off_the_grid(op, dt, H):
+    t = tn.tile(op, H, dt, off_grid=True)
+    assert t["mis"] and not t["multi_pass"]

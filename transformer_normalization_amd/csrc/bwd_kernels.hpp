@@ -65,13 +65,15 @@ struct BwdParams {
 // address is one instruction.  When the row's last vector is only partly
 // inside the row, its lane takes the row's last 16 bytes instead (columns
 // H - VEC .. H - 1): the leading `dup` columns of that window are also the
-// previous vector's, for which it computes and writes the same values; its
-// row-sum terms take them with a weight of zero, and its dw partial sums for
-// them are not stored.  No access leaves the row.
+// previous vector's; its row-sum terms take them with a weight of zero.  In
+// one pass, where every load of the row has returned before any store, the
+// window lane also computes and writes the same dx values for them, and its
+// dw partial sums for them are not stored; two passes use the window in
+// pass 1 only (see there).  No access leaves the row.
 
 template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
-    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: one-pass vector tiles");
+    static_assert(!MIS || VEC * Fmt<XDT>::bytes == 16, "rows off the grid: 16-byte vector tiles");
     // (rows off the grid: at least 16 bytes long, so that the last 16 bytes lie inside the row)
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;  // == blockDim.x
@@ -299,7 +301,19 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // at 1024 threads, no spills); the sums of later chunks are added
         // into the workgroup's workspace row at each row.  Either way each
         // column adds its rows in row order, so dw has the same bits.
+        //
+        // Rows off the grid (MIS): the row's whole vectors are read and
+        // written at the row's byte offset.  A last partial vector (the
+        // row's last H mod VEC columns) is read in pass 1 as the window over
+        // the row's last 16 bytes, its leading columns left out of the sum;
+        // in pass 2 its lane takes only its own columns, one element at a
+        // time.  Pass 2 writes dx while other lanes still read the row, and
+        // later chunks read-modify-write the workspace row, so there no two
+        // lanes may touch the same column.
         constexpr int RCH = 64 / (VPT * VEC) > 0 ? 64 / (VPT * VEC) : 1;
+        constexpr int ES = Fmt<XDT>::bytes;
+        constexpr int WES = Fmt<WDT>::bytes;
+        const int nfull = MIS ? p.H / VEC : p.nvec;  // whole vectors of a row
         float dwr[RCH > 0 ? RCH : 1][VPT][VEC];
 #pragma unroll
         for (int c = 0; c < (RCH > 0 ? RCH : 1); ++c)
@@ -307,11 +321,80 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
             for (int k = 0; k < VPT; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) dwr[c][k][e] = 0.0f;
+        // VEC float32 partial sums of vector v in the workspace row; off the
+        // grid the row is only 4-byte aligned (rows H floats apart), and the
+        // last partial vector holds H - v*VEC of them
+        auto part_load = [&](int v, float *pa) {
+            if constexpr (MIS) {
+                if (v < nfull) {
+#pragma unroll
+                    for (int c = 0; c < VEC / 4; ++c) {
+                        const u32x4 r =
+                            load16_at<false>(reinterpret_cast<const char *>(part + (int64_t)v * VEC + 4 * c));
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) pa[4 * c + q] = __builtin_bit_cast(float, r[q]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) pa[e] = v * VEC + e < p.H ? part[(int64_t)v * VEC + e] : 0.0f;
+                }
+            } else {
+                load_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+            }
+        };
+        auto part_store = [&](int v, const float *pa) {
+            if constexpr (MIS) {
+                if (v < nfull) {
+#pragma unroll
+                    for (int c = 0; c < VEC / 4; ++c) {
+                        u32x4 r;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) r[q] = __builtin_bit_cast(uint32_t, pa[4 * c + q]);
+                        store16_at<false>(reinterpret_cast<char *>(part + (int64_t)v * VEC + 4 * c), r);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        if (v * VEC + e < p.H) part[(int64_t)v * VEC + e] = pa[e];
+                }
+            } else {
+                store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+            }
+        };
         if (part != nullptr) {
             const float z[VEC] = {};
-            for (int v = RCH * chunk + t; v < p.nvec; v += row_threads)
-                store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, z);
+            for (int v = RCH * chunk + t; v < p.nvec; v += row_threads) part_store(v, z);
         }
+        // the VEC weights of vector v starting at column col (1 when weightless)
+        auto load_w = [&](int col, float *wv) {
+            if (p.w != nullptr) {
+                if constexpr (MIS) {
+                    Raw<WDT, VEC> wr;
+#pragma unroll
+                    for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+                        wr.v[c] = load16_at<false>(static_cast<const char *>(p.w) + (int64_t)col * WES + 16 * c);
+                    wr.widen_to(wv);
+                } else {
+                    load_elems<WDT, VEC>(p.w, col, wv);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
+            }
+        };
+        // VEC elements of a row at column col, off the grid at the row's byte offset
+        auto load_vec = [&](const void *base, int64_t rowoff, int col, float *out, auto nt) {
+            constexpr bool NTL = decltype(nt)::value;
+            if constexpr (MIS) {
+                Raw<XDT, VEC> r;
+                r.v[0] = load16_at<NTL>(static_cast<const char *>(base) + (rowoff + col) * ES);
+                r.widen_to(out);
+            } else {
+                load_elems<XDT, VEC, NTL>(base, rowoff + col, out);
+            }
+        };
+        using Cached = std::false_type;
+        using Stream = std::integral_constant<bool, NT>;
         int parity = 0;
         for (int64_t j = 0; j < nsteps; ++j, parity ^= 1) {
             const int64_t row = start + j * step;
@@ -327,38 +410,34 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + tc + k * row_threads;
                     if (v < p.nvec) {
+                        // the last partial vector: the window over the row's
+                        // last VEC columns, whose first `dup` are another lane's
+                        const int col = MIS && v >= nfull ? p.H - VEC : v * VEC;
+                        const int dup = v * VEC - col;
                         float xv[VEC], dv[VEC], wv[VEC];
                         // cached: pass 2 reads the same chunk again
-                        load_elems<XDT, VEC>(p.x, row * p.xs + (int64_t)v * VEC, xv);
-                        load_elems<XDT, VEC>(p.dy, row * p.dys + (int64_t)v * VEC, dv);
-                        if (p.w != nullptr) {
-                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
-                        } else {
+                        load_vec(p.x, row * p.xs, col, xv, Cached{});
+                        load_vec(p.dy, row * p.dys, col, dv, Cached{});
+                        load_w(col, wv);
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
-                        }
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, acc);
+                        for (int e = 0; e < VEC; ++e)
+                            if (!MIS || e >= dup) acc = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, acc);
                     }
                 }
             }
             const float cs = row_sum(acc, p.wpr, wave, &red[parity][0]);
             const float s = (cs * p.inv_h) * rs;
-            // pass 2 over chunk c; dw_add(k, e-array) receives dy * xn
+            // pass 2 over chunk c; dw_add(k, v, dv, xn) receives dy * xn
+            // (zero in the columns past the row's end)
             auto pass2 = [&](int c, auto &&dw_add) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + tc + k * row_threads;
-                    if (v < p.nvec) {
+                    if (v < nfull) {
                         float xv[VEC], dv[VEC], wv[VEC], o[VEC];
-                        load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, xv);
-                        load_elems<XDT, VEC, NT>(p.dy, row * p.dys + (int64_t)v * VEC, dv);
-                        if (p.w != nullptr) {
-                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
-                        }
+                        load_vec(p.x, row * p.xs, v * VEC, xv, Stream{});
+                        load_vec(p.dy, row * p.dys, v * VEC, dv, Stream{});
+                        load_w(v * VEC, wv);
                         float xn[VEC];
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
@@ -367,11 +446,42 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                         }
                         if constexpr (RES) {
                             float gv[VEC];
-                            load_elems<XDT, VEC, NT>(p.dres, row * p.drs + (int64_t)v * VEC, gv);
+                            load_vec(p.dres, row * p.drs, v * VEC, gv, Stream{});
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) o[e] += gv[e];
                         }
-                        store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                        if constexpr (MIS) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(o + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.dx) + (row * p.dxs + (int64_t)v * VEC) * ES, raw);
+                        } else {
+                            store_elems<XDT, VEC, NT>(p.dx, row * p.dxs + (int64_t)v * VEC, o);
+                        }
+                        dw_add(k, v, dv, xn);
+                    } else if (MIS && v < p.nvec) {
+                        // the last partial vector, one element at a time
+                        float dv[VEC], xn[VEC];
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const int col = v * VEC + e;
+                            dv[e] = 0.0f;
+                            xn[e] = 0.0f;
+                            if (col < p.H) {
+                                float xv, wv = 1.0f, o;
+                                load_elems<XDT, 1, NT>(p.x, row * p.xs + col, &xv);
+                                load_elems<XDT, 1, NT>(p.dy, row * p.dys + col, &dv[e]);
+                                if (p.w != nullptr) load_elems<WDT, 1>(p.w, col, &wv);
+                                xn[e] = xv * rs;
+                                o = rs * (dv[e] * wv) - xn[e] * s;
+                                if constexpr (RES) {
+                                    float gv;
+                                    load_elems<XDT, 1, NT>(p.dres, row * p.drs + col, &gv);
+                                    o += gv;
+                                }
+                                store_elems<XDT, 1, NT>(p.dx, row * p.dxs + col, &o);
+                            }
+                        }
                         dw_add(k, v, dv, xn);
                     }
                 }
@@ -391,10 +501,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 pass2(c, [&](int, int v, const float *dv, const float *xn) {
                     if (part != nullptr) {
                         float pa[VEC];
-                        load_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+                        part_load(v, pa);
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) pa[e] = __builtin_fmaf(dv[e], xn[e], pa[e]);
-                        store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, pa);
+                        part_store(v, pa);
                     }
                 });
         }
@@ -404,7 +514,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
-                    if (c < p.nchunks && v < p.nvec) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, dwr[c][k]);
+                    if (c < p.nchunks && v < p.nvec) part_store(v, dwr[c][k]);
                 }
             }
         }

@@ -32,9 +32,10 @@ fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bo
 bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 // the backward of the fused residual pre-norm (adds the residual-stream gradient)
 bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
-// the one-pass backward for rows off the 16-byte grid (16-byte vectors at the
-// row's byte offset; x, dy, dres and dx element-aligned, w 16-byte aligned)
-bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool res, bool nt);
+// the backward for rows off the 16-byte grid (16-byte vectors at the row's
+// byte offset; x, dy, dres and dx element-aligned, w 16-byte aligned), one
+// pass or, for rows longer than a tile, two (vpt 4)
+bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, bool res, bool nt);
 const void *dw_finalize_kernel();
 // vec: 16 / element size, or 1 for single elements; tdt: x's format or
 // float32; xchg: the lane-exchange layout (vectors only)

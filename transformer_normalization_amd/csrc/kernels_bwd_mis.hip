@@ -1,14 +1,15 @@
-// kernels_bwd_mis.hip -- instantiations of the one-pass backward (plain and
-// residual) for rows off the 16-byte grid: 16-byte vectors read and written at
-// the row's byte offset (bwd_kernels.hpp, MIS).
+// kernels_bwd_mis.hip -- instantiations of the backward (plain and residual)
+// for rows off the 16-byte grid: 16-byte vectors read and written at the row's
+// byte offset (bwd_kernels.hpp, MIS), in one pass or two.
 #include "kernel_tables.hpp"
 
 namespace rmsn {
 namespace {
 
 template <int XDT, int WDT, bool RES, bool NT>
-bwd_fn mis_kernel(int vpt) {
+bwd_fn mis_kernel(int vpt, bool two_pass) {
     constexpr int V = 16 / Fmt<XDT>::bytes;
+    if (two_pass) return vpt == 4 ? rmsnorm_bwd_kernel<XDT, WDT, V, 4, RES, true, NT, 1024, true> : nullptr;
     switch (vpt) {
     case 1: return rmsnorm_bwd_kernel<XDT, WDT, V, 1, RES, false, NT, bwd_max_threads(1 * V, RES), true>;
     case 2: return rmsnorm_bwd_kernel<XDT, WDT, V, 2, RES, false, NT, bwd_max_threads(2 * V, RES), true>;
@@ -20,14 +21,14 @@ bwd_fn mis_kernel(int vpt) {
 }
 
 template <bool RES, bool NT>
-bwd_fn mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt) {
+bwd_fn mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool tp) {
     const bool wf32 = (wdt == RMSN_F32);
     switch (xdt) {
-    case RMSN_F32: return mis_kernel<DT_F32, DT_F32, RES, NT>(vpt);
+    case RMSN_F32: return mis_kernel<DT_F32, DT_F32, RES, NT>(vpt, tp);
     case RMSN_F16:
-        return wf32 ? mis_kernel<DT_F16, DT_F32, RES, NT>(vpt) : mis_kernel<DT_F16, DT_F16, RES, NT>(vpt);
+        return wf32 ? mis_kernel<DT_F16, DT_F32, RES, NT>(vpt, tp) : mis_kernel<DT_F16, DT_F16, RES, NT>(vpt, tp);
     case RMSN_BF16:
-        return wf32 ? mis_kernel<DT_BF16, DT_F32, RES, NT>(vpt) : mis_kernel<DT_BF16, DT_BF16, RES, NT>(vpt);
+        return wf32 ? mis_kernel<DT_BF16, DT_F32, RES, NT>(vpt, tp) : mis_kernel<DT_BF16, DT_BF16, RES, NT>(vpt, tp);
     default: break;  // any other value: no kernel
     }
     return nullptr;
@@ -35,9 +36,10 @@ bwd_fn mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt) {
 
 }  // namespace
 
-bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool res, bool nt) {
-    if (res) return nt ? mis_lookup<true, true>(xdt, wdt, vpt) : mis_lookup<true, false>(xdt, wdt, vpt);
-    return nt ? mis_lookup<false, true>(xdt, wdt, vpt) : mis_lookup<false, false>(xdt, wdt, vpt);
+bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, bool res, bool nt) {
+    if (res)
+        return nt ? mis_lookup<true, true>(xdt, wdt, vpt, two_pass) : mis_lookup<true, false>(xdt, wdt, vpt, two_pass);
+    return nt ? mis_lookup<false, true>(xdt, wdt, vpt, two_pass) : mis_lookup<false, false>(xdt, wdt, vpt, two_pass);
 }
 
 }  // namespace rmsn

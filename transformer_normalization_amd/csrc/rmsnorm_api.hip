@@ -465,21 +465,18 @@ Geom pick_bwd_elem_geom(Kind kind, int H, int *groups_per_cu) {
 // The backward's tile with no forced geometry.  vec_ok: every row start is
 // 16-byte aligned and H a whole number of vectors.  mis_ok: otherwise, every
 // row start element-aligned and w 16-byte aligned.  Rows off the grid take
-// 16-byte vectors at their byte offset when the row holds at least 16 bytes
-// and fits one pass; otherwise rows from 512 elements take the single-element
-// rule (*elem_groups = its workgroups per CU), shorter ones the vector rule's
-// single-element tile.
+// 16-byte vectors at their byte offset when mis_ok and the row holds at least
+// 16 bytes, in one pass or, for rows longer than a tile, two; otherwise rows
+// from 512 elements take the single-element rule (*elem_groups = its
+// workgroups per CU), shorter ones the vector rule's single-element tile.
 Geom bwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis, int *elem_groups) {
     const int vecw = 16 / eb;
     Geom g = pick_row_geom(kind, H, vec_ok ? vecw : 1, 8);
     *mis = false;
     *elem_groups = 0;
     if (!vec_ok && mis_ok && (int64_t)H * eb >= 16) {
-        const Geom m = pick_row_geom(kind, H, vecw, 8);
-        if (!m.two_pass) {
-            g = m;
-            *mis = true;
-        }
+        g = pick_row_geom(kind, H, vecw, 8);
+        *mis = true;
     }
     if (!vec_ok && !*mis && H >= 512) {
         const Geom e = pick_bwd_elem_geom(kind, H, elem_groups);
@@ -637,7 +634,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (ov.d == 2) interleave = false;
     }
     const bool nt = use_streaming((res ? 4 : 3) * M * H * eb);
-    bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, res, nt)
+    bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, g.two_pass, res, nt)
                 : res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
                       : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);

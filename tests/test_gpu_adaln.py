@@ -142,13 +142,14 @@ def test_adaln_misaligned_rows():
 
 @pytest.mark.parametrize("per_batch", [True, False], ids=["per_batch", "per_token"])
 @pytest.mark.parametrize("dtype,pdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("H", [2049, 4096])
+@pytest.mark.parametrize("H", [2049, 4096, 16385, 40001])
 def test_adaln_rows_off_the_grid(H, dtype, pdtype, per_batch):
     """Rows off the 16-byte grid (ragged H, x and the modulation at element
     offsets; scale and shift as column slices of one modulation tensor, per
     batch as [B, 1, H] views): the tile depends on H only, so every layout
     gives the same bits, at parity with the oracle, and nothing around the
-    output rows is written."""
+    output rows is written.  16385 and 40001 are longer than any resident
+    tile and take two passes."""
     B, S = 3, 11
     M = B * S
     C = B if per_batch else M

@@ -181,14 +181,15 @@ def test_ln_misaligned_and_strided_rows(dtype):
 
 
 @pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("H", [600, 2049, 4096, 6143])
+@pytest.mark.parametrize("H", [600, 2049, 4096, 6143, 16385, 70001])
 def test_ln_rows_off_the_grid(dtype, wdtype, H):
     """Rows off the 16-byte grid (ragged H, or views at element offsets)
     are read and written in 16-byte vectors at each row's byte offset, on a
     tile that depends on H only: every layout gives the same bits, at parity
     with the oracle, and nothing around the output rows is written; the
-    forced element-wise tile is at parity too."""
-    M = 67
+    forced element-wise tile is at parity too.  16385 and 70001 are longer
+    than any resident tile and take the passes over the row."""
+    M = 67 if H <= 8192 else 9
     d = G.inputs(5100 + H, M, H, dtype, wdtype=wdtype, residual=True)
     b = bias_of(5100 + H, H, wdtype)
     wt, bt = G.to_dev(d["w"], wdtype), G.to_dev(b, wdtype)
@@ -231,7 +232,8 @@ def test_ln_rows_off_the_grid(dtype, wdtype, H):
                                     name=f"ln element tile {dtype} H={H}"))
 
 
-@pytest.mark.parametrize("H", [4096, 65536, 4097])  # 4097: rows off the 16-byte grid
+# 4097: rows off the 16-byte grid; 70001: off the grid and longer than a tile
+@pytest.mark.parametrize("H", [4096, 65536, 4097, 70001])
 def test_ln_in_place(H):
     M = 64 if H <= 8192 else 4
     d = G.inputs(48, M, H, "bf16", residual=True)

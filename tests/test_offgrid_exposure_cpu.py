@@ -126,10 +126,13 @@ def test_tile_query_aligned_rows():
 
 @pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16385), ("bwd", "f32", 16385), ("bwd", "bf16", 70001),
                                      ("bwd_residual", "bf16", 8193), ("bwd_residual", "f16", 12289),
-                                     ("bwd_residual", "f32", 8193)])
-def test_long_backward_rows_off_the_grid_take_vectors(op, dt, H):
-    # rows longer than one tile: two passes in 16-byte vectors at each row's
-    # byte offset, not single elements
+                                     ("bwd_residual", "f32", 8193), ("fwd", "bf16", 70001),
+                                     ("fwd_residual", "bf16", 16385), ("fwd_residual", "f32", 30001),
+                                     ("adaln", "bf16", 16385), ("layernorm", "bf16", 16385),
+                                     ("layernorm", "f32", 70001)])
+def test_long_rows_off_the_grid_take_vectors(op, dt, H):
+    # rows longer than one tile: passes over the row in 16-byte vectors at
+    # each row's byte offset, not single elements
     t = tn.tile(op, H, dt, off_grid=True)
     assert t["multi_pass"] and t["mis"] and t["vec"] == 16 // ES[dt]
 

@@ -27,15 +27,16 @@
 //     ("Required reasoning process", step 3, the persistent pattern).
 //   * Two-pass path (longer rows): pass 1 sums squares chunk by chunk, pass 2
 //     reloads each chunk with the same bounds and scales it (step 11).
-//   * MIS kernels (resident path only) take rows off the 16-byte grid (a
-//     start that is not 16-byte aligned, or a length that is not a whole
-//     number of vectors) in the same 16-byte vectors, each read and written
-//     with one access at the row's own byte offset.  When a row's last vector
-//     is only partly inside the row, its lane takes the row's last 16 bytes
-//     instead (columns H - VEC .. H - 1): the window's leading `dup` columns
-//     are also the previous vector's, for which it computes and writes the
-//     same values, and they are left out of its sum of squares.  Every lane
-//     runs the same code, and no access leaves the row.
+//   * MIS kernels take rows off the 16-byte grid (a start that is not
+//     16-byte aligned, or a length that is not a whole number of vectors) in
+//     the same 16-byte vectors, each read and written with one access at the
+//     row's own byte offset.  When a row's last vector is only partly inside
+//     the row, its lane takes the row's last 16 bytes instead (columns
+//     H - VEC .. H - 1): the window's leading `dup` columns are also the
+//     previous vector's and are left out of its sum of squares.  Resident,
+//     it computes and writes the same values for them after the row's
+//     reduction; in two passes it reads the window in pass 1 only and writes
+//     its own columns one by one.  No access leaves the row.
 //   * NT kernels stream x, r, y and r_out past the caches (non-temporal
 //     accesses); the weight and rrms use ordinary cached accesses.
 //   * The reduction is a per-thread float32 sum over the thread's elements in
@@ -77,7 +78,7 @@ enum : int { MODE_PLAIN = 0, MODE_RESID = 1, MODE_ADALN = 2 };
 
 template <int XDT, int WDT, int VEC, int VPT, int MODE, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
-    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: resident vector tiles");
+    static_assert(!MIS || VEC * Fmt<XDT>::bytes == 16, "rows off the grid: 16-byte vector tiles");
     constexpr int ES = Fmt<XDT>::bytes;
     constexpr int WES = Fmt<WDT>::bytes;
     constexpr bool RESID = MODE == MODE_RESID;
@@ -270,7 +271,27 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
             if (it + 1 < p.iters) load_row(it + 1);
         }
     } else {
+        // Rows off the grid (MIS): the row's whole vectors are read and
+        // written at the row's byte offset.  Pass 1 reads a last partial
+        // vector as the window over the row's last 16 bytes and leaves its
+        // leading columns out of the sum; pass 2 writes while other lanes may
+        // still read the row (an output can be the same buffer as an input),
+        // so there that lane takes only its own columns, one at a time.
         const int chunk = row_threads * VPT;
+        const int nfull = MIS ? p.H / VEC : p.nvec;  // whole vectors of a row
+        // VEC parameter-format elements at element offset `off` (weight,
+        // AdaLN's rows)
+        auto load_param = [&](const void *base, int64_t off, float *out) {
+            if constexpr (MIS) {
+                Raw<WDT, VEC> r;
+#pragma unroll
+                for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+                    r.v[c] = load16_at<false>(static_cast<const char *>(base) + off * WES + 16 * c);
+                r.widen_to(out);
+            } else {
+                load_elems<WDT, VEC>(base, off, out);
+            }
+        };
         for (int64_t it = 0; it < p.iters; ++it) {
             const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
             const bool valid = row < p.M;
@@ -284,8 +305,15 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                     const int v = c * chunk + t + k * row_threads;
                     if (valid && v < p.nvec) {
                         // cached: pass 2 reads the same chunk again
-                        xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
-                        if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
+                        if constexpr (MIS) {
+                            const int col = v >= nfull ? p.H - VEC : v * VEC;
+                            xr[k].v[0] = load16_at<false>(static_cast<const char *>(p.x) + (row * p.xs + col) * ES);
+                            if constexpr (RESID)
+                                rr[k].v[0] = load16_at<false>(static_cast<const char *>(p.r) + (row * p.rs + col) * ES);
+                        } else {
+                            xr[k].load(p.x, row * p.xs + (int64_t)v * VEC);
+                            if constexpr (RESID) rr[k].load(p.r, row * p.rs + (int64_t)v * VEC);
+                        }
                     } else {
                         xr[k].zero();
                         if constexpr (RESID) rr[k].zero();
@@ -293,6 +321,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                 }
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
+                    const int v = c * chunk + t + k * row_threads;
+                    // the window's leading columns, another lane's
+                    const int dup = MIS && v >= nfull && v < p.nvec ? v * VEC - (p.H - VEC) : 0;
                     float hv[VEC];
                     xr[k].widen_to(hv);
                     if constexpr (RESID) {
@@ -302,7 +333,8 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
                         for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                     }
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc = __builtin_fmaf(hv[e], hv[e], acc);
+                    for (int e = 0; e < VEC; ++e)
+                        if (!MIS || e >= dup) acc = __builtin_fmaf(hv[e], hv[e], acc);
                 }
             }
             const float ss = row_sum(acc, p.wpr, wave_in_row, &red[it & 1][slot * p.wpr]);
@@ -315,30 +347,54 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
-                    if (valid && v < p.nvec) {
+                    if (valid && v < nfull) {
                         float hv[VEC], wv[VEC];
-                        load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                        if constexpr (MIS) {
+                            Raw<XDT, VEC> xv;
+                            xv.v[0] = load16_at<NT>(static_cast<const char *>(p.x) +
+                                                    (row * p.xs + (int64_t)v * VEC) * ES);
+                            xv.widen_to(hv);
+                        } else {
+                            load_elems<XDT, VEC, NT>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                        }
                         if constexpr (RESID) {
                             float rv[VEC];
-                            load_elems<XDT, VEC, NT>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+                            if constexpr (MIS) {
+                                Raw<XDT, VEC> rw;
+                                rw.v[0] = load16_at<NT>(static_cast<const char *>(p.r) +
+                                                        (row * p.rs + (int64_t)v * VEC) * ES);
+                                rw.widen_to(rv);
+                            } else {
+                                load_elems<XDT, VEC, NT>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+                            }
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                         }
                         if (p.w != nullptr) {
-                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
+                            load_param(p.w, (int64_t)v * VEC, wv);
                         } else {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
                         }
                         if constexpr (RESID) {
-                            if (p.ro != nullptr) store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                            if (p.ro != nullptr) {
+                                if constexpr (MIS) {
+                                    u32x4 raw;
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(hv + q * (4 / ES));
+                                    store16_at<NT>(static_cast<char *>(p.ro) + (row * p.ros + (int64_t)v * VEC) * ES,
+                                                   raw);
+                                } else {
+                                    store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                                }
+                            }
                         }
                         float o[VEC];
                         if constexpr (ADALN) {
                             const int64_t crow = row / p.rows_per_cond;
                             float sc[VEC], sh[VEC];
-                            load_elems<WDT, VEC>(p.scale, crow * p.cs + (int64_t)v * VEC, sc);
-                            load_elems<WDT, VEC>(p.shift, crow * p.cs + (int64_t)v * VEC, sh);
+                            load_param(p.scale, crow * p.cs + (int64_t)v * VEC, sc);
+                            load_param(p.shift, crow * p.cs + (int64_t)v * VEC, sh);
 #pragma unroll
                             for (int e = 0; e < VEC; ++e)
                                 o[e] = __builtin_fmaf((hv[e] * rs) * wv[e], 1.0f + sc[e], sh[e]);
@@ -346,7 +402,41 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_fwd_kernel(const FwdParams p) {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) o[e] = (hv[e] * rs) * wv[e];
                         }
-                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                        if constexpr (MIS) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(o + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.y) + (row * p.ys + (int64_t)v * VEC) * ES, raw);
+                        } else {
+                            store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                        }
+                    } else if (MIS && valid && v < p.nvec) {
+                        // the last partial vector, one element at a time
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const int col = v * VEC + e;
+                            if (col < p.H) {
+                                float h, wv = 1.0f, o;
+                                load_elems<XDT, 1, NT>(p.x, row * p.xs + col, &h);
+                                if constexpr (RESID) {
+                                    float rv;
+                                    load_elems<XDT, 1, NT>(p.r, row * p.rs + col, &rv);
+                                    h = h + rv;
+                                    if (p.ro != nullptr) store_elems<XDT, 1, NT>(p.ro, row * p.ros + col, &h);
+                                }
+                                if (p.w != nullptr) load_elems<WDT, 1>(p.w, col, &wv);
+                                if constexpr (ADALN) {
+                                    const int64_t crow = row / p.rows_per_cond;
+                                    float sc, sh;
+                                    load_elems<WDT, 1>(p.scale, crow * p.cs + col, &sc);
+                                    load_elems<WDT, 1>(p.shift, crow * p.cs + col, &sh);
+                                    o = __builtin_fmaf((h * rs) * wv, 1.0f + sc, sh);
+                                } else {
+                                    o = (h * rs) * wv;
+                                }
+                                store_elems<XDT, 1, NT>(p.y, row * p.ys + col, &o);
+                            }
+                        }
                     }
                 }
             }

@@ -24,9 +24,10 @@ typedef void (*ln_fn)(const LnParams);
 // accesses per thread; nt: streaming accesses)
 fwd_fn fwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
-// the resident forward for rows off the 16-byte grid (16-byte vectors at the
-// row's byte offset; mode: MODE_PLAIN, MODE_RESID or MODE_ADALN)
-fwd_fn fwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, int mode, bool nt);
+// the forward for rows off the 16-byte grid (16-byte vectors at the row's
+// byte offset; mode: MODE_PLAIN, MODE_RESID or MODE_ADALN), resident or, for
+// rows longer than a tile, in two passes (vpt 4)
+fwd_fn fwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, int mode, bool nt);
 // AdaLN: wdt is the format of the weight, scale and shift
 fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
@@ -41,9 +42,9 @@ const void *dw_finalize_kernel();
 // float32; xchg: the lane-exchange layout (vectors only)
 // LayerNorm forward, plain or fused with the residual add (resid)
 ln_fn ln_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt, bool resid);
-// LayerNorm for rows off the 16-byte grid, resident, in 16-byte vectors at
-// the row's byte offset
-ln_fn ln_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool nt, bool resid);
+// LayerNorm for rows off the 16-byte grid in 16-byte vectors at the row's
+// byte offset, resident or, for rows longer than a tile, in passes (vpt 4)
+ln_fn ln_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, bool nt, bool resid);
 rope_fn rope_lookup(rmsn_dtype_t xdt, rmsn_dtype_t tdt, int vec, bool nt, bool xchg);
 
 }  // namespace rmsn

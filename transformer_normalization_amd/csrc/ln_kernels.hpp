@@ -49,15 +49,16 @@ struct LnParams {
     float inv_h;
 };
 
-// MIS (resident path only): rows off the 16-byte grid in the same 16-byte
-// vectors, each read and written with one access at the row's own byte
-// offset; a row's last vector, when only partly inside the row, is the window
-// over the row's last 16 bytes, whose leading `dup` columns (the previous
-// vector's, written again with the same values) are left out of both sums
-// (fwd_kernels.hpp).
+// MIS: rows off the 16-byte grid in the same 16-byte vectors, each read and
+// written with one access at the row's own byte offset; a row's last vector,
+// when only partly inside the row, is the window over the row's last 16
+// bytes, whose leading `dup` columns (the previous vector's) are left out of
+// both sums.  Resident, the window lane writes them again with the same
+// values after the reductions; on long rows it writes only its own columns,
+// one at a time (fwd_kernels.hpp).
 template <int XDT, int WDT, int VEC, int VPT, bool RESID, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
 __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
-    static_assert(!MIS || (!TWO_PASS && VEC * Fmt<XDT>::bytes == 16), "rows off the grid: resident vector tiles");
+    static_assert(!MIS || VEC * Fmt<XDT>::bytes == 16, "rows off the grid: 16-byte vector tiles");
     constexpr int ES = Fmt<XDT>::bytes;
     constexpr int WES = Fmt<WDT>::bytes;
     // one LDS area per reduction of a row; consecutive reductions alternate
@@ -225,20 +226,57 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
             if (it + 1 < p.iters) load_row(it + 1);
         }
     } else {
+        // Rows off the grid (MIS): whole vectors at the row's byte offset;
+        // a last partial vector is the window over the row's last 16 bytes
+        // in the two reduction passes (its leading columns left out of both
+        // sums) and, in pass 3, which writes while other lanes may still read
+        // the row, only its own columns, one at a time.
         const int chunk = row_threads * VPT;
+        const int nfull = MIS ? p.H / VEC : p.nvec;  // whole vectors of a row
+        auto load_param = [&](const void *base, int v, float *out) {
+            if constexpr (MIS) {
+                Raw<WDT, VEC> r;
+#pragma unroll
+                for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
+                    r.v[c] = load16_at<false>(static_cast<const char *>(base) + (int64_t)v * VEC * WES + 16 * c);
+                r.widen_to(out);
+            } else {
+                load_elems<WDT, VEC>(base, (int64_t)v * VEC, out);
+            }
+        };
         for (int64_t it = 0; it < p.iters; ++it) {
             const int64_t row = ((int64_t)blockIdx.x + it * gstride) * p.rpw + slot;
             const bool valid = row < p.M;
-            // h of vector v (cached loads for the two reduction passes)
-            auto load_h = [&](int v, float *hv, auto nt_tag) {
+            // h of the VEC columns from col (cached loads for the two
+            // reduction passes)
+            auto load_h = [&](int col, float *hv, auto nt_tag) {
                 constexpr bool LNT = decltype(nt_tag)::value;
-                load_elems<XDT, VEC, LNT>(p.x, row * p.xs + (int64_t)v * VEC, hv);
+                if constexpr (MIS) {
+                    Raw<XDT, VEC> xr;
+                    xr.v[0] = load16_at<LNT>(static_cast<const char *>(p.x) + (row * p.xs + col) * ES);
+                    xr.widen_to(hv);
+                } else {
+                    load_elems<XDT, VEC, LNT>(p.x, row * p.xs + col, hv);
+                }
                 if constexpr (RESID) {
                     float rv[VEC];
-                    load_elems<XDT, VEC, LNT>(p.r, row * p.rs + (int64_t)v * VEC, rv);
+                    if constexpr (MIS) {
+                        Raw<XDT, VEC> rr;
+                        rr.v[0] = load16_at<LNT>(static_cast<const char *>(p.r) + (row * p.rs + col) * ES);
+                        rr.widen_to(rv);
+                    } else {
+                        load_elems<XDT, VEC, LNT>(p.r, row * p.rs + col, rv);
+                    }
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) hv[e] = hv[e] + rv[e];
                 }
+            };
+            // the first column a reduction pass reads for vector v, and how
+            // many of its leading columns are another lane's
+            auto window = [&](int v, int *dup) {
+                const int col = MIS && v >= nfull ? p.H - VEC : v * VEC;
+                *dup = v * VEC - col;
+                return col;
             };
             using cached = std::integral_constant<bool, false>;
             using streamed = std::integral_constant<bool, NT>;
@@ -249,10 +287,13 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
                     if (valid && v < p.nvec) {
+                        int dup;
+                        const int col = window(v, &dup);
                         float hv[VEC];
-                        load_h(v, hv, cached{});
+                        load_h(col, hv, cached{});
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) s1 += hv[e];
+                        for (int e = 0; e < VEC; ++e)
+                            if (!MIS || e >= dup) s1 += hv[e];
                     }
                 }
             }
@@ -264,12 +305,14 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
                     if (valid && v < p.nvec) {
+                        int dup;
+                        const int col = window(v, &dup);
                         float hv[VEC];
-                        load_h(v, hv, cached{});
+                        load_h(col, hv, cached{});
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
                             const float d = hv[e] - mean;
-                            s2 = __builtin_fmaf(d, d, s2);
+                            if (!MIS || e >= dup) s2 = __builtin_fmaf(d, d, s2);
                         }
                     }
                 }
@@ -286,27 +329,64 @@ __global__ void __launch_bounds__(MAXT) layernorm_fwd_kernel(const LnParams p) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int v = c * chunk + t + k * row_threads;
-                    if (valid && v < p.nvec) {
+                    if (valid && v < nfull) {
                         float hv[VEC], wv[VEC], bv[VEC], o[VEC];
-                        load_h(v, hv, streamed{});
+                        load_h(v * VEC, hv, streamed{});
                         if constexpr (RESID) {
-                            if (p.ro != nullptr) store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                            if (p.ro != nullptr) {
+                                if constexpr (MIS) {
+                                    u32x4 raw;
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(hv + q * (4 / ES));
+                                    store16_at<NT>(static_cast<char *>(p.ro) + (row * p.ros + (int64_t)v * VEC) * ES,
+                                                   raw);
+                                } else {
+                                    store_elems<XDT, VEC, NT>(p.ro, row * p.ros + (int64_t)v * VEC, hv);
+                                }
+                            }
                         }
                         if (p.w != nullptr) {
-                            load_elems<WDT, VEC>(p.w, (int64_t)v * VEC, wv);
+                            load_param(p.w, v, wv);
                         } else {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) wv[e] = 1.0f;
                         }
                         if (p.b != nullptr) {
-                            load_elems<WDT, VEC>(p.b, (int64_t)v * VEC, bv);
+                            load_param(p.b, v, bv);
                         } else {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e) bv[e] = 0.0f;
                         }
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf((hv[e] - mean) * rs, wv[e], bv[e]);
-                        store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                        if constexpr (MIS) {
+                            u32x4 raw;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) raw[q] = pack_word<XDT>(o + q * (4 / ES));
+                            store16_at<NT>(static_cast<char *>(p.y) + (row * p.ys + (int64_t)v * VEC) * ES, raw);
+                        } else {
+                            store_elems<XDT, VEC, NT>(p.y, row * p.ys + (int64_t)v * VEC, o);
+                        }
+                    } else if (MIS && valid && v < p.nvec) {
+                        // the last partial vector, one element at a time
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) {
+                            const int col = v * VEC + e;
+                            if (col < p.H) {
+                                float h, wv = 1.0f, bv = 0.0f, o;
+                                load_elems<XDT, 1, NT>(p.x, row * p.xs + col, &h);
+                                if constexpr (RESID) {
+                                    float rv;
+                                    load_elems<XDT, 1, NT>(p.r, row * p.rs + col, &rv);
+                                    h = h + rv;
+                                    if (p.ro != nullptr) store_elems<XDT, 1, NT>(p.ro, row * p.ros + col, &h);
+                                }
+                                if (p.w != nullptr) load_elems<WDT, 1>(p.w, col, &wv);
+                                if (p.b != nullptr) load_elems<WDT, 1>(p.b, col, &bv);
+                                o = __builtin_fmaf((h - mean) * rs, wv, bv);
+                                store_elems<XDT, 1, NT>(p.y, row * p.ys + col, &o);
+                            }
+                        }
                     }
                 }
             }

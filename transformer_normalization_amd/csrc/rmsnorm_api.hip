@@ -167,9 +167,10 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
 // The forward family's tile with no forced geometry (vec_ok, mis_ok as for
 // bwd_tile; mis_ok also needs the bias and AdaLN's conditioning rows
 // aligned).  Rows off the 16-byte grid take 16-byte vectors at each row's
-// byte offset when the row holds at least 512 bytes and fits the resident
-// tile: RMSNorm rows and 16-bit LayerNorm rows from 1 KiB on the off-grid
-// tile rule, shorter rows, AdaLN and float32 LayerNorm on the aligned rule.
+// byte offset when the row holds at least 512 bytes: RMSNorm rows and 16-bit
+// LayerNorm rows from 1 KiB on the off-grid tile rule, shorter rows, AdaLN
+// and float32 LayerNorm on the aligned rule, rows longer than any resident
+// tile in passes over the row.
 // Measured on gfx950 against the element-wise tile (bf16, 2^25 elements):
 // H = 257 49.5 % against 37.4 % of peak, H = 511 68.9 % and 56.3 %, but
 // H = 127 27.8 % and 31.3 % (16 vectors leave most of a wave idle);
@@ -188,10 +189,8 @@ Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
     if (!vec_ok && mis_ok && (int64_t)H * eb >= 512) {
         Geom m = offrule && (int64_t)H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
         if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
-        if (!m.two_pass) {
-            *mis = true;
-            return m;
-        }
+        *mis = true;
+        return m;
     }
     return pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
 }
@@ -329,7 +328,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     const rmsn_dtype_t kwdt = (w || adaln || bias) ? wdt : xdt;
     int cus = 0;  // the device must be a readable gfx950 before anything is enqueued
     if (ln) {
-        ln_fn fn = mis ? ln_mis_lookup(xdt, kwdt, g.vpt, nt, resid)
+        ln_fn fn = mis ? ln_mis_lookup(xdt, kwdt, g.vpt, g.two_pass, nt, resid)
                        : ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
         if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
         if ((st = device_info(&cus)) != RMSN_OK) return st;
@@ -359,7 +358,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         return launch((const void *)fn, dim3((unsigned)grid), dim3(64 * g.wpr * g.rpw), args, stream,
                       resid ? "layernorm_fwd_residual" : "layernorm_fwd");
     }
-    fwd_fn fn = mis     ? fwd_mis_lookup(xdt, kwdt, g.vpt, mode, nt)
+    fwd_fn fn = mis     ? fwd_mis_lookup(xdt, kwdt, g.vpt, g.two_pass, mode, nt)
                 : resid ? fwd_lookup_resid(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                 : adaln ? fwd_lookup_adaln(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt)
                         : fwd_lookup_plain(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt);

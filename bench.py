@@ -12,7 +12,7 @@ launched on.  One JSON line is printed.
 
 Workloads (default: the forward at bf16 M=8192 H=4096):
   fwd_bf16_8192x4096, fwd_f32_64x512, fwd_bf16_32768x2048, fwd_bf16_32768x2048_noweight,
-  fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144,
+  fwd_f16_32768x2048_outliers, fwd_residual_bf16_16384x8192, bwd_bf16_8192x6144, bwd_bf16_8192x4097,
   bwd_residual_bf16_16384x8192, adaln_bf16_2x4096x2048_batchcond, adaln_bf16_2x4096x2048_tokencond,
   rope_bf16_2x8064x32x64, rope_bf16_2x4096x32x128, ln_residual_f32_16384x1024
 
@@ -65,20 +65,23 @@ KERNEL_SOURCES = {
     "rope": ("numerics.hpp", "rope_kernels.hpp", "kernel_tables.hpp", "kernels_rope.hip", "rope_api.hip"),
     "ln_residual": ("numerics.hpp", "ln_kernels.hpp", "kernel_tables.hpp", "kernels_ln.hip", "rmsnorm_api.hip"),
     "fwd_offgrid": _FWD + ("kernels_fwd_mis.hip", "rmsnorm_api.hip"),
+    "bwd_offgrid": _BWD + ("kernels_bwd_mis.hip", "rmsnorm_api.hip"),
 }
 # the kernel whose launches the counters describe
 KERNEL_KEY = {"fwd": "rmsnorm_fwd_kernel", "fwd_residual": "rmsnorm_fwd_kernel", "adaln": "rmsnorm_fwd_kernel",
               "bwd": "rmsnorm_bwd_kernel", "bwd_residual": "rmsnorm_bwd_kernel", "rope": "rope_apply_kernel",
-              "ln_residual": "layernorm_fwd_kernel", "fwd_offgrid": "rmsnorm_fwd_kernel"}
+              "ln_residual": "layernorm_fwd_kernel", "fwd_offgrid": "rmsnorm_fwd_kernel",
+              "bwd_offgrid": "rmsnorm_bwd_kernel"}
 
 
 def kernel_kind(spec) -> str:
     """The kernel family a workload's calls run: its kind, except that a
-    forward on contiguous rows whose byte length is not a multiple of 16 (so
-    that rows leave the 16-byte grid) runs the forward's instantiations for
-    rows off the grid (16-byte vectors at each row's byte offset)."""
-    if spec["kind"] == "fwd" and (spec["H"] * _size(spec["dtype"])) % 16:
-        return "fwd_offgrid"
+    forward or backward on contiguous rows whose byte length is not a
+    multiple of 16 (so that rows leave the 16-byte grid) runs the
+    instantiations for rows off the grid (16-byte vectors at each row's byte
+    offset)."""
+    if spec["kind"] in ("fwd", "bwd") and (spec["H"] * _size(spec["dtype"])) % 16:
+        return spec["kind"] + "_offgrid"
     return spec["kind"]
 
 WORKLOADS = {
@@ -95,6 +98,7 @@ WORKLOADS = {
     "rope_bf16_2x8064x32x64": ("rope_bf16_2x8064x32x64", True),
     "rope_bf16_2x4096x32x128": ("rope_bf16_2x4096x32x128", True),
     "fwd_bf16_8192x4097": ("fwd_bf16_8192x4097", True),
+    "bwd_bf16_8192x4097": ("bwd_bf16_8192x4097", True),
     "ln_residual_f32_16384x1024": ("ln_residual_f32_16384x1024", True),
 }
 
@@ -674,7 +678,7 @@ def main():
     if not args.no_ceiling:
         result["copy_ceiling"] = copy_ceiling(per_step, dev, min(args.steps, 1000))
         result["copy_ceiling"]["step_over_copy"] = round(gbs / result["copy_ceiling"]["value"], 4)
-        if kernel_kind(spec) == "fwd_offgrid":
+        if kernel_kind(spec).endswith("_offgrid"):
             # rows off the grid make unaligned 16-byte accesses: the copy
             # that makes the same ones
             un = copy_ceiling(per_step, dev, min(args.steps, 1000), offset=2)

@@ -177,6 +177,9 @@ WORKLOADS = {
                                          x=(0.0, 1.0), r=(0.0, 1.0), w=(1.0, 0.1), eps=1e-5, seed=1004),
     "bwd_bf16_8192x6144": dict(kind="bwd", M=8192, H=6144, dtype="bf16", wdtype="bf16",
                                x=(0.0, 1.0), w=(1.0, 0.1), dy=(0.0, 1.0), eps=1e-6, seed=1005),
+    # the backward on the ragged row length above (rows off the 16-byte grid)
+    "bwd_bf16_8192x4097": dict(kind="bwd", M=8192, H=4097, dtype="bf16", wdtype="bf16",
+                               x=(0.0, 1.0), w=(1.0, 0.1), dy=(0.0, 1.0), eps=1e-6, seed=1015),
     # backward of the residual pre-norm above: h is the stored post-add
     # stream (x + r of two N(0, 1) draws has std sqrt(2)); dres is the
     # gradient arriving on it, drawn from the residual stream

@@ -61,6 +61,10 @@ def test_ragged_forward_runs_the_off_grid_kernels():
     assert bench.kernel_kind(spec("fwd_bf16_8192x4096")) == "fwd"
     assert bench.kernel_kind(spec("fwd_f32_64x512")) == "fwd"
     assert bench.algorithmic_bytes(spec("fwd_bf16_8192x4097"), True) == 2 * 8192 * 4097 * 2 + 4097 * 2
+    # and so does the backward on them
+    assert bench.kernel_kind(spec("bwd_bf16_8192x4097")) == "bwd_offgrid"
+    assert bench.KERNEL_KEY["bwd_offgrid"] == "rmsnorm_bwd_kernel"
+    assert bench.kernel_kind(spec("bwd_bf16_8192x6144")) == "bwd"
 
 
 @pytest.mark.parametrize("argv,needle", [(["--gpus", "2"], "one GPU"), (["--graph", "--steps", "150"], "multiple")])

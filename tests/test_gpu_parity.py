@@ -110,8 +110,9 @@ def test_workload_fwd_residual():
                                       name=name), record=name)
 
 
-def test_workload_bwd():
-    name = "bwd_bf16_8192x6144"
+# bwd_bf16_8192x4097: the backward on rows off the 16-byte grid at full size
+@pytest.mark.parametrize("name", ["bwd_bf16_8192x6144", "bwd_bf16_8192x4097"])
+def test_workload_bwd(name):
     d = synthetic.make_inputs(name)
     print(f"[gpu] {name}", flush=True)
     rr = oracle_rrms32(d["x"], d["w"], d["eps"], d["dtype"])
@@ -122,8 +123,13 @@ def test_workload_bwd():
     # nearly cancel: at most 1e-4 of them (a rough count from the size of
     # float32 rounding against the terms gives 10-100 of the 5e7)
     assert rep_dx.floor_used <= 1e-4 * rep_dx.n, rep_dx
-    # every column, cancelling or not, meets the pure relative bound here
-    assert rep_dw.max_rel <= 1e-3, rep_dw
+    # columns whose sum does not cancel meet the pure relative bound
+    assert rep_dw.wc_cols > 0 and rep_dw.wc_max_rel <= 1e-3, rep_dw
+    if name == "bwd_bf16_8192x6144":
+        # here every column, cancelling or not, meets it too (max 1.6e-4);
+        # at H = 4097 one strongly cancelling column is 1.2e-3 off, inside
+        # the cancellation floor
+        assert rep_dw.max_rel <= 1e-3, rep_dw
 
 
 def test_workload_bwd_chained_with_gpu_rrms():
@@ -496,6 +502,36 @@ def test_determinism():
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
     assert torch.equal(c[0].view(torch.int16), e[0].view(torch.int16)) and torch.equal(c[1], e[1])
+
+
+@pytest.mark.parametrize("H,groups", [(512, 4), (3072, 1)])
+def test_bwd_deep_prefetch_same_bits(H, groups):
+    """bf16 rows on the grid whose one-vector tile leaves at most 6 waves per
+    CU (H = 512: one wave per row, 4 workgroups per CU; H = 3072: 6 waves,
+    one workgroup) keep three rows in flight per wave.  The same tile forced
+    through the tuning hook, with the same number of workgroups, runs the
+    kernel with two rows in flight: dx and dw keep their bits, and both are
+    at parity with the oracle."""
+    M = 4096
+    d = G.inputs(73 + H, M, H, "bf16", dy=True)
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-5, "bf16")
+    rr = torch.from_numpy(r32).to(G.DEV)
+    xd, dyd, wd = G.to_dev(d["x"], "bf16"), G.to_dev(d["dy"], "bf16"), G.to_dev(d["w"], "bf16")
+    t = tn.tile("bwd", H, "bf16", off_grid=False)
+    assert (t["vec"], t["vpt"], t["mis"], t["multi_pass"]) == (8, 1, False, False)
+    assert groups * t["wpr"] <= 6
+    print(f"[gpu] deep prefetch bf16 H={H}", flush=True)
+    dx, dw = tn.rmsnorm_bwd(dyd, xd, wd, rr)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tn.set_geometry("bwd", 1, t["wpr"], groups * cus, 1)
+    try:
+        dx2, dw2 = tn.rmsnorm_bwd(dyd, xd, wd, rr)
+        torch.cuda.synchronize()
+    finally:
+        tn.set_geometry("bwd")
+    assert torch.equal(dx.view(torch.int16), dx2.view(torch.int16)) and torch.equal(dw, dw2)
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx, "bf16"), dw.cpu().numpy(), "bf16",
+                                 name=f"bwd deep bf16 H={H}"))
 
 
 def test_weightless_equals_weight_of_ones():

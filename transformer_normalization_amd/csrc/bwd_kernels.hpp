@@ -71,9 +71,13 @@ struct BwdParams {
 // dw partial sums for them are not stored; two passes use the window in
 // pass 1 only (see there).  No access leaves the row.
 
-template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT, bool MIS = false>
+// DEEP: one more row in flight per wave (three prefetched instead of two), for
+// one-vector tiles that leave few waves resident per CU (the host's rule).
+template <int XDT, int WDT, int VEC, int VPT, bool RES, bool TWO_PASS, bool NT, int MAXT, bool MIS = false,
+          bool DEEP = false>
 __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
     static_assert(!MIS || VEC * Fmt<XDT>::bytes == 16, "rows off the grid: 16-byte vector tiles");
+    static_assert(!DEEP || (!TWO_PASS && VPT == 1 && VEC > 1), "deeper prefetch: one-vector resident tiles");
     // (rows off the grid: at least 16 bytes long, so that the last 16 bytes lie inside the row)
     __shared__ float red[2][16];
     const int row_threads = 64 * p.wpr;  // == blockDim.x
@@ -146,9 +150,10 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // per lane, and taken with v_readlane, so that no vector load inside
         // the loop makes the in-order memory counter wait for the prefetch.
         // depth 2 for small tiles, 1 where three rows would not fit the
-        // register budget (32-bit words holding x, dy and dres of one row)
+        // register budget (32-bit words holding x, dy and dres of one row),
+        // 3 with DEEP
         constexpr int WORDS = (RES ? 3 : 2) * VPT * (int)(sizeof(Raw<XDT, VEC>) / 4);
-        constexpr int PF = WORDS <= 16 ? 2 : 1;
+        constexpr int PF = DEEP ? 3 : WORDS <= 16 ? 2 : 1;
         Raw<XDT, VEC> xb[PF + 1][VPT], db[PF + 1][VPT], gb[RES ? PF + 1 : 1][VPT];
         constexpr int ES = Fmt<XDT>::bytes;
         const int lane = t & 63;

@@ -10,7 +10,14 @@ namespace rmsn {
 namespace tables {
 
 template <int XDT, int WDT, int VEC, bool RES, bool NT>
-bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
+bwd_fn bwd_kernel_for(int vpt, bool two_pass, bool deep) {
+    if (deep) {  // the plain backward's one-vector tile, three rows prefetched (16-bit formats)
+        if constexpr (VEC > 1 && !RES && Fmt<XDT>::bytes == 2)
+            return vpt == 1 && !two_pass
+                       ? rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, bwd_max_threads(VEC, RES), false, true>
+                       : nullptr;
+        return nullptr;
+    }
     if (two_pass) {
         constexpr int V = VEC > 1 ? 4 : 8;
         return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, RES, true, NT, 1024>;
@@ -34,23 +41,23 @@ bwd_fn bwd_kernel_for(int vpt, bool two_pass) {
 }
 
 template <int XDT, int WDT, bool RES, bool NT>
-bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass) {
+bwd_fn bwd_kernel_vec(int vec, int vpt, bool two_pass, bool deep) {
     constexpr int V = 16 / Fmt<XDT>::bytes;
-    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1, RES, NT>(vpt, two_pass)
-                    : bwd_kernel_for<XDT, WDT, V, RES, NT>(vpt, two_pass);
+    return vec == 1 ? bwd_kernel_for<XDT, WDT, 1, RES, NT>(vpt, two_pass, deep)
+                    : bwd_kernel_for<XDT, WDT, V, RES, NT>(vpt, two_pass, deep);
 }
 
 template <bool RES, bool NT>
-bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass) {
+bwd_fn bwd_lookup_nt(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool deep) {
     const bool wf32 = (wdt == RMSN_F32);
     switch (xdt) {
-    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32, RES, NT>(vec, vpt, two_pass);
+    case RMSN_F32: return bwd_kernel_vec<DT_F32, DT_F32, RES, NT>(vec, vpt, two_pass, deep);
     case RMSN_F16:
-        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32, RES, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_F16, DT_F16, RES, NT>(vec, vpt, two_pass);
+        return wf32 ? bwd_kernel_vec<DT_F16, DT_F32, RES, NT>(vec, vpt, two_pass, deep)
+                    : bwd_kernel_vec<DT_F16, DT_F16, RES, NT>(vec, vpt, two_pass, deep);
     case RMSN_BF16:
-        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, RES, NT>(vec, vpt, two_pass)
-                    : bwd_kernel_vec<DT_BF16, DT_BF16, RES, NT>(vec, vpt, two_pass);
+        return wf32 ? bwd_kernel_vec<DT_BF16, DT_F32, RES, NT>(vec, vpt, two_pass, deep)
+                    : bwd_kernel_vec<DT_BF16, DT_BF16, RES, NT>(vec, vpt, two_pass, deep);
     default: break;  // any other value: no kernel
     }
     return nullptr;

@@ -30,13 +30,14 @@ fwd_fn fwd_lookup_resid(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bo
 fwd_fn fwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, int mode, bool nt);
 // AdaLN: wdt is the format of the weight, scale and shift
 fwd_fn fwd_lookup_adaln(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
-bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
+// deep: the one-vector tile with three rows prefetched per wave (rmsnorm_bwd_kernel's DEEP)
+bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt, bool deep);
 // the backward of the fused residual pre-norm (adds the residual-stream gradient)
 bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt);
 // the backward for rows off the 16-byte grid (16-byte vectors at the row's
 // byte offset; x, dy, dres and dx element-aligned, w 16-byte aligned), one
 // pass or, for rows longer than a tile, two (vpt 4)
-bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, bool res, bool nt);
+bwd_fn bwd_mis_lookup(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vpt, bool two_pass, bool res, bool nt, bool deep);
 const void *dw_finalize_kernel();
 // vec: 16 / element size, or 1 for single elements; tdt: x's format or
 // float32; xchg: the lane-exchange layout (vectors only)

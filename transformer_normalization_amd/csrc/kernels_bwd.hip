@@ -32,9 +32,10 @@ __global__ void __launch_bounds__(kFinCols * kFinSlices) rmsnorm_dw_finalize(con
     }
 }
 
-bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
-    return nt ? tables::bwd_lookup_nt<false, true>(xdt, wdt, vec, vpt, two_pass)
-              : tables::bwd_lookup_nt<false, false>(xdt, wdt, vec, vpt, two_pass);
+bwd_fn bwd_lookup_plain(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt,
+                        bool deep) {
+    return nt ? tables::bwd_lookup_nt<false, true>(xdt, wdt, vec, vpt, two_pass, deep)
+              : tables::bwd_lookup_nt<false, false>(xdt, wdt, vec, vpt, two_pass, deep);
 }
 
 const void *dw_finalize_kernel() { return (const void *)rmsnorm_dw_finalize; }

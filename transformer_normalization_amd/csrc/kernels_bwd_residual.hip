@@ -6,8 +6,8 @@
 namespace rmsn {
 
 bwd_fn bwd_lookup_res(rmsn_dtype_t xdt, rmsn_dtype_t wdt, int vec, int vpt, bool two_pass, bool nt) {
-    return nt ? tables::bwd_lookup_nt<true, true>(xdt, wdt, vec, vpt, two_pass)
-              : tables::bwd_lookup_nt<true, false>(xdt, wdt, vec, vpt, two_pass);
+    return nt ? tables::bwd_lookup_nt<true, true>(xdt, wdt, vec, vpt, two_pass, false)
+              : tables::bwd_lookup_nt<true, false>(xdt, wdt, vec, vpt, two_pass, false);
 }
 
 }  // namespace rmsn

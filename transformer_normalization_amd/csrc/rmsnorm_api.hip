@@ -633,17 +633,29 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (ov.d == 2) interleave = false;
     }
     const bool nt = use_streaming((res ? 4 : 3) * M * H * eb);
-    bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, g.two_pass, res, nt)
+    // Whole row groups per CU, rows interleaved (see bwd_groups_per_cu).
+    const int gpc = elem_groups > 0 ? elem_groups : bwd_groups_per_cu(res, g.wpr, g.nvec);
+    // A one-vector tile whose rule leaves at most 6 waves per CU keeps three
+    // rows in flight per wave instead of two.  Measured on gfx950 (bf16,
+    // 2^25-element calls, two rows in brackets): plain aligned H = 512 (4
+    // waves) 66.4 % (61.2 %), off the grid H = 2049 (5) 50.4 % (44.7 %),
+    // 1025 (6) 52.7 % (48.5 %), residual off the grid H = 1025 (3) 44.6 %
+    // (39.6 %), 2049 (5) 57.2 % (53.2 %).  With more waves it lost: plain
+    // aligned H = 2048 and 1024 (8 waves) -1.1 and -0.6 points, 6144 (12)
+    // -1.0; and so did the aligned residual H = 512 (4 waves, -3.3), which
+    // keeps two.  Same bits either way.  16-bit formats only (as measured).
+    const bool deep =
+        !ov.set && eb == 2 && !g.two_pass && g.vec > 1 && g.vpt == 1 && (mis || !res) && gpc * g.wpr <= 6;
+    bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, g.two_pass, res, nt, deep)
                 : res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
-                      : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt);
+                      : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt, deep);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     int cus = 0;
     if ((st = device_info(&cus)) != RMSN_OK) return st;
-    // Whole row groups per CU, rows interleaved (see bwd_groups_per_cu); the
-    // dw partial sums are P x H x 4 bytes, written and read once.  A grid that
-    // is not a multiple of the CU count leaves a tail of CUs with an extra
-    // block.
-    if (P <= 0) P = (int64_t)cus * (elem_groups > 0 ? elem_groups : bwd_groups_per_cu(res, g.wpr, g.nvec));
+    // The dw partial sums are P x H x 4 bytes, written and read once.  A grid
+    // that is not a multiple of the CU count leaves a tail of CUs with an
+    // extra block.
+    if (P <= 0) P = (int64_t)cus * gpc;
     if (P > max_partials(H)) P = max_partials(H);
     if (P > M) P = M;
     const int64_t rows_per = (M + P - 1) / P;

@@ -638,12 +638,13 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     // A one-vector tile whose rule leaves at most 6 waves per CU keeps three
     // rows in flight per wave instead of two.  Measured on gfx950 (bf16,
     // 2^25-element calls, two rows in brackets): plain aligned H = 512 (4
-    // waves) 66.4 % (61.2 %), off the grid H = 2049 (5) 50.4 % (44.7 %),
-    // 1025 (6) 52.7 % (48.5 %), residual off the grid H = 1025 (3) 44.6 %
-    // (39.6 %), 2049 (5) 57.2 % (53.2 %).  With more waves it lost: plain
-    // aligned H = 2048 and 1024 (8 waves) -1.1 and -0.6 points, 6144 (12)
-    // -1.0; and so did the aligned residual H = 512 (4 waves, -3.3), which
-    // keeps two.  Same bits either way.  16-bit formats only (as measured).
+    // waves) 67.4 % (61.2 %), 3072 (6) 62.5 % (60.0 %), off the grid
+    // H = 1025 (6) 52.9 % (48.7 %), 2049 (5) 50.0 % (44.7 %), residual off the
+    // grid H = 1025 (3) 44.3 % (39.2 %), 2049 (5) 56.7 % (52.8 %).  With more
+    // waves it lost: plain aligned H = 2048 and 1024 (8 waves) -1.1 and -0.6
+    // points, 6144 (12) -1.0; and so did the aligned residual H = 512 (4
+    // waves, -3.3), which keeps two.  Same bits either way.  16-bit formats
+    // only (as measured).
     const bool deep =
         !ov.set && eb == 2 && !g.two_pass && g.vec > 1 && g.vpt == 1 && (mis || !res) && gpc * g.wpr <= 6;
     bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, g.two_pass, res, nt, deep)

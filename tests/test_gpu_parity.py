@@ -398,9 +398,9 @@ def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
 def test_in_place_outputs(H):
     """y written over x, residual_out over the residual, dx over dy.  At
     H = 4097 (bf16) the rows are off the 16-byte grid and take 16-byte
-    vectors at the row's byte offset on a 3-wave row (3 vectors per thread):
+    vectors at the row's byte offset on a 2-wave row (6 vectors per thread):
     the row's last vector, 512, is a window over the row's last 16 bytes,
-    held by thread 128 (wave 2), and its leading 7 columns are also vector
+    held by thread 0 (wave 0), and its leading 7 columns are also vector
     511's, held by thread 127 (wave 1).  Only the order of every aligned-away
     store after all of the row's loads keeps the in-place result equal to
     the out-of-place one there.  At H = 70001 every call takes two passes

@@ -80,11 +80,12 @@ def test_exposure_rule_matches_mapping():
 
 
 def test_worked_case_is_exposed():
-    # bf16 H = 4097 fused residual: vectors 511 and 512 (the window) are
-    # threads 127 and 128 of a 3-wave row, waves 1 and 2
+    # bf16 H = 4097 fused residual: 513 vectors on a 2-wave row of 128
+    # threads, 6 vectors per thread; vector 511 is thread 127 (wave 1) and
+    # vector 512 (the window) thread 0 (wave 0)
     t = tn.tile("fwd_residual", 4097, "bf16", off_grid=True)
-    assert t["mis"] and (t["vpt"], t["wpr"]) == (3, 3)
-    assert _exposed(4097, 8, 3)
+    assert t["mis"] and (t["vpt"], t["wpr"]) == (6, 2)
+    assert _exposed(4097, 8, 2)
 
 
 def test_exposure_table(capsys):
@@ -99,7 +100,7 @@ def test_exposure_table(capsys):
     # the exposure only arises for rows of several waves whose last vector
     # starts a wave; every row whose length leaves H % vec != 0 and nvec - 1
     # a multiple of 64 and that takes a multi-wave tile is listed
-    assert ("fwd_residual", "bf16", 4097, 3, 3) in rows
+    assert ("fwd_residual", "bf16", 4097, 6, 2) in rows
     for op, dt, H, vpt, wpr in rows:
         vec = 16 // ES[dt]
         assert wpr > 1 and (-(-H // vec) - 1) % 64 == 0

@@ -164,13 +164,53 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
     return g;
 }
 
+// 16-bit rows off the grid of 193 to 768 vectors, every forward kind: two
+// waves per row, with the fewest idle vector slots over vpt in {1, 2, 3, 4, 6};
+// vpt = 0 for other rows.  Measured on gfx950 (bf16, HIP events, previous rule
+// in brackets):
+//   AdaLN, 2 x 4096 rows, against the aligned rule: per-batch conditioning
+//   H = 2049 45.1 % (37.3 %), 3073 50.1 % (44.9 %), 4097 48.5 % (41.2 %),
+//   6143 54.0 % (46.4 %); per-token H = 2049 66.8 % (53.1 %), 4097 71.2 %
+//   (63.1 %), 6143 73.8 % (60.7 %); 1537 and 7169 within 0.3 %.  The plain
+//   forward's off-grid rule, which takes fewer waves per row, lost to the
+//   aligned rule there at H = 1537, 7169 and 8191 with per-batch
+//   conditioning (-3 to -4 points).
+//   Plain forward and fused residual, 2^25 elements, against the off-grid
+//   rule: H = 1537 61.7 % (59.3 %), 2049 66.4 % (63.4 %), 4097 63.6 %
+//   (62.2 %), fused residual 2049 67.1 % (65.5 %); LayerNorm 2049 58.4 %
+//   (53.6 %), 4097 54.6 % (53.9 %); 3073, 5121 and 6143 the same tile.
+//   float32 rows lost 0.5 points at H = 2049 and keep their rules.  Rows of
+//   up to 192 vectors keep them too: at H = 1023 and 1025 the plain forward
+//   lost 3.6 and 4.4 points and LayerNorm 7.9 to one-wave rows (the fused
+//   residual, AdaLN and residual LayerNorm gained 1.6 to 2.7).
+Geom pick_two_wave_geom(Kind kind, int H, int vec) {
+    static const int kVpt[] = {1, 2, 3, 4, 6};
+    Geom g{};
+    g.vec = vec;
+    g.nvec = (H + vec - 1) / vec;
+    if (g.nvec <= 192) return g;
+    int best = 0;
+    for (int vpt : kVpt) {
+        if (128 * vpt < g.nvec || max_threads_for(kind, vpt, vec) < 128) continue;
+        if (best == 0) best = vpt;  // the smallest vpt that holds the row idles the fewest slots
+    }
+    if (best == 0) return g;
+    g.vpt = best;
+    g.wpr = 2;
+    g.nchunks = 1;
+    g.two_pass = false;
+    g.rpw = 64 * 2 * 2 <= max_threads_for(kind, best, vec) ? 2 : 1;
+    return g;
+}
+
 // The forward family's tile with no forced geometry (vec_ok, mis_ok as for
 // bwd_tile; mis_ok also needs the bias and AdaLN's conditioning rows
 // aligned).  Rows off the 16-byte grid take 16-byte vectors at each row's
-// byte offset when the row holds at least 512 bytes: RMSNorm rows and 16-bit
-// LayerNorm rows from 1 KiB on the off-grid tile rule, shorter rows, AdaLN
-// and float32 LayerNorm on the aligned rule, rows longer than any resident
-// tile in passes over the row.
+// byte offset when the row holds at least 512 bytes.  16-bit rows of 193 to
+// 768 vectors, every forward kind, take two waves per row; other RMSNorm and
+// 16-bit LayerNorm rows from 1 KiB take the off-grid tile rule; shorter rows,
+// other AdaLN rows and float32 LayerNorm the aligned rule; rows longer than
+// any resident tile passes over the row.
 // Measured on gfx950 against the element-wise tile (bf16, 2^25 elements):
 // H = 257 49.5 % against 37.4 % of peak, H = 511 68.9 % and 56.3 %, but
 // H = 127 27.8 % and 31.3 % (16 vectors leave most of a wave idle);
@@ -187,7 +227,10 @@ Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
     const bool offrule = kind == Kind::Fwd || kind == Kind::FwdResid || (kind == Kind::Ln && eb == 2);
     *mis = false;
     if (!vec_ok && mis_ok && (int64_t)H * eb >= 512) {
-        Geom m = offrule && (int64_t)H * eb >= 1024 ? pick_offgrid_geom(kind, H, vecw) : Geom{};
+        Geom m{};
+        if (eb == 2 && (offrule || kind == Kind::FwdAdaln) && (int64_t)H * eb >= 1024)
+            m = pick_two_wave_geom(kind, H, vecw);
+        if (m.vpt == 0 && offrule && (int64_t)H * eb >= 1024) m = pick_offgrid_geom(kind, H, vecw);
         if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
         *mis = true;
         return m;

@@ -1,6 +1,7 @@
 """Randomised GPU parity: seeded random shapes, formats, row paddings
 (aligned and misaligned) and optional parameters for every entry point,
-against the float64 oracle with each operation's stated tolerance; and
+against the float64 oracle with each operation's stated tolerance; a second
+draw over every class of tile, with rows up to 80000 elements; and
 concurrent calls from several host threads on their own streams.
 
 The cases are drawn once from a fixed seed, so a failure names a case that
@@ -195,3 +196,143 @@ def test_concurrent_calls_from_threads_on_their_own_streams():
         for a, b in zip(got[k], want[k]):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), k
+
+
+# ---------------------------------------------------------------------------
+# tile classes: rows from 1 to 80000 elements
+# ---------------------------------------------------------------------------
+# Row lengths drawn log-uniformly from three bands, 1 to 80000, 1000 to 20000
+# and 16000 to 80000, reach every class of tile the library picks from the
+# shape alone: one-vector and multi-vector resident tiles, one and two waves
+# per row, rows off the 16-byte grid read in 16-byte vectors or element by
+# element, passes over rows longer than any tile (with the backward's later
+# chunks in the workspace beyond 65536 columns), and the backward's deeper
+# prefetch.  Weights are float32 for some 16-bit cases.  Half of the cases
+# place every tensor in a padded buffer at an element offset of its own, and
+# their outputs' padding must stay untouched.
+
+TILE_OPS = ("fwd", "residual", "adaln_batch", "adaln_token", "layernorm", "bwd", "bwd_residual")
+N_TILE_CASES = 280
+
+
+def _tile_cases():
+    rng = np.random.default_rng(20261202)  # picks shapes and layouts only
+    out = []
+    for i in range(N_TILE_CASES):
+        op = TILE_OPS[i % len(TILE_OPS)]
+        lo, hi = ((1.0, 80000.0), (1000.0, 20000.0), (16000.0, 80000.0))[i % 3]
+        H = int(np.exp(rng.uniform(np.log(lo), np.log(hi))))
+        M = int(rng.integers(1, 25))
+        dtype = ("bf16", "f16", "f32")[int(rng.integers(0, 3))]
+        wdtype = "f32" if dtype != "f32" and rng.uniform() < 0.3 else dtype
+        view = bool(rng.uniform() < 0.5)
+        out.append((i, op, M, H, dtype, wdtype, view))
+    return out
+
+
+TILE_CASES = _tile_cases()
+
+
+def _placed(a, dtype, view, pad, offset):
+    """Device copy of host array a: contiguous, or a padded view at an
+    element offset."""
+    d = G.to_dev(a, dtype)
+    if not view:
+        return d
+    _, v = G.sentinel_view(a.shape[0], a.shape[1], pad, offset, dtype, 0.0)
+    v.copy_(d)
+    return v
+
+
+def _out_view(M, H, dtype, view, pad, offset):
+    """An output: a fresh tensor, or a sentinel-filled padded view."""
+    if not view:
+        return None, torch.empty((M, H), dtype=G.torch_dtype(dtype), device=G.DEV)
+    return G.sentinel_view(M, H, pad, offset, dtype, -77.0)
+
+
+def _rrms32_as(x, w, eps, dtype, wdtype):
+    _, r = oracle.fwd(x, w, G.eps32(eps), dtype, wdtype)
+    return r.astype(np.float32)
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=[f"{c[0]}-{c[1]}-{c[4]}-{c[2]}x{c[3]}{'-view' if c[6] else ''}"
+                                                  for c in TILE_CASES])
+def test_random_tile_class(case):
+    i, op, M, H, dtype, wdtype, view = case
+    seed = 9000 + i
+    print(f"[gpu] sweep {i} {op} {dtype}/{wdtype} M={M} H={H} view={view}", flush=True)
+    reps = []
+    outs = []  # (buffer, view) pairs whose padding must stay untouched
+    if op in ("adaln_batch", "adaln_token"):
+        B = 2 if M >= 2 else 1
+        S = M // B
+        M = B * S
+        C = B if op == "adaln_batch" else M
+        d = G.inputs(seed, M, H, dtype, wdtype=wdtype)
+        sc = synthetic.normal_tensor(seed, synthetic.STREAM_SCALE, (C, H), wdtype, 0.0, 0.5)
+        sh = synthetic.normal_tensor(seed, synthetic.STREAM_SHIFT, (C, H), wdtype, 0.0, 0.5)
+        x = _placed(d["x"], dtype, view, 3, 1)
+        scd, shd = _placed(sc, wdtype, view, 5, 2), _placed(sh, wdtype, view, 5, 2)
+        if op == "adaln_batch":
+            scd, shd = scd.unsqueeze(1), shd.unsqueeze(1)
+        else:
+            scd, shd = scd.view(B, S, H), shd.view(B, S, H)
+        buf, y = _out_view(M, H, dtype, view, 2, 3)
+        y, rr = tn.rmsnorm_adaln_fwd(x.view(B, S, H), G.to_dev(d["w"], wdtype), scd, shd, 1e-6,
+                                     out=y.view(B, S, H), return_rrms=True)
+        torch.cuda.synchronize()
+        outs.append((buf, y.view(M, H)))
+        reps += G.adaln_vs_oracle(d["x"], d["w"], sc, sh, S if op == "adaln_batch" else 1,
+                                  G.to_host(y.reshape(M, H), dtype), rr.view(-1).cpu().numpy(), 1e-6, dtype, wdtype,
+                                  chunk=M, name=f"sweep {i} {op}")
+    elif op in ("fwd", "residual", "layernorm"):
+        d = G.inputs(seed, M, H, dtype, wdtype=wdtype, residual=True)
+        x, r = _placed(d["x"], dtype, view, 1, 3), _placed(d["r"], dtype, view, 2, 1)
+        w = G.to_dev(d["w"], wdtype)
+        buf, y = _out_view(M, H, dtype, view, 3, 5)
+        if op == "fwd":
+            y, rr = tn.rmsnorm_fwd(x, w, 1e-5, out=y, return_rrms=True)
+            torch.cuda.synchronize()
+            reps += G.fwd_vs_oracle(d["x"], d["w"], G.to_host(y, dtype), rr.cpu().numpy(), 1e-5, dtype, wdtype,
+                                    name=f"sweep {i} fwd")
+        else:
+            rbuf, ro = _out_view(M, H, dtype, view, 1, 2)
+            if op == "residual":
+                y, ro, rr = tn.rmsnorm_fwd_residual(x, r, w, 1e-5, out=y, residual_out=ro, return_rrms=True)
+                torch.cuda.synchronize()
+                reps += G.residual_vs_oracle(d["x"], d["r"], d["w"], G.to_host(y, dtype), G.to_host(ro, dtype),
+                                             rr.cpu().numpy(), 1e-5, dtype, wdtype, name=f"sweep {i} residual")
+            else:
+                b = synthetic.normal_tensor(seed, synthetic.STREAM_BIAS, (H,), wdtype, 0.0, 0.1)
+                y, ro, mean, rstd = tn.layernorm_fwd_residual(x, r, w, G.to_dev(b, wdtype), 1e-5, out=y,
+                                                              residual_out=ro, return_stats=True)
+                torch.cuda.synchronize()
+                reps += G.ln_vs_oracle(d["x"], d["r"], d["w"], b, G.to_host(y, dtype), G.to_host(ro, dtype),
+                                       mean.cpu().numpy(), rstd.cpu().numpy(), 1e-5, dtype, wdtype,
+                                       name=f"sweep {i} layernorm")
+            outs.append((rbuf, ro))
+        outs.append((buf, y))
+    else:
+        d = G.inputs(seed, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
+        r32 = _rrms32_as(d["x"], d["w"], 1e-5, dtype, wdtype)
+        rr = torch.from_numpy(r32).to(G.DEV)
+        dy, x = _placed(d["dy"], dtype, view, 1, 1), _placed(d["x"], dtype, view, 3, 2)
+        w = G.to_dev(d["w"], wdtype)
+        buf, dx = _out_view(M, H, dtype, view, 5, 5)
+        if op == "bwd":
+            dx, dw = tn.rmsnorm_bwd(dy, x, w, rr, dx=dx)
+            torch.cuda.synchronize()
+            reps += G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx, dtype), dw.cpu().numpy(), dtype,
+                                    wdtype, name=f"sweep {i} bwd")
+        else:
+            g = _placed(d["r"], dtype, view, 2, 3)
+            dx, dw = tn.rmsnorm_bwd_residual(dy, x, g, w, rr, dh=dx)
+            torch.cuda.synchronize()
+            reps += G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], r32, G.to_host(dx, dtype),
+                                             dw.cpu().numpy(), dtype, wdtype, name=f"sweep {i} bwd_residual")
+        outs.append((buf, dx))
+    G.assert_ok(*reps)
+    for b, v in outs:
+        if b is not None:
+            assert G.untouched(b, v, -77.0), case

@@ -143,3 +143,21 @@ def test_long_rows_off_the_grid_take_vectors(op, dt, H):
 def test_longest_one_pass_backward_rows_off_the_grid(op, dt, H):
     t = tn.tile(op, H, dt, off_grid=True)
     assert t["mis"] and not t["multi_pass"]
+
+
+@pytest.mark.parametrize("op", ["fwd", "fwd_residual", "adaln", "layernorm"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_two_waves_per_row_for_16bit_rows_of_193_to_768_vectors(op, dt):
+    # from 193 vectors (H = 1537) to 768 (H = 6144) a 16-bit row off the grid
+    # takes two waves, with the fewest idle slots over 1-6 vectors per thread
+    for H, vpt in ((1537, 2), (2049, 3), (3073, 4), (4097, 6), (6143, 6), (6144, 6)):
+        t = tn.tile(op, H, dt, off_grid=True)
+        assert t["mis"] and (t["vpt"], t["wpr"], t["rpw"]) == (vpt, 2, 2), (H, t)
+    # 192 vectors and fewer, and 769 and more, keep the other rules
+    assert tn.tile(op, 1535, dt, off_grid=True)["wpr"] == 1
+    assert tn.tile(op, 6145, dt, off_grid=True)["wpr"] > 2
+
+
+def test_float32_rows_keep_their_rules():
+    assert tn.tile("fwd", 2049, "f32", off_grid=True)["wpr"] == 3
+    assert tn.tile("fwd", 4097, "f32", off_grid=True)["wpr"] == 3

@@ -59,6 +59,21 @@ def test_noalloc_matches_workspace_backward_over_consecutive_calls():
         assert torch.equal(dw.view(torch.int32), ref_dw.view(torch.int32)), (M, H)
 
 
+def test_noalloc_long_rows_off_the_grid_reuse_the_scratch():
+    # rows off the grid longer than one tile take two passes; beyond 65536
+    # columns their later chunks zero and then add into the workgroup's
+    # partial row at every row, here in the static scratch, so a second call
+    # with other data must not see the first one's sums; then a shorter row
+    for seed, M, H in ((1203, 32, 70001), (1204, 32, 70001), (1205, 24, 30001)):
+        print(f"[gpu] noalloc M={M} H={H}", flush=True)
+        dy, x, w, rr = _case(seed, M, H)
+        ref_dx, ref_dw = tn.rmsnorm_bwd(dy, x, w, rr)
+        dx, dw = _noalloc(dy, x, w, rr)
+        torch.cuda.synchronize()
+        assert torch.equal(dx.view(torch.int16), ref_dx.view(torch.int16)), (M, H)
+        assert torch.equal(dw.view(torch.int32), ref_dw.view(torch.int32)), (M, H)
+
+
 def test_noalloc_weightless_and_binding():
     dy, x, _, rr = _case(1203, 64, 1000)
     ref_dx, _ = tn.rmsnorm_bwd(dy, x, None, rr)

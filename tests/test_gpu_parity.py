@@ -641,8 +641,8 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
     tails never written, dx written in place over dy and dh over dres with the
     same bits, and, for an H of whole vectors, the bits of the contiguous
     (aligned) run; the forced single-element tile is at parity too.  Rows
-    longer than one tile (16-bit plain from 16385, residual from 8193,
-    float32 residual from 8193 and plain from 16385) take two passes; beyond
+    longer than one tile (plain from 16385; residual from 16385 at 16 bits,
+    from 8193 in float32) take two passes; beyond
     65536 columns their later chunks add into the workspace row at each row,
     and at 70001 the row's last partial vector lies in such a chunk."""
     M = 41 if H <= 8192 else 9

@@ -126,7 +126,7 @@ def test_tile_query_aligned_rows():
 
 
 @pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16385), ("bwd", "f32", 16385), ("bwd", "bf16", 70001),
-                                     ("bwd_residual", "bf16", 8193), ("bwd_residual", "f16", 12289),
+                                     ("bwd_residual", "bf16", 16385), ("bwd_residual", "f16", 20001),
                                      ("bwd_residual", "f32", 8193), ("fwd", "bf16", 70001),
                                      ("fwd_residual", "bf16", 16385), ("fwd_residual", "f32", 30001),
                                      ("adaln", "bf16", 16385), ("layernorm", "bf16", 16385),
@@ -138,8 +138,8 @@ def test_long_rows_off_the_grid_take_vectors(op, dt, H):
     assert t["multi_pass"] and t["mis"] and t["vec"] == 16 // ES[dt]
 
 
-@pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16383), ("bwd", "f32", 16383), ("bwd_residual", "bf16", 8191),
-                                     ("bwd_residual", "f32", 8191)])
+@pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16383), ("bwd", "f32", 16383), ("bwd_residual", "bf16", 16383),
+                                     ("bwd_residual", "f16", 12289), ("bwd_residual", "f32", 8191)])
 def test_longest_one_pass_backward_rows_off_the_grid(op, dt, H):
     t = tn.tile(op, H, dt, off_grid=True)
     assert t["mis"] and not t["multi_pass"]

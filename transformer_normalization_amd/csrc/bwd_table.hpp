@@ -11,11 +11,12 @@ namespace tables {
 
 template <int XDT, int WDT, int VEC, bool RES, bool NT>
 bwd_fn bwd_kernel_for(int vpt, bool two_pass, bool deep) {
+    constexpr int ES = Fmt<XDT>::bytes;  // x's element size, for the register budget
     if (deep) {  // the plain backward's one-vector tile, three rows prefetched (16-bit formats)
-        if constexpr (VEC > 1 && !RES && Fmt<XDT>::bytes == 2)
-            return vpt == 1 && !two_pass
-                       ? rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, bwd_max_threads(VEC, RES), false, true>
-                       : nullptr;
+        constexpr int T = bwd_max_threads(VEC, RES, ES);
+        if constexpr (VEC > 1 && !RES && ES == 2)
+            return vpt == 1 && !two_pass ? rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, T, false, true>
+                                         : nullptr;
         return nullptr;
     }
     if (two_pass) {
@@ -23,17 +24,17 @@ bwd_fn bwd_kernel_for(int vpt, bool two_pass, bool deep) {
         return rmsnorm_bwd_kernel<XDT, WDT, VEC, V, RES, true, NT, 1024>;
     }
     switch (vpt) {
-    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, bwd_max_threads(1 * VEC, RES)>;
-    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, RES, false, NT, bwd_max_threads(2 * VEC, RES)>;
-    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, RES, false, NT, bwd_max_threads(4 * VEC, RES)>;
+    case 1: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, bwd_max_threads(1 * VEC, RES, ES)>;
+    case 2: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 2, RES, false, NT, bwd_max_threads(2 * VEC, RES, ES)>;
+    case 4: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 4, RES, false, NT, bwd_max_threads(4 * VEC, RES, ES)>;
     default: break;
     }
     if constexpr (VEC == 1) {
-        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, RES, false, NT, bwd_max_threads(8 * VEC, RES)>;
+        if (vpt == 8) return rmsnorm_bwd_kernel<XDT, WDT, VEC, 8, RES, false, NT, bwd_max_threads(8 * VEC, RES, ES)>;
     }
     if constexpr (VEC > 1) {
         switch (vpt) {
-        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, RES, false, NT, bwd_max_threads(3 * VEC, RES)>;
+        case 3: return rmsnorm_bwd_kernel<XDT, WDT, VEC, 3, RES, false, NT, bwd_max_threads(3 * VEC, RES, ES)>;
         default: break;
         }
     }

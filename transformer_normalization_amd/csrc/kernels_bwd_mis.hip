@@ -8,19 +8,20 @@ namespace {
 
 template <int XDT, int WDT, bool RES, bool NT>
 bwd_fn mis_kernel(int vpt, bool two_pass, bool deep) {
-    constexpr int V = 16 / Fmt<XDT>::bytes;
+    constexpr int ES = Fmt<XDT>::bytes;  // x's element size, for the register budget
+    constexpr int V = 16 / ES;
     if (two_pass) return vpt == 4 ? rmsnorm_bwd_kernel<XDT, WDT, V, 4, RES, true, NT, 1024, true> : nullptr;
     if (deep) {  // the one-vector tile, three rows prefetched (16-bit formats)
-        if constexpr (Fmt<XDT>::bytes == 2)
-            return vpt == 1 ? rmsnorm_bwd_kernel<XDT, WDT, V, 1, RES, false, NT, bwd_max_threads(V, RES), true, true>
-                            : nullptr;
+        constexpr int T = bwd_max_threads(V, RES, ES);
+        if constexpr (ES == 2)
+            return vpt == 1 ? rmsnorm_bwd_kernel<XDT, WDT, V, 1, RES, false, NT, T, true, true> : nullptr;
         return nullptr;
     }
     switch (vpt) {
-    case 1: return rmsnorm_bwd_kernel<XDT, WDT, V, 1, RES, false, NT, bwd_max_threads(1 * V, RES), true>;
-    case 2: return rmsnorm_bwd_kernel<XDT, WDT, V, 2, RES, false, NT, bwd_max_threads(2 * V, RES), true>;
-    case 3: return rmsnorm_bwd_kernel<XDT, WDT, V, 3, RES, false, NT, bwd_max_threads(3 * V, RES), true>;
-    case 4: return rmsnorm_bwd_kernel<XDT, WDT, V, 4, RES, false, NT, bwd_max_threads(4 * V, RES), true>;
+    case 1: return rmsnorm_bwd_kernel<XDT, WDT, V, 1, RES, false, NT, bwd_max_threads(1 * V, RES, ES), true>;
+    case 2: return rmsnorm_bwd_kernel<XDT, WDT, V, 2, RES, false, NT, bwd_max_threads(2 * V, RES, ES), true>;
+    case 3: return rmsnorm_bwd_kernel<XDT, WDT, V, 3, RES, false, NT, bwd_max_threads(3 * V, RES, ES), true>;
+    case 4: return rmsnorm_bwd_kernel<XDT, WDT, V, 4, RES, false, NT, bwd_max_threads(4 * V, RES, ES), true>;
     default: break;
     }
     return nullptr;

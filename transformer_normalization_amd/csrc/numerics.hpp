@@ -329,9 +329,15 @@ constexpr int fwd_max_threads(int elems, int mode) {  // mode: 0 plain, 1 residu
 }
 // LayerNorm keeps x (and the residual) packed plus packed weight and bias
 constexpr int ln_max_threads(int elems) { return elems <= 16 ? 1024 : elems <= 32 ? 512 : 256; }
-// (res: the residual backward holds a third row tile, dres, in registers)
-constexpr int bwd_max_threads(int elems, bool res = false) {
-    return res ? (elems <= 8 ? 1024 : elems <= 16 ? 512 : 256) : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);
+// (res: the residual backward holds a third row tile, dres, in registers;
+// es: bytes per element of x.  16-bit residual tiles of 16 elements, two
+// 16-byte vectors per row stream, take 111-128 VGPRs and fit 1024 threads;
+// measured on gfx950 against the 512-thread cap, which sent rows of 8193 to
+// 16384 elements to two passes: bf16 2048 x 16384 59.9 % of peak against
+// 50.4 %, 4096 x 10240 66.3 % against 48.1 %.)
+constexpr int bwd_max_threads(int elems, bool res = false, int es = 4) {
+    return res ? (elems <= 8 || (es == 2 && elems <= 16) ? 1024 : elems <= 16 ? 512 : 256)
+               : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);
 }
 
 }  // namespace rmsn

@@ -63,7 +63,7 @@ constexpr int kScalarVpt[] = {1, 2, 4, 8};
 // largest workgroup each register tile may use (the kernels' launch bounds)
 int max_threads_for(Kind kind, int vpt, int vec) {
     return kind == Kind::Bwd        ? bwd_max_threads(vpt * vec)
-           : kind == Kind::BwdRes   ? bwd_max_threads(vpt * vec, true)
+           : kind == Kind::BwdRes   ? bwd_max_threads(vpt * vec, true, vec == 8 ? 2 : 4)
            : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID)
            : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN)
            : kind == Kind::Ln       ? ln_max_threads(vpt * vec)

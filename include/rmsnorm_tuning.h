@@ -47,7 +47,9 @@ void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t
  * geometry.  op: 0 RMSNorm forward, 1 fused residual, 2 AdaLN, 3 LayerNorm,
  * 4 backward, 5 residual backward.  layout 0: every row start 16-byte
  * aligned; 1: row starts only element-aligned (parameters 16-byte aligned).
- * Writes out[0] elements per access, out[1] accesses per thread, out[2] waves
+ * The parameters (weight, AdaLN's rows, LayerNorm's bias) are taken in x's
+ * format; a float32 weight on 16-bit data can give another tile (a smaller
+ * register budget).  Writes out[0] elements per access, out[1] accesses per thread, out[2] waves
  * per row, out[3] rows per workgroup, out[4] 1 when rows off the 16-byte grid
  * take 16-byte vectors at each row's byte offset (0: single elements or rows
  * on the grid), out[5] 1 when the row takes the multi-pass path (out[1] and

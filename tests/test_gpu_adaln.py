@@ -77,7 +77,9 @@ def test_per_batch_rows_walked_by_each_row_group(B, S):
 
 @pytest.mark.parametrize("pdtype", ["same", "f32"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 3072, 4097, 8192, 16384, 20000])  # 16384: capped tile
+# 16384: capped tile; 32768: the longest 16-bit row held in registers with
+# 16-bit parameters (two passes with float32 ones)
+@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 3072, 4097, 8192, 16384, 20000, 32768])
 def test_adaln_shapes(dtype, pdtype, H):
     pd = dtype if pdtype == "same" else "f32"
     B, S = 3, 7
@@ -142,14 +144,15 @@ def test_adaln_misaligned_rows():
 
 @pytest.mark.parametrize("per_batch", [True, False], ids=["per_batch", "per_token"])
 @pytest.mark.parametrize("dtype,pdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("H", [2049, 4096, 16385, 40001])
+@pytest.mark.parametrize("H", [2049, 4096, 16385, 32767, 40001])
 def test_adaln_rows_off_the_grid(H, dtype, pdtype, per_batch):
     """Rows off the 16-byte grid (ragged H, x and the modulation at element
     offsets; scale and shift as column slices of one modulation tensor, per
     batch as [B, 1, H] views): the tile depends on H only, so every layout
     gives the same bits, at parity with the oracle, and nothing around the
-    output rows is written.  16385 and 40001 are longer than any resident
-    tile and take two passes."""
+    output rows is written.  16-bit rows with 16-bit parameters stay in
+    registers to 32767 columns; 16385 and 32767 with float32 parameters, and
+    40001 everywhere, take two passes."""
     B, S = 3, 11
     M = B * S
     C = B if per_batch else M

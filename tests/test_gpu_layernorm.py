@@ -66,8 +66,9 @@ def test_workload_ln_residual():
     check(d["x"], d["r"], d["w"], d["b"], d["eps"], d["dtype"], d["wdtype"], name=name, record=name)
 
 
-# 12288 and 16384 (16-bit) and 8192 (float32) take tiles capped at 4 waves per row
-LN_H = [1, 3, 8, 64, 65, 512, 1000, 1024, 2049, 4096, 8191, 8192, 12288, 16384, 16385, 65536]
+# 12288 and 16384 (16-bit) and 8192 (float32) take tiles capped at 4 waves per
+# row; 24576 is the longest 16-bit row held in registers
+LN_H = [1, 3, 8, 64, 65, 512, 1000, 1024, 2049, 4096, 8191, 8192, 12288, 16384, 16385, 24576, 24577, 65536]
 
 
 @pytest.mark.parametrize("resid", [True, False], ids=["residual", "plain"])
@@ -181,14 +182,16 @@ def test_ln_misaligned_and_strided_rows(dtype):
 
 
 @pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
-@pytest.mark.parametrize("H", [600, 2049, 4096, 6143, 16385, 70001])
+@pytest.mark.parametrize("H", [600, 2049, 4096, 6143, 16385, 24577, 70001])
 def test_ln_rows_off_the_grid(dtype, wdtype, H):
     """Rows off the 16-byte grid (ragged H, or views at element offsets)
     are read and written in 16-byte vectors at each row's byte offset, on a
     tile that depends on H only: every layout gives the same bits, at parity
     with the oracle, and nothing around the output rows is written; the
-    forced element-wise tile is at parity too.  16385 and 70001 are longer
-    than any resident tile and take the passes over the row."""
+    forced element-wise tile is at parity too.  16-bit rows with 16-bit
+    parameters stay in registers to 24575 columns; 16385 in float32 or with
+    float32 parameters, and 24577 and 70001 everywhere, take the passes over
+    the row."""
     M = 67 if H <= 8192 else 9
     d = G.inputs(5100 + H, M, H, dtype, wdtype=wdtype, residual=True)
     b = bias_of(5100 + H, H, wdtype)

@@ -148,10 +148,12 @@ def test_workload_bwd_chained_with_gpu_rrms():
 # shapes: ragged, tiny and long rows, every format
 # ---------------------------------------------------------------------------
 
-# 16384 takes a tile capped below 16 waves per row (16-bit: 3 x 11 plain,
-# 4 x 8 residual; float32: 6 x 11), and so does 8192 in float32 (3 x 11)
+# 16384 takes a tile capped below 16 waves per row (3 x 11 in 16 bits, 6 x 11
+# for the plain float32 forward), and so does 8192 in float32 (3 x 11);
+# 32768 and 65536 (32767 and 65535 off the grid) are the longest 16-bit rows
+# the fused residual and the plain forward hold in registers
 EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 3072, 4097, 5120, 6144, 8191, 8192, 12288,
-          16384, 16385, 32768, 65536]
+          16384, 16385, 32767, 32768, 65535, 65536]
 
 
 def _rows_for(H):
@@ -357,13 +359,15 @@ def test_misaligned_views_same_bits_at_any_offset(dtype):
 
 
 @pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32"), ("bf16", "f32")])
-@pytest.mark.parametrize("H", [5, 13, 63, 129, 1001, 4097, 6143, 8190, 12289, 16385, 30001, 70001])
+@pytest.mark.parametrize("H", [5, 13, 63, 129, 1001, 4097, 6143, 8190, 12289, 16385, 30001, 32769, 70001])
 def test_ragged_rows_parity_and_pads(dtype, wdtype, H):
     """Ragged H (rows off the 16-byte grid by their length) in padded
     layouts: parity with the oracle for the plain and fused residual forward,
     and the pads between output rows never written; the forced element-wise
-    tile gives results at parity too.  The fused residual takes two passes
-    from 16385, the plain forward at 70001."""
+    tile gives results at parity too.  16-bit rows with a 16-bit weight stay
+    in registers to 32767 columns (fused residual) and 65535 (plain); in
+    float32 or with a float32 weight the fused residual takes two passes from
+    16385 and the plain forward from 32769."""
     M = 41 if H <= 8192 else 9
     d = G.inputs(67 + H, M, H, dtype, wdtype=wdtype, residual=True)
     wd = G.to_dev(d["w"], wdtype)

@@ -128,14 +128,27 @@ def test_tile_query_aligned_rows():
 @pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16385), ("bwd", "f32", 16385), ("bwd", "bf16", 70001),
                                      ("bwd_residual", "bf16", 16385), ("bwd_residual", "f16", 20001),
                                      ("bwd_residual", "f32", 8193), ("fwd", "bf16", 70001),
-                                     ("fwd_residual", "bf16", 16385), ("fwd_residual", "f32", 30001),
-                                     ("adaln", "bf16", 16385), ("layernorm", "bf16", 16385),
+                                     ("fwd_residual", "bf16", 32769), ("fwd_residual", "f32", 30001),
+                                     ("adaln", "bf16", 32769), ("layernorm", "bf16", 24577),
                                      ("layernorm", "f32", 70001)])
 def test_long_rows_off_the_grid_take_vectors(op, dt, H):
     # rows longer than one tile: passes over the row in 16-byte vectors at
     # each row's byte offset, not single elements
     t = tn.tile(op, H, dt, off_grid=True)
     assert t["multi_pass"] and t["mis"] and t["vec"] == 16 // ES[dt]
+
+
+# the forward family's longest rows held in registers: 16-bit rows whose
+# parameters are 16-bit too take twice the elements per thread of float32 rows
+# at the same workgroup size
+@pytest.mark.parametrize("op,limit16,limit32", [("fwd", 65536, 32768), ("fwd_residual", 32768, 16384),
+                                                ("adaln", 32768, 16384), ("layernorm", 24576, 16384)])
+def test_longest_one_pass_forward_rows(op, limit16, limit32):
+    for dt, limit in (("bf16", limit16), ("f16", limit16), ("f32", limit32)):
+        assert not tn.tile(op, limit, dt, off_grid=False)["multi_pass"], (dt, limit)
+        assert not tn.tile(op, limit - 1, dt, off_grid=True)["multi_pass"], (dt, limit - 1)
+        assert tn.tile(op, limit + 16 // ES[dt], dt, off_grid=False)["multi_pass"], (dt, limit)
+        assert tn.tile(op, limit + 1, dt, off_grid=True)["multi_pass"], (dt, limit + 1)
 
 
 @pytest.mark.parametrize("op,dt,H", [("bwd", "bf16", 16383), ("bwd", "f32", 16383), ("bwd_residual", "bf16", 16383),

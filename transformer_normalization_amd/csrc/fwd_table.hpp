@@ -11,21 +11,23 @@ namespace tables {
 
 template <int XDT, int WDT, int VEC, int MODE, bool NT>
 fwd_fn fwd_kernel_for(int vpt, bool two_pass) {
+    // 2: x and its parameters are all 16-bit (the register budget)
+    constexpr int ES2 = Fmt<XDT>::bytes == 2 && Fmt<WDT>::bytes == 2 ? 2 : 4;
     if (two_pass) {
         constexpr int V = VEC > 1 ? 4 : 8;
         return rmsnorm_fwd_kernel<XDT, WDT, VEC, V, MODE, true, NT, 1024>;
     }
     switch (vpt) {
-    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, MODE, false, NT, fwd_max_threads(1 * VEC, MODE)>;
-    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, MODE, false, NT, fwd_max_threads(2 * VEC, MODE)>;
-    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, MODE, false, NT, fwd_max_threads(4 * VEC, MODE)>;
-    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, MODE, false, NT, fwd_max_threads(8 * VEC, MODE)>;
+    case 1: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 1, MODE, false, NT, fwd_max_threads(1 * VEC, MODE, ES2)>;
+    case 2: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 2, MODE, false, NT, fwd_max_threads(2 * VEC, MODE, ES2)>;
+    case 4: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 4, MODE, false, NT, fwd_max_threads(4 * VEC, MODE, ES2)>;
+    case 8: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 8, MODE, false, NT, fwd_max_threads(8 * VEC, MODE, ES2)>;
     default: break;
     }
     if constexpr (VEC > 1) {
         switch (vpt) {
-        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, MODE, false, NT, fwd_max_threads(3 * VEC, MODE)>;
-        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, MODE, false, NT, fwd_max_threads(6 * VEC, MODE)>;
+        case 3: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 3, MODE, false, NT, fwd_max_threads(3 * VEC, MODE, ES2)>;
+        case 6: return rmsnorm_fwd_kernel<XDT, WDT, VEC, 6, MODE, false, NT, fwd_max_threads(6 * VEC, MODE, ES2)>;
         default: break;
         }
     }

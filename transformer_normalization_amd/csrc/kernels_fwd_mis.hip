@@ -8,15 +8,17 @@ namespace {
 
 template <int XDT, int WDT, int MODE, bool NT>
 fwd_fn mis_kernel(int vpt, bool tp) {
+    // 2: x and its parameters are all 16-bit (the register budget)
+    constexpr int ES2 = Fmt<XDT>::bytes == 2 && Fmt<WDT>::bytes == 2 ? 2 : 4;
     constexpr int V = 16 / Fmt<XDT>::bytes;
     if (tp) return vpt == 4 ? rmsnorm_fwd_kernel<XDT, WDT, V, 4, MODE, true, NT, 1024, true> : nullptr;
     switch (vpt) {
-    case 1: return rmsnorm_fwd_kernel<XDT, WDT, V, 1, MODE, false, NT, fwd_max_threads(1 * V, MODE), true>;
-    case 2: return rmsnorm_fwd_kernel<XDT, WDT, V, 2, MODE, false, NT, fwd_max_threads(2 * V, MODE), true>;
-    case 3: return rmsnorm_fwd_kernel<XDT, WDT, V, 3, MODE, false, NT, fwd_max_threads(3 * V, MODE), true>;
-    case 4: return rmsnorm_fwd_kernel<XDT, WDT, V, 4, MODE, false, NT, fwd_max_threads(4 * V, MODE), true>;
-    case 6: return rmsnorm_fwd_kernel<XDT, WDT, V, 6, MODE, false, NT, fwd_max_threads(6 * V, MODE), true>;
-    case 8: return rmsnorm_fwd_kernel<XDT, WDT, V, 8, MODE, false, NT, fwd_max_threads(8 * V, MODE), true>;
+    case 1: return rmsnorm_fwd_kernel<XDT, WDT, V, 1, MODE, false, NT, fwd_max_threads(1 * V, MODE, ES2), true>;
+    case 2: return rmsnorm_fwd_kernel<XDT, WDT, V, 2, MODE, false, NT, fwd_max_threads(2 * V, MODE, ES2), true>;
+    case 3: return rmsnorm_fwd_kernel<XDT, WDT, V, 3, MODE, false, NT, fwd_max_threads(3 * V, MODE, ES2), true>;
+    case 4: return rmsnorm_fwd_kernel<XDT, WDT, V, 4, MODE, false, NT, fwd_max_threads(4 * V, MODE, ES2), true>;
+    case 6: return rmsnorm_fwd_kernel<XDT, WDT, V, 6, MODE, false, NT, fwd_max_threads(6 * V, MODE, ES2), true>;
+    case 8: return rmsnorm_fwd_kernel<XDT, WDT, V, 8, MODE, false, NT, fwd_max_threads(8 * V, MODE, ES2), true>;
     default: break;
     }
     return nullptr;

@@ -8,21 +8,23 @@ namespace {
 
 template <int XDT, int WDT, int VEC, bool RES, bool NT>
 ln_fn ln_kernel_for(int vpt, bool two_pass) {
+    // 2: x and its parameters are all 16-bit (the register budget)
+    constexpr int ES2 = Fmt<XDT>::bytes == 2 && Fmt<WDT>::bytes == 2 ? 2 : 4;
     if (two_pass) {
         constexpr int V = VEC > 1 ? 4 : 8;
         return layernorm_fwd_kernel<XDT, WDT, VEC, V, RES, true, NT, 1024>;
     }
     switch (vpt) {
-    case 1: return layernorm_fwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, ln_max_threads(1 * VEC)>;
-    case 2: return layernorm_fwd_kernel<XDT, WDT, VEC, 2, RES, false, NT, ln_max_threads(2 * VEC)>;
-    case 4: return layernorm_fwd_kernel<XDT, WDT, VEC, 4, RES, false, NT, ln_max_threads(4 * VEC)>;
-    case 8: return layernorm_fwd_kernel<XDT, WDT, VEC, 8, RES, false, NT, ln_max_threads(8 * VEC)>;
+    case 1: return layernorm_fwd_kernel<XDT, WDT, VEC, 1, RES, false, NT, ln_max_threads(1 * VEC, ES2)>;
+    case 2: return layernorm_fwd_kernel<XDT, WDT, VEC, 2, RES, false, NT, ln_max_threads(2 * VEC, ES2)>;
+    case 4: return layernorm_fwd_kernel<XDT, WDT, VEC, 4, RES, false, NT, ln_max_threads(4 * VEC, ES2)>;
+    case 8: return layernorm_fwd_kernel<XDT, WDT, VEC, 8, RES, false, NT, ln_max_threads(8 * VEC, ES2)>;
     default: break;
     }
     if constexpr (VEC > 1) {
         switch (vpt) {
-        case 3: return layernorm_fwd_kernel<XDT, WDT, VEC, 3, RES, false, NT, ln_max_threads(3 * VEC)>;
-        case 6: return layernorm_fwd_kernel<XDT, WDT, VEC, 6, RES, false, NT, ln_max_threads(6 * VEC)>;
+        case 3: return layernorm_fwd_kernel<XDT, WDT, VEC, 3, RES, false, NT, ln_max_threads(3 * VEC, ES2)>;
+        case 6: return layernorm_fwd_kernel<XDT, WDT, VEC, 6, RES, false, NT, ln_max_threads(6 * VEC, ES2)>;
         default: break;
         }
     }

@@ -9,15 +9,17 @@ namespace {
 
 template <int XDT, int WDT, bool RES, bool NT>
 ln_fn mis_kernel(int vpt, bool tp) {
+    // 2: x and its parameters are all 16-bit (the register budget)
+    constexpr int ES2 = Fmt<XDT>::bytes == 2 && Fmt<WDT>::bytes == 2 ? 2 : 4;
     constexpr int V = 16 / Fmt<XDT>::bytes;
     if (tp) return vpt == 4 ? layernorm_fwd_kernel<XDT, WDT, V, 4, RES, true, NT, 1024, true> : nullptr;
     switch (vpt) {
-    case 1: return layernorm_fwd_kernel<XDT, WDT, V, 1, RES, false, NT, ln_max_threads(1 * V), true>;
-    case 2: return layernorm_fwd_kernel<XDT, WDT, V, 2, RES, false, NT, ln_max_threads(2 * V), true>;
-    case 3: return layernorm_fwd_kernel<XDT, WDT, V, 3, RES, false, NT, ln_max_threads(3 * V), true>;
-    case 4: return layernorm_fwd_kernel<XDT, WDT, V, 4, RES, false, NT, ln_max_threads(4 * V), true>;
-    case 6: return layernorm_fwd_kernel<XDT, WDT, V, 6, RES, false, NT, ln_max_threads(6 * V), true>;
-    case 8: return layernorm_fwd_kernel<XDT, WDT, V, 8, RES, false, NT, ln_max_threads(8 * V), true>;
+    case 1: return layernorm_fwd_kernel<XDT, WDT, V, 1, RES, false, NT, ln_max_threads(1 * V, ES2), true>;
+    case 2: return layernorm_fwd_kernel<XDT, WDT, V, 2, RES, false, NT, ln_max_threads(2 * V, ES2), true>;
+    case 3: return layernorm_fwd_kernel<XDT, WDT, V, 3, RES, false, NT, ln_max_threads(3 * V, ES2), true>;
+    case 4: return layernorm_fwd_kernel<XDT, WDT, V, 4, RES, false, NT, ln_max_threads(4 * V, ES2), true>;
+    case 6: return layernorm_fwd_kernel<XDT, WDT, V, 6, RES, false, NT, ln_max_threads(6 * V, ES2), true>;
+    case 8: return layernorm_fwd_kernel<XDT, WDT, V, 8, RES, false, NT, ln_max_threads(8 * V, ES2), true>;
     default: break;
     }
     return nullptr;

@@ -323,12 +323,19 @@ __device__ __forceinline__ float fast_rsqrt(float v) { return __builtin_amdgcn_r
 // waves of a SIMD) to hold the tile without spilling.  The host geometry uses
 // the same functions.  The forward keeps x (and the residual) packed; the
 // backward keeps x, dy and w packed plus float32 dw partial sums.
-constexpr int fwd_max_threads(int elems, int mode) {  // mode: 0 plain, 1 residual, 2 AdaLN
-    return mode == 0 ? (elems <= 32 ? 1024 : 512)
-                     : (elems <= 16 ? 1024 : elems <= 32 ? 512 : 256);
+// es = 2 when x and its parameters (weight, AdaLN's scale and shift, LayerNorm's
+// bias) are all 16-bit: then the plain forward's tiles of 48 and 64 elements
+// (91-121 VGPRs), the fused residual's and AdaLN's of 24 and 32 (95-124) and
+// LayerNorm's of 24 (69-108) fit 1024 threads, so longer rows stay resident
+// (a float32 parameter adds 4 VGPRs per vector, and those tiles would spill).
+constexpr int fwd_max_threads(int elems, int mode, int es = 4) {  // mode: 0 plain, 1 residual, 2 AdaLN
+    return mode == 0 ? (elems <= 32 || (es == 2 && elems <= 64) ? 1024 : 512)
+                     : (elems <= 16 || (es == 2 && elems <= 32) ? 1024 : elems <= 32 ? 512 : 256);
 }
 // LayerNorm keeps x (and the residual) packed plus packed weight and bias
-constexpr int ln_max_threads(int elems) { return elems <= 16 ? 1024 : elems <= 32 ? 512 : 256; }
+constexpr int ln_max_threads(int elems, int es = 4) {
+    return elems <= 16 || (es == 2 && elems <= 24) ? 1024 : elems <= 32 ? 512 : 256;
+}
 // (res: the residual backward holds a third row tile, dres, in registers;
 // es: bytes per element of x.  16-bit residual tiles of 16 elements, two
 // 16-byte vectors per row stream, take 111-128 VGPRs and fit 1024 threads;

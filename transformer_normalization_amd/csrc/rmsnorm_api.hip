@@ -60,14 +60,17 @@ enum class Kind { Fwd, FwdResid, FwdAdaln, Ln, Bwd, BwdRes };
 constexpr int kFwdVecVpt[] = {1, 2, 3, 4, 6, 8};
 constexpr int kBwdVecVpt[] = {1, 2, 3, 4};
 constexpr int kScalarVpt[] = {1, 2, 4, 8};
-// largest workgroup each register tile may use (the kernels' launch bounds)
-int max_threads_for(Kind kind, int vpt, int vec) {
+// largest workgroup each register tile may use (the kernels' launch bounds);
+// pb: bytes per element of the forward family's parameters (weight, AdaLN's
+// rows, LayerNorm's bias; x's format when there are none)
+int max_threads_for(Kind kind, int vpt, int vec, int pb = 4) {
+    const int es2 = vec == 8 && pb == 2 ? 2 : 4;  // x and its parameters all 16-bit
     return kind == Kind::Bwd        ? bwd_max_threads(vpt * vec)
            : kind == Kind::BwdRes   ? bwd_max_threads(vpt * vec, true, vec == 8 ? 2 : 4)
-           : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID)
-           : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN)
-           : kind == Kind::Ln       ? ln_max_threads(vpt * vec)
-                                    : fwd_max_threads(vpt * vec, MODE_PLAIN);
+           : kind == Kind::FwdResid ? fwd_max_threads(vpt * vec, MODE_RESID, es2)
+           : kind == Kind::FwdAdaln ? fwd_max_threads(vpt * vec, MODE_ADALN, es2)
+           : kind == Kind::Ln       ? ln_max_threads(vpt * vec, es2)
+                                    : fwd_max_threads(vpt * vec, MODE_PLAIN, es2);
 }
 
 struct Geom {
@@ -83,7 +86,7 @@ struct Geom {
 // Pick (vpt, wpr) so that 64*wpr*vpt covers nvec with the least idle slots,
 // preferring `pref` elements per thread; rows longer than the largest tile
 // use two passes.
-Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
+Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems, int pb = 4) {
     Geom g{};
     g.vec = vec;
     g.nvec = (H + vec - 1) / vec;
@@ -98,17 +101,23 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
     // at H = 16384, while at H <= 8192 its tiles were within 1 %).  A
     // penalty, not a limit: with no tile under the cap the row stays
     // resident on the best tile over it.
+    // AdaLN tiles of more than 16 elements per thread (104-124 VGPRs, four
+    // waves per SIMD) count as over the cap beyond 8 waves: one such
+    // workgroup per CU then leaves SIMDs idle (bf16, 2048 rows: H = 16384 on
+    // 3 x 11 waves 74.5 % against 82.8 % on 4 x 8, H = 12296 on 3 x 9 66.1 %
+    // against 76.9 % on 4 x 7).
     const int wcap = kind == Kind::Ln ? (g.nvec > 1024 ? 4 : 16) : bwd ? 16 : 12;
     double best = 1e30;
     for (int i = 0; i < nset; ++i) {
         const int vpt = set[i];
-        const int maxw = max_threads_for(kind, vpt, vec) / 64;
+        const int maxw = max_threads_for(kind, vpt, vec, pb) / 64;
         const int wpr = (g.nvec + 64 * vpt - 1) / (64 * vpt);
         if (wpr > maxw) continue;
         const double slots = 64.0 * wpr * vpt;
         const double idle = (slots - g.nvec) / slots;
         const double pref = std::fabs(std::log2((double)(vpt * vec) / pref_elems));
-        const double cost = 8.0 * idle + pref + (wpr > wcap ? 4.0 : 0.0);
+        const int cap = kind == Kind::FwdAdaln && vpt * vec > 16 ? 8 : wcap;
+        const double cost = 8.0 * idle + pref + (wpr > cap ? 4.0 : 0.0);
         if (cost < best) {
             best = cost;
             g.vpt = vpt;
@@ -126,7 +135,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
         g.two_pass = true;
     }
     g.rpw = 1;
-    while (g.rpw * g.wpr < 4 && 64 * g.wpr * g.rpw * 2 <= max_threads_for(kind, g.vpt, g.vec)) g.rpw *= 2;
+    while (g.rpw * g.wpr < 4 && 64 * g.wpr * g.rpw * 2 <= max_threads_for(kind, g.vpt, g.vec, pb)) g.rpw *= 2;
     return g;
 }
 
@@ -141,7 +150,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems) {
 // rule, 58.5 % staged), H = 4097 63.7 % (61.3 % staged; one row per
 // workgroup: 60.1 %), H = 6143 64.5 % (58.7 % staged), fused residual
 // H = 6143 68.7 % (58.4 % staged).
-Geom pick_offgrid_geom(Kind kind, int H, int vec) {
+Geom pick_offgrid_geom(Kind kind, int H, int vec, int pb) {
     static const int kOffgridVpt[] = {1, 2, 3, 4, 6};
     Geom g{};
     g.vec = vec;
@@ -149,7 +158,7 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
     double best = 1e30;
     for (int vpt : kOffgridVpt) {
         const int wpr = (g.nvec + 64 * vpt - 1) / (64 * vpt);
-        if (wpr > max_threads_for(kind, vpt, vec) / 64) continue;
+        if (wpr > max_threads_for(kind, vpt, vec, pb) / 64) continue;
         const double slots = 64.0 * wpr * vpt;
         const double cost = wpr + 8.0 * (slots - g.nvec) / slots;
         if (cost < best) {
@@ -160,7 +169,7 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
     }
     g.two_pass = best >= 1e30;
     g.nchunks = 1;
-    g.rpw = g.wpr <= 3 && 64 * g.wpr * 2 <= max_threads_for(kind, g.vpt, vec) ? 2 : 1;
+    g.rpw = g.wpr <= 3 && 64 * g.wpr * 2 <= max_threads_for(kind, g.vpt, vec, pb) ? 2 : 1;
     return g;
 }
 
@@ -183,7 +192,7 @@ Geom pick_offgrid_geom(Kind kind, int H, int vec) {
 //   up to 192 vectors keep them too: at H = 1023 and 1025 the plain forward
 //   lost 3.6 and 4.4 points and LayerNorm 7.9 to one-wave rows (the fused
 //   residual, AdaLN and residual LayerNorm gained 1.6 to 2.7).
-Geom pick_two_wave_geom(Kind kind, int H, int vec) {
+Geom pick_two_wave_geom(Kind kind, int H, int vec, int pb) {
     static const int kVpt[] = {1, 2, 3, 4, 6};
     Geom g{};
     g.vec = vec;
@@ -191,7 +200,7 @@ Geom pick_two_wave_geom(Kind kind, int H, int vec) {
     if (g.nvec <= 192) return g;
     int best = 0;
     for (int vpt : kVpt) {
-        if (128 * vpt < g.nvec || max_threads_for(kind, vpt, vec) < 128) continue;
+        if (128 * vpt < g.nvec || max_threads_for(kind, vpt, vec, pb) < 128) continue;
         if (best == 0) best = vpt;  // the smallest vpt that holds the row idles the fewest slots
     }
     if (best == 0) return g;
@@ -199,7 +208,7 @@ Geom pick_two_wave_geom(Kind kind, int H, int vec) {
     g.wpr = 2;
     g.nchunks = 1;
     g.two_pass = false;
-    g.rpw = 64 * 2 * 2 <= max_threads_for(kind, best, vec) ? 2 : 1;
+    g.rpw = 64 * 2 * 2 <= max_threads_for(kind, best, vec, pb) ? 2 : 1;
     return g;
 }
 
@@ -222,20 +231,20 @@ Geom pick_two_wave_geom(Kind kind, int H, int vec) {
 // 0.1 %; float32 H = 4097 the same, fused residual H = 1025 66.1 % against
 // 68.3 %, so float32 keeps the aligned rule.  Otherwise the element-wise
 // tile.
-Geom fwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis) {
+Geom fwd_tile(Kind kind, int H, int eb, int pb, bool vec_ok, bool mis_ok, bool *mis) {
     const int vecw = 16 / eb;
     const bool offrule = kind == Kind::Fwd || kind == Kind::FwdResid || (kind == Kind::Ln && eb == 2);
     *mis = false;
     if (!vec_ok && mis_ok && (int64_t)H * eb >= 512) {
         Geom m{};
         if (eb == 2 && (offrule || kind == Kind::FwdAdaln) && (int64_t)H * eb >= 1024)
-            m = pick_two_wave_geom(kind, H, vecw);
-        if (m.vpt == 0 && offrule && (int64_t)H * eb >= 1024) m = pick_offgrid_geom(kind, H, vecw);
-        if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16);
+            m = pick_two_wave_geom(kind, H, vecw, pb);
+        if (m.vpt == 0 && offrule && (int64_t)H * eb >= 1024) m = pick_offgrid_geom(kind, H, vecw, pb);
+        if (m.vpt == 0 || m.two_pass) m = pick_row_geom(kind, H, vecw, eb == 4 ? 8 : 16, pb);
         *mis = true;
         return m;
     }
-    return pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16);
+    return pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16, pb);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +345,9 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
                         (!resid || (aligned_to(r, eb) && (ro == nullptr || aligned_to(ro, eb)))) &&
                         (!adaln || (aligned_to(cond.scale, pb) && aligned_to(cond.shift, pb)));
     bool mis = false;
-    Geom g = fwd_tile(kind, (int)H, eb, vec_ok, mis_ok, &mis);
+    // the parameters' format as the kernels see it (x's when there are none)
+    const int kpb = dtype_bytes((w || adaln || bias) ? wdt : xdt);
+    Geom g = fwd_tile(kind, (int)H, eb, kpb, vec_ok, mis_ok, &mis);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     if (ov.set) {
         // bounds first: the products below are then small
@@ -347,7 +358,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         o.vpt = ov.a;
         o.wpr = ov.b;
         o.rpw = ov.c > 0 ? ov.c : 1;
-        const int maxt = max_threads_for(kind, o.vpt, o.vec);
+        const int maxt = max_threads_for(kind, o.vpt, o.vec, kpb);
         if (o.vpt < 1 || o.wpr < 1 || o.wpr * o.rpw * 64 > maxt || o.wpr * o.rpw > 16)
             return fail(RMSN_ERR_INVALID_ARG,
                         "forced forward geometry: bad tile vpt %d wpr %d rpw %d (max %d threads)", o.vpt, o.wpr,
@@ -876,7 +887,7 @@ RMSN_API rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dty
     bool mis = false;
     int elem_groups = 0;
     const Geom g = op >= 4 ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
-                           : fwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis);
+                           : fwd_tile(kind, (int)H, eb, eb, vec_ok, !vec_ok, &mis);
     out[0] = g.vec;
     out[1] = g.two_pass ? 0 : g.vpt;
     out[2] = g.two_pass ? 0 : g.wpr;

@@ -174,3 +174,17 @@ def test_two_waves_per_row_for_16bit_rows_of_193_to_768_vectors(op, dt):
 def test_float32_rows_keep_their_rules():
     assert tn.tile("fwd", 2049, "f32", off_grid=True)["wpr"] == 3
     assert tn.tile("fwd", 4097, "f32", off_grid=True)["wpr"] == 3
+
+
+def test_adaln_keeps_two_workgroups_per_cu_on_its_large_tiles():
+    # AdaLN tiles of more than 16 elements per thread hold a CU at four waves
+    # per SIMD, so past 8 waves a workgroup would run alone on its CU: rows
+    # that a tile of at most 8 waves covers take it, where the fused residual
+    # takes the tile with the preferred element count
+    for H, tile in ((12296, (4, 7)), (16384, (4, 8))):
+        t = tn.tile("adaln", H, "bf16", off_grid=False)
+        assert (t["vpt"], t["wpr"]) == tile, (H, t)
+    assert (lambda t: (t["vpt"], t["wpr"]))(tn.tile("fwd_residual", 16384, "bf16", off_grid=False)) == (3, 11)
+    # rows no 8-wave tile covers stay resident on the best tile over the cap
+    t = tn.tile("adaln", 24576, "bf16", off_grid=False)
+    assert not t["multi_pass"] and t["wpr"] > 8

@@ -283,3 +283,27 @@ def test_ln_guard_regions_untouched():
     torch.cuda.synchronize()
     for t in (yb, rb):
         assert torch.all(t[:64] == 7.0) and torch.all(t[64 + n:] == 7.0)
+
+
+@pytest.mark.parametrize("dtype,H,M", [("bf16", 4096, 8195), ("f32", 4096, 8195), ("bf16", 4097, 16389)])
+def test_ln_rows_walked_in_pairs(dtype, H, M):
+    """LayerNorm without the residual whose weight and bias take 16 KiB or
+    more, on at least 32 row groups per CU, has each row group walk 2 rows
+    (an odd number of row groups leaves the last workgroup one row): parity
+    with the oracle over the whole call and, on the 16-byte grid, the same
+    bits as the same tile on one row per row group (a forced geometry never
+    walks)."""
+    print(f"[gpu] ln walked {dtype} M={M} H={H}", flush=True)
+    d = G.inputs(6100 + H, M, H, dtype)
+    b = bias_of(6100 + H, H, dtype)
+    y, _, mean, rstd = run_ln(d["x"], None, d["w"], b, 1e-5, dtype)
+    G.assert_ok(*G.ln_vs_oracle(d["x"], None, d["w"], b, y, None, mean, rstd, 1e-5, dtype,
+                                name=f"ln walked {dtype} H={H}"))
+    if H % 8 == 0:
+        t = tn.tile("layernorm", H, dtype, off_grid=False)
+        tn.set_geometry("fwd", t["vpt"], t["wpr"], t["rpw"], 0)
+        try:
+            y1, _, mean1, rstd1 = run_ln(d["x"], None, d["w"], b, 1e-5, dtype)
+        finally:
+            tn.set_geometry("fwd")
+        assert np.array_equal(y, y1) and np.array_equal(mean, mean1) and np.array_equal(rstd, rstd1)

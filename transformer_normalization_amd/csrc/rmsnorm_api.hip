@@ -375,7 +375,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     }
     const int64_t groups = (M + g.rpw - 1) / g.rpw;
     if (grid > INT32_MAX) grid = INT32_MAX;
-    const int64_t iters = (groups + grid - 1) / grid;
+    int64_t iters = (groups + grid - 1) / grid;
 
     const int64_t streamed = (resid ? (ro ? 4 : 3) : 2) * M * H * eb;
     const bool nt = use_streaming(streamed);
@@ -386,6 +386,24 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
                        : ln_lookup(xdt, kwdt, g.vec, g.vpt, g.two_pass, nt, resid);
         if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
         if ((st = device_info(&cus)) != RMSN_OK) return st;
+        // LayerNorm (no residual) whose weight and bias take 16 KiB or more
+        // between them: each row group walks 2 rows, so that the parameters
+        // it holds in registers serve both.  Every row's workgroup otherwise
+        // fetches them from L2 again (they miss the CU's L1).  Measured on
+        // gfx950, the same tiles and bits (one row per row group in
+        // brackets): bf16 8192 x 4096 64.5 % (62.5 %), 8192 x 6144 66.2 %
+        // (60.2 %), 8192 x 8192 70.0 % (66.0 %), 16384 x 4096 72.0 % (68.1 %),
+        // off the grid 8192 x 4097 55.3 % (53.6 %); float32 8192 x 4096
+        // 71.4 % (65.5 %), 16384 x 2048 72.6 % (69.3 %).  Only from 32 row
+        // groups per CU: with half the workgroups, smaller calls pay a
+        // partial last round of resident workgroups (bf16 4096 x 4096 53.6 %
+        // against 56.6 %).  The residual form, with twice the row streams,
+        // and RMSNorm's one weight row lost or gained nothing.
+        if (!resid && w != nullptr && bias != nullptr && !ov.set && !g.two_pass && 2 * H * kpb >= 16384 &&
+            groups >= 32LL * cus) {
+            grid = (groups + 1) / 2;
+            iters = (groups + grid - 1) / grid;
+        }
         LnParams p;
         p.x = x;
         p.r = r;

@@ -311,3 +311,21 @@ def test_autograd_rope_gradient_is_transposed_rotation():
     cg = cd.clone().requires_grad_(True)
     with pytest.raises(NotImplementedError):
         ag.rope_3d(G.to_dev(x_h, "bf16"), cg, sd).float().sum().backward()
+
+
+@pytest.mark.parametrize("shape,dtype,tdtype", [((1, 300, 32, 128), "bf16", "bf16"), ((1, 77, 8, 256), "f32", "f32"),
+                                                ((1, 129, 64, 128), "f16", "f32"), ((1, 45, 16, 64), "f32", "f32")],
+                         ids=["bf16_32x128", "f32_8x256", "f16_64x128", "f32_16x64"])
+def test_batch_one_split_layout(shape, dtype, tdtype):
+    """One batch whose half-heads are whole 128-byte lines and whose
+    per-position vectors fill 256-thread workgroups takes the split layout:
+    parity with the oracle, and the same bits as the lane exchange the same
+    rows take as the first batch of a two-batch call."""
+    B, S, NH, D = shape
+    x = rand_x(41, shape, dtype)
+    c, s = tables(41, S, D, tdtype)
+    got = run(x, c, s, dtype, tdtype)
+    G.assert_ok(rope_vs_oracle(x, c, s, got, dtype, tdtype, name=f"rope batch one {shape}"))
+    x2 = np.concatenate([x, rand_x(42, shape, dtype)])
+    both = run(x2, c, s, dtype, tdtype)
+    assert np.array_equal(both[:1], got)

@@ -80,6 +80,19 @@ rmsn_status_t rope_impl(const void *x, int64_t xrs, int64_t xhs, const void *cos
     // power-of-two group of lanes (padding lanes idle), so heads never
     // straddle waves
     bool xchg = vec > 1 && nvec <= 32;
+    // One batch, half-heads of whole 128-byte lines, and a position's vectors
+    // filling 256-thread workgroups exactly: the split layout, whose threads
+    // then read two whole lines each, none idle.  Measured on gfx950 (split
+    // against exchange, same bits): [1, 8192, 32, 128] bf16 68.9 % (63.9 %),
+    // float32 78.2 % (71.1 %), f16 with float32 tables 68.3 % (66.0 %);
+    // [1, 8192, 64, 128] bf16 74.8 % (69.4 %); [1, 8192, 32, 256] 75.0 %
+    // (70.1 %); [1, 8192, 32, 64] float32 72.4 % (67.3 %); 8 and 16 heads
+    // level or +1.3.  Not taken: two or more batches (split -3 to -12),
+    // 64-byte half-heads ([1, 8192, 32, 64] bf16 -4.3), 40 heads of 128
+    // (320 vectors a position, -7).
+    const int64_t pos_vecs = NH * nvec;
+    if (xchg && B == 1 && half * eb >= 128 && (pos_vecs % kRopeThreads == 0 || kRopeThreads % pos_vecs == 0))
+        xchg = false;
     int group = 1;
     while (group < 2 * nvec) group *= 2;
     const Override ov = get_override(2);

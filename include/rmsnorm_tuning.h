@@ -46,13 +46,19 @@ void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t
  * Host only (touches no device): the tile a call takes with no forced
  * geometry.  op: 0 RMSNorm forward, 1 fused residual, 2 AdaLN, 3 LayerNorm,
  * 4 backward, 5 residual backward.  layout 0: every row start 16-byte
- * aligned; 1: row starts only element-aligned (parameters 16-byte aligned).
+ * aligned; 1: row starts only element-aligned (parameters 16-byte aligned);
+ * 2: as 1, with every row stream of the call (x, dy, dres, dx) at one shared
+ * offset within its 16-byte chunks, the same for every row a backward
+ * workgroup owns (the backward then sets its vectors on memory's 16-byte
+ * grid; the forward ops take layout 1's tile).
  * The parameters (weight, AdaLN's rows, LayerNorm's bias) are taken in x's
  * format; a float32 weight on 16-bit data can give another tile (a smaller
  * register budget).  Writes out[0] elements per access, out[1] accesses per thread, out[2] waves
  * per row, out[3] rows per workgroup, out[4] 1 when rows off the 16-byte grid
- * take 16-byte vectors at each row's byte offset (0: single elements or rows
- * on the grid), out[5] 1 when the row takes the multi-pass path (out[1] and
+ * take 16-byte vectors at each row's byte offset, 2 when a backward takes
+ * them on memory's 16-byte grid (layout 2, one pass; the tile then covers the
+ * one more vector such a row may touch), 0 for single elements or rows on
+ * the grid, out[5] 1 when the row takes the multi-pass path (out[1] and
  * out[2] are then 0).  RMSN_ERR_INVALID_ARG for a bad op, layout, H or a NULL
  * out; RMSN_ERR_UNSUPPORTED for an unknown format or H > 2^30.
  */

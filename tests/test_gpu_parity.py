@@ -700,6 +700,77 @@ def test_bwd_rows_off_the_grid_views_and_pads(dtype, wdtype, H):
                                      wdtype=wdtype, name=f"bwd element tile {dtype} H={H}"))
 
 
+@pytest.mark.parametrize("dtype,wdtype", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("H,M,off,pad", [(4097, 300, 1, 0), (4095, 41, 3, 0), (2049, 263, 1, 6), (1001, 5, 2, 1),
+                                         (8, 64, 1, 0), (12, 33, 1, 3), (6143, 17, 1, 0), (4096, 90, 1, 0),
+                                         (12289, 9, 1, 0)])
+def test_bwd_rows_off_the_grid_shared_offset(dtype, wdtype, H, M, off, pad):
+    """dy, x, dres and dx rows at one shared offset within their 16-byte
+    chunks (the same element offset and row stride in every buffer), so the
+    backward sets its vectors on memory's 16-byte grid: the row's first
+    vector at the row start, the chunks in between aligned, the last one the
+    window over the row's last 16 bytes.  Row lengths that touch one more
+    chunk than vectors at the row offset (4095, 2049 + 6 pad, 12), rows of
+    one vector (8), several hundred rows whose workgroup count is rounded down
+    so that every row of a workgroup keeps one offset (300 rows of 4097).
+    Parity with the oracle for the plain and the residual backward, pads and
+    buffer ends never written; dx written over dy and over x, and dh over
+    dres, give the same bits; and dx at another offset (vectors at the row
+    offset) is at parity too."""
+    d = G.inputs(91 + H + off, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
+    r32 = oracle_rrms32(d["x"], d["w"], 1e-5, dtype, wdtype)
+    rr = torch.from_numpy(r32).to(G.DEV)
+    wd = G.to_dev(d["w"], wdtype)
+    es = 4 if dtype == "f32" else 2
+    print(f"[gpu] bwd shared offset {dtype}/{wdtype} H={H} M={M} off={off} pad={pad}", flush=True)
+    assert tn.tile("bwd", H, dtype, off_grid=True, shared_offset=True)["frame"] == \
+        (not tn.tile("bwd", H, dtype, off_grid=True)["multi_pass"]
+         and not tn.tile("bwd", H + (16 - es) // es, dtype, off_grid=True)["multi_pass"])
+
+    def views():
+        out = {}
+        for key in ("dy", "x", "r"):
+            _, v = G.sentinel_view(M, H, pad, off, dtype, 0.0)
+            v.copy_(G.to_dev(d[key], dtype))
+            out[key] = v
+        return out
+
+    v = views()
+    dxbuf, dxv = G.sentinel_view(M, H, pad, off, dtype, -77.0)
+    dhbuf, dhv = G.sentinel_view(M, H, pad, off, dtype, -77.0)
+    _, dw = tn.rmsnorm_bwd(v["dy"], v["x"], wd, rr, dx=dxv)
+    _, dw2 = tn.rmsnorm_bwd_residual(v["dy"], v["x"], v["r"], wd, rr, dh=dhv)
+    torch.cuda.synchronize()
+    assert G.untouched(dxbuf, dxv, -77.0) and G.untouched(dhbuf, dhv, -77.0)
+    reps = list(G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dxv, dtype), dw.cpu().numpy(), dtype,
+                                wdtype=wdtype, name=f"bwd frame {dtype}/{wdtype} H={H}"))
+    reps += list(G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], r32, G.to_host(dhv, dtype),
+                                          dw2.cpu().numpy(), dtype, wdtype=wdtype, name=f"bwd_res frame {dtype} H={H}"))
+    G.assert_ok(*reps)
+    bits = (lambda t: t.contiguous().view(torch.int32)) if dtype == "f32" else \
+        (lambda t: t.contiguous().view(torch.int16))
+    # in place (fresh inputs for each call): the same tile, the same bits
+    _, dw_a = tn.rmsnorm_bwd(v["dy"], v["x"], wd, rr, dx=v["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(v["dy"]), bits(dxv)) and torch.equal(dw_a, dw)
+    v = views()
+    _, dw_b = tn.rmsnorm_bwd_residual(v["dy"], v["x"], v["r"], wd, rr, dh=v["r"])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(v["r"]), bits(dhv)) and torch.equal(dw_b, dw2)
+    v = views()
+    _, dw_c = tn.rmsnorm_bwd(v["dy"], v["x"], wd, rr, dx=v["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(bits(v["x"]), bits(dxv)) and torch.equal(dw_c, dw)
+    # dx one element further on: its rows sit at another offset, so the
+    # vectors go to each row's offset instead
+    v = views()
+    _, dxo = G.sentinel_view(M, H, pad, off + 1, dtype, -77.0)
+    _, dw_o = tn.rmsnorm_bwd(v["dy"], v["x"], wd, rr, dx=dxo)
+    torch.cuda.synchronize()
+    G.assert_ok(*G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dxo, dtype), dw_o.cpu().numpy(), dtype,
+                                 wdtype=wdtype, name=f"bwd row offset {dtype}/{wdtype} H={H}"))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("H", [8, 15, 63, 64, 128, 255, 256, 257, 384, 511])
 def test_fwd_short_rows_off_the_grid(dtype, H):

@@ -16,6 +16,13 @@ This test needs no GPU: it asks the library for the tile each call takes
 (rmsnorm_tuning_tile) and lists the exposed shapes, H <= 8192 in every
 format.  The in-place GPU tests run the listed worked case, bf16 H = 4097.
 
+A backward whose row streams share one offset within their 16-byte chunks
+sets its vectors on memory's 16-byte grid instead (the frame): the row's
+first vector then sits at the row start and overlaps the next chunk (lanes 0
+and 1, always one wave), and its last is the same window over the row's last
+16 bytes, after up to one more vector than at the row's offset.  The same row
+barrier orders those overlaps.
+
 Backward rows longer than one tile take two passes; there the window is read
 in pass 1 only, and in pass 2 (dx stores, workspace updates) the lane of the
 last partial vector takes its own columns one by one, so no shape of that
@@ -106,7 +113,8 @@ def test_exposure_table(capsys):
         assert wpr > 1 and (-(-H // vec) - 1) % 64 == 0
 
 
-@pytest.mark.parametrize("args", [(-1, 64, 2, 0), (6, 64, 2, 0), (0, 64, 2, 2), (0, 0, 2, 0), (0, 64, 9, 0)])
+@pytest.mark.parametrize("args", [(-1, 64, 2, 0), (6, 64, 2, 0), (0, 64, 2, 3), (0, 64, 2, -1), (0, 0, 2, 0),
+                                  (0, 64, 9, 0)])
 def test_tile_query_rejects_bad_arguments(args):
     import ctypes
     lib = _lib()
@@ -188,3 +196,42 @@ def test_adaln_keeps_two_workgroups_per_cu_on_its_large_tiles():
     # rows no 8-wave tile covers stay resident on the best tile over the cap
     t = tn.tile("adaln", 24576, "bf16", off_grid=False)
     assert not t["multi_pass"] and t["wpr"] > 8
+
+
+@pytest.mark.parametrize("op", ["bwd", "bwd_residual"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_frame_tile_covers_the_chunks_a_row_touches(op, dt):
+    # a row of H elements at offset a (a multiple of the element size, below
+    # 16) within its first 16-byte chunk touches ceil((a + H*es) / 16)
+    # chunks, at most ceil((H*es + 16 - es) / 16); the frame's tile holds that
+    # many vectors, in one pass, wherever the row-offset tile is one pass and
+    # the rule for the extra vector stays one pass
+    es = ES[dt]
+    _lib()
+    seen = 0
+    for H in list(range(16 // es, 2600)) + [4095, 4097, 6143, 8191, 12287, 12289, 16383]:
+        off = tn.tile(op, H, dt, off_grid=True)
+        fr = tn.tile(op, H, dt, off_grid=True, shared_offset=True)
+        chunks = -(-(H * es + 16 - es) // 16)
+        if fr["frame"]:
+            seen += 1
+            assert off["mis"] and not off["multi_pass"] and not fr["multi_pass"], (H, off, fr)
+            assert fr["vec"] == 16 // es and 64 * fr["wpr"] * fr["vpt"] >= chunks, (H, fr)
+        else:
+            assert off["multi_pass"] or not off["mis"] or \
+                tn.tile(op, H + (16 - es) // es, dt, off_grid=True)["multi_pass"], (H, off, fr)
+    assert seen > 2000
+    # on the grid (layout 0) there is no frame
+    assert not tn.tile(op, 4096, dt, off_grid=False, shared_offset=True)["frame"]
+
+
+def test_frame_worked_case():
+    # bf16 H = 4097: 8194 bytes touch 513 chunks at any even offset, the same
+    # 9-wave one-vector tile as at the row offset
+    off = tn.tile("bwd", 4097, "bf16", off_grid=True)
+    fr = tn.tile("bwd", 4097, "bf16", off_grid=True, shared_offset=True)
+    assert fr["frame"] and (fr["vpt"], fr["wpr"]) == (off["vpt"], off["wpr"]) == (1, 9)
+    # bf16 H = 4095: 8190 bytes touch 513 chunks at offsets 4 .. 14 (512
+    # vectors at the row offset)
+    assert tn.tile("bwd", 4095, "bf16", off_grid=True, shared_offset=True)["wpr"] == 9
+    assert tn.tile("bwd", 4095, "bf16", off_grid=True)["wpr"] == 8

@@ -509,16 +509,19 @@ _TILE_OPS = {"fwd": 0, "fwd_residual": 1, "adaln": 2, "layernorm": 3, "bwd": 4, 
 _DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
 
 
-def tile(op: str, H: int, dtype: str, off_grid: bool) -> dict:
+def tile(op: str, H: int, dtype: str, off_grid: bool, shared_offset: bool = False) -> dict:
     """Development hook (include/rmsnorm_tuning.h), host only: the register
     tile the library picks for `op` at row length H in `dtype` ("f32", "f16",
     "bf16"), for rows on the 16-byte grid (off_grid False) or rows whose
-    starts are only element-aligned (True)."""
+    starts are only element-aligned (True); shared_offset: off the grid, with
+    every row stream of a backward at one offset within its 16-byte chunks
+    ("frame": the backward's vectors then sit on memory's 16-byte grid)."""
     lib = load_library()
     out = (ctypes.c_int32 * 6)()
-    _check(lib, lib.rmsnorm_tuning_tile(_TILE_OPS[op], int(H), _DTYPE_NAMES[dtype], 1 if off_grid else 0, out))
+    layout = (2 if shared_offset else 1) if off_grid else 0
+    _check(lib, lib.rmsnorm_tuning_tile(_TILE_OPS[op], int(H), _DTYPE_NAMES[dtype], layout, out))
     return {"vec": out[0], "vpt": out[1], "wpr": out[2], "rpw": out[3], "mis": bool(out[4]),
-            "multi_pass": bool(out[5])}
+            "frame": out[4] == 2, "multi_pass": bool(out[5])}
 
 
 def copy_reference(src, dst) -> None:

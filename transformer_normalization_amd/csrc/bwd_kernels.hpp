@@ -51,6 +51,7 @@ struct BwdParams {
     int64_t M;
     int64_t rows_per_wg;  // contiguous order: rows of one workgroup
     int interleave;       // 1: workgroup b owns rows b, b+P, b+2P, ...
+    int frame;            // MIS, one pass: 1 = vectors on memory's 16-byte grid (below)
     int H;
     int nvec;
     int wpr;
@@ -70,6 +71,18 @@ struct BwdParams {
 // window lane also computes and writes the same dx values for them, and its
 // dw partial sums for them are not stored; two passes use the window in
 // pass 1 only (see there).  No access leaves the row.
+//
+// With `frame` set (one pass), the host has checked that x, dy, dres and dx
+// rows all sit at the same offset a within their 16-byte chunks of memory,
+// the same for every row of a workgroup.  Vector v then covers the aligned
+// chunk (row start - a) + 16v, i.e. columns c = (16v - a)/ES ..; the first
+// vector is moved to the row start (columns 0 ..) and the last one to the
+// window over the row's last 16 bytes, so that every access stays inside the
+// row, and only those two are unaligned.  Each lane owns the columns of its
+// chunk that lie in the row, [max(c, 0), min(c + VEC, H)); the other columns
+// of its vector are also a neighbour lane's, and it leaves them out of the
+// row sum and the dw partial sums exactly as the window does.  a = 0 gives
+// the vectors at the row's offset above, so one code path serves both.
 
 // DEEP: one more row in flight per wave (three prefetched instead of two), for
 // one-vector tiles that leave few waves resident per CU (the host's rule).
@@ -103,15 +116,39 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
         // only the dw partial sums are float32 registers.
         Raw<WDT, VEC> wr[VPT];
         float dwa[VPT][VEC];
-        // rows off the grid: column of the thread's window, and how many of
-        // its leading columns are the previous vector's (last vector only)
-        int col0[VPT], dup[VPT];
+        // rows off the grid: the rows' offset a in the 16-byte frame (0
+        // without `frame`) and the vectors a row takes
+        int fa = 0, nact = p.nvec;
+        if constexpr (MIS) {
+            if (p.frame)
+                fa = (int)((reinterpret_cast<uintptr_t>(p.x) + (uint64_t)start * (uint64_t)p.xs * Fmt<XDT>::bytes) &
+                           15u);
+            nact = (fa + p.H * Fmt<XDT>::bytes + 15) >> 4;
+        }
+        // rows off the grid: first column of the thread's vector; own(k)
+        // gives the columns [lo, hi) of it that the thread owns (recomputed
+        // where needed rather than held across the row loop)
+        int col0[VPT];
+        auto own = [&](int k, int &lo, int &hi) {
+            if constexpr (MIS) {
+                const int c = (16 * (t + k * row_threads) - fa) / Fmt<XDT>::bytes;  // negative: the first chunk
+                lo = (c < 0 ? 0 : c) - col0[k];
+                hi = (c + VEC < p.H ? c + VEC : p.H) - col0[k];
+            } else {
+                lo = 0;
+                hi = VEC;
+            }
+        };
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const int v = t + k * row_threads;
-            col0[k] = MIS && v * VEC > p.H - VEC ? p.H - VEC : v * VEC;
-            dup[k] = MIS ? v * VEC - col0[k] : 0;
-            if (p.w != nullptr && v < p.nvec) {
+            if constexpr (MIS) {
+                const int c = (16 * v - fa) / Fmt<XDT>::bytes;
+                col0[k] = c < 0 ? 0 : c > p.H - VEC ? p.H - VEC : c;
+            } else {
+                col0[k] = v * VEC;
+            }
+            if (p.w != nullptr && v < nact) {
                 if constexpr (MIS) {
                     constexpr int WES = Fmt<WDT>::bytes;
 #pragma unroll
@@ -135,9 +172,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 constexpr int PER_WORD = 4 / Fmt<WDT>::bytes;
                 float f[VEC];
                 wr[k].widen_to(f);
+                int lo, hi;
+                own(k, lo, hi);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    if (e < dup[k]) f[e] = 0.0f;
+                    if (e < lo || e >= hi) f[e] = 0.0f;
 #pragma unroll
                 for (int c = 0; c < Raw<WDT, VEC>::CHUNKS; ++c)
 #pragma unroll
@@ -174,9 +213,9 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
                     const int vv = t + k * row_threads;
-                    const int v = vv < p.nvec ? vv : p.nvec - 1;
+                    const int v = vv < nact ? vv : nact - 1;
                     if constexpr (MIS) {
-                        const int64_t o = (int64_t)(vv < p.nvec ? col0[k] : p.H - VEC) * ES;
+                        const int64_t o = (int64_t)(vv < nact ? col0[k] : p.H - VEC) * ES;
                         xd[k].v[0] = load16_at<NT>(static_cast<const char *>(p.x) + row * p.xs * ES + o);
                         dd[k].v[0] = load16_at<NT>(static_cast<const char *>(p.dy) + row * p.dys * ES + o);
                         if constexpr (RES)
@@ -205,7 +244,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     float part = 0.0f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) part = __builtin_fmaf(dv[e] * wv[e], xv[e] * rs, part);
-                    if (t + k * row_threads < p.nvec) acc += part;
+                    if (t + k * row_threads < nact) acc += part;
                 }
                 // Off the grid, the window lane's leading columns are another
                 // lane's too, possibly in another wave, and dh may be the same
@@ -232,7 +271,7 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                     xr[k].widen_to(xv);
                     dr[k].widen_to(dv);
                     wr[k].widen_to(wv);
-                    if (v < p.nvec) {
+                    if (v < nact) {
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
                             const float xn = xv[e] * rs;
@@ -289,9 +328,11 @@ __global__ void __launch_bounds__(MAXT) rmsnorm_bwd_kernel(const BwdParams p) {
                 const int v = t + k * row_threads;
                 if constexpr (MIS) {
                     // the workspace rows are H floats apart, so off the grid too
+                    int lo, hi;
+                    own(k, lo, hi);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e)
-                        if (v < p.nvec && e >= dup[k]) part[(int64_t)col0[k] + e] = dwa[k][e];
+                        if (v < nact && e >= lo && e < hi) part[(int64_t)col0[k] + e] = dwa[k][e];
                 } else {
                     if (v < p.nvec) store_elems<DT_F32, VEC>(part, (int64_t)v * VEC, dwa[k]);
                 }

@@ -559,6 +559,21 @@ Geom bwd_tile(Kind kind, int H, int eb, bool vec_ok, bool mis_ok, bool *mis, int
     return g;
 }
 
+// The tile of a backward on rows off the grid whose vectors sit on memory's
+// 16-byte grid (`frame`): a row of H elements at offset a within its first
+// chunk spans up to ceil((H * eb + 16 - eb) / 16) chunks, one more vector than
+// at the row's offset when H * eb mod 16 is 0 or above eb.  The vector tile
+// rule for that many vectors; false when it takes two passes (the frame is
+// for one pass only) or single elements.
+bool bwd_frame_tile(Kind kind, int H, int eb, Geom *out) {
+    bool mis = false;
+    int elem_groups = 0;
+    const Geom g = bwd_tile(kind, H + (16 - eb) / eb, eb, false, true, &mis, &elem_groups);
+    if (!mis || g.two_pass) return false;
+    *out = g;
+    return true;
+}
+
 size_t bwd_workspace(int64_t M, int64_t H) {
     if (M <= 0 || H <= 0 || H > kMaxH) return 0;
     const int64_t cap = max_partials(H);
@@ -705,34 +720,67 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
         if (ov.d == 2) interleave = false;
     }
     const bool nt = use_streaming((res ? 4 : 3) * M * H * eb);
-    // Whole row groups per CU, rows interleaved (see bwd_groups_per_cu).
-    const int gpc = elem_groups > 0 ? elem_groups : bwd_groups_per_cu(res, g.wpr, g.nvec);
-    // A one-vector tile whose rule leaves at most 6 waves per CU keeps three
-    // rows in flight per wave instead of two.  Measured on gfx950 (bf16,
-    // 2^25-element calls, two rows in brackets): plain aligned H = 512 (4
-    // waves) 67.4 % (61.2 %), 3072 (6) 62.5 % (60.0 %), off the grid
-    // H = 1025 (6) 52.9 % (48.7 %), 2049 (5) 50.0 % (44.7 %), residual off the
-    // grid H = 1025 (3) 44.3 % (39.2 %), 2049 (5) 56.7 % (52.8 %).  With more
-    // waves it lost: plain aligned H = 2048 and 1024 (8 waves) -1.1 and -0.6
-    // points, 6144 (12) -1.0; and so did the aligned residual H = 512 (4
-    // waves, -3.3), which keeps two.  Same bits either way.  16-bit formats
-    // only (as measured).
-    const bool deep =
-        !ov.set && eb == 2 && !g.two_pass && g.vec > 1 && g.vpt == 1 && (mis || !res) && gpc * g.wpr <= 6;
+    // Rows off the grid whose x, dy, dres and dx rows all sit at the same
+    // offset within their 16-byte chunks take their vectors on memory's
+    // 16-byte grid instead (`frame` in rmsnorm_bwd_kernel), on the tile that
+    // covers the one extra vector a row may then take.  Measured on gfx950,
+    // bf16 8192 x 4097: 16-byte vectors at the row offset took 48.5 us, the
+    // same tile on rows on the grid (H = 4104) 39.6 us.
+    bool af = false;
+    const Geom g_off = g;  // the row-offset tile
+    if (mis && !g.two_pass && interleave) {
+        const uintptr_t bx = reinterpret_cast<uintptr_t>(x);
+        auto same_offsets = [&](const void *q, int64_t s) {
+            return ((reinterpret_cast<uintptr_t>(q) - bx) & 15u) == 0 && (((uint64_t)(s - xs) * eb) & 15u) == 0;
+        };
+        if (same_offsets(dy, dys) && same_offsets(dx, dxs) && (!res || same_offsets(dres, drs)))
+            af = bwd_frame_tile(kind, (int)H, eb, &g);
+    }
+    int cus = 0;
+    if ((st = device_info(&cus)) != RMSN_OK) return st;
+    int gpc = 0;
+    bool deep = false;
+    int64_t rows_per = 0;
+    const int64_t P_set = P;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        // Whole row groups per CU, rows interleaved (see bwd_groups_per_cu).
+        gpc = elem_groups > 0 ? elem_groups : bwd_groups_per_cu(res, g.wpr, g.nvec);
+        // A one-vector tile whose rule leaves at most 6 waves per CU keeps three
+        // rows in flight per wave instead of two.  Measured on gfx950 (bf16,
+        // 2^25-element calls, two rows in brackets): plain aligned H = 512 (4
+        // waves) 67.4 % (61.2 %), 3072 (6) 62.5 % (60.0 %), off the grid
+        // H = 1025 (6) 52.9 % (48.7 %), 2049 (5) 50.0 % (44.7 %), residual off the
+        // grid H = 1025 (3) 44.3 % (39.2 %), 2049 (5) 56.7 % (52.8 %).  With more
+        // waves it lost: plain aligned H = 2048 and 1024 (8 waves) -1.1 and -0.6
+        // points, 6144 (12) -1.0; and so did the aligned residual H = 512 (4
+        // waves, -3.3), which keeps two.  Same bits either way.  16-bit formats
+        // only (as measured).
+        deep = !ov.set && eb == 2 && !g.two_pass && g.vec > 1 && g.vpt == 1 && (mis || !res) && gpc * g.wpr <= 6;
+        // The dw partial sums are P x H x 4 bytes, written and read once.  A
+        // grid that is not a multiple of the CU count leaves a tail of CUs
+        // with an extra block.
+        P = P_set > 0 ? P_set : (int64_t)cus * gpc;
+        if (P > max_partials(H)) P = max_partials(H);
+        if (P > M) P = M;
+        rows_per = (M + P - 1) / P;
+        P = (M + rows_per - 1) / rows_per;
+        if (!af || P >= M) break;
+        // AF: the rows b, b + P, ... of a workgroup share one offset when P
+        // rows span a whole number of 16-byte chunks
+        const uint64_t rb = ((uint64_t)xs * eb) & 15u;
+        const int64_t q = rb == 0 ? 1 : rb % 8 == 0 ? 2 : rb % 4 == 0 ? 4 : rb % 2 == 0 ? 8 : 16;
+        if (P >= q) {
+            P = P / q * q;
+            rows_per = (M + P - 1) / P;
+            break;
+        }
+        af = false;  // too few workgroups for that: the row-offset tile
+        g = g_off;
+    }
     bwd_fn fn = mis   ? bwd_mis_lookup(xdt, w ? wdt : xdt, g.vpt, g.two_pass, res, nt, deep)
                 : res ? bwd_lookup_res(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt)
                       : bwd_lookup_plain(xdt, w ? wdt : xdt, g.vec, g.vpt, g.two_pass, nt, deep);
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
-    int cus = 0;
-    if ((st = device_info(&cus)) != RMSN_OK) return st;
-    // The dw partial sums are P x H x 4 bytes, written and read once.  A grid
-    // that is not a multiple of the CU count leaves a tail of CUs with an
-    // extra block.
-    if (P <= 0) P = (int64_t)cus * gpc;
-    if (P > max_partials(H)) P = max_partials(H);
-    if (P > M) P = M;
-    const int64_t rows_per = (M + P - 1) / P;
-    P = (M + rows_per - 1) / rows_per;
     if (use_scratch && dw != nullptr) {
         if ((uint64_t)P * (uint64_t)H * sizeof(float) > kScratchBytes)
             return fail(RMSN_ERR_WORKSPACE,
@@ -757,6 +805,7 @@ rmsn_status_t bwd_impl(const void *dy, int64_t dys, const void *x, int64_t xs, c
     p.M = M;
     p.rows_per_wg = rows_per;
     p.interleave = interleave ? 1 : 0;
+    p.frame = af ? 1 : 0;
     p.H = (int)H;
     p.nvec = g.nvec;
     p.wpr = g.wpr;
@@ -895,7 +944,7 @@ RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third
 RMSN_API rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dtype, int layout, int32_t out[6]) {
     if (out == nullptr) return fail(RMSN_ERR_INVALID_ARG, "out is NULL");
     if (op < 0 || op > 5) return fail(RMSN_ERR_INVALID_ARG, "op = %d must be 0 .. 5", op);
-    if (layout != 0 && layout != 1) return fail(RMSN_ERR_INVALID_ARG, "layout = %d must be 0 or 1", layout);
+    if (layout < 0 || layout > 2) return fail(RMSN_ERR_INVALID_ARG, "layout = %d must be 0, 1 or 2", layout);
     rmsn_status_t st = check_common(0, H, x_dtype, nullptr, x_dtype);
     if (st != RMSN_OK) return st;
     static const Kind kinds[6] = {Kind::Fwd, Kind::FwdResid, Kind::FwdAdaln, Kind::Ln, Kind::Bwd, Kind::BwdRes};
@@ -904,13 +953,14 @@ RMSN_API rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dty
     const bool vec_ok = layout == 0 && H % (16 / eb) == 0;
     bool mis = false;
     int elem_groups = 0;
-    const Geom g = op >= 4 ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
-                           : fwd_tile(kind, (int)H, eb, eb, vec_ok, !vec_ok, &mis);
+    Geom g = op >= 4 ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
+                     : fwd_tile(kind, (int)H, eb, eb, vec_ok, !vec_ok, &mis);
+    const bool frame = layout == 2 && op >= 4 && mis && !g.two_pass && bwd_frame_tile(kind, (int)H, eb, &g);
     out[0] = g.vec;
     out[1] = g.two_pass ? 0 : g.vpt;
     out[2] = g.two_pass ? 0 : g.wpr;
     out[3] = op >= 4 ? 1 : g.rpw;
-    out[4] = mis ? 1 : 0;
+    out[4] = frame ? 2 : mis ? 1 : 0;
     out[5] = g.two_pass ? 1 : 0;
     return ok();
 }

@@ -53,24 +53,25 @@ def test_workload_adaln(name):
                                    chunk=4096, name=name), record=name)
 
 
-@pytest.mark.parametrize("B,S", [(3, 6000), (3, 6001), (16, 1100)])
-def test_per_batch_rows_walked_by_each_row_group(B, S):
+@pytest.mark.parametrize("B,S,H", [(3, 6000, 2048), (3, 6001, 2048), (16, 1100, 2048), (3, 6001, 4104)])
+def test_per_batch_rows_walked_by_each_row_group(B, S, H):
     """Per-batch conditioning on a large grid: each row group walks 4 rows
     a quarter of the call apart, so its rows cross batch boundaries (the
     conditioning rows are reloaded there) and the last iteration runs past
     M (ragged: 3 x 6001 rows is an odd number of two-row groups).  Parity
     with the oracle and the same bits as the one-row-per-row-group grid of
-    the same tile."""
-    H, dt = 2048, "bf16"
+    the same tile (H = 4104: the two-wave tile of 513 vectors)."""
+    dt = "bf16"
     M = B * S
     d = G.inputs(470 + S, M, H, dt)
     sc = synthetic.normal_tensor(470 + S, synthetic.STREAM_SCALE, (B, H), dt, 0.0, 0.5)
     sh = synthetic.normal_tensor(470 + S, synthetic.STREAM_SHIFT, (B, H), dt, 0.0, 0.5)
-    print(f"[gpu] adaln per-batch walk B={B} S={S}", flush=True)
+    print(f"[gpu] adaln per-batch walk B={B} S={S} H={H}", flush=True)
     y, rr = run(d["x"], d["w"], sc, sh, B, S, 1e-6, dt)
     G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, S, y, rr, 1e-6, dt, chunk=S * max(1, 4096 // S),
                                    name=f"adaln walk {B}x{S}"))
-    tn.set_geometry("fwd", 2, 2, 2, 0)  # the same tile, one row per row group
+    t = tn.tile("adaln", H, dt, off_grid=False)
+    tn.set_geometry("fwd", t["vpt"], t["wpr"], t["rpw"], 0)  # the same tile, one row per row group
     y1, rr1 = run(d["x"], d["w"], sc, sh, B, S, 1e-6, dt)
     assert np.array_equal(y, y1) and np.array_equal(rr, rr1)
 
@@ -79,7 +80,7 @@ def test_per_batch_rows_walked_by_each_row_group(B, S):
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 # 16384: capped tile; 32768: the longest 16-bit row held in registers with
 # 16-bit parameters (two passes with float32 ones)
-@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 3072, 4097, 8192, 16384, 20000, 32768])
+@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 2056, 3072, 3584, 4097, 4104, 6144, 8192, 16384, 20000, 32768])
 def test_adaln_shapes(dtype, pdtype, H):
     pd = dtype if pdtype == "same" else "f32"
     B, S = 3, 7

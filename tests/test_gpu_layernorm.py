@@ -68,7 +68,8 @@ def test_workload_ln_residual():
 
 # 12288 and 16384 (16-bit) and 8192 (float32) take tiles capped at 4 waves per
 # row; 24576 is the longest 16-bit row held in registers
-LN_H = [1, 3, 8, 64, 65, 512, 1000, 1024, 2049, 4096, 8191, 8192, 12288, 16384, 16385, 24576, 24577, 65536]
+LN_H = [1, 3, 8, 64, 65, 512, 1000, 1024, 2049, 2056, 3584, 4096, 6144, 8191, 8192, 12288, 16384, 16385, 24576,
+        24577, 65536]
 
 
 @pytest.mark.parametrize("resid", [True, False], ids=["residual", "plain"])

@@ -152,7 +152,8 @@ def test_workload_bwd_chained_with_gpu_rrms():
 # for the plain float32 forward), and so does 8192 in float32 (3 x 11);
 # 32768 and 65536 (32767 and 65535 off the grid) are the longest 16-bit rows
 # the fused residual and the plain forward hold in registers
-EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 3072, 4097, 5120, 6144, 8191, 8192, 12288,
+EDGE_H = [1, 3, 7, 8, 63, 64, 65, 127, 511, 512, 513, 1000, 2047, 2049, 2056, 3072, 3584, 4097, 4104, 5120, 6144,
+          8191, 8192, 12288,
           16384, 16385, 32767, 32768, 65535, 65536]
 
 

@@ -235,3 +235,22 @@ def test_frame_worked_case():
     # vectors at the row offset)
     assert tn.tile("bwd", 4095, "bf16", off_grid=True, shared_offset=True)["wpr"] == 9
     assert tn.tile("bwd", 4095, "bf16", off_grid=True)["wpr"] == 8
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_two_waves_per_row_for_16bit_rows_on_the_grid(dt):
+    # 16-bit rows on the grid of 193 to 768 vectors take two waves per row
+    # for LayerNorm and AdaLN always, for the plain forward unless the
+    # general rule's tile is a whole tile of 2 or more vectors per thread
+    # (3072, 4096, 5120, 6144 keep it); the fused residual keeps its rule
+    tile = lambda op, H: tuple(tn.tile(op, H, dt, off_grid=False)[k] for k in ("vpt", "wpr", "rpw"))
+    for H, vpt in ((2056, 3), (2560, 3), (3072, 3), (3584, 4), (4096, 4), (4104, 6), (5120, 6), (6144, 6)):
+        assert tile("layernorm", H) == (vpt, 2, 2), H
+        assert tile("adaln", H) == (vpt, 2, 2), H
+    for H, want in ((2056, (3, 2, 2)), (2560, (3, 2, 2)), (3584, (4, 2, 2)), (4104, (6, 2, 2)),
+                    (3072, (2, 3, 2)), (4096, (2, 4, 1)), (5120, (2, 5, 1)), (6144, (2, 6, 1))):
+        assert tile("fwd", H) == want, H
+    assert tile("fwd_residual", 2056) == (1, 5, 1)
+    # outside the range, and float32 rows, the general rule
+    assert tile("layernorm", 8192) == (2, 8, 1)
+    assert tn.tile("layernorm", 4096, "f32", off_grid=False)["wpr"] != 2

@@ -244,7 +244,17 @@ Geom fwd_tile(Kind kind, int H, int eb, int pb, bool vec_ok, bool mis_ok, bool *
         *mis = true;
         return m;
     }
-    return pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16, pb);
+    Geom g = pick_row_geom(kind, H, vec_ok ? vecw : 1, eb == 4 ? 8 : 16, pb);
+    // 16-bit rows on the grid of 193 to 768 vectors: two waves per row too,
+    // for LayerNorm and AdaLN always, for the plain forward unless the rule's
+    // tile is a whole tile of 2 or more vectors per thread; the fused
+    // residual keeps the rule's tile.
+    if (vec_ok && eb == 2 && kind != Kind::FwdResid && !g.two_pass) {
+        const Geom t = pick_two_wave_geom(kind, H, vecw, pb);
+        const bool whole = g.vpt >= 2 && 64 * g.wpr * g.vpt == g.nvec;
+        if (t.vpt != 0 && (kind != Kind::Fwd || !whole)) g = t;
+    }
+    return g;
 }
 
 // ---------------------------------------------------------------------------

@@ -46,9 +46,13 @@
  *    which is off unless a caller sets it through that header's functions
  *    (no environment variable or other input reaches it).
  *  - Results do not depend on the stream, on timing or on other calls: the
- *    same inputs give the same bits on the same device.  A tile forced
- *    through rmsnorm_tuning_set_geometry() changes the order of the float32
- *    sums, and so may change bits, within the same tolerances.
+ *    same inputs in the same layout give the same bits on the same device.
+ *    The order of the float32 sums follows the tile, which depends on H, the
+ *    formats and whether rows sit on the 16-byte grid; a backward on rows off
+ *    it whose tensors share one offset within their 16-byte blocks also
+ *    follows that offset.  Other layouts of the same values may then differ
+ *    in the last bits, within the same tolerances; so may a tile forced
+ *    through rmsnorm_tuning_set_geometry().
  */
 #ifndef RMSNORM_H
 #define RMSNORM_H

@@ -336,3 +336,69 @@ def test_random_tile_class(case):
     for b, v in outs:
         if b is not None:
             assert G.untouched(b, v, -77.0), case
+
+
+# ---------------------------------------------------------------------------
+# backward on rows off the 16-byte grid whose tensors share one offset
+# ---------------------------------------------------------------------------
+# Every tensor of the call (dy, x, dres, dx) in a buffer of the same padding
+# at the same element offset, so that the backward sets its vectors on
+# memory's 16-byte grid: row lengths drawn log-uniformly from 16 bytes to
+# 20000 elements, 1 to 700 rows (the workgroup count rounded down for larger
+# calls), every format, float32 weights for some 16-bit cases, and dx either
+# a separate padded buffer or written over dy, x or dres.
+
+N_FRAME_CASES = 60
+
+
+def _frame_cases():
+    rng = np.random.default_rng(20261203)  # picks shapes and layouts only
+    out = []
+    for i in range(N_FRAME_CASES):
+        op = ("bwd", "bwd_residual")[i % 2]
+        dtype = ("bf16", "f16", "f32")[int(rng.integers(0, 3))]
+        es = 4 if dtype == "f32" else 2
+        H = int(np.exp(rng.uniform(np.log(16 // es), np.log(20000.0))))
+        H = max(H, 16 // es)
+        M = int(np.exp(rng.uniform(0.0, np.log(700.0))))
+        wdtype = "f32" if dtype != "f32" and rng.uniform() < 0.3 else dtype
+        off = int(rng.integers(1, 16 // es))
+        pad = int(rng.integers(0, 10))
+        dest = ("separate", "dy", "x", "dres")[int(rng.integers(0, 4 if op == "bwd_residual" else 3))]
+        out.append((i, op, M, H, dtype, wdtype, off, pad, dest))
+    return out
+
+
+FRAME_CASES = _frame_cases()
+
+
+@pytest.mark.parametrize("case", FRAME_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[4]}-{c[2]}x{c[3]}-o{c[6]}p{c[7]}-{c[8]}" for c in FRAME_CASES])
+def test_random_shared_offset_backward(case):
+    i, op, M, H, dtype, wdtype, off, pad, dest = case
+    seed = 9500 + i
+    print(f"[gpu] frame {i} {op} {dtype}/{wdtype} M={M} H={H} off={off} pad={pad} dx={dest}", flush=True)
+    d = G.inputs(seed, M, H, dtype, wdtype=wdtype, residual=True, dy=True)
+    r32 = _rrms32_as(d["x"], d["w"], 1e-5, dtype, wdtype)
+    rr = torch.from_numpy(r32).to(G.DEV)
+    t = {k: _placed(d[k], dtype, True, pad, off) for k in ("dy", "x", "r")}
+    w = G.to_dev(d["w"], wdtype)
+    buf = None
+    if dest == "separate":
+        buf, out = G.sentinel_view(M, H, pad, off, dtype, -77.0)
+    else:
+        out = t[{"dy": "dy", "x": "x", "dres": "r"}[dest]]
+    if op == "bwd":
+        dx, dw = tn.rmsnorm_bwd(t["dy"], t["x"], w, rr, dx=out)
+        torch.cuda.synchronize()
+        reps = G.bwd_vs_oracle(d["dy"], d["x"], d["w"], r32, G.to_host(dx, dtype), dw.cpu().numpy(), dtype, wdtype,
+                               name=f"frame {i} bwd")
+    else:
+        dx, dw = tn.rmsnorm_bwd_residual(t["dy"], t["x"], t["r"], w, rr, dh=out)
+        torch.cuda.synchronize()
+        reps = G.bwd_residual_vs_oracle(d["dy"], d["x"], d["r"], d["w"], r32, G.to_host(dx, dtype),
+                                        dw.cpu().numpy(), dtype, wdtype, name=f"frame {i} bwd_residual")
+    assert dx.data_ptr() == out.data_ptr()
+    G.assert_ok(*reps)
+    if buf is not None:
+        assert G.untouched(buf, out, -77.0), case

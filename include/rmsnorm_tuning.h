@@ -45,7 +45,7 @@ void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third, int64_t
 /*
  * Host only (touches no device): the tile a call takes with no forced
  * geometry.  op: 0 RMSNorm forward, 1 fused residual, 2 AdaLN, 3 LayerNorm,
- * 4 backward, 5 residual backward.  layout 0: every row start 16-byte
+ * 4 backward, 5 residual backward, 6 LayerNorm fused with the residual add.  layout 0: every row start 16-byte
  * aligned; 1: row starts only element-aligned (parameters 16-byte aligned);
  * 2: as 1, with every row stream of the call (x, dy, dres, dx) at one shared
  * offset within its 16-byte chunks, the same for every row a backward

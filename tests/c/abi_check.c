@@ -147,7 +147,7 @@ int main(void) {
         expect("tile query off grid", rmsnorm_tuning_tile(1, 4097, RMSN_BF16, 1, t), RMSN_OK);
         if (t[4] != 1) { printf("FAIL tile query off grid: mis %d\n", t[4]); ++failures; }
         expect("tile query NULL", rmsnorm_tuning_tile(0, 4096, RMSN_BF16, 0, NULL), RMSN_ERR_INVALID_ARG);
-        expect("tile query bad op", rmsnorm_tuning_tile(6, 4096, RMSN_BF16, 0, t), RMSN_ERR_INVALID_ARG);
+        expect("tile query bad op", rmsnorm_tuning_tile(7, 4096, RMSN_BF16, 0, t), RMSN_ERR_INVALID_ARG);
         expect("tile query H 0", rmsnorm_tuning_tile(0, 0, RMSN_BF16, 0, t), RMSN_ERR_INVALID_ARG);
         expect("tile query bad dtype", rmsnorm_tuning_tile(0, 64, (rmsn_dtype_t)9, 0, t), RMSN_ERR_UNSUPPORTED);
     }

@@ -113,7 +113,7 @@ def test_exposure_table(capsys):
         assert wpr > 1 and (-(-H // vec) - 1) % 64 == 0
 
 
-@pytest.mark.parametrize("args", [(-1, 64, 2, 0), (6, 64, 2, 0), (0, 64, 2, 3), (0, 64, 2, -1), (0, 0, 2, 0),
+@pytest.mark.parametrize("args", [(-1, 64, 2, 0), (7, 64, 2, 0), (0, 64, 2, 3), (0, 64, 2, -1), (0, 0, 2, 0),
                                   (0, 64, 9, 0)])
 def test_tile_query_rejects_bad_arguments(args):
     import ctypes
@@ -252,5 +252,19 @@ def test_two_waves_per_row_for_16bit_rows_on_the_grid(dt):
         assert tile("fwd", H) == want, H
     assert tile("fwd_residual", 2056) == (1, 5, 1)
     # outside the range, and float32 rows, the general rule
-    assert tile("layernorm", 8192) == (2, 8, 1)
+    assert tile("layernorm", 12288)[1] != 2
     assert tn.tile("layernorm", 4096, "f32", off_grid=False)["wpr"] != 2
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_layernorm_two_wave_tile_of_up_to_eight_vectors(dt):
+    # plain LayerNorm of 16-bit rows on the grid of 769 to 1024 vectors:
+    # two waves of 8 vectors per thread, two rows per workgroup; the
+    # LayerNorm fused with the residual add keeps the general rule
+    tile = lambda op, H: tuple(tn.tile(op, H, dt, off_grid=False)[k] for k in ("vpt", "wpr", "rpw"))
+    for H in (6152, 7168, 7176, 8192):
+        assert tile("layernorm", H) == (8, 2, 2), H
+    assert tile("layernorm", 6144) == (6, 2, 2)
+    assert tile("layernorm_residual", 8192) == (2, 8, 1)
+    assert tile("layernorm_residual", 4096) == tile("layernorm", 4096)
+    assert tile("layernorm", 8200) != (8, 2, 2)

@@ -505,7 +505,8 @@ def set_geometry(which: str, vpt: int = 0, wpr: int = 0, third: int = 0, grid: i
     load_library().rmsnorm_tuning_set_geometry(code, int(vpt), int(wpr), int(third), int(grid))
 
 
-_TILE_OPS = {"fwd": 0, "fwd_residual": 1, "adaln": 2, "layernorm": 3, "bwd": 4, "bwd_residual": 5}
+_TILE_OPS = {"fwd": 0, "fwd_residual": 1, "adaln": 2, "layernorm": 3, "bwd": 4, "bwd_residual": 5,
+             "layernorm_residual": 6}
 _DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
 
 

@@ -101,11 +101,17 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems, int pb = 4) {
     // at H = 16384, while at H <= 8192 its tiles were within 1 %).  A
     // penalty, not a limit: with no tile under the cap the row stays
     // resident on the best tile over it.
-    // AdaLN tiles of more than 16 elements per thread (104-124 VGPRs, four
-    // waves per SIMD) count as over the cap beyond 8 waves: one such
-    // workgroup per CU then leaves SIMDs idle (bf16, 2048 rows: H = 16384 on
-    // 3 x 11 waves 74.5 % against 82.8 % on 4 x 8, H = 12296 on 3 x 9 66.1 %
-    // against 76.9 % on 4 x 7).
+    // AdaLN tiles count as over the cap beyond 8 waves: 16-bit ones always,
+    // float32 ones of more than 16 elements per thread.  Tiles of more than
+    // 16 elements per thread take 104-124 VGPRs (four waves per SIMD), and
+    // one such workgroup per CU leaves SIMDs idle (bf16, 2048 rows:
+    // H = 16384 on 3 x 11 waves 74.5 % against 82.8 % on 4 x 8, H = 12296 on
+    // 3 x 9 66.1 % against 76.9 % on 4 x 7).  16-bit rows of 2 vectors per
+    // thread on more than 8 waves ran slow too (bf16 8192 rows, per token:
+    // H = 10240 on 2 x 10 waves 65.7 % against 79.0 % on 3 x 7, H = 12288 on
+    // 2 x 12 67.5 % against 81.0 % on 3 x 8; per batch 51.0 % and 54.5 %
+    // against 62.0 % and 68.6 %); float32 rows on 12 waves lost nothing
+    // (float32 8192 x 6144 80.7 % against 79.4 % on 3 x 8).
     const int wcap = kind == Kind::Ln ? (g.nvec > 1024 ? 4 : 16) : bwd ? 16 : 12;
     double best = 1e30;
     for (int i = 0; i < nset; ++i) {
@@ -116,7 +122,7 @@ Geom pick_row_geom(Kind kind, int H, int vec, int pref_elems, int pb = 4) {
         const double slots = 64.0 * wpr * vpt;
         const double idle = (slots - g.nvec) / slots;
         const double pref = std::fabs(std::log2((double)(vpt * vec) / pref_elems));
-        const int cap = kind == Kind::FwdAdaln && vpt * vec > 16 ? 8 : wcap;
+        const int cap = kind == Kind::FwdAdaln && (vpt * vec > 16 || vec == 8) ? 8 : wcap;
         const double cost = 8.0 * idle + pref + (wpr > cap ? 4.0 : 0.0);
         if (cost < best) {
             best = cost;
@@ -231,7 +237,7 @@ Geom pick_two_wave_geom(Kind kind, int H, int vec, int pb) {
 // 0.1 %; float32 H = 4097 the same, fused residual H = 1025 66.1 % against
 // 68.3 %, so float32 keeps the aligned rule.  Otherwise the element-wise
 // tile.
-Geom fwd_tile(Kind kind, int H, int eb, int pb, bool vec_ok, bool mis_ok, bool *mis) {
+Geom fwd_tile(Kind kind, int H, int eb, int pb, bool vec_ok, bool mis_ok, bool *mis, bool ln_resid = false) {
     const int vecw = 16 / eb;
     const bool offrule = kind == Kind::Fwd || kind == Kind::FwdResid || (kind == Kind::Ln && eb == 2);
     *mis = false;
@@ -253,6 +259,20 @@ Geom fwd_tile(Kind kind, int H, int eb, int pb, bool vec_ok, bool mis_ok, bool *
         const Geom t = pick_two_wave_geom(kind, H, vecw, pb);
         const bool whole = g.vpt >= 2 && 64 * g.wpr * g.vpt == g.nvec;
         if (t.vpt != 0 && (kind != Kind::Fwd || !whole)) g = t;
+    }
+    // 16-bit LayerNorm rows on the grid of 769 to 1024 vectors: two waves of
+    // 8 vectors per thread, two rows per workgroup.  Measured on gfx950,
+    // bf16 8192 x 8192: 46.6 us against 47.6 us on 2 x 8 waves walking two
+    // rows (50.0 us without the walk), 16384 x 8192 88.1 against 90.4 us,
+    // 8192 x 7168 41.2 against 43.8 us; the fused residual LayerNorm (90.1
+    // against 88.7 us), the plain forward and AdaLN lost on that tile (45.5
+    // against 44.8 us, 86.8 against 85.0 us).
+    if (vec_ok && eb == 2 && kind == Kind::Ln && !ln_resid && !g.two_pass && g.nvec > 768 && g.nvec <= 1024 &&
+        max_threads_for(kind, 8, vecw, pb) >= 256) {
+        g.vpt = 8;
+        g.wpr = 2;
+        g.rpw = 2;
+        g.nchunks = 1;
     }
     return g;
 }
@@ -357,7 +377,7 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     bool mis = false;
     // the parameters' format as the kernels see it (x's when there are none)
     const int kpb = dtype_bytes((w || adaln || bias) ? wdt : xdt);
-    Geom g = fwd_tile(kind, (int)H, eb, kpb, vec_ok, mis_ok, &mis);
+    Geom g = fwd_tile(kind, (int)H, eb, kpb, vec_ok, mis_ok, &mis, ln && resid);
     int64_t grid = (M + g.rpw - 1) / g.rpw;
     if (ov.set) {
         // bounds first: the products below are then small
@@ -408,9 +428,12 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
         // groups per CU: with half the workgroups, smaller calls pay a
         // partial last round of resident workgroups (bf16 4096 x 4096 53.6 %
         // against 56.6 %).  The residual form, with twice the row streams,
-        // and RMSNorm's one weight row lost or gained nothing.
-        if (!resid && w != nullptr && bias != nullptr && !ov.set && !g.two_pass && 2 * H * kpb >= 16384 &&
-            groups >= 32LL * cus) {
+        // and RMSNorm's one weight row lost or gained nothing.  Rows of one or
+        // two waves do not walk: on the two-wave tiles the walk measured level
+        // or slower (bf16 8192 x 4096 24.5-24.7 us either way, 8192 x 6144
+        // 40.7 us walking against 38.7 us).
+        if (!resid && w != nullptr && bias != nullptr && !ov.set && !g.two_pass && g.wpr > 2 &&
+            2 * H * kpb >= 16384 && groups >= 32LL * cus) {
             grid = (groups + 1) / 2;
             iters = (groups + grid - 1) / grid;
         }
@@ -953,23 +976,25 @@ RMSN_API void rmsnorm_tuning_set_geometry(int which, int vpt, int wpr, int third
 
 RMSN_API rmsn_status_t rmsnorm_tuning_tile(int op, int64_t H, rmsn_dtype_t x_dtype, int layout, int32_t out[6]) {
     if (out == nullptr) return fail(RMSN_ERR_INVALID_ARG, "out is NULL");
-    if (op < 0 || op > 5) return fail(RMSN_ERR_INVALID_ARG, "op = %d must be 0 .. 5", op);
+    if (op < 0 || op > 6) return fail(RMSN_ERR_INVALID_ARG, "op = %d must be 0 .. 6", op);
     if (layout < 0 || layout > 2) return fail(RMSN_ERR_INVALID_ARG, "layout = %d must be 0, 1 or 2", layout);
     rmsn_status_t st = check_common(0, H, x_dtype, nullptr, x_dtype);
     if (st != RMSN_OK) return st;
-    static const Kind kinds[6] = {Kind::Fwd, Kind::FwdResid, Kind::FwdAdaln, Kind::Ln, Kind::Bwd, Kind::BwdRes};
+    static const Kind kinds[7] = {Kind::Fwd, Kind::FwdResid, Kind::FwdAdaln, Kind::Ln,
+                                  Kind::Bwd, Kind::BwdRes, Kind::Ln};
     const Kind kind = kinds[op];
     const int eb = dtype_bytes(x_dtype);
     const bool vec_ok = layout == 0 && H % (16 / eb) == 0;
     bool mis = false;
     int elem_groups = 0;
-    Geom g = op >= 4 ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
-                     : fwd_tile(kind, (int)H, eb, eb, vec_ok, !vec_ok, &mis);
-    const bool frame = layout == 2 && op >= 4 && mis && !g.two_pass && bwd_frame_tile(kind, (int)H, eb, &g);
+    const bool bwd = op == 4 || op == 5;
+    Geom g = bwd ? bwd_tile(kind, (int)H, eb, vec_ok, !vec_ok, &mis, &elem_groups)
+                 : fwd_tile(kind, (int)H, eb, eb, vec_ok, !vec_ok, &mis, op == 6);
+    const bool frame = layout == 2 && bwd && mis && !g.two_pass && bwd_frame_tile(kind, (int)H, eb, &g);
     out[0] = g.vec;
     out[1] = g.two_pass ? 0 : g.vpt;
     out[2] = g.two_pass ? 0 : g.wpr;
-    out[3] = op >= 4 ? 1 : g.rpw;
+    out[3] = bwd ? 1 : g.rpw;
     out[4] = frame ? 2 : mis ? 1 : 0;
     out[5] = g.two_pass ? 1 : 0;
     return ok();

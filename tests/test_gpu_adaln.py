@@ -78,9 +78,11 @@ def test_per_batch_rows_walked_by_each_row_group(B, S, H):
 
 @pytest.mark.parametrize("pdtype", ["same", "f32"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-# 16384: capped tile; 32768: the longest 16-bit row held in registers with
-# 16-bit parameters (two passes with float32 ones)
-@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 2056, 3072, 3584, 4097, 4104, 6144, 8192, 16384, 20000, 32768])
+# 10240 and 16384: capped tiles (16-bit rows at most 8 waves); 32768: the
+# longest 16-bit row held in registers with 16-bit parameters (two passes with
+# float32 ones)
+@pytest.mark.parametrize("H", [1, 7, 64, 1000, 2048, 2056, 3072, 3584, 4097, 4104, 6144, 8192, 10240, 16384, 20000,
+                               32768])
 def test_adaln_shapes(dtype, pdtype, H):
     pd = dtype if pdtype == "same" else "f32"
     B, S = 3, 7

@@ -10,6 +10,7 @@ reproduces exactly (its id lists op, format, shape and padding).
 
 from __future__ import annotations
 
+import os
 import random
 import threading
 
@@ -29,7 +30,13 @@ if not torch.cuda.is_available():
 import transformer_normalization_amd as tn  # noqa: E402
 
 
-def _draw_cases(n=60, seed=20261202):
+# A longer soak: TN_RANDOM_SCALE multiplies the case count of every draw
+# below and TN_RANDOM_SEED shifts its seeds (unset: the committed draws).
+_SCALE = max(1, int(os.environ.get("TN_RANDOM_SCALE", "1")))
+_SEED = int(os.environ.get("TN_RANDOM_SEED", "0"))
+
+
+def _draw_cases(n=60 * _SCALE, seed=20261202 + _SEED):
     rng = random.Random(seed)
     ops = ["fwd", "fwd_residual", "adaln", "bwd", "bwd_residual", "layernorm", "layernorm_residual", "rope"]
     cases = []
@@ -212,11 +219,11 @@ def test_concurrent_calls_from_threads_on_their_own_streams():
 # their outputs' padding must stay untouched.
 
 TILE_OPS = ("fwd", "residual", "adaln_batch", "adaln_token", "layernorm", "bwd", "bwd_residual")
-N_TILE_CASES = 280
+N_TILE_CASES = 280 * _SCALE
 
 
 def _tile_cases():
-    rng = np.random.default_rng(20261202)  # picks shapes and layouts only
+    rng = np.random.default_rng(20261202 + _SEED)  # picks shapes and layouts only
     out = []
     for i in range(N_TILE_CASES):
         op = TILE_OPS[i % len(TILE_OPS)]
@@ -348,11 +355,11 @@ def test_random_tile_class(case):
 # calls), every format, float32 weights for some 16-bit cases, and dx either
 # a separate padded buffer or written over dy, x or dres.
 
-N_FRAME_CASES = 60
+N_FRAME_CASES = 60 * _SCALE
 
 
 def _frame_cases():
-    rng = np.random.default_rng(20261203)  # picks shapes and layouts only
+    rng = np.random.default_rng(20261203 + _SEED)  # picks shapes and layouts only
     out = []
     for i in range(N_FRAME_CASES):
         op = ("bwd", "bwd_residual")[i % 2]

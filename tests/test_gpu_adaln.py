@@ -53,20 +53,23 @@ def test_workload_adaln(name):
                                    chunk=4096, name=name), record=name)
 
 
-@pytest.mark.parametrize("B,S,H", [(3, 6000, 2048), (3, 6001, 2048), (16, 1100, 2048), (3, 6001, 4104)])
-def test_per_batch_rows_walked_by_each_row_group(B, S, H):
+@pytest.mark.parametrize("B,S,H,dt", [(2, 6000, 2048, "bf16"), (2, 9001, 2048, "bf16"), (2, 9001, 4104, "bf16"),
+                                      (3, 6001, 2048, "f32"), (16, 1100, 2048, "f32"), (3, 6001, 2048, "bf16"),
+                                      (16, 1100, 2048, "bf16")])
+def test_per_batch_rows_walked_by_each_row_group(B, S, H, dt):
     """Per-batch conditioning on a large grid: each row group walks 4 rows
-    a quarter of the call apart, so its rows cross batch boundaries (the
-    conditioning rows are reloaded there) and the last iteration runs past
-    M (ragged: 3 x 6001 rows is an odd number of two-row groups).  Parity
-    with the oracle and the same bits as the one-row-per-row-group grid of
-    the same tile (H = 4104: the two-wave tile of 513 vectors)."""
-    dt = "bf16"
+    a quarter of the call apart (16-bit rows with at most two conditioning
+    rows, float32 rows with any number), so its rows cross batch boundaries
+    (the conditioning rows are reloaded there) and the last iteration runs
+    past M (ragged: 2 x 9001 rows is an odd number of two-row groups);
+    16-bit calls of more batches take one row per row group.  Parity with
+    the oracle and the same bits as the one-row-per-row-group grid of the
+    same tile (H = 4104: the two-wave tile of 513 vectors)."""
     M = B * S
     d = G.inputs(470 + S, M, H, dt)
     sc = synthetic.normal_tensor(470 + S, synthetic.STREAM_SCALE, (B, H), dt, 0.0, 0.5)
     sh = synthetic.normal_tensor(470 + S, synthetic.STREAM_SHIFT, (B, H), dt, 0.0, 0.5)
-    print(f"[gpu] adaln per-batch walk B={B} S={S} H={H}", flush=True)
+    print(f"[gpu] adaln per-batch walk {dt} B={B} S={S} H={H}", flush=True)
     y, rr = run(d["x"], d["w"], sc, sh, B, S, 1e-6, dt)
     G.assert_ok(*G.adaln_vs_oracle(d["x"], d["w"], sc, sh, S, y, rr, 1e-6, dt, chunk=S * max(1, 4096 // S),
                                    name=f"adaln walk {B}x{S}"))

@@ -475,9 +475,17 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     // gfx950, bf16 2 x 4096 x 2048 with one conditioning row per batch:
     // 14.30 us against 15.25 us with one row per row group (same tile, same
     // bits); per-token conditioning gained nothing.  Only where the grid
-    // keeps at least 4 workgroups per CU.
+    // keeps at least 4 workgroups per CU.  16-bit rows walk only when the
+    // call has at most two conditioning rows: with more, a row group's rows
+    // (a quarter of the call apart) mostly fall in different batches and
+    // reload theirs, and the smaller grid lost (bf16, one row per row group
+    // first: 4 x 4096 x 2048 26.5 against 27.5 us, 16 x 1024 x 2048 25.8
+    // against 27.4 us, 3 x 4096 x 2048 22.3 against 22.7 us, 8 x 1024 x 2048
+    // level).  float32 rows, with twice the weight bytes, still gained from
+    // the walk at three batches (3 x 4096 x 2048 38.4 against 40.5 us).
     int64_t run_iters = iters;
-    if (adaln && !ov.set && !g.two_pass && cond.rows_per_cond >= 4 && groups >= 16LL * cus) {
+    const bool walk_rows = eb == 4 || M <= 2 * cond.rows_per_cond;
+    if (adaln && !ov.set && !g.two_pass && cond.rows_per_cond >= 4 && walk_rows && groups >= 16LL * cus) {
         grid = (groups + 3) / 4;
         if (grid > INT32_MAX) grid = INT32_MAX;
         run_iters = (groups + grid - 1) / grid;

@@ -55,11 +55,12 @@ def test_workload_adaln(name):
 
 @pytest.mark.parametrize("B,S,H,dt", [(2, 6000, 2048, "bf16"), (2, 9001, 2048, "bf16"), (2, 9001, 4104, "bf16"),
                                       (3, 6001, 2048, "f32"), (16, 1100, 2048, "f32"), (3, 6001, 2048, "bf16"),
-                                      (16, 1100, 2048, "bf16")])
+                                      (16, 1100, 2048, "bf16"), (2, 4501, 4096, "bf16"), (2, 4501, 2048, "f32")])
 def test_per_batch_rows_walked_by_each_row_group(B, S, H, dt):
     """Per-batch conditioning on a large grid: each row group walks 4 rows
     a quarter of the call apart (16-bit rows with at most two conditioning
-    rows, float32 rows with any number), so its rows cross batch boundaries
+    rows, float32 rows with any number; rows of 8 KiB or more with at most
+    two conditioning rows walk 8), so its rows cross batch boundaries
     (the conditioning rows are reloaded there) and the last iteration runs
     past M (ragged: 2 x 9001 rows is an odd number of two-row groups);
     16-bit calls of more batches take one row per row group.  Parity with

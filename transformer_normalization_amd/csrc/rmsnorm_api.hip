@@ -470,12 +470,13 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     if (fn == nullptr) return fail(RMSN_ERR_INVALID_ARG, "no kernel for vec %d vpt %d", g.vec, g.vpt);
     if ((st = device_info(&cus)) != RMSN_OK) return st;
     // AdaLN with conditioning rows shared by many rows (per-batch scale and
-    // shift): each row group walks 4 rows, so that the weight and the
+    // shift): each row group walks 4 (or 8) rows, so that the weight and the
     // conditioning rows it holds in registers serve all of them.  Measured on
     // gfx950, bf16 2 x 4096 x 2048 with one conditioning row per batch:
     // 14.30 us against 15.25 us with one row per row group (same tile, same
-    // bits); per-token conditioning gained nothing.  Only where the grid
-    // keeps at least 4 workgroups per CU.  16-bit rows walk only when the
+    // bits); per-token conditioning gained nothing.  Only where the grid of
+    // one row per row group has at least 16 workgroups per CU.  16-bit rows
+    // walk only when the
     // call has at most two conditioning rows: with more, a row group's rows
     // (a quarter of the call apart) mostly fall in different batches and
     // reload theirs, and the smaller grid lost (bf16, one row per row group
@@ -483,10 +484,18 @@ rmsn_status_t fwd_impl(int mode, const void *x, int64_t xs, const void *r, int64
     // against 27.4 us, 3 x 4096 x 2048 22.3 against 22.7 us, 8 x 1024 x 2048
     // level).  float32 rows, with twice the weight bytes, still gained from
     // the walk at three batches (3 x 4096 x 2048 38.4 against 40.5 us).
+    // Rows of 8 KiB or more walk 8 rows when the call has at most two
+    // conditioning rows (walk of 4 first): bf16 2 x 4096 x 8192 51.7 against
+    // 48.7 us, 2 x 4096 x 6144 37.3 against 36.8 us, float32 2 x 4096 x 2048
+    // 26.1 against 24.9 us, 2 x 4096 x 4096 47.8 against 46.8 us; 4 KiB rows
+    // lost on 8 (bf16 2 x 4096 x 2048 14.3 against 16.3 us, float32
+    // 2 x 4096 x 1024 14.0 against 14.8 us).
     int64_t run_iters = iters;
-    const bool walk_rows = eb == 4 || M <= 2 * cond.rows_per_cond;
+    const bool few_cond = M <= 2 * cond.rows_per_cond;
+    const bool walk_rows = eb == 4 || few_cond;
+    const int64_t walk = H * eb >= 8192 && few_cond ? 8 : 4;
     if (adaln && !ov.set && !g.two_pass && cond.rows_per_cond >= 4 && walk_rows && groups >= 16LL * cus) {
-        grid = (groups + 3) / 4;
+        grid = (groups + walk - 1) / walk;
         if (grid > INT32_MAX) grid = INT32_MAX;
         run_iters = (groups + grid - 1) / grid;
     }

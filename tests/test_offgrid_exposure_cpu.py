@@ -196,6 +196,14 @@ def test_adaln_keeps_two_workgroups_per_cu_on_its_large_tiles():
     # rows no 8-wave tile covers stay resident on the best tile over the cap
     t = tn.tile("adaln", 24576, "bf16", off_grid=False)
     assert not t["multi_pass"] and t["wpr"] > 8
+    # 16-bit rows take the 8-wave cap at 2 vectors per thread too (3 x 7
+    # rather than 2 x 10 at H = 10240); float32 rows of 16 elements per
+    # thread keep the 12-wave cap
+    for H, tile in ((10240, (3, 7)), (12288, (3, 8))):
+        t = tn.tile("adaln", H, "bf16", off_grid=False)
+        assert (t["vpt"], t["wpr"]) == tile, (H, t)
+    t = tn.tile("adaln", 12288, "f32", off_grid=False)
+    assert (t["vpt"], t["wpr"]) == (4, 12), t
 
 
 @pytest.mark.parametrize("op", ["bwd", "bwd_residual"])
